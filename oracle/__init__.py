@@ -1,0 +1,250 @@
+"""Delta-KV CPU oracle (TEST INFRASTRUCTURE ONLY).
+
+ctypes wrapper around ``dkv_oracle.c``: the plain sequential C reference of the
+Delta-KV codec (keyframe + closed-loop Q4_0 deltas) and float64 decode
+attention.  Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline
+leg of ``bench.py`` may import this package; the HIP library never does, and
+the two share no code.
+
+Canonical encoded layout of one stream (what every function here produces):
+
+* ``kf_rows``  uint16 ``[ceil(S/kf), D]`` -- fp16 bits of each group's keyframe
+* ``codes``    uint8  ``[n_delta, D/2]``  -- Q4_0 bytes, block-major, byte i of a
+  block holds code i (low nibble) and code i+16 (high nibble)
+* ``scales``   uint16 ``[n_delta, D/32]`` -- fp16 bits of each block scale
+
+with ``n_delta = S - ceil(S/kf)``; delta token t sits at row
+``(t//kf)*(kf-1) + t%kf - 1``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "dkv_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libdkv_oracle.so")
+_lib = None
+
+CFLAGS = ["-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared"]
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.check_call(["gcc", *CFLAGS, _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        build(force=True)
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.c_void_p
+    L = ctypes.c_long
+    I = ctypes.c_int
+    lib.oracle_f16_to_f32.argtypes = [ctypes.c_uint16]
+    lib.oracle_f16_to_f32.restype = ctypes.c_float
+    lib.oracle_f32_to_f16.argtypes = [ctypes.c_float]
+    lib.oracle_f32_to_f16.restype = ctypes.c_uint16
+    lib.oracle_q40_block.argtypes = [P, P, P]
+    lib.oracle_q40_block.restype = None
+    lib.oracle_q40_pack.argtypes = [P, P]
+    lib.oracle_q40_unpack.argtypes = [P, P]
+    lib.oracle_delta_index.argtypes = [L, I]
+    lib.oracle_delta_index.restype = L
+    lib.oracle_step.argtypes = [P, L, I, I, P, P, P, P]
+    lib.oracle_encode_stream.argtypes = [P, L, I, I, P, P, P, P, P]
+    lib.oracle_reconstruct_stream.argtypes = [P, P, P, L, I, I, P]
+    lib.oracle_q40_abs_stream.argtypes = [P, L, I, P, P]
+    lib.oracle_q40_dequant_stream.argtypes = [P, P, L, I, P]
+    lib.oracle_attention_f64.argtypes = [P, I, P, P, L, I, ctypes.c_float, P]
+    for name in ("oracle_step", "oracle_encode_stream", "oracle_reconstruct_stream",
+                 "oracle_q40_abs_stream", "oracle_q40_dequant_stream", "oracle_attention_f64",
+                 "oracle_q40_pack", "oracle_q40_unpack"):
+        getattr(lib, name).restype = None
+    _lib = lib
+    return lib
+
+
+def _p(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _as_f16_bits(x) -> np.ndarray:
+    x = np.asarray(x)
+    if x.dtype == np.float16:
+        x = x.view(np.uint16)
+    assert x.dtype == np.uint16, x.dtype
+    return np.ascontiguousarray(x)
+
+
+# ---------------------------------------------------------------- scalars
+def f16_to_f32(h: int) -> float:
+    return float(_load().oracle_f16_to_f32(int(h)))
+
+
+def f32_to_f16(f: float) -> int:
+    return int(_load().oracle_f32_to_f16(float(np.float32(f))))
+
+
+def n_groups(S: int, kf: int) -> int:
+    return -(-S // kf)
+
+
+def n_delta(S: int, kf: int) -> int:
+    return S - n_groups(S, kf)
+
+
+def delta_index(t: int, kf: int) -> int:
+    return int(_load().oracle_delta_index(t, kf))
+
+
+# ---------------------------------------------------------------- Q4_0 block
+def q40_block(v) -> tuple[int, np.ndarray]:
+    """Quantise 32 fp32 values -> (fp16 scale bits, codes[32] in 0..15)."""
+    v = np.ascontiguousarray(np.asarray(v, dtype=np.float32))
+    assert v.shape == (32,)
+    s = np.zeros(1, np.uint16)
+    c = np.zeros(32, np.uint8)
+    _load().oracle_q40_block(_p(v), _p(s), _p(c))
+    return int(s[0]), c
+
+
+def q40_pack(codes) -> np.ndarray:
+    codes = np.ascontiguousarray(np.asarray(codes, dtype=np.uint8))
+    out = np.zeros(16, np.uint8)
+    _load().oracle_q40_pack(_p(codes), _p(out))
+    return out
+
+
+def q40_unpack(b) -> np.ndarray:
+    b = np.ascontiguousarray(np.asarray(b, dtype=np.uint8))
+    out = np.zeros(32, np.uint8)
+    _load().oracle_q40_unpack(_p(b), _p(out))
+    return out
+
+
+# ---------------------------------------------------------------- streams
+class EncodedStream:
+    __slots__ = ("kf_rows", "codes", "scales", "recon", "state", "S", "D", "kf")
+
+    def __init__(self, S, D, kf):
+        self.S, self.D, self.kf = S, D, kf
+        self.kf_rows = np.zeros((n_groups(S, kf), D), np.uint16)
+        self.codes = np.zeros((n_delta(S, kf), D // 2), np.uint8)
+        self.scales = np.zeros((n_delta(S, kf), D // 32), np.uint16)
+        self.recon = None
+        self.state = np.zeros(D, np.float32)
+
+
+def encode_stream(x, kf: int, want_recon: bool = True) -> EncodedStream:
+    """Encode one stream x[S][D] (fp16) with keyframe interval kf."""
+    x = _as_f16_bits(x)
+    S, D = x.shape
+    assert D % 32 == 0 and kf >= 1
+    e = EncodedStream(S, D, kf)
+    if want_recon:
+        e.recon = np.zeros((S, D), np.float32)
+    _load().oracle_encode_stream(_p(x), S, D, kf, _p(e.kf_rows), _p(e.codes), _p(e.scales),
+                                 _p(e.recon) if want_recon else None, _p(e.state))
+    return e
+
+
+def step(e: EncodedStream, x_row, t: int, xh: np.ndarray) -> None:
+    """Append token t of a stream into the canonical arrays (in place)."""
+    x_row = _as_f16_bits(x_row)
+    assert xh.dtype == np.float32 and xh.flags["C_CONTIGUOUS"]
+    _load().oracle_step(_p(x_row), t, e.D, e.kf, _p(e.kf_rows), _p(e.codes), _p(e.scales), _p(xh))
+
+
+def reconstruct_stream(kf_rows, codes, scales, S: int, D: int, kf: int) -> np.ndarray:
+    kf_rows = _as_f16_bits(kf_rows)
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = _as_f16_bits(scales)
+    out = np.zeros((S, D), np.float32)
+    _load().oracle_reconstruct_stream(_p(kf_rows), _p(codes), _p(scales), S, D, kf, _p(out))
+    return out
+
+
+def q40_abs_stream(x) -> tuple[np.ndarray, np.ndarray]:
+    x = _as_f16_bits(x)
+    S, D = x.shape
+    codes = np.zeros((S, D // 2), np.uint8)
+    scales = np.zeros((S, D // 32), np.uint16)
+    _load().oracle_q40_abs_stream(_p(x), S, D, _p(codes), _p(scales))
+    return codes, scales
+
+
+def q40_dequant_stream(codes, scales) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = _as_f16_bits(scales)
+    S, D = codes.shape[0], codes.shape[1] * 2
+    out = np.zeros((S, D), np.float32)
+    _load().oracle_q40_dequant_stream(_p(codes), _p(scales), S, D, _p(out))
+    return out
+
+
+def attention_f64(q, K, V, scale: float) -> np.ndarray:
+    """Float64 decode attention of G heads q[G][D] over K[S][D], V[S][D]."""
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    K = np.ascontiguousarray(K, dtype=np.float32)
+    V = np.ascontiguousarray(V, dtype=np.float32)
+    G, D = q.shape
+    S = K.shape[0]
+    assert K.shape == (S, D) and V.shape == (S, D)
+    out = np.zeros((G, D), np.float64)
+    _load().oracle_attention_f64(_p(q), G, _p(K), _p(V), S, D, float(np.float32(scale)), _p(out))
+    return out
+
+
+# ---------------------------------------------------------------- whole caches
+def encode_cache(k, v, seq_lens, kf: int, want_recon: bool = True):
+    """Encode every stream of fp16 K/V [B][Hkv][s_max][D].
+
+    Returns a dict of per-(b, h, stream) EncodedStream objects keyed
+    ``(b, h, s)`` with s = 0 for K and 1 for V.
+    """
+    k = _as_f16_bits(k)
+    v = _as_f16_bits(v)
+    B, H, _, D = k.shape
+    out = {}
+    for b in range(B):
+        S = int(seq_lens[b])
+        for h in range(H):
+            for s, x in ((0, k), (1, v)):
+                out[(b, h, s)] = encode_stream(np.ascontiguousarray(x[b, h, :S]), kf, want_recon)
+    return out
+
+
+def attention_cache(enc, q, seq_lens, n_kv_heads: int, scale: float, heads=None):
+    """Float64 attention for q[B][Hq][D] over an encoded cache (from encode_cache).
+
+    ``heads``: optional list of (b, hq) pairs to compute; others stay NaN.
+    """
+    q = np.asarray(q, dtype=np.float32)
+    B, Hq, D = q.shape
+    G = Hq // n_kv_heads
+    out = np.full((B, Hq, D), np.nan)
+    want = None if heads is None else set(heads)
+    for b in range(B):
+        for h in range(n_kv_heads):
+            hq = [h * G + g for g in range(G)]
+            if want is not None:
+                hq = [x for x in hq if (b, x) in want]
+                if not hq:
+                    continue
+            Kr = enc[(b, h, 0)].recon
+            Vr = enc[(b, h, 1)].recon
+            res = attention_f64(q[b, hq], Kr, Vr, scale)
+            out[b, hq] = res
+    return out
