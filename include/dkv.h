@@ -1,0 +1,218 @@
+/*
+ * dkv.h -- Delta-KV compressed KV cache and fused decode attention on MI355X
+ * (gfx950).  C ABI of libdkv.so.
+ *
+ * Method (web page "영상 압축 기법을 KV 캐시에 적용해 Q4 양자화 오차를 10,000배
+ * 줄인 Delta-KV", jeff.news, sections "핵심 아이디어" and "벤치마크"): each K
+ * and each V stream of one (sequence, kv-head) is stored as an fp16 keyframe
+ * every kf tokens; every other token stores the closed-loop difference to the
+ * previous reconstructed token, quantised Q4_0-style (32-element blocks, an
+ * fp16 scale and 4-bit codes: 18 bytes per 32 elements).  Decode attention
+ * (page "KV 캐시 벡터 양자화와 주의 보존 변환", llm-wiki.hwlabs.dev, sections
+ * "KV 캐시가 왜 병목인가" and "왜 복원 오차가 틀린 기준인가") reads the
+ * compressed cache directly: softmax(q.K^T * scale) . V with grouped-query
+ * heads (query head hq uses kv-head hq / (Hq/Hkv)).
+ *
+ * Conventions for every entry point:
+ *  - Pointers marked (device) are device memory on the current HIP device;
+ *    (host) pointers are host memory read during the call.  The caller owns
+ *    every buffer; the library allocates no memory and keeps no state.
+ *  - Every launch is asynchronous on `stream` (0 = the null stream).
+ *  - Arguments are validated on the host before anything is launched; a
+ *    failed check returns a status and launches nothing.  A HIP launch error
+ *    returns DKV_ERR_HIP.  No C++ exception crosses this interface.
+ *  - Preconditions the library cannot check (caller's responsibility, as for
+ *    any KV cache): K/V inputs are finite; positions and sequence lengths stay
+ *    within the cache capacity; appends arrive in token order; device arrays
+ *    have the documented sizes.
+ *
+ * Cache layout (one buffer holds one attention layer):
+ *  A "group" is the kf tokens that start at a keyframe.  Each (sequence,
+ *  kv-head, group) owns one group record of dkv_group_record_bytes() bytes
+ *  holding, in order, for K then for V:
+ *    keyframe  D fp16 values (channel order permuted for the matrix cores);
+ *    scales    kf x D/32 fp16 -- slot 0 holds the largest |scale| of each
+ *              block over the group's delta tokens, slots 1..kf-1 the scale
+ *              of each delta token's blocks;
+ *    codes     K: (kf-1) rows of D/2 bytes, one per delta token, each Q4_0
+ *              block's 16 canonical bytes split into four 4-byte pieces;
+ *              V: ceil(kf/32) tiles of 32 token slots, each channel's nibbles
+ *              of 8 tokens packed in one 32-bit word (slot 0 of a group is the
+ *              keyframe and carries no code).
+ *  Contiguous mode (page_tokens == 0): records are ordered
+ *  [batch][n_kv_heads][ceil(max_tokens/kf)].  Paged mode (page_tokens > 0,
+ *  page_tokens % kf == 0): a page holds page_tokens tokens of every kv-head,
+ *  ordered [n_kv_heads][page_tokens/kf]; block_table (device, int32
+ *  [batch][max_pages_per_seq]) maps a sequence's logical page to a physical
+ *  page in [0, n_pages).
+ *
+ * Reconstruction (the decoder): xhat = float(keyframe); then per delta token,
+ * per channel, xhat = fp32(xhat + (code-8)*float(scale)), folded in token
+ * order -- bit-identical to the encoder's closed loop.
+ */
+#ifndef DKV_H
+#define DKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t *dkv_stream_t; /* a hipStream_t */
+
+typedef enum {
+    DKV_OK = 0,
+    DKV_ERR_ARG = 1,         /* null pointer, non-positive size, inconsistent shape */
+    DKV_ERR_UNSUPPORTED = 2, /* valid but not built: head_dim not 64/128, kf > 1024 ... */
+    DKV_ERR_WORKSPACE = 3,   /* workspace missing or smaller than dkv_workspace_bytes() */
+    DKV_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
+} dkv_status;
+
+typedef struct {
+    int32_t batch;             /* B, sequences per call, >= 1 */
+    int32_t n_q_heads;         /* Hq, multiple of n_kv_heads */
+    int32_t n_kv_heads;        /* Hkv >= 1 */
+    int32_t head_dim;          /* D: 64 or 128 */
+    int32_t kf;                /* keyframe interval, 1..1024 */
+    int32_t max_tokens;        /* capacity per sequence (tokens), >= 1 */
+    int32_t page_tokens;       /* 0 = contiguous; else tokens per page, multiple of kf */
+    int32_t n_pages;           /* paged mode: physical pages in the buffer */
+    int32_t max_pages_per_seq; /* paged mode: row length of block_table */
+} dkv_config;
+
+/* Human-readable name of a status code (static string). */
+const char *dkv_status_str(dkv_status s);
+
+/* Checks a configuration without touching the GPU. */
+dkv_status dkv_check_config(const dkv_config *cfg);
+
+/* Bytes of one group record (K and V of one kv-head, kf tokens). 0 if cfg is invalid. */
+size_t dkv_group_record_bytes(const dkv_config *cfg);
+
+/* Bytes of one layer's compressed cache for cfg (header-free). 0 if cfg is invalid. */
+size_t dkv_cache_bytes(const dkv_config *cfg);
+
+/* Bytes of the reconstruction state: fp32 [batch][n_kv_heads][2][head_dim]
+ * (the last reconstructed K and V row of each sequence). */
+size_t dkv_state_bytes(const dkv_config *cfg);
+
+/* Bytes of the split-K workspace that dkv_attn_decode needs for cfg. */
+size_t dkv_workspace_bytes(const dkv_config *cfg);
+
+/*
+ * Bulk prefill encode.  Encodes tokens [0, seq_lens[b]) of every sequence.
+ *  k, v      (device) fp16 [batch][n_kv_heads][s_max][head_dim]
+ *  seq_lens  (device) int32 [batch], each in [0, min(s_max, capacity)]
+ *  cache     (device) dkv_cache_bytes(cfg) bytes, written
+ *  state     (device) fp32 state, written for every sequence with seq_lens > 0
+ *  block_table (device) int32 [batch][max_pages_per_seq] in paged mode, else NULL
+ * Parallel over (sequence, kv-head, K/V, group); each group is encoded
+ * token by token (closed loop).
+ */
+dkv_status dkv_encode_prefill(const dkv_config *cfg, void *cache, float *state,
+                              const int32_t *block_table, const uint16_t *k,
+                              const uint16_t *v, const int32_t *seq_lens, int32_t s_max,
+                              dkv_stream_t stream);
+
+/*
+ * Append one token per sequence (one decode step).
+ *  k_new, v_new (device) fp16 [batch][n_kv_heads][head_dim]
+ *  positions    (device) int32 [batch]: index of the new token (= tokens
+ *               already cached); a negative position skips the sequence.
+ *               The caller advances it afterwards.
+ * A token at a multiple of kf becomes a keyframe; any other token is
+ * quantised against `state`, which is updated.
+ */
+dkv_status dkv_append(const dkv_config *cfg, void *cache, float *state,
+                      const int32_t *block_table, const uint16_t *k_new,
+                      const uint16_t *v_new, const int32_t *positions, dkv_stream_t stream);
+
+/*
+ * Fused decode attention over the compressed cache.
+ *  q        (device) fp32 [batch][n_q_heads][head_dim]
+ *  seq_lens (device) int32 [batch]: tokens attended (0 gives a zero row)
+ *  softmax_scale: logit scale; 0 means 1/sqrt(head_dim)
+ *  out      (device) fp32 [batch][n_q_heads][head_dim]
+ *  workspace (device) at least dkv_workspace_bytes(cfg) bytes
+ */
+dkv_status dkv_attn_decode(const dkv_config *cfg, const void *cache,
+                           const int32_t *block_table, const float *q,
+                           const int32_t *seq_lens, float softmax_scale, float *out,
+                           void *workspace, size_t workspace_bytes, dkv_stream_t stream);
+
+/* The split phase of dkv_attn_decode alone: writes the per-split partial
+ * results (acc[D], running max, running sum) to the workspace and launches no
+ * combine.  For callers that overlap or merge the combine themselves, and for
+ * timing the fused kernel on its own.  Same arguments as dkv_attn_decode
+ * without `out`. */
+dkv_status dkv_attn_decode_partial(const dkv_config *cfg, const void *cache,
+                                   const int32_t *block_table, const float *q,
+                                   const int32_t *seq_lens, float softmax_scale,
+                                   void *workspace, size_t workspace_bytes,
+                                   dkv_stream_t stream);
+
+/* Same as dkv_attn_decode but through the plain (unfused-layout-agnostic)
+ * reference kernel: reconstructs each tile in fp32 and runs fp32 attention.
+ * Kept as a cross-check of the fused kernel. */
+dkv_status dkv_attn_decode_ref(const dkv_config *cfg, const void *cache,
+                               const int32_t *block_table, const float *q,
+                               const int32_t *seq_lens, float softmax_scale, float *out,
+                               void *workspace, size_t workspace_bytes,
+                               dkv_stream_t stream);
+
+/*
+ * Diagnostics.  Dense fp32 reconstruction of every cached token:
+ *  k_out, v_out (device) fp32 [batch][n_kv_heads][s_max][head_dim]; rows at
+ *  t >= seq_lens[b] are left untouched.
+ */
+dkv_status dkv_reconstruct(const dkv_config *cfg, const void *cache,
+                           const int32_t *block_table, const int32_t *seq_lens,
+                           int32_t s_max, float *k_out, float *v_out, dkv_stream_t stream);
+
+/*
+ * Diagnostics.  The encoded stream in canonical Q4_0 form, for bit-exact checks.
+ * With ng = ceil(s_max/kf) and nd = s_max - ng, for stream s (0 = K, 1 = V):
+ *  kf_rows (device) uint16 [batch][n_kv_heads][2][ng][head_dim], fp16 keyframes
+ *  codes   (device) uint8  [batch][n_kv_heads][2][nd][head_dim/2], delta token t
+ *          at row (t/kf)*(kf-1) + t%kf - 1, byte i of a block = code i | code i+16 << 4
+ *  scales  (device) uint16 [batch][n_kv_heads][2][nd][head_dim/32]
+ * codes and scales may be NULL when nd == 0 (kf == 1).
+ * Rows beyond a sequence's length are left untouched.
+ */
+dkv_status dkv_export(const dkv_config *cfg, const void *cache, const int32_t *block_table,
+                      const int32_t *seq_lens, int32_t s_max, uint16_t *kf_rows,
+                      uint8_t *codes, uint16_t *scales, dkv_stream_t stream);
+
+/*
+ * In-run comparison: plain Q4_0 cache of absolute values (the 4-bit baseline
+ * of the Delta-KV article's "벤치마크" section), 18 bytes per 32 elements.
+ * Contiguous layout only (page_tokens must be 0); kf is ignored.
+ */
+size_t dkv_q4_0_cache_bytes(const dkv_config *cfg);
+dkv_status dkv_q4_0_encode(const dkv_config *cfg, void *q4_cache, const uint16_t *k,
+                           const uint16_t *v, const int32_t *seq_lens, int32_t s_max,
+                           dkv_stream_t stream);
+dkv_status dkv_attn_decode_q4_0(const dkv_config *cfg, const void *q4_cache, const float *q,
+                                const int32_t *seq_lens, float softmax_scale, float *out,
+                                void *workspace, size_t workspace_bytes, dkv_stream_t stream);
+/* Canonical export of the Q4_0 cache: codes uint8 [batch][Hkv][2][s_max][D/2],
+ * scales uint16 [batch][Hkv][2][s_max][D/32]. */
+dkv_status dkv_q4_0_export(const dkv_config *cfg, const void *q4_cache, const int32_t *seq_lens,
+                           int32_t s_max, uint8_t *codes, uint16_t *scales, dkv_stream_t stream);
+
+/*
+ * In-run comparison: F16 cache (the unquantised baseline of the same section).
+ *  k, v (device) fp16 [batch][n_kv_heads][s_max][head_dim]; kf and paging ignored.
+ */
+dkv_status dkv_attn_decode_f16(const dkv_config *cfg, const uint16_t *k, const uint16_t *v,
+                               int32_t s_max, const float *q, const int32_t *seq_lens,
+                               float softmax_scale, float *out, void *workspace,
+                               size_t workspace_bytes, dkv_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DKV_H */

@@ -1,0 +1,319 @@
+// C entry points of libdkv.so: argument validation, size queries, split
+// planning and kernel dispatch.  Every check runs on the host before any
+// launch; nothing here allocates device memory.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+
+#include "dkv.h"
+#include "dkv_common.h"
+
+namespace dkv {
+hipError_t launch_encode_prefill(const dkv_config &, void *, float *, const int32_t *, const uint16_t *,
+                                 const uint16_t *, const int32_t *, int, hipStream_t);
+hipError_t launch_append(const dkv_config &, void *, float *, const int32_t *, const uint16_t *,
+                         const uint16_t *, const int32_t *, hipStream_t);
+hipError_t launch_reconstruct(const dkv_config &, const void *, const int32_t *, const int32_t *, int,
+                              float *, float *, hipStream_t);
+hipError_t launch_export(const dkv_config &, const void *, const int32_t *, const int32_t *, int,
+                         uint16_t *, uint8_t *, uint16_t *, hipStream_t);
+hipError_t launch_attn_ref(const dkv_config &, const void *, const int32_t *, const float *,
+                           const int32_t *, float, float *, int, int, hipStream_t);
+hipError_t launch_combine(const dkv_config &, const float *, int, float *, hipStream_t);
+hipError_t launch_attn_fused(const dkv_config &, const void *, const int32_t *, const float *,
+                             const int32_t *, float, float *, int, int, hipStream_t);
+bool fused_supported(const dkv_config &);
+hipError_t launch_q40_encode(const dkv_config &, void *, const uint16_t *, const uint16_t *,
+                             const int32_t *, int, hipStream_t);
+hipError_t launch_q40_export(const dkv_config &, const void *, const int32_t *, int, uint8_t *,
+                             uint16_t *, hipStream_t);
+hipError_t launch_attn_q40(const dkv_config &, const void *, const float *, const int32_t *, float,
+                           float *, int, int, hipStream_t);
+hipError_t launch_attn_f16(const dkv_config &, const uint16_t *, const uint16_t *, int, const float *,
+                           const int32_t *, float, float *, int, int, hipStream_t);
+
+// Split plan: runs of whole units (groups, or 32-token tiles) per workgroup,
+// sized for about 2048 workgroups over the batch.
+struct Plan {
+    int nsplit, chunk;
+};
+static Plan make_plan(int units_cap, int B, int Hkv)
+{
+    Plan p;
+    const int64_t pairs = (int64_t)B * Hkv;
+    int64_t ns = (2048 + pairs - 1) / pairs;
+    if (ns < 1) ns = 1;
+    if (ns > units_cap) ns = units_cap;
+    if (ns < 1) ns = 1;
+    p.chunk = (int)((units_cap + ns - 1) / ns);
+    if (p.chunk < 1) p.chunk = 1;
+    p.nsplit = (units_cap + p.chunk - 1) / p.chunk;
+    if (p.nsplit < 1) p.nsplit = 1;
+    return p;
+}
+Plan delta_plan(const dkv_config &c)
+{
+    const Geom g = make_geom(c);
+    return make_plan(g.ng_cap, c.batch, c.n_kv_heads);
+}
+Plan tile_plan(const dkv_config &c)
+{
+    const int tiles = (c.max_tokens + 31) / 32;
+    return make_plan(tiles, c.batch, c.n_kv_heads);
+}
+static size_t ws_for(const dkv_config &c, const Plan &p)
+{
+    return (size_t)c.batch * c.n_q_heads * p.nsplit * (c.head_dim + 2) * sizeof(float);
+}
+
+static dkv_status hip_status(hipError_t e) { return e == hipSuccess ? DKV_OK : DKV_ERR_HIP; }
+
+static float resolve_scale(const dkv_config &c, float s)
+{
+    const float sc = (s == 0.0f) ? 1.0f / std::sqrt((float)c.head_dim) : s;
+    return sc * 1.4426950408889634f;     // logits kept in log2 units
+}
+
+}  // namespace dkv
+
+using namespace dkv;
+
+extern "C" {
+
+const char *dkv_status_str(dkv_status s)
+{
+    switch (s) {
+    case DKV_OK: return "ok";
+    case DKV_ERR_ARG: return "invalid argument";
+    case DKV_ERR_UNSUPPORTED: return "unsupported configuration";
+    case DKV_ERR_WORKSPACE: return "workspace missing or too small";
+    case DKV_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+dkv_status dkv_check_config(const dkv_config *c)
+{
+    if (!c) return DKV_ERR_ARG;
+    if (c->batch < 1 || c->n_kv_heads < 1 || c->n_q_heads < 1) return DKV_ERR_ARG;
+    if (c->n_q_heads % c->n_kv_heads != 0) return DKV_ERR_ARG;
+    if (c->head_dim <= 0 || c->head_dim % 32 != 0) return DKV_ERR_ARG;
+    if (c->kf < 1) return DKV_ERR_ARG;
+    if (c->page_tokens < 0) return DKV_ERR_ARG;
+    if (c->page_tokens == 0) {
+        if (c->max_tokens < 1) return DKV_ERR_ARG;
+    } else {
+        if (c->page_tokens % c->kf != 0) return DKV_ERR_ARG;
+        if (c->n_pages < 1 || c->max_pages_per_seq < 1) return DKV_ERR_ARG;
+        if ((int64_t)c->max_pages_per_seq * c->page_tokens > INT_MAX / 2) return DKV_ERR_ARG;
+    }
+    if (c->head_dim != 64 && c->head_dim != 128) return DKV_ERR_UNSUPPORTED;
+    if (c->kf > kMaxKf) return DKV_ERR_UNSUPPORTED;
+    if (c->n_q_heads / c->n_kv_heads > 16) return DKV_ERR_UNSUPPORTED;
+    return DKV_OK;
+}
+
+size_t dkv_group_record_bytes(const dkv_config *c)
+{
+    if (dkv_check_config(c) != DKV_OK) return 0;
+    return (size_t)make_geom(*c).rec;
+}
+
+size_t dkv_cache_bytes(const dkv_config *c)
+{
+    if (dkv_check_config(c) != DKV_OK) return 0;
+    const Geom g = make_geom(*c);
+    if (g.paged) return (size_t)c->n_pages * (size_t)g.page_bytes;
+    return (size_t)c->batch * (size_t)g.page_bytes;
+}
+
+size_t dkv_state_bytes(const dkv_config *c)
+{
+    if (dkv_check_config(c) != DKV_OK) return 0;
+    return (size_t)c->batch * c->n_kv_heads * 2 * c->head_dim * sizeof(float);
+}
+
+size_t dkv_workspace_bytes(const dkv_config *c)
+{
+    if (dkv_check_config(c) != DKV_OK) return 0;
+    size_t a = ws_for(*c, delta_plan(*c));
+    size_t b = c->page_tokens == 0 ? ws_for(*c, tile_plan(*c)) : 0;
+    return a > b ? a : b;
+}
+
+dkv_status dkv_encode_prefill(const dkv_config *c, void *cache, float *state, const int32_t *bt,
+                              const uint16_t *k, const uint16_t *v, const int32_t *lens, int32_t s_max,
+                              dkv_stream_t stream)
+{
+    dkv_status st = dkv_check_config(c);
+    if (st != DKV_OK) return st;
+    if (!cache || !state || !k || !v || !lens || s_max < 0) return DKV_ERR_ARG;
+    if (c->page_tokens > 0 && !bt) return DKV_ERR_ARG;
+    if (s_max == 0) return DKV_OK;
+    return hip_status(launch_encode_prefill(*c, cache, state, c->page_tokens > 0 ? bt : nullptr, k, v, lens,
+                                            s_max, (hipStream_t)stream));
+}
+
+dkv_status dkv_append(const dkv_config *c, void *cache, float *state, const int32_t *bt,
+                      const uint16_t *k, const uint16_t *v, const int32_t *pos, dkv_stream_t stream)
+{
+    dkv_status st = dkv_check_config(c);
+    if (st != DKV_OK) return st;
+    if (!cache || !state || !k || !v || !pos) return DKV_ERR_ARG;
+    if (c->page_tokens > 0 && !bt) return DKV_ERR_ARG;
+    return hip_status(launch_append(*c, cache, state, c->page_tokens > 0 ? bt : nullptr, k, v, pos,
+                                    (hipStream_t)stream));
+}
+
+static dkv_status attn_common(const dkv_config *c, const void *cache, const int32_t *bt, const float *q,
+                              const int32_t *lens, float *out, void *ws, size_t ws_bytes)
+{
+    dkv_status st = dkv_check_config(c);
+    if (st != DKV_OK) return st;
+    if (!cache || !q || !lens || !out) return DKV_ERR_ARG;
+    if (c->page_tokens > 0 && !bt) return DKV_ERR_ARG;
+    if (!ws || ws_bytes < ws_for(*c, delta_plan(*c))) return DKV_ERR_WORKSPACE;
+    return DKV_OK;
+}
+
+dkv_status dkv_attn_decode(const dkv_config *c, const void *cache, const int32_t *bt, const float *q,
+                           const int32_t *lens, float scale, float *out, void *ws, size_t ws_bytes,
+                           dkv_stream_t stream)
+{
+    dkv_status st = attn_common(c, cache, bt, q, lens, out, ws, ws_bytes);
+    if (st != DKV_OK) return st;
+    const Plan p = delta_plan(*c);
+    const int32_t *btp = c->page_tokens > 0 ? bt : nullptr;
+    hipError_t e;
+    if (fused_supported(*c))
+        e = launch_attn_fused(*c, cache, btp, q, lens, resolve_scale(*c, scale), (float *)ws, p.nsplit,
+                              p.chunk, (hipStream_t)stream);
+    else
+        e = launch_attn_ref(*c, cache, btp, q, lens, resolve_scale(*c, scale), (float *)ws, p.nsplit,
+                            p.chunk, (hipStream_t)stream);
+    if (e != hipSuccess) return DKV_ERR_HIP;
+    return hip_status(launch_combine(*c, (const float *)ws, p.nsplit, out, (hipStream_t)stream));
+}
+
+dkv_status dkv_attn_decode_partial(const dkv_config *c, const void *cache, const int32_t *bt, const float *q,
+                                   const int32_t *lens, float scale, void *ws, size_t ws_bytes,
+                                   dkv_stream_t stream)
+{
+    dkv_status st = attn_common(c, cache, bt, q, lens, (float *)ws, ws, ws_bytes);
+    if (st != DKV_OK) return st;
+    const Plan p = delta_plan(*c);
+    const int32_t *btp = c->page_tokens > 0 ? bt : nullptr;
+    if (fused_supported(*c))
+        return hip_status(launch_attn_fused(*c, cache, btp, q, lens, resolve_scale(*c, scale), (float *)ws,
+                                            p.nsplit, p.chunk, (hipStream_t)stream));
+    return hip_status(launch_attn_ref(*c, cache, btp, q, lens, resolve_scale(*c, scale), (float *)ws, p.nsplit,
+                                      p.chunk, (hipStream_t)stream));
+}
+
+dkv_status dkv_attn_decode_ref(const dkv_config *c, const void *cache, const int32_t *bt, const float *q,
+                               const int32_t *lens, float scale, float *out, void *ws, size_t ws_bytes,
+                               dkv_stream_t stream)
+{
+    dkv_status st = attn_common(c, cache, bt, q, lens, out, ws, ws_bytes);
+    if (st != DKV_OK) return st;
+    const Plan p = delta_plan(*c);
+    hipError_t e = launch_attn_ref(*c, cache, c->page_tokens > 0 ? bt : nullptr, q, lens,
+                                   resolve_scale(*c, scale), (float *)ws, p.nsplit, p.chunk,
+                                   (hipStream_t)stream);
+    if (e != hipSuccess) return DKV_ERR_HIP;
+    return hip_status(launch_combine(*c, (const float *)ws, p.nsplit, out, (hipStream_t)stream));
+}
+
+dkv_status dkv_reconstruct(const dkv_config *c, const void *cache, const int32_t *bt, const int32_t *lens,
+                           int32_t s_max, float *ko, float *vo, dkv_stream_t stream)
+{
+    dkv_status st = dkv_check_config(c);
+    if (st != DKV_OK) return st;
+    if (!cache || !lens || !ko || !vo || s_max < 0) return DKV_ERR_ARG;
+    if (c->page_tokens > 0 && !bt) return DKV_ERR_ARG;
+    if (s_max == 0) return DKV_OK;
+    return hip_status(launch_reconstruct(*c, cache, c->page_tokens > 0 ? bt : nullptr, lens, s_max, ko, vo,
+                                         (hipStream_t)stream));
+}
+
+dkv_status dkv_export(const dkv_config *c, const void *cache, const int32_t *bt, const int32_t *lens,
+                      int32_t s_max, uint16_t *kf_rows, uint8_t *codes, uint16_t *scales,
+                      dkv_stream_t stream)
+{
+    dkv_status st = dkv_check_config(c);
+    if (st != DKV_OK) return st;
+    if (!cache || !lens || !kf_rows || s_max < 0) return DKV_ERR_ARG;
+    const int64_t nd = (int64_t)s_max - (s_max + c->kf - 1) / c->kf;   // delta rows (0 when kf == 1)
+    if (nd > 0 && (!codes || !scales)) return DKV_ERR_ARG;
+    if (c->page_tokens > 0 && !bt) return DKV_ERR_ARG;
+    if (s_max == 0) return DKV_OK;
+    return hip_status(launch_export(*c, cache, c->page_tokens > 0 ? bt : nullptr, lens, s_max, kf_rows,
+                                    codes, scales, (hipStream_t)stream));
+}
+
+size_t dkv_q4_0_cache_bytes(const dkv_config *c)
+{
+    if (dkv_check_config(c) != DKV_OK || c->page_tokens != 0) return 0;
+    const int64_t tiles = (c->max_tokens + 31) / 32;
+    return (size_t)c->batch * c->n_kv_heads * tiles * 2 * (16 * c->head_dim + 64 * (c->head_dim / 32));
+}
+
+static dkv_status q40_common(const dkv_config *c)
+{
+    dkv_status st = dkv_check_config(c);
+    if (st != DKV_OK) return st;
+    if (c->page_tokens != 0) return DKV_ERR_UNSUPPORTED;
+    return DKV_OK;
+}
+
+dkv_status dkv_q4_0_encode(const dkv_config *c, void *q4, const uint16_t *k, const uint16_t *v,
+                           const int32_t *lens, int32_t s_max, dkv_stream_t stream)
+{
+    dkv_status st = q40_common(c);
+    if (st != DKV_OK) return st;
+    if (!q4 || !k || !v || !lens || s_max < 0) return DKV_ERR_ARG;
+    if (s_max == 0) return DKV_OK;
+    return hip_status(launch_q40_encode(*c, q4, k, v, lens, s_max, (hipStream_t)stream));
+}
+
+dkv_status dkv_q4_0_export(const dkv_config *c, const void *q4, const int32_t *lens, int32_t s_max,
+                           uint8_t *codes, uint16_t *scales, dkv_stream_t stream)
+{
+    dkv_status st = q40_common(c);
+    if (st != DKV_OK) return st;
+    if (!q4 || !lens || !codes || !scales || s_max < 0) return DKV_ERR_ARG;
+    if (s_max == 0) return DKV_OK;
+    return hip_status(launch_q40_export(*c, q4, lens, s_max, codes, scales, (hipStream_t)stream));
+}
+
+dkv_status dkv_attn_decode_q4_0(const dkv_config *c, const void *q4, const float *q, const int32_t *lens,
+                                float scale, float *out, void *ws, size_t ws_bytes, dkv_stream_t stream)
+{
+    dkv_status st = q40_common(c);
+    if (st != DKV_OK) return st;
+    if (!q4 || !q || !lens || !out) return DKV_ERR_ARG;
+    const Plan p = tile_plan(*c);
+    if (!ws || ws_bytes < ws_for(*c, p)) return DKV_ERR_WORKSPACE;
+    hipError_t e = launch_attn_q40(*c, q4, q, lens, resolve_scale(*c, scale), (float *)ws, p.nsplit, p.chunk,
+                                   (hipStream_t)stream);
+    if (e != hipSuccess) return DKV_ERR_HIP;
+    return hip_status(launch_combine(*c, (const float *)ws, p.nsplit, out, (hipStream_t)stream));
+}
+
+dkv_status dkv_attn_decode_f16(const dkv_config *c, const uint16_t *k, const uint16_t *v, int32_t s_max,
+                               const float *q, const int32_t *lens, float scale, float *out, void *ws,
+                               size_t ws_bytes, dkv_stream_t stream)
+{
+    dkv_status st = q40_common(c);
+    if (st != DKV_OK) return st;
+    if (!k || !v || !q || !lens || !out || s_max < 1 || s_max > c->max_tokens) return DKV_ERR_ARG;
+    const Plan p = tile_plan(*c);
+    if (!ws || ws_bytes < ws_for(*c, p)) return DKV_ERR_WORKSPACE;
+    hipError_t e = launch_attn_f16(*c, k, v, s_max, q, lens, resolve_scale(*c, scale), (float *)ws, p.nsplit,
+                                   p.chunk, (hipStream_t)stream);
+    if (e != hipSuccess) return DKV_ERR_HIP;
+    return hip_status(launch_combine(*c, (const float *)ws, p.nsplit, out, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,141 @@
+// Shared definitions of the Delta-KV HIP library: cache geometry, the
+// channel permutations of the group record, and small device helpers.
+//
+// Geometry of one group record (K part, then V part; every piece 16-byte
+// aligned).  nb = D/32 Q4_0 blocks per row.
+//   keyframe   2*D bytes          fp16, permuted (see kf_k_channel / kf_v_channel)
+//   scales     pad16(kf*nb*2)     fp16 [kf][nb]; slot 0 = per-block max |scale|
+//   codes (K)  pad16((kf-1)*D/2)  one row per delta token; the 16 canonical
+//                                 Q4_0 bytes of block b are split in four
+//                                 32-bit pieces, piece j at word j*nb + b
+//   codes (V)  ntiles*16*D        32-token tiles; word ((j*16+m)*(D/16)+cc)
+//                                 holds channel 16*cc+m for the 8 token slots
+//                                 16*e+4*j+r (r<4, e<2) at nibble r+4*e
+// The permutations line the data up with the operand layout of the gfx950
+// 16x16x32 fp16 matrix instruction (lane = 16*j + m, eight K values per lane).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dkv.h"
+
+namespace dkv {
+
+constexpr int kMaxKf = 1024;
+constexpr int kWave = 64;
+
+__host__ __device__ inline int64_t pad16(int64_t x) { return (x + 15) & ~int64_t(15); }
+
+struct Geom {
+    int D, nb, kf, Hkv, Hq, G, B;
+    int ntiles_v;              // 32-token tiles of V codes per group
+    int64_t off_ksc, off_kcd, off_vkf, off_vsc, off_vcd, rec;
+    // addressing
+    int paged;                 // 1 if paged
+    int gpp;                   // groups per page (paged) or per sequence (contiguous)
+    int64_t page_bytes;        // bytes of a page (paged) or of one sequence (contiguous)
+    int max_pages;             // block-table row length (paged)
+    int n_pages;               // physical pages (paged)
+    int ng_cap;                // group capacity per sequence
+    int cap_tokens;            // token capacity per sequence
+};
+
+__host__ __device__ inline Geom make_geom(const dkv_config &c)
+{
+    Geom g{};
+    g.D = c.head_dim;
+    g.nb = c.head_dim / 32;
+    g.kf = c.kf;
+    g.Hkv = c.n_kv_heads;
+    g.Hq = c.n_q_heads;
+    g.G = c.n_q_heads / c.n_kv_heads;
+    g.B = c.batch;
+    g.ntiles_v = c.kf > 1 ? (c.kf + 31) / 32 : 0;
+    int64_t kfb = 2 * (int64_t)g.D;
+    int64_t scb = pad16((int64_t)c.kf * g.nb * 2);
+    int64_t kcb = pad16((int64_t)(c.kf - 1) * g.D / 2);
+    g.off_ksc = kfb;
+    g.off_kcd = g.off_ksc + scb;
+    g.off_vkf = g.off_kcd + kcb;
+    g.off_vsc = g.off_vkf + kfb;
+    g.off_vcd = g.off_vsc + scb;
+    g.rec = g.off_vcd + (int64_t)g.ntiles_v * 16 * g.D;
+    g.paged = c.page_tokens > 0;
+    if (g.paged) {
+        g.gpp = c.page_tokens / c.kf;
+        g.page_bytes = (int64_t)g.Hkv * g.gpp * g.rec;
+        g.max_pages = c.max_pages_per_seq;
+        g.n_pages = c.n_pages;
+        g.cap_tokens = c.max_pages_per_seq * c.page_tokens;
+        g.ng_cap = g.cap_tokens / c.kf;
+    } else {
+        g.ng_cap = (c.max_tokens + c.kf - 1) / c.kf;
+        g.gpp = g.ng_cap;
+        g.page_bytes = (int64_t)g.Hkv * g.ng_cap * g.rec;
+        g.max_pages = 1;
+        g.n_pages = c.batch;
+        g.cap_tokens = g.ng_cap * c.kf;
+    }
+    return g;
+}
+
+// Byte offset of the group record of (sequence b, kv-head h, group gi).
+// Returns -1 for an unmapped (or out-of-range) page in paged mode.
+__host__ __device__ inline int64_t group_offset(const Geom &g, const int32_t *block_table,
+                                                int b, int h, int gi)
+{
+    if (g.paged) {
+        int lp = gi / g.gpp;
+        int phys = block_table[(int64_t)b * g.max_pages + lp];
+        if (phys < 0 || phys >= g.n_pages) return -1;
+        return (int64_t)phys * g.page_bytes + ((int64_t)h * g.gpp + gi % g.gpp) * g.rec;
+    }
+    return (int64_t)b * g.page_bytes + ((int64_t)h * g.gpp + gi) * g.rec;
+}
+
+// ---- channel permutations -------------------------------------------------
+// Within a 32-bit code piece (canonical bytes 4j..4j+3 of a block), nibble p
+// is byte p/2, low (p even) or high (p odd) half, i.e. block channel
+// 4j + p/2 + 16*(p&1).  The matrix-core unpack places nibble r+4e in half
+// 2r+e of the eight K values.  kf_k_channel gives the block channel held in
+// half h of lane group j.
+__host__ __device__ inline int half_to_nibble(int h) { return (h >> 1) + 4 * (h & 1); }
+__host__ __device__ inline int nibble_channel(int j, int p) { return 4 * j + (p >> 1) + 16 * (p & 1); }
+__host__ __device__ inline int kf_k_channel(int j, int h) { return nibble_channel(j, half_to_nibble(h)); }
+
+// K keyframe: element (j*nb + b)*8 + h holds channel 32*b + kf_k_channel(j, h).
+__host__ __device__ inline int kkf_pos(int nb, int c)
+{
+    int b = c >> 5, cb = c & 31;
+    int hi = cb >> 4, rem = cb & 15;           // cb = 4j + k + 16*hi
+    int j = rem >> 2, k = rem & 3;
+    int p = 2 * k + hi;                        // nibble position
+    int h = 2 * (p & 3) + (p >> 2);            // inverse of half_to_nibble
+    return (j * nb + b) * 8 + h;
+}
+// V keyframe: element (j*(D/16) + cc)*4 + r holds channel 16*cc + 4*j + r.
+__host__ __device__ inline int vkf_pos(int D, int c)
+{
+    int cc = c >> 4, m = c & 15;
+    int j = m >> 2, r = m & 3;
+    return (j * (D / 16) + cc) * 4 + r;
+}
+// K code row: byte offset of canonical byte i (0..15) of block b.
+__host__ __device__ inline int kcode_byte(int nb, int b, int i) { return 4 * ((i >> 2) * nb + b) + (i & 3); }
+// V code tile: word index and nibble of (token slot tau in 0..31, channel c).
+__host__ __device__ inline int vcode_word(int D, int tau, int c)
+{
+    int j = (tau & 15) >> 2;
+    int m = c & 15, cc = c >> 4;
+    return (j * 16 + m) * (D / 16) + cc;
+}
+__host__ __device__ inline int vcode_nibble(int tau) { return (tau & 3) + 4 * (tau >> 4); }
+
+// ---- small device helpers --------------------------------------------------
+// fp16 <-> fp32 through the compiler's _Float16 (v_cvt_f32_f16 / v_cvt_f16_f32,
+// round to nearest even, subnormals kept).
+__device__ inline float h2f(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+__device__ inline uint16_t f2h_rn(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+
+}  // namespace dkv

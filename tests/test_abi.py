@@ -1,0 +1,112 @@
+"""CPU checks of the C ABI: the library loads, exports every entry point the
+header declares, and rejects bad arguments on the host before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantized_decode_attention_delta_amd as dkv
+from quantized_decode_attention_delta_amd import dkv as binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dkv.h")
+
+
+def _lib():
+    if not os.path.exists(binding.LIB_PATH):
+        from quantized_decode_attention_delta_amd import build
+        build.build()
+    return dkv.load()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dkv_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    lib = _lib()
+    names = header_functions()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(binding._SIGS), set(names) ^ set(binding._SIGS)
+
+
+def _cfg(**kw):
+    base = dict(batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, kf=32, max_tokens=1000)
+    base.update(kw)
+    return dkv.Config(**base)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(), binding.DKV_OK),
+    (dict(batch=0), binding.DKV_ERR_ARG),
+    (dict(n_q_heads=7), binding.DKV_ERR_ARG),
+    (dict(head_dim=48), binding.DKV_ERR_ARG),
+    (dict(head_dim=96), binding.DKV_ERR_UNSUPPORTED),
+    (dict(head_dim=256), binding.DKV_ERR_UNSUPPORTED),
+    (dict(kf=0), binding.DKV_ERR_ARG),
+    (dict(kf=2048), binding.DKV_ERR_UNSUPPORTED),
+    (dict(max_tokens=0), binding.DKV_ERR_ARG),
+    (dict(page_tokens=256, kf=512, n_pages=4, max_pages_per_seq=2), binding.DKV_ERR_ARG),
+    (dict(page_tokens=256, n_pages=0, max_pages_per_seq=2), binding.DKV_ERR_ARG),
+    (dict(page_tokens=256, n_pages=4, max_pages_per_seq=2), binding.DKV_OK),
+    (dict(n_q_heads=64, n_kv_heads=2), binding.DKV_ERR_UNSUPPORTED),
+])
+def test_check_config(kw, want):
+    _lib()
+    assert dkv.dkv_check_config(_cfg(**kw)) == want
+
+
+def test_sizes():
+    _lib()
+    c = _cfg(batch=16, n_q_heads=64, n_kv_heads=8, max_tokens=32768)
+    rec = dkv.dkv_group_record_bytes(c)
+    # two streams of 2,488 algorithmic bytes per 32-token group, plus 64 bytes of
+    # V code padding (the keyframe slot) and 8+8 bytes of scale slot 0
+    assert rec == 2 * 2488 + 64 + 16
+    assert dkv.dkv_cache_bytes(c) == 16 * 8 * 1024 * rec
+    assert dkv.dkv_state_bytes(c) == 16 * 8 * 2 * 128 * 4
+    assert dkv.dkv_workspace_bytes(c) > 0
+    assert dkv.dkv_q4_0_cache_bytes(c) == 16 * 8 * 2 * 32768 * 128 // 32 * 18
+    assert dkv.dkv_cache_bytes(_cfg(head_dim=96)) == 0
+
+
+def test_argument_errors_return_before_launch():
+    lib = _lib()
+    c = _cfg()
+    cp = ctypes.byref(c.c())
+    fake = ctypes.c_void_p(0x1000)
+    null = None
+    # null pointers
+    assert lib.dkv_encode_prefill(cp, null, fake, null, fake, fake, fake, 10, null) == binding.DKV_ERR_ARG
+    assert lib.dkv_append(cp, fake, fake, null, fake, null, fake, null) == binding.DKV_ERR_ARG
+    assert lib.dkv_attn_decode(cp, fake, null, null, fake, 0.0, fake, fake, 1 << 30, null) == binding.DKV_ERR_ARG
+    # missing / short workspace
+    assert lib.dkv_attn_decode(cp, fake, null, fake, fake, 0.0, fake, null, 0, null) == binding.DKV_ERR_WORKSPACE
+    assert lib.dkv_attn_decode(cp, fake, null, fake, fake, 0.0, fake, fake, 16, null) == binding.DKV_ERR_WORKSPACE
+    assert lib.dkv_attn_decode_ref(cp, fake, null, fake, fake, 0.0, fake, fake, 16, null) == binding.DKV_ERR_WORKSPACE
+    # paged mode needs a block table
+    cpg = ctypes.byref(_cfg(page_tokens=256, n_pages=8, max_pages_per_seq=4).c())
+    assert lib.dkv_encode_prefill(cpg, fake, fake, null, fake, fake, fake, 10, null) == binding.DKV_ERR_ARG
+    # unsupported config propagates
+    cbad = ctypes.byref(_cfg(head_dim=96).c())
+    assert lib.dkv_append(cbad, fake, fake, null, fake, fake, fake, null) == binding.DKV_ERR_UNSUPPORTED
+    # Q4_0 comparison is contiguous only
+    assert lib.dkv_q4_0_encode(cpg, fake, fake, fake, fake, 10, null) == binding.DKV_ERR_UNSUPPORTED
+    # F16 comparison: s_max beyond capacity
+    assert lib.dkv_attn_decode_f16(cp, fake, fake, 5000, fake, fake, 0.0, fake, fake, 1 << 30, null) == binding.DKV_ERR_ARG
+    assert lib.dkv_check_config(None) == binding.DKV_ERR_ARG
+    assert dkv.status_str(binding.DKV_ERR_WORKSPACE) == "workspace missing or too small"
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    _lib()
+    c = _cfg()
+    t = torch.zeros(10)
+    with pytest.raises((ValueError, TypeError)):
+        dkv.dkv_encode_prefill(c, t, t, None, t, t, t, 10)

@@ -1,0 +1,155 @@
+"""GPU parity of the Delta-KV path against the CPU oracle, through the C ABI.
+
+Codec results (keyframes, Q4_0 codes, fp16 scale bit patterns, reconstructed
+K/V, recon state) must be bit-exact; decode attention must be within 2e-3 max
+relative error per output row of the float64 oracle.  Sizes span several
+groups and tiles with ragged tails; every workload recipe is covered.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_decode_attention_delta_amd as dkv
+from quantized_decode_attention_delta_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+import gpu_util as U  # noqa: E402
+
+
+def _case(name, **kw):
+    return synth.make(name, **kw)
+
+
+CODEC_CASES = [
+    ("tiny", dict(), 32, 0),
+    ("8b", dict(S=700, Hq=8, Hkv=2), 32, 0),
+    ("8b", dict(S=700, Hq=8, Hkv=2, D=64), 32, 0),
+    ("long", dict(S=1500, B=2, Hq=8, Hkv=2, kf=128), 128, 0),
+    ("long", dict(S=1300, B=2, Hq=8, Hkv=2, kf=512), 512, 0),
+    ("70b", dict(S=999, B=3, Hq=16, Hkv=2), 32, 0),
+    ("mixed", dict(S=1400, B=4, Hq=8, Hkv=2, min_len=100, extra_tokens=0), 32, 256),
+    ("8b", dict(S=100, Hq=4, Hkv=1), 1, 0),
+    ("8b", dict(S=97, Hq=4, Hkv=1), 7, 0),
+]
+
+
+@pytest.mark.parametrize("name,kw,kf,page", CODEC_CASES, ids=lambda x: str(x))
+def test_prefill_codec_bit_exact(name, kw, kf, page):
+    w = _case(name, **kw)
+    r = U.prefill(w, kf=kf, page_tokens=page)
+    enc = U.oracle_encode(w, kf, r.lens_np)
+    U.assert_codec_exact(r, enc, kf)
+
+
+@pytest.mark.parametrize("name,kw,kf,page", CODEC_CASES, ids=lambda x: str(x))
+@pytest.mark.parametrize("fn", ["dkv_attn_decode", "dkv_attn_decode_ref"])
+def test_attention_parity(name, kw, kf, page, fn):
+    w = _case(name, **kw)
+    r = U.prefill(w, kf=kf, page_tokens=page)
+    enc = U.oracle_encode(w, kf, r.lens_np)
+    q = synth.queries(w)
+    got = U.attention(r, q, fn)
+    ref = U.oracle_attention(enc, w, q, r.lens_np)
+    err = U.rel_err(got, ref)
+    assert err <= U.ATTN_TOL, err
+
+
+def test_ragged_and_empty_sequences():
+    w = _case("8b", S=300, B=5, Hq=8, Hkv=2)
+    lens = np.array([0, 1, 31, 33, 300], np.int32)
+    r = U.prefill(w, lens=lens)
+    enc = U.oracle_encode(w, w.kf, lens)
+    U.assert_codec_exact(r, enc, w.kf)
+    q = synth.queries(w)
+    for fn in ("dkv_attn_decode", "dkv_attn_decode_ref"):
+        got = U.attention(r, q, fn)
+        assert np.all(got[0] == 0.0)                      # empty sequence: zero rows
+        ref = U.oracle_attention(enc, w, q, lens)
+        ref[0] = 0.0
+        assert U.rel_err(got, ref) <= U.ATTN_TOL
+
+
+def test_appends_equal_prefill_and_oracle():
+    """Prefill part of each sequence, append the rest token by token: the cache
+    and state match a single prefill and the oracle bit for bit."""
+    w = _case("8b", S=200, B=3, Hq=8, Hkv=2)
+    kf = 32
+    full = U.prefill(w, kf=kf)
+    start = np.array([0, 37, 64], np.int32)
+    r = U.prefill(w, kf=kf, lens=start)
+    k, v = full.k, full.v
+    pos = torch.from_numpy(start.copy()).to(U.DEV)
+    for t in range(int(start.min()), w.S):
+        p = np.where(t >= start, t, -1).astype(np.int32)
+        pos.copy_(torch.from_numpy(p))
+        kn = k[:, :, min(t, w.S - 1)].contiguous()
+        vn = v[:, :, min(t, w.S - 1)].contiguous()
+        dkv.dkv_append(r.cfg, r.cache, r.state, None, kn, vn, pos)
+    r.lens = full.lens
+    r.lens_np = full.lens_np
+    enc = U.oracle_encode(w, kf, full.lens_np)
+    U.assert_codec_exact(r, enc, kf)
+    assert torch.equal(r.state, full.state)
+
+
+def test_append_paged_matches_oracle():
+    w = _case("mixed", S=600, B=4, Hq=8, Hkv=2, min_len=64, extra_tokens=40)
+    r = U.prefill(w, page_tokens=256)
+    lens = r.lens_np.copy()
+    for step in range(40):
+        pos = torch.from_numpy(lens.astype(np.int32)).to(U.DEV)
+        kn = torch.stack([r.k[b, :, int(lens[b])] for b in range(w.B)]).contiguous()
+        vn = torch.stack([r.v[b, :, int(lens[b])] for b in range(w.B)]).contiguous()
+        dkv.dkv_append(r.cfg, r.cache, r.state, r.bt, kn, vn, pos)
+        lens += 1
+    r.lens_np = lens.astype(np.int32)
+    r.lens = torch.from_numpy(r.lens_np).to(U.DEV)
+    enc = U.oracle_encode(w, w.kf, r.lens_np)
+    U.assert_codec_exact(r, enc, w.kf)
+    q = synth.queries(w, step=3)
+    got = U.attention(r, q)
+    ref = U.oracle_attention(enc, w, q, r.lens_np)
+    assert U.rel_err(got, ref) <= U.ATTN_TOL
+
+
+def test_resume_through_host_copy():
+    """Cache + state copied to the host and back continue bit-exactly."""
+    w = _case("8b", S=160, B=2, Hq=8, Hkv=2)
+    a = U.prefill(w, lens=np.array([100, 120], np.int32))
+    cache_h, state_h = a.cache.cpu(), a.state.cpu()
+    b_cache, b_state = cache_h.to(U.DEV), state_h.to(U.DEV)
+    for t in range(100, 160):
+        p = torch.tensor([t, t if t >= 120 else -1], dtype=torch.int32, device=U.DEV)
+        kn = a.k[:, :, t].contiguous()
+        vn = a.v[:, :, t].contiguous()
+        dkv.dkv_append(a.cfg, a.cache, a.state, None, kn, vn, p)
+        dkv.dkv_append(a.cfg, b_cache, b_state, None, kn, vn, p)
+    assert torch.equal(a.cache, b_cache) and torch.equal(a.state, b_state)
+
+
+def test_attention_repeatable():
+    w = _case("70b", S=700, B=2, Hq=16, Hkv=2)
+    r = U.prefill(w)
+    q = synth.queries(w)
+    a = U.attention(r, q)
+    b = U.attention(r, q)
+    assert np.array_equal(a, b)
+
+
+def test_softmax_scale_argument():
+    w = _case("8b", S=200, Hq=8, Hkv=2)
+    r = U.prefill(w)
+    enc = U.oracle_encode(w, w.kf, r.lens_np)
+    q = synth.queries(w)
+    qd = torch.from_numpy(q).to(U.DEV)
+    out = torch.zeros(w.B, w.Hq, w.D, dtype=torch.float32, device=U.DEV)
+    dkv.dkv_attn_decode(r.cfg, r.cache, None, qd, r.lens, out, r.ws, softmax_scale=0.25)
+    scale = np.float32(0.25)
+    ref = np.zeros((w.B, w.Hq, w.D))
+    G = w.Hq // w.Hkv
+    for h in range(w.Hkv):
+        ref[0, h * G:(h + 1) * G] = oracle.attention_f64(q[0, h * G:(h + 1) * G], enc[(0, h, 0)].recon,
+                                                         enc[(0, h, 1)].recon, scale)
+    assert U.rel_err(out.cpu().numpy(), ref) <= U.ATTN_TOL
