@@ -64,7 +64,7 @@ Plan tile_plan(const dkv_config &c)
 }
 static size_t ws_for(const dkv_config &c, const Plan &p)
 {
-    return (size_t)c.batch * c.n_q_heads * p.nsplit * (c.head_dim + 2) * sizeof(float);
+    return (size_t)c.batch * c.n_q_heads * p.nsplit * part_stride(c.head_dim) * sizeof(float);
 }
 
 static dkv_status hip_status(hipError_t e) { return e == hipSuccess ? DKV_OK : DKV_ERR_HIP; }

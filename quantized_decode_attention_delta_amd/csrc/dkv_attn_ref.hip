@@ -132,11 +132,11 @@ __global__ void __launch_bounds__(kRefThreads)
         const int i = tid + k * kRefThreads;
         if (i < G * D) {
             const int hh = i / D, c = i % D;
-            ws[(((int64_t)b * g.Hq + h * G + hh) * nsplit + split) * (D + 2) + c] = acc[k];
+            ws[(((int64_t)b * g.Hq + h * G + hh) * nsplit + split) * part_stride(D) + c] = acc[k];
         }
     }
     if (tid < G) {
-        float *rec = ws + (((int64_t)b * g.Hq + h * G + tid) * nsplit + split) * (D + 2);
+        float *rec = ws + (((int64_t)b * g.Hq + h * G + tid) * nsplit + split) * part_stride(D);
         rec[D] = sm[tid];
         rec[D + 1] = sls[tid];
     }
@@ -148,19 +148,20 @@ __global__ void __launch_bounds__(D) k_combine(const float *ws, int nsplit, floa
 {
     const int64_t row = blockIdx.x;
     const int c = threadIdx.x;
-    const float *p = ws + row * nsplit * (D + 2);
+    constexpr int R = part_stride(D);
+    const float *p = ws + row * nsplit * R;
     float M = -INFINITY;
     for (int s = 0; s < nsplit; ++s) {
-        const float l = p[s * (D + 2) + D + 1];
-        if (l > 0.0f) M = fmaxf(M, p[s * (D + 2) + D]);
+        const float l = p[s * R + D + 1];
+        if (l > 0.0f) M = fmaxf(M, p[s * R + D]);
     }
     float num = 0.0f, den = 0.0f;
     if (M > -INFINITY) {
         for (int s = 0; s < nsplit; ++s) {
-            const float l = p[s * (D + 2) + D + 1];
+            const float l = p[s * R + D + 1];
             if (l > 0.0f) {
-                const float w = exp2f(p[s * (D + 2) + D] - M);
-                num = fmaf(w, p[s * (D + 2) + c], num);
+                const float w = exp2f(p[s * R + D] - M);
+                num = fmaf(w, p[s * R + c], num);
                 den = fmaf(w, l, den);
             }
         }

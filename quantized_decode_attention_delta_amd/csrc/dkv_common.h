@@ -27,6 +27,10 @@ constexpr int kWave = 64;
 
 __host__ __device__ inline int64_t pad16(int64_t x) { return (x + 15) & ~int64_t(15); }
 
+// Split-K partial record per (sequence, query head, split): acc[D], running
+// max (log2 units), running sum, two pad floats (16-byte aligned records).
+__host__ __device__ constexpr int part_stride(int D) { return D + 4; }
+
 struct Geom {
     int D, nb, kf, Hkv, Hq, G, B;
     int ntiles_v;              // 32-token tiles of V codes per group
