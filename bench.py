@@ -131,7 +131,7 @@ def main():
     torch.cuda.synchronize()
     q = torch.from_numpy(synth.queries(w)).to(dev)
     out = torch.empty(w.B, w.Hq, w.D, dtype=torch.float32, device=dev)
-    ws = torch.empty(dkv.dkv_workspace_bytes(cfg), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(dkv.dkv_workspace_bytes(cfg), dtype=torch.uint8, device=dev)
     step_fn = dkv.dkv_attn_decode if args.kernel == "fused" else dkv.dkv_attn_decode_ref
 
     def step(i):

@@ -135,7 +135,10 @@ dkv_status dkv_append(const dkv_config *cfg, void *cache, float *state,
  *  seq_lens (device) int32 [batch]: tokens attended (0 gives a zero row)
  *  softmax_scale: logit scale; 0 means 1/sqrt(head_dim)
  *  out      (device) fp32 [batch][n_q_heads][head_dim]
- *  workspace (device) at least dkv_workspace_bytes(cfg) bytes
+ *  workspace (device) at least dkv_workspace_bytes(cfg) bytes of scratch for
+ *           the split-K partial results (no initial contents needed; calls
+ *           that share a workspace must not run concurrently)
+ * Two launches on `stream`: the fused split phase, then the split combine.
  */
 dkv_status dkv_attn_decode(const dkv_config *cfg, const void *cache,
                            const int32_t *block_table, const float *q,

@@ -21,6 +21,8 @@ HIPCC_FLAGS = [
     "-ffp-contract=off",
     # packed fp32 ALU ops stay off (v_pk_*_f32)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core accumulators in ordinary VGPRs (no AGPR copies around the VALU epilogues)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wno-unused-command-line-argument",
 ]
 

@@ -66,6 +66,12 @@ static size_t ws_for(const dkv_config &c, const Plan &p)
 {
     return (size_t)c.batch * c.n_q_heads * p.nsplit * part_stride(c.head_dim) * sizeof(float);
 }
+static size_t workspace_total(const dkv_config &c)
+{
+    const size_t a = ws_for(c, delta_plan(c));
+    const size_t b = c.page_tokens == 0 ? ws_for(c, tile_plan(c)) : 0;
+    return a > b ? a : b;
+}
 
 static dkv_status hip_status(hipError_t e) { return e == hipSuccess ? DKV_OK : DKV_ERR_HIP; }
 
@@ -137,9 +143,7 @@ size_t dkv_state_bytes(const dkv_config *c)
 size_t dkv_workspace_bytes(const dkv_config *c)
 {
     if (dkv_check_config(c) != DKV_OK) return 0;
-    size_t a = ws_for(*c, delta_plan(*c));
-    size_t b = c->page_tokens == 0 ? ws_for(*c, tile_plan(*c)) : 0;
-    return a > b ? a : b;
+    return workspace_total(*c);
 }
 
 dkv_status dkv_encode_prefill(const dkv_config *c, void *cache, float *state, const int32_t *bt,
@@ -173,8 +177,18 @@ static dkv_status attn_common(const dkv_config *c, const void *cache, const int3
     if (st != DKV_OK) return st;
     if (!cache || !q || !lens || !out) return DKV_ERR_ARG;
     if (c->page_tokens > 0 && !bt) return DKV_ERR_ARG;
-    if (!ws || ws_bytes < ws_for(*c, delta_plan(*c))) return DKV_ERR_WORKSPACE;
+    if (!ws || ws_bytes < workspace_total(*c)) return DKV_ERR_WORKSPACE;
     return DKV_OK;
+}
+
+static hipError_t launch_split_phase(const dkv_config &c, const void *cache, const int32_t *bt, const float *q,
+                                     const int32_t *lens, float scale, void *ws, const Plan &p, hipStream_t st)
+{
+    const int32_t *btp = c.page_tokens > 0 ? bt : nullptr;
+    if (fused_supported(c))
+        return launch_attn_fused(c, cache, btp, q, lens, resolve_scale(c, scale), (float *)ws, p.nsplit, p.chunk,
+                                 st);
+    return launch_attn_ref(c, cache, btp, q, lens, resolve_scale(c, scale), (float *)ws, p.nsplit, p.chunk, st);
 }
 
 dkv_status dkv_attn_decode(const dkv_config *c, const void *cache, const int32_t *bt, const float *q,
@@ -184,14 +198,7 @@ dkv_status dkv_attn_decode(const dkv_config *c, const void *cache, const int32_t
     dkv_status st = attn_common(c, cache, bt, q, lens, out, ws, ws_bytes);
     if (st != DKV_OK) return st;
     const Plan p = delta_plan(*c);
-    const int32_t *btp = c->page_tokens > 0 ? bt : nullptr;
-    hipError_t e;
-    if (fused_supported(*c))
-        e = launch_attn_fused(*c, cache, btp, q, lens, resolve_scale(*c, scale), (float *)ws, p.nsplit,
-                              p.chunk, (hipStream_t)stream);
-    else
-        e = launch_attn_ref(*c, cache, btp, q, lens, resolve_scale(*c, scale), (float *)ws, p.nsplit,
-                            p.chunk, (hipStream_t)stream);
+    hipError_t e = launch_split_phase(*c, cache, bt, q, lens, scale, ws, p, (hipStream_t)stream);
     if (e != hipSuccess) return DKV_ERR_HIP;
     return hip_status(launch_combine(*c, (const float *)ws, p.nsplit, out, (hipStream_t)stream));
 }
@@ -202,13 +209,7 @@ dkv_status dkv_attn_decode_partial(const dkv_config *c, const void *cache, const
 {
     dkv_status st = attn_common(c, cache, bt, q, lens, (float *)ws, ws, ws_bytes);
     if (st != DKV_OK) return st;
-    const Plan p = delta_plan(*c);
-    const int32_t *btp = c->page_tokens > 0 ? bt : nullptr;
-    if (fused_supported(*c))
-        return hip_status(launch_attn_fused(*c, cache, btp, q, lens, resolve_scale(*c, scale), (float *)ws,
-                                            p.nsplit, p.chunk, (hipStream_t)stream));
-    return hip_status(launch_attn_ref(*c, cache, btp, q, lens, resolve_scale(*c, scale), (float *)ws, p.nsplit,
-                                      p.chunk, (hipStream_t)stream));
+    return hip_status(launch_split_phase(*c, cache, bt, q, lens, scale, ws, delta_plan(*c), (hipStream_t)stream));
 }
 
 dkv_status dkv_attn_decode_ref(const dkv_config *c, const void *cache, const int32_t *bt, const float *q,
@@ -294,7 +295,7 @@ dkv_status dkv_attn_decode_q4_0(const dkv_config *c, const void *q4, const float
     if (st != DKV_OK) return st;
     if (!q4 || !q || !lens || !out) return DKV_ERR_ARG;
     const Plan p = tile_plan(*c);
-    if (!ws || ws_bytes < ws_for(*c, p)) return DKV_ERR_WORKSPACE;
+    if (!ws || ws_bytes < workspace_total(*c)) return DKV_ERR_WORKSPACE;
     hipError_t e = launch_attn_q40(*c, q4, q, lens, resolve_scale(*c, scale), (float *)ws, p.nsplit, p.chunk,
                                    (hipStream_t)stream);
     if (e != hipSuccess) return DKV_ERR_HIP;
@@ -309,7 +310,7 @@ dkv_status dkv_attn_decode_f16(const dkv_config *c, const uint16_t *k, const uin
     if (st != DKV_OK) return st;
     if (!k || !v || !q || !lens || !out || s_max < 1 || s_max > c->max_tokens) return DKV_ERR_ARG;
     const Plan p = tile_plan(*c);
-    if (!ws || ws_bytes < ws_for(*c, p)) return DKV_ERR_WORKSPACE;
+    if (!ws || ws_bytes < workspace_total(*c)) return DKV_ERR_WORKSPACE;
     hipError_t e = launch_attn_f16(*c, k, v, s_max, q, lens, resolve_scale(*c, scale), (float *)ws, p.nsplit,
                                    p.chunk, (hipStream_t)stream);
     if (e != hipSuccess) return DKV_ERR_HIP;

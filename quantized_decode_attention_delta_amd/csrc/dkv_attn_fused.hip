@@ -36,6 +36,7 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 
 __device__ inline h8 as_h8(u4 v) { return __builtin_bit_cast(h8, v); }
 
@@ -59,6 +60,72 @@ __device__ inline float hlo(uint32_t p) { return (float)__builtin_bit_cast(h2, p
 __device__ inline float hhi(uint32_t p) { return (float)__builtin_bit_cast(h2, p)[1]; }
 __device__ inline float half_at(const uint32_t *w, int k) { return (k & 1) ? hhi(w[k >> 1]) : hlo(w[k >> 1]); }
 
+// Cross-row exchanges with gfx950 permlane swaps (VALU, no LDS round trip).
+// The 64 lanes form 4 rows j of 16; these helpers combine the 4 values that
+// one column n holds in rows 0..3.
+// (Inline asm on two distinct registers: the compiler builtins return the
+// same register for both results when both inputs are the same value.  The
+// s_nop pairs cover the VALU-write / permlane-read hazards.)
+__device__ inline void swap16(float x, float &r0, float &r1)
+{
+    // r0 = rows (x0, x0, x2, x2), r1 = rows (x1, x1, x3, x3)
+    float a = x, b = x;
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+    r0 = a;
+    r1 = b;
+}
+__device__ inline void swap32(float x, float &r0, float &r1)
+{
+    // r0 = rows (x0, x1, x0, x1), r1 = rows (x2, x3, x2, x3)
+    float a = x, b = x;
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+    r0 = a;
+    r1 = b;
+}
+// Inclusive prefix over rows 0..j of the column, and the column total.
+__device__ inline void rows_prefix(float x, int j, float &incl, float &total)
+{
+    float a0, a1, b0, b1;
+    swap16(x, a0, a1);
+    const float t = a0 + a1;
+    swap32(t, b0, b1);
+    incl = ((j & 1) ? t : a0) + (j >= 2 ? b0 : 0.0f);
+    total = b0 + b1;
+}
+// Inclusive suffix over rows j..3 of the column, and the column total.
+__device__ inline void rows_suffix(float x, int j, float &incl, float &total)
+{
+    float a0, a1, b0, b1;
+    swap16(x, a0, a1);
+    const float t = a0 + a1;
+    swap32(t, b0, b1);
+    incl = ((j & 1) ? a1 : t) + (j < 2 ? b1 : 0.0f);
+    total = b0 + b1;
+}
+__device__ inline float rows_max(float x)
+{
+    float a0, a1, b0, b1;
+    swap16(x, a0, a1);
+    swap32(fmaxf(a0, a1), b0, b1);
+    return fmaxf(b0, b1);
+}
+
+// Lane index computed afresh (not CSE-able), to keep it out of the register
+// allocation of long loops.
+__device__ inline int fresh_lane_id()
+{
+    int x;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(x));
+    return x;
+}
+
+// Both fp16 halves of a word times 1/16.
+__device__ inline uint32_t scale_h2_16th(uint32_t x)
+{
+    const h2 sc = {(_Float16)0.0625f, (_Float16)0.0625f};
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, x) * sc);
+}
+
 __device__ inline uint32_t pack_h2(float lo, float hi)
 {
     h2 v;
@@ -72,16 +139,274 @@ bool fused_supported(const dkv_config &c)
     return c.kf == 32 && (c.head_dim == 64 || c.head_dim == 128) && c.n_q_heads / c.n_kv_heads <= 16;
 }
 
-// LDS image of a group's side data (kf = 32): [K keyframe][K scales][V keyframe][V scales], 2*D bytes each.
+// Per-group inputs of the fused kernel, fetched one group ahead.
 template <int D>
-__global__ void __launch_bounds__(64)
+struct GroupRegs {
+    u4 side;                          // 16 B of the group's side data (this lane's share)
+    uint32_t kc[2][D / 32];           // K code pieces of tokens 16T + n (piece j)
+    uint32_t vc[D / 16];              // V code words of channel n (piece j)
+};
+
+// Byte offsets of a lane's loads inside a group record (the same for every group).
+struct LaneOffsets {
+    int side, k0, k1, v;
+};
+
+template <int D>
+__device__ inline LaneOffsets lane_offsets(const Geom &g, int lane, int j, int n)
+{
+    constexpr int NB = D / 32, NCC = D / 16, SIDE_LANES = D / 4;
+    LaneOffsets o;
+    // lanes beyond the side data read past the record: the buffer unit returns zeros
+    o.side = lane < SIDE_LANES ? 16 * lane
+           : lane < 2 * SIDE_LANES ? (int)g.off_vkf + 16 * (lane - SIDE_LANES) : 0x40000000;
+    const int row0 = n > 0 ? n - 1 : 0;        // token n of tile 0 (token 0 is the keyframe)
+    o.k0 = (int)g.off_kcd + row0 * (D / 2) + 4 * j * NB;
+    o.k1 = (int)g.off_kcd + (15 + n) * (D / 2) + 4 * j * NB;
+    o.v = (int)g.off_vcd + (j * 16 + n) * NCC * 4;
+    return o;
+}
+
+template <int D>
+__device__ inline void load_group(GroupRegs<D> &r, const uint8_t *rec, int rec_bytes, const LaneOffsets &o)
+{
+    constexpr int NB = D / 32, NCC = D / 16;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)rec, (short)0, rec_bytes, 0x00020000);
+    r.side = __builtin_amdgcn_raw_buffer_load_b128(rs, o.side, 0, 0);
+    if constexpr (NB == 4) {
+        u4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, o.k0, 0, 0);
+        u4 c = __builtin_amdgcn_raw_buffer_load_b128(rs, o.k1, 0, 0);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            r.kc[0][k] = a[k];
+            r.kc[1][k] = c[k];
+        }
+    } else {
+        u2 a = __builtin_amdgcn_raw_buffer_load_b64(rs, o.k0, 0, 0);
+        u2 c = __builtin_amdgcn_raw_buffer_load_b64(rs, o.k1, 0, 0);
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            r.kc[0][k] = a[k];
+            r.kc[1][k] = c[k];
+        }
+    }
+#pragma unroll
+    for (int q4 = 0; q4 < NCC / 4; ++q4) {
+        u4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, o.v + 16 * q4, 0, 0);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) r.vc[4 * q4 + k] = a[k];
+    }
+}
+
+// Softmax / accumulation state of one wavefront.
+template <int D>
+struct RunState {
+    f4 acc[D / 16];    // sum_t p_t Vhat_t, channels 16cc + 4j + i of head n, units 2^(beta-20)
+    f4 Z[D / 32];      // the "-8" part of each block, same units
+    float m, l;        // running max (log2 units) and sum of the softmax weights
+    int beta;          // fp16 range bias of the V weights
+};
+
+// One 32-token group: K-side logits, online-softmax update, V-side accumulation.
+// FULL: all 32 tokens valid (no masking).  side_b: the group's side data in LDS.
+template <int D, bool FULL>
+__device__ inline void process_group(RunState<D> &st, const GroupRegs<D> &r, const uint8_t *side_b, int nval,
+                                     int j, int n, const u4 *qB, float c2E, h8 B2h, h8 B2l, h8 AZ)
+{
+    constexpr int NB = D / 32, NCC = D / 16;
+    const int lane = 16 * j + n;
+    // ---- K side: delta logits per (token, head)
+    float dl[2][4];
+#pragma unroll
+    for (int T = 0; T < 2; ++T) {
+        uint32_t sg[4][NB / 2];
+        const uint32_t *sp = (const uint32_t *)(side_b + 2 * D + (16 * T + 4 * j) * 2 * NB);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int k = 0; k < NB / 2; ++k) sg[i][k] = sp[i * (NB / 2) + k];
+        if (T == 0) {
+#pragma unroll
+            for (int k = 0; k < NB / 2; ++k) sg[0][k] = j == 0 ? 0x00100010u : sg[0][k];   // keyframe row: 2^-20
+        }
+        f4 u = f4{0, 0, 0, 0};
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb) {
+            h8 A = unpack8(r.kc[T][bb]);
+            if (T == 0) {
+                // token 0 of the group is the keyframe (staged in LDS already scaled by f(hh)/16)
+                const u4 k = *(const u4 *)(side_b + (j * NB + bb) * 16);
+                u4 a = __builtin_bit_cast(u4, A);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) a[e] = n == 0 ? k[e] : a[e];
+                A = as_h8(a);
+            }
+            // query operand (hi, lo) of block bb for this lane, staged in LDS
+            const h8 bh = as_h8(qB[(2 * bb) * 64 + 16 * j + n]);
+            const h8 bl = as_h8(qB[(2 * bb + 1) * 64 + 16 * j + n]);
+            f4 P = mfma(A, bh, f4{0, 0, 0, 0});
+            P = mfma(A, bl, P);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) u[i] = __builtin_fmaf(half_at(sg[i], bb), P[i], u[i]);
+        }
+        u4 a2 = u4{0, 0, 0, 0};
+        {
+            const uint32_t *ap = (const uint32_t *)(side_b + 2 * D + (16 * T + n) * 2 * NB);
+            const bool use = j == 0 && !(T == 0 && n == 0);
+#pragma unroll
+            for (int k = 0; k < NB / 2; ++k) a2[k] = use ? ap[k] : 0u;
+        }
+        f4 C2 = mfma(as_h8(a2), B2h, f4{0, 0, 0, 0});
+        C2 = mfma(as_h8(a2), B2l, C2);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float d = __builtin_fmaf(u[i], 1048576.0f, C2[i]);
+            dl[T][i] = (FULL || 16 * T + 4 * j + i < nval) ? d : 0.0f;
+        }
+    }
+
+    // ---- prefix over the group's tokens (order T, j, i)
+    float Lg[2][4];
+    float excl[2], all[2];
+#pragma unroll
+    for (int T = 0; T < 2; ++T) {
+        Lg[T][0] = dl[T][0];
+#pragma unroll
+        for (int i = 1; i < 4; ++i) Lg[T][i] = Lg[T][i - 1] + dl[T][i];
+        const float tot = Lg[T][3];
+        float incl;
+        rows_prefix(tot, j, incl, all[T]);
+        excl[T] = incl - tot;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int T = 0; T < 2; ++T)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            Lg[T][i] += excl[T] + (T == 1 ? all[0] : 0.0f);
+            if (FULL || 16 * T + 4 * j + i < nval) mx = fmaxf(mx, Lg[T][i]);
+        }
+    mx = rows_max(mx);
+    const float m_g = mx * c2E;
+
+    // ---- V range bias from the group's largest |scale| (slot 0 of the V scale plane)
+    const uint32_t *vs0 = (const uint32_t *)(side_b + 6 * D);
+    uint32_t vmx = 0;
+#pragma unroll
+    for (int k = 0; k < NB / 2; ++k) {
+        const uint32_t w = vs0[k] & 0x7FFF7FFFu;
+        vmx = max(vmx, max(w & 0xFFFFu, w >> 16));
+    }
+    const int ev = (vmx >> 10) == 0 ? -14 : (int)(vmx >> 10) - 15;
+    const int beta_g = vmx == 0 ? 19 : 5 - ev;            // 32 * 16 * |s| * 2^beta < 2^15
+
+    const float m_new = fmaxf(st.m, m_g);
+    const int beta_new = min(st.beta, beta_g);
+    const float a_m = __builtin_amdgcn_exp2f(st.m - m_new);
+    if (__any(m_new != st.m || beta_new != st.beta)) {
+        const float alpha = a_m * ldexpf(1.0f, beta_new - st.beta);
+#pragma unroll
+        for (int cc = 0; cc < NCC; ++cc) st.acc[cc] *= alpha;
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb) st.Z[bb] *= alpha;
+        st.l *= a_m;
+    }
+    st.m = m_new;
+    st.beta = beta_new;
+
+    // ---- softmax weights and suffix sums
+    float S[2][4];
+#pragma unroll
+    for (int T = 0; T < 2; ++T)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(Lg[T][i], c2E, -m_new));
+            S[T][i] = (FULL || 16 * T + 4 * j + i < nval) ? p : 0.0f;
+        }
+    float sexcl[2], sall[2];
+#pragma unroll
+    for (int T = 0; T < 2; ++T) {
+#pragma unroll
+        for (int i = 2; i >= 0; --i) S[T][i] += S[T][i + 1];
+        const float tot = S[T][0];
+        float incl;
+        rows_suffix(tot, j, incl, sall[T]);
+        sexcl[T] = incl - tot;
+    }
+    const float Pg = sall[0] + sall[1];
+    st.l += Pg;
+
+    // ---- V weights W = S * s * 2^beta * 16/f in hi + lo fp16 (slot 0 = keyframe: weight 0)
+    const float bsc = ldexpf(1.0f, st.beta);
+    float Sp[2][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float k16 = (i & 1) ? bsc : 16.0f * bsc;
+        Sp[1][i] = (S[1][i] + sexcl[1]) * k16;
+        Sp[0][i] = (S[0][i] + (sexcl[0] + sall[1])) * k16;
+    }
+    Sp[0][0] = j == 0 ? 0.0f : Sp[0][0];
+    // weights per block pair, then the V MFMAs of the two 16-channel chunks of each block
+#pragma unroll
+    for (int k = 0; k < NB / 2; ++k) {
+        uint32_t vs[2][4];
+#pragma unroll
+        for (int T = 0; T < 2; ++T) {
+            const uint32_t *sp = (const uint32_t *)(side_b + 6 * D + (16 * T + 4 * j) * 2 * NB);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                vs[T][i] = (FULL || 16 * T + 4 * j + i < nval) ? sp[i * (NB / 2) + k] : 0u;
+        }
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int bb = 2 * k + e;
+            h8 Wh, Wl;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float s0 = e ? hhi(vs[0][i]) : hlo(vs[0][i]);
+                const float s1 = e ? hhi(vs[1][i]) : hlo(vs[1][i]);
+                const _Float16 h0 = (_Float16)__builtin_fmaf(s0, Sp[0][i], 0.0f);
+                const _Float16 h1 = (_Float16)__builtin_fmaf(s1, Sp[1][i], 0.0f);
+                Wh[2 * i] = h0;
+                Wh[2 * i + 1] = h1;
+                Wl[2 * i] = (_Float16)__builtin_fmaf(s0, Sp[0][i], -(float)h0);
+                Wl[2 * i + 1] = (_Float16)__builtin_fmaf(s1, Sp[1][i], -(float)h1);
+            }
+#pragma unroll
+            for (int c2 = 0; c2 < 2; ++c2) {
+                const int cc = 2 * bb + c2;
+                const h8 A = unpack8(r.vc[cc]);
+                st.acc[cc] = mfma(A, Wh, st.acc[cc]);
+                st.acc[cc] = mfma(A, Wl, st.acc[cc]);
+            }
+            st.Z[bb] = mfma(AZ, Wh, st.Z[bb]);
+            st.Z[bb] = mfma(AZ, Wl, st.Z[bb]);
+        }
+    }
+    // ---- keyframe: acc += P_g * x0 (accumulator units 2^(beta-20))
+    const float pk = Pg * ldexpf(1.0f, st.beta - 20);
+    const uint32_t *kp = (const uint32_t *)(side_b + 4 * D + j * NCC * 8);
+#pragma unroll
+    for (int cc = 0; cc < NCC; ++cc) {
+        const uint32_t w01 = kp[2 * cc], w23 = kp[2 * cc + 1];
+        st.acc[cc][0] = __builtin_fmaf(hlo(w01), pk, st.acc[cc][0]);
+        st.acc[cc][1] = __builtin_fmaf(hhi(w01), pk, st.acc[cc][1]);
+        st.acc[cc][2] = __builtin_fmaf(hlo(w23), pk, st.acc[cc][2]);
+        st.acc[cc][3] = __builtin_fmaf(hhi(w23), pk, st.acc[cc][3]);
+    }
+}
+
+// kf = 32.  LDS image of a group's side data: [K keyframe][K scales][V keyframe][V scales], 2*D bytes each,
+// double-buffered so the next group's data lands while the current one is read.
+template <int D>
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
     k_attn_fused32(dkv_config cfg, const uint8_t *__restrict__ cache, const int32_t *__restrict__ bt,
                    const float *__restrict__ q, const int32_t *__restrict__ seq_lens, float scale_log2,
                    float *__restrict__ ws, int nsplit, int chunk)
 {
-    constexpr int NB = D / 32;      // Q4_0 blocks per row
-    constexpr int NCC = D / 16;     // 16-channel chunks
-    constexpr int SIDE_LANES = D / 4; // lanes loading 16 B each per side range (4*D bytes)
+    constexpr int NB = D / 32;
+    constexpr int NCC = D / 16;
+    constexpr int SIDE_LANES = D / 4;
     const Geom g = make_geom(cfg);
     const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int lane = threadIdx.x, j = lane >> 4, n = lane & 15;
@@ -91,7 +416,9 @@ __global__ void __launch_bounds__(64)
     const int g0 = split * chunk, g1 = min(ng, g0 + chunk);
 
     __shared__ float sq[16][D + 4];
-    __shared__ __attribute__((aligned(16))) uint32_t side[2 * D];   // 8*D bytes
+    __shared__ __attribute__((aligned(16))) uint32_t side[2][2 * D];   // 2 x 8*D bytes
+    // per lane: query operands (block, hi/lo), the K correction operand (hi, lo) and the V "-8" operand
+    __shared__ u4 qB[(2 * NB + 3) * 64];
 
     // ---------------------------------------------------------------- query
     for (int i = lane; i < 16 * D; i += 64) {
@@ -108,6 +435,7 @@ __global__ void __launch_bounds__(64)
     const float qscale = ldexpf(1.0f, -E);
     const float c2E = ldexpf(1.0f, E);
 
+    // K-side operand: q * 2^-E * 16/f in hi + lo fp16, in the code unpack order
     h8 Bh[NB], Bl[NB];
     float Qs[NB];
 #pragma unroll
@@ -126,281 +454,121 @@ __global__ void __launch_bounds__(64)
         qsum += __shfl_xor(qsum, 16);
         qsum += __shfl_xor(qsum, 32);
         Qs[bb] = qsum;
+        qB[(2 * bb) * 64 + lane] = __builtin_bit_cast(u4, Bh[bb]);
+        qB[(2 * bb + 1) * 64 + lane] = __builtin_bit_cast(u4, Bl[bb]);
     }
     // correction operand: -8 * Qs[block] at K index = block (lane group 0)
-    h8 B2h, B2l;
+    {
+        h8 B2h, B2l;
 #pragma unroll
-    for (int hh = 0; hh < 8; ++hh) {
-        const float x = (j == 0 && hh < NB) ? -8.0f * Qs[hh < NB ? hh : 0] : 0.0f;
-        const _Float16 hi = (_Float16)x;
-        B2h[hh] = hi;
-        B2l[hh] = (_Float16)(x - (float)hi);
+        for (int hh = 0; hh < 8; ++hh) {
+            const float x = (j == 0 && hh < NB) ? -8.0f * Qs[hh < NB ? hh : 0] : 0.0f;
+            const _Float16 hi = (_Float16)x;
+            B2h[hh] = hi;
+            B2l[hh] = (_Float16)(x - (float)hi);
+        }
+        qB[(2 * NB) * 64 + lane] = __builtin_bit_cast(u4, B2h);
+        qB[(2 * NB + 1) * 64 + lane] = __builtin_bit_cast(u4, B2l);
+        // V "-8" operand: -8 * 2^-24 * f(hh) as fp16 subnormals
+        u4 azr;
+        azr[0] = 0x80088008u;
+        azr[1] = 0x80808080u;
+        azr[2] = 0x80088008u;
+        azr[3] = 0x80808080u;
+        qB[(2 * NB + 2) * 64 + lane] = azr;
     }
-    // V "-8" operand: -8 * 2^-24 * f(hh) as fp16 subnormals
-    u4 azr;
-    azr[0] = 0x80088008u;
-    azr[1] = 0x80808080u;
-    azr[2] = 0x80088008u;
-    azr[3] = 0x80808080u;
-    const h8 AZ = as_h8(azr);
 
-    f4 acc[NCC];
-    f4 Z[NB];
+    RunState<D> st;
 #pragma unroll
-    for (int cc = 0; cc < NCC; ++cc) acc[cc] = f4{0, 0, 0, 0};
+    for (int cc = 0; cc < NCC; ++cc) st.acc[cc] = f4{0, 0, 0, 0};
 #pragma unroll
-    for (int bb = 0; bb < NB; ++bb) Z[bb] = f4{0, 0, 0, 0};
-    float m_run = -INFINITY, l_run = 0.0f;
-    int beta_run = 127;
+    for (int bb = 0; bb < NB; ++bb) st.Z[bb] = f4{0, 0, 0, 0};
+    st.m = -INFINITY;
+    st.l = 0.0f;
+    st.beta = 127;
 
-    const uint8_t *side_b = (const uint8_t *)side;
-    for (int gi = g0; gi < g1; ++gi) {
-        const int64_t off = group_offset(g, bt, b, h, gi);
-        if (off < 0) continue;
-        const uint8_t *rec = cache + off;
-        const int nval = min(32, L - gi * 32);
+    const h8 B2hr = as_h8(qB[(2 * NB) * 64 + lane]), B2lr = as_h8(qB[(2 * NB + 1) * 64 + lane]);
+    const h8 AZr = as_h8(qB[(2 * NB + 2) * 64 + lane]);
+    const LaneOffsets lo = lane_offsets<D>(g, lane, j, n);
 
-        // ---- loads: side data, K codes (two 16-token tiles), V codes
-        u4 sidev = u4{0, 0, 0, 0};
-        if (lane < SIDE_LANES) sidev = *(const u4 *)(rec + 16 * lane);
-        else if (lane < 2 * SIDE_LANES) sidev = *(const u4 *)(rec + g.off_vkf + 16 * (lane - SIDE_LANES));
-        uint32_t kc[2][NB];
-#pragma unroll
-        for (int T = 0; T < 2; ++T) {
-            const int tau = 16 * T + n;
-            const int row = tau > 0 ? tau - 1 : 0;
-            const uint32_t *src = (const uint32_t *)(rec + g.off_kcd + (int64_t)row * (D / 2) + 4 * j * NB);
-#pragma unroll
-            for (int bb = 0; bb < NB; ++bb) kc[T][bb] = src[bb];
+    const int rec_bytes = (int)g.rec;
+    // first mapped group at or after x (paged mode may leave pages unmapped); uniform
+    auto next_mapped = [&](int x, int64_t &o) {
+        for (; x < g1; ++x) {
+            o = group_offset(g, bt, b, h, x);
+            if (o >= 0) break;
         }
-        uint32_t vc[NCC];
-        {
-            const uint32_t *src = (const uint32_t *)(rec + g.off_vcd) + (j * 16 + n) * NCC;
-#pragma unroll
-            for (int cc = 0; cc < NCC; ++cc) vc[cc] = src[cc];
+        return x;
+    };
+    // stage a group's side data into LDS buffer `bf`; the K keyframe (lanes < D/8)
+    // is scaled by f(hh)/16 here, once, for the keyframe row of the K-side MFMA
+    auto stage = [&](const GroupRegs<D> &r, int bf) {
+        if (lane < 2 * SIDE_LANES) {
+            u4 v = r.side;
+            if (lane < D / 8) {
+                // (scalar temporaries: bit_cast of a vector element lvalue is miscompiled)
+                const uint32_t w0 = v[0], w2 = v[2];
+                v[0] = scale_h2_16th(w0);
+                v[2] = scale_h2_16th(w2);
+            }
+            // lane id recomputed here (two VALU ops) rather than kept live across the loop
+            ((u4 *)side[bf])[fresh_lane_id()] = v;
         }
+    };
+    auto run = [&](const GroupRegs<D> &r, int gcur, int bf) {
         __syncthreads();
-        if (lane < 2 * SIDE_LANES) ((u4 *)side)[lane] = sidev;
-        __syncthreads();
+        const int nval = min(32, L - gcur * 32);
+        const uint8_t *sb = (const uint8_t *)side[bf];
+        if (nval == 32)
+            process_group<D, true>(st, r, sb, nval, j, n, qB, c2E, B2hr, B2lr, AZr);
+        else
+            process_group<D, false>(st, r, sb, nval, j, n, qB, c2E, B2hr, B2lr, AZr);
+    };
 
-        // ---- K side: delta logits per (token, head)
-        float dl[2][4];
-#pragma unroll
-        for (int T = 0; T < 2; ++T) {
-            // scales of tokens 16T + 4j + i (fp16 pairs over blocks)
-            uint32_t sg[4][NB / 2];
-            const uint32_t *sp = (const uint32_t *)(side_b + 2 * D + (16 * T + 4 * j) * 2 * NB);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int k = 0; k < NB / 2; ++k) sg[i][k] = sp[i * (NB / 2) + k];
-            if (T == 0 && j == 0) {
-#pragma unroll
-                for (int k = 0; k < NB / 2; ++k) sg[0][k] = 0x00100010u;   // keyframe row: 2^-20
-            }
-            f4 u = f4{0, 0, 0, 0};
-#pragma unroll
-            for (int bb = 0; bb < NB; ++bb) {
-                h8 A = unpack8(kc[T][bb]);
-                if (T == 0 && n == 0) {
-                    // keyframe row: fp16 keyframe values times f(hh)/16
-                    u4 kv = *(const u4 *)(side_b + (j * NB + bb) * 16);
-                    h8 kh = as_h8(kv);
-#pragma unroll
-                    for (int hh = 0; hh < 8; ++hh)
-                        if (((hh >> 1) & 1) == 0) kh[hh] = kh[hh] * (_Float16)0.0625f;
-                    A = kh;
-                }
-                f4 P = mfma(A, Bh[bb], f4{0, 0, 0, 0});
-                P = mfma(A, Bl[bb], P);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) u[i] = __builtin_fmaf(half_at(sg[i], bb), P[i], u[i]);
-            }
-            // correction: -8 * sum_b s_{t,b} Qs_b, with the token's scales at K index = block
-            u4 a2 = u4{0, 0, 0, 0};
-            if (j == 0 && !(T == 0 && n == 0)) {
-                const uint32_t *ap = (const uint32_t *)(side_b + 2 * D + (16 * T + n) * 2 * NB);
-#pragma unroll
-                for (int k = 0; k < NB / 2; ++k) a2[k] = ap[k];
-            }
-            f4 C2 = mfma(as_h8(a2), B2h, f4{0, 0, 0, 0});
-            C2 = mfma(as_h8(a2), B2l, C2);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int tok = 16 * T + 4 * j + i;
-                dl[T][i] = tok < nval ? __builtin_fmaf(u[i], 1048576.0f, C2[i]) : 0.0f;
-            }
-        }
-
-        // ---- prefix over the group's tokens: order (T, j, i)
-        float Lg[2][4];
-        float tot[2], excl[2], all[2];
-#pragma unroll
-        for (int T = 0; T < 2; ++T) {
-            Lg[T][0] = dl[T][0];
-#pragma unroll
-            for (int i = 1; i < 4; ++i) Lg[T][i] = Lg[T][i - 1] + dl[T][i];
-            tot[T] = Lg[T][3];
-            float x = tot[T];
-            float y = __shfl_up(x, 16);
-            if (j >= 1) x += y;
-            y = __shfl_up(x, 32);
-            if (j >= 2) x += y;
-            excl[T] = x - tot[T];
-            all[T] = __shfl(x, 48 + n);
-        }
-        float mx = -INFINITY;
-#pragma unroll
-        for (int T = 0; T < 2; ++T)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                Lg[T][i] += excl[T] + (T == 1 ? all[0] : 0.0f);
-                const int tok = 16 * T + 4 * j + i;
-                if (tok < nval) mx = fmaxf(mx, Lg[T][i]);
-            }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_g = mx * c2E;
-
-        // ---- V range: largest |scale| of the group sets the fp16 bias of the weights
-        int vmax = 0;
-#pragma unroll
-        for (int bb = 0; bb < NB; ++bb) {
-            const uint16_t sv = ((const uint16_t *)(side_b + 6 * D))[bb] & 0x7FFF;
-            vmax = max(vmax, (int)sv);
-        }
-        const int ev = (vmax >> 10) == 0 ? -14 : (vmax >> 10) - 15;
-        const int beta_g = vmax == 0 ? 19 : 5 - ev;             // kf * 16 * |s| * 2^beta < 2^15
-
-        const float m_new = fmaxf(m_run, m_g);
-        const int beta_new = min(beta_run, beta_g);
-        const float a_m = exp2f(m_run - m_new);
-        const float alpha = a_m * ldexpf(1.0f, beta_new - beta_run);
-        if (__any(alpha != 1.0f)) {
-#pragma unroll
-            for (int cc = 0; cc < NCC; ++cc) acc[cc] *= alpha;
-#pragma unroll
-            for (int bb = 0; bb < NB; ++bb) Z[bb] *= alpha;
-        }
-        l_run *= a_m;
-        m_run = m_new;
-        beta_run = beta_new;
-
-        // ---- softmax weights and suffix sums
-        float p[2][4], S[2][4];
-#pragma unroll
-        for (int T = 0; T < 2; ++T)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int tok = 16 * T + 4 * j + i;
-                p[T][i] = tok < nval ? exp2f(__builtin_fmaf(Lg[T][i], c2E, -m_new)) : 0.0f;
-            }
-        float stot[2], sexcl[2], sall[2];
-#pragma unroll
-        for (int T = 0; T < 2; ++T) {
-            S[T][3] = p[T][3];
-#pragma unroll
-            for (int i = 2; i >= 0; --i) S[T][i] = S[T][i + 1] + p[T][i];
-            stot[T] = S[T][0];
-            float x = stot[T];
-            float y = __shfl_down(x, 16);
-            if (j <= 2) x += y;
-            y = __shfl_down(x, 32);
-            if (j <= 1) x += y;
-            sexcl[T] = x - stot[T];
-            sall[T] = __shfl(x, n);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            S[1][i] += sexcl[1];
-            S[0][i] += sexcl[0] + sall[1];
-        }
-        const float Pg = sall[0] + sall[1];
-        l_run += Pg;
-
-        // ---- V weights W = S * s * 2^beta * 16/f, split hi + lo fp16 (slot 0 = keyframe: 0)
-        uint32_t vs[2][4][NB / 2];
-#pragma unroll
-        for (int T = 0; T < 2; ++T) {
-            const uint32_t *sp = (const uint32_t *)(side_b + 6 * D + (16 * T + 4 * j) * 2 * NB);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int k = 0; k < NB / 2; ++k) {
-                    const int tok = 16 * T + 4 * j + i;
-                    vs[T][i][k] = tok < nval ? sp[i * (NB / 2) + k] : 0u;
-                }
-        }
-        const float bsc = ldexpf(1.0f, beta_run);
-        float Sp[2][4];
-#pragma unroll
-        for (int T = 0; T < 2; ++T)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) Sp[T][i] = S[T][i] * bsc * ((i & 1) ? 1.0f : 16.0f);
-        if (j == 0) Sp[0][0] = 0.0f;
-        h8 Wh[NB], Wl[NB];
-#pragma unroll
-        for (int bb = 0; bb < NB; ++bb) {
-            u4 rh, rl;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float w0 = Sp[0][i] * half_at(vs[0][i], bb);
-                const float w1 = Sp[1][i] * half_at(vs[1][i], bb);
-                const _Float16 h0 = (_Float16)w0, h1 = (_Float16)w1;
-                rh[i] = pack_h2((float)h0, (float)h1);
-                rl[i] = pack_h2(w0 - (float)h0, w1 - (float)h1);
-            }
-            Wh[bb] = as_h8(rh);
-            Wl[bb] = as_h8(rl);
-        }
-        // ---- V side MFMAs
-#pragma unroll
-        for (int cc = 0; cc < NCC; ++cc) {
-            const h8 A = unpack8(vc[cc]);
-            acc[cc] = mfma(A, Wh[cc >> 1], acc[cc]);
-            acc[cc] = mfma(A, Wl[cc >> 1], acc[cc]);
-        }
-#pragma unroll
-        for (int bb = 0; bb < NB; ++bb) {
-            Z[bb] = mfma(AZ, Wh[bb], Z[bb]);
-            Z[bb] = mfma(AZ, Wl[bb], Z[bb]);
-        }
-        // ---- keyframe: acc += P_g * x0 (in the accumulator's units 2^(beta-20))
-        {
-            const float pk = Pg * ldexpf(1.0f, beta_run - 20);
-            const uint32_t *kp = (const uint32_t *)(side_b + 4 * D + j * NCC * 8);
-#pragma unroll
-            for (int cc = 0; cc < NCC; ++cc) {
-                const uint32_t w01 = kp[2 * cc], w23 = kp[2 * cc + 1];
-                acc[cc][0] = __builtin_fmaf(hlo(w01), pk, acc[cc][0]);
-                acc[cc][1] = __builtin_fmaf(hhi(w01), pk, acc[cc][1]);
-                acc[cc][2] = __builtin_fmaf(hlo(w23), pk, acc[cc][2]);
-                acc[cc][3] = __builtin_fmaf(hhi(w23), pk, acc[cc][3]);
-            }
-        }
+    GroupRegs<D> ra, rb;
+    int64_t off = -1, offn = -1;
+    int gi = next_mapped(g0, off);
+    if (gi < g1) load_group<D>(ra, cache + off, rec_bytes, lo);
+    // two groups per trip: ra and rb alternate as current / prefetch buffers
+    while (gi < g1) {
+        int gn = next_mapped(gi + 1, offn);
+        stage(ra, 0);
+        // prefetch unconditionally so the wait counts stay exact (past the end it
+        // re-reads the current record and the values are unused)
+        load_group<D>(rb, cache + (gn < g1 ? offn : off), rec_bytes, lo);
+        run(ra, gi, 0);
+        gi = gn;
+        off = offn;
+        if (gi >= g1) break;
+        gn = next_mapped(gi + 1, offn);
+        stage(rb, 1);
+        load_group<D>(ra, cache + (gn < g1 ? offn : off), rec_bytes, lo);
+        run(rb, gi, 1);
+        gi = gn;
+        off = offn;
     }
 
     // ---------------------------------------------------------------- partials
+    const int64_t row0 = (int64_t)b * g.Hq + h * G;       // first query head of this kv-head
     if (n < G) {
-        float *rec = ws + (((int64_t)b * g.Hq + h * G + n) * nsplit + split) * part_stride(D);
-        const float un = ldexpf(1.0f, 20 - beta_run);
+        float *rec = ws + ((row0 + n) * nsplit + split) * part_stride(D);
+        const float un = ldexpf(1.0f, 20 - st.beta);
 #pragma unroll
         for (int cc = 0; cc < NCC; ++cc) {
             f4 o;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) o[i] = (acc[cc][i] + Z[cc >> 1][i]) * un;
+            for (int i = 0; i < 4; ++i) o[i] = (st.acc[cc][i] + st.Z[cc >> 1][i]) * un;
             *(f4 *)(rec + 16 * cc + 4 * j) = o;
         }
         if (j == 0) {
-            rec[D] = m_run;
-            rec[D + 1] = l_run;
+            rec[D] = st.m;
+            rec[D + 1] = st.l;
         }
     }
 }
 
 hipError_t launch_attn_fused(const dkv_config &c, const void *cache, const int32_t *bt, const float *q,
-                             const int32_t *lens, float scale_log2, float *ws, int nsplit, int chunk,
-                             hipStream_t st)
+                             const int32_t *lens, float scale_log2, float *ws, int nsplit, int chunk, hipStream_t st)
 {
     dim3 grid(nsplit, c.n_kv_heads, c.batch);
     if (c.head_dim == 64)

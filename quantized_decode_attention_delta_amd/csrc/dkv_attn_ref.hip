@@ -142,31 +142,45 @@ __global__ void __launch_bounds__(kRefThreads)
     }
 }
 
-// Merge split partials: grid (B*Hq), block D.
+// Merge split partials: grid (B*Hq), one wavefront per output row; lane c
+// holds channels c and c+64.  All loads of a run of 8 splits are issued before
+// the merge arithmetic, so a row costs about one memory round trip per 8 splits.
 template <int D>
-__global__ void __launch_bounds__(D) k_combine(const float *ws, int nsplit, float *out)
+__global__ void __launch_bounds__(64) k_combine(const float *__restrict__ ws, int nsplit, float *__restrict__ out)
 {
+    constexpr int R = part_stride(D);
+    constexpr int NCH = D / 64;
     const int64_t row = blockIdx.x;
     const int c = threadIdx.x;
-    constexpr int R = part_stride(D);
     const float *p = ws + row * nsplit * R;
-    float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) {
-        const float l = p[s * R + D + 1];
-        if (l > 0.0f) M = fmaxf(M, p[s * R + D]);
-    }
-    float num = 0.0f, den = 0.0f;
-    if (M > -INFINITY) {
-        for (int s = 0; s < nsplit; ++s) {
-            const float l = p[s * R + D + 1];
-            if (l > 0.0f) {
-                const float w = exp2f(p[s * R + D] - M);
-                num = fmaf(w, p[s * R + c], num);
-                den = fmaf(w, l, den);
+    float M = -INFINITY, den = 0.0f, num[NCH];
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) num[k] = 0.0f;
+    for (int s0 = 0; s0 < nsplit; s0 += 8) {
+        float ms[8], ls[8], a[8][NCH];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const bool ok = s0 + u < nsplit;
+            const float *r = p + (int64_t)(ok ? s0 + u : 0) * R;
+            ms[u] = r[D];
+            ls[u] = ok ? r[D + 1] : 0.0f;
+#pragma unroll
+            for (int k = 0; k < NCH; ++k) a[u][k] = r[c + 64 * k];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            if (ls[u] > 0.0f) {
+                const float mn = fmaxf(M, ms[u]);
+                const float al = exp2f(M - mn), w = exp2f(ms[u] - mn);
+#pragma unroll
+                for (int k = 0; k < NCH; ++k) num[k] = fmaf(w, a[u][k], num[k] * al);
+                den = fmaf(w, ls[u], den * al);
+                M = mn;
             }
         }
     }
-    out[row * D + c] = den > 0.0f ? num / den : 0.0f;
+#pragma unroll
+    for (int k = 0; k < NCH; ++k) out[row * D + c + 64 * k] = den > 0.0f ? num[k] / den : 0.0f;
 }
 
 hipError_t launch_attn_ref(const dkv_config &c, const void *cache, const int32_t *bt, const float *q,
@@ -189,7 +203,7 @@ hipError_t launch_combine(const dkv_config &c, const float *ws, int nsplit, floa
     if (c.head_dim == 64)
         hipLaunchKernelGGL(k_combine<64>, grid, dim3(64), 0, st, ws, nsplit, out);
     else
-        hipLaunchKernelGGL(k_combine<128>, grid, dim3(128), 0, st, ws, nsplit, out);
+        hipLaunchKernelGGL(k_combine<128>, grid, dim3(64), 0, st, ws, nsplit, out);
     return hipGetLastError();
 }
 
