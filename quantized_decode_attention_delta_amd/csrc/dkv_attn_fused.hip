@@ -28,111 +28,9 @@
 // tokens 16T + 4j + i (i < 4) of head n, which is exactly the operand layout
 // the V-side MFMA wants for its weights, so no data moves between the phases.
 // The group's scales and keyframes (1 KB) are staged through LDS once.
-#include "dkv_common.h"
+#include "dkv_fused_common.h"
 
 namespace dkv {
-
-typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-typedef float f4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u2 __attribute__((ext_vector_type(2)));
-
-__device__ inline h8 as_h8(u4 v) { return __builtin_bit_cast(h8, v); }
-
-// Eight 4-bit codes -> eight fp16 subnormals.  Half hh holds nibble
-// (hh>>1) + 4*(hh&1) of w, valued nibble * 2^-24 * f(hh) with f = 16 for
-// hh in {2,3,6,7} and 1 otherwise.
-__device__ inline h8 unpack8(uint32_t w)
-{
-    u4 r;
-    r[0] = w & 0x000F000Fu;
-    r[1] = w & 0x00F000F0u;
-    const uint32_t w8 = w >> 8;
-    r[2] = w8 & 0x000F000Fu;
-    r[3] = w8 & 0x00F000F0u;
-    return as_h8(r);
-}
-
-__device__ inline f4 mfma(h8 a, h8 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
-
-__device__ inline float hlo(uint32_t p) { return (float)__builtin_bit_cast(h2, p)[0]; }
-__device__ inline float hhi(uint32_t p) { return (float)__builtin_bit_cast(h2, p)[1]; }
-__device__ inline float half_at(const uint32_t *w, int k) { return (k & 1) ? hhi(w[k >> 1]) : hlo(w[k >> 1]); }
-
-// Cross-row exchanges with gfx950 permlane swaps (VALU, no LDS round trip).
-// The 64 lanes form 4 rows j of 16; these helpers combine the 4 values that
-// one column n holds in rows 0..3.
-// (Inline asm on two distinct registers: the compiler builtins return the
-// same register for both results when both inputs are the same value.  The
-// s_nop pairs cover the VALU-write / permlane-read hazards.)
-__device__ inline void swap16(float x, float &r0, float &r1)
-{
-    // r0 = rows (x0, x0, x2, x2), r1 = rows (x1, x1, x3, x3)
-    float a = x, b = x;
-    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
-    r0 = a;
-    r1 = b;
-}
-__device__ inline void swap32(float x, float &r0, float &r1)
-{
-    // r0 = rows (x0, x1, x0, x1), r1 = rows (x2, x3, x2, x3)
-    float a = x, b = x;
-    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
-    r0 = a;
-    r1 = b;
-}
-// Inclusive prefix over rows 0..j of the column, and the column total.
-__device__ inline void rows_prefix(float x, int j, float &incl, float &total)
-{
-    float a0, a1, b0, b1;
-    swap16(x, a0, a1);
-    const float t = a0 + a1;
-    swap32(t, b0, b1);
-    incl = ((j & 1) ? t : a0) + (j >= 2 ? b0 : 0.0f);
-    total = b0 + b1;
-}
-// Inclusive suffix over rows j..3 of the column, and the column total.
-__device__ inline void rows_suffix(float x, int j, float &incl, float &total)
-{
-    float a0, a1, b0, b1;
-    swap16(x, a0, a1);
-    const float t = a0 + a1;
-    swap32(t, b0, b1);
-    incl = ((j & 1) ? a1 : t) + (j < 2 ? b1 : 0.0f);
-    total = b0 + b1;
-}
-__device__ inline float rows_max(float x)
-{
-    float a0, a1, b0, b1;
-    swap16(x, a0, a1);
-    swap32(fmaxf(a0, a1), b0, b1);
-    return fmaxf(b0, b1);
-}
-
-// Lane index computed afresh (not CSE-able), to keep it out of the register
-// allocation of long loops.
-__device__ inline int fresh_lane_id()
-{
-    int x;
-    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(x));
-    return x;
-}
-
-// Both fp16 halves of a word times 1/16.
-__device__ inline uint32_t scale_h2_16th(uint32_t x)
-{
-    const h2 sc = {(_Float16)0.0625f, (_Float16)0.0625f};
-    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, x) * sc);
-}
-
-__device__ inline uint32_t pack_h2(float lo, float hi)
-{
-    h2 v;
-    v[0] = (_Float16)lo;
-    v[1] = (_Float16)hi;
-    return __builtin_bit_cast(uint32_t, v);
-}
 
 bool fused_supported(const dkv_config &c)
 {
@@ -146,26 +44,6 @@ struct GroupRegs {
     uint32_t kc[2][D / 32];           // K code pieces of tokens 16T + n (piece j)
     uint32_t vc[D / 16];              // V code words of channel n (piece j)
 };
-
-// Byte offsets of a lane's loads inside a group record (the same for every group).
-struct LaneOffsets {
-    int side, k0, k1, v;
-};
-
-template <int D>
-__device__ inline LaneOffsets lane_offsets(const Geom &g, int lane, int j, int n)
-{
-    constexpr int NB = D / 32, NCC = D / 16, SIDE_LANES = D / 4;
-    LaneOffsets o;
-    // lanes beyond the side data read past the record: the buffer unit returns zeros
-    o.side = lane < SIDE_LANES ? 16 * lane
-           : lane < 2 * SIDE_LANES ? (int)g.off_vkf + 16 * (lane - SIDE_LANES) : 0x40000000;
-    const int row0 = n > 0 ? n - 1 : 0;        // token n of tile 0 (token 0 is the keyframe)
-    o.k0 = (int)g.off_kcd + row0 * (D / 2) + 4 * j * NB;
-    o.k1 = (int)g.off_kcd + (15 + n) * (D / 2) + 4 * j * NB;
-    o.v = (int)g.off_vcd + (j * 16 + n) * NCC * 4;
-    return o;
-}
 
 template <int D>
 __device__ inline void load_group(GroupRegs<D> &r, const uint8_t *rec, int rec_bytes, const LaneOffsets &o)
@@ -197,15 +75,6 @@ __device__ inline void load_group(GroupRegs<D> &r, const uint8_t *rec, int rec_b
         for (int k = 0; k < 4; ++k) r.vc[4 * q4 + k] = a[k];
     }
 }
-
-// Softmax / accumulation state of one wavefront.
-template <int D>
-struct RunState {
-    f4 acc[D / 16];    // sum_t p_t Vhat_t, channels 16cc + 4j + i of head n, units 2^(beta-20)
-    f4 Z[D / 32];      // the "-8" part of each block, same units
-    float m, l;        // running max (log2 units) and sum of the softmax weights
-    int beta;          // fp16 range bias of the V weights
-};
 
 // One 32-token group: K-side logits, online-softmax update, V-side accumulation.
 // FULL: all 32 tokens valid (no masking).  side_b: the group's side data in LDS.

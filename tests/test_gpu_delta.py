@@ -28,6 +28,10 @@ CODEC_CASES = [
     ("8b", dict(S=700, Hq=8, Hkv=2, D=64), 32, 0),
     ("long", dict(S=1500, B=2, Hq=8, Hkv=2, kf=128), 128, 0),
     ("long", dict(S=1300, B=2, Hq=8, Hkv=2, kf=512), 512, 0),
+    ("long", dict(S=700, B=2, Hq=8, Hkv=2, D=64, kf=128), 128, 0),
+    ("long", dict(S=900, B=1, Hq=16, Hkv=1, kf=128), 128, 0),
+    ("8b", dict(S=500, Hq=8, Hkv=2), 96, 0),
+    ("mixed", dict(S=1400, B=3, Hq=8, Hkv=2, min_len=100, extra_tokens=0), 64, 256),
     ("70b", dict(S=999, B=3, Hq=16, Hkv=2), 32, 0),
     ("mixed", dict(S=1400, B=4, Hq=8, Hkv=2, min_len=100, extra_tokens=0), 32, 256),
     ("8b", dict(S=100, Hq=4, Hkv=1), 1, 0),
@@ -66,6 +70,21 @@ def test_ragged_and_empty_sequences():
     for fn in ("dkv_attn_decode", "dkv_attn_decode_ref"):
         got = U.attention(r, q, fn)
         assert np.all(got[0] == 0.0)                      # empty sequence: zero rows
+        ref = U.oracle_attention(enc, w, q, lens)
+        ref[0] = 0.0
+        assert U.rel_err(got, ref) <= U.ATTN_TOL
+
+
+def test_ragged_and_empty_sequences_long_interval():
+    w = _case("long", S=700, B=6, Hq=8, Hkv=2, kf=128)
+    lens = np.array([0, 1, 33, 128, 129, 700], np.int32)
+    r = U.prefill(w, kf=128, lens=lens)
+    enc = U.oracle_encode(w, 128, lens)
+    U.assert_codec_exact(r, enc, 128)
+    q = synth.queries(w)
+    for fn in ("dkv_attn_decode", "dkv_attn_decode_ref"):
+        got = U.attention(r, q, fn)
+        assert np.all(got[0] == 0.0)
         ref = U.oracle_attention(enc, w, q, lens)
         ref[0] = 0.0
         assert U.rel_err(got, ref) <= U.ATTN_TOL
