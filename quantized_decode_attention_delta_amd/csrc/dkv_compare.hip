@@ -1,27 +1,600 @@
-// In-run comparison caches: plain Q4_0 of absolute values and F16.
-#include "dkv_common.h"
+// In-run comparison paths of the Delta-KV article's "벤치마크" section: a
+// plain Q4_0 cache of absolute values (the 4-bit baseline) and an F16 cache
+// (the unquantised baseline), each with a matrix-core decode-attention kernel
+// built like the Delta-KV one (same split-K partials, same combine), so that
+// the three are compared on equal footing.
+//
+// Q4_0 cache: per (sequence, kv-head) a run of 32-token tiles of 36*D bytes
+//   [K scales 2D: fp16 [32][nb]][K codes 16D: 32 rows, same piece order as
+//   the Delta-KV K code rows][V scales 2D][V codes 16D: same tile order as the
+//   Delta-KV V codes]
+// i.e. exactly 18 bytes per 32 elements, laid out for the 16x16x32 fp16
+// matrix instruction.
+#include "dkv_fused_common.h"
+#include "dkv_q40.h"
 
 namespace dkv {
 
-hipError_t launch_q40_encode(const dkv_config &, void *, const uint16_t *, const uint16_t *, const int32_t *, int,
-                             hipStream_t)
+__host__ __device__ inline int64_t q40_tile_bytes(int D) { return 36LL * D; }
+__host__ __device__ inline int q40_ntiles(const dkv_config &c) { return (c.max_tokens + 31) / 32; }
+__host__ __device__ inline int64_t q40_tile_offset(const dkv_config &c, int b, int h, int tile)
 {
-    return hipErrorNotSupported;
+    return (((int64_t)b * c.n_kv_heads + h) * q40_ntiles(c) + tile) * q40_tile_bytes(c.head_dim);
 }
-hipError_t launch_q40_export(const dkv_config &, const void *, const int32_t *, int, uint8_t *, uint16_t *,
-                             hipStream_t)
+
+// ------------------------------------------------------------------------
+// Q4_0 encode: grid (tiles, Hkv*2, B), one wavefront per (tile, stream);
+// lanes own channels as in the Delta-KV encoder, the quantiser sees the
+// absolute value (reference 0).
+// ------------------------------------------------------------------------
+template <int D>
+__global__ void __launch_bounds__(64) k_q40_encode(dkv_config cfg, uint8_t *q4, const uint16_t *kin,
+                                                   const uint16_t *vin, const int32_t *seq_lens, int s_max)
 {
-    return hipErrorNotSupported;
+    constexpr int NC = D / 64, nb = D / 32;
+    const int tile = blockIdx.x, h = blockIdx.y >> 1, s = blockIdx.y & 1, b = blockIdx.z;
+    const int L = min(min(seq_lens[b], q40_ntiles(cfg) * 32), s_max);
+    const int t0 = tile * 32;
+    if (t0 >= L) return;
+    const int n = min(32, L - t0);
+    uint8_t *base = q4 + q40_tile_offset(cfg, b, h, tile) + (s ? 18 * D : 0);
+    uint16_t *sc = (uint16_t *)base;
+    uint8_t *cd = base + 2 * D;
+    const uint16_t *x = (s ? vin : kin) + (((int64_t)b * cfg.n_kv_heads + h) * s_max + t0) * D;
+    const int lane = threadIdx.x;
+
+    uint32_t vw[NC][4];
+#pragma unroll
+    for (int i = 0; i < NC; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) vw[i][j] = 0x88888888u;
+
+    for (int r = 0; r < n; ++r) {
+#pragma unroll
+        for (int i = 0; i < NC; ++i) {
+            const int c = lane + 64 * i;
+            const int blk = c >> 5;
+            float ref = 0.0f;
+            int code;
+            uint16_t s16;
+            q40_delta_step(h2f(x[(int64_t)r * D + c]), ref, code, s16);
+            if ((lane & 31) == 0) sc[r * nb + blk] = s16;
+            if (s == 0) {
+                store_k_codes<D>(cd + r * (D / 2), blk, code);
+            } else {
+                const int j = (r & 15) >> 2, sh = 4 * vcode_nibble(r);
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj)
+                    if (jj == j) vw[i][jj] = (vw[i][jj] & ~(0xFu << sh)) | ((uint32_t)code << sh);
+            }
+        }
+    }
+    if (s == 1) {
+        uint32_t *tw = (uint32_t *)cd;
+#pragma unroll
+        for (int i = 0; i < NC; ++i) {
+            const int c = lane + 64 * i;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) tw[vcode_word(D, 4 * j, c)] = vw[i][j];
+        }
+    }
 }
-hipError_t launch_attn_q40(const dkv_config &, const void *, const float *, const int32_t *, float, float *, int,
-                           int, hipStream_t)
+
+// Canonical export: codes uint8 [B][Hkv][2][s_max][D/2] (byte i of a block =
+// code i | code i+16 << 4), scales uint16 [B][Hkv][2][s_max][D/32].
+// grid (ceil(s_max*D/2 / 256), Hkv*2, B), one thread per output code byte.
+template <int D>
+__global__ void __launch_bounds__(256) k_q40_export(dkv_config cfg, const uint8_t *q4, const int32_t *seq_lens,
+                                                    int s_max, uint8_t *codes, uint16_t *scales)
 {
-    return hipErrorNotSupported;
+    constexpr int nb = D / 32, RB = D / 2;
+    const int h = blockIdx.y >> 1, s = blockIdx.y & 1, b = blockIdx.z;
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int t = (int)(e / RB), byte = (int)(e % RB);
+    const int L = min(min(seq_lens[b], q40_ntiles(cfg) * 32), s_max);
+    if (t >= L) return;
+    const uint8_t *base = q4 + q40_tile_offset(cfg, b, h, t >> 5) + (s ? 18 * D : 0);
+    const int tau = t & 31, blk = byte >> 4, i = byte & 15;
+    uint8_t out;
+    if (s == 0) {
+        out = base[2 * D + tau * RB + kcode_byte(nb, blk, i)];
+    } else {
+        const uint32_t *tw = (const uint32_t *)(base + 2 * D);
+        const int sh = 4 * vcode_nibble(tau);
+        const uint32_t lo = (tw[vcode_word(D, tau, 32 * blk + i)] >> sh) & 0xFu;
+        const uint32_t hi = (tw[vcode_word(D, tau, 32 * blk + i + 16)] >> sh) & 0xFu;
+        out = (uint8_t)(lo | (hi << 4));
+    }
+    const int64_t row = (((int64_t)b * cfg.n_kv_heads + h) * 2 + s) * s_max + t;
+    codes[row * RB + byte] = out;
+    if (byte < nb) scales[row * nb + byte] = ((const uint16_t *)base)[tau * nb + byte];
 }
-hipError_t launch_attn_f16(const dkv_config &, const uint16_t *, const uint16_t *, int, const float *,
-                           const int32_t *, float, float *, int, int, hipStream_t)
+
+// ------------------------------------------------------------------------
+// Shared set-up of the comparison attention kernels: the query of the G heads
+// of one kv-head, scaled by softmax_scale*log2(e) and by 2^-E (E = exponent of
+// its largest element), split in hi + lo fp16 as the K-side MFMA operand.
+// natural = true: K channels in natural order (F16); false: the Q4_0 code
+// unpack order with the 16/f factors (Q4_0).
+// ------------------------------------------------------------------------
+template <int D, bool NATURAL>
+__device__ inline void setup_query(float (*sq)[D + 4], u4 *qB, const float *q, int64_t row0, int G, float scale_log2,
+                                   int lane, int j, int n, float &c2E, float *Qs)
 {
-    return hipErrorNotSupported;
+    constexpr int NB = D / 32;
+    for (int i = lane; i < 16 * D; i += 64) {
+        const int hh = i / D, c = i % D;
+        sq[hh][c] = hh < G ? q[(row0 + hh) * D + c] * scale_log2 : 0.0f;
+    }
+    __syncthreads();
+    float qm = 0.0f;
+    for (int c = j * (D / 4); c < (j + 1) * (D / 4); ++c) qm = fmaxf(qm, fabsf(sq[n][c]));
+    qm = fmaxf(qm, __shfl_xor(qm, 16));
+    qm = fmaxf(qm, __shfl_xor(qm, 32));
+    int E = 0;
+    if (qm > 0.0f) frexpf(qm, &E);
+    const float qscale = ldexpf(1.0f, -E);
+    c2E = ldexpf(1.0f, E);
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) {
+        float qsum = 0.0f;
+        h8 Bh, Bl;
+#pragma unroll
+        for (int hh = 0; hh < 8; ++hh) {
+            const bool f16x = !NATURAL && ((hh >> 1) & 1) != 0;
+            const int ch = NATURAL ? 8 * j + hh : kf_k_channel(j, hh);
+            const float x = sq[n][32 * bb + ch] * qscale * ((NATURAL || f16x) ? 1.0f : 16.0f);
+            const _Float16 hi = (_Float16)x;
+            const _Float16 lo = (_Float16)(x - (float)hi);
+            Bh[hh] = hi;
+            Bl[hh] = lo;
+            qsum += ((float)hi + (float)lo) * ((NATURAL || f16x) ? 1.0f : 0.0625f);
+        }
+        qsum += __shfl_xor(qsum, 16);
+        qsum += __shfl_xor(qsum, 32);
+        if (Qs) Qs[bb] = qsum;
+        qB[(2 * bb) * 64 + lane] = __builtin_bit_cast(u4, Bh);
+        qB[(2 * bb + 1) * 64 + lane] = __builtin_bit_cast(u4, Bl);
+    }
+}
+
+// Sum over the 4 rows of a column (all rows get the total).
+__device__ inline float rows_sum(float x)
+{
+    float a0, a1, b0, b1;
+    swap16(x, a0, a1);
+    swap32(a0 + a1, b0, b1);
+    return b0 + b1;
+}
+
+// ------------------------------------------------------------------------
+// Q4_0 decode attention: grid (nsplit, Hkv, B), one wavefront per
+// (sequence, kv-head, run of 32-token tiles); lane = 16*j + n.
+// Per tile: logits of 32 tokens x 16 heads by MFMA on the raw codes (scale per
+// (token, block) applied to the fp32 results, "-8" by one small MFMA), online
+// softmax, then P.V by MFMA with the weights p*s*2^beta (hi + lo fp16).
+// ------------------------------------------------------------------------
+template <int D>
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
+    k_attn_q40(dkv_config cfg, const uint8_t *__restrict__ q4, const float *__restrict__ q,
+               const int32_t *__restrict__ seq_lens, float scale_log2, float *__restrict__ ws, int nsplit, int chunk)
+{
+    constexpr int NB = D / 32, NCC = D / 16;
+    const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int lane = threadIdx.x, j = lane >> 4, n = lane & 15;
+    const int G = cfg.n_q_heads / cfg.n_kv_heads;
+    const int ntiles = q40_ntiles(cfg);
+    const int L = min(seq_lens[b], ntiles * 32);
+    const int nt = (L + 31) >> 5;
+    const int t0 = split * chunk, t1 = min(nt, t0 + chunk);
+    const int64_t row0 = (int64_t)b * cfg.n_q_heads + h * G;
+
+    __shared__ float sq[16][D + 4];
+    __shared__ __attribute__((aligned(16))) uint32_t side[D];      // [K scales 2D bytes][V scales 2D bytes]
+    __shared__ u4 qB[2 * NB * 64];
+
+    float Qs[NB];
+    float c2E;
+    setup_query<D, false>(sq, qB, q, row0, G, scale_log2, lane, j, n, c2E, Qs);
+    h8 B2h, B2l;
+#pragma unroll
+    for (int hh = 0; hh < 8; ++hh) {
+        const float x = (j == 0 && hh < NB) ? -8.0f * Qs[hh < NB ? hh : 0] : 0.0f;
+        const _Float16 hi = (_Float16)x;
+        B2h[hh] = hi;
+        B2l[hh] = (_Float16)(x - (float)hi);
+    }
+    u4 azr;
+    azr[0] = 0x80088008u;
+    azr[1] = 0x80808080u;
+    azr[2] = 0x80088008u;
+    azr[3] = 0x80808080u;
+    const h8 AZ = as_h8(azr);
+
+    RunState<D> st;
+#pragma unroll
+    for (int cc = 0; cc < NCC; ++cc) st.acc[cc] = f4{0, 0, 0, 0};
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) st.Z[bb] = f4{0, 0, 0, 0};
+    st.m = -INFINITY;
+    st.l = 0.0f;
+    st.beta = 127;
+    const uint8_t *sb = (const uint8_t *)side;
+    const int tb = (int)q40_tile_bytes(D);
+
+    for (int tl = t0; tl < t1; ++tl) {
+        const uint8_t *tp = q4 + q40_tile_offset(cfg, b, h, tl);
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)tp, (short)0, tb, 0x00020000);
+        const int nvt = min(32, L - 32 * tl);
+        __syncthreads();
+        if (lane < D / 8)
+            ((u4 *)side)[lane] = __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * lane, 0, 0);
+        else if (lane < D / 4)
+            ((u4 *)side)[lane] = __builtin_amdgcn_raw_buffer_load_b128(rs, 18 * D + 16 * (lane - D / 8), 0, 0);
+        uint32_t kc[2][NB];
+#pragma unroll
+        for (int T = 0; T < 2; ++T) {
+            const int off = 2 * D + (16 * T + n) * (D / 2) + 4 * j * NB;
+            if constexpr (NB == 4) {
+                const u4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) kc[T][k] = a[k];
+            } else {
+                const u2 a = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
+#pragma unroll
+                for (int k = 0; k < 2; ++k) kc[T][k] = a[k];
+            }
+        }
+        uint32_t vc[NCC];
+#pragma unroll
+        for (int q4i = 0; q4i < NCC / 4; ++q4i) {
+            const u4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, 20 * D + (j * 16 + n) * NCC * 4 + 16 * q4i, 0, 0);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) vc[4 * q4i + k] = a[k];
+        }
+        __syncthreads();
+
+        // ---- logits
+        float Lg[2][4];
+#pragma unroll
+        for (int T = 0; T < 2; ++T) {
+            uint32_t sg[4][NB / 2];
+            const uint32_t *sp = (const uint32_t *)(sb + (16 * T + 4 * j) * 2 * NB);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int k = 0; k < NB / 2; ++k) sg[i][k] = sp[i * (NB / 2) + k];
+            f4 u = f4{0, 0, 0, 0};
+#pragma unroll
+            for (int bb = 0; bb < NB; ++bb) {
+                const h8 A = unpack8(kc[T][bb]);
+                const h8 bh = as_h8(qB[(2 * bb) * 64 + lane]);
+                const h8 bl = as_h8(qB[(2 * bb + 1) * 64 + lane]);
+                f4 P = mfma(A, bh, f4{0, 0, 0, 0});
+                P = mfma(A, bl, P);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) u[i] = __builtin_fmaf(half_at(sg[i], bb), P[i], u[i]);
+            }
+            u4 a2 = u4{0, 0, 0, 0};
+            {
+                const uint32_t *ap = (const uint32_t *)(sb + (16 * T + n) * 2 * NB);
+#pragma unroll
+                for (int k = 0; k < NB / 2; ++k) a2[k] = j == 0 ? ap[k] : 0u;
+            }
+            f4 C2 = mfma(as_h8(a2), B2h, f4{0, 0, 0, 0});
+            C2 = mfma(as_h8(a2), B2l, C2);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Lg[T][i] = __builtin_fmaf(u[i], 1048576.0f, C2[i]);
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int T = 0; T < 2; ++T)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (16 * T + 4 * j + i < nvt) mx = fmaxf(mx, Lg[T][i]);
+        mx = rows_max(mx);
+        const float m_new = fmaxf(st.m, mx * c2E);
+
+        // ---- V scales of this lane's 8 tokens (invalid tokens: 0) and the tile's max |scale|
+        uint32_t vs[2][4][NB / 2];
+        uint32_t vmx2 = 0;
+#pragma unroll
+        for (int T = 0; T < 2; ++T) {
+            const uint32_t *sp = (const uint32_t *)(sb + 2 * D + (16 * T + 4 * j) * 2 * NB);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int k = 0; k < NB / 2; ++k) {
+                    const uint32_t w = (16 * T + 4 * j + i < nvt) ? sp[i * (NB / 2) + k] : 0u;
+                    vs[T][i][k] = w;
+                    const uint32_t a = w & 0x7FFF7FFFu;
+                    vmx2 = max(vmx2, max(a & 0xFFFFu, a >> 16));
+                }
+        }
+        const int vmx = (int)rows_max((float)vmx2);
+        const int ev = (vmx >> 10) == 0 ? -14 : (vmx >> 10) - 15;
+        const int beta_g = vmx == 0 ? 127 : 10 - ev;                      // 16 * |s| * 2^beta < 2^15
+        const int beta_new = min(st.beta, beta_g);
+        const float a_m = __builtin_amdgcn_exp2f(st.m - m_new);
+        if (__any(m_new != st.m || beta_new != st.beta)) {
+            const float alpha = a_m * ldexpf(1.0f, beta_new - st.beta);
+#pragma unroll
+            for (int cc = 0; cc < NCC; ++cc) st.acc[cc] *= alpha;
+#pragma unroll
+            for (int bb = 0; bb < NB; ++bb) st.Z[bb] *= alpha;
+            st.l *= a_m;
+        }
+        st.m = m_new;
+        st.beta = beta_new;
+        const float bsc = ldexpf(1.0f, st.beta);
+
+        // ---- weights
+        float p[2][4];
+        float ps = 0.0f;
+#pragma unroll
+        for (int T = 0; T < 2; ++T)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(Lg[T][i], c2E, -m_new));
+                p[T][i] = (16 * T + 4 * j + i < nvt) ? e : 0.0f;
+                ps += p[T][i];
+            }
+        st.l += rows_sum(ps);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float k16 = (i & 1) ? bsc : 16.0f * bsc;
+            p[0][i] *= k16;
+            p[1][i] *= k16;
+        }
+#pragma unroll
+        for (int k = 0; k < NB / 2; ++k) {
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int bb = 2 * k + e;
+                h8 Wh, Wl;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float s0 = e ? hhi(vs[0][i][k]) : hlo(vs[0][i][k]);
+                    const float s1 = e ? hhi(vs[1][i][k]) : hlo(vs[1][i][k]);
+                    const _Float16 h0 = (_Float16)__builtin_fmaf(s0, p[0][i], 0.0f);
+                    const _Float16 h1 = (_Float16)__builtin_fmaf(s1, p[1][i], 0.0f);
+                    Wh[2 * i] = h0;
+                    Wh[2 * i + 1] = h1;
+                    Wl[2 * i] = (_Float16)__builtin_fmaf(s0, p[0][i], -(float)h0);
+                    Wl[2 * i + 1] = (_Float16)__builtin_fmaf(s1, p[1][i], -(float)h1);
+                }
+#pragma unroll
+                for (int c2 = 0; c2 < 2; ++c2) {
+                    const int cc = 2 * bb + c2;
+                    const h8 A = unpack8(vc[cc]);
+                    st.acc[cc] = mfma(A, Wh, st.acc[cc]);
+                    st.acc[cc] = mfma(A, Wl, st.acc[cc]);
+                }
+                st.Z[bb] = mfma(AZ, Wh, st.Z[bb]);
+                st.Z[bb] = mfma(AZ, Wl, st.Z[bb]);
+            }
+        }
+    }
+
+    if (n < G) {
+        float *recp = ws + ((row0 + n) * nsplit + split) * part_stride(D);
+        const float un = ldexpf(1.0f, 20 - st.beta);
+#pragma unroll
+        for (int cc = 0; cc < NCC; ++cc) {
+            f4 o;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] = (st.acc[cc][i] + st.Z[cc >> 1][i]) * un;
+            *(f4 *)(recp + 16 * cc + 4 * j) = o;
+        }
+        if (j == 0) {
+            recp[D] = st.m;
+            recp[D + 1] = st.l;
+        }
+    }
+}
+
+// ------------------------------------------------------------------------
+// F16 decode attention over token-major fp16 K/V [B][Hkv][s_max][D]:
+// grid (nsplit, Hkv, B), one wavefront per (sequence, kv-head, run of tiles).
+// K side: the 16-byte K row pieces are the MFMA A operand as loaded.  V side:
+// lane (j, n) loads channels n*CPL..n*CPL+CPL-1 of its 8 tokens 16T+4j+i and
+// regroups them (v_perm) into one A operand per channel offset r, so that MFMA
+// r yields channels m*CPL + r; weights p*2^14 in hi + lo fp16.
+// ------------------------------------------------------------------------
+__device__ inline uint32_t pack_lo16(uint32_t a, uint32_t b) { return (a & 0xFFFFu) | (b << 16); }
+__device__ inline uint32_t pack_hi16(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xFFFF0000u); }
+
+template <int D>
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
+    k_attn_f16(dkv_config cfg, const uint16_t *__restrict__ kin, const uint16_t *__restrict__ vin, int s_max,
+               const float *__restrict__ q, const int32_t *__restrict__ seq_lens, float scale_log2,
+               float *__restrict__ ws, int nsplit, int chunk)
+{
+    constexpr int NB = D / 32;
+    constexpr int CPL = D / 16;             // channels per lane per V token load
+    constexpr int VW = CPL / 2;             // dwords per V load
+    const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int lane = threadIdx.x, j = lane >> 4, n = lane & 15;
+    const int G = cfg.n_q_heads / cfg.n_kv_heads;
+    const int L = min(seq_lens[b], s_max);
+    const int nt = (L + 31) >> 5;
+    const int t0 = split * chunk, t1 = min(nt, t0 + chunk);
+    const int64_t row0 = (int64_t)b * cfg.n_q_heads + h * G;
+
+    __shared__ float sq[16][D + 4];
+    __shared__ u4 qB[2 * NB * 64];
+    float c2E;
+    setup_query<D, true>(sq, qB, q, row0, G, scale_log2, lane, j, n, c2E, nullptr);
+
+    f4 acc[CPL];
+#pragma unroll
+    for (int r = 0; r < CPL; ++r) acc[r] = f4{0, 0, 0, 0};
+    float m = -INFINITY, l = 0.0f;
+    const int64_t sbase = ((int64_t)b * cfg.n_kv_heads + h) * s_max;
+
+    for (int tl = t0; tl < t1; ++tl) {
+        const int64_t e0 = (sbase + 32 * tl) * D;
+        const int bytes = (s_max - 32 * tl) * D * 2;      // rest of this stream: loads past it return 0
+        const __amdgpu_buffer_rsrc_t rk =
+            __builtin_amdgcn_make_buffer_rsrc((void *)(kin + e0), (short)0, bytes, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rv =
+            __builtin_amdgcn_make_buffer_rsrc((void *)(vin + e0), (short)0, bytes, 0x00020000);
+        const int nvt = min(32, L - 32 * tl);
+        u4 kr[2][NB];
+#pragma unroll
+        for (int T = 0; T < 2; ++T)
+#pragma unroll
+            for (int bb = 0; bb < NB; ++bb)
+                kr[T][bb] = __builtin_amdgcn_raw_buffer_load_b128(rk, ((16 * T + n) * D + 32 * bb + 8 * j) * 2, 0, 0);
+        uint32_t vr[2][4][VW];
+#pragma unroll
+        for (int T = 0; T < 2; ++T)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int off = ((16 * T + 4 * j + i) * D + CPL * n) * 2;
+                if constexpr (VW == 4) {
+                    const u4 a = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) vr[T][i][k] = a[k];
+                } else {
+                    const u2 a = __builtin_amdgcn_raw_buffer_load_b64(rv, off, 0, 0);
+#pragma unroll
+                    for (int k = 0; k < 2; ++k) vr[T][i][k] = a[k];
+                }
+            }
+
+        // ---- logits (units: q * 2^-E)
+        float Lg[2][4];
+#pragma unroll
+        for (int T = 0; T < 2; ++T) {
+            f4 P = f4{0, 0, 0, 0};
+#pragma unroll
+            for (int bb = 0; bb < NB; ++bb) {
+                const h8 A = as_h8(kr[T][bb]);
+                P = mfma(A, as_h8(qB[(2 * bb) * 64 + lane]), P);
+                P = mfma(A, as_h8(qB[(2 * bb + 1) * 64 + lane]), P);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Lg[T][i] = P[i];
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int T = 0; T < 2; ++T)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (16 * T + 4 * j + i < nvt) mx = fmaxf(mx, Lg[T][i]);
+        mx = rows_max(mx);
+        const float m_new = fmaxf(m, mx * c2E);
+        const float a_m = __builtin_amdgcn_exp2f(m - m_new);
+        if (__any(m_new != m)) {
+#pragma unroll
+            for (int r = 0; r < CPL; ++r) acc[r] *= a_m;
+            l *= a_m;
+        }
+        m = m_new;
+
+        // ---- weights p * 2^14, hi + lo fp16, in the operand order 2i + T
+        h8 Wh, Wl;
+        float ps = 0.0f;
+#pragma unroll
+        for (int T = 0; T < 2; ++T)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool ok = 16 * T + 4 * j + i < nvt;
+                const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(Lg[T][i], c2E, -m_new));
+                const float p = ok ? e : 0.0f;
+                ps += p;
+                const float w = p * 16384.0f;
+                const _Float16 hi = (_Float16)w;
+                Wh[2 * i + T] = hi;
+                Wl[2 * i + T] = (_Float16)(w - (float)hi);
+                if (!ok) {
+#pragma unroll
+                    for (int k = 0; k < VW; ++k) vr[T][i][k] = 0u;      // rows past the end may hold non-finite values
+                }
+            }
+        l += rows_sum(ps);
+
+        // ---- V operands per channel offset r, then P.V
+#pragma unroll
+        for (int r = 0; r < CPL; ++r) {
+            u4 a;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t w0 = vr[0][i][r >> 1], w1 = vr[1][i][r >> 1];
+                a[i] = (r & 1) ? pack_hi16(w0, w1) : pack_lo16(w0, w1);
+            }
+            acc[r] = mfma(as_h8(a), Wh, acc[r]);
+            acc[r] = mfma(as_h8(a), Wl, acc[r]);
+        }
+    }
+
+    if (n < G) {
+        float *recp = ws + ((row0 + n) * nsplit + split) * part_stride(D);
+#pragma unroll
+        for (int r = 0; r < CPL; ++r)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) recp[(4 * j + i) * CPL + r] = acc[r][i] * (1.0f / 16384.0f);
+        if (j == 0) {
+            recp[D] = m;
+            recp[D + 1] = l;
+        }
+    }
+}
+
+// ------------------------------------------------------------------------
+// Launchers
+// ------------------------------------------------------------------------
+hipError_t launch_q40_encode(const dkv_config &c, void *q4, const uint16_t *k, const uint16_t *v,
+                             const int32_t *lens, int s_max, hipStream_t st)
+{
+    const int tiles = min(q40_ntiles(c), (s_max + 31) / 32);
+    dim3 grid(tiles, c.n_kv_heads * 2, c.batch);
+    if (c.head_dim == 64)
+        hipLaunchKernelGGL(k_q40_encode<64>, grid, dim3(64), 0, st, c, (uint8_t *)q4, k, v, lens, s_max);
+    else
+        hipLaunchKernelGGL(k_q40_encode<128>, grid, dim3(64), 0, st, c, (uint8_t *)q4, k, v, lens, s_max);
+    return hipGetLastError();
+}
+
+hipError_t launch_q40_export(const dkv_config &c, const void *q4, const int32_t *lens, int s_max, uint8_t *codes,
+                             uint16_t *scales, hipStream_t st)
+{
+    const int64_t per = (int64_t)s_max * (c.head_dim / 2);
+    dim3 grid((unsigned)((per + 255) / 256), c.n_kv_heads * 2, c.batch);
+    if (c.head_dim == 64)
+        hipLaunchKernelGGL(k_q40_export<64>, grid, dim3(256), 0, st, c, (const uint8_t *)q4, lens, s_max, codes,
+                           scales);
+    else
+        hipLaunchKernelGGL(k_q40_export<128>, grid, dim3(256), 0, st, c, (const uint8_t *)q4, lens, s_max, codes,
+                           scales);
+    return hipGetLastError();
+}
+
+hipError_t launch_attn_q40(const dkv_config &c, const void *q4, const float *q, const int32_t *lens, float scale_log2,
+                           float *ws, int nsplit, int chunk, hipStream_t st)
+{
+    dim3 grid(nsplit, c.n_kv_heads, c.batch);
+    if (c.head_dim == 64)
+        hipLaunchKernelGGL(k_attn_q40<64>, grid, dim3(64), 0, st, c, (const uint8_t *)q4, q, lens, scale_log2, ws,
+                           nsplit, chunk);
+    else
+        hipLaunchKernelGGL(k_attn_q40<128>, grid, dim3(64), 0, st, c, (const uint8_t *)q4, q, lens, scale_log2, ws,
+                           nsplit, chunk);
+    return hipGetLastError();
+}
+
+hipError_t launch_attn_f16(const dkv_config &c, const uint16_t *k, const uint16_t *v, int s_max, const float *q,
+                           const int32_t *lens, float scale_log2, float *ws, int nsplit, int chunk, hipStream_t st)
+{
+    dim3 grid(nsplit, c.n_kv_heads, c.batch);
+    if (c.head_dim == 64)
+        hipLaunchKernelGGL(k_attn_f16<64>, grid, dim3(64), 0, st, c, k, v, s_max, q, lens, scale_log2, ws, nsplit,
+                           chunk);
+    else
+        hipLaunchKernelGGL(k_attn_f16<128>, grid, dim3(64), 0, st, c, k, v, s_max, q, lens, scale_log2, ws, nsplit,
+                           chunk);
+    return hipGetLastError();
 }
 
 }  // namespace dkv
