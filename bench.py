@@ -15,6 +15,10 @@ Reported:
                duration from HIP events on the launch stream, vs 8 TB/s
   cpu_baseline the CPU oracle (reconstruct + float64 attention) on a bounded
                sample of the same workload, single thread
+  comparisons  the in-run F16 and plain-Q4_0 decode attentions on the same
+               data (same split-K plan and combine), with their own rates
+  quality      reconstruction MSE of Delta-KV and of Q4_0 against the fp16
+               input, from the GPU outputs (dkv_reconstruct, dkv_q4_0_export)
 """
 import argparse
 import json
@@ -27,6 +31,32 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+
+# HBM bytes per launch of the kf = 32 split kernel on the 70b workload, from
+# rocprofv3 FETCH_SIZE (x2.0) and WRITE_SIZE (x1.0) counters, each scaled by
+# what the counter reads for a 1 GiB device copy.  Valid only for the kernel
+# sources it was measured on (sha256 below); otherwise traffic is null.
+MEASURED_TRAFFIC = {
+    "workload": "70b", "kf": 32, "bytes": 676061850,
+    "sources": {
+        "dkv_attn_fused.hip": "bbb2baba2631b67df2ea6b916b4576a0cb20a5824bd1d06025999fc550d94269",
+        "dkv_fused_common.h": "0893e04395403ba2ce108a29b691a50cf98546315af501e07892cec1bbe86f39",
+        "dkv_common.h": "e597c5419e2c67e83797a166c6b6aac76ec5dad8c3cc27cc967c0cb5e552b0b7",
+    },
+}
+
+
+def measured_traffic(workload, kf, kernel):
+    import hashlib
+    t = MEASURED_TRAFFIC
+    if kernel != "fused" or workload != t["workload"] or kf != t["kf"]:
+        return None
+    src = os.path.join(ROOT, "quantized_decode_attention_delta_amd", "csrc")
+    for name, digest in t["sources"].items():
+        with open(os.path.join(src, name), "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() != digest:
+                return None
+    return t["bytes"]
 METRIC = "Delta-KV decode attn: effective KV GB/s (% HBM peak) + layer-steps/s"
 
 
@@ -53,6 +83,10 @@ def parse():
     ap.add_argument("--replicas", type=int, default=0, help="cache copies rotated per step (0 = auto, >= 1 GiB)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-compare", action="store_true", help="skip the F16 / Q4_0 comparisons and the MSE report")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first copy a 1 GiB device buffer 3 times (a plain copy kernel of known size, "
+                         "to scale the FETCH_SIZE / WRITE_SIZE counters of a profiled run)")
     return ap.parse_args()
 
 
@@ -96,6 +130,84 @@ def cpu_baseline(w, kf, budget_s):
     }
 
 
+def _time(fn, n, stream):
+    """Mean ms per call of fn(i), i = 0..n-1, from HIP events on `stream`."""
+    import torch
+    for i in range(3):
+        fn(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(n):
+        fn(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def comparisons(w, cfg, k, v, q, lens, ws, steps, stream, qo):
+    """In-run F16 and plain-Q4_0 decode attention on the same K/V and queries."""
+    import torch
+
+    import quantized_decode_attention_delta_amd as dkv
+    out = torch.empty(w.B, w.Hq, w.D, dtype=torch.float32, device=k.device)
+    res = {}
+    f16_bytes = f16_equiv_bytes(w.B, w.Hkv, w.D, w.S)
+    reps = max(1, math.ceil((1 << 30) / f16_bytes))
+    ks = [k] + [k.clone() for _ in range(reps - 1)]
+    vs = [v] + [v.clone() for _ in range(reps - 1)]
+    ms = _time(lambda i: dkv.dkv_attn_decode_f16(cfg, ks[i % reps], vs[i % reps], w.S, q, lens, out, ws),
+               steps, stream)
+    res["f16"] = {"ms_per_step": round(ms, 5), "GBps": round((f16_bytes + qo) / (ms * 1e-3) / 1e9, 2),
+                  "hbm_frac": round((f16_bytes + qo) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                  "bytes": f16_bytes, "replicas": reps}
+    del ks, vs
+    q4_bytes = 2 * w.B * w.Hkv * w.S * (w.D // 32) * 18
+    q4 = torch.empty(dkv.dkv_q4_0_cache_bytes(cfg), dtype=torch.uint8, device=k.device)
+    dkv.dkv_q4_0_encode(cfg, q4, k, v, lens, w.S)
+    reps = max(1, math.ceil((1 << 30) / q4.numel()))
+    q4s = [q4] + [q4.clone() for _ in range(reps - 1)]
+    ms = _time(lambda i: dkv.dkv_attn_decode_q4_0(cfg, q4s[i % reps], q, lens, out, ws), steps, stream)
+    res["q4_0"] = {"ms_per_step": round(ms, 5), "GBps": round((q4_bytes + qo) / (ms * 1e-3) / 1e9, 2),
+                   "hbm_frac": round((q4_bytes + qo) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                   "bytes": q4_bytes, "replicas": reps}
+    del q4s
+    return res, q4
+
+
+def quality(w, cfg, cache, q4, k, v, lens):
+    """Reconstruction MSE against the fp16 input, over every valid token, from
+    the GPU's own outputs: Delta-KV via dkv_reconstruct, Q4_0 via its export."""
+    import torch
+
+    import quantized_decode_attention_delta_amd as dkv
+    dev = k.device
+    B, H, S, D = w.B, w.Hkv, w.S, w.D
+    valid = (torch.arange(S, device=dev)[None, :] < lens[:, None].long())[:, None, :, None]
+    nval = float(valid.sum()) * H * D
+    kr = torch.empty(B, H, S, D, dtype=torch.float32, device=dev)
+    vr = torch.empty_like(kr)
+    dkv.dkv_reconstruct(cfg, cache, None, lens, S, kr, vr)
+    mse_d = [float((((kr - k.float()) ** 2) * valid).sum()) / nval,
+             float((((vr - v.float()) ** 2) * valid).sum()) / nval]
+    del kr, vr
+    codes = torch.empty(B, H, 2, S, D // 2, dtype=torch.uint8, device=dev)
+    scales = torch.empty(B, H, 2, S, D // 32, dtype=torch.int16, device=dev)
+    dkv.dkv_q4_0_export(cfg, q4, lens, S, codes, scales)
+    mse_q = []
+    for s, x in enumerate((k, v)):
+        c = codes[:, :, s].reshape(B, H, S, D // 32, 16)
+        full = torch.cat([(c & 15), (c >> 4)], dim=-1).float() - 8.0
+        sc = scales[:, :, s].view(torch.float16).float()[..., None]
+        deq = (full * sc).reshape(B, H, S, D)
+        mse_q.append(float((((deq - x.float()) ** 2) * valid).sum()) / nval)
+        del c, full, deq
+    md, mq = sum(mse_d) / 2, sum(mse_q) / 2
+    return {"mse_delta_kv": md, "mse_q4_0": mq, "ratio_q4_0_over_delta_kv": round(mq / md, 2) if md > 0 else None,
+            "mse_delta_kv_kv": mse_d, "mse_q4_0_kv": mse_q}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -110,6 +222,13 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     over = {} if args.kf is None else {"kf": args.kf}
     t_gen = time.time()
     w = synth.make(args.workload, **over)
@@ -126,7 +245,6 @@ def main():
     v = torch.from_numpy(w.v).to(dev)
     cache0 = torch.empty(cache_bytes, dtype=torch.uint8, device=dev)
     dkv.dkv_encode_prefill(cfg, cache0, state, None, k, v, lens, w.S)
-    del k, v
     caches = [cache0] + [cache0.clone() for _ in range(replicas - 1)]
     torch.cuda.synchronize()
     q = torch.from_numpy(synth.queries(w)).to(dev)
@@ -194,11 +312,17 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(args.workload, kf, args.kernel),
             "kernel_ms": round(kern_ms, 5),
             "algorithmic_bytes": comp + qo,
         },
     }
+    if not args.no_compare:
+        res["comparisons"], q4 = comparisons(w, cfg, k, v, q, lens, ws, args.steps, stream, qo)
+        res["comparisons"]["delta_kv"] = {"ms_per_step": res["ms_per_step"], "GBps": res["compressed_GBps"],
+                                          "hbm_frac": res["hbm_frac_step"], "bytes": comp}
+        res["quality"] = quality(w, cfg, cache0, q4, k, v, lens)
+        del q4
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, kf, args.cpu_seconds)
     print(json.dumps(res), flush=True)
