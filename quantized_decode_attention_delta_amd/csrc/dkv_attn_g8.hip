@@ -1,0 +1,455 @@
+// Matrix-core fused decode attention, kf = 32, at most 8 query heads per
+// kv-head (GQA groups of 1..8): the same delta-domain arithmetic as the
+// general 32-token kernel (Delta-KV article, "핵심 아이디어"; attention as in
+// "KV 캐시 벡터 양자화와 주의 보존 변환", "왜 복원 오차가 틀린 기준인가"), laid
+// out so that the 8 operand columns a GQA group of <= 8 heads leaves free do
+// useful work instead of padding.
+//
+// Lane = 16*j + n, column n = 8*h2 + hq: column half h2 in {0,1}, head hq.
+//  K side: the two 16-token halves T of the group go to the two column halves.
+//    B operand of half T is the query in columns 8T..8T+7 and zero elsewhere,
+//    so the four matrix instructions of a block (T = 0,1 x hi/lo query)
+//    accumulate into one result whose column half h2 holds the logits of
+//    tokens 16*h2 + row.  Every per-token step (scales, prefix sums, softmax
+//    weights) then runs on 4 tokens per lane instead of 8.
+//  V side: the V code tile rows are in block-pair order (rows 0..7 from block
+//    p, rows 8..15 from block p + nb/2).  Column half h2 carries the weights
+//    of block p + h2*nb/2, so one B operand serves both blocks of a pair and
+//    every lane forms the weights of one block instead of two; only the
+//    matching (row half, column half) results are kept.
+#include "dkv_fused_common.h"
+
+namespace dkv {
+
+bool fused_g8_supported(const dkv_config &c) { return vbp_layout(c) != 0; }
+
+// Value of lane n ^ 8 within each row of 16 lanes (DPP row rotate by 8).
+__device__ inline float other_half(float x)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x128, 0xF, 0xF, false));
+}
+
+template <int D>
+struct G8Regs {
+    u4 side;                  // 16 B of the group's side data
+    uint32_t kc[2][D / 32];   // K code pieces of tokens 16T + n (piece j)
+    uint32_t vc[D / 16];      // V code words of tile row n (piece j)
+};
+
+template <int D>
+__device__ inline void load_g8(G8Regs<D> &r, const uint8_t *rec, int rec_bytes, const LaneOffsets &o)
+{
+    constexpr int NB = D / 32, NCC = D / 16;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)rec, (short)0, rec_bytes, 0x00020000);
+    r.side = __builtin_amdgcn_raw_buffer_load_b128(rs, o.side, 0, 0);
+    if constexpr (NB == 4) {
+        u4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, o.k0, 0, 0);
+        u4 c = __builtin_amdgcn_raw_buffer_load_b128(rs, o.k1, 0, 0);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            r.kc[0][k] = a[k];
+            r.kc[1][k] = c[k];
+        }
+    } else {
+        u2 a = __builtin_amdgcn_raw_buffer_load_b64(rs, o.k0, 0, 0);
+        u2 c = __builtin_amdgcn_raw_buffer_load_b64(rs, o.k1, 0, 0);
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            r.kc[0][k] = a[k];
+            r.kc[1][k] = c[k];
+        }
+    }
+#pragma unroll
+    for (int q4 = 0; q4 < NCC / 4; ++q4) {
+        u4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, o.v + 16 * q4, 0, 0);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) r.vc[4 * q4 + k] = a[k];
+    }
+}
+
+// LDS operand addresses of one lane: the query (K side) and the "-8"
+// correction operands, per token half T; a lane of the other column half reads
+// an all-zero image instead.
+struct G8Ops {
+    const u4 *qk[2];   // + (2*bb + hl) * 64
+    const u4 *qc[2];   // + hl * 64
+};
+
+template <int D, bool FULL>
+__device__ inline void process_g8(RunState<D> &st, const G8Regs<D> &r, const uint8_t *sb, int nval, int j, int n,
+                                  const G8Ops &op, float c2E, h8 AZ)
+{
+    constexpr int NB = D / 32, NCC = D / 16, NP = NB / 2;
+    const int h2 = n >> 3;
+    const int tb = 16 * h2 + 4 * j;          // first of this lane's 4 tokens
+
+    // ---- K side: delta logits of tokens tb..tb+3
+    uint32_t sg[4][NP];
+    {
+        const uint32_t *sp = (const uint32_t *)(sb + 2 * D + tb * 2 * NB);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int k = 0; k < NP; ++k) sg[i][k] = sp[i * NP + k];
+#pragma unroll
+        for (int k = 0; k < NP; ++k) sg[0][k] = tb == 0 ? 0x00100010u : sg[0][k];   // keyframe row: 2^-20
+    }
+    f4 u = f4{0, 0, 0, 0};
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) {
+        h8 A0 = unpack8(r.kc[0][bb]);
+        {
+            // token 0 of the group is the keyframe (staged already scaled by f(hh)/16)
+            const u4 k = *(const u4 *)(sb + (j * NB + bb) * 16);
+            u4 a = __builtin_bit_cast(u4, A0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a[e] = n == 0 ? k[e] : a[e];
+            A0 = as_h8(a);
+        }
+        const h8 A1 = unpack8(r.kc[1][bb]);
+        f4 P = mfma(A0, as_h8(op.qk[0][(2 * bb) * 64]), f4{0, 0, 0, 0});
+        P = mfma(A0, as_h8(op.qk[0][(2 * bb + 1) * 64]), P);
+        P = mfma(A1, as_h8(op.qk[1][(2 * bb) * 64]), P);
+        P = mfma(A1, as_h8(op.qk[1][(2 * bb + 1) * 64]), P);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) u[i] = __builtin_fmaf(half_at(sg[i], bb), P[i], u[i]);
+    }
+    f4 C2;
+    {
+        u4 a0 = u4{0, 0, 0, 0}, a1 = u4{0, 0, 0, 0};
+        const uint32_t *p0 = (const uint32_t *)(sb + 2 * D + n * 2 * NB);
+        const uint32_t *p1 = (const uint32_t *)(sb + 2 * D + (16 + n) * 2 * NB);
+#pragma unroll
+        for (int k = 0; k < NP; ++k) {
+            a0[k] = (j == 0 && n != 0) ? p0[k] : 0u;
+            a1[k] = j == 0 ? p1[k] : 0u;
+        }
+        C2 = mfma(as_h8(a0), as_h8(op.qc[0][0]), f4{0, 0, 0, 0});
+        C2 = mfma(as_h8(a0), as_h8(op.qc[0][64]), C2);
+        C2 = mfma(as_h8(a1), as_h8(op.qc[1][0]), C2);
+        C2 = mfma(as_h8(a1), as_h8(op.qc[1][64]), C2);
+    }
+    float Lg[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float d = __builtin_fmaf(u[i], 1048576.0f, C2[i]);
+        Lg[i] = (FULL || tb + i < nval) ? d : 0.0f;
+    }
+
+    // ---- prefix over the group's tokens: in-lane, over rows j, then the first half's total
+#pragma unroll
+    for (int i = 1; i < 4; ++i) Lg[i] += Lg[i - 1];
+    {
+        float incl, all;
+        rows_prefix(Lg[3], j, incl, all);
+        const float allx = other_half(all);           // (every lane takes part in the exchange)
+        const float off = (incl - Lg[3]) + (h2 ? allx : 0.0f);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Lg[i] += off;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        if (FULL || tb + i < nval) mx = fmaxf(mx, Lg[i]);
+    mx = rows_max(mx);
+    mx = fmaxf(mx, other_half(mx));
+    const float m_g = mx * c2E;
+
+    // ---- V range bias from the group's largest |scale| (slot 0 of the V scale plane)
+    uint32_t vmx = 0;
+    {
+        const uint32_t *vs0 = (const uint32_t *)(sb + 6 * D);
+#pragma unroll
+        for (int k = 0; k < NP; ++k) {
+            const uint32_t w = vs0[k] & 0x7FFF7FFFu;
+            vmx = max(vmx, max(w & 0xFFFFu, w >> 16));
+        }
+    }
+    const int ev = (vmx >> 10) == 0 ? -14 : (int)(vmx >> 10) - 15;
+    const int beta_g = vmx == 0 ? 19 : 5 - ev;            // 32 * 16 * |s| * 2^beta < 2^15
+
+    const float m_new = fmaxf(st.m, m_g);
+    const int beta_new = min(st.beta, beta_g);
+    const float a_m = __builtin_amdgcn_exp2f(st.m - m_new);
+    if (__any(m_new != st.m || beta_new != st.beta)) {
+        const float alpha = a_m * ldexpf(1.0f, beta_new - st.beta);
+#pragma unroll
+        for (int cc = 0; cc < NCC; ++cc) st.acc[cc] *= alpha;
+#pragma unroll
+        for (int p = 0; p < NP; ++p) st.Z[p] *= alpha;
+        st.l *= a_m;
+    }
+    st.m = m_new;
+    st.beta = beta_new;
+
+    // ---- softmax weights of this lane's tokens and suffix sums over the group
+    float S[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(Lg[i], c2E, -m_new));
+        S[i] = (FULL || tb + i < nval) ? p : 0.0f;
+    }
+#pragma unroll
+    for (int i = 2; i >= 0; --i) S[i] += S[i + 1];
+    float Pg;
+    {
+        float incl, all;
+        rows_suffix(S[0], j, incl, all);
+        const float allx = other_half(all);
+        Pg = all + allx;
+        const float off = (incl - S[0]) + (h2 ? 0.0f : allx);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S[i] += off;
+    }
+    st.l += Pg;
+
+    // suffix sums of both token halves: own half and the other column half's
+    const float bsc = ldexpf(1.0f, st.beta);
+    float Sp[2][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float x = other_half(S[i]);
+        const float k16 = (i & 1) ? bsc : 16.0f * bsc;
+        Sp[0][i] = (h2 ? x : S[i]) * k16;
+        Sp[1][i] = (h2 ? S[i] : x) * k16;
+    }
+    Sp[0][0] = j == 0 ? 0.0f : Sp[0][0];      // keyframe slot
+
+    // ---- V: scales of the 8 token slots for this lane's block of each pair
+    uint32_t vs[2][4];
+    {
+        const int wsel = NB == 4 ? h2 : 0;
+#pragma unroll
+        for (int T = 0; T < 2; ++T) {
+            const uint32_t *sp = (const uint32_t *)(sb + 6 * D + (16 * T + 4 * j) * 2 * NB) + wsel;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                uint32_t w = sp[i * NP];
+                if constexpr (NB == 2) w >>= 16 * h2;        // block h2 of the single pair
+                vs[T][i] = (FULL || 16 * T + 4 * j + i < nval) ? w : 0u;
+            }
+        }
+    }
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        h8 Wh, Wl;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float s0 = (NB == 4 && p == 1) ? hhi(vs[0][i]) : hlo(vs[0][i]);
+            const float s1 = (NB == 4 && p == 1) ? hhi(vs[1][i]) : hlo(vs[1][i]);
+            const _Float16 w0 = (_Float16)__builtin_fmaf(s0, Sp[0][i], 0.0f);
+            const _Float16 w1 = (_Float16)__builtin_fmaf(s1, Sp[1][i], 0.0f);
+            Wh[2 * i] = w0;
+            Wh[2 * i + 1] = w1;
+            Wl[2 * i] = (_Float16)__builtin_fmaf(s0, Sp[0][i], -(float)w0);
+            Wl[2 * i + 1] = (_Float16)__builtin_fmaf(s1, Sp[1][i], -(float)w1);
+        }
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) {
+            const int cc = 4 * p + c4;
+            const h8 A = unpack8(r.vc[cc]);
+            st.acc[cc] = mfma(A, Wh, st.acc[cc]);
+            st.acc[cc] = mfma(A, Wl, st.acc[cc]);
+        }
+        st.Z[p] = mfma(AZ, Wh, st.Z[p]);
+        st.Z[p] = mfma(AZ, Wl, st.Z[p]);
+    }
+    // ---- keyframe: acc += P_g * x0 (accumulator units 2^(beta-20))
+    const float pk = Pg * ldexpf(1.0f, st.beta - 20);
+    const uint32_t *kp = (const uint32_t *)(sb + 4 * D + j * NCC * 8);
+#pragma unroll
+    for (int cc = 0; cc < NCC; ++cc) {
+        const uint32_t w01 = kp[2 * cc], w23 = kp[2 * cc + 1];
+        st.acc[cc][0] = __builtin_fmaf(hlo(w01), pk, st.acc[cc][0]);
+        st.acc[cc][1] = __builtin_fmaf(hhi(w01), pk, st.acc[cc][1]);
+        st.acc[cc][2] = __builtin_fmaf(hlo(w23), pk, st.acc[cc][2]);
+        st.acc[cc][3] = __builtin_fmaf(hhi(w23), pk, st.acc[cc][3]);
+    }
+}
+
+template <int D>
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
+    k_attn_g8(dkv_config cfg, const uint8_t *__restrict__ cache, const int32_t *__restrict__ bt,
+              const float *__restrict__ q, const int32_t *__restrict__ seq_lens, float scale_log2,
+              float *__restrict__ ws, int nsplit, int chunk)
+{
+    constexpr int NB = D / 32, NCC = D / 16, NP = NB / 2;
+    constexpr int SIDE_LANES = D / 4;
+    const Geom g = make_geom(cfg);
+    const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int lane = threadIdx.x, j = lane >> 4, n = lane & 15;
+    const int h2 = n >> 3, hq = n & 7;
+    const int G = g.G;
+    const int L = min(seq_lens[b], g.cap_tokens);
+    const int ng = (L + 31) >> 5;
+    const int g0 = split * chunk, g1 = min(ng, g0 + chunk);
+    const int64_t row0 = (int64_t)b * g.Hq + h * G;
+
+    __shared__ __attribute__((aligned(16))) uint32_t side[2][2 * D];
+    __shared__ u4 qk[2 * NB * 64];      // query operand (block, hi/lo) per lane, head hq
+    __shared__ u4 qc[2 * 64];           // "-8" correction operand (hi/lo) per lane
+    __shared__ u4 qz[2 * NB * 64];      // zeros (operand of the other column half)
+
+    // ---------------------------------------------------------------- query
+    // lane (j, n) holds head hq's channels 32*bb + kf_k_channel(j, hh), scaled by softmax_scale*log2(e)
+    float xq[NB][8];
+    float qm = 0.0f;
+    {
+        const float *qr = q + (row0 + hq) * D;
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb)
+#pragma unroll
+            for (int hh = 0; hh < 8; ++hh) {
+                const float x = hq < G ? qr[32 * bb + kf_k_channel(j, hh)] * scale_log2 : 0.0f;
+                xq[bb][hh] = x;
+                qm = fmaxf(qm, fabsf(x));
+            }
+    }
+    qm = rows_max(qm);
+    int E = 0;
+    if (qm > 0.0f) frexpf(qm, &E);         // |q'| * 2^-E < 1
+    const float qscale = ldexpf(1.0f, -E);
+    const float c2E = ldexpf(1.0f, E);
+    float Qs[NB];
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) {
+        float qsum = 0.0f;
+        h8 Bh, Bl;
+#pragma unroll
+        for (int hh = 0; hh < 8; ++hh) {
+            const bool f16x = ((hh >> 1) & 1) != 0;            // code half carries a factor 16
+            const float x = xq[bb][hh] * qscale * (f16x ? 1.0f : 16.0f);
+            const _Float16 hi = (_Float16)x;
+            const _Float16 lo = (_Float16)(x - (float)hi);
+            Bh[hh] = hi;
+            Bl[hh] = lo;
+            qsum += ((float)hi + (float)lo) * (f16x ? 1.0f : 0.0625f);
+        }
+        float incl, all;
+        rows_prefix(qsum, j, incl, all);
+        Qs[bb] = all;
+        qk[(2 * bb) * 64 + lane] = __builtin_bit_cast(u4, Bh);
+        qk[(2 * bb + 1) * 64 + lane] = __builtin_bit_cast(u4, Bl);
+        qz[(2 * bb) * 64 + lane] = u4{0, 0, 0, 0};
+        qz[(2 * bb + 1) * 64 + lane] = u4{0, 0, 0, 0};
+    }
+    {
+        h8 B2h, B2l;
+#pragma unroll
+        for (int hh = 0; hh < 8; ++hh) {
+            const float x = (j == 0 && hh < NB) ? -8.0f * Qs[hh < NB ? hh : 0] : 0.0f;
+            const _Float16 hi = (_Float16)x;
+            B2h[hh] = hi;
+            B2l[hh] = (_Float16)(x - (float)hi);
+        }
+        qc[lane] = __builtin_bit_cast(u4, B2h);
+        qc[64 + lane] = __builtin_bit_cast(u4, B2l);
+    }
+    u4 azr;
+    azr[0] = 0x80088008u;
+    azr[1] = 0x80808080u;
+    azr[2] = 0x80088008u;
+    azr[3] = 0x80808080u;
+    const h8 AZ = as_h8(azr);
+
+    G8Ops op;
+    op.qk[0] = (h2 == 0 ? qk : qz) + lane;
+    op.qk[1] = (h2 == 1 ? qk : qz) + lane;
+    op.qc[0] = (h2 == 0 ? qc : qz) + lane;
+    op.qc[1] = (h2 == 1 ? qc : qz) + lane;
+
+    RunState<D> st;
+#pragma unroll
+    for (int cc = 0; cc < NCC; ++cc) st.acc[cc] = f4{0, 0, 0, 0};
+#pragma unroll
+    for (int p = 0; p < NB; ++p) st.Z[p] = f4{0, 0, 0, 0};
+    st.m = -INFINITY;
+    st.l = 0.0f;
+    st.beta = 127;
+
+    const LaneOffsets lo = lane_offsets<D>(g, lane, j, n);
+    const int rec_bytes = (int)g.rec;
+    auto next_mapped = [&](int x, int64_t &o) {
+        for (; x < g1; ++x) {
+            o = group_offset(g, bt, b, h, x);
+            if (o >= 0) break;
+        }
+        return x;
+    };
+    auto stage = [&](const G8Regs<D> &r, int bf) {
+        if (lane < 2 * SIDE_LANES) {
+            u4 v = r.side;
+            if (lane < D / 8) {
+                const uint32_t w0 = v[0], w2 = v[2];
+                v[0] = scale_h2_16th(w0);
+                v[2] = scale_h2_16th(w2);
+            }
+            ((u4 *)side[bf])[fresh_lane_id()] = v;
+        }
+    };
+    auto run = [&](const G8Regs<D> &r, int gcur, int bf) {
+        __syncthreads();
+        const int nval = min(32, L - gcur * 32);
+        const uint8_t *sb = (const uint8_t *)side[bf];
+        if (nval == 32)
+            process_g8<D, true>(st, r, sb, nval, j, n, op, c2E, AZ);
+        else
+            process_g8<D, false>(st, r, sb, nval, j, n, op, c2E, AZ);
+    };
+
+    G8Regs<D> ra, rb;
+    int64_t off = -1, offn = -1;
+    int gi = next_mapped(g0, off);
+    if (gi < g1) load_g8<D>(ra, cache + off, rec_bytes, lo);
+    while (gi < g1) {
+        int gn = next_mapped(gi + 1, offn);
+        stage(ra, 0);
+        load_g8<D>(rb, cache + (gn < g1 ? offn : off), rec_bytes, lo);
+        run(ra, gi, 0);
+        gi = gn;
+        off = offn;
+        if (gi >= g1) break;
+        gn = next_mapped(gi + 1, offn);
+        stage(rb, 1);
+        load_g8<D>(ra, cache + (gn < g1 ? offn : off), rec_bytes, lo);
+        run(rb, gi, 1);
+        gi = gn;
+        off = offn;
+    }
+
+    // ---------------------------------------------------------------- partials
+    // lane (j, n) keeps rows 4j..4j+3 of each slice; they belong to its column
+    // half's block when (j < 2) == (h2 == 0)
+    if (hq < G) {
+        float *recp = ws + ((row0 + hq) * nsplit + split) * part_stride(D);
+        const float un = ldexpf(1.0f, 20 - st.beta);
+        if ((j < 2) == (h2 == 0)) {
+#pragma unroll
+            for (int cc = 0; cc < NCC; ++cc) {
+                f4 o;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o[i] = (st.acc[cc][i] + st.Z[cc >> 2][i]) * un;
+                *(f4 *)(recp + vchan(D, cc, 4 * j, 1)) = o;
+            }
+        }
+        if (lane == hq) {
+            recp[D] = st.m;
+            recp[D + 1] = st.l;
+        }
+    }
+}
+
+hipError_t launch_attn_g8(const dkv_config &c, const void *cache, const int32_t *bt, const float *q,
+                          const int32_t *lens, float scale_log2, float *ws, int nsplit, int chunk, hipStream_t st)
+{
+    dim3 grid(nsplit, c.n_kv_heads, c.batch);
+    if (c.head_dim == 64)
+        hipLaunchKernelGGL(k_attn_g8<64>, grid, dim3(64), 0, st, c, (const uint8_t *)cache, bt, q, lens, scale_log2,
+                           ws, nsplit, chunk);
+    else
+        hipLaunchKernelGGL(k_attn_g8<128>, grid, dim3(64), 0, st, c, (const uint8_t *)cache, bt, q, lens, scale_log2,
+                           ws, nsplit, chunk);
+    return hipGetLastError();
+}
+
+}  // namespace dkv

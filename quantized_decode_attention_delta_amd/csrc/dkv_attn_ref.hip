@@ -20,7 +20,7 @@ constexpr int kRefThreads = 256;
 constexpr int kMaxG = 16;
 
 template <int D>
-__device__ inline int ref_code(const uint8_t *cd, int s, int r, int c)
+__device__ inline int ref_code(const uint8_t *cd, int s, int r, int c, int bp)
 {
     if (s == 0) {
         const int cb = c & 31;
@@ -28,7 +28,7 @@ __device__ inline int ref_code(const uint8_t *cd, int s, int r, int c)
         return (byte >> (4 * (cb >> 4))) & 15;
     }
     const int tau = r & 31;
-    const uint32_t w = ((const uint32_t *)(cd + (int64_t)(r >> 5) * 16 * D))[vcode_word(D, tau, c)];
+    const uint32_t w = ((const uint32_t *)(cd + (int64_t)(r >> 5) * 16 * D))[vcode_word(D, tau, c, bp)];
     return (w >> (4 * vcode_nibble(tau))) & 15;
 }
 
@@ -78,9 +78,9 @@ __global__ void __launch_bounds__(kRefThreads)
                 for (int tt = 0; tt < nt; ++tt) {
                     const int r = tok0 + tt;
                     if (r == 0) {
-                        xh = h2f(((const uint16_t *)pkf)[rs ? vkf_pos(D, rc) : kkf_pos(nb, rc)]);
+                        xh = h2f(((const uint16_t *)pkf)[rs ? vkf_pos(D, rc, g.vbp) : kkf_pos(nb, rc)]);
                     } else {
-                        const int code = ref_code<D>(pcd, rs, r, rc);
+                        const int code = ref_code<D>(pcd, rs, r, rc, g.vbp);
                         const float sf = h2f(psc[r * nb + (rc >> 5)]);
                         xh = __fadd_rn(xh, __fmul_rn((float)(code - 8), sf));
                     }

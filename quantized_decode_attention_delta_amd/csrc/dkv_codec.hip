@@ -85,7 +85,7 @@ __global__ void __launch_bounds__(64) k_encode_prefill(dkv_config cfg, uint8_t *
 #pragma unroll
             for (int i = 0; i < NC; ++i) {
                 const int c = lane + 64 * i;
-                ((uint16_t *)p.kf)[s ? vkf_pos(D, c) : kkf_pos(nb, c)] = xv[i];
+                ((uint16_t *)p.kf)[s ? vkf_pos(D, c, g.vbp) : kkf_pos(nb, c)] = xv[i];
                 xh[i] = h2f(xv[i]);
             }
         } else {
@@ -118,7 +118,7 @@ __global__ void __launch_bounds__(64) k_encode_prefill(dkv_config cfg, uint8_t *
                 const int c = lane + 64 * i;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    tw[vcode_word(D, 4 * j, c)] = vw[i][j];
+                    tw[vcode_word(D, 4 * j, c, g.vbp)] = vw[i][j];
                     vw[i][j] = 0x88888888u;
                 }
             }
@@ -169,7 +169,7 @@ __global__ void __launch_bounds__(64) k_append(dkv_config cfg, uint8_t *cache, f
         const int blk = c >> 5;
         const uint16_t xv = x[c];
         if (r == 0) {
-            ((uint16_t *)p.kf)[s ? vkf_pos(D, c) : kkf_pos(nb, c)] = xv;
+            ((uint16_t *)p.kf)[s ? vkf_pos(D, c, g.vbp) : kkf_pos(nb, c)] = xv;
             if ((lane & 31) == 0) p.sc[blk] = 0;       // new group: reset the max-|scale| slot
             st[c] = h2f(xv);
         } else {
@@ -185,7 +185,7 @@ __global__ void __launch_bounds__(64) k_append(dkv_config cfg, uint8_t *cache, f
                 store_k_codes<D>(p.cd + (int64_t)(r - 1) * (D / 2), blk, code);
             } else {
                 const int tau = r & 31;
-                uint32_t *w = (uint32_t *)(p.cd + (int64_t)(r >> 5) * 16 * D) + vcode_word(D, tau, c);
+                uint32_t *w = (uint32_t *)(p.cd + (int64_t)(r >> 5) * 16 * D) + vcode_word(D, tau, c, g.vbp);
                 const int sh = 4 * vcode_nibble(tau);
                 *w = (*w & ~(0xFu << sh)) | ((uint32_t)code << sh);
             }
@@ -198,7 +198,7 @@ __global__ void __launch_bounds__(64) k_append(dkv_config cfg, uint8_t *cache, f
 // Code / scale readers shared by the decoder kernels.
 // ------------------------------------------------------------------------
 template <int D>
-__device__ inline int read_code(const StreamPtrs &p, int s, int r, int c)
+__device__ inline int read_code(const StreamPtrs &p, int s, int r, int c, int bp)
 {
     if (s == 0) {
         const int cb = c & 31;
@@ -206,7 +206,7 @@ __device__ inline int read_code(const StreamPtrs &p, int s, int r, int c)
         return (byte >> (4 * (cb >> 4))) & 15;
     }
     const int tau = r & 31;
-    const uint32_t w = ((const uint32_t *)(p.cd + (int64_t)(r >> 5) * 16 * D))[vcode_word(D, tau, c)];
+    const uint32_t w = ((const uint32_t *)(p.cd + (int64_t)(r >> 5) * 16 * D))[vcode_word(D, tau, c, bp)];
     return (w >> (4 * vcode_nibble(tau))) & 15;
 }
 
@@ -235,9 +235,9 @@ __global__ void __launch_bounds__(64) k_reconstruct(dkv_config cfg, const uint8_
         for (int i = 0; i < NC; ++i) {
             const int c = lane + 64 * i;
             if (r == 0) {
-                xh[i] = h2f(((const uint16_t *)p.kf)[s ? vkf_pos(D, c) : kkf_pos(nb, c)]);
+                xh[i] = h2f(((const uint16_t *)p.kf)[s ? vkf_pos(D, c, g.vbp) : kkf_pos(nb, c)]);
             } else {
-                const int code = read_code<D>(p, s, r, c);
+                const int code = read_code<D>(p, s, r, c, g.vbp);
                 const float sf = h2f(p.sc[r * nb + (c >> 5)]);
                 xh[i] = __fadd_rn(xh[i], __fmul_rn((float)(code - 8), sf));
             }
@@ -271,10 +271,10 @@ __global__ void __launch_bounds__(64) k_export(dkv_config cfg, const uint8_t *ca
         for (int i = 0; i < NC; ++i) {
             const int c = lane + 64 * i;
             if (r == 0) {
-                okf[(sidx * ng + gi) * D + c] = ((const uint16_t *)p.kf)[s ? vkf_pos(D, c) : kkf_pos(nb, c)];
+                okf[(sidx * ng + gi) * D + c] = ((const uint16_t *)p.kf)[s ? vkf_pos(D, c, g.vbp) : kkf_pos(nb, c)];
             } else {
                 const int64_t di = (int64_t)gi * (g.kf - 1) + r - 1;
-                const int code = read_code<D>(p, s, r, c);
+                const int code = read_code<D>(p, s, r, c, g.vbp);
                 const int hi = __shfl_down(code, 16, 32);
                 const int sl = lane & 31;
                 if (sl < 16) ocd[(sidx * nd + di) * (D / 2) + (c >> 5) * 16 + sl] = (uint8_t)(code | (hi << 4));

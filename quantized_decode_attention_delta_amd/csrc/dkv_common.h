@@ -9,8 +9,8 @@
 //                                 Q4_0 bytes of block b are split in four
 //                                 32-bit pieces, piece j at word j*nb + b
 //   codes (V)  ntiles*16*D        32-token tiles; word ((j*16+m)*(D/16)+cc)
-//                                 holds channel 16*cc+m for the 8 token slots
-//                                 16*e+4*j+r (r<4, e<2) at nibble r+4*e
+//                                 holds channel vchan(cc, m) for the 8 token
+//                                 slots 16*e+4*j+r (r<4, e<2) at nibble r+4*e
 // The permutations line the data up with the operand layout of the gfx950
 // 16x16x32 fp16 matrix instruction (lane = 16*j + m, eight K values per lane).
 #pragma once
@@ -34,6 +34,7 @@ __host__ __device__ constexpr int part_stride(int D) { return D + 4; }
 struct Geom {
     int D, nb, kf, Hkv, Hq, G, B;
     int ntiles_v;              // 32-token tiles of V codes per group
+    int vbp;                   // V tiles in block-pair order (see vchan)
     int64_t off_ksc, off_kcd, off_vkf, off_vsc, off_vcd, rec;
     // addressing
     int paged;                 // 1 if paged
@@ -44,6 +45,14 @@ struct Geom {
     int ng_cap;                // group capacity per sequence
     int cap_tokens;            // token capacity per sequence
 };
+
+// V code tiles use the block-pair row order when at most 8 query heads share
+// a kv-head (the matrix-core kernel then spends the 8 spare operand columns
+// on the second block of a pair) and kf = 32.
+__host__ __device__ inline int vbp_layout(const dkv_config &c)
+{
+    return c.kf == 32 && c.n_q_heads / c.n_kv_heads <= 8 && (c.head_dim == 64 || c.head_dim == 128);
+}
 
 __host__ __device__ inline Geom make_geom(const dkv_config &c)
 {
@@ -56,6 +65,7 @@ __host__ __device__ inline Geom make_geom(const dkv_config &c)
     g.G = c.n_q_heads / c.n_kv_heads;
     g.B = c.batch;
     g.ntiles_v = c.kf > 1 ? (c.kf + 31) / 32 : 0;
+    g.vbp = vbp_layout(c);
     int64_t kfb = 2 * (int64_t)g.D;
     int64_t scb = pad16((int64_t)c.kf * g.nb * 2);
     int64_t kcb = pad16((int64_t)(c.kf - 1) * g.D / 2);
@@ -118,20 +128,47 @@ __host__ __device__ inline int kkf_pos(int nb, int c)
     int h = 2 * (p & 3) + (p >> 2);            // inverse of half_to_nibble
     return (j * nb + b) * 8 + h;
 }
-// V keyframe: element (j*(D/16) + cc)*4 + r holds channel 16*cc + 4*j + r.
-__host__ __device__ inline int vkf_pos(int D, int c)
+// V tile rows.  A V code tile is D/16 slices of 16 rows (cc, m), each row one
+// channel.  Plain order: vchan(cc, m) = 16*cc + m (slice cc lies in block
+// cc/2).  Block-pair order (bp): with np = nb/2 block pairs (p, p+np), slice
+// cc = 4p + c4 holds channels 8*c4 + (m & 7) of block p in rows m < 8 and of
+// block p + np in rows m >= 8.
+__host__ __device__ inline int vchan(int D, int cc, int m, int bp)
 {
-    int cc = c >> 4, m = c & 15;
+    if (!bp) return 16 * cc + m;
+    const int np = D / 64, p = cc >> 2, c4 = cc & 3;
+    return 32 * (p + (m >> 3) * np) + 8 * c4 + (m & 7);
+}
+// inverse of vchan: slice and row of channel c
+__host__ __device__ inline void vslot(int D, int c, int bp, int &cc, int &m)
+{
+    if (!bp) {
+        cc = c >> 4;
+        m = c & 15;
+        return;
+    }
+    const int np = D / 64, b = c >> 5, w = c & 31;
+    const int hi = b >= np;
+    cc = 4 * (b - hi * np) + (w >> 3);
+    m = 8 * hi + (w & 7);
+}
+// V keyframe: element (j*(D/16) + cc)*4 + r holds channel vchan(cc, 4*j + r),
+// the accumulator order of the V-side matrix instruction.
+__host__ __device__ inline int vkf_pos(int D, int c, int bp)
+{
+    int cc, m;
+    vslot(D, c, bp, cc, m);
     int j = m >> 2, r = m & 3;
     return (j * (D / 16) + cc) * 4 + r;
 }
 // K code row: byte offset of canonical byte i (0..15) of block b.
 __host__ __device__ inline int kcode_byte(int nb, int b, int i) { return 4 * ((i >> 2) * nb + b) + (i & 3); }
 // V code tile: word index and nibble of (token slot tau in 0..31, channel c).
-__host__ __device__ inline int vcode_word(int D, int tau, int c)
+__host__ __device__ inline int vcode_word(int D, int tau, int c, int bp)
 {
     int j = (tau & 15) >> 2;
-    int m = c & 15, cc = c >> 4;
+    int cc, m;
+    vslot(D, c, bp, cc, m);
     return (j * 16 + m) * (D / 16) + cc;
 }
 __host__ __device__ inline int vcode_nibble(int tau) { return (tau & 3) + 4 * (tau >> 4); }

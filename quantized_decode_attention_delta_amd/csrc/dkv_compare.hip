@@ -75,7 +75,7 @@ __global__ void __launch_bounds__(64) k_q40_encode(dkv_config cfg, uint8_t *q4, 
         for (int i = 0; i < NC; ++i) {
             const int c = lane + 64 * i;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) tw[vcode_word(D, 4 * j, c)] = vw[i][j];
+            for (int j = 0; j < 4; ++j) tw[vcode_word(D, 4 * j, c, 0)] = vw[i][j];
         }
     }
 }
@@ -101,8 +101,8 @@ __global__ void __launch_bounds__(256) k_q40_export(dkv_config cfg, const uint8_
     } else {
         const uint32_t *tw = (const uint32_t *)(base + 2 * D);
         const int sh = 4 * vcode_nibble(tau);
-        const uint32_t lo = (tw[vcode_word(D, tau, 32 * blk + i)] >> sh) & 0xFu;
-        const uint32_t hi = (tw[vcode_word(D, tau, 32 * blk + i + 16)] >> sh) & 0xFu;
+        const uint32_t lo = (tw[vcode_word(D, tau, 32 * blk + i, 0)] >> sh) & 0xFu;
+        const uint32_t hi = (tw[vcode_word(D, tau, 32 * blk + i + 16, 0)] >> sh) & 0xFu;
         out = (uint8_t)(lo | (hi << 4));
     }
     const int64_t row = (((int64_t)b * cfg.n_kv_heads + h) * 2 + s) * s_max + t;
