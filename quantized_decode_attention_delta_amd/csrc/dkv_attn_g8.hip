@@ -75,15 +75,18 @@ struct G8Ops {
     const u4 *qc[2];   // + hl * 64
 };
 
+// K phase of one group: prefixed logits of this lane's 4 tokens (units q * 2^-E)
+// and the group maximum in log2 units.
 template <int D, bool FULL>
-__device__ inline void process_g8(RunState<D> &st, const G8Regs<D> &r, const uint8_t *sb, int nval, int j, int n,
-                                  const G8Ops &op, float c2E, h8 AZ)
+__device__ inline float k_phase_g8(const uint32_t (&kc)[2][D / 32], const uint8_t *sb, const u4 *kf_row, int nval,
+                                   int j, int n, const G8Ops &op, float c2E, float (&Lg)[4])
 {
-    constexpr int NB = D / 32, NCC = D / 16, NP = NB / 2;
+    constexpr int NB = D / 32, NP = NB / 2;
     const int h2 = n >> 3;
     const int tb = 16 * h2 + 4 * j;          // first of this lane's 4 tokens
 
-    // ---- K side: delta logits of tokens tb..tb+3
+    // ---- K side: delta logits of tokens tb..tb+3 (row 0 of the first half is the
+    // keyframe: its code row reads as zeros, its logit enters through C2 below)
     uint32_t sg[4][NP];
     {
         const uint32_t *sp = (const uint32_t *)(sb + 2 * D + tb * 2 * NB);
@@ -91,29 +94,10 @@ __device__ inline void process_g8(RunState<D> &st, const G8Regs<D> &r, const uin
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int k = 0; k < NP; ++k) sg[i][k] = sp[i * NP + k];
-#pragma unroll
-        for (int k = 0; k < NP; ++k) sg[0][k] = tb == 0 ? 0x00100010u : sg[0][k];   // keyframe row: 2^-20
     }
-    f4 u = f4{0, 0, 0, 0};
-#pragma unroll
-    for (int bb = 0; bb < NB; ++bb) {
-        h8 A0 = unpack8(r.kc[0][bb]);
-        {
-            // token 0 of the group is the keyframe (staged already scaled by f(hh)/16)
-            const u4 k = *(const u4 *)(sb + (j * NB + bb) * 16);
-            u4 a = __builtin_bit_cast(u4, A0);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) a[e] = n == 0 ? k[e] : a[e];
-            A0 = as_h8(a);
-        }
-        const h8 A1 = unpack8(r.kc[1][bb]);
-        f4 P = mfma(A0, as_h8(op.qk[0][(2 * bb) * 64]), f4{0, 0, 0, 0});
-        P = mfma(A0, as_h8(op.qk[0][(2 * bb + 1) * 64]), P);
-        P = mfma(A1, as_h8(op.qk[1][(2 * bb) * 64]), P);
-        P = mfma(A1, as_h8(op.qk[1][(2 * bb + 1) * 64]), P);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) u[i] = __builtin_fmaf(half_at(sg[i], bb), P[i], u[i]);
-    }
+    // C2: the "-8" correction of every delta token, plus the keyframe logit in
+    // row 0: the keyframe (staged scaled by f(hh)/16, read as zeros by lanes
+    // n != 0) times the first half's query operand gives q . x0 directly
     f4 C2;
     {
         u4 a0 = u4{0, 0, 0, 0}, a1 = u4{0, 0, 0, 0};
@@ -129,7 +113,22 @@ __device__ inline void process_g8(RunState<D> &st, const G8Regs<D> &r, const uin
         C2 = mfma(as_h8(a1), as_h8(op.qc[1][0]), C2);
         C2 = mfma(as_h8(a1), as_h8(op.qc[1][64]), C2);
     }
-    float Lg[4];
+    f4 u = f4{0, 0, 0, 0};
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) {
+        const h8 A0 = unpack8(kc[0][bb]);
+        const h8 A1 = unpack8(kc[1][bb]);
+        const h8 bh0 = as_h8(op.qk[0][(2 * bb) * 64]), bl0 = as_h8(op.qk[0][(2 * bb + 1) * 64]);
+        f4 P = mfma(A0, bh0, f4{0, 0, 0, 0});
+        P = mfma(A0, bl0, P);
+        P = mfma(A1, as_h8(op.qk[1][(2 * bb) * 64]), P);
+        P = mfma(A1, as_h8(op.qk[1][(2 * bb + 1) * 64]), P);
+        const h8 K = as_h8(kf_row[bb]);
+        C2 = mfma(K, bh0, C2);
+        C2 = mfma(K, bl0, C2);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) u[i] = __builtin_fmaf(half_at(sg[i], bb), P[i], u[i]);
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const float d = __builtin_fmaf(u[i], 1048576.0f, C2[i]);
@@ -153,9 +152,16 @@ __device__ inline void process_g8(RunState<D> &st, const G8Regs<D> &r, const uin
         if (FULL || tb + i < nval) mx = fmaxf(mx, Lg[i]);
     mx = rows_max(mx);
     mx = fmaxf(mx, other_half(mx));
-    const float m_g = mx * c2E;
+    return mx * c2E;
+}
 
-    // ---- V range bias from the group's largest |scale| (slot 0 of the V scale plane)
+// Softmax state update for a group with maximum m_g: new running max and V
+// range bias (from the group's largest |scale|, slot 0 of the V scale plane);
+// the accumulators are rescaled only when either changes.
+template <int D>
+__device__ inline void update_g8(RunState<D> &st, float m_g, const uint8_t *sb)
+{
+    constexpr int NB = D / 32, NCC = D / 16, NP = NB / 2;
     uint32_t vmx = 0;
     {
         const uint32_t *vs0 = (const uint32_t *)(sb + 6 * D);
@@ -181,8 +187,18 @@ __device__ inline void process_g8(RunState<D> &st, const G8Regs<D> &r, const uin
     }
     st.m = m_new;
     st.beta = beta_new;
+}
 
-    // ---- softmax weights of this lane's tokens and suffix sums over the group
+// V phase of one group: softmax weights of this lane's tokens, suffix sums over
+// the group, the weighted V codes by matrix instructions, and the keyframe.
+template <int D, bool FULL>
+__device__ inline void v_phase_g8(RunState<D> &st, const uint32_t (&vc)[D / 16], const uint8_t *sb,
+                                  const float (&Lg)[4], int nval, int j, int n, float c2E, h8 AZ)
+{
+    constexpr int NB = D / 32, NCC = D / 16, NP = NB / 2;
+    const int h2 = n >> 3;
+    const int tb = 16 * h2 + 4 * j;
+    const float m_new = st.m;
     float S[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -247,7 +263,7 @@ __device__ inline void process_g8(RunState<D> &st, const G8Regs<D> &r, const uin
 #pragma unroll
         for (int c4 = 0; c4 < 4; ++c4) {
             const int cc = 4 * p + c4;
-            const h8 A = unpack8(r.vc[cc]);
+            const h8 A = unpack8(vc[cc]);
             st.acc[cc] = mfma(A, Wh, st.acc[cc]);
             st.acc[cc] = mfma(A, Wl, st.acc[cc]);
         }
@@ -265,6 +281,16 @@ __device__ inline void process_g8(RunState<D> &st, const G8Regs<D> &r, const uin
         st.acc[cc][2] = __builtin_fmaf(hlo(w23), pk, st.acc[cc][2]);
         st.acc[cc][3] = __builtin_fmaf(hhi(w23), pk, st.acc[cc][3]);
     }
+}
+
+template <int D, bool FULL>
+__device__ inline void process_g8(RunState<D> &st, const G8Regs<D> &r, const uint8_t *sb, const u4 *kf_row,
+                                  int nval, int j, int n, const G8Ops &op, float c2E, h8 AZ)
+{
+    float Lg[4];
+    const float m_g = k_phase_g8<D, FULL>(r.kc, sb, kf_row, nval, j, n, op, c2E, Lg);
+    update_g8<D>(st, m_g, sb);
+    v_phase_g8<D, FULL>(st, r.vc, sb, Lg, nval, j, n, c2E, AZ);
 }
 
 template <int D>
@@ -285,7 +311,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
     const int g0 = split * chunk, g1 = min(ng, g0 + chunk);
     const int64_t row0 = (int64_t)b * g.Hq + h * G;
 
-    __shared__ __attribute__((aligned(16))) uint32_t side[2][2 * D];
+    __shared__ __attribute__((aligned(16))) uint32_t side[2 * D];
     __shared__ u4 qk[2 * NB * 64];      // query operand (block, hi/lo) per lane, head hq
     __shared__ u4 qc[2 * 64];           // "-8" correction operand (hi/lo) per lane
     __shared__ u4 qz[2 * NB * 64];      // zeros (operand of the other column half)
@@ -367,16 +393,17 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
     st.l = 0.0f;
     st.beta = 127;
 
-    const LaneOffsets lo = lane_offsets<D>(g, lane, j, n);
+    const LaneOffsets lo = lane_offsets<D>(g, lane, j, n, true);
     const int rec_bytes = (int)g.rec;
-    auto next_mapped = [&](int x, int64_t &o) {
-        for (; x < g1; ++x) {
+    // first mapped group in [x, lim) (paged mode may leave pages unmapped); uniform
+    auto next_mapped = [&](int x, int lim, int64_t &o) {
+        for (; x < lim; ++x) {
             o = group_offset(g, bt, b, h, x);
             if (o >= 0) break;
         }
         return x;
     };
-    auto stage = [&](const G8Regs<D> &r, int bf) {
+    auto stage = [&](const G8Regs<D> &r) {
         if (lane < 2 * SIDE_LANES) {
             u4 v = r.side;
             if (lane < D / 8) {
@@ -384,37 +411,47 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
                 v[0] = scale_h2_16th(w0);
                 v[2] = scale_h2_16th(w2);
             }
-            ((u4 *)side[bf])[fresh_lane_id()] = v;
+            ((u4 *)side)[fresh_lane_id()] = v;
         }
     };
-    auto run = [&](const G8Regs<D> &r, int gcur, int bf) {
+    // keyframe pieces of this lane's K-operand row (lane n == 0), zeros elsewhere
+    const u4 *kf_row = n == 0 ? (const u4 *)((const uint8_t *)side + j * NB * 16) : qz;
+    auto run = [&](const G8Regs<D> &r, int gcur) {
         __syncthreads();
         const int nval = min(32, L - gcur * 32);
-        const uint8_t *sb = (const uint8_t *)side[bf];
         if (nval == 32)
-            process_g8<D, true>(st, r, sb, nval, j, n, op, c2E, AZ);
+            process_g8<D, true>(st, r, (const uint8_t *)side, kf_row, nval, j, n, op, c2E, AZ);
         else
-            process_g8<D, false>(st, r, sb, nval, j, n, op, c2E, AZ);
+            process_g8<D, false>(st, r, (const uint8_t *)side, kf_row, nval, j, n, op, c2E, AZ);
     };
 
-    G8Regs<D> ra, rb;
-    int64_t off = -1, offn = -1;
-    int gi = next_mapped(g0, off);
-    if (gi < g1) load_g8<D>(ra, cache + off, rec_bytes, lo);
-    while (gi < g1) {
-        int gn = next_mapped(gi + 1, offn);
-        stage(ra, 0);
-        load_g8<D>(rb, cache + (gn < g1 ? offn : off), rec_bytes, lo);
-        run(ra, gi, 0);
-        gi = gn;
-        off = offn;
-        if (gi >= g1) break;
-        gn = next_mapped(gi + 1, offn);
-        stage(rb, 1);
-        load_g8<D>(ra, cache + (gn < g1 ? offn : off), rec_bytes, lo);
-        run(rb, gi, 1);
-        gi = gn;
-        off = offn;
+    // Two groups in flight: while group c is processed, groups c+1 and c+2 are
+    // being fetched (three register buffers in rotation).  The side data of the
+    // current group is staged into LDS right before it is processed (one wave per
+    // workgroup: the staging and the reads are ordered by the wave itself).
+    int64_t offc = -1, offn = -1, offp = -1;
+    int gc = next_mapped(g0, g1, offc);
+    if (gc < g1) {
+        G8Regs<D> r0, r1, r2;
+        load_g8<D>(r0, cache + offc, rec_bytes, lo);
+        int gn = next_mapped(gc + 1, g1, offn);
+        load_g8<D>(r1, cache + (gn < g1 ? offn : offc), rec_bytes, lo);
+        auto step = [&](const G8Regs<D> &cur, G8Regs<D> &pf) {
+            const int gp = gn < g1 ? next_mapped(gn + 1, g1, offp) : g1;
+            __syncthreads();
+            stage(cur);
+            // unconditional prefetch keeps the wait counts exact (past the end it
+            // re-reads the current record and the values are unused)
+            load_g8<D>(pf, cache + (gp < g1 ? offp : offc), rec_bytes, lo);
+            run(cur, gc);
+            gc = gn;
+            offc = offn;
+            gn = gp;
+            offn = offp;
+            return gc < g1;
+        };
+        while (step(r0, r2) && step(r1, r0) && step(r2, r1)) {
+        }
     }
 
     // ---------------------------------------------------------------- partials

@@ -112,8 +112,10 @@ struct LaneOffsets {
     int side, k0, k1, v;
 };
 
+// zero_kf_row: the keyframe row (token 0) of the K operand reads past the
+// record (zeros) instead of a dummy code row.
 template <int D>
-__device__ inline LaneOffsets lane_offsets(const Geom &g, int lane, int j, int n)
+__device__ inline LaneOffsets lane_offsets(const Geom &g, int lane, int j, int n, bool zero_kf_row = false)
 {
     constexpr int NB = D / 32, NCC = D / 16, SIDE_LANES = D / 4;
     LaneOffsets o;
@@ -121,7 +123,7 @@ __device__ inline LaneOffsets lane_offsets(const Geom &g, int lane, int j, int n
     o.side = lane < SIDE_LANES ? 16 * lane
            : lane < 2 * SIDE_LANES ? (int)g.off_vkf + 16 * (lane - SIDE_LANES) : 0x40000000;
     const int row0 = n > 0 ? n - 1 : 0;        // token n of tile 0 (token 0 is the keyframe)
-    o.k0 = (int)g.off_kcd + row0 * (D / 2) + 4 * j * NB;
+    o.k0 = (zero_kf_row && n == 0) ? 0x40000000 : (int)g.off_kcd + row0 * (D / 2) + 4 * j * NB;
     o.k1 = (int)g.off_kcd + (15 + n) * (D / 2) + 4 * j * NB;
     o.v = (int)g.off_vcd + (j * 16 + n) * NCC * 4;
     return o;
