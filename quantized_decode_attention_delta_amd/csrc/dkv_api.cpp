@@ -30,6 +30,7 @@ bool fused_long_supported(const dkv_config &);
 hipError_t launch_attn_g8(const dkv_config &, const void *, const int32_t *, const float *, const int32_t *,
                           float, float *, int, int, hipStream_t);
 bool fused_g8_supported(const dkv_config &);
+bool fused_long_g8_supported(const dkv_config &);
 hipError_t launch_q40_encode(const dkv_config &, void *, const uint16_t *, const uint16_t *,
                              const int32_t *, int, hipStream_t);
 hipError_t launch_q40_export(const dkv_config &, const void *, const int32_t *, int, uint8_t *,
@@ -191,7 +192,7 @@ static hipError_t launch_split_phase(const dkv_config &c, const void *cache, con
                                      const int32_t *lens, float scale, void *ws, const Plan &p, hipStream_t st)
 {
     const int32_t *btp = c.page_tokens > 0 ? bt : nullptr;
-    if (fused_g8_supported(c))
+    if (fused_g8_supported(c) || fused_long_g8_supported(c))
         return launch_attn_g8(c, cache, btp, q, lens, resolve_scale(c, scale), (float *)ws, p.nsplit, p.chunk, st);
     if (fused_supported(c))
         return launch_attn_fused(c, cache, btp, q, lens, resolve_scale(c, scale), (float *)ws, p.nsplit, p.chunk,

@@ -34,7 +34,8 @@ namespace dkv {
 
 bool fused_supported(const dkv_config &c)
 {
-    return c.kf == 32 && (c.head_dim == 64 || c.head_dim == 128) && c.n_q_heads / c.n_kv_heads <= 16;
+    return c.kf == 32 && (c.head_dim == 64 || c.head_dim == 128) && c.n_q_heads / c.n_kv_heads <= 16 &&
+           !vbp_layout(c);
 }
 
 // Per-group inputs of the fused kernel, fetched one group ahead.

@@ -381,7 +381,8 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
 bool fused_long_supported(const dkv_config &c)
 {
     const int kf = c.kf;
-    return kf > 32 && kf <= 32 * kMaxTilesLong && kf % 32 == 0 && (c.head_dim == 64 || c.head_dim == 128) &&
+    return !vbp_layout(c) && kf > 32 && kf <= 32 * kMaxTilesLong && kf % 32 == 0 &&
+           (c.head_dim == 64 || c.head_dim == 128) &&
            c.n_q_heads / c.n_kv_heads <= 16;
 }
 

@@ -1,27 +1,30 @@
-// Matrix-core fused decode attention, kf = 32, at most 8 query heads per
-// kv-head (GQA groups of 1..8): the same delta-domain arithmetic as the
-// general 32-token kernel (Delta-KV article, "핵심 아이디어"; attention as in
-// "KV 캐시 벡터 양자화와 주의 보존 변환", "왜 복원 오차가 틀린 기준인가"), laid
-// out so that the 8 operand columns a GQA group of <= 8 heads leaves free do
-// useful work instead of padding.
+// Matrix-core fused decode attention for GQA groups of at most 8 query heads
+// per kv-head: the same delta-domain arithmetic as the general kernels
+// (Delta-KV article, "핵심 아이디어"; attention as in "KV 캐시 벡터 양자화와 주의
+// 보존 변환", "왜 복원 오차가 틀린 기준인가"), laid out so that the 8 operand
+// columns such a group leaves free do useful work instead of padding.
 //
 // Lane = 16*j + n, column n = 8*h2 + hq: column half h2 in {0,1}, head hq.
-//  K side: the two 16-token halves T of the group go to the two column halves.
-//    B operand of half T is the query in columns 8T..8T+7 and zero elsewhere,
-//    so the four matrix instructions of a block (T = 0,1 x hi/lo query)
-//    accumulate into one result whose column half h2 holds the logits of
+//  K side: the two 16-token halves T of a 32-token tile go to the two column
+//    halves.  The query operand of half T sits in columns 8T..8T+7 (zeros
+//    elsewhere), so the four matrix instructions of a block (T = 0,1 x hi/lo
+//    query) accumulate into one result whose column half h2 holds the logits of
 //    tokens 16*h2 + row.  Every per-token step (scales, prefix sums, softmax
 //    weights) then runs on 4 tokens per lane instead of 8.
 //  V side: the V code tile rows are in block-pair order (rows 0..7 from block
-//    p, rows 8..15 from block p + nb/2).  Column half h2 carries the weights
-//    of block p + h2*nb/2, so one B operand serves both blocks of a pair and
-//    every lane forms the weights of one block instead of two; only the
-//    matching (row half, column half) results are kept.
+//    p, rows 8..15 from block p + nb/2).  Column half h2 carries the weights of
+//    block p + h2*nb/2, so one operand serves both blocks of a pair and every
+//    lane forms the weights of one block instead of two; only the matching
+//    (row half, column half) results are kept.
+// Two kernels: kf = 32 (one tile per group, two groups in flight) and
+// kf = 32*NT, NT = 2..16 (a K pass over the tiles keeps the prefix logits in
+// LDS, a V pass runs over them in reverse carrying the suffix sums).
 #include "dkv_fused_common.h"
 
 namespace dkv {
 
-bool fused_g8_supported(const dkv_config &c) { return vbp_layout(c) != 0; }
+bool fused_g8_supported(const dkv_config &c) { return vbp_layout(c) != 0 && c.kf == 32; }
+bool fused_long_g8_supported(const dkv_config &c) { return vbp_layout(c) != 0 && c.kf > 32 && c.kf <= 512; }
 
 // Value of lane n ^ 8 within each row of 16 lanes (DPP row rotate by 8).
 __device__ inline float other_half(float x)
@@ -29,64 +32,108 @@ __device__ inline float other_half(float x)
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x128, 0xF, 0xF, false));
 }
 
+// LDS images of the query-side operands, shared by all groups of a workgroup.
+// Entry e = 8*j + hq of each image holds lane (j, n)'s operand for head hq; a
+// lane of the other column half reads the all-zero image at the same index.
 template <int D>
-struct G8Regs {
-    u4 side;                  // 16 B of the group's side data
-    uint32_t kc[2][D / 32];   // K code pieces of tokens 16T + n (piece j)
-    uint32_t vc[D / 16];      // V code words of tile row n (piece j)
+struct G8Shared {
+    u4 qk[2 * (D / 32) * 32];   // query (block bb, hi/lo) at (2*bb + hl)*32 + e
+    u4 qc[2 * 32];              // "-8" correction operand (hi/lo) at hl*32 + e
+    u4 qz[2 * (D / 32) * 32];   // zeros
 };
 
+// LDS operand addresses of one lane, per token half T.
+struct G8Ops {
+    const u4 *qk[2];   // + (2*bb + hl) * 32
+    const u4 *qc[2];   // + hl * 32
+};
+
+// Query set-up: head hq's query scaled by softmax_scale*log2(e) and by 2^-E
+// (E = exponent of its largest element), split in hi + lo fp16 in the K-code
+// unpack order with the 16/f factors; the "-8" operand -8*sum(q) per block.
+// Returns 2^E.
 template <int D>
-__device__ inline void load_g8(G8Regs<D> &r, const uint8_t *rec, int rec_bytes, const LaneOffsets &o)
+__device__ inline float setup_g8(G8Shared<D> &sh, G8Ops &op, const float *q, int64_t row0, int G, float scale_log2,
+                                 int j, int n)
 {
-    constexpr int NB = D / 32, NCC = D / 16;
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)rec, (short)0, rec_bytes, 0x00020000);
-    r.side = __builtin_amdgcn_raw_buffer_load_b128(rs, o.side, 0, 0);
-    if constexpr (NB == 4) {
-        u4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, o.k0, 0, 0);
-        u4 c = __builtin_amdgcn_raw_buffer_load_b128(rs, o.k1, 0, 0);
+    constexpr int NB = D / 32;
+    const int h2 = n >> 3, hq = n & 7, e = 8 * j + hq;
+    float xq[NB][8];
+    float qm = 0.0f;
+    {
+        const float *qr = q + (row0 + hq) * D;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            r.kc[0][k] = a[k];
-            r.kc[1][k] = c[k];
+        for (int bb = 0; bb < NB; ++bb)
+#pragma unroll
+            for (int hh = 0; hh < 8; ++hh) {
+                const float x = hq < G ? qr[32 * bb + kf_k_channel(j, hh)] * scale_log2 : 0.0f;
+                xq[bb][hh] = x;
+                qm = fmaxf(qm, fabsf(x));
+            }
+    }
+    qm = rows_max(qm);
+    int E = 0;
+    if (qm > 0.0f) frexpf(qm, &E);         // |q'| * 2^-E < 1
+    const float qscale = ldexpf(1.0f, -E);
+    float Qs[NB];
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) {
+        float qsum = 0.0f;
+        h8 Bh, Bl;
+#pragma unroll
+        for (int hh = 0; hh < 8; ++hh) {
+            const bool f16x = ((hh >> 1) & 1) != 0;            // code half carries a factor 16
+            const float x = xq[bb][hh] * qscale * (f16x ? 1.0f : 16.0f);
+            const _Float16 hi = (_Float16)x;
+            const _Float16 lo = (_Float16)(x - (float)hi);
+            Bh[hh] = hi;
+            Bl[hh] = lo;
+            qsum += ((float)hi + (float)lo) * (f16x ? 1.0f : 0.0625f);
         }
-    } else {
-        u2 a = __builtin_amdgcn_raw_buffer_load_b64(rs, o.k0, 0, 0);
-        u2 c = __builtin_amdgcn_raw_buffer_load_b64(rs, o.k1, 0, 0);
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            r.kc[0][k] = a[k];
-            r.kc[1][k] = c[k];
+        float incl, all;
+        rows_prefix(qsum, j, incl, all);
+        Qs[bb] = all;
+        if (h2 == 0) {
+            sh.qk[(2 * bb) * 32 + e] = __builtin_bit_cast(u4, Bh);
+            sh.qk[(2 * bb + 1) * 32 + e] = __builtin_bit_cast(u4, Bl);
+        } else {
+            sh.qz[(2 * bb) * 32 + e] = u4{0, 0, 0, 0};
+            sh.qz[(2 * bb + 1) * 32 + e] = u4{0, 0, 0, 0};
         }
     }
+    if (h2 == 0) {
+        h8 B2h, B2l;
 #pragma unroll
-    for (int q4 = 0; q4 < NCC / 4; ++q4) {
-        u4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, o.v + 16 * q4, 0, 0);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) r.vc[4 * q4 + k] = a[k];
+        for (int hh = 0; hh < 8; ++hh) {
+            const float x = (j == 0 && hh < NB) ? -8.0f * Qs[hh < NB ? hh : 0] : 0.0f;
+            const _Float16 hi = (_Float16)x;
+            B2h[hh] = hi;
+            B2l[hh] = (_Float16)(x - (float)hi);
+        }
+        sh.qc[e] = __builtin_bit_cast(u4, B2h);
+        sh.qc[32 + e] = __builtin_bit_cast(u4, B2l);
     }
+    op.qk[0] = (h2 == 0 ? sh.qk : sh.qz) + e;
+    op.qk[1] = (h2 == 1 ? sh.qk : sh.qz) + e;
+    op.qc[0] = (h2 == 0 ? sh.qc : sh.qz) + e;
+    op.qc[1] = (h2 == 1 ? sh.qc : sh.qz) + e;
+    return ldexpf(1.0f, E);
 }
 
-// LDS operand addresses of one lane: the query (K side) and the "-8"
-// correction operands, per token half T; a lane of the other column half reads
-// an all-zero image instead.
-struct G8Ops {
-    const u4 *qk[2];   // + (2*bb + hl) * 64
-    const u4 *qc[2];   // + hl * 64
-};
-
-// K phase of one group: prefixed logits of this lane's 4 tokens (units q * 2^-E)
-// and the group maximum in log2 units.
-template <int D, bool FULL>
-__device__ inline float k_phase_g8(const uint32_t (&kc)[2][D / 32], const uint8_t *sb, const u4 *kf_row, int nval,
-                                   int j, int n, const G8Ops &op, float c2E, float (&Lg)[4])
+// K phase of one 32-token tile.  sb: the tile's K side data in LDS
+// ([keyframe 2D bytes][scales 2D bytes]); FIRST: the tile opens a group (its
+// token 0 is the keyframe: the code row reads as zeros and the keyframe logit
+// enters through C2).  Lg: prefixed logits of this lane's 4 tokens (units
+// q*2^-E) including `carry` (the sum over earlier tiles of the group); total:
+// this tile's sum.  Returns the tile maximum in log2 units.
+template <int D, bool FULL, bool FIRST>
+__device__ inline float k_phase_g8(const uint32_t *kc, const uint8_t *sb, const u4 *kf_row, int nval, int j, int n,
+                                   const G8Ops &op, float c2E, float carry, float (&Lg)[4], float &total)
 {
     constexpr int NB = D / 32, NP = NB / 2;
     const int h2 = n >> 3;
     const int tb = 16 * h2 + 4 * j;          // first of this lane's 4 tokens
 
-    // ---- K side: delta logits of tokens tb..tb+3 (row 0 of the first half is the
-    // keyframe: its code row reads as zeros, its logit enters through C2 below)
     uint32_t sg[4][NP];
     {
         const uint32_t *sp = (const uint32_t *)(sb + 2 * D + tb * 2 * NB);
@@ -95,9 +142,9 @@ __device__ inline float k_phase_g8(const uint32_t (&kc)[2][D / 32], const uint8_
 #pragma unroll
             for (int k = 0; k < NP; ++k) sg[i][k] = sp[i * NP + k];
     }
-    // C2: the "-8" correction of every delta token, plus the keyframe logit in
-    // row 0: the keyframe (staged scaled by f(hh)/16, read as zeros by lanes
-    // n != 0) times the first half's query operand gives q . x0 directly
+    // C2: the "-8" correction of every delta token (and, in a first tile, the
+    // keyframe logit in row 0: the keyframe, staged scaled by f(hh)/16 and read
+    // as zeros by lanes n != 0, times the first half's query operand)
     f4 C2;
     {
         u4 a0 = u4{0, 0, 0, 0}, a1 = u4{0, 0, 0, 0};
@@ -105,27 +152,29 @@ __device__ inline float k_phase_g8(const uint32_t (&kc)[2][D / 32], const uint8_
         const uint32_t *p1 = (const uint32_t *)(sb + 2 * D + (16 + n) * 2 * NB);
 #pragma unroll
         for (int k = 0; k < NP; ++k) {
-            a0[k] = (j == 0 && n != 0) ? p0[k] : 0u;
+            a0[k] = (j == 0 && (!FIRST || n != 0)) ? p0[k] : 0u;
             a1[k] = j == 0 ? p1[k] : 0u;
         }
         C2 = mfma(as_h8(a0), as_h8(op.qc[0][0]), f4{0, 0, 0, 0});
-        C2 = mfma(as_h8(a0), as_h8(op.qc[0][64]), C2);
+        C2 = mfma(as_h8(a0), as_h8(op.qc[0][32]), C2);
         C2 = mfma(as_h8(a1), as_h8(op.qc[1][0]), C2);
-        C2 = mfma(as_h8(a1), as_h8(op.qc[1][64]), C2);
+        C2 = mfma(as_h8(a1), as_h8(op.qc[1][32]), C2);
     }
     f4 u = f4{0, 0, 0, 0};
 #pragma unroll
     for (int bb = 0; bb < NB; ++bb) {
-        const h8 A0 = unpack8(kc[0][bb]);
-        const h8 A1 = unpack8(kc[1][bb]);
-        const h8 bh0 = as_h8(op.qk[0][(2 * bb) * 64]), bl0 = as_h8(op.qk[0][(2 * bb + 1) * 64]);
+        const h8 A0 = unpack8(kc[bb]);
+        const h8 A1 = unpack8(kc[NB + bb]);
+        const h8 bh0 = as_h8(op.qk[0][(2 * bb) * 32]), bl0 = as_h8(op.qk[0][(2 * bb + 1) * 32]);
         f4 P = mfma(A0, bh0, f4{0, 0, 0, 0});
         P = mfma(A0, bl0, P);
-        P = mfma(A1, as_h8(op.qk[1][(2 * bb) * 64]), P);
-        P = mfma(A1, as_h8(op.qk[1][(2 * bb + 1) * 64]), P);
-        const h8 K = as_h8(kf_row[bb]);
-        C2 = mfma(K, bh0, C2);
-        C2 = mfma(K, bl0, C2);
+        P = mfma(A1, as_h8(op.qk[1][(2 * bb) * 32]), P);
+        P = mfma(A1, as_h8(op.qk[1][(2 * bb + 1) * 32]), P);
+        if constexpr (FIRST) {
+            const h8 K = as_h8(kf_row[bb]);
+            C2 = mfma(K, bh0, C2);
+            C2 = mfma(K, bl0, C2);
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) u[i] = __builtin_fmaf(half_at(sg[i], bb), P[i], u[i]);
     }
@@ -134,15 +183,15 @@ __device__ inline float k_phase_g8(const uint32_t (&kc)[2][D / 32], const uint8_
         const float d = __builtin_fmaf(u[i], 1048576.0f, C2[i]);
         Lg[i] = (FULL || tb + i < nval) ? d : 0.0f;
     }
-
-    // ---- prefix over the group's tokens: in-lane, over rows j, then the first half's total
+    // prefix over the tile's tokens: in-lane, over rows j, then the first half's total
 #pragma unroll
     for (int i = 1; i < 4; ++i) Lg[i] += Lg[i - 1];
     {
         float incl, all;
         rows_prefix(Lg[3], j, incl, all);
         const float allx = other_half(all);           // (every lane takes part in the exchange)
-        const float off = (incl - Lg[3]) + (h2 ? allx : 0.0f);
+        total = all + allx;
+        const float off = (incl - Lg[3]) + (h2 ? allx : 0.0f) + carry;
 #pragma unroll
         for (int i = 0; i < 4; ++i) Lg[i] += off;
     }
@@ -156,23 +205,20 @@ __device__ inline float k_phase_g8(const uint32_t (&kc)[2][D / 32], const uint8_
 }
 
 // Softmax state update for a group with maximum m_g: new running max and V
-// range bias (from the group's largest |scale|, slot 0 of the V scale plane);
-// the accumulators are rescaled only when either changes.
+// range bias from the group's largest |V scale| (slot 0 of the V scale plane,
+// vs0) and kf <= 2^lkf; the accumulators are rescaled only when either changes.
 template <int D>
-__device__ inline void update_g8(RunState<D> &st, float m_g, const uint8_t *sb)
+__device__ inline void update_g8(RunState<D> &st, float m_g, const uint32_t *vs0, int lkf)
 {
     constexpr int NB = D / 32, NCC = D / 16, NP = NB / 2;
     uint32_t vmx = 0;
-    {
-        const uint32_t *vs0 = (const uint32_t *)(sb + 6 * D);
 #pragma unroll
-        for (int k = 0; k < NP; ++k) {
-            const uint32_t w = vs0[k] & 0x7FFF7FFFu;
-            vmx = max(vmx, max(w & 0xFFFFu, w >> 16));
-        }
+    for (int k = 0; k < NP; ++k) {
+        const uint32_t w = vs0[k] & 0x7FFF7FFFu;
+        vmx = max(vmx, max(w & 0xFFFFu, w >> 16));
     }
     const int ev = (vmx >> 10) == 0 ? -14 : (int)(vmx >> 10) - 15;
-    const int beta_g = vmx == 0 ? 19 : 5 - ev;            // 32 * 16 * |s| * 2^beta < 2^15
+    const int beta_g = vmx == 0 ? 24 - lkf : 10 - lkf - ev;       // kf * 16 * |s| * 2^beta < 2^15
 
     const float m_new = fmaxf(st.m, m_g);
     const int beta_new = min(st.beta, beta_g);
@@ -189,11 +235,15 @@ __device__ inline void update_g8(RunState<D> &st, float m_g, const uint8_t *sb)
     st.beta = beta_new;
 }
 
-// V phase of one group: softmax weights of this lane's tokens, suffix sums over
-// the group, the weighted V codes by matrix instructions, and the keyframe.
-template <int D, bool FULL>
-__device__ inline void v_phase_g8(RunState<D> &st, const uint32_t (&vc)[D / 16], const uint8_t *sb,
-                                  const float (&Lg)[4], int nval, int j, int n, float c2E, h8 AZ)
+// V phase of one 32-token tile.  sb: the tile's V side data in LDS ([keyframe
+// 2D bytes][scales 2D bytes]); Lg: the tile's prefixed logits from the K phase;
+// carry: the sum of the softmax weights of the later tiles of the group.
+// Adds the tile's weighted V codes to the accumulators; a FIRST tile (the last
+// one processed) also adds the keyframe with the group's total weight.
+// Returns the tile's weight sum.
+template <int D, bool FULL, bool FIRST>
+__device__ inline float v_phase_g8(RunState<D> &st, const uint32_t *vc, const uint8_t *sb, const float (&Lg)[4],
+                                   int nval, int j, int n, float c2E, h8 AZ, float carry)
 {
     constexpr int NB = D / 32, NCC = D / 16, NP = NB / 2;
     const int h2 = n >> 3;
@@ -207,17 +257,17 @@ __device__ inline void v_phase_g8(RunState<D> &st, const uint32_t (&vc)[D / 16],
     }
 #pragma unroll
     for (int i = 2; i >= 0; --i) S[i] += S[i + 1];
-    float Pg;
+    float Pt;
     {
         float incl, all;
         rows_suffix(S[0], j, incl, all);
         const float allx = other_half(all);
-        Pg = all + allx;
-        const float off = (incl - S[0]) + (h2 ? 0.0f : allx);
+        Pt = all + allx;
+        const float off = (incl - S[0]) + (h2 ? 0.0f : allx) + carry;
 #pragma unroll
         for (int i = 0; i < 4; ++i) S[i] += off;
     }
-    st.l += Pg;
+    st.l += Pt;
 
     // suffix sums of both token halves: own half and the other column half's
     const float bsc = ldexpf(1.0f, st.beta);
@@ -229,15 +279,15 @@ __device__ inline void v_phase_g8(RunState<D> &st, const uint32_t (&vc)[D / 16],
         Sp[0][i] = (h2 ? x : S[i]) * k16;
         Sp[1][i] = (h2 ? S[i] : x) * k16;
     }
-    Sp[0][0] = j == 0 ? 0.0f : Sp[0][0];      // keyframe slot
+    if constexpr (FIRST) Sp[0][0] = j == 0 ? 0.0f : Sp[0][0];      // keyframe slot
 
-    // ---- V: scales of the 8 token slots for this lane's block of each pair
+    // scales of the 8 token slots for this lane's block of each pair
     uint32_t vs[2][4];
     {
         const int wsel = NB == 4 ? h2 : 0;
 #pragma unroll
         for (int T = 0; T < 2; ++T) {
-            const uint32_t *sp = (const uint32_t *)(sb + 6 * D + (16 * T + 4 * j) * 2 * NB) + wsel;
+            const uint32_t *sp = (const uint32_t *)(sb + 2 * D + (16 * T + 4 * j) * 2 * NB) + wsel;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 uint32_t w = sp[i * NP];
@@ -270,16 +320,108 @@ __device__ inline void v_phase_g8(RunState<D> &st, const uint32_t (&vc)[D / 16],
         st.Z[p] = mfma(AZ, Wh, st.Z[p]);
         st.Z[p] = mfma(AZ, Wl, st.Z[p]);
     }
-    // ---- keyframe: acc += P_g * x0 (accumulator units 2^(beta-20))
-    const float pk = Pg * ldexpf(1.0f, st.beta - 20);
-    const uint32_t *kp = (const uint32_t *)(sb + 4 * D + j * NCC * 8);
+    if constexpr (FIRST) {
+        // keyframe: acc += P_group * x0 (accumulator units 2^(beta-20))
+        const float pk = (Pt + carry) * ldexpf(1.0f, st.beta - 20);
+        const uint32_t *kp = (const uint32_t *)(sb + j * NCC * 8);
 #pragma unroll
-    for (int cc = 0; cc < NCC; ++cc) {
-        const uint32_t w01 = kp[2 * cc], w23 = kp[2 * cc + 1];
-        st.acc[cc][0] = __builtin_fmaf(hlo(w01), pk, st.acc[cc][0]);
-        st.acc[cc][1] = __builtin_fmaf(hhi(w01), pk, st.acc[cc][1]);
-        st.acc[cc][2] = __builtin_fmaf(hlo(w23), pk, st.acc[cc][2]);
-        st.acc[cc][3] = __builtin_fmaf(hhi(w23), pk, st.acc[cc][3]);
+        for (int cc = 0; cc < NCC; ++cc) {
+            const uint32_t w01 = kp[2 * cc], w23 = kp[2 * cc + 1];
+            st.acc[cc][0] = __builtin_fmaf(hlo(w01), pk, st.acc[cc][0]);
+            st.acc[cc][1] = __builtin_fmaf(hhi(w01), pk, st.acc[cc][1]);
+            st.acc[cc][2] = __builtin_fmaf(hlo(w23), pk, st.acc[cc][2]);
+            st.acc[cc][3] = __builtin_fmaf(hhi(w23), pk, st.acc[cc][3]);
+        }
+    }
+    return Pt;
+}
+
+template <int D>
+__device__ inline void init_state(RunState<D> &st)
+{
+#pragma unroll
+    for (int cc = 0; cc < D / 16; ++cc) st.acc[cc] = f4{0, 0, 0, 0};
+#pragma unroll
+    for (int p = 0; p < D / 32; ++p) st.Z[p] = f4{0, 0, 0, 0};
+    st.m = -INFINITY;
+    st.l = 0.0f;
+    st.beta = 127;
+}
+
+// Split-K partial record of the wave's run: lane (j, n) keeps rows 4j..4j+3
+// of each V slice; they belong to its column half's block when
+// (j < 2) == (h2 == 0).
+template <int D>
+__device__ inline void write_partial_g8(const RunState<D> &st, float *ws, int64_t row0, int G, int nsplit, int split,
+                                        int lane, int j, int n)
+{
+    constexpr int NCC = D / 16;
+    const int h2 = n >> 3, hq = n & 7;
+    if (hq >= G) return;
+    float *recp = ws + ((row0 + hq) * nsplit + split) * part_stride(D);
+    const float un = ldexpf(1.0f, 20 - st.beta);
+    if ((j < 2) == (h2 == 0)) {
+#pragma unroll
+        for (int cc = 0; cc < NCC; ++cc) {
+            f4 o;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] = (st.acc[cc][i] + st.Z[cc >> 2][i]) * un;
+            *(f4 *)(recp + vchan(D, cc, 4 * j, 1)) = o;
+        }
+    }
+    if (lane == hq) {
+        recp[D] = st.m;
+        recp[D + 1] = st.l;
+    }
+}
+
+// "-8" operand of the V side: -8 * 2^-24 * f(hh) as fp16 subnormals
+__device__ inline h8 v_minus8_operand()
+{
+    u4 azr;
+    azr[0] = 0x80088008u;
+    azr[1] = 0x80808080u;
+    azr[2] = 0x80088008u;
+    azr[3] = 0x80808080u;
+    return as_h8(azr);
+}
+
+// ============================================================================ kf = 32
+template <int D>
+struct G8Regs {
+    u4 side;                     // 16 B of the group's side data
+    uint32_t kc[2 * (D / 32)];   // K code pieces of tokens n (first NB) and 16 + n (piece j)
+    uint32_t vc[D / 16];         // V code words of tile row n (piece j)
+};
+
+template <int D>
+__device__ inline void load_g8(G8Regs<D> &r, const uint8_t *rec, int rec_bytes, const LaneOffsets &o)
+{
+    constexpr int NB = D / 32, NCC = D / 16;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)rec, (short)0, rec_bytes, 0x00020000);
+    r.side = __builtin_amdgcn_raw_buffer_load_b128(rs, o.side, 0, 0);
+    if constexpr (NB == 4) {
+        u4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, o.k0, 0, 0);
+        u4 c = __builtin_amdgcn_raw_buffer_load_b128(rs, o.k1, 0, 0);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            r.kc[k] = a[k];
+            r.kc[NB + k] = c[k];
+        }
+    } else {
+        u2 a = __builtin_amdgcn_raw_buffer_load_b64(rs, o.k0, 0, 0);
+        u2 c = __builtin_amdgcn_raw_buffer_load_b64(rs, o.k1, 0, 0);
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            r.kc[k] = a[k];
+            r.kc[NB + k] = c[k];
+        }
+    }
+#pragma unroll
+    for (int q4 = 0; q4 < NCC / 4; ++q4) {
+        u4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, o.v + 16 * q4, 0, 0);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) r.vc[4 * q4 + k] = a[k];
     }
 }
 
@@ -287,10 +429,10 @@ template <int D, bool FULL>
 __device__ inline void process_g8(RunState<D> &st, const G8Regs<D> &r, const uint8_t *sb, const u4 *kf_row,
                                   int nval, int j, int n, const G8Ops &op, float c2E, h8 AZ)
 {
-    float Lg[4];
-    const float m_g = k_phase_g8<D, FULL>(r.kc, sb, kf_row, nval, j, n, op, c2E, Lg);
-    update_g8<D>(st, m_g, sb);
-    v_phase_g8<D, FULL>(st, r.vc, sb, Lg, nval, j, n, c2E, AZ);
+    float Lg[4], tot;
+    const float m_g = k_phase_g8<D, FULL, true>(r.kc, sb, kf_row, nval, j, n, op, c2E, 0.0f, Lg, tot);
+    update_g8<D>(st, m_g, (const uint32_t *)(sb + 6 * D), 5);
+    v_phase_g8<D, FULL, true>(st, r.vc, sb + 4 * D, Lg, nval, j, n, c2E, AZ, 0.0f);
 }
 
 template <int D>
@@ -299,99 +441,27 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
               const float *__restrict__ q, const int32_t *__restrict__ seq_lens, float scale_log2,
               float *__restrict__ ws, int nsplit, int chunk)
 {
-    constexpr int NB = D / 32, NCC = D / 16, NP = NB / 2;
+    constexpr int NB = D / 32;
     constexpr int SIDE_LANES = D / 4;
     const Geom g = make_geom(cfg);
     const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int lane = threadIdx.x, j = lane >> 4, n = lane & 15;
-    const int h2 = n >> 3, hq = n & 7;
     const int G = g.G;
     const int L = min(seq_lens[b], g.cap_tokens);
     const int ng = (L + 31) >> 5;
     const int g0 = split * chunk, g1 = min(ng, g0 + chunk);
     const int64_t row0 = (int64_t)b * g.Hq + h * G;
 
+    // [K keyframe][K scales][V keyframe][V scales] of the current group, 2*D bytes each
     __shared__ __attribute__((aligned(16))) uint32_t side[2 * D];
-    __shared__ u4 qk[2 * NB * 64];      // query operand (block, hi/lo) per lane, head hq
-    __shared__ u4 qc[2 * 64];           // "-8" correction operand (hi/lo) per lane
-    __shared__ u4 qz[2 * NB * 64];      // zeros (operand of the other column half)
-
-    // ---------------------------------------------------------------- query
-    // lane (j, n) holds head hq's channels 32*bb + kf_k_channel(j, hh), scaled by softmax_scale*log2(e)
-    float xq[NB][8];
-    float qm = 0.0f;
-    {
-        const float *qr = q + (row0 + hq) * D;
-#pragma unroll
-        for (int bb = 0; bb < NB; ++bb)
-#pragma unroll
-            for (int hh = 0; hh < 8; ++hh) {
-                const float x = hq < G ? qr[32 * bb + kf_k_channel(j, hh)] * scale_log2 : 0.0f;
-                xq[bb][hh] = x;
-                qm = fmaxf(qm, fabsf(x));
-            }
-    }
-    qm = rows_max(qm);
-    int E = 0;
-    if (qm > 0.0f) frexpf(qm, &E);         // |q'| * 2^-E < 1
-    const float qscale = ldexpf(1.0f, -E);
-    const float c2E = ldexpf(1.0f, E);
-    float Qs[NB];
-#pragma unroll
-    for (int bb = 0; bb < NB; ++bb) {
-        float qsum = 0.0f;
-        h8 Bh, Bl;
-#pragma unroll
-        for (int hh = 0; hh < 8; ++hh) {
-            const bool f16x = ((hh >> 1) & 1) != 0;            // code half carries a factor 16
-            const float x = xq[bb][hh] * qscale * (f16x ? 1.0f : 16.0f);
-            const _Float16 hi = (_Float16)x;
-            const _Float16 lo = (_Float16)(x - (float)hi);
-            Bh[hh] = hi;
-            Bl[hh] = lo;
-            qsum += ((float)hi + (float)lo) * (f16x ? 1.0f : 0.0625f);
-        }
-        float incl, all;
-        rows_prefix(qsum, j, incl, all);
-        Qs[bb] = all;
-        qk[(2 * bb) * 64 + lane] = __builtin_bit_cast(u4, Bh);
-        qk[(2 * bb + 1) * 64 + lane] = __builtin_bit_cast(u4, Bl);
-        qz[(2 * bb) * 64 + lane] = u4{0, 0, 0, 0};
-        qz[(2 * bb + 1) * 64 + lane] = u4{0, 0, 0, 0};
-    }
-    {
-        h8 B2h, B2l;
-#pragma unroll
-        for (int hh = 0; hh < 8; ++hh) {
-            const float x = (j == 0 && hh < NB) ? -8.0f * Qs[hh < NB ? hh : 0] : 0.0f;
-            const _Float16 hi = (_Float16)x;
-            B2h[hh] = hi;
-            B2l[hh] = (_Float16)(x - (float)hi);
-        }
-        qc[lane] = __builtin_bit_cast(u4, B2h);
-        qc[64 + lane] = __builtin_bit_cast(u4, B2l);
-    }
-    u4 azr;
-    azr[0] = 0x80088008u;
-    azr[1] = 0x80808080u;
-    azr[2] = 0x80088008u;
-    azr[3] = 0x80808080u;
-    const h8 AZ = as_h8(azr);
+    __shared__ G8Shared<D> sh;
 
     G8Ops op;
-    op.qk[0] = (h2 == 0 ? qk : qz) + lane;
-    op.qk[1] = (h2 == 1 ? qk : qz) + lane;
-    op.qc[0] = (h2 == 0 ? qc : qz) + lane;
-    op.qc[1] = (h2 == 1 ? qc : qz) + lane;
+    const float c2E = setup_g8<D>(sh, op, q, row0, G, scale_log2, j, n);
+    const h8 AZ = v_minus8_operand();
 
     RunState<D> st;
-#pragma unroll
-    for (int cc = 0; cc < NCC; ++cc) st.acc[cc] = f4{0, 0, 0, 0};
-#pragma unroll
-    for (int p = 0; p < NB; ++p) st.Z[p] = f4{0, 0, 0, 0};
-    st.m = -INFINITY;
-    st.l = 0.0f;
-    st.beta = 127;
+    init_state<D>(st);
 
     const LaneOffsets lo = lane_offsets<D>(g, lane, j, n, true);
     const int rec_bytes = (int)g.rec;
@@ -407,6 +477,8 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
         if (lane < 2 * SIDE_LANES) {
             u4 v = r.side;
             if (lane < D / 8) {
+                // K keyframe scaled by f(hh)/16 for the K operand (scalar temporaries:
+                // bit_cast of a vector element lvalue is miscompiled)
                 const uint32_t w0 = v[0], w2 = v[2];
                 v[0] = scale_h2_16th(w0);
                 v[2] = scale_h2_16th(w2);
@@ -415,7 +487,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
         }
     };
     // keyframe pieces of this lane's K-operand row (lane n == 0), zeros elsewhere
-    const u4 *kf_row = n == 0 ? (const u4 *)((const uint8_t *)side + j * NB * 16) : qz;
+    const u4 *kf_row = n == 0 ? (const u4 *)((const uint8_t *)side + j * NB * 16) : sh.qz;
     auto run = [&](const G8Regs<D> &r, int gcur) {
         __syncthreads();
         const int nval = min(32, L - gcur * 32);
@@ -453,39 +525,215 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
         while (step(r0, r2) && step(r1, r0) && step(r2, r1)) {
         }
     }
+    write_partial_g8<D>(st, ws, row0, G, nsplit, split, lane, j, n);
+}
 
-    // ---------------------------------------------------------------- partials
-    // lane (j, n) keeps rows 4j..4j+3 of each slice; they belong to its column
-    // half's block when (j < 2) == (h2 == 0)
-    if (hq < G) {
-        float *recp = ws + ((row0 + hq) * nsplit + split) * part_stride(D);
-        const float un = ldexpf(1.0f, 20 - st.beta);
-        if ((j < 2) == (h2 == 0)) {
+// ==================================================================== kf = 32*NT
+// One step = one 32-token tile of one pass: the K pass visits tiles 0..nt-1 of
+// a group, the V pass tiles nt-1..0.  The registers of the next step are
+// fetched while the current one is processed.
+template <int D>
+struct TileRegs {
+    u4 side;                  // 16 B of the tile's side data (keyframe / scales / V slot 0)
+    uint32_t code[D / 16];    // K: pieces of rows n and 16 + n (NB words each); V: the lane's tile words
+};
+
+template <int D>
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
+    k_attn_long_g8(dkv_config cfg, const uint8_t *__restrict__ cache, const int32_t *__restrict__ bt,
+                   const float *__restrict__ q, const int32_t *__restrict__ seq_lens, float scale_log2,
+                   float *__restrict__ ws, int nsplit, int chunk)
+{
+    constexpr int NB = D / 32, NCC = D / 16;
+    const Geom g = make_geom(cfg);
+    const int kf = g.kf;
+    const int lkf = 32 - __builtin_clz((unsigned)kf - 1u);       // kf <= 2^lkf
+    const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int lane = threadIdx.x, j = lane >> 4, n = lane & 15;
+    const int G = g.G;
+    const int L = min(seq_lens[b], g.cap_tokens);
+    const int ng = (L + kf - 1) / kf;
+    const int g0 = split * chunk, g1 = min(ng, g0 + chunk);
+    const int64_t row0 = (int64_t)b * g.Hq + h * G;
+
+    // side: [keyframe 2D bytes][scales of the tile 2D bytes] of the current step;
+    // vslot0: slot 0 (max |scale|) of the group's V scale plane
+    __shared__ __attribute__((aligned(16))) uint32_t side[D];
+    __shared__ __attribute__((aligned(16))) uint32_t vslot0[4];
+    __shared__ G8Shared<D> sh;
+    extern __shared__ f4 lgs[];               // prefixed logits [tile][lane] of the current group
+
+    G8Ops op;
+    const float c2E = setup_g8<D>(sh, op, q, row0, G, scale_log2, j, n);
+    const h8 AZ = v_minus8_operand();
+
+    RunState<D> st;
+    init_state<D>(st);
+
+    const int rec_bytes = (int)g.rec;
+    auto next_mapped = [&](int x, int64_t &o) {
+        for (; x < g1; ++x) {
+            o = group_offset(g, bt, b, h, x);
+            if (o >= 0) break;
+        }
+        return x;
+    };
+    auto ntiles = [&](int gi) { return (min(kf, L - gi * kf) + 31) >> 5; };
+    // step s of a group with nt tiles: s < nt -> K tile s, else V tile 2*nt-1-s.
+    // Every step issues the same three loads (side data, two code pieces of NB
+    // words); only the offsets differ, so the wait counts stay exact.
+    auto load_step = [&](TileRegs<D> &r, int64_t off, int s, int nt) {
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc((void *)(cache + off), (short)0, rec_bytes, 0x00020000);
+        const bool kp = s < nt;
+        const int t = kp ? s : 2 * nt - 1 - s;
+        // side: lanes < D/8 the keyframe, D/8..D/4 the tile's scales, lane D/4 (K pass) V slot 0
+        int so;
+        if (lane < D / 8)
+            so = (kp ? 0 : (int)g.off_vkf) + 16 * lane;
+        else if (lane < D / 4)
+            so = (int)(kp ? g.off_ksc : g.off_vsc) + 64 * NB * t + 16 * (lane - D / 8);
+        else
+            so = (kp && lane == D / 4) ? (int)g.off_vsc : 0x40000000;
+        // K: token 32t + n is code row 32t + n - 1 (the keyframe row of tile 0 reads
+        // as zeros), token 32t + 16 + n row 32t + 15 + n.  V: the lane's 2*NB tile words.
+        const int ov = (int)g.off_vcd + 16 * D * t + (j * 16 + n) * NCC * 4;
+        const int o0 = kp ? ((t == 0 && n == 0) ? 0x40000000 : (int)g.off_kcd + (32 * t + n - 1) * (D / 2) + 4 * j * NB)
+                          : ov;
+        const int o1 = kp ? (int)g.off_kcd + (32 * t + 15 + n) * (D / 2) + 4 * j * NB : ov + 4 * NB;
+        r.side = __builtin_amdgcn_raw_buffer_load_b128(rs, so, 0, 0);
+        if constexpr (NB == 4) {
+            const u4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, o0, 0, 0);
+            const u4 c = __builtin_amdgcn_raw_buffer_load_b128(rs, o1, 0, 0);
 #pragma unroll
-            for (int cc = 0; cc < NCC; ++cc) {
-                f4 o;
+            for (int k = 0; k < 4; ++k) {
+                r.code[k] = a[k];
+                r.code[4 + k] = c[k];
+            }
+        } else {
+            const u2 a = __builtin_amdgcn_raw_buffer_load_b64(rs, o0, 0, 0);
+            const u2 c = __builtin_amdgcn_raw_buffer_load_b64(rs, o1, 0, 0);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) o[i] = (st.acc[cc][i] + st.Z[cc >> 2][i]) * un;
-                *(f4 *)(recp + vchan(D, cc, 4 * j, 1)) = o;
+            for (int k = 0; k < 2; ++k) {
+                r.code[k] = a[k];
+                r.code[2 + k] = c[k];
             }
         }
-        if (lane == hq) {
-            recp[D] = st.m;
-            recp[D + 1] = st.l;
+    };
+    auto stage = [&](const TileRegs<D> &r, bool kpass) {
+        u4 v = r.side;
+        if (kpass && lane < D / 8) {
+            const uint32_t w0 = v[0], w2 = v[2];
+            v[0] = scale_h2_16th(w0);
+            v[2] = scale_h2_16th(w2);
+        }
+        if (lane < D / 4) ((u4 *)side)[fresh_lane_id()] = v;
+        if (kpass && lane == D / 4) *(u4 *)vslot0 = v;
+    };
+    const u4 *kf_row = n == 0 ? (const u4 *)((const uint8_t *)side + j * NB * 16) : sh.qz;
+
+    float carry = 0.0f, mx = -INFINITY;       // per-group pass state
+    int64_t offc = -1, offn = -1;
+    int gc = next_mapped(g0, offc);
+    if (gc < g1) {
+        int ntc = ntiles(gc), s = 0;
+        // the step after (gc, s): the same group, or K tile 0 of the next mapped group
+        int gn = gc, sn = 1, ntn = ntc;
+        offn = offc;
+        auto advance = [&]() {
+            if (sn < 2 * ntn) return;
+            gn = next_mapped(gn + 1, offn);
+            sn = 0;
+            ntn = gn < g1 ? ntiles(gn) : 1;
+        };
+        advance();
+        TileRegs<D> ra, rb;
+        load_step(ra, offc, 0, ntc);
+        auto step = [&](const TileRegs<D> &cur, TileRegs<D> &pf) {
+            __syncthreads();
+            const bool kp = s < ntc;
+            const int t = kp ? s : 2 * ntc - 1 - s;
+            const int nval = min(kf, L - gc * kf) - 32 * t;     // valid tokens from the tile start
+            stage(cur, kp);
+            // prefetch the following step (past the end: the current step again)
+            const bool more = gn < g1;
+            load_step(pf, more ? offn : offc, more ? sn : s, more ? ntn : ntc);
+            __syncthreads();
+            const uint8_t *sb = (const uint8_t *)side;
+            if (kp) {
+                float Lg[4], tot, m;
+                if (t == 0) {
+                    carry = 0.0f;
+                    if (nval >= 32)
+                        m = k_phase_g8<D, true, true>(cur.code, sb, kf_row, nval, j, n, op, c2E, carry, Lg, tot);
+                    else
+                        m = k_phase_g8<D, false, true>(cur.code, sb, kf_row, nval, j, n, op, c2E, carry, Lg, tot);
+                    mx = m;
+                } else {
+                    if (nval >= 32)
+                        m = k_phase_g8<D, true, false>(cur.code, sb, kf_row, nval, j, n, op, c2E, carry, Lg, tot);
+                    else
+                        m = k_phase_g8<D, false, false>(cur.code, sb, kf_row, nval, j, n, op, c2E, carry, Lg, tot);
+                    mx = fmaxf(mx, m);
+                }
+                carry += tot;
+                lgs[t * 64 + lane] = f4{Lg[0], Lg[1], Lg[2], Lg[3]};
+                if (t == ntc - 1) {
+                    update_g8<D>(st, mx, vslot0, lkf);
+                    carry = 0.0f;            // from here on: the suffix carry of the V pass
+                }
+            } else {
+                const f4 lv = lgs[t * 64 + lane];
+                const float Lg[4] = {lv[0], lv[1], lv[2], lv[3]};
+                float pt;
+                if (t == 0) {
+                    if (nval >= 32)
+                        pt = v_phase_g8<D, true, true>(st, cur.code, sb, Lg, nval, j, n, c2E, AZ, carry);
+                    else
+                        pt = v_phase_g8<D, false, true>(st, cur.code, sb, Lg, nval, j, n, c2E, AZ, carry);
+                } else {
+                    if (nval >= 32)
+                        pt = v_phase_g8<D, true, false>(st, cur.code, sb, Lg, nval, j, n, c2E, AZ, carry);
+                    else
+                        pt = v_phase_g8<D, false, false>(st, cur.code, sb, Lg, nval, j, n, c2E, AZ, carry);
+                }
+                carry += pt;
+            }
+            // move to the next step
+            gc = gn;
+            offc = offn;
+            s = sn;
+            ntc = ntn;
+            ++sn;
+            advance();
+            return gc < g1;
+        };
+        while (step(ra, rb) && step(rb, ra)) {
         }
     }
+    write_partial_g8<D>(st, ws, row0, G, nsplit, split, lane, j, n);
 }
 
 hipError_t launch_attn_g8(const dkv_config &c, const void *cache, const int32_t *bt, const float *q,
                           const int32_t *lens, float scale_log2, float *ws, int nsplit, int chunk, hipStream_t st)
 {
     dim3 grid(nsplit, c.n_kv_heads, c.batch);
-    if (c.head_dim == 64)
-        hipLaunchKernelGGL(k_attn_g8<64>, grid, dim3(64), 0, st, c, (const uint8_t *)cache, bt, q, lens, scale_log2,
-                           ws, nsplit, chunk);
-    else
-        hipLaunchKernelGGL(k_attn_g8<128>, grid, dim3(64), 0, st, c, (const uint8_t *)cache, bt, q, lens, scale_log2,
-                           ws, nsplit, chunk);
+    if (c.kf == 32) {
+        if (c.head_dim == 64)
+            hipLaunchKernelGGL(k_attn_g8<64>, grid, dim3(64), 0, st, c, (const uint8_t *)cache, bt, q, lens,
+                               scale_log2, ws, nsplit, chunk);
+        else
+            hipLaunchKernelGGL(k_attn_g8<128>, grid, dim3(64), 0, st, c, (const uint8_t *)cache, bt, q, lens,
+                               scale_log2, ws, nsplit, chunk);
+    } else {
+        const size_t lds = (size_t)((c.kf + 31) / 32) * 64 * sizeof(f4);
+        if (c.head_dim == 64)
+            hipLaunchKernelGGL(k_attn_long_g8<64>, grid, dim3(64), lds, st, c, (const uint8_t *)cache, bt, q, lens,
+                               scale_log2, ws, nsplit, chunk);
+        else
+            hipLaunchKernelGGL(k_attn_long_g8<128>, grid, dim3(64), lds, st, c, (const uint8_t *)cache, bt, q, lens,
+                               scale_log2, ws, nsplit, chunk);
+    }
     return hipGetLastError();
 }
 

@@ -47,11 +47,13 @@ struct Geom {
 };
 
 // V code tiles use the block-pair row order when at most 8 query heads share
-// a kv-head (the matrix-core kernel then spends the 8 spare operand columns
-// on the second block of a pair) and kf = 32.
+// a kv-head (the matrix-core kernels then spend the 8 spare operand columns
+// on the second block of a pair), kf is a multiple of 32 up to 512 and D is
+// 64 or 128.
 __host__ __device__ inline int vbp_layout(const dkv_config &c)
 {
-    return c.kf == 32 && c.n_q_heads / c.n_kv_heads <= 8 && (c.head_dim == 64 || c.head_dim == 128);
+    return c.kf % 32 == 0 && c.kf <= 512 && c.n_q_heads / c.n_kv_heads <= 8 &&
+           (c.head_dim == 64 || c.head_dim == 128);
 }
 
 __host__ __device__ inline Geom make_geom(const dkv_config &c)
