@@ -77,7 +77,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="70b", choices=["tiny", "8b", "long", "70b"])
+    ap.add_argument("--workload", default="70b", choices=["tiny", "8b", "long", "70b", "mixed"])
+    ap.add_argument("--mixed-batch", type=int, default=None, help="mixed workload: fewer sequences (default 64)")
+    ap.add_argument("--mixed-max-len", type=int, default=None, help="mixed workload: shorter maximum length")
     ap.add_argument("--kf", type=int, default=None)
     ap.add_argument("--kernel", default="fused", choices=["fused", "ref"])
     ap.add_argument("--replicas", type=int, default=0, help="cache copies rotated per step (0 = auto, >= 1 GiB)")
@@ -208,6 +210,135 @@ def quality(w, cfg, cache, q4, k, v, lens):
             "mse_delta_kv_kv": mse_d, "mse_q4_0_kv": mse_q}
 
 
+def run_mixed(args):
+    """Serving loop of the mixed workload: paged cache (256-token pages, shuffled
+    physical ids), bulk prefill, then per step one appended token per sequence
+    followed by decode attention over the grown cache.  A step = append + decode
+    of one layer; the timed steps follow the warm-up steps."""
+    import numpy as np
+    import torch
+
+    import quantized_decode_attention_delta_amd as dkv
+    from quantized_decode_attention_delta_amd import synth
+
+    dev = torch.device("cuda:0")
+    over = {}
+    if args.mixed_batch:
+        over["B"] = args.mixed_batch
+    if args.mixed_max_len:
+        over["S"] = args.mixed_max_len
+    t_gen = time.time()
+
+    def progress(b):
+        if b % 8 == 7:
+            print(f"# generated {b + 1} sequences ({time.time() - t_gen:.0f} s)", file=sys.stderr, flush=True)
+
+    w = synth.make("mixed", progress=progress, **over)
+    nsteps = w.extra_tokens
+    if args.warmup + args.steps > nsteps:
+        sys.exit(f"bench.py: mixed workload has {nsteps} append+decode steps; warmup + steps must not exceed it")
+    print(f"# workload mixed: B={w.B} Hq={w.Hq} Hkv={w.Hkv} D={w.D} L in [{int(w.seq_lens.min())}, "
+          f"{int(w.seq_lens.max())}] pages {w.page_tokens} kf={w.kf} (generated in {time.time() - t_gen:.1f} s)",
+          file=sys.stderr, flush=True)
+    table, n_pages = synth.page_table(w)
+    cfg = dkv.Config(batch=w.B, n_q_heads=w.Hq, n_kv_heads=w.Hkv, head_dim=w.D, kf=w.kf,
+                     page_tokens=w.page_tokens, n_pages=n_pages, max_pages_per_seq=table.shape[1])
+    lens0 = w.seq_lens.astype(np.int32)
+    # the appended tokens of every step: [step][B][Hkv][D]
+    kn = np.empty((nsteps, w.B, w.Hkv, w.D), np.float16)
+    vn = np.empty_like(kn)
+    for b in range(w.B):
+        sl = slice(int(lens0[b]), int(lens0[b]) + nsteps)
+        kn[:, b] = w.k[b, :, sl].transpose(1, 0, 2)
+        vn[:, b] = w.v[b, :, sl].transpose(1, 0, 2)
+    cache = torch.empty(dkv.dkv_cache_bytes(cfg), dtype=torch.uint8, device=dev)
+    state = torch.zeros(w.B, w.Hkv, 2, w.D, dtype=torch.float32, device=dev)
+    bt = torch.from_numpy(table).to(dev)
+    lens = torch.from_numpy(lens0).to(dev)
+    k = torch.from_numpy(w.k).to(dev)
+    v = torch.from_numpy(w.v).to(dev)
+    dkv.dkv_encode_prefill(cfg, cache, state, bt, k, v, lens, w.k.shape[2])
+    torch.cuda.synchronize()
+    del k, v
+    w.k = w.v = None
+    kn_t = torch.from_numpy(kn).to(dev)
+    vn_t = torch.from_numpy(vn).to(dev)
+    pos = torch.from_numpy(lens0[None, :] + np.arange(nsteps, dtype=np.int32)[:, None]).to(dev)   # [step][B]
+    lens_after = pos + 1
+    q = torch.from_numpy(np.stack([synth.queries(w, s) for s in range(nsteps)])).to(dev)
+    out = torch.empty(w.B, w.Hq, w.D, dtype=torch.float32, device=dev)
+    ws = torch.zeros(dkv.dkv_workspace_bytes(cfg), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(s):
+        dkv.dkv_append(cfg, cache, state, bt, kn_t[s], vn_t[s], pos[s])
+        dkv.dkv_attn_decode(cfg, cache, bt, q[s], lens_after[s], out, ws)
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for s in range(args.warmup, args.warmup + args.steps):
+        step(s)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+
+    # the decode kernel alone on the final cache (timed per launch), and the append alone
+    last = args.warmup + args.steps - 1
+    n_k = max(10, args.steps)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_k)]
+    for i in range(n_k):
+        evs[i][0].record(stream)
+        dkv.dkv_attn_decode_partial(cfg, cache, bt, q[last], lens_after[last], ws)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    Lf = lens0 + last + 1                                    # lengths during the last timed decode
+    Lt = [lens0 + s + 1 for s in range(args.warmup, args.warmup + args.steps)]
+    comp_last = sum(algorithmic_bytes(1, w.Hkv, w.Hq, w.D, int(L), w.kf) for L in Lf)
+    comp_avg = float(np.mean([sum(algorithmic_bytes(1, w.Hkv, w.Hq, w.D, int(L), w.kf) for L in x) for x in Lt]))
+    eff_avg = float(np.mean([int(x.sum()) * w.Hkv * w.D * 2 * 2 for x in Lt]))
+    qo = w.B * w.Hq * w.D * 4 * 2
+    achieved = (comp_last + qo) / (kern_ms * 1e-3) / 1e9
+    res = {
+        "metric": METRIC,
+        "value": round(eff_avg / (ms_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"mixed: B={w.B} Hq={w.Hq} Hkv={w.Hkv} D={w.D} L~U[{int(w.seq_lens.min())}..] "
+                        f"max {w.S}, {w.page_tokens}-token pages (shuffled), kf={w.kf}, step = append + decode",
+            "kernel": "fused",
+        },
+        "layer_steps_per_s": round(1000.0 / ms_step, 2),
+        "compressed_GBps": round((comp_avg + qo) / (ms_step * 1e-3) / 1e9, 2),
+        "hbm_frac_step": round((comp_avg + qo) / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+            "kernel_ms": round(kern_ms, 5),
+            "algorithmic_bytes": comp_last + qo,
+        },
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -221,6 +352,8 @@ def main():
     from quantized_decode_attention_delta_amd import synth
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.workload == "mixed":
+        return run_mixed(args)
     dev = torch.device("cuda:0")
     if args.copy_calibration:
         src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)

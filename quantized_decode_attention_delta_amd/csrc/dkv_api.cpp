@@ -41,11 +41,14 @@ hipError_t launch_attn_f16(const dkv_config &, const uint16_t *, const uint16_t 
                            const int32_t *, float, float *, int, int, hipStream_t);
 
 // Split plan: runs of whole units (groups, or 32-token tiles) per workgroup,
-// sized for about 2048 workgroups over the batch.
+// sized for about 2048 workgroups over the batch, and at most max_units
+// (about 2048 tokens) per run so that ragged batches, where the capacity is far
+// above most sequences' lengths, stay balanced: runs past a sequence's end exit
+// at once and the combine skips their empty partial records.
 struct Plan {
     int nsplit, chunk;
 };
-static Plan make_plan(int units_cap, int B, int Hkv)
+static Plan make_plan(int units_cap, int B, int Hkv, int max_units)
 {
     Plan p;
     const int64_t pairs = (int64_t)B * Hkv;
@@ -54,6 +57,7 @@ static Plan make_plan(int units_cap, int B, int Hkv)
     if (ns > units_cap) ns = units_cap;
     if (ns < 1) ns = 1;
     p.chunk = (int)((units_cap + ns - 1) / ns);
+    if (p.chunk > max_units) p.chunk = max_units;
     if (p.chunk < 1) p.chunk = 1;
     p.nsplit = (units_cap + p.chunk - 1) / p.chunk;
     if (p.nsplit < 1) p.nsplit = 1;
@@ -62,12 +66,12 @@ static Plan make_plan(int units_cap, int B, int Hkv)
 Plan delta_plan(const dkv_config &c)
 {
     const Geom g = make_geom(c);
-    return make_plan(g.ng_cap, c.batch, c.n_kv_heads);
+    return make_plan(g.ng_cap, c.batch, c.n_kv_heads, c.kf >= 2048 ? 1 : 2048 / c.kf);
 }
 Plan tile_plan(const dkv_config &c)
 {
     const int tiles = (c.max_tokens + 31) / 32;
-    return make_plan(tiles, c.batch, c.n_kv_heads);
+    return make_plan(tiles, c.batch, c.n_kv_heads, 64);
 }
 static size_t ws_for(const dkv_config &c, const Plan &p)
 {

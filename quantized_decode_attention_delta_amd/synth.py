@@ -96,8 +96,9 @@ def _ar1_stream_block(rng, T, H, D, sigma, scales, jump_p=0.0, jump_sigma=0.0):
     return z
 
 
-def make(name: str, seed: int = 0, **over) -> Workload:
-    """Build a workload.  Keyword overrides (B, S, Hq, Hkv, D, kf, ...) shrink it."""
+def make(name: str, seed: int = 0, progress=None, **over) -> Workload:
+    """Build a workload.  Keyword overrides (B, S, Hq, Hkv, D, kf, ...) shrink it.
+    ``progress(b)``, if given, is called after each sequence of the mixed workload."""
     p = default_sizes(name)
     p.update(over)
     B, Hq, Hkv, D, S, kf = p["B"], p["Hq"], p["Hkv"], p["D"], p["S"], p["kf"]
@@ -161,6 +162,8 @@ def make(name: str, seed: int = 0, **over) -> Workload:
                 x = x + 0.01 * rng.standard_normal((2, Hkv, Tb, D), dtype=np.float32)
             k[b, :, :Tb] = x[0].astype(np.float16)
             v[b, :, :Tb] = x[1].astype(np.float16)
+            if progress is not None:
+                progress(b)
     else:
         raise ValueError(name)
 
