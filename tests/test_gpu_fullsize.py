@@ -1,0 +1,94 @@
+"""Parity at the benchmark sizes, in the launch configuration bench.py times.
+
+The 70B-layer workload (B=16, 64 q / 8 kv heads, D=128, S=32768, kf=32), the
+long-context workload (B=8, S=16384, kf=512 and 128) and the mixed serving
+workload (full lengths 1K..64K in shuffled 256-token pages, 16 of its 64
+sequences) are encoded and attended on the GPU exactly as the benchmark does.
+The oracle checks sampled (sequence, kv-head) pairs: keyframes, Q4_0 codes,
+fp16 scale bits and the reconstruction state bit-exact, decode attention of the
+pair's query heads within 2e-3 of float64.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_decode_attention_delta_amd as dkv
+from quantized_decode_attention_delta_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+import gpu_util as U  # noqa: E402
+
+
+def _run(w, kf, pairs, paged=False):
+    cfg = U.make_cfg(w, kf, w.page_tokens if paged else 0)
+    bt = None
+    if paged:
+        table, n = synth.page_table(w)
+        cfg.n_pages = n
+        cfg.max_pages_per_seq = table.shape[1]
+        bt = torch.from_numpy(table).to(U.DEV)
+    lens_np = np.asarray(w.seq_lens, np.int32)
+    lens = torch.from_numpy(lens_np).to(U.DEV)
+    s_max = w.k.shape[2]
+    cache = torch.empty(dkv.dkv_cache_bytes(cfg), dtype=torch.uint8, device=U.DEV)
+    state = torch.zeros(w.B, w.Hkv, 2, w.D, dtype=torch.float32, device=U.DEV)
+    k = torch.from_numpy(w.k).to(U.DEV)
+    v = torch.from_numpy(w.v).to(U.DEV)
+    dkv.dkv_encode_prefill(cfg, cache, state, bt, k, v, lens, s_max)
+    del k, v
+    q_np = synth.queries(w)
+    q = torch.from_numpy(q_np).to(U.DEV)
+    out = torch.full((w.B, w.Hq, w.D), float("nan"), dtype=torch.float32, device=U.DEV)
+    ws = torch.zeros(dkv.dkv_workspace_bytes(cfg), dtype=torch.uint8, device=U.DEV)
+    dkv.dkv_attn_decode(cfg, cache, bt, q, lens, out, ws)
+    got = out.cpu().numpy()
+
+    skf, scd, ssc = dkv.export_shapes(cfg, s_max)
+    ekf = torch.zeros(skf, dtype=torch.int16, device=U.DEV)
+    ecd = torch.zeros(scd, dtype=torch.uint8, device=U.DEV)
+    esc = torch.zeros(ssc, dtype=torch.int16, device=U.DEV)
+    dkv.dkv_export(cfg, cache, bt, lens, s_max, ekf, ecd, esc)
+    st = state.cpu().numpy()
+
+    G = w.Hq // w.Hkv
+    scale = np.float32(1 / math.sqrt(w.D))
+    worst = 0.0
+    for (b, h) in pairs:
+        L = int(lens_np[b])
+        ng, nd = oracle.n_groups(L, kf), oracle.n_delta(L, kf)
+        recon = []
+        for s, x in ((0, w.k), (1, w.v)):
+            e = oracle.encode_stream(np.ascontiguousarray(x[b, h, :L]), kf)
+            assert np.array_equal(ekf[b, h, s, :ng].cpu().numpy().view(np.uint16), e.kf_rows), ("kf", b, h, s)
+            assert np.array_equal(ecd[b, h, s, :nd].cpu().numpy(), e.codes), ("codes", b, h, s)
+            assert np.array_equal(esc[b, h, s, :nd].cpu().numpy().view(np.uint16), e.scales), ("scales", b, h, s)
+            assert np.array_equal(st[b, h, s].view(np.uint32), e.state.view(np.uint32)), ("state", b, h, s)
+            recon.append(e.recon)
+        ref = oracle.attention_f64(q_np[b, h * G:(h + 1) * G], recon[0], recon[1], scale)
+        g = got[b, h * G:(h + 1) * G].astype(np.float64)
+        err = float((np.abs(g - ref).max(-1) / np.abs(ref).max(-1)).max())
+        worst = max(worst, err)
+    assert worst <= U.ATTN_TOL, worst
+    assert np.isfinite(got).all()
+
+
+def test_70b_layer_full_size():
+    w = synth.make("70b")
+    _run(w, 32, [(0, 0), (5, 3), (9, 6), (15, 7)])
+
+
+@pytest.mark.parametrize("kf", [512, 128])
+def test_long_context_full_size(kf):
+    w = synth.make("long")
+    _run(w, kf, [(0, 0), (3, 5), (7, 7)])
+
+
+def test_mixed_serving_full_lengths():
+    w = synth.make("mixed", B=16, extra_tokens=0)
+    longest = int(np.argmax(w.seq_lens))
+    shortest = int(np.argmin(w.seq_lens))
+    _run(w, 32, [(longest, 0), (shortest, 3), (2, 7), (12, 1)], paged=True)
