@@ -126,7 +126,8 @@ __device__ inline float setup_g8(G8Shared<D> &sh, G8Ops &op, const float *q, int
 // enters through C2).  Lg: prefixed logits of this lane's 4 tokens (units
 // q*2^-E) including `carry` (the sum over earlier tiles of the group); total:
 // this tile's sum.  Returns the tile maximum in log2 units.
-template <int D, bool FULL, bool FIRST>
+// DELTA = false: plain Q4_0 tile (absolute values: no prefix sums, no keyframe).
+template <int D, bool FULL, bool FIRST, bool DELTA = true>
 __device__ inline float k_phase_g8(const uint32_t *kc, const uint8_t *sb, const u4 *kf_row, int nval, int j, int n,
                                    const G8Ops &op, float c2E, float carry, float (&Lg)[4], float &total)
 {
@@ -183,10 +184,10 @@ __device__ inline float k_phase_g8(const uint32_t *kc, const uint8_t *sb, const 
         const float d = __builtin_fmaf(u[i], 1048576.0f, C2[i]);
         Lg[i] = (FULL || tb + i < nval) ? d : 0.0f;
     }
-    // prefix over the tile's tokens: in-lane, over rows j, then the first half's total
+    if constexpr (DELTA) {
+        // prefix over the tile's tokens: in-lane, over rows j, then the first half's total
 #pragma unroll
-    for (int i = 1; i < 4; ++i) Lg[i] += Lg[i - 1];
-    {
+        for (int i = 1; i < 4; ++i) Lg[i] += Lg[i - 1];
         float incl, all;
         rows_prefix(Lg[3], j, incl, all);
         const float allx = other_half(all);           // (every lane takes part in the exchange)
@@ -194,6 +195,8 @@ __device__ inline float k_phase_g8(const uint32_t *kc, const uint8_t *sb, const 
         const float off = (incl - Lg[3]) + (h2 ? allx : 0.0f) + carry;
 #pragma unroll
         for (int i = 0; i < 4; ++i) Lg[i] += off;
+    } else {
+        total = 0.0f;
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -208,15 +211,9 @@ __device__ inline float k_phase_g8(const uint32_t *kc, const uint8_t *sb, const 
 // range bias from the group's largest |V scale| (slot 0 of the V scale plane,
 // vs0) and kf <= 2^lkf; the accumulators are rescaled only when either changes.
 template <int D>
-__device__ inline void update_g8(RunState<D> &st, float m_g, const uint32_t *vs0, int lkf)
+__device__ inline void update_g8_vmx(RunState<D> &st, float m_g, uint32_t vmx, int lkf)
 {
     constexpr int NB = D / 32, NCC = D / 16, NP = NB / 2;
-    uint32_t vmx = 0;
-#pragma unroll
-    for (int k = 0; k < NP; ++k) {
-        const uint32_t w = vs0[k] & 0x7FFF7FFFu;
-        vmx = max(vmx, max(w & 0xFFFFu, w >> 16));
-    }
     const int ev = (vmx >> 10) == 0 ? -14 : (int)(vmx >> 10) - 15;
     const int beta_g = vmx == 0 ? 24 - lkf : 10 - lkf - ev;       // kf * 16 * |s| * 2^beta < 2^15
 
@@ -234,14 +231,27 @@ __device__ inline void update_g8(RunState<D> &st, float m_g, const uint32_t *vs0
     st.m = m_new;
     st.beta = beta_new;
 }
+template <int D>
+__device__ inline void update_g8(RunState<D> &st, float m_g, const uint32_t *vs0, int lkf)
+{
+    constexpr int NP = D / 64;
+    uint32_t vmx = 0;
+#pragma unroll
+    for (int k = 0; k < NP; ++k) {
+        const uint32_t w = vs0[k] & 0x7FFF7FFFu;
+        vmx = max(vmx, max(w & 0xFFFFu, w >> 16));
+    }
+    update_g8_vmx<D>(st, m_g, vmx, lkf);
+}
 
 // V phase of one 32-token tile.  sb: the tile's V side data in LDS ([keyframe
 // 2D bytes][scales 2D bytes]); Lg: the tile's prefixed logits from the K phase;
 // carry: the sum of the softmax weights of the later tiles of the group.
 // Adds the tile's weighted V codes to the accumulators; a FIRST tile (the last
 // one processed) also adds the keyframe with the group's total weight.
-// Returns the tile's weight sum.
-template <int D, bool FULL, bool FIRST>
+// Returns the tile's weight sum.  DELTA = false: plain Q4_0 tile (the weight of
+// token t is p_t itself, no suffix sums, no keyframe).
+template <int D, bool FULL, bool FIRST, bool DELTA = true>
 __device__ inline float v_phase_g8(RunState<D> &st, const uint32_t *vc, const uint8_t *sb, const float (&Lg)[4],
                                    int nval, int j, int n, float c2E, h8 AZ, float carry)
 {
@@ -255,10 +265,10 @@ __device__ inline float v_phase_g8(RunState<D> &st, const uint32_t *vc, const ui
         const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(Lg[i], c2E, -m_new));
         S[i] = (FULL || tb + i < nval) ? p : 0.0f;
     }
-#pragma unroll
-    for (int i = 2; i >= 0; --i) S[i] += S[i + 1];
     float Pt;
-    {
+    if constexpr (DELTA) {
+#pragma unroll
+        for (int i = 2; i >= 0; --i) S[i] += S[i + 1];
         float incl, all;
         rows_suffix(S[0], j, incl, all);
         const float allx = other_half(all);
@@ -266,6 +276,9 @@ __device__ inline float v_phase_g8(RunState<D> &st, const uint32_t *vc, const ui
         const float off = (incl - S[0]) + (h2 ? 0.0f : allx) + carry;
 #pragma unroll
         for (int i = 0; i < 4; ++i) S[i] += off;
+    } else {
+        const float all = rows_sum((S[0] + S[1]) + (S[2] + S[3]));
+        Pt = all + other_half(all);
     }
     st.l += Pt;
 
@@ -734,6 +747,133 @@ hipError_t launch_attn_g8(const dkv_config &c, const void *cache, const int32_t 
             hipLaunchKernelGGL(k_attn_long_g8<128>, grid, dim3(64), lds, st, c, (const uint8_t *)cache, bt, q, lens,
                                scale_log2, ws, nsplit, chunk);
     }
+    return hipGetLastError();
+}
+
+// ============================================================ plain Q4_0, GQA <= 8
+// The same layout tricks on the plain Q4_0 comparison cache: one 32-token tile
+// per step, the next tile fetched while the current one is processed.  The
+// tile's largest |V scale| (the V weight range) is reduced over the wave.
+template <int D>
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
+    k_attn_q40_g8(dkv_config cfg, const uint8_t *__restrict__ q4, const float *__restrict__ q,
+                  const int32_t *__restrict__ seq_lens, float scale_log2, float *__restrict__ ws, int nsplit,
+                  int chunk)
+{
+    constexpr int NB = D / 32;
+    const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int lane = threadIdx.x, j = lane >> 4, n = lane & 15;
+    const int G = cfg.n_q_heads / cfg.n_kv_heads;
+    const int L = min(seq_lens[b], q40_ntiles(cfg) * 32);
+    const int nt = (L + 31) >> 5;
+    const int t0 = split * chunk, t1 = min(nt, t0 + chunk);
+    const int64_t row0 = (int64_t)b * cfg.n_q_heads + h * G;
+    const int tbytes = (int)q40_tile_bytes(D);
+
+    // [unused 2D][K scales 2D][unused 2D][V scales 2D]: the side layout of the phases
+    __shared__ __attribute__((aligned(16))) uint32_t side[2 * D];
+    __shared__ G8Shared<D> sh;
+
+    G8Ops op;
+    const float c2E = setup_g8<D>(sh, op, q, row0, G, scale_log2, j, n);
+    const h8 AZ = v_minus8_operand();
+    RunState<D> st;
+    init_state<D>(st);
+
+    // per-lane offsets inside a tile
+    const int so = (lane >= D / 8 && lane < D / 4) ? 16 * (lane - D / 8)
+                 : (lane >= 3 * D / 8 && lane < D / 2) ? 18 * D + 16 * (lane - 3 * D / 8) : 0x40000000;
+    const int ok0 = 2 * D + n * (D / 2) + 4 * j * NB;
+    const int ok1 = 2 * D + (16 + n) * (D / 2) + 4 * j * NB;
+    const int ov = 20 * D + (j * 16 + n) * (D / 16) * 4;
+    auto load_tile = [&](G8Regs<D> &r, int tl) {
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(q4 + q40_tile_offset(cfg, b, h, tl)), (short)0, tbytes, 0x00020000);
+        r.side = __builtin_amdgcn_raw_buffer_load_b128(rs, so, 0, 0);
+        if constexpr (NB == 4) {
+            const u4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, ok0, 0, 0);
+            const u4 c = __builtin_amdgcn_raw_buffer_load_b128(rs, ok1, 0, 0);
+            const u4 v0 = __builtin_amdgcn_raw_buffer_load_b128(rs, ov, 0, 0);
+            const u4 v1 = __builtin_amdgcn_raw_buffer_load_b128(rs, ov + 16, 0, 0);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                r.kc[k] = a[k];
+                r.kc[4 + k] = c[k];
+                r.vc[k] = v0[k];
+                r.vc[4 + k] = v1[k];
+            }
+        } else {
+            const u2 a = __builtin_amdgcn_raw_buffer_load_b64(rs, ok0, 0, 0);
+            const u2 c = __builtin_amdgcn_raw_buffer_load_b64(rs, ok1, 0, 0);
+            const u4 v0 = __builtin_amdgcn_raw_buffer_load_b128(rs, ov, 0, 0);
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                r.kc[k] = a[k];
+                r.kc[2 + k] = c[k];
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) r.vc[k] = v0[k];
+        }
+    };
+    auto run = [&](const G8Regs<D> &r, int tl) {
+        __syncthreads();
+        if (lane < D / 2) ((u4 *)side)[fresh_lane_id()] = r.side;
+        __syncthreads();
+        const uint8_t *sb = (const uint8_t *)side;
+        const int nval = min(32, L - 32 * tl);
+        // largest |V scale| of the tile (2*D bytes = D/2 words over the wave)
+        uint32_t vmx;
+        {
+            const uint32_t w = ((const uint32_t *)(sb + 6 * D))[lane & (D / 2 - 1)];
+            const int valid_tok = (lane & (D / 2 - 1)) / (NB / 2) < nval;
+            const uint32_t a = valid_tok ? (w & 0x7FFF7FFFu) : 0u;
+            float m = (float)max(a & 0xFFFFu, a >> 16);
+            m = rows_max(m);
+#pragma unroll
+            for (int sh2 = 8; sh2 >= 1; sh2 >>= 1)
+                m = fmaxf(m, __shfl_xor(m, sh2, 16));
+            vmx = (uint32_t)m;
+        }
+        float Lg[4], tot;
+        const u4 *none = sh.qz;
+        float mt;
+        if (nval == 32)
+            mt = k_phase_g8<D, true, false, false>(r.kc, sb, none, nval, j, n, op, c2E, 0.0f, Lg, tot);
+        else
+            mt = k_phase_g8<D, false, false, false>(r.kc, sb, none, nval, j, n, op, c2E, 0.0f, Lg, tot);
+        update_g8_vmx<D>(st, mt, vmx, 0);
+        if (nval == 32)
+            v_phase_g8<D, true, false, false>(st, r.vc, sb + 4 * D, Lg, nval, j, n, c2E, AZ, 0.0f);
+        else
+            v_phase_g8<D, false, false, false>(st, r.vc, sb + 4 * D, Lg, nval, j, n, c2E, AZ, 0.0f);
+    };
+    if (t0 < t1) {
+        G8Regs<D> ra, rb;
+        int tl = t0;
+        load_tile(ra, tl);
+        auto step = [&](const G8Regs<D> &cur, G8Regs<D> &pf) {
+            // prefetch unconditionally (past the end: the current tile again)
+            load_tile(pf, tl + 1 < t1 ? tl + 1 : tl);
+            run(cur, tl);
+            ++tl;
+            return tl < t1;
+        };
+        while (step(ra, rb) && step(rb, ra)) {
+        }
+    }
+    write_partial_g8<D>(st, ws, row0, G, nsplit, split, lane, j, n);
+}
+
+hipError_t launch_attn_q40_g8(const dkv_config &c, const void *q4, const float *q, const int32_t *lens,
+                              float scale_log2, float *ws, int nsplit, int chunk, hipStream_t st)
+{
+    dim3 grid(nsplit, c.n_kv_heads, c.batch);
+    if (c.head_dim == 64)
+        hipLaunchKernelGGL(k_attn_q40_g8<64>, grid, dim3(64), 0, st, c, (const uint8_t *)q4, q, lens, scale_log2, ws,
+                           nsplit, chunk);
+    else
+        hipLaunchKernelGGL(k_attn_q40_g8<128>, grid, dim3(64), 0, st, c, (const uint8_t *)q4, q, lens, scale_log2,
+                           ws, nsplit, chunk);
     return hipGetLastError();
 }
 

@@ -110,6 +110,22 @@ __host__ __device__ inline int64_t group_offset(const Geom &g, const int32_t *bl
     return (int64_t)b * g.page_bytes + ((int64_t)h * g.gpp + gi) * g.rec;
 }
 
+// ---- plain Q4_0 comparison cache --------------------------------------------
+// Per (sequence, kv-head) a run of 32-token tiles of 36*D bytes:
+// [K scales 2D][K codes 16D][V scales 2D][V codes 16D], codes in the same
+// orders as the Delta-KV K code rows and V code tiles (V in block-pair order
+// under the same condition on G and D).
+__host__ __device__ inline int64_t q40_tile_bytes(int D) { return 36LL * D; }
+__host__ __device__ inline int q40_ntiles(const dkv_config &c) { return (c.max_tokens + 31) / 32; }
+__host__ __device__ inline int64_t q40_tile_offset(const dkv_config &c, int b, int h, int tile)
+{
+    return (((int64_t)b * c.n_kv_heads + h) * q40_ntiles(c) + tile) * q40_tile_bytes(c.head_dim);
+}
+__host__ __device__ inline int q40_vbp(const dkv_config &c)
+{
+    return c.n_q_heads / c.n_kv_heads <= 8 && (c.head_dim == 64 || c.head_dim == 128);
+}
+
 // ---- channel permutations -------------------------------------------------
 // Within a 32-bit code piece (canonical bytes 4j..4j+3 of a block), nibble p
 // is byte p/2, low (p even) or high (p odd) half, i.e. block channel

@@ -4,23 +4,15 @@
 // built like the Delta-KV one (same split-K partials, same combine), so that
 // the three are compared on equal footing.
 //
-// Q4_0 cache: per (sequence, kv-head) a run of 32-token tiles of 36*D bytes
-//   [K scales 2D: fp16 [32][nb]][K codes 16D: 32 rows, same piece order as
-//   the Delta-KV K code rows][V scales 2D][V codes 16D: same tile order as the
-//   Delta-KV V codes]
-// i.e. exactly 18 bytes per 32 elements, laid out for the 16x16x32 fp16
-// matrix instruction.
+// Q4_0 cache (layout in dkv_common.h): exactly 18 bytes per 32 elements,
+// laid out for the 16x16x32 fp16 matrix instruction.  With at most 8 query
+// heads per kv-head the attention runs on the GQA<=8 kernel family
+// (dkv_attn_g8.hip); this file keeps the general 16-column kernel.
 #include "dkv_fused_common.h"
 #include "dkv_q40.h"
 
 namespace dkv {
 
-__host__ __device__ inline int64_t q40_tile_bytes(int D) { return 36LL * D; }
-__host__ __device__ inline int q40_ntiles(const dkv_config &c) { return (c.max_tokens + 31) / 32; }
-__host__ __device__ inline int64_t q40_tile_offset(const dkv_config &c, int b, int h, int tile)
-{
-    return (((int64_t)b * c.n_kv_heads + h) * q40_ntiles(c) + tile) * q40_tile_bytes(c.head_dim);
-}
 
 // ------------------------------------------------------------------------
 // Q4_0 encode: grid (tiles, Hkv*2, B), one wavefront per (tile, stream);
@@ -75,7 +67,7 @@ __global__ void __launch_bounds__(64) k_q40_encode(dkv_config cfg, uint8_t *q4, 
         for (int i = 0; i < NC; ++i) {
             const int c = lane + 64 * i;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) tw[vcode_word(D, 4 * j, c, 0)] = vw[i][j];
+            for (int j = 0; j < 4; ++j) tw[vcode_word(D, 4 * j, c, q40_vbp(cfg))] = vw[i][j];
         }
     }
 }
@@ -101,8 +93,9 @@ __global__ void __launch_bounds__(256) k_q40_export(dkv_config cfg, const uint8_
     } else {
         const uint32_t *tw = (const uint32_t *)(base + 2 * D);
         const int sh = 4 * vcode_nibble(tau);
-        const uint32_t lo = (tw[vcode_word(D, tau, 32 * blk + i, 0)] >> sh) & 0xFu;
-        const uint32_t hi = (tw[vcode_word(D, tau, 32 * blk + i + 16, 0)] >> sh) & 0xFu;
+        const int bp = q40_vbp(cfg);
+        const uint32_t lo = (tw[vcode_word(D, tau, 32 * blk + i, bp)] >> sh) & 0xFu;
+        const uint32_t hi = (tw[vcode_word(D, tau, 32 * blk + i + 16, bp)] >> sh) & 0xFu;
         out = (uint8_t)(lo | (hi << 4));
     }
     const int64_t row = (((int64_t)b * cfg.n_kv_heads + h) * 2 + s) * s_max + t;
@@ -158,14 +151,6 @@ __device__ inline void setup_query(float (*sq)[D + 4], u4 *qB, const float *q, i
     }
 }
 
-// Sum over the 4 rows of a column (all rows get the total).
-__device__ inline float rows_sum(float x)
-{
-    float a0, a1, b0, b1;
-    swap16(x, a0, a1);
-    swap32(a0 + a1, b0, b1);
-    return b0 + b1;
-}
 
 // ------------------------------------------------------------------------
 // Q4_0 decode attention: grid (nsplit, Hkv, B), one wavefront per
@@ -571,9 +556,13 @@ hipError_t launch_q40_export(const dkv_config &c, const void *q4, const int32_t 
     return hipGetLastError();
 }
 
+hipError_t launch_attn_q40_g8(const dkv_config &c, const void *q4, const float *q, const int32_t *lens,
+                              float scale_log2, float *ws, int nsplit, int chunk, hipStream_t st);
+
 hipError_t launch_attn_q40(const dkv_config &c, const void *q4, const float *q, const int32_t *lens, float scale_log2,
                            float *ws, int nsplit, int chunk, hipStream_t st)
 {
+    if (q40_vbp(c)) return launch_attn_q40_g8(c, q4, q, lens, scale_log2, ws, nsplit, chunk, st);
     dim3 grid(nsplit, c.n_kv_heads, c.batch);
     if (c.head_dim == 64)
         hipLaunchKernelGGL(k_attn_q40<64>, grid, dim3(64), 0, st, c, (const uint8_t *)q4, q, lens, scale_log2, ws,

@@ -75,6 +75,14 @@ __device__ inline void rows_suffix(float x, int j, float &incl, float &total)
     incl = ((j & 1) ? a1 : t) + (j < 2 ? b1 : 0.0f);
     total = b0 + b1;
 }
+// Sum over the 4 rows of a column (all rows get the total).
+__device__ inline float rows_sum(float x)
+{
+    float a0, a1, b0, b1;
+    swap16(x, a0, a1);
+    swap32(a0 + a1, b0, b1);
+    return b0 + b1;
+}
 __device__ inline float rows_max(float x)
 {
     float a0, a1, b0, b1;
