@@ -51,18 +51,18 @@ __device__ inline void load_group(GroupRegs<D> &r, const uint8_t *rec, int rec_b
 {
     constexpr int NB = D / 32, NCC = D / 16;
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)rec, (short)0, rec_bytes, 0x00020000);
-    r.side = __builtin_amdgcn_raw_buffer_load_b128(rs, o.side, 0, 0);
+    r.side = __builtin_amdgcn_raw_buffer_load_b128(rs, o.side, 0, kStream);
     if constexpr (NB == 4) {
-        u4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, o.k0, 0, 0);
-        u4 c = __builtin_amdgcn_raw_buffer_load_b128(rs, o.k1, 0, 0);
+        u4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, o.k0, 0, kStream);
+        u4 c = __builtin_amdgcn_raw_buffer_load_b128(rs, o.k1, 0, kStream);
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             r.kc[0][k] = a[k];
             r.kc[1][k] = c[k];
         }
     } else {
-        u2 a = __builtin_amdgcn_raw_buffer_load_b64(rs, o.k0, 0, 0);
-        u2 c = __builtin_amdgcn_raw_buffer_load_b64(rs, o.k1, 0, 0);
+        u2 a = __builtin_amdgcn_raw_buffer_load_b64(rs, o.k0, 0, kStream);
+        u2 c = __builtin_amdgcn_raw_buffer_load_b64(rs, o.k1, 0, kStream);
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
             r.kc[0][k] = a[k];
@@ -71,7 +71,7 @@ __device__ inline void load_group(GroupRegs<D> &r, const uint8_t *rec, int rec_b
     }
 #pragma unroll
     for (int q4 = 0; q4 < NCC / 4; ++q4) {
-        u4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, o.v + 16 * q4, 0, 0);
+        u4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, o.v + 16 * q4, 0, kStream);
 #pragma unroll
         for (int k = 0; k < 4; ++k) r.vc[4 * q4 + k] = a[k];
     }

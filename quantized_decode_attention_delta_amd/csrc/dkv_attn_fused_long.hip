@@ -122,7 +122,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
             __syncthreads();
             if (lane < D / 8) {
                 if (t == 0) {
-                    u4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * lane, 0, 0);
+                    u4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * lane, 0, kStream);
                     const uint32_t w0 = v[0], w2 = v[2];
                     v[0] = scale_h2_16th(w0);
                     v[2] = scale_h2_16th(w2);
@@ -130,7 +130,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
                 }
             } else if (lane < D / 4) {
                 ((u4 *)side)[lane] = __builtin_amdgcn_raw_buffer_load_b128(
-                    rs, (int)g.off_ksc + 64 * NB * t + 16 * (lane - D / 8), 0, 0);
+                    rs, (int)g.off_ksc + 64 * NB * t + 16 * (lane - D / 8), 0, kStream);
             }
             // K codes of tokens 32t + 16T + m (row = token - 1; the keyframe slot reads a dummy row)
             uint32_t kc[2][NB];
@@ -139,16 +139,16 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
                 const int k0t = (t == 0) ? lo.k0 : (int)g.off_kcd + (32 * t + n - 1) * (D / 2) + 4 * j * NB;
                 const int k1t = lo.k1 + 32 * t * (D / 2);
                 if constexpr (NB == 4) {
-                    const u4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, k0t, 0, 0);
-                    const u4 c = __builtin_amdgcn_raw_buffer_load_b128(rs, k1t, 0, 0);
+                    const u4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, k0t, 0, kStream);
+                    const u4 c = __builtin_amdgcn_raw_buffer_load_b128(rs, k1t, 0, kStream);
 #pragma unroll
                     for (int k = 0; k < 4; ++k) {
                         kc[0][k] = a[k];
                         kc[1][k] = c[k];
                     }
                 } else {
-                    const u2 a = __builtin_amdgcn_raw_buffer_load_b64(rs, k0t, 0, 0);
-                    const u2 c = __builtin_amdgcn_raw_buffer_load_b64(rs, k1t, 0, 0);
+                    const u2 a = __builtin_amdgcn_raw_buffer_load_b64(rs, k0t, 0, kStream);
+                    const u2 c = __builtin_amdgcn_raw_buffer_load_b64(rs, k1t, 0, kStream);
 #pragma unroll
                     for (int k = 0; k < 2; ++k) {
                         kc[0][k] = a[k];
@@ -234,7 +234,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
         // ---------------------------------------------------------- softmax update
         uint32_t vmx = 0;
         {
-            const u2 s0 = __builtin_amdgcn_raw_buffer_load_b64(rs, (int)g.off_vsc, 0, 0);   // slot 0: max |scale|
+            const u2 s0 = __builtin_amdgcn_raw_buffer_load_b64(rs, (int)g.off_vsc, 0, kStream);   // slot 0: max |scale|
 #pragma unroll
             for (int k = 0; k < NB / 2; ++k) {
                 const uint32_t w = s0[k] & 0x7FFF7FFFu;
@@ -267,15 +267,15 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
             if (lane < D / 8) {
                 if (t == 0)
                     ((u4 *)side)[D / 4 + lane] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)g.off_vkf + 16 * lane,
-                                                                                       0, 0);
+                                                                                       0, kStream);
             } else if (lane < D / 4) {
                 ((u4 *)side)[D / 4 + lane] = __builtin_amdgcn_raw_buffer_load_b128(
-                    rs, (int)g.off_vsc + 64 * NB * t + 16 * (lane - D / 8), 0, 0);
+                    rs, (int)g.off_vsc + 64 * NB * t + 16 * (lane - D / 8), 0, kStream);
             }
             uint32_t vc[NCC];
 #pragma unroll
             for (int q4 = 0; q4 < NCC / 4; ++q4) {
-                const u4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, lo.v + 16 * D * t + 16 * q4, 0, 0);
+                const u4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, lo.v + 16 * D * t + 16 * q4, 0, kStream);
 #pragma unroll
                 for (int k = 0; k < 4; ++k) vc[4 * q4 + k] = a[k];
             }

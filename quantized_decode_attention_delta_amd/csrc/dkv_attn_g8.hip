@@ -151,10 +151,12 @@ __device__ inline float k_phase_g8(const uint32_t *kc, const uint8_t *sb, const 
         u4 a0 = u4{0, 0, 0, 0}, a1 = u4{0, 0, 0, 0};
         const uint32_t *p0 = (const uint32_t *)(sb + 2 * D + n * 2 * NB);
         const uint32_t *p1 = (const uint32_t *)(sb + 2 * D + (16 + n) * 2 * NB);
+        // (loaded by every lane, then selected: a guarded load would split the code)
 #pragma unroll
         for (int k = 0; k < NP; ++k) {
-            a0[k] = (j == 0 && (!FIRST || n != 0)) ? p0[k] : 0u;
-            a1[k] = j == 0 ? p1[k] : 0u;
+            const uint32_t w0 = p0[k], w1 = p1[k];
+            a0[k] = (j == 0 && (!FIRST || n != 0)) ? w0 : 0u;
+            a1[k] = j == 0 ? w1 : 0u;
         }
         C2 = mfma(as_h8(a0), as_h8(op.qc[0][0]), f4{0, 0, 0, 0});
         C2 = mfma(as_h8(a0), as_h8(op.qc[0][32]), C2);
@@ -412,18 +414,18 @@ __device__ inline void load_g8(G8Regs<D> &r, const uint8_t *rec, int rec_bytes, 
 {
     constexpr int NB = D / 32, NCC = D / 16;
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)rec, (short)0, rec_bytes, 0x00020000);
-    r.side = __builtin_amdgcn_raw_buffer_load_b128(rs, o.side, 0, 0);
+    r.side = __builtin_amdgcn_raw_buffer_load_b128(rs, o.side, 0, kStream);
     if constexpr (NB == 4) {
-        u4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, o.k0, 0, 0);
-        u4 c = __builtin_amdgcn_raw_buffer_load_b128(rs, o.k1, 0, 0);
+        u4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, o.k0, 0, kStream);
+        u4 c = __builtin_amdgcn_raw_buffer_load_b128(rs, o.k1, 0, kStream);
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             r.kc[k] = a[k];
             r.kc[NB + k] = c[k];
         }
     } else {
-        u2 a = __builtin_amdgcn_raw_buffer_load_b64(rs, o.k0, 0, 0);
-        u2 c = __builtin_amdgcn_raw_buffer_load_b64(rs, o.k1, 0, 0);
+        u2 a = __builtin_amdgcn_raw_buffer_load_b64(rs, o.k0, 0, kStream);
+        u2 c = __builtin_amdgcn_raw_buffer_load_b64(rs, o.k1, 0, kStream);
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
             r.kc[k] = a[k];
@@ -432,22 +434,103 @@ __device__ inline void load_g8(G8Regs<D> &r, const uint8_t *rec, int rec_bytes, 
     }
 #pragma unroll
     for (int q4 = 0; q4 < NCC / 4; ++q4) {
-        u4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, o.v + 16 * q4, 0, 0);
+        u4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, o.v + 16 * q4, 0, kStream);
 #pragma unroll
         for (int k = 0; k < 4; ++k) r.vc[4 * q4 + k] = a[k];
     }
 }
 
-template <int D, bool FULL>
-__device__ inline void process_g8(RunState<D> &st, const G8Regs<D> &r, const uint8_t *sb, const u4 *kf_row,
-                                  int nval, int j, int n, const G8Ops &op, float c2E, h8 AZ)
+// The kf = 32 kernel fetches the two parts of a group separately: the K part
+// (side data and K code pieces) and the V part (V code words), each two groups
+// ahead of its use.
+template <int D>
+struct G8KRegs {
+    u4 side;
+    uint32_t kc[2 * (D / 32)];
+};
+template <int D>
+struct G8VRegs {
+    uint32_t vc[D / 16];
+};
+
+template <int D>
+__device__ inline void load_g8k(G8KRegs<D> &r, const uint8_t *rec, int rec_bytes, const LaneOffsets &o)
 {
-    float Lg[4], tot;
-    const float m_g = k_phase_g8<D, FULL, true>(r.kc, sb, kf_row, nval, j, n, op, c2E, 0.0f, Lg, tot);
-    update_g8<D>(st, m_g, (const uint32_t *)(sb + 6 * D), 5);
-    v_phase_g8<D, FULL, true>(st, r.vc, sb + 4 * D, Lg, nval, j, n, c2E, AZ, 0.0f);
+    constexpr int NB = D / 32;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)rec, (short)0, rec_bytes, 0x00020000);
+    r.side = __builtin_amdgcn_raw_buffer_load_b128(rs, o.side, 0, kStream);
+    if constexpr (NB == 4) {
+        const u4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, o.k0, 0, kStream);
+        const u4 c = __builtin_amdgcn_raw_buffer_load_b128(rs, o.k1, 0, kStream);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            r.kc[k] = a[k];
+            r.kc[NB + k] = c[k];
+        }
+    } else {
+        const u2 a = __builtin_amdgcn_raw_buffer_load_b64(rs, o.k0, 0, kStream);
+        const u2 c = __builtin_amdgcn_raw_buffer_load_b64(rs, o.k1, 0, kStream);
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            r.kc[k] = a[k];
+            r.kc[NB + k] = c[k];
+        }
+    }
 }
 
+template <int D>
+__device__ inline void load_g8v(G8VRegs<D> &r, const uint8_t *rec, int rec_bytes, const LaneOffsets &o)
+{
+    constexpr int NCC = D / 16;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)rec, (short)0, rec_bytes, 0x00020000);
+#pragma unroll
+    for (int q4 = 0; q4 < NCC / 4; ++q4) {
+        const u4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, o.v + 16 * q4, 0, kStream);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) r.vc[4 * q4 + k] = a[k];
+    }
+}
+
+// Largest |V scale| of a group: slot 0 of its V scale plane (side data + 6*D).
+template <int D>
+__device__ inline uint32_t group_vmax(const uint8_t *sb)
+{
+    const uint32_t *vs0 = (const uint32_t *)(sb + 6 * D);
+    uint32_t vmx = 0;
+#pragma unroll
+    for (int k = 0; k < D / 64; ++k) {
+        const uint32_t w = vs0[k] & 0x7FFF7FFFu;
+        vmx = max(vmx, max(w & 0xFFFFu, w >> 16));
+    }
+    return vmx;
+}
+
+// Steps between the fetch of a group part and its use in the kf = 32 kernel
+// (2..4; each step of lead holds one more group, 20 registers, in flight).
+constexpr int kG8Lead = 3;
+
+template <int V>
+struct IC {
+    static constexpr int value = V;
+};
+
+// Offset of the k-th mapped group of a batch as a wave-uniform value.
+__device__ inline int64_t uniform_offset(const int64_t *list, int k)
+{
+    const int64_t v = list[k];
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// kf = 32: the groups of a run are software-pipelined.  Step i runs the V
+// phase of group i and the K phase (with the softmax update) of group i + 1,
+// two independent streams of work that the compiler interleaves in one block
+// of code.  The mapped groups of a batch of up to 64 are listed in LDS first;
+// whole groups go through the pipeline, a partial last group of the sequence
+// is taken on its own afterwards.  The last step's K phase re-reads the first
+// group of the batch: its maximum and V range are already in the state, so its
+// update changes nothing and its logits are not used.
 template <int D>
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
     k_attn_g8(dkv_config cfg, const uint8_t *__restrict__ cache, const int32_t *__restrict__ bt,
@@ -456,6 +539,9 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
 {
     constexpr int NB = D / 32;
     constexpr int SIDE_LANES = D / 4;
+    constexpr int BATCH = 64;
+    constexpr int LEAD = kG8Lead, NBUF = LEAD + 1;
+    static_assert(LEAD >= 2 && LEAD <= 4, "fetch lead of 2..4 steps");
     const Geom g = make_geom(cfg);
     const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int lane = threadIdx.x, j = lane >> 4, n = lane & 15;
@@ -465,8 +551,10 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
     const int g0 = split * chunk, g1 = min(ng, g0 + chunk);
     const int64_t row0 = (int64_t)b * g.Hq + h * G;
 
-    // [K keyframe][K scales][V keyframe][V scales] of the current group, 2*D bytes each
-    __shared__ __attribute__((aligned(16))) uint32_t side[2 * D];
+    // side data of NBUF groups (slot = position in the batch mod NBUF):
+    // [K keyframe][K scales][V keyframe][V scales], 2*D bytes each
+    __shared__ __attribute__((aligned(16))) uint32_t side[NBUF][2 * D];
+    __shared__ int64_t glist[BATCH];
     __shared__ G8Shared<D> sh;
 
     G8Ops op;
@@ -478,64 +566,95 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
 
     const LaneOffsets lo = lane_offsets<D>(g, lane, j, n, true);
     const int rec_bytes = (int)g.rec;
-    // first mapped group in [x, lim) (paged mode may leave pages unmapped); uniform
-    auto next_mapped = [&](int x, int lim, int64_t &o) {
-        for (; x < lim; ++x) {
-            o = group_offset(g, bt, b, h, x);
-            if (o >= 0) break;
-        }
-        return x;
+    auto stage = [&](const G8KRegs<D> &r, int slot) {
+        // lanes < D/8 hold the K keyframe: scaled by f(hh)/16 for the K operand
+        // (scalar temporaries: bit_cast of a vector element lvalue is miscompiled;
+        // computed by every lane and selected, so the step stays one block of code)
+        u4 v = r.side;
+        const uint32_t w0 = v[0], w2 = v[2];
+        const bool kfl = lane < D / 8;
+        v[0] = kfl ? scale_h2_16th(w0) : w0;
+        v[2] = kfl ? scale_h2_16th(w2) : w2;
+        if (2 * SIDE_LANES == 64 || lane < 2 * SIDE_LANES) ((u4 *)side[slot])[fresh_lane_id()] = v;
     };
-    auto stage = [&](const G8Regs<D> &r) {
-        if (lane < 2 * SIDE_LANES) {
-            u4 v = r.side;
-            if (lane < D / 8) {
-                // K keyframe scaled by f(hh)/16 for the K operand (scalar temporaries:
-                // bit_cast of a vector element lvalue is miscompiled)
-                const uint32_t w0 = v[0], w2 = v[2];
-                v[0] = scale_h2_16th(w0);
-                v[2] = scale_h2_16th(w2);
-            }
-            ((u4 *)side)[fresh_lane_id()] = v;
-        }
-    };
+    auto sbp = [&](int slot) { return (const uint8_t *)side[slot]; };
     // keyframe pieces of this lane's K-operand row (lane n == 0), zeros elsewhere
-    const u4 *kf_row = n == 0 ? (const u4 *)((const uint8_t *)side + j * NB * 16) : sh.qz;
-    auto run = [&](const G8Regs<D> &r, int gcur) {
-        __syncthreads();
-        const int nval = min(32, L - gcur * 32);
-        if (nval == 32)
-            process_g8<D, true>(st, r, (const uint8_t *)side, kf_row, nval, j, n, op, c2E, AZ);
-        else
-            process_g8<D, false>(st, r, (const uint8_t *)side, kf_row, nval, j, n, op, c2E, AZ);
-    };
+    auto kfrow = [&](int slot) { return n == 0 ? (const u4 *)(sbp(slot) + j * NB * 16) : (const u4 *)sh.qz; };
 
-    // Two groups in flight: while group c is processed, groups c+1 and c+2 are
-    // being fetched (three register buffers in rotation).  The side data of the
-    // current group is staged into LDS right before it is processed (one wave per
-    // workgroup: the staging and the reads are ordered by the wave itself).
-    int64_t offc = -1, offn = -1, offp = -1;
-    int gc = next_mapped(g0, g1, offc);
-    if (gc < g1) {
-        G8Regs<D> r0, r1, r2;
-        load_g8<D>(r0, cache + offc, rec_bytes, lo);
-        int gn = next_mapped(gc + 1, g1, offn);
-        load_g8<D>(r1, cache + (gn < g1 ? offn : offc), rec_bytes, lo);
-        auto step = [&](const G8Regs<D> &cur, G8Regs<D> &pf) {
-            const int gp = gn < g1 ? next_mapped(gn + 1, g1, offp) : g1;
+    for (int gb0 = g0; gb0 < g1; gb0 += BATCH) {
+        const int gend = min(g1, gb0 + BATCH);
+        const int x = gb0 + lane;
+        const int64_t o = x < gend ? group_offset(g, bt, b, h, x) : -1;
+        const uint64_t mk = __ballot(o >= 0);
+        const int cnt = __popcll(mk);
+        const bool last_partial = (L & 31) != 0 && gend == ng && ((mk >> (ng - 1 - gb0)) & 1) != 0;
+        const int nfull = cnt - (last_partial ? 1 : 0);
+        __syncthreads();
+        if (o >= 0)
+            glist[__builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mk, 0u))] = o;
+        __syncthreads();
+
+        if (nfull > 0) {
+            // past the end of the whole groups the fetches re-read the first one
+            auto rec_at = [&](int k) { return cache + uniform_offset(glist, k < nfull ? k : 0); };
+            // group x: K part in buffer / side slot x % NBUF (fetched LEAD steps
+            // before the step that stages it), V part in buffer x % NBUF
+            G8KRegs<D> kb[NBUF];
+            G8VRegs<D> vb[NBUF];
+#pragma unroll
+            for (int x = 0; x <= LEAD; ++x) {
+                load_g8k<D>(kb[x % NBUF], rec_at(x), rec_bytes, lo);
+                if (x < LEAD) load_g8v<D>(vb[x % NBUF], rec_at(x), rec_bytes, lo);
+            }
+            float Lg[4], tot;
             __syncthreads();
-            stage(cur);
-            // unconditional prefetch keeps the wait counts exact (past the end it
-            // re-reads the current record and the values are unused)
-            load_g8<D>(pf, cache + (gp < g1 ? offp : offc), rec_bytes, lo);
-            run(cur, gc);
-            gc = gn;
-            offc = offn;
-            gn = gp;
-            offn = offp;
-            return gc < g1;
-        };
-        while (step(r0, r2) && step(r1, r0) && step(r2, r1)) {
+            stage(kb[0], 0);
+            __syncthreads();
+            {
+                const float m = k_phase_g8<D, true, true>(kb[0].kc, sbp(0), kfrow(0), 32, j, n, op, c2E, 0.0f, Lg, tot);
+                update_g8_vmx<D>(st, m, group_vmax<D>(sbp(0)), 5);
+            }
+            // step i (u = i % NBUF): stage the K part of group i + 1, fetch the K
+            // part of group i + 1 + LEAD and the V part of group i + LEAD, V phase
+            // of i, K phase of i + 1
+            auto step = [&](int i, auto uc) {
+                constexpr int u = decltype(uc)::value;
+                constexpr int un = (u + 1) % NBUF, ulast = (u + LEAD) % NBUF;
+                __syncthreads();
+                stage(kb[un], un);
+                load_g8k<D>(kb[u], rec_at(i + 1 + LEAD), rec_bytes, lo);
+                load_g8v<D>(vb[ulast], rec_at(i + LEAD), rec_bytes, lo);
+                __syncthreads();
+                v_phase_g8<D, true, true>(st, vb[u].vc, sbp(u) + 4 * D, Lg, 32, j, n, c2E, AZ, 0.0f);
+                const float m = k_phase_g8<D, true, true>(kb[un].kc, sbp(un), kfrow(un), 32, j, n, op, c2E, 0.0f,
+                                                          Lg, tot);
+                update_g8_vmx<D>(st, m, group_vmax<D>(sbp(un)), 5);
+                return i + 1 < nfull;
+            };
+            for (int i = 0;; i += NBUF) {
+                if (!step(i, IC<0>{})) break;
+                if (!step(i + 1, IC<1 % NBUF>{})) break;
+                if (!step(i + 2, IC<2 % NBUF>{})) break;
+                if constexpr (NBUF > 3)
+                    if (!step(i + 3, IC<3 % NBUF>{})) break;
+                if constexpr (NBUF > 4)
+                    if (!step(i + 4, IC<4 % NBUF>{})) break;
+            }
+        }
+        if (last_partial) {
+            G8KRegs<D> kr;
+            G8VRegs<D> vr;
+            const uint8_t *rec = cache + uniform_offset(glist, cnt - 1);
+            load_g8k<D>(kr, rec, rec_bytes, lo);
+            load_g8v<D>(vr, rec, rec_bytes, lo);
+            __syncthreads();
+            stage(kr, 0);
+            __syncthreads();
+            const int nval = L - (ng - 1) * 32;
+            float Lg[4], tot;
+            const float m = k_phase_g8<D, false, true>(kr.kc, sbp(0), kfrow(0), nval, j, n, op, c2E, 0.0f, Lg, tot);
+            update_g8_vmx<D>(st, m, group_vmax<D>(sbp(0)), 5);
+            v_phase_g8<D, false, true>(st, vr.vc, sbp(0) + 4 * D, Lg, nval, j, n, c2E, AZ, 0.0f);
         }
     }
     write_partial_g8<D>(st, ws, row0, G, nsplit, split, lane, j, n);
@@ -614,18 +733,18 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
         const int o0 = kp ? ((t == 0 && n == 0) ? 0x40000000 : (int)g.off_kcd + (32 * t + n - 1) * (D / 2) + 4 * j * NB)
                           : ov;
         const int o1 = kp ? (int)g.off_kcd + (32 * t + 15 + n) * (D / 2) + 4 * j * NB : ov + 4 * NB;
-        r.side = __builtin_amdgcn_raw_buffer_load_b128(rs, so, 0, 0);
+        r.side = __builtin_amdgcn_raw_buffer_load_b128(rs, so, 0, kStream);
         if constexpr (NB == 4) {
-            const u4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, o0, 0, 0);
-            const u4 c = __builtin_amdgcn_raw_buffer_load_b128(rs, o1, 0, 0);
+            const u4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, o0, 0, kStream);
+            const u4 c = __builtin_amdgcn_raw_buffer_load_b128(rs, o1, 0, kStream);
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 r.code[k] = a[k];
                 r.code[4 + k] = c[k];
             }
         } else {
-            const u2 a = __builtin_amdgcn_raw_buffer_load_b64(rs, o0, 0, 0);
-            const u2 c = __builtin_amdgcn_raw_buffer_load_b64(rs, o1, 0, 0);
+            const u2 a = __builtin_amdgcn_raw_buffer_load_b64(rs, o0, 0, kStream);
+            const u2 c = __builtin_amdgcn_raw_buffer_load_b64(rs, o1, 0, kStream);
 #pragma unroll
             for (int k = 0; k < 2; ++k) {
                 r.code[k] = a[k];
@@ -789,12 +908,12 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
     auto load_tile = [&](G8Regs<D> &r, int tl) {
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
             (void *)(q4 + q40_tile_offset(cfg, b, h, tl)), (short)0, tbytes, 0x00020000);
-        r.side = __builtin_amdgcn_raw_buffer_load_b128(rs, so, 0, 0);
+        r.side = __builtin_amdgcn_raw_buffer_load_b128(rs, so, 0, kStream);
         if constexpr (NB == 4) {
-            const u4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, ok0, 0, 0);
-            const u4 c = __builtin_amdgcn_raw_buffer_load_b128(rs, ok1, 0, 0);
-            const u4 v0 = __builtin_amdgcn_raw_buffer_load_b128(rs, ov, 0, 0);
-            const u4 v1 = __builtin_amdgcn_raw_buffer_load_b128(rs, ov + 16, 0, 0);
+            const u4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, ok0, 0, kStream);
+            const u4 c = __builtin_amdgcn_raw_buffer_load_b128(rs, ok1, 0, kStream);
+            const u4 v0 = __builtin_amdgcn_raw_buffer_load_b128(rs, ov, 0, kStream);
+            const u4 v1 = __builtin_amdgcn_raw_buffer_load_b128(rs, ov + 16, 0, kStream);
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 r.kc[k] = a[k];
@@ -803,9 +922,9 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
                 r.vc[4 + k] = v1[k];
             }
         } else {
-            const u2 a = __builtin_amdgcn_raw_buffer_load_b64(rs, ok0, 0, 0);
-            const u2 c = __builtin_amdgcn_raw_buffer_load_b64(rs, ok1, 0, 0);
-            const u4 v0 = __builtin_amdgcn_raw_buffer_load_b128(rs, ov, 0, 0);
+            const u2 a = __builtin_amdgcn_raw_buffer_load_b64(rs, ok0, 0, kStream);
+            const u2 c = __builtin_amdgcn_raw_buffer_load_b64(rs, ok1, 0, kStream);
+            const u4 v0 = __builtin_amdgcn_raw_buffer_load_b128(rs, ov, 0, kStream);
 #pragma unroll
             for (int k = 0; k < 2; ++k) {
                 r.kc[k] = a[k];

@@ -23,6 +23,9 @@
 namespace dkv {
 
 constexpr int kMaxKf = 1024;
+// Cache policy of the attention kernels' loads: the compressed cache is read
+// once per decode step, so its loads carry the nontemporal (streaming) hint.
+constexpr int kStream = 2;
 constexpr int kWave = 64;
 
 __host__ __device__ inline int64_t pad16(int64_t x) { return (x + 15) & ~int64_t(15); }

@@ -213,19 +213,19 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
         const int nvt = min(32, L - 32 * tl);
         __syncthreads();
         if (lane < D / 8)
-            ((u4 *)side)[lane] = __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * lane, 0, 0);
+            ((u4 *)side)[lane] = __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * lane, 0, kStream);
         else if (lane < D / 4)
-            ((u4 *)side)[lane] = __builtin_amdgcn_raw_buffer_load_b128(rs, 18 * D + 16 * (lane - D / 8), 0, 0);
+            ((u4 *)side)[lane] = __builtin_amdgcn_raw_buffer_load_b128(rs, 18 * D + 16 * (lane - D / 8), 0, kStream);
         uint32_t kc[2][NB];
 #pragma unroll
         for (int T = 0; T < 2; ++T) {
             const int off = 2 * D + (16 * T + n) * (D / 2) + 4 * j * NB;
             if constexpr (NB == 4) {
-                const u4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+                const u4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kStream);
 #pragma unroll
                 for (int k = 0; k < 4; ++k) kc[T][k] = a[k];
             } else {
-                const u2 a = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
+                const u2 a = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, kStream);
 #pragma unroll
                 for (int k = 0; k < 2; ++k) kc[T][k] = a[k];
             }
@@ -233,7 +233,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
         uint32_t vc[NCC];
 #pragma unroll
         for (int q4i = 0; q4i < NCC / 4; ++q4i) {
-            const u4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, 20 * D + (j * 16 + n) * NCC * 4 + 16 * q4i, 0, 0);
+            const u4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, 20 * D + (j * 16 + n) * NCC * 4 + 16 * q4i, 0, kStream);
 #pragma unroll
             for (int k = 0; k < 4; ++k) vc[4 * q4i + k] = a[k];
         }
@@ -430,7 +430,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
         for (int T = 0; T < 2; ++T)
 #pragma unroll
             for (int bb = 0; bb < NB; ++bb)
-                kr[T][bb] = __builtin_amdgcn_raw_buffer_load_b128(rk, ((16 * T + n) * D + 32 * bb + 8 * j) * 2, 0, 0);
+                kr[T][bb] = __builtin_amdgcn_raw_buffer_load_b128(rk, ((16 * T + n) * D + 32 * bb + 8 * j) * 2, 0, kStream);
         uint32_t vr[2][4][VW];
 #pragma unroll
         for (int T = 0; T < 2; ++T)
@@ -438,11 +438,11 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
             for (int i = 0; i < 4; ++i) {
                 const int off = ((16 * T + 4 * j + i) * D + CPL * n) * 2;
                 if constexpr (VW == 4) {
-                    const u4 a = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
+                    const u4 a = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, kStream);
 #pragma unroll
                     for (int k = 0; k < 4; ++k) vr[T][i][k] = a[k];
                 } else {
-                    const u2 a = __builtin_amdgcn_raw_buffer_load_b64(rv, off, 0, 0);
+                    const u2 a = __builtin_amdgcn_raw_buffer_load_b64(rv, off, 0, kStream);
 #pragma unroll
                     for (int k = 0; k < 2; ++k) vr[T][i][k] = a[k];
                 }
