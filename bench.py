@@ -303,16 +303,18 @@ def run_mixed(args):
     torch.cuda.synchronize()
     ms_step = ev0.elapsed_time(ev1) / args.steps
 
-    # the decode kernel alone on the final cache (timed per launch), and the append alone
+    # the decode kernel alone on the final cache (launches back to back between
+    # two events on the kernel's stream: the mean launch duration), and the append alone
     last = args.warmup + args.steps - 1
     n_k = max(10, args.steps)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_k)]
+    k0 = torch.cuda.Event(enable_timing=True)
+    k1 = torch.cuda.Event(enable_timing=True)
+    k0.record(stream)
     for i in range(n_k):
-        evs[i][0].record(stream)
         dkv.dkv_attn_decode_partial(cfg, cache, bt, q[last], lens_after[last], ws)
-        evs[i][1].record(stream)
+    k1.record(stream)
     torch.cuda.synchronize()
-    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    kern_ms = k0.elapsed_time(k1) / n_k
 
     Lf = lens0 + last + 1                                    # lengths during the last timed decode
     Lt = [lens0 + s + 1 for s in range(args.warmup, args.warmup + args.steps)]
@@ -418,18 +420,20 @@ def main():
     torch.cuda.synchronize()
     ms_step = ev0.elapsed_time(ev1) / args.steps
 
-    # dominant kernel alone: the split phase, timed per launch with events
+    # dominant kernel alone: the split phase, launched back to back between two
+    # events on its stream (the mean launch duration)
     n_k = max(10, args.steps)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_k)]
+    k0 = torch.cuda.Event(enable_timing=True)
+    k1 = torch.cuda.Event(enable_timing=True)
+    k0.record(stream)
     for i in range(n_k):
-        evs[i][0].record(stream)
         if args.kernel == "fused":
             dkv.dkv_attn_decode_partial(cfg, caches[i % replicas], None, q, lens, ws)
         else:
             dkv.dkv_attn_decode_ref(cfg, caches[i % replicas], None, q, lens, out, ws)
-        evs[i][1].record(stream)
+    k1.record(stream)
     torch.cuda.synchronize()
-    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    kern_ms = k0.elapsed_time(k1) / n_k
 
     comp = algorithmic_bytes(w.B, w.Hkv, w.Hq, w.D, w.S, kf)
     qo = w.B * w.Hq * w.D * 4 * 2

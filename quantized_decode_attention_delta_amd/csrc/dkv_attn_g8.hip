@@ -26,7 +26,31 @@ namespace dkv {
 bool fused_g8_supported(const dkv_config &c) { return vbp_layout(c) != 0 && c.kf == 32; }
 bool fused_long_g8_supported(const dkv_config &c) { return vbp_layout(c) != 0 && c.kf > 32 && c.kf <= 512; }
 
+// V weights of two token slots: w0 = s0 * x0 into the low half and w1 = s1 * x1
+// into the high half of `hi` (fp16, round to nearest), and the fp16 residues
+// x*s - w into `lo`.  s0, s1: fp16 in half SEL of sw0, sw1; the residue reads
+// its w straight from the half of `hi` it sits in.
+template <int SEL>
+__device__ inline void split_w(uint32_t sw0, uint32_t sw1, float x0, float x1, uint32_t &hi, uint32_t &lo)
+{
+    if constexpr (SEL == 0)
+        asm("v_fma_mixlo_f16 %0, %2, %4, 0 op_sel_hi:[1,0,0]\n\t"
+            "v_fma_mixhi_f16 %0, %3, %5, 0 op_sel_hi:[1,0,0]\n\t"
+            "v_fma_mixlo_f16 %1, %2, %4, -%0 op_sel_hi:[1,0,1]\n\t"
+            "v_fma_mixhi_f16 %1, %3, %5, -%0 op_sel:[0,0,1] op_sel_hi:[1,0,1]"
+            : "=&v"(hi), "=&v"(lo)
+            : "v"(sw0), "v"(sw1), "v"(x0), "v"(x1));
+    else
+        asm("v_fma_mixlo_f16 %0, %2, %4, 0 op_sel:[1,0,0] op_sel_hi:[1,0,0]\n\t"
+            "v_fma_mixhi_f16 %0, %3, %5, 0 op_sel:[1,0,0] op_sel_hi:[1,0,0]\n\t"
+            "v_fma_mixlo_f16 %1, %2, %4, -%0 op_sel:[1,0,0] op_sel_hi:[1,0,1]\n\t"
+            "v_fma_mixhi_f16 %1, %3, %5, -%0 op_sel:[1,0,1] op_sel_hi:[1,0,1]"
+            : "=&v"(hi), "=&v"(lo)
+            : "v"(sw0), "v"(sw1), "v"(x0), "v"(x1));
+}
+
 // Value of lane n ^ 8 within each row of 16 lanes (DPP row rotate by 8).
+
 __device__ inline float other_half(float x)
 {
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x128, 0xF, 0xF, false));
@@ -313,18 +337,19 @@ __device__ inline float v_phase_g8(RunState<D> &st, const uint32_t *vc, const ui
     }
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
-        h8 Wh, Wl;
+        uint32_t whd[4], wld[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float s0 = (NB == 4 && p == 1) ? hhi(vs[0][i]) : hlo(vs[0][i]);
-            const float s1 = (NB == 4 && p == 1) ? hhi(vs[1][i]) : hlo(vs[1][i]);
-            const _Float16 w0 = (_Float16)__builtin_fmaf(s0, Sp[0][i], 0.0f);
-            const _Float16 w1 = (_Float16)__builtin_fmaf(s1, Sp[1][i], 0.0f);
-            Wh[2 * i] = w0;
-            Wh[2 * i + 1] = w1;
-            Wl[2 * i] = (_Float16)__builtin_fmaf(s0, Sp[0][i], -(float)w0);
-            Wl[2 * i + 1] = (_Float16)__builtin_fmaf(s1, Sp[1][i], -(float)w1);
+            uint32_t hi, lo;
+            if (NB == 4 && p == 1)
+                split_w<1>(vs[0][i], vs[1][i], Sp[0][i], Sp[1][i], hi, lo);
+            else
+                split_w<0>(vs[0][i], vs[1][i], Sp[0][i], Sp[1][i], hi, lo);
+            whd[i] = hi;
+            wld[i] = lo;
         }
+        const h8 Wh = __builtin_bit_cast(h8, u4{whd[0], whd[1], whd[2], whd[3]});
+        const h8 Wl = __builtin_bit_cast(h8, u4{wld[0], wld[1], wld[2], wld[3]});
 #pragma unroll
         for (int c4 = 0; c4 < 4; ++c4) {
             const int cc = 4 * p + c4;
@@ -581,6 +606,8 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
     // keyframe pieces of this lane's K-operand row (lane n == 0), zeros elsewhere
     auto kfrow = [&](int slot) { return n == 0 ? (const u4 *)(sbp(slot) + j * NB * 16) : (const u4 *)sh.qz; };
 
+    // A group is one tile here, so the phases get no carry: -0.0, since
+    // x + -0.0 == x for every x and the add folds away.
     for (int gb0 = g0; gb0 < g1; gb0 += BATCH) {
         const int gend = min(g1, gb0 + BATCH);
         const int x = gb0 + lane;
@@ -611,7 +638,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
             stage(kb[0], 0);
             __syncthreads();
             {
-                const float m = k_phase_g8<D, true, true>(kb[0].kc, sbp(0), kfrow(0), 32, j, n, op, c2E, 0.0f, Lg, tot);
+                const float m = k_phase_g8<D, true, true>(kb[0].kc, sbp(0), kfrow(0), 32, j, n, op, c2E, -0.0f, Lg, tot);
                 update_g8_vmx<D>(st, m, group_vmax<D>(sbp(0)), 5);
             }
             // step i (u = i % NBUF): stage the K part of group i + 1, fetch the K
@@ -625,8 +652,8 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
                 load_g8k<D>(kb[u], rec_at(i + 1 + LEAD), rec_bytes, lo);
                 load_g8v<D>(vb[ulast], rec_at(i + LEAD), rec_bytes, lo);
                 __syncthreads();
-                v_phase_g8<D, true, true>(st, vb[u].vc, sbp(u) + 4 * D, Lg, 32, j, n, c2E, AZ, 0.0f);
-                const float m = k_phase_g8<D, true, true>(kb[un].kc, sbp(un), kfrow(un), 32, j, n, op, c2E, 0.0f,
+                v_phase_g8<D, true, true>(st, vb[u].vc, sbp(u) + 4 * D, Lg, 32, j, n, c2E, AZ, -0.0f);
+                const float m = k_phase_g8<D, true, true>(kb[un].kc, sbp(un), kfrow(un), 32, j, n, op, c2E, -0.0f,
                                                           Lg, tot);
                 update_g8_vmx<D>(st, m, group_vmax<D>(sbp(un)), 5);
                 return i + 1 < nfull;
@@ -652,9 +679,9 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
             __syncthreads();
             const int nval = L - (ng - 1) * 32;
             float Lg[4], tot;
-            const float m = k_phase_g8<D, false, true>(kr.kc, sbp(0), kfrow(0), nval, j, n, op, c2E, 0.0f, Lg, tot);
+            const float m = k_phase_g8<D, false, true>(kr.kc, sbp(0), kfrow(0), nval, j, n, op, c2E, -0.0f, Lg, tot);
             update_g8_vmx<D>(st, m, group_vmax<D>(sbp(0)), 5);
-            v_phase_g8<D, false, true>(st, vr.vc, sbp(0) + 4 * D, Lg, nval, j, n, c2E, AZ, 0.0f);
+            v_phase_g8<D, false, true>(st, vr.vc, sbp(0) + 4 * D, Lg, nval, j, n, c2E, AZ, -0.0f);
         }
     }
     write_partial_g8<D>(st, ws, row0, G, nsplit, split, lane, j, n);

@@ -36,14 +36,14 @@ __device__ inline float half_at(const uint32_t *w, int k) { return (k & 1) ? hhi
 // Cross-row exchanges with gfx950 permlane swaps (VALU, no LDS round trip).
 // The 64 lanes form 4 rows j of 16; these helpers combine the 4 values that
 // one column n holds in rows 0..3.
-// (Inline asm on two distinct registers: the compiler builtins return the
-// same register for both results when both inputs are the same value.  The
-// s_nop pairs cover the VALU-write / permlane-read hazards.)
+// (Inline asm on two distinct registers: the compiler builtin models both
+// results in one register.  The s_nop covers the VALU-write -> permlane-read
+// gap; the asm has no side effects, so the scheduler may move it.)
 __device__ inline void swap16(float x, float &r0, float &r1)
 {
     // r0 = rows (x0, x0, x2, x2), r1 = rows (x1, x1, x3, x3)
     float a = x, b = x;
-    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+    asm("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
     r0 = a;
     r1 = b;
 }
@@ -51,7 +51,7 @@ __device__ inline void swap32(float x, float &r0, float &r1)
 {
     // r0 = rows (x0, x1, x0, x1), r1 = rows (x2, x3, x2, x3)
     float a = x, b = x;
-    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+    asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
     r0 = a;
     r1 = b;
 }
