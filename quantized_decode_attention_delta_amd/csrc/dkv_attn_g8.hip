@@ -235,9 +235,10 @@ __device__ inline float k_phase_g8(const uint32_t *kc, const uint8_t *sb, const 
 
 // Softmax state update for a group with maximum m_g: new running max and V
 // range bias from the group's largest |V scale| (slot 0 of the V scale plane,
-// vs0) and kf <= 2^lkf; the accumulators are rescaled only when either changes.
+// vs0) and kf <= 2^lkf; the accumulators are rescaled only when either changes,
+// and with them `pend`, keyframe weights not yet added (same units).
 template <int D>
-__device__ inline void update_g8_vmx(RunState<D> &st, float m_g, uint32_t vmx, int lkf)
+__device__ inline void update_g8_vmx(RunState<D> &st, float m_g, uint32_t vmx, int lkf, float &pend)
 {
     constexpr int NB = D / 32, NCC = D / 16, NP = NB / 2;
     const int ev = (vmx >> 10) == 0 ? -14 : (int)(vmx >> 10) - 15;
@@ -253,6 +254,7 @@ __device__ inline void update_g8_vmx(RunState<D> &st, float m_g, uint32_t vmx, i
 #pragma unroll
         for (int p = 0; p < NP; ++p) st.Z[p] *= alpha;
         st.l *= a_m;
+        pend *= alpha;
     }
     st.m = m_new;
     st.beta = beta_new;
@@ -267,7 +269,8 @@ __device__ inline void update_g8(RunState<D> &st, float m_g, const uint32_t *vs0
         const uint32_t w = vs0[k] & 0x7FFF7FFFu;
         vmx = max(vmx, max(w & 0xFFFFu, w >> 16));
     }
-    update_g8_vmx<D>(st, m_g, vmx, lkf);
+    float none = 0.0f;
+    update_g8_vmx<D>(st, m_g, vmx, lkf, none);
 }
 
 // V phase of one 32-token tile.  sb: the tile's V side data in LDS ([keyframe
@@ -277,7 +280,26 @@ __device__ inline void update_g8(RunState<D> &st, float m_g, const uint32_t *vs0
 // one processed) also adds the keyframe with the group's total weight.
 // Returns the tile's weight sum.  DELTA = false: plain Q4_0 tile (the weight of
 // token t is p_t itself, no suffix sums, no keyframe).
-template <int D, bool FULL, bool FIRST, bool DELTA = true>
+// Keyframe term of a group: acc += pk * x0, pk = the group's weight in
+// accumulator units 2^(beta-20); sb: the group's V side data in LDS.
+template <int D>
+__device__ inline void kf_fma_g8(RunState<D> &st, const uint8_t *sb, float pk, int j)
+{
+    constexpr int NCC = D / 16;
+    const uint32_t *kp = (const uint32_t *)(sb + j * NCC * 8);
+#pragma unroll
+    for (int cc = 0; cc < NCC; ++cc) {
+        const uint32_t w01 = kp[2 * cc], w23 = kp[2 * cc + 1];
+        st.acc[cc][0] = __builtin_fmaf(hlo(w01), pk, st.acc[cc][0]);
+        st.acc[cc][1] = __builtin_fmaf(hhi(w01), pk, st.acc[cc][1]);
+        st.acc[cc][2] = __builtin_fmaf(hlo(w23), pk, st.acc[cc][2]);
+        st.acc[cc][3] = __builtin_fmaf(hhi(w23), pk, st.acc[cc][3]);
+    }
+}
+
+// KFD = false: a FIRST tile leaves the keyframe term to the caller (the return
+// value plus carry is the group's weight).
+template <int D, bool FULL, bool FIRST, bool DELTA = true, bool KFD = true>
 __device__ inline float v_phase_g8(RunState<D> &st, const uint32_t *vc, const uint8_t *sb, const float (&Lg)[4],
                                    int nval, int j, int n, float c2E, h8 AZ, float carry)
 {
@@ -360,19 +382,7 @@ __device__ inline float v_phase_g8(RunState<D> &st, const uint32_t *vc, const ui
         st.Z[p] = mfma(AZ, Wh, st.Z[p]);
         st.Z[p] = mfma(AZ, Wl, st.Z[p]);
     }
-    if constexpr (FIRST) {
-        // keyframe: acc += P_group * x0 (accumulator units 2^(beta-20))
-        const float pk = (Pt + carry) * ldexpf(1.0f, st.beta - 20);
-        const uint32_t *kp = (const uint32_t *)(sb + j * NCC * 8);
-#pragma unroll
-        for (int cc = 0; cc < NCC; ++cc) {
-            const uint32_t w01 = kp[2 * cc], w23 = kp[2 * cc + 1];
-            st.acc[cc][0] = __builtin_fmaf(hlo(w01), pk, st.acc[cc][0]);
-            st.acc[cc][1] = __builtin_fmaf(hhi(w01), pk, st.acc[cc][1]);
-            st.acc[cc][2] = __builtin_fmaf(hlo(w23), pk, st.acc[cc][2]);
-            st.acc[cc][3] = __builtin_fmaf(hhi(w23), pk, st.acc[cc][3]);
-        }
-    }
+    if constexpr (FIRST && KFD) kf_fma_g8<D>(st, sb, (Pt + carry) * ldexpf(1.0f, st.beta - 20), j);
     return Pt;
 }
 
@@ -562,11 +572,12 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
               const float *__restrict__ q, const int32_t *__restrict__ seq_lens, float scale_log2,
               float *__restrict__ ws, int nsplit, int chunk)
 {
-    constexpr int NB = D / 32;
+    constexpr int NB = D / 32, NCC = D / 16;
     constexpr int SIDE_LANES = D / 4;
     constexpr int BATCH = 64;
     constexpr int LEAD = kG8Lead, NBUF = LEAD + 1;
-    static_assert(LEAD >= 2 && LEAD <= 4, "fetch lead of 2..4 steps");
+    static_assert(NBUF == 4, "the keyframe batches of 4 groups close on the last step of an unrolled round");
+    constexpr int NSLOT = 8;
     const Geom g = make_geom(cfg);
     const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int lane = threadIdx.x, j = lane >> 4, n = lane & 15;
@@ -576,9 +587,11 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
     const int g0 = split * chunk, g1 = min(ng, g0 + chunk);
     const int64_t row0 = (int64_t)b * g.Hq + h * G;
 
-    // side data of NBUF groups (slot = position in the batch mod NBUF):
-    // [K keyframe][K scales][V keyframe][V scales], 2*D bytes each
-    __shared__ __attribute__((aligned(16))) uint32_t side[NBUF][2 * D];
+    // side data of the groups at positions x of the batch in slot x % NSLOT:
+    // [K keyframe][K scales][V keyframe][V scales], 2*D bytes each.  A group is
+    // staged two steps before its V phase; its slot is rewritten six steps
+    // after it, when the group's keyframe batch has long been added.
+    __shared__ __attribute__((aligned(16))) uint32_t side[NSLOT][2 * D];
     __shared__ int64_t glist[BATCH];
     __shared__ G8Shared<D> sh;
 
@@ -588,10 +601,15 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
 
     RunState<D> st;
     init_state<D>(st);
+    // keyframe weights of the open batch of 4 groups: lane (j, n) holds the
+    // weight of head column n of the batch's group j (the B operand of an
+    // fp32 16x16x4 matrix instruction whose A operand holds the 4 keyframes)
+    float kfw = 0.0f;
 
     const LaneOffsets lo = lane_offsets<D>(g, lane, j, n, true);
     const int rec_bytes = (int)g.rec;
-    auto stage = [&](const G8KRegs<D> &r, int slot) {
+    auto sbp = [&](int x) { return (const uint8_t *)side[x & (NSLOT - 1)]; };
+    auto stage = [&](const G8KRegs<D> &r, int x) {
         // lanes < D/8 hold the K keyframe: scaled by f(hh)/16 for the K operand
         // (scalar temporaries: bit_cast of a vector element lvalue is miscompiled;
         // computed by every lane and selected, so the step stays one block of code)
@@ -600,14 +618,25 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
         const bool kfl = lane < D / 8;
         v[0] = kfl ? scale_h2_16th(w0) : w0;
         v[2] = kfl ? scale_h2_16th(w2) : w2;
-        if (2 * SIDE_LANES == 64 || lane < 2 * SIDE_LANES) ((u4 *)side[slot])[fresh_lane_id()] = v;
+        if (2 * SIDE_LANES == 64 || lane < 2 * SIDE_LANES) ((u4 *)side[x & (NSLOT - 1)])[fresh_lane_id()] = v;
     };
-    auto sbp = [&](int slot) { return (const uint8_t *)side[slot]; };
     // keyframe pieces of this lane's K-operand row (lane n == 0), zeros elsewhere
-    auto kfrow = [&](int slot) { return n == 0 ? (const u4 *)(sbp(slot) + j * NB * 16) : (const u4 *)sh.qz; };
+    auto kfrow = [&](int x) { return n == 0 ? (const u4 *)(sbp(x) + j * NB * 16) : (const u4 *)sh.qz; };
+    // add the keyframe terms of the batch whose last group is at position x:
+    // lane (j, n) supplies channel row n of slice cc of group (x & ~3) + j
+    // (rows past x, if any, are masked to zero)
+    auto kf_flush = [&](int x, bool whole) {
+        const int gj = (x & ~3) + j;
+        const uint16_t *kfv = (const uint16_t *)(sbp(gj) + 4 * D) + (n >> 2) * NCC * 4 + (n & 3);
+        const bool live = whole || gj <= x;
+#pragma unroll
+        for (int cc = 0; cc < NCC; ++cc) {
+            const float a = live ? h2f(kfv[4 * cc]) : 0.0f;
+            st.acc[cc] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, kfw, st.acc[cc], 0, 0, 0);
+        }
+        kfw = 0.0f;
+    };
 
-    // A group is one tile here, so the phases get no carry: -0.0, since
-    // x + -0.0 == x for every x and the add folds away.
     for (int gb0 = g0; gb0 < g1; gb0 += BATCH) {
         const int gend = min(g1, gb0 + BATCH);
         const int x = gb0 + lane;
@@ -621,52 +650,56 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
             glist[__builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mk, 0u))] = o;
         __syncthreads();
 
+        // A group is one tile here, so the phases get no carry: -0.0, since
+        // x + -0.0 == x for every x and the add folds away.
         if (nfull > 0) {
             // past the end of the whole groups the fetches re-read the first one
             auto rec_at = [&](int k) { return cache + uniform_offset(glist, k < nfull ? k : 0); };
-            // group x: K part in buffer / side slot x % NBUF (fetched LEAD steps
-            // before the step that stages it), V part in buffer x % NBUF
+            // group x: K part in buffer x % NBUF (fetched LEAD steps before the
+            // step that stages it), V part in buffer x % NBUF
             G8KRegs<D> kb[NBUF];
             G8VRegs<D> vb[NBUF];
 #pragma unroll
-            for (int x = 0; x <= LEAD; ++x) {
-                load_g8k<D>(kb[x % NBUF], rec_at(x), rec_bytes, lo);
-                if (x < LEAD) load_g8v<D>(vb[x % NBUF], rec_at(x), rec_bytes, lo);
+            for (int y = 0; y <= LEAD; ++y) {
+                load_g8k<D>(kb[y % NBUF], rec_at(y), rec_bytes, lo);
+                if (y < LEAD) load_g8v<D>(vb[y % NBUF], rec_at(y), rec_bytes, lo);
             }
             float Lg[4], tot;
             __syncthreads();
             stage(kb[0], 0);
+            stage(kb[1], 1);
             __syncthreads();
             {
                 const float m = k_phase_g8<D, true, true>(kb[0].kc, sbp(0), kfrow(0), 32, j, n, op, c2E, -0.0f, Lg, tot);
-                update_g8_vmx<D>(st, m, group_vmax<D>(sbp(0)), 5);
+                update_g8_vmx<D>(st, m, group_vmax<D>(sbp(0)), 5, kfw);
             }
-            // step i (u = i % NBUF): stage the K part of group i + 1, fetch the K
-            // part of group i + 1 + LEAD and the V part of group i + LEAD, V phase
-            // of i, K phase of i + 1
+            // step i (u = i % NBUF): fetch the K part of group i + 1 + LEAD and
+            // the V part of group i + LEAD, V phase of i (its keyframe weight
+            // joins the open batch), K phase of i + 1, then stage the K part of
+            // group i + 2 for the next step.  The wave is alone in its workgroup:
+            // its LDS accesses stay in program order without barriers.
             auto step = [&](int i, auto uc) {
                 constexpr int u = decltype(uc)::value;
-                constexpr int un = (u + 1) % NBUF, ulast = (u + LEAD) % NBUF;
-                __syncthreads();
-                stage(kb[un], un);
+                constexpr int un = (u + 1) % NBUF, u2 = (u + 2) % NBUF, ulast = (u + LEAD) % NBUF;
                 load_g8k<D>(kb[u], rec_at(i + 1 + LEAD), rec_bytes, lo);
                 load_g8v<D>(vb[ulast], rec_at(i + LEAD), rec_bytes, lo);
-                __syncthreads();
-                v_phase_g8<D, true, true>(st, vb[u].vc, sbp(u) + 4 * D, Lg, 32, j, n, c2E, AZ, -0.0f);
-                const float m = k_phase_g8<D, true, true>(kb[un].kc, sbp(un), kfrow(un), 32, j, n, op, c2E, -0.0f,
-                                                          Lg, tot);
-                update_g8_vmx<D>(st, m, group_vmax<D>(sbp(un)), 5);
+                const float pt =
+                    v_phase_g8<D, true, true, true, false>(st, vb[u].vc, sbp(i) + 4 * D, Lg, 32, j, n, c2E, AZ, -0.0f);
+                kfw = j == u ? pt * ldexpf(1.0f, st.beta - 20) : kfw;
+                if constexpr (u == NBUF - 1) kf_flush(i, true);
+                const float m = k_phase_g8<D, true, true>(kb[un].kc, sbp(i + 1), kfrow(i + 1), 32, j, n, op, c2E,
+                                                          -0.0f, Lg, tot);
+                update_g8_vmx<D>(st, m, group_vmax<D>(sbp(i + 1)), 5, kfw);
+                stage(kb[u2], i + 2);
                 return i + 1 < nfull;
             };
             for (int i = 0;; i += NBUF) {
                 if (!step(i, IC<0>{})) break;
-                if (!step(i + 1, IC<1 % NBUF>{})) break;
-                if (!step(i + 2, IC<2 % NBUF>{})) break;
-                if constexpr (NBUF > 3)
-                    if (!step(i + 3, IC<3 % NBUF>{})) break;
-                if constexpr (NBUF > 4)
-                    if (!step(i + 4, IC<4 % NBUF>{})) break;
+                if (!step(i + 1, IC<1>{})) break;
+                if (!step(i + 2, IC<2>{})) break;
+                if (!step(i + 3, IC<3>{})) break;
             }
+            if (((nfull - 1) & 3) != 3) kf_flush(nfull - 1, false);
         }
         if (last_partial) {
             G8KRegs<D> kr;
@@ -674,14 +707,16 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
             const uint8_t *rec = cache + uniform_offset(glist, cnt - 1);
             load_g8k<D>(kr, rec, rec_bytes, lo);
             load_g8v<D>(vr, rec, rec_bytes, lo);
+            // position nfull: its slot holds no group of an open batch
             __syncthreads();
-            stage(kr, 0);
+            stage(kr, nfull);
             __syncthreads();
             const int nval = L - (ng - 1) * 32;
             float Lg[4], tot;
-            const float m = k_phase_g8<D, false, true>(kr.kc, sbp(0), kfrow(0), nval, j, n, op, c2E, -0.0f, Lg, tot);
-            update_g8_vmx<D>(st, m, group_vmax<D>(sbp(0)), 5);
-            v_phase_g8<D, false, true>(st, vr.vc, sbp(0) + 4 * D, Lg, nval, j, n, c2E, AZ, -0.0f);
+            const float m =
+                k_phase_g8<D, false, true>(kr.kc, sbp(nfull), kfrow(nfull), nval, j, n, op, c2E, -0.0f, Lg, tot);
+            update_g8_vmx<D>(st, m, group_vmax<D>(sbp(nfull)), 5, kfw);
+            v_phase_g8<D, false, true>(st, vr.vc, sbp(nfull) + 4 * D, Lg, nval, j, n, c2E, AZ, -0.0f);
         }
     }
     write_partial_g8<D>(st, ws, row0, G, nsplit, split, lane, j, n);
@@ -987,7 +1022,8 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
             mt = k_phase_g8<D, true, false, false>(r.kc, sb, none, nval, j, n, op, c2E, 0.0f, Lg, tot);
         else
             mt = k_phase_g8<D, false, false, false>(r.kc, sb, none, nval, j, n, op, c2E, 0.0f, Lg, tot);
-        update_g8_vmx<D>(st, mt, vmx, 0);
+        float no_kf = 0.0f;
+        update_g8_vmx<D>(st, mt, vmx, 0, no_kf);
         if (nval == 32)
             v_phase_g8<D, true, false, false>(st, r.vc, sb + 4 * D, Lg, nval, j, n, c2E, AZ, 0.0f);
         else
