@@ -755,7 +755,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
     __shared__ __attribute__((aligned(16))) uint32_t side[D];
     __shared__ __attribute__((aligned(16))) uint32_t vslot0[4];
     __shared__ G8Shared<D> sh;
-    extern __shared__ f4 lgs[];               // prefixed logits [tile][lane] of the current group
+    extern __shared__ f4 lgs[];               // prefixed logits [tile][row] of the current group
 
     G8Ops op;
     const float c2E = setup_g8<D>(sh, op, q, row0, G, scale_log2, j, n);
@@ -826,32 +826,52 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
     };
     const u4 *kf_row = n == 0 ? (const u4 *)((const uint8_t *)side + j * NB * 16) : sh.qz;
 
+    // Logit rows of a tile: one f4 per lane.  With at most 4 query heads per
+    // kv-head only the lanes of heads 0..3 carry logits, so a tile takes 32 rows
+    // (lane (j, n) -> 8j + 4(n >> 3) + (n & 3)); the other lanes read those rows
+    // (finite values they do not use) and write to one spare row past the tiles.
+    const bool half_rows = G <= 4;
+    const int lrow = half_rows ? 8 * j + 4 * (n >> 3) + (n & 3) : lane;
+    const int lstride = half_rows ? 32 : 64;
+    const int spare = ((kf + 31) >> 5) * 32;
+    const bool wr_spare = half_rows && (n & 7) >= 4;
+
     float carry = 0.0f, mx = -INFINITY;       // per-group pass state
-    int64_t offc = -1, offn = -1;
-    int gc = next_mapped(g0, offc);
-    if (gc < g1) {
-        int ntc = ntiles(gc), s = 0;
-        // the step after (gc, s): the same group, or K tile 0 of the next mapped group
-        int gn = gc, sn = 1, ntn = ntc;
-        offn = offc;
-        auto advance = [&]() {
-            if (sn < 2 * ntn) return;
-            gn = next_mapped(gn + 1, offn);
-            sn = 0;
-            ntn = gn < g1 ? ntiles(gn) : 1;
-        };
-        advance();
-        TileRegs<D> ra, rb;
-        load_step(ra, offc, 0, ntc);
+    // a position in the run: group g (record at off), step s of its 2*nt steps
+    struct Cursor {
+        int g;
+        int64_t off;
+        int s, nt;
+    };
+    auto next_pos = [&](Cursor c) {
+        Cursor r = c;
+        if (++r.s < 2 * r.nt) return r;
+        r.g = next_mapped(c.g + 1, r.off);
+        r.s = 0;
+        r.nt = r.g < g1 ? ntiles(r.g) : 1;
+        return r;
+    };
+    Cursor cc0;
+    cc0.off = -1;
+    cc0.g = next_mapped(g0, cc0.off);
+    if (cc0.g < g1) {
+        cc0.s = 0;
+        cc0.nt = ntiles(cc0.g);
+        // two steps in flight: the registers of steps +1 and +2 are being fetched
+        Cursor cc1 = next_pos(cc0), cc2 = cc1.g < g1 ? next_pos(cc1) : cc1;
+        TileRegs<D> ra, rb, rc;
+        load_step(ra, cc0.off, 0, cc0.nt);
+        load_step(rb, cc1.g < g1 ? cc1.off : cc0.off, cc1.g < g1 ? cc1.s : 0, cc1.g < g1 ? cc1.nt : cc0.nt);
         auto step = [&](const TileRegs<D> &cur, TileRegs<D> &pf) {
+            const int gc = cc0.g, s = cc0.s, ntc = cc0.nt;
             __syncthreads();
             const bool kp = s < ntc;
             const int t = kp ? s : 2 * ntc - 1 - s;
             const int nval = min(kf, L - gc * kf) - 32 * t;     // valid tokens from the tile start
             stage(cur, kp);
-            // prefetch the following step (past the end: the current step again)
-            const bool more = gn < g1;
-            load_step(pf, more ? offn : offc, more ? sn : s, more ? ntn : ntc);
+            // prefetch two steps ahead (past the end: the current step again)
+            const bool more = cc2.g < g1;
+            load_step(pf, more ? cc2.off : cc0.off, more ? cc2.s : s, more ? cc2.nt : ntc);
             __syncthreads();
             const uint8_t *sb = (const uint8_t *)side;
             if (kp) {
@@ -871,13 +891,13 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
                     mx = fmaxf(mx, m);
                 }
                 carry += tot;
-                lgs[t * 64 + lane] = f4{Lg[0], Lg[1], Lg[2], Lg[3]};
+                lgs[wr_spare ? spare : t * lstride + lrow] = f4{Lg[0], Lg[1], Lg[2], Lg[3]};
                 if (t == ntc - 1) {
                     update_g8<D>(st, mx, vslot0, lkf);
                     carry = 0.0f;            // from here on: the suffix carry of the V pass
                 }
             } else {
-                const f4 lv = lgs[t * 64 + lane];
+                const f4 lv = lgs[t * lstride + lrow];
                 const float Lg[4] = {lv[0], lv[1], lv[2], lv[3]};
                 float pt;
                 if (t == 0) {
@@ -894,15 +914,12 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
                 carry += pt;
             }
             // move to the next step
-            gc = gn;
-            offc = offn;
-            s = sn;
-            ntc = ntn;
-            ++sn;
-            advance();
-            return gc < g1;
+            cc0 = cc1;
+            cc1 = cc2;
+            if (cc2.g < g1) cc2 = next_pos(cc2);
+            return cc0.g < g1;
         };
-        while (step(ra, rb) && step(rb, ra)) {
+        while (step(ra, rc) && step(rb, ra) && step(rc, rb)) {
         }
     }
     write_partial_g8<D>(st, ws, row0, G, nsplit, split, lane, j, n);
@@ -920,7 +937,10 @@ hipError_t launch_attn_g8(const dkv_config &c, const void *cache, const int32_t 
             hipLaunchKernelGGL(k_attn_g8<128>, grid, dim3(64), 0, st, c, (const uint8_t *)cache, bt, q, lens,
                                scale_log2, ws, nsplit, chunk);
     } else {
-        const size_t lds = (size_t)((c.kf + 31) / 32) * 64 * sizeof(f4);
+        // logit rows (see the kernel): 32 per tile and a spare row when at most
+        // 4 query heads share a kv-head, 64 per tile otherwise
+        const int nt = (c.kf + 31) / 32;
+        const size_t lds = (c.n_q_heads / c.n_kv_heads <= 4 ? (size_t)nt * 32 + 1 : (size_t)nt * 64) * sizeof(f4);
         if (c.head_dim == 64)
             hipLaunchKernelGGL(k_attn_long_g8<64>, grid, dim3(64), lds, st, c, (const uint8_t *)cache, bt, q, lens,
                                scale_log2, ws, nsplit, chunk);
