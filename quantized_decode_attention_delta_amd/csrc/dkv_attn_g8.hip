@@ -549,7 +549,7 @@ struct IC {
     static constexpr int value = V;
 };
 
-// Offset of the k-th mapped group of a batch as a wave-uniform value.
+// Offset of the k-th mapped group of a run as a wave-uniform value.
 __device__ inline int64_t uniform_offset(const int64_t *list, int k)
 {
     const int64_t v = list[k];
@@ -558,14 +558,13 @@ __device__ inline int64_t uniform_offset(const int64_t *list, int k)
     return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
-// kf = 32: the groups of a run are software-pipelined.  Step i runs the V
-// phase of group i and the K phase (with the softmax update) of group i + 1,
-// two independent streams of work that the compiler interleaves in one block
-// of code.  The mapped groups of a batch of up to 64 are listed in LDS first;
-// whole groups go through the pipeline, a partial last group of the sequence
-// is taken on its own afterwards.  The last step's K phase re-reads the first
-// group of the batch: its maximum and V range are already in the state, so its
-// update changes nothing and its logits are not used.
+// kf = 32: the groups of a run (at most 64) are software-pipelined.  Step i
+// runs the V phase of group i and the K phase (with the softmax update) of
+// group i + 1, two independent streams of work that the compiler interleaves
+// in one block of code.  The keyframe terms of every 4 groups are added
+// together by fp32 matrix instructions.  The last step's K phase re-reads the
+// first group of the run: its maximum and V range are already in the state,
+// so its update changes nothing and its logits are not used.
 template <int D>
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
     k_attn_g8(dkv_config cfg, const uint8_t *__restrict__ cache, const int32_t *__restrict__ bt,
@@ -587,13 +586,42 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
     const int g0 = split * chunk, g1 = min(ng, g0 + chunk);
     const int64_t row0 = (int64_t)b * g.Hq + h * G;
 
-    // side data of the groups at positions x of the batch in slot x % NSLOT:
+    // side data of the groups at positions x of the run in slot x % NSLOT:
     // [K keyframe][K scales][V keyframe][V scales], 2*D bytes each.  A group is
     // staged two steps before its V phase; its slot is rewritten six steps
     // after it, when the group's keyframe batch has long been added.
     __shared__ __attribute__((aligned(16))) uint32_t side[NSLOT][2 * D];
     __shared__ int64_t glist[BATCH];
     __shared__ G8Shared<D> sh;
+
+    // The run's mapped groups (a run has at most BATCH groups: the split plan
+    // caps it at 2048 tokens) listed in LDS.  The whole groups go through the
+    // pipeline; a partial last group of the sequence is taken on its own after.
+    const int x0 = g0 + lane;
+    const int64_t o0 = x0 < g1 ? group_offset(g, bt, b, h, x0) : -1;
+    const uint64_t mk = __ballot(o0 >= 0);
+    const int cnt = __popcll(mk);
+    const bool last_partial = (L & 31) != 0 && g1 == ng && ng > g0 && ((mk >> (ng - 1 - g0)) & 1) != 0;
+    const int nfull = cnt - (last_partial ? 1 : 0);
+    if (o0 >= 0) glist[__builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mk, 0u))] = o0;
+    __syncthreads();
+    // past the end of the whole groups the fetches re-read the first one
+    auto rec_at = [&](int k) { return cache + uniform_offset(glist, k < nfull ? k : 0); };
+
+    const LaneOffsets lo = lane_offsets<D>(g, lane, j, n, true);
+    const int rec_bytes = (int)g.rec;
+    // group x: K part in buffer x % NBUF (fetched LEAD steps before the step
+    // that stages it), V part in buffer x % NBUF.  The first fetches go out
+    // before the query set-up, whose own loads then overlap them.
+    G8KRegs<D> kb[NBUF];
+    G8VRegs<D> vb[NBUF];
+    if (nfull > 0) {
+#pragma unroll
+        for (int y = 0; y <= LEAD; ++y) {
+            load_g8k<D>(kb[y % NBUF], rec_at(y), rec_bytes, lo);
+            if (y < LEAD) load_g8v<D>(vb[y % NBUF], rec_at(y), rec_bytes, lo);
+        }
+    }
 
     G8Ops op;
     const float c2E = setup_g8<D>(sh, op, q, row0, G, scale_log2, j, n);
@@ -606,8 +634,6 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
     // fp32 16x16x4 matrix instruction whose A operand holds the 4 keyframes)
     float kfw = 0.0f;
 
-    const LaneOffsets lo = lane_offsets<D>(g, lane, j, n, true);
-    const int rec_bytes = (int)g.rec;
     auto sbp = [&](int x) { return (const uint8_t *)side[x & (NSLOT - 1)]; };
     auto stage = [&](const G8KRegs<D> &r, int x) {
         // lanes < D/8 hold the K keyframe: scaled by f(hh)/16 for the K operand
@@ -637,87 +663,83 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
         kfw = 0.0f;
     };
 
-    for (int gb0 = g0; gb0 < g1; gb0 += BATCH) {
-        const int gend = min(g1, gb0 + BATCH);
-        const int x = gb0 + lane;
-        const int64_t o = x < gend ? group_offset(g, bt, b, h, x) : -1;
-        const uint64_t mk = __ballot(o >= 0);
-        const int cnt = __popcll(mk);
-        const bool last_partial = (L & 31) != 0 && gend == ng && ((mk >> (ng - 1 - gb0)) & 1) != 0;
-        const int nfull = cnt - (last_partial ? 1 : 0);
+    // A group is one tile here, so the phases get no carry: -0.0, since
+    // x + -0.0 == x for every x and the add folds away.
+    if (nfull > 0) {
+        float Lg[4], tot;
         __syncthreads();
-        if (o >= 0)
-            glist[__builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mk, 0u))] = o;
+        stage(kb[0], 0);
+        stage(kb[1], 1);
         __syncthreads();
-
-        // A group is one tile here, so the phases get no carry: -0.0, since
-        // x + -0.0 == x for every x and the add folds away.
-        if (nfull > 0) {
-            // past the end of the whole groups the fetches re-read the first one
-            auto rec_at = [&](int k) { return cache + uniform_offset(glist, k < nfull ? k : 0); };
-            // group x: K part in buffer x % NBUF (fetched LEAD steps before the
-            // step that stages it), V part in buffer x % NBUF
-            G8KRegs<D> kb[NBUF];
-            G8VRegs<D> vb[NBUF];
-#pragma unroll
-            for (int y = 0; y <= LEAD; ++y) {
-                load_g8k<D>(kb[y % NBUF], rec_at(y), rec_bytes, lo);
-                if (y < LEAD) load_g8v<D>(vb[y % NBUF], rec_at(y), rec_bytes, lo);
-            }
-            float Lg[4], tot;
-            __syncthreads();
-            stage(kb[0], 0);
-            stage(kb[1], 1);
-            __syncthreads();
-            {
-                const float m = k_phase_g8<D, true, true>(kb[0].kc, sbp(0), kfrow(0), 32, j, n, op, c2E, -0.0f, Lg, tot);
-                update_g8_vmx<D>(st, m, group_vmax<D>(sbp(0)), 5, kfw);
-            }
-            // step i (u = i % NBUF): fetch the K part of group i + 1 + LEAD and
-            // the V part of group i + LEAD, V phase of i (its keyframe weight
-            // joins the open batch), K phase of i + 1, then stage the K part of
-            // group i + 2 for the next step.  The wave is alone in its workgroup:
-            // its LDS accesses stay in program order without barriers.
-            auto step = [&](int i, auto uc) {
-                constexpr int u = decltype(uc)::value;
-                constexpr int un = (u + 1) % NBUF, u2 = (u + 2) % NBUF, ulast = (u + LEAD) % NBUF;
-                load_g8k<D>(kb[u], rec_at(i + 1 + LEAD), rec_bytes, lo);
-                load_g8v<D>(vb[ulast], rec_at(i + LEAD), rec_bytes, lo);
-                const float pt =
-                    v_phase_g8<D, true, true, true, false>(st, vb[u].vc, sbp(i) + 4 * D, Lg, 32, j, n, c2E, AZ, -0.0f);
-                kfw = j == u ? pt * ldexpf(1.0f, st.beta - 20) : kfw;
-                if constexpr (u == NBUF - 1) kf_flush(i, true);
-                const float m = k_phase_g8<D, true, true>(kb[un].kc, sbp(i + 1), kfrow(i + 1), 32, j, n, op, c2E,
-                                                          -0.0f, Lg, tot);
-                update_g8_vmx<D>(st, m, group_vmax<D>(sbp(i + 1)), 5, kfw);
-                stage(kb[u2], i + 2);
-                return i + 1 < nfull;
-            };
-            for (int i = 0;; i += NBUF) {
-                if (!step(i, IC<0>{})) break;
-                if (!step(i + 1, IC<1>{})) break;
-                if (!step(i + 2, IC<2>{})) break;
-                if (!step(i + 3, IC<3>{})) break;
-            }
-            if (((nfull - 1) & 3) != 3) kf_flush(nfull - 1, false);
+        {
+            const float m = k_phase_g8<D, true, true>(kb[0].kc, sbp(0), kfrow(0), 32, j, n, op, c2E, -0.0f, Lg, tot);
+            update_g8_vmx<D>(st, m, group_vmax<D>(sbp(0)), 5, kfw);
         }
-        if (last_partial) {
-            G8KRegs<D> kr;
-            G8VRegs<D> vr;
-            const uint8_t *rec = cache + uniform_offset(glist, cnt - 1);
-            load_g8k<D>(kr, rec, rec_bytes, lo);
-            load_g8v<D>(vr, rec, rec_bytes, lo);
-            // position nfull: its slot holds no group of an open batch
-            __syncthreads();
-            stage(kr, nfull);
-            __syncthreads();
-            const int nval = L - (ng - 1) * 32;
-            float Lg[4], tot;
+        // step i (u = i % NBUF): fetch the K part of group i + 1 + LEAD and the
+        // V part of group i + LEAD, V phase of i (its keyframe weight joins the
+        // open batch), K phase of i + 1, then stage the K part of group i + 2 for
+        // the next step.  The wave is alone in its workgroup: its LDS accesses
+        // stay in program order without barriers.
+        auto step = [&](int i, auto uc) {
+            constexpr int u = decltype(uc)::value;
+            constexpr int un = (u + 1) % NBUF, u2 = (u + 2) % NBUF, ulast = (u + LEAD) % NBUF;
+            load_g8k<D>(kb[u], rec_at(i + 1 + LEAD), rec_bytes, lo);
+            load_g8v<D>(vb[ulast], rec_at(i + LEAD), rec_bytes, lo);
+            const float pt =
+                v_phase_g8<D, true, true, true, false>(st, vb[u].vc, sbp(i) + 4 * D, Lg, 32, j, n, c2E, AZ, -0.0f);
+            kfw = j == u ? pt * ldexpf(1.0f, st.beta - 20) : kfw;
+            if constexpr (u == NBUF - 1) kf_flush(i, true);
             const float m =
-                k_phase_g8<D, false, true>(kr.kc, sbp(nfull), kfrow(nfull), nval, j, n, op, c2E, -0.0f, Lg, tot);
-            update_g8_vmx<D>(st, m, group_vmax<D>(sbp(nfull)), 5, kfw);
-            v_phase_g8<D, false, true>(st, vr.vc, sbp(nfull) + 4 * D, Lg, nval, j, n, c2E, AZ, -0.0f);
+                k_phase_g8<D, true, true>(kb[un].kc, sbp(i + 1), kfrow(i + 1), 32, j, n, op, c2E, -0.0f, Lg, tot);
+            update_g8_vmx<D>(st, m, group_vmax<D>(sbp(i + 1)), 5, kfw);
+            stage(kb[u2], i + 2);
+            return i + 1 < nfull;
+        };
+        // Two waves share each SIMD, and the issue arbiter favours the older one:
+        // with equal runs the first-dispatched half of the grid finished in
+        // about 118 us and the second in about 151 us.  So the wave priority
+        // falls with the run's progress (quarters), and the first-dispatched
+        // half runs one level lower; a wave that falls behind wins the issue
+        // slots until it has caught up.  (Order only: results are unaffected.)
+        const bool older = (blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z)) <
+                           (gridDim.x * gridDim.y * gridDim.z) / 2;
+        const int q1 = nfull >> 2, q2 = nfull >> 1, q3 = (3 * nfull) >> 2;
+        if (older) __builtin_amdgcn_s_setprio(2); else __builtin_amdgcn_s_setprio(3);
+        for (int i = 0;; i += NBUF) {
+            if (i >= q1) {
+                const int lvl = (i >= q3 ? 0 : i >= q2 ? 1 : 2) - (older ? 1 : 0);
+                if (lvl <= 0)
+                    __builtin_amdgcn_s_setprio(0);
+                else if (lvl == 1)
+                    __builtin_amdgcn_s_setprio(1);
+                else
+                    __builtin_amdgcn_s_setprio(2);
+            }
+            if (!step(i, IC<0>{})) break;
+
+            if (!step(i + 1, IC<1>{})) break;
+            if (!step(i + 2, IC<2>{})) break;
+            if (!step(i + 3, IC<3>{})) break;
         }
+        if (((nfull - 1) & 3) != 3) kf_flush(nfull - 1, false);
+        __builtin_amdgcn_s_setprio(0);
+    }
+    if (last_partial) {
+        G8KRegs<D> kr;
+        G8VRegs<D> vr;
+        const uint8_t *rec = cache + uniform_offset(glist, cnt - 1);
+        load_g8k<D>(kr, rec, rec_bytes, lo);
+        load_g8v<D>(vr, rec, rec_bytes, lo);
+        // position nfull: its slot holds no group of an open batch
+        __syncthreads();
+        stage(kr, nfull);
+        __syncthreads();
+        const int nval = L - (ng - 1) * 32;
+        float Lg[4], tot;
+        const float m =
+            k_phase_g8<D, false, true>(kr.kc, sbp(nfull), kfrow(nfull), nval, j, n, op, c2E, -0.0f, Lg, tot);
+        update_g8_vmx<D>(st, m, group_vmax<D>(sbp(nfull)), 5, kfw);
+        v_phase_g8<D, false, true>(st, vr.vc, sbp(nfull) + 4 * D, Lg, nval, j, n, c2E, AZ, -0.0f);
     }
     write_partial_g8<D>(st, ws, row0, G, nsplit, split, lane, j, n);
 }
@@ -862,8 +884,27 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
         TileRegs<D> ra, rb, rc;
         load_step(ra, cc0.off, 0, cc0.nt);
         load_step(rb, cc1.g < g1 ? cc1.off : cc0.off, cc1.g < g1 ? cc1.s : 0, cc1.g < g1 ? cc1.nt : cc0.nt);
+        // wave priority by progress through the run, one level lower for the
+        // first-dispatched half of the grid (as in the kf = 32 kernel)
+        const bool older = (blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z)) <
+                           (gridDim.x * gridDim.y * gridDim.z) / 2;
+        const int ntmax = (kf + 31) >> 5;
+        const int run_steps = (g1 - g0) * 2 * ntmax;
+        auto set_priority = [&](int gc, int s) {
+            const int done = (gc - g0) * 2 * ntmax + s;
+            const int lvl = 3 - min(3, (4 * done) / run_steps) - (older ? 1 : 0);
+            if (lvl <= 0)
+                __builtin_amdgcn_s_setprio(0);
+            else if (lvl == 1)
+                __builtin_amdgcn_s_setprio(1);
+            else if (lvl == 2)
+                __builtin_amdgcn_s_setprio(2);
+            else
+                __builtin_amdgcn_s_setprio(3);
+        };
         auto step = [&](const TileRegs<D> &cur, TileRegs<D> &pf) {
             const int gc = cc0.g, s = cc0.s, ntc = cc0.nt;
+            set_priority(gc, s);
             __syncthreads();
             const bool kp = s < ntc;
             const int t = kp ? s : 2 * ntc - 1 - s;
@@ -921,6 +962,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
         };
         while (step(ra, rc) && step(rb, ra) && step(rc, rb)) {
         }
+        __builtin_amdgcn_s_setprio(0);
     }
     write_partial_g8<D>(st, ws, row0, G, nsplit, split, lane, j, n);
 }
@@ -930,6 +972,7 @@ hipError_t launch_attn_g8(const dkv_config &c, const void *cache, const int32_t 
 {
     dim3 grid(nsplit, c.n_kv_heads, c.batch);
     if (c.kf == 32) {
+        if (chunk > 64) return hipErrorInvalidValue;     // a run's group list holds 64 groups
         if (c.head_dim == 64)
             hipLaunchKernelGGL(k_attn_g8<64>, grid, dim3(64), 0, st, c, (const uint8_t *)cache, bt, q, lens,
                                scale_log2, ws, nsplit, chunk);
