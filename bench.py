@@ -37,11 +37,11 @@ HBM_PEAK_GBPS = 8000.0
 # what the counter reads for a 1 GiB device copy.  Valid only for the kernel
 # sources it was measured on (sha256 below); otherwise traffic is null.
 MEASURED_TRAFFIC = {
-    "workload": "70b", "kf": 32, "bytes": 676204074,
+    "workload": "70b", "kf": 32, "bytes": 676255273,
     "sources": {
-        "dkv_attn_g8.hip": "4c2c6d8175acbfa267e1c887cd38f3307b2a9031d9b092179754ad555d167d57",
-        "dkv_fused_common.h": "644b0e8df654d49fa1afb2c1c437dedd92dc94a926b4d899a969dc9d632a4254",
-        "dkv_common.h": "b02f7f7cbccc9cc4ffc34e8772549e52d168cd5ac360827894c6f7deb653789e",
+        "dkv_attn_g8.hip": "07c6d820c4c9cc9239d7f06518a9e8d68e6a4fcc6a76a418f8f551070547602e",
+        "dkv_fused_common.h": "2c50df85d9aa3b9209a8d244cff5e767abdb35abaf5330c8ee72f33a87d4b4d0",
+        "dkv_common.h": "b510681129fd0cce8d387ea05fcbcff54529be910d0b37376c8c8ebd0444b2b7",
     },
 }
 

@@ -563,7 +563,7 @@ __device__ inline int64_t uniform_offset(const int64_t *list, int k)
 // group i + 1, two independent streams of work that the compiler interleaves
 // in one block of code.  The keyframe terms of every 4 groups are added
 // together by fp32 matrix instructions.  The last step's K phase re-reads the
-// first group of the run: its maximum and V range are already in the state,
+// last group of the run: its maximum and V range are already in the state,
 // so its update changes nothing and its logits are not used.
 template <int D>
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
@@ -605,8 +605,9 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
     const int nfull = cnt - (last_partial ? 1 : 0);
     if (o0 >= 0) glist[__builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mk, 0u))] = o0;
     __syncthreads();
-    // past the end of the whole groups the fetches re-read the first one
-    auto rec_at = [&](int k) { return cache + uniform_offset(glist, k < nfull ? k : 0); };
+    // past the end of the whole groups the fetches re-read the last one (still
+    // in L2: it was fetched a few steps earlier)
+    auto rec_at = [&](int k) { return cache + uniform_offset(glist, k < nfull ? k : nfull - 1); };
 
     const LaneOffsets lo = lane_offsets<D>(g, lane, j, n, true);
     const int rec_bytes = (int)g.rec;
