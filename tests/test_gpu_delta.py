@@ -172,3 +172,27 @@ def test_softmax_scale_argument():
         ref[0, h * G:(h + 1) * G] = oracle.attention_f64(q[0, h * G:(h + 1) * G], enc[(0, h, 0)].recon,
                                                          enc[(0, h, 1)].recon, scale)
     assert U.rel_err(out.cpu().numpy(), ref) <= U.ATTN_TOL
+
+
+# Runs of several whole groups per workgroup: 32 sequences x 8 kv-heads make
+# the split plan cut each sequence into 8 runs (8 groups at kf = 32, 2 at
+# kf = 128), and the lengths put every count of whole groups in a run, with
+# and without a partial last group, through the pipelined kernels (keyframe
+# batches of 4 closed early, a run of one group, the partial group after it).
+RUN_LENS = [0, 1, 31, 32, 33, 63, 64, 65, 96, 97, 127, 128, 129, 160, 192, 224,
+            255, 256, 257, 300, 511, 512, 513, 640, 1000, 1024, 1025, 1500, 2000, 2016, 2047, 2048]
+
+
+@pytest.mark.parametrize("kf", [32, 128])
+def test_runs_of_every_length(kf):
+    w = _case("70b", S=2048, B=32)
+    lens = np.array(RUN_LENS, np.int32)
+    r = U.prefill(w, kf=kf, lens=lens)
+    pairs = {(b, h) for b in range(1, w.B) for h in (0, 5)}
+    enc = U.oracle_encode(w, kf, lens, pairs=pairs)
+    q = synth.queries(w)
+    got = U.attention(r, q)
+    assert np.all(got[0] == 0.0)                      # empty sequence: zero rows
+    ref = U.oracle_attention(enc, w, q, lens, pairs=pairs)
+    assert U.rel_err(got, ref) <= U.ATTN_TOL
+    assert np.isfinite(got).all()
