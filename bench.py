@@ -464,6 +464,11 @@ def main():
     qo = w.B * w.Hq * w.D * 4 * 2
     eff = f16_equiv_bytes(w.B, w.Hkv, w.D, w.S)
     achieved = (comp + qo) / (kern_ms * 1e-3) / 1e9
+
+    # streaming-read ceiling: the library's plain read of the same cache replicas
+    sink = torch.empty(dkv.dkv_stream_read_sink_words(), dtype=torch.int32, device=dev)
+    sr_ms = _time(lambda i: dkv.dkv_stream_read(caches[i % replicas], sink), n_k, stream)
+    sr_gbps = cache_bytes / (sr_ms * 1e-3) / 1e9
     res = {
         "metric": METRIC,
         "value": round(eff / (ms_step * 1e-3) / 1e9, 2),
@@ -494,8 +499,11 @@ def main():
             "traffic": measured_traffic(args.workload, kf, args.kernel),
             "kernel_ms": round(kern_ms, 5),
             "host_issue_ms": round(host_ms, 5),
+            "frac_of_stream_read": round(achieved / sr_gbps, 4),
             "algorithmic_bytes": comp + qo,
         },
+        "stream_read_ceiling": {"GBps": round(sr_gbps, 1), "frac_of_peak": round(sr_gbps / HBM_PEAK_GBPS, 4),
+                                "bytes": cache_bytes, "how": "dkv_stream_read over the same cache replicas"},
     }
     if not args.no_compare:
         res["comparisons"], q4 = comparisons(w, cfg, k, v, q, lens, ws, args.steps, stream, qo)

@@ -214,6 +214,24 @@ dkv_status dkv_attn_decode_f16(const dkv_config *cfg, const uint16_t *k, const u
                                float softmax_scale, float *out, void *workspace,
                                size_t workspace_bytes, dkv_stream_t stream);
 
+/*
+ * Diagnostic: the streaming-read ceiling.  Decode attention is a streaming
+ * read of the cache (the cost model of "KV 캐시 벡터 양자화와 주의 보존 변환",
+ * section "KV 캐시가 왜 병목인가"); this call only reads, with no arithmetic of
+ * the method, so its rate is the practical bandwidth the decode kernels are
+ * measured against.
+ *  buf  (device) any readable buffer; the first floor(bytes/16)*16 bytes are
+ *       read once with 16-byte loads.  bytes >= 16.
+ *  sink (device) uint32 [dkv_stream_read_sink_words()], caller-owned: one word
+ *       per work-item, the XOR of the 32-bit words it read (the XOR of all sink
+ *       words is the XOR of all words read).
+ * Errors: DKV_ERR_ARG (null pointer, bytes < 16), DKV_ERR_WORKSPACE (sink too
+ * small), DKV_ERR_HIP (launch failure).  Asynchronous on `stream`.
+ */
+size_t dkv_stream_read_sink_words(void);
+dkv_status dkv_stream_read(const void *buf, size_t bytes, uint32_t *sink, size_t sink_words,
+                           dkv_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

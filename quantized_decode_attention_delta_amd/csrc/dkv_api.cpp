@@ -21,6 +21,8 @@ hipError_t launch_export(const dkv_config &, const void *, const int32_t *, cons
 hipError_t launch_attn_ref(const dkv_config &, const void *, const int32_t *, const float *,
                            const int32_t *, float, float *, int, int, hipStream_t);
 hipError_t launch_combine(const dkv_config &, const float *, int, float *, hipStream_t);
+hipError_t launch_stream_read(const void *, size_t, uint32_t *, hipStream_t);
+size_t stream_read_sink_words();
 hipError_t launch_attn_fused(const dkv_config &, const void *, const int32_t *, const float *,
                              const int32_t *, float, float *, int, int, hipStream_t);
 bool fused_supported(const dkv_config &);
@@ -334,3 +336,12 @@ dkv_status dkv_attn_decode_f16(const dkv_config *c, const uint16_t *k, const uin
 }
 
 }  // extern "C"
+
+size_t dkv_stream_read_sink_words(void) { return dkv::stream_read_sink_words(); }
+
+dkv_status dkv_stream_read(const void *buf, size_t bytes, uint32_t *sink, size_t sink_words, dkv_stream_t stream)
+{
+    if (!buf || !sink || bytes < 16) return DKV_ERR_ARG;
+    if (sink_words < dkv::stream_read_sink_words()) return DKV_ERR_WORKSPACE;
+    return dkv::hip_status(dkv::launch_stream_read(buf, bytes, sink, (hipStream_t)stream));
+}

@@ -77,6 +77,8 @@ _SIGS = {
     "dkv_q4_0_export": ([_CFG, _P, _P, _I32, _P, _P, _P], _I32),
     "dkv_attn_decode_q4_0": ([_CFG, _P, _P, _P, _F, _P, _P, _SZ, _P], _I32),
     "dkv_attn_decode_f16": ([_CFG, _P, _P, _I32, _P, _P, _F, _P, _P, _SZ, _P], _I32),
+    "dkv_stream_read_sink_words": ([], _SZ),
+    "dkv_stream_read": ([_P, _SZ, _P, _SZ, _P], _I32),
 }
 
 
@@ -288,3 +290,16 @@ def dkv_attn_decode_f16(cfg: Config, k, v, s_max: int, q, seq_lens, out, workspa
         _ptr(workspace, torch.uint8, "workspace"), workspace.numel() if workspace is not None else 0,
         _stream(stream))
     _check("dkv_attn_decode_f16", st)
+
+
+def dkv_stream_read_sink_words() -> int:
+    return load().dkv_stream_read_sink_words()
+
+
+def dkv_stream_read(buf, sink, nbytes=None, stream=None):
+    """Streaming-read ceiling: read `buf` (any GPU tensor) once; sink: int32/uint32 GPU tensor."""
+    import torch
+    n = buf.numel() * buf.element_size() if nbytes is None else int(nbytes)
+    st = load().dkv_stream_read(_ptr(buf, None, "buf"), n, _ptr(sink, (torch.int32,), "sink"), sink.numel(),
+                                _stream(stream))
+    _check("dkv_stream_read", st)

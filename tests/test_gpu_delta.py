@@ -196,3 +196,16 @@ def test_runs_of_every_length(kf):
     ref = U.oracle_attention(enc, w, q, lens, pairs=pairs)
     assert U.rel_err(got, ref) <= U.ATTN_TOL
     assert np.isfinite(got).all()
+
+
+def test_stream_read_reads_every_word():
+    """The streaming-read diagnostic: the XOR of its sink words is the XOR of
+    every 32-bit word of the buffer (each word is read exactly once)."""
+    rng = np.random.default_rng(7)
+    for nbytes in (16, 1040, 3 * 1024 * 1024 + 48):
+        host = rng.integers(0, 2**32, nbytes // 4, dtype=np.uint32)
+        buf = torch.from_numpy(host.view(np.int32)).to(U.DEV)
+        sink = torch.full((dkv.dkv_stream_read_sink_words(),), -1, dtype=torch.int32, device=U.DEV)
+        dkv.dkv_stream_read(buf, sink)
+        got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+        assert got == np.bitwise_xor.reduce(host), nbytes
