@@ -781,7 +781,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
     extern __shared__ f4 lgs[];               // prefixed logits [tile][row] of the current group
 
     G8Ops op;
-    const float c2E = setup_g8<D>(sh, op, q, row0, G, scale_log2, j, n);
+    float c2E = 0.0f;                         // set once the first fetches are out
     const h8 AZ = v_minus8_operand();
 
     RunState<D> st;
@@ -885,6 +885,8 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
         TileRegs<D> ra, rb, rc;
         load_step(ra, cc0.off, 0, cc0.nt);
         load_step(rb, cc1.g < g1 ? cc1.off : cc0.off, cc1.g < g1 ? cc1.s : 0, cc1.g < g1 ? cc1.nt : cc0.nt);
+        // query set-up after the first fetches, so its loads overlap them
+        c2E = setup_g8<D>(sh, op, q, row0, G, scale_log2, j, n);
         // wave priority by progress through the run, one level lower for the
         // first-dispatched half of the grid (as in the kf = 32 kernel)
         const bool older = (blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z)) <
