@@ -142,26 +142,32 @@ __global__ void __launch_bounds__(kRefThreads)
     }
 }
 
-// Merge split partials: grid (B*Hq), one wavefront per output row; lane c
-// holds channels c and c+64.  All loads of a run of 8 splits are issued before
-// the merge arithmetic, so a row costs about one memory round trip per 8 splits.
+// Merge split partials: grid (B*Hq), four wavefronts per output row; lane c
+// holds channels c and c+64.  Wave w merges splits w, w+4, w+8, ...: all loads
+// of a run of 8 of its splits are issued before the merge arithmetic, so a row
+// costs about one memory round trip per 32 splits.  The four waves' (max, sum,
+// numerators) are then merged through LDS by wave 0.
+constexpr int kCombineWaves = 4;
+
 template <int D>
-__global__ void __launch_bounds__(64) k_combine(const float *__restrict__ ws, int nsplit, float *__restrict__ out)
+__global__ void __launch_bounds__(64 * kCombineWaves) k_combine(const float *__restrict__ ws, int nsplit,
+                                                                float *__restrict__ out)
 {
     constexpr int R = part_stride(D);
     constexpr int NCH = D / 64;
     const int64_t row = blockIdx.x;
-    const int c = threadIdx.x;
+    const int c = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const float *p = ws + row * nsplit * R;
     float M = -INFINITY, den = 0.0f, num[NCH];
 #pragma unroll
     for (int k = 0; k < NCH; ++k) num[k] = 0.0f;
-    for (int s0 = 0; s0 < nsplit; s0 += 8) {
+    for (int s0 = wv; s0 < nsplit; s0 += 8 * kCombineWaves) {
         float ms[8], ls[8], a[8][NCH];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-            const bool ok = s0 + u < nsplit;
-            const float *r = p + (int64_t)(ok ? s0 + u : 0) * R;
+            const int sp = s0 + u * kCombineWaves;
+            const bool ok = sp < nsplit;
+            const float *r = p + (int64_t)(ok ? sp : 0) * R;
             ms[u] = r[D];
             ls[u] = ok ? r[D + 1] : 0.0f;
 #pragma unroll
@@ -179,8 +185,34 @@ __global__ void __launch_bounds__(64) k_combine(const float *__restrict__ ws, in
             }
         }
     }
+    __shared__ float sM[kCombineWaves], sden[kCombineWaves], snum[kCombineWaves][D];
+    if (c == 0) {
+        sM[wv] = M;
+        sden[wv] = den;
+    }
 #pragma unroll
-    for (int k = 0; k < NCH; ++k) out[row * D + c + 64 * k] = den > 0.0f ? num[k] / den : 0.0f;
+    for (int k = 0; k < NCH; ++k) snum[wv][c + 64 * k] = num[k];
+    __syncthreads();
+    if (wv == 0) {
+        M = -INFINITY;
+        den = 0.0f;
+#pragma unroll
+        for (int k = 0; k < NCH; ++k) num[k] = 0.0f;
+#pragma unroll
+        for (int w2 = 0; w2 < kCombineWaves; ++w2) {
+            const float l2 = sden[w2];
+            if (l2 > 0.0f) {
+                const float mn = fmaxf(M, sM[w2]);
+                const float al = exp2f(M - mn), w = exp2f(sM[w2] - mn);
+#pragma unroll
+                for (int k = 0; k < NCH; ++k) num[k] = fmaf(w, snum[w2][c + 64 * k], num[k] * al);
+                den = fmaf(w, l2, den * al);
+                M = mn;
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < NCH; ++k) out[row * D + c + 64 * k] = den > 0.0f ? num[k] / den : 0.0f;
+    }
 }
 
 hipError_t launch_attn_ref(const dkv_config &c, const void *cache, const int32_t *bt, const float *q,
@@ -201,9 +233,9 @@ hipError_t launch_combine(const dkv_config &c, const float *ws, int nsplit, floa
 {
     dim3 grid(c.batch * c.n_q_heads);
     if (c.head_dim == 64)
-        hipLaunchKernelGGL(k_combine<64>, grid, dim3(64), 0, st, ws, nsplit, out);
+        hipLaunchKernelGGL(k_combine<64>, grid, dim3(64 * kCombineWaves), 0, st, ws, nsplit, out);
     else
-        hipLaunchKernelGGL(k_combine<128>, grid, dim3(64), 0, st, ws, nsplit, out);
+        hipLaunchKernelGGL(k_combine<128>, grid, dim3(64 * kCombineWaves), 0, st, ws, nsplit, out);
     return hipGetLastError();
 }
 
