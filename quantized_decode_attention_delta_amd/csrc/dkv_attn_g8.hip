@@ -78,7 +78,7 @@ struct G8Ops {
 // Returns 2^E.
 template <int D>
 __device__ inline float setup_g8(G8Shared<D> &sh, G8Ops &op, const float *q, int64_t row0, int G, float scale_log2,
-                                 int j, int n)
+                                 int j, int n, float *qs_out = nullptr)
 {
     constexpr int NB = D / 32;
     const int h2 = n >> 3, hq = n & 7, e = 8 * j + hq;
@@ -117,6 +117,7 @@ __device__ inline float setup_g8(G8Shared<D> &sh, G8Ops &op, const float *q, int
         float incl, all;
         rows_prefix(qsum, j, incl, all);
         Qs[bb] = all;
+        if (qs_out) qs_out[bb] = all;
         if (h2 == 0) {
             sh.qk[(2 * bb) * 32 + e] = __builtin_bit_cast(u4, Bh);
             sh.qk[(2 * bb + 1) * 32 + e] = __builtin_bit_cast(u4, Bl);
@@ -231,6 +232,103 @@ __device__ inline float k_phase_g8(const uint32_t *kc, const uint8_t *sb, const 
     mx = rows_max(mx);
     mx = fmaxf(mx, other_half(mx));
     return mx * c2E;
+}
+
+// K phase of one whole keyframe group of 32 tokens (kf = 32), with the two
+// per-token terms that do not depend on the codes taken out of the code
+// matrix instructions:
+//  - the "-8" of every code: the accumulator of block bb starts at
+//    bias[bb] = -8 * (sum of the head's query over the block) * 2^-20, the
+//    units of the code products, so each block result is sum((c - 8) * q);
+//  - the keyframe logit q.x0, computed for the whole run beforehand
+//    (kf_logits_g8) and passed as `carry`, which the prefix sums add to every
+//    token of the group.
+// Token 0 is the keyframe: its code row reads as zeros and its scale slot
+// holds the group's largest |scale| (used by the V side), so its delta term
+// is dropped here and its logit is the carry alone.
+template <int D, bool FULL>
+__device__ inline float k_phase_g8b(const uint32_t *kc, const uint8_t *sb, int nval, int j, int n, const G8Ops &op,
+                                    const f4 (&bias)[D / 32], float c2E, float carry, float (&Lg)[4])
+{
+    constexpr int NB = D / 32, NP = NB / 2;
+    const int h2 = n >> 3;
+    const int tb = 16 * h2 + 4 * j;          // first of this lane's 4 tokens
+
+    uint32_t sg[4][NP];
+    {
+        const uint32_t *sp = (const uint32_t *)(sb + 2 * D + tb * 2 * NB);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int k = 0; k < NP; ++k) sg[i][k] = sp[i * NP + k];
+    }
+    f4 u = f4{0, 0, 0, 0};
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) {
+        const h8 A0 = unpack8(kc[bb]);
+        const h8 A1 = unpack8(kc[NB + bb]);
+        f4 P = mfma(A0, as_h8(op.qk[0][(2 * bb) * 32]), bias[bb]);
+        P = mfma(A0, as_h8(op.qk[0][(2 * bb + 1) * 32]), P);
+        P = mfma(A1, as_h8(op.qk[1][(2 * bb) * 32]), P);
+        P = mfma(A1, as_h8(op.qk[1][(2 * bb + 1) * 32]), P);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) u[i] = __builtin_fmaf(half_at(sg[i], bb), P[i], u[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float d = u[i] * 1048576.0f;
+        Lg[i] = (FULL || tb + i < nval) ? d : 0.0f;
+    }
+    Lg[0] = tb == 0 ? 0.0f : Lg[0];
+#pragma unroll
+    for (int i = 1; i < 4; ++i) Lg[i] += Lg[i - 1];
+    float incl, all;
+    rows_prefix(Lg[3], j, incl, all);
+    const float allx = other_half(all);           // (every lane takes part in the exchange)
+    const float off = (incl - Lg[3]) + (h2 ? allx : 0.0f) + carry;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Lg[i] += off;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        if (FULL || tb + i < nval) mx = fmaxf(mx, Lg[i]);
+    mx = rows_max(mx);
+    mx = fmaxf(mx, other_half(mx));
+    return mx * c2E;
+}
+
+// Keyframe logits q.x0 of the first `cnt` groups of a run (offsets in `list`),
+// 16 groups per set of matrix instructions: row r of the K operand is the
+// keyframe of group c + r (in the K-code operand order, scaled by f(hh)/16 as
+// the code operand expects), the B operand the query of column half 0.
+// out[x * 8 + hq]: the logit of head hq for the group at position x, in the
+// units of the K phase's logits.
+template <int D>
+__device__ inline void kf_logits_g8(float *out, const int64_t *list, int cnt, const uint8_t *cache, const G8Ops &op,
+                                    int j, int n)
+{
+    constexpr int NB = D / 32;
+    for (int c = 0; c < cnt; c += 16) {
+        const int gi = min(c + n, cnt - 1);
+        const u4 *kfp = (const u4 *)(cache + list[gi]) + j * NB;
+        u4 a[NB];
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb) a[bb] = kfp[bb];
+        f4 C = f4{0, 0, 0, 0};
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb) {
+            u4 v = a[bb];
+            const uint32_t w0 = v[0], w2 = v[2];
+            v[0] = scale_h2_16th(w0);
+            v[2] = scale_h2_16th(w2);
+            C = mfma(as_h8(v), as_h8(op.qk[0][(2 * bb) * 32]), C);
+            C = mfma(as_h8(v), as_h8(op.qk[0][(2 * bb + 1) * 32]), C);
+        }
+        if (n < 8) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) out[(c + 4 * j + i) * 8 + n] = C[i];
+        }
+    }
 }
 
 // Softmax state update for a group with maximum m_g: new running max and V
@@ -593,6 +691,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
     __shared__ __attribute__((aligned(16))) uint32_t side[NSLOT][2 * D];
     __shared__ int64_t glist[BATCH];
     __shared__ G8Shared<D> sh;
+    __shared__ float kls[BATCH * 8];          // keyframe logits [position][head]
 
     // The run's mapped groups (a run has at most BATCH groups: the split plan
     // caps it at 2048 tokens) listed in LDS.  The whole groups go through the
@@ -609,7 +708,10 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
     // in L2: it was fetched a few steps earlier)
     auto rec_at = [&](int k) { return cache + uniform_offset(glist, k < nfull ? k : nfull - 1); };
 
-    const LaneOffsets lo = lane_offsets<D>(g, lane, j, n, true);
+    LaneOffsets lo = lane_offsets<D>(g, lane, j, n, true);
+    // the K keyframe (side lanes < D/8) is read once, by the keyframe-logit
+    // prologue: these lanes' side loads read past the record (zeros)
+    if (lane < D / 8) lo.side = 0x40000000;
     const int rec_bytes = (int)g.rec;
     // group x: K part in buffer x % NBUF (fetched LEAD steps before the step
     // that stages it), V part in buffer x % NBUF.  The first fetches go out
@@ -625,8 +727,18 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
     }
 
     G8Ops op;
-    const float c2E = setup_g8<D>(sh, op, q, row0, G, scale_log2, j, n);
+    float qs[NB];
+    const float c2E = setup_g8<D>(sh, op, q, row0, G, scale_log2, j, n, qs);
     const h8 AZ = v_minus8_operand();
+    // accumulator start of each block's code products: the "-8" term
+    f4 kbias[NB];
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) {
+        const float x = -8.0f * 0x1p-20f * qs[bb];
+        kbias[bb] = f4{x, x, x, x};
+    }
+    if (cnt > 0) kf_logits_g8<D>(kls, glist, cnt, cache, op, j, n);
+    auto klog = [&](int x) { return kls[x * 8 + (n & 7)]; };
 
     RunState<D> st;
     init_state<D>(st);
@@ -637,18 +749,8 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
 
     auto sbp = [&](int x) { return (const uint8_t *)side[x & (NSLOT - 1)]; };
     auto stage = [&](const G8KRegs<D> &r, int x) {
-        // lanes < D/8 hold the K keyframe: scaled by f(hh)/16 for the K operand
-        // (scalar temporaries: bit_cast of a vector element lvalue is miscompiled;
-        // computed by every lane and selected, so the step stays one block of code)
-        u4 v = r.side;
-        const uint32_t w0 = v[0], w2 = v[2];
-        const bool kfl = lane < D / 8;
-        v[0] = kfl ? scale_h2_16th(w0) : w0;
-        v[2] = kfl ? scale_h2_16th(w2) : w2;
-        if (2 * SIDE_LANES == 64 || lane < 2 * SIDE_LANES) ((u4 *)side[x & (NSLOT - 1)])[fresh_lane_id()] = v;
+        if (2 * SIDE_LANES == 64 || lane < 2 * SIDE_LANES) ((u4 *)side[x & (NSLOT - 1)])[fresh_lane_id()] = r.side;
     };
-    // keyframe pieces of this lane's K-operand row (lane n == 0), zeros elsewhere
-    auto kfrow = [&](int x) { return n == 0 ? (const u4 *)(sbp(x) + j * NB * 16) : (const u4 *)sh.qz; };
     // add the keyframe terms of the batch whose last group is at position x:
     // lane (j, n) supplies channel row n of slice cc of group (x & ~3) + j
     // (rows past x, if any, are masked to zero)
@@ -664,16 +766,17 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
         kfw = 0.0f;
     };
 
-    // A group is one tile here, so the phases get no carry: -0.0, since
-    // x + -0.0 == x for every x and the add folds away.
+    // A group is one tile here: the V phases get no carry (-0.0, since
+    // x + -0.0 == x for every x and the add folds away); the K phases get the
+    // group's keyframe logit.
     if (nfull > 0) {
-        float Lg[4], tot;
+        float Lg[4];
         __syncthreads();
         stage(kb[0], 0);
         stage(kb[1], 1);
         __syncthreads();
         {
-            const float m = k_phase_g8<D, true, true>(kb[0].kc, sbp(0), kfrow(0), 32, j, n, op, c2E, -0.0f, Lg, tot);
+            const float m = k_phase_g8b<D, true>(kb[0].kc, sbp(0), 32, j, n, op, kbias, c2E, klog(0), Lg);
             update_g8_vmx<D>(st, m, group_vmax<D>(sbp(0)), 5, kfw);
         }
         // step i (u = i % NBUF): fetch the K part of group i + 1 + LEAD and the
@@ -690,8 +793,8 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
                 v_phase_g8<D, true, true, true, false>(st, vb[u].vc, sbp(i) + 4 * D, Lg, 32, j, n, c2E, AZ, -0.0f);
             kfw = j == u ? pt * ldexpf(1.0f, st.beta - 20) : kfw;
             if constexpr (u == NBUF - 1) kf_flush(i, true);
-            const float m =
-                k_phase_g8<D, true, true>(kb[un].kc, sbp(i + 1), kfrow(i + 1), 32, j, n, op, c2E, -0.0f, Lg, tot);
+            const float m = k_phase_g8b<D, true>(kb[un].kc, sbp(i + 1), 32, j, n, op, kbias, c2E,
+                                                 klog(min(i + 1, nfull - 1)), Lg);
             update_g8_vmx<D>(st, m, group_vmax<D>(sbp(i + 1)), 5, kfw);
             stage(kb[u2], i + 2);
             return i + 1 < nfull;
@@ -736,9 +839,8 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
         stage(kr, nfull);
         __syncthreads();
         const int nval = L - (ng - 1) * 32;
-        float Lg[4], tot;
-        const float m =
-            k_phase_g8<D, false, true>(kr.kc, sbp(nfull), kfrow(nfull), nval, j, n, op, c2E, -0.0f, Lg, tot);
+        float Lg[4];
+        const float m = k_phase_g8b<D, false>(kr.kc, sbp(nfull), nval, j, n, op, kbias, c2E, klog(nfull), Lg);
         update_g8_vmx<D>(st, m, group_vmax<D>(sbp(nfull)), 5, kfw);
         v_phase_g8<D, false, true>(st, vr.vc, sbp(nfull) + 4 * D, Lg, nval, j, n, c2E, AZ, -0.0f);
     }
