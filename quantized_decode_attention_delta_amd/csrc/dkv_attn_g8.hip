@@ -230,7 +230,7 @@ __device__ inline float k_phase_g8(const uint32_t *kc, const uint8_t *sb, const 
     for (int i = 0; i < 4; ++i)
         if (FULL || tb + i < nval) mx = fmaxf(mx, Lg[i]);
     mx = rows_max(mx);
-    mx = fmaxf(mx, other_half(mx));
+    mx = fmax_nc(mx, other_half(mx));
     return mx * c2E;
 }
 
@@ -248,7 +248,8 @@ __device__ inline float k_phase_g8(const uint32_t *kc, const uint8_t *sb, const 
 // is dropped here and its logit is the carry alone.
 template <int D, bool FULL>
 __device__ inline float k_phase_g8b(const uint32_t *kc, const uint8_t *sb, int nval, int j, int n, const G8Ops &op,
-                                    const f4 (&bias)[D / 32], float c2E, float carry, float (&Lg)[4])
+                                    const h8 (&qh)[2][D / 32], const f4 (&bias)[D / 32], float c2E, float carry,
+                                    float (&Lg)[4])
 {
     constexpr int NB = D / 32, NP = NB / 2;
     const int h2 = n >> 3;
@@ -267,18 +268,17 @@ __device__ inline float k_phase_g8b(const uint32_t *kc, const uint8_t *sb, int n
     for (int bb = 0; bb < NB; ++bb) {
         const h8 A0 = unpack8(kc[bb]);
         const h8 A1 = unpack8(kc[NB + bb]);
-        f4 P = mfma(A0, as_h8(op.qk[0][(2 * bb) * 32]), bias[bb]);
+        f4 P = mfma(A0, qh[0][bb], bias[bb]);
         P = mfma(A0, as_h8(op.qk[0][(2 * bb + 1) * 32]), P);
-        P = mfma(A1, as_h8(op.qk[1][(2 * bb) * 32]), P);
+        P = mfma(A1, qh[1][bb], P);
         P = mfma(A1, as_h8(op.qk[1][(2 * bb + 1) * 32]), P);
 #pragma unroll
         for (int i = 0; i < 4; ++i) u[i] = __builtin_fmaf(half_at(sg[i], bb), P[i], u[i]);
     }
+    // logits stay in the units of the code products (2^-20 of the query
+    // units); the factor 2^20 is folded into c2E
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float d = u[i] * 1048576.0f;
-        Lg[i] = (FULL || tb + i < nval) ? d : 0.0f;
-    }
+    for (int i = 0; i < 4; ++i) Lg[i] = (FULL || tb + i < nval) ? u[i] : 0.0f;
     Lg[0] = tb == 0 ? 0.0f : Lg[0];
 #pragma unroll
     for (int i = 1; i < 4; ++i) Lg[i] += Lg[i - 1];
@@ -293,7 +293,7 @@ __device__ inline float k_phase_g8b(const uint32_t *kc, const uint8_t *sb, int n
     for (int i = 0; i < 4; ++i)
         if (FULL || tb + i < nval) mx = fmaxf(mx, Lg[i]);
     mx = rows_max(mx);
-    mx = fmaxf(mx, other_half(mx));
+    mx = fmax_nc(mx, other_half(mx));
     return mx * c2E;
 }
 
@@ -302,7 +302,7 @@ __device__ inline float k_phase_g8b(const uint32_t *kc, const uint8_t *sb, int n
 // keyframe of group c + r (in the K-code operand order, scaled by f(hh)/16 as
 // the code operand expects), the B operand the query of column half 0.
 // out[x * 8 + hq]: the logit of head hq for the group at position x, in the
-// units of the K phase's logits.
+// units of k_phase_g8b's logits (2^-20 of the query units).
 template <int D>
 __device__ inline void kf_logits_g8(float *out, const int64_t *list, int cnt, const uint8_t *cache, const G8Ops &op,
                                     int j, int n)
@@ -326,7 +326,7 @@ __device__ inline void kf_logits_g8(float *out, const int64_t *list, int cnt, co
         }
         if (n < 8) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) out[(c + 4 * j + i) * 8 + n] = C[i];
+            for (int i = 0; i < 4; ++i) out[(c + 4 * j + i) * 8 + n] = C[i] * 0x1p-20f;
         }
     }
 }
@@ -342,10 +342,11 @@ __device__ inline void update_g8_vmx(RunState<D> &st, float m_g, uint32_t vmx, i
     const int ev = (vmx >> 10) == 0 ? -14 : (int)(vmx >> 10) - 15;
     const int beta_g = vmx == 0 ? 24 - lkf : 10 - lkf - ev;       // kf * 16 * |s| * 2^beta < 2^15
 
-    const float m_new = fmaxf(st.m, m_g);
+    const float m_new = fmax_nc(st.m, m_g);
     const int beta_new = min(st.beta, beta_g);
     const float a_m = __builtin_amdgcn_exp2f(st.m - m_new);
     if (__any(m_new != st.m || beta_new != st.beta)) {
+        st.bsc = ldexpf(1.0f, beta_new);
         const float alpha = a_m * ldexpf(1.0f, beta_new - st.beta);
 #pragma unroll
         for (int cc = 0; cc < NCC; ++cc) st.acc[cc] *= alpha;
@@ -429,14 +430,16 @@ __device__ inline float v_phase_g8(RunState<D> &st, const uint32_t *vc, const ui
     st.l += Pt;
 
     // suffix sums of both token halves: own half and the other column half's
-    const float bsc = ldexpf(1.0f, st.beta);
+    // (scaled to the weight units first: 2^beta, and 16 for the token slots
+    // whose code nibble sits 4 bits up)
+    const float bsc = st.bsc, bsc16 = 16.0f * bsc;
     float Sp[2][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const float x = other_half(S[i]);
-        const float k16 = (i & 1) ? bsc : 16.0f * bsc;
-        Sp[0][i] = (h2 ? x : S[i]) * k16;
-        Sp[1][i] = (h2 ? S[i] : x) * k16;
+        const float y = S[i] * ((i & 1) ? bsc : bsc16);
+        const float x = other_half(y);
+        Sp[0][i] = h2 ? x : y;
+        Sp[1][i] = h2 ? y : x;
     }
     if constexpr (FIRST) Sp[0][0] = j == 0 ? 0.0f : Sp[0][0];      // keyframe slot
 
@@ -480,7 +483,7 @@ __device__ inline float v_phase_g8(RunState<D> &st, const uint32_t *vc, const ui
         st.Z[p] = mfma(AZ, Wh, st.Z[p]);
         st.Z[p] = mfma(AZ, Wl, st.Z[p]);
     }
-    if constexpr (FIRST && KFD) kf_fma_g8<D>(st, sb, (Pt + carry) * ldexpf(1.0f, st.beta - 20), j);
+    if constexpr (FIRST && KFD) kf_fma_g8<D>(st, sb, (Pt + carry) * (st.bsc * 0x1p-20f), j);
     return Pt;
 }
 
@@ -494,6 +497,7 @@ __device__ inline void init_state(RunState<D> &st)
     st.m = -INFINITY;
     st.l = 0.0f;
     st.beta = 127;
+    st.bsc = 0x1p127f;
 }
 
 // Split-K partial record of the wave's run: lane (j, n) keeps rows 4j..4j+3
@@ -739,6 +743,14 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
     }
     if (cnt > 0) kf_logits_g8<D>(kls, glist, cnt, cache, op, j, n);
     auto klog = [&](int x) { return kls[x * 8 + (n & 7)]; };
+    // the K phases' logits are in 2^-20 of the query units
+    const float c2Eu = c2E * 1048576.0f;
+    // the hi query operands of both token halves stay in registers
+    h8 qh[2][NB];
+#pragma unroll
+    for (int T = 0; T < 2; ++T)
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb) qh[T][bb] = as_h8(op.qk[T][(2 * bb) * 32]);
 
     RunState<D> st;
     init_state<D>(st);
@@ -776,7 +788,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
         stage(kb[1], 1);
         __syncthreads();
         {
-            const float m = k_phase_g8b<D, true>(kb[0].kc, sbp(0), 32, j, n, op, kbias, c2E, klog(0), Lg);
+            const float m = k_phase_g8b<D, true>(kb[0].kc, sbp(0), 32, j, n, op, qh, kbias, c2Eu, klog(0), Lg);
             update_g8_vmx<D>(st, m, group_vmax<D>(sbp(0)), 5, kfw);
         }
         // step i (u = i % NBUF): fetch the K part of group i + 1 + LEAD and the
@@ -790,10 +802,10 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
             load_g8k<D>(kb[u], rec_at(i + 1 + LEAD), rec_bytes, lo);
             load_g8v<D>(vb[ulast], rec_at(i + LEAD), rec_bytes, lo);
             const float pt =
-                v_phase_g8<D, true, true, true, false>(st, vb[u].vc, sbp(i) + 4 * D, Lg, 32, j, n, c2E, AZ, -0.0f);
-            kfw = j == u ? pt * ldexpf(1.0f, st.beta - 20) : kfw;
+                v_phase_g8<D, true, true, true, false>(st, vb[u].vc, sbp(i) + 4 * D, Lg, 32, j, n, c2Eu, AZ, -0.0f);
+            kfw = j == u ? pt * (st.bsc * 0x1p-20f) : kfw;
             if constexpr (u == NBUF - 1) kf_flush(i, true);
-            const float m = k_phase_g8b<D, true>(kb[un].kc, sbp(i + 1), 32, j, n, op, kbias, c2E,
+            const float m = k_phase_g8b<D, true>(kb[un].kc, sbp(i + 1), 32, j, n, op, qh, kbias, c2Eu,
                                                  klog(min(i + 1, nfull - 1)), Lg);
             update_g8_vmx<D>(st, m, group_vmax<D>(sbp(i + 1)), 5, kfw);
             stage(kb[u2], i + 2);
@@ -840,9 +852,9 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
         __syncthreads();
         const int nval = L - (ng - 1) * 32;
         float Lg[4];
-        const float m = k_phase_g8b<D, false>(kr.kc, sbp(nfull), nval, j, n, op, kbias, c2E, klog(nfull), Lg);
+        const float m = k_phase_g8b<D, false>(kr.kc, sbp(nfull), nval, j, n, op, qh, kbias, c2Eu, klog(nfull), Lg);
         update_g8_vmx<D>(st, m, group_vmax<D>(sbp(nfull)), 5, kfw);
-        v_phase_g8<D, false, true>(st, vr.vc, sbp(nfull) + 4 * D, Lg, nval, j, n, c2E, AZ, -0.0f);
+        v_phase_g8<D, false, true>(st, vr.vc, sbp(nfull) + 4 * D, Lg, nval, j, n, c2Eu, AZ, -0.0f);
     }
     write_partial_g8<D>(st, ws, row0, G, nsplit, split, lane, j, n);
 }

@@ -83,12 +83,21 @@ __device__ inline float rows_sum(float x)
     swap32(a0 + a1, b0, b1);
     return b0 + b1;
 }
+// fp32 max without the quieting copies that fmaxf adds around operands the
+// compiler cannot prove canonical (results of lane exchanges); the operands
+// here are never signalling NaNs.
+__device__ inline float fmax_nc(float a, float b)
+{
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
 __device__ inline float rows_max(float x)
 {
     float a0, a1, b0, b1;
     swap16(x, a0, a1);
-    swap32(fmaxf(a0, a1), b0, b1);
-    return fmaxf(b0, b1);
+    swap32(fmax_nc(a0, a1), b0, b1);
+    return fmax_nc(b0, b1);
 }
 
 // Lane index computed afresh (not CSE-able), to keep it out of the register
@@ -144,6 +153,7 @@ struct RunState {
     f4 Z[D / 32];      // the "-8" part of each block, same units
     float m, l;        // running max (log2 units) and sum of the softmax weights
     int beta;          // fp16 range bias of the V weights
+    float bsc;         // 2^beta (kept by the GQA <= 8 kernels)
 };
 
 }  // namespace dkv
