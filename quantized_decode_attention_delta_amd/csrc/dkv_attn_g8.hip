@@ -72,29 +72,41 @@ struct G8Ops {
     const u4 *qc[2];   // + hl * 32
 };
 
-// Query set-up: head hq's query scaled by softmax_scale*log2(e) and by 2^-E
-// (E = exponent of its largest element), split in hi + lo fp16 in the K-code
-// unpack order with the 16/f factors; the "-8" operand -8*sum(q) per block.
-// Returns 2^E.
+// The query elements lane (j, n) needs, in the K-code unpack order, of head
+// n & 7 of the kv-head's group (rows row0 ..).  Lanes of heads beyond the group
+// read head 0 (every load is unconditional, so they all go out together) and
+// setup_g8 zeroes them.
 template <int D>
-__device__ inline float setup_g8(G8Shared<D> &sh, G8Ops &op, const float *q, int64_t row0, int G, float scale_log2,
+__device__ inline void load_q_g8(float (&xq)[D / 32][8], const float *q, int64_t row0, int G, int j, int n)
+{
+    const int hq = n & 7;
+    const float *qr = q + (row0 + (hq < G ? hq : 0)) * D;
+#pragma unroll
+    for (int bb = 0; bb < D / 32; ++bb)
+#pragma unroll
+        for (int hh = 0; hh < 8; ++hh) xq[bb][hh] = qr[32 * bb + kf_k_channel(j, hh)];
+}
+
+// Query set-up from load_q_g8's elements: head hq's query scaled by
+// softmax_scale*log2(e) and by 2^-E (E = exponent of its largest element),
+// split in hi + lo fp16 in the K-code unpack order with the 16/f factors; the
+// "-8" operand -8*sum(q) per block.  Returns 2^E.
+template <int D>
+__device__ inline float setup_g8(G8Shared<D> &sh, G8Ops &op, const float (&qraw)[D / 32][8], int G, float scale_log2,
                                  int j, int n, float *qs_out = nullptr)
 {
     constexpr int NB = D / 32;
     const int h2 = n >> 3, hq = n & 7, e = 8 * j + hq;
     float xq[NB][8];
     float qm = 0.0f;
-    {
-        const float *qr = q + (row0 + hq) * D;
 #pragma unroll
-        for (int bb = 0; bb < NB; ++bb)
+    for (int bb = 0; bb < NB; ++bb)
 #pragma unroll
-            for (int hh = 0; hh < 8; ++hh) {
-                const float x = hq < G ? qr[32 * bb + kf_k_channel(j, hh)] * scale_log2 : 0.0f;
-                xq[bb][hh] = x;
-                qm = fmaxf(qm, fabsf(x));
-            }
-    }
+        for (int hh = 0; hh < 8; ++hh) {
+            const float x = hq < G ? qraw[bb][hh] * scale_log2 : 0.0f;
+            xq[bb][hh] = x;
+            qm = fmaxf(qm, fabsf(x));
+        }
     qm = rows_max(qm);
     int E = 0;
     if (qm > 0.0f) frexpf(qm, &E);         // |q'| * 2^-E < 1
@@ -297,27 +309,37 @@ __device__ inline float k_phase_g8b(const uint32_t *kc, const uint8_t *sb, int n
     return mx * c2E;
 }
 
-// Keyframe logits q.x0 of the first `cnt` groups of a run (offsets in `list`),
-// 16 groups per set of matrix instructions: row r of the K operand is the
-// keyframe of group c + r (in the K-code operand order, scaled by f(hh)/16 as
-// the code operand expects), the B operand the query of column half 0.
-// out[x * 8 + hq]: the logit of head hq for the group at position x, in the
-// units of k_phase_g8b's logits (2^-20 of the query units).
+// Keyframe logits q.x0 of the first `cnt` (1..64) groups of a run (offsets in
+// `list`), 16 groups per set of matrix instructions: row r of the K operand is
+// the keyframe of group c + r (in the K-code operand order, scaled by f(hh)/16
+// as the code operand expects), the B operand the query of column half 0.
+// kf_load_g8 fetches lane (j, n)'s pieces of every 16-group set (positions past
+// cnt re-read the last group), kf_logits_g8 writes out[x * 8 + hq]: the logit
+// of head hq for the group at position x, in the units of k_phase_g8b's logits
+// (2^-20 of the query units).
 template <int D>
-__device__ inline void kf_logits_g8(float *out, const int64_t *list, int cnt, const uint8_t *cache, const G8Ops &op,
-                                    int j, int n)
+__device__ inline void kf_load_g8(u4 (&a)[4][D / 32], const int64_t *list, int cnt, const uint8_t *cache, int j, int n)
 {
     constexpr int NB = D / 32;
-    for (int c = 0; c < cnt; c += 16) {
-        const int gi = min(c + n, cnt - 1);
-        const u4 *kfp = (const u4 *)(cache + list[gi]) + j * NB;
-        u4 a[NB];
 #pragma unroll
-        for (int bb = 0; bb < NB; ++bb) a[bb] = kfp[bb];
+    for (int c4 = 0; c4 < 4; ++c4) {
+        const u4 *kfp = (const u4 *)(cache + list[min(16 * c4 + n, cnt - 1)]) + j * NB;
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb) a[c4][bb] = kfp[bb];
+    }
+}
+template <int D>
+__device__ inline void kf_logits_g8(float *out, const u4 (&a)[4][D / 32], int cnt, const G8Ops &op, int j, int n)
+{
+    constexpr int NB = D / 32;
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4) {
+        const int c = 16 * c4;
+        if (c >= cnt) break;
         f4 C = f4{0, 0, 0, 0};
 #pragma unroll
         for (int bb = 0; bb < NB; ++bb) {
-            u4 v = a[bb];
+            u4 v = a[c4][bb];
             const uint32_t w0 = v[0], w2 = v[2];
             v[0] = scale_h2_16th(w0);
             v[2] = scale_h2_16th(w2);
@@ -706,11 +728,20 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
     const int cnt = __popcll(mk);
     const bool last_partial = (L & 31) != 0 && g1 == ng && ng > g0 && ((mk >> (ng - 1 - g0)) & 1) != 0;
     const int nfull = cnt - (last_partial ? 1 : 0);
+    if (cnt == 0) {
+        // a run past the sequence's end (or wholly unmapped): an empty record
+        RunState<D> st;
+        init_state<D>(st);
+        write_partial_g8<D>(st, ws, row0, G, nsplit, split, lane, j, n);
+        return;
+    }
     if (o0 >= 0) glist[__builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mk, 0u))] = o0;
     __syncthreads();
     // past the end of the whole groups the fetches re-read the last one (still
-    // in L2: it was fetched a few steps earlier)
-    auto rec_at = [&](int k) { return cache + uniform_offset(glist, k < nfull ? k : nfull - 1); };
+    // in L2: it was fetched a few steps earlier); a run whose only group is a
+    // partial one fetches that group.  Every start-up load is unconditional, so
+    // all of them go out together and each wait covers only what it needs.
+    auto rec_at = [&](int k) { return cache + uniform_offset(glist, k < nfull ? k : max(nfull - 1, 0)); };
 
     LaneOffsets lo = lane_offsets<D>(g, lane, j, n, true);
     // the K keyframe (side lanes < D/8) is read once, by the keyframe-logit
@@ -720,19 +751,21 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
     // group x: K part in buffer x % NBUF (fetched LEAD steps before the step
     // that stages it), V part in buffer x % NBUF.  The first fetches go out
     // before the query set-up, whose own loads then overlap them.
+    float qraw[NB][8];
+    load_q_g8<D>(qraw, q, row0, G, j, n);
+    u4 kfa[4][NB];
+    kf_load_g8<D>(kfa, glist, cnt, cache, j, n);
     G8KRegs<D> kb[NBUF];
     G8VRegs<D> vb[NBUF];
-    if (nfull > 0) {
 #pragma unroll
-        for (int y = 0; y <= LEAD; ++y) {
-            load_g8k<D>(kb[y % NBUF], rec_at(y), rec_bytes, lo);
-            if (y < LEAD) load_g8v<D>(vb[y % NBUF], rec_at(y), rec_bytes, lo);
-        }
+    for (int y = 0; y <= LEAD; ++y) {
+        load_g8k<D>(kb[y % NBUF], rec_at(y), rec_bytes, lo);
+        if (y < LEAD) load_g8v<D>(vb[y % NBUF], rec_at(y), rec_bytes, lo);
     }
 
     G8Ops op;
     float qs[NB];
-    const float c2E = setup_g8<D>(sh, op, q, row0, G, scale_log2, j, n, qs);
+    const float c2E = setup_g8<D>(sh, op, qraw, G, scale_log2, j, n, qs);
     const h8 AZ = v_minus8_operand();
     // accumulator start of each block's code products: the "-8" term
     f4 kbias[NB];
@@ -741,7 +774,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
         const float x = -8.0f * 0x1p-20f * qs[bb];
         kbias[bb] = f4{x, x, x, x};
     }
-    if (cnt > 0) kf_logits_g8<D>(kls, glist, cnt, cache, op, j, n);
+    kf_logits_g8<D>(kls, kfa, cnt, op, j, n);
     auto klog = [&](int x) { return kls[x * 8 + (n & 7)]; };
     // the K phases' logits are in 2^-20 of the query units
     const float c2Eu = c2E * 1048576.0f;
@@ -821,7 +854,12 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
                            (gridDim.x * gridDim.y * gridDim.z) / 2;
         const int q1 = nfull >> 2, q2 = nfull >> 1, q3 = (3 * nfull) >> 2;
         if (older) __builtin_amdgcn_s_setprio(2); else __builtin_amdgcn_s_setprio(3);
-        for (int i = 0;; i += NBUF) {
+        // Whole rounds of 4 steps, then the remaining 0..3 steps.  (No exit from
+        // inside a round: an exit path that shares the loop's back edge makes the
+        // compiler drain every fetch in flight at the top of each round.)
+        const int nround = nfull / NBUF, nrest = nfull % NBUF;
+        for (int r = 0; r < nround; ++r) {
+            const int i = r * NBUF;
             if (i >= q1) {
                 const int lvl = (i >= q3 ? 0 : i >= q2 ? 1 : 2) - (older ? 1 : 0);
                 if (lvl <= 0)
@@ -831,11 +869,16 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
                 else
                     __builtin_amdgcn_s_setprio(2);
             }
-            if (!step(i, IC<0>{})) break;
-
-            if (!step(i + 1, IC<1>{})) break;
-            if (!step(i + 2, IC<2>{})) break;
-            if (!step(i + 3, IC<3>{})) break;
+            step(i, IC<0>{});
+            step(i + 1, IC<1>{});
+            step(i + 2, IC<2>{});
+            step(i + 3, IC<3>{});
+        }
+        if (nrest > 0) {
+            const int i = nround * NBUF;
+            step(i, IC<0>{});
+            if (nrest > 1) step(i + 1, IC<1>{});
+            if (nrest > 2) step(i + 2, IC<2>{});
         }
         if (((nfull - 1) & 3) != 3) kf_flush(nfull - 1, false);
         __builtin_amdgcn_s_setprio(0);
@@ -988,6 +1031,8 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
         r.nt = r.g < g1 ? ntiles(r.g) : 1;
         return r;
     };
+    float qraw[NB][8];
+    load_q_g8<D>(qraw, q, row0, G, j, n);
     Cursor cc0;
     cc0.off = -1;
     cc0.g = next_mapped(g0, cc0.off);
@@ -1000,7 +1045,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
         load_step(ra, cc0.off, 0, cc0.nt);
         load_step(rb, cc1.g < g1 ? cc1.off : cc0.off, cc1.g < g1 ? cc1.s : 0, cc1.g < g1 ? cc1.nt : cc0.nt);
         // query set-up after the first fetches, so its loads overlap them
-        c2E = setup_g8<D>(sh, op, q, row0, G, scale_log2, j, n);
+        c2E = setup_g8<D>(sh, op, qraw, G, scale_log2, j, n);
         // wave priority by progress through the run, one level lower for the
         // first-dispatched half of the grid (as in the kf = 32 kernel)
         const bool older = (blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z)) <
@@ -1136,7 +1181,9 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
     __shared__ G8Shared<D> sh;
 
     G8Ops op;
-    const float c2E = setup_g8<D>(sh, op, q, row0, G, scale_log2, j, n);
+    float qraw[NB][8];
+    load_q_g8<D>(qraw, q, row0, G, j, n);
+    const float c2E = setup_g8<D>(sh, op, qraw, G, scale_log2, j, n);
     const h8 AZ = v_minus8_operand();
     RunState<D> st;
     init_state<D>(st);
