@@ -37,10 +37,10 @@ HBM_PEAK_GBPS = 8000.0
 # what the counter reads for a 1 GiB device copy.  Valid only for the kernel
 # sources it was measured on (sha256 below); otherwise traffic is null.
 MEASURED_TRAFFIC = {
-    "workload": "70b", "kf": 32, "bytes": 676275814,
+    "workload": "70b", "kf": 32, "bytes": 692564307,
     "sources": {
-        "dkv_attn_g8.hip": "90c0d1697a7b0c0ebccf9eb1de4e28f3c66e8062773457321974645e21218cae",
-        "dkv_fused_common.h": "2c50df85d9aa3b9209a8d244cff5e767abdb35abaf5330c8ee72f33a87d4b4d0",
+        "dkv_attn_g8.hip": "64cb67008fdd2c5a0f461f5386653a43fae9d0bc04560af2f0b109eea720d86b",
+        "dkv_fused_common.h": "fdaf23f919b7f5576833b80881851acabb27f65d569c3f957be0ac5f1f8f35bd",
         "dkv_common.h": "b510681129fd0cce8d387ea05fcbcff54529be910d0b37376c8c8ebd0444b2b7",
     },
 }
