@@ -214,9 +214,13 @@ def comparisons(w, cfg, k, v, q, lens, ws, steps, stream, qo):
     return res, q4
 
 
-def quality(w, cfg, cache, q4, k, v, lens):
+def quality(w, cfg, cache, q4, k, v, lens, q):
     """Reconstruction MSE against the fp16 input, over every valid token, from
-    the GPU's own outputs: Delta-KV via dkv_reconstruct, Q4_0 via its export."""
+    the GPU's own outputs: Delta-KV via dkv_reconstruct, Q4_0 via its export.
+    Next to it the attention-preserving distortion of the same reconstructions
+    (dkv_attn_distortion): the mean over (sequence, query head) of
+    d_k = ||q.Khat^T - q.K^T||^2 and d_v = ||a.Vhat - a.V||^2 for this step's
+    queries."""
     import torch
 
     import quantized_decode_attention_delta_amd as dkv
@@ -229,21 +233,40 @@ def quality(w, cfg, cache, q4, k, v, lens):
     dkv.dkv_reconstruct(cfg, cache, None, lens, S, kr, vr)
     mse_d = [float((((kr - k.float()) ** 2) * valid).sum()) / nval,
              float((((vr - v.float()) ** 2) * valid).sum()) / nval]
+    logits = torch.empty(B * w.Hq * S, dtype=torch.float32, device=dev)
+    dk = torch.empty(B, w.Hq, dtype=torch.float32, device=dev)
+    dv = torch.empty_like(dk)
+
+    def distortion(kh, vh):
+        dkv.dkv_attn_distortion(cfg, kh, vh, k, v, S, q, lens, dk, dv, logits)
+        return float(dk.double().mean()), float(dv.double().mean())
+
+    dist_d = distortion(kr, vr)
     del kr, vr
     codes = torch.empty(B, H, 2, S, D // 2, dtype=torch.uint8, device=dev)
     scales = torch.empty(B, H, 2, S, D // 32, dtype=torch.int16, device=dev)
     dkv.dkv_q4_0_export(cfg, q4, lens, S, codes, scales)
-    mse_q = []
+    mse_q, deqs = [], []
     for s, x in enumerate((k, v)):
         c = codes[:, :, s].reshape(B, H, S, D // 32, 16)
         full = torch.cat([(c & 15), (c >> 4)], dim=-1).float() - 8.0
         sc = scales[:, :, s].view(torch.float16).float()[..., None]
-        deq = (full * sc).reshape(B, H, S, D)
+        deq = (full * sc).reshape(B, H, S, D).contiguous()
         mse_q.append(float((((deq - x.float()) ** 2) * valid).sum()) / nval)
-        del c, full, deq
+        deqs.append(deq)
+        del c, full
+    dist_q = distortion(deqs[0], deqs[1])
+    del deqs
     md, mq = sum(mse_d) / 2, sum(mse_q) / 2
     return {"mse_delta_kv": md, "mse_q4_0": mq, "ratio_q4_0_over_delta_kv": round(mq / md, 2) if md > 0 else None,
-            "mse_delta_kv_kv": mse_d, "mse_q4_0_kv": mse_q}
+            "mse_delta_kv_kv": mse_d, "mse_q4_0_kv": mse_q,
+            "attention_distortion": {
+                "d_k_delta_kv": dist_d[0], "d_v_delta_kv": dist_d[1],
+                "d_k_q4_0": dist_q[0], "d_v_q4_0": dist_q[1],
+                "ratio_d_k_q4_0_over_delta_kv": round(dist_q[0] / dist_d[0], 2) if dist_d[0] > 0 else None,
+                "ratio_d_v_q4_0_over_delta_kv": round(dist_q[1] / dist_d[1], 2) if dist_d[1] > 0 else None,
+                "how": "mean over (sequence, query head) of ||q.Khat^T - q.K^T||^2 and ||a.Vhat - a.V||^2, "
+                       "a = softmax on the exact keys, this step's queries (dkv_attn_distortion)"}}
 
 
 def run_mixed(args):
@@ -509,7 +532,7 @@ def main():
         res["comparisons"], q4 = comparisons(w, cfg, k, v, q, lens, ws, args.steps, stream, qo)
         res["comparisons"]["delta_kv"] = {"ms_per_step": res["ms_per_step"], "GBps": res["compressed_GBps"],
                                           "hbm_frac": res["hbm_frac_step"], "bytes": comp}
-        res["quality"] = quality(w, cfg, cache0, q4, k, v, lens)
+        res["quality"] = quality(w, cfg, cache0, q4, k, v, lens, q)
         del q4
     if not args.no_cpu_baseline:
         threads = args.cpu_threads or min(16, os.cpu_count() or 1)

@@ -215,6 +215,33 @@ dkv_status dkv_attn_decode_f16(const dkv_config *cfg, const uint16_t *k, const u
                                size_t workspace_bytes, dkv_stream_t stream);
 
 /*
+ * Diagnostic: attention-preserving distortion of reconstructed keys and values
+ * ("KV 캐시 벡터 양자화와 주의 보존 변환", section 어텐션 보존 왜곡), one
+ * decode step, per (sequence b, query head hq) over the sequence's tokens
+ * t < min(seq_lens[b], s_max), kv-head h = hq / (n_q_heads / n_kv_heads):
+ *   d_k[b][hq] = sum_t ( q . (k_hat_t - k_t) )^2        (unscaled logit row)
+ *   d_v[b][hq] = || sum_t a_t (v_hat_t - v_t) ||^2,
+ *   a_t = softmax_t( softmax_scale * q . k_t )          (exact keys)
+ * The page's expectation E[.] is the mean of these over the rows.
+ *  k_hat, v_hat (device) float [batch][n_kv_heads][s_max][head_dim]: the
+ *               reconstruction under test (dkv_reconstruct's output, or any other)
+ *  k, v         (device) fp16 bits [batch][n_kv_heads][s_max][head_dim]: originals
+ *  q            (device) float [batch][n_q_heads][head_dim]
+ *  seq_lens     (device) int32 [batch]
+ *  softmax_scale  0 => 1/sqrt(head_dim)
+ *  logits       (device) float [batch][n_q_heads][s_max], caller-owned scratch
+ *               (holds the exact scaled logits afterwards)
+ *  d_k, d_v     (device) float [batch][n_q_heads]; a row with no tokens gets 0
+ * Only batch, n_q_heads, n_kv_heads and head_dim of cfg are used (head_dim 64
+ * or 128).  Errors: DKV_ERR_ARG (null pointer, s_max < 1, bad head counts),
+ * DKV_ERR_UNSUPPORTED (head_dim), DKV_ERR_HIP.  Asynchronous on `stream`.
+ */
+dkv_status dkv_attn_distortion(const dkv_config *cfg, const float *k_hat, const float *v_hat,
+                               const uint16_t *k, const uint16_t *v, int32_t s_max, const float *q,
+                               const int32_t *seq_lens, float softmax_scale, float *logits,
+                               float *d_k, float *d_v, dkv_stream_t stream);
+
+/*
  * Diagnostic: the streaming-read ceiling.  Decode attention is a streaming
  * read of the cache (the cost model of "KV 캐시 벡터 양자화와 주의 보존 변환",
  * section "KV 캐시가 왜 병목인가"); this call only reads, with no arithmetic of

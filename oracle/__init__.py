@@ -207,6 +207,37 @@ def attention_f64(q, K, V, scale: float) -> np.ndarray:
     return out
 
 
+def attention_distortion_f64(q, K, V, K_hat, V_hat, scale: float):
+    """Attention-preserving distortion of one decode step ("KV 캐시 벡터 양자화와
+    주의 보존 변환", section 어텐션 보존 왜곡), in float64, for G query heads
+    q[G][D] over one kv-head's keys/values K, V [S][D] and their
+    reconstructions K_hat, V_hat:
+
+      d_k[g] = || q_g K_hat^T - q_g K^T ||^2       the logit row, unscaled dot
+                                                   products as the page prints them
+      d_v[g] = || a_g V_hat - a_g V ||^2          a_g = softmax(scale * q_g K^T),
+                                                   the attention weights on the
+                                                   exact keys (so d_v isolates V)
+
+    The page's expectation is the mean of these over (sequence, head) rows.
+    With S = 0 both are 0.  Returns (d_k[G], d_v[G]).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    K_hat = np.asarray(K_hat, dtype=np.float64)
+    V_hat = np.asarray(V_hat, dtype=np.float64)
+    G = q.shape[0]
+    if K.shape[0] == 0:
+        return np.zeros(G), np.zeros(G)
+    d_k = ((q @ K_hat.T - q @ K.T) ** 2).sum(axis=1)
+    logits = float(np.float32(scale)) * (q @ K.T)                 # [G][S]
+    a = np.exp(logits - logits.max(axis=1, keepdims=True))
+    a /= a.sum(axis=1, keepdims=True)
+    d_v = ((a @ V_hat - a @ V) ** 2).sum(axis=1)
+    return d_k, d_v
+
+
 # ---------------------------------------------------------------- whole caches
 def encode_cache(k, v, seq_lens, kf: int, want_recon: bool = True):
     """Encode every stream of fp16 K/V [B][Hkv][s_max][D].
@@ -224,6 +255,26 @@ def encode_cache(k, v, seq_lens, kf: int, want_recon: bool = True):
             for s, x in ((0, k), (1, v)):
                 out[(b, h, s)] = encode_stream(np.ascontiguousarray(x[b, h, :S]), kf, want_recon)
     return out
+
+
+def attention_distortion_cache(enc, k, v, q, seq_lens, n_kv_heads: int, scale: float):
+    """attention_distortion_f64 for every (sequence, query head) of q[B][Hq][D]
+    over an encoded cache (from encode_cache) and its fp16 inputs k, v
+    [B][Hkv][s_max][D].  Returns (d_k[B][Hq], d_v[B][Hq])."""
+    q = np.asarray(q, dtype=np.float32)
+    B, Hq, D = q.shape
+    G = Hq // n_kv_heads
+    kx = _as_f16_bits(k).view(np.float16)
+    vx = _as_f16_bits(v).view(np.float16)
+    d_k = np.zeros((B, Hq))
+    d_v = np.zeros((B, Hq))
+    for b in range(B):
+        S = int(seq_lens[b])
+        for h in range(n_kv_heads):
+            hq = slice(h * G, (h + 1) * G)
+            d_k[b, hq], d_v[b, hq] = attention_distortion_f64(
+                q[b, hq], kx[b, h, :S], vx[b, h, :S], enc[(b, h, 0)].recon, enc[(b, h, 1)].recon, scale)
+    return d_k, d_v
 
 
 def attention_cache(enc, q, seq_lens, n_kv_heads: int, scale: float, heads=None):

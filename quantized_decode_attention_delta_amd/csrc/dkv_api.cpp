@@ -22,6 +22,9 @@ hipError_t launch_attn_ref(const dkv_config &, const void *, const int32_t *, co
                            const int32_t *, float, float *, int, int, hipStream_t);
 hipError_t launch_combine(const dkv_config &, const float *, int, float *, hipStream_t);
 hipError_t launch_stream_read(const void *, size_t, uint32_t *, hipStream_t);
+hipError_t launch_attn_distortion(const dkv_config &, const float *, const float *, const uint16_t *,
+                                  const uint16_t *, int, const float *, const int32_t *, float, float *, float *,
+                                  float *, hipStream_t);
 size_t stream_read_sink_words();
 hipError_t launch_attn_fused(const dkv_config &, const void *, const int32_t *, const float *,
                              const int32_t *, float, float *, int, int, hipStream_t);
@@ -254,6 +257,19 @@ dkv_status dkv_reconstruct(const dkv_config *c, const void *cache, const int32_t
     if (s_max == 0) return DKV_OK;
     return hip_status(launch_reconstruct(*c, cache, c->page_tokens > 0 ? bt : nullptr, lens, s_max, ko, vo,
                                          (hipStream_t)stream));
+}
+
+dkv_status dkv_attn_distortion(const dkv_config *c, const float *khat, const float *vhat, const uint16_t *k,
+                               const uint16_t *v, int32_t s_max, const float *q, const int32_t *lens,
+                               float softmax_scale, float *logits, float *dk, float *dv, dkv_stream_t stream)
+{
+    if (!c || !khat || !vhat || !k || !v || !q || !lens || !logits || !dk || !dv || s_max < 1) return DKV_ERR_ARG;
+    if (c->batch < 1 || c->n_kv_heads < 1 || c->n_q_heads < 1 || c->n_q_heads % c->n_kv_heads != 0)
+        return DKV_ERR_ARG;
+    if (c->head_dim != 64 && c->head_dim != 128) return DKV_ERR_UNSUPPORTED;
+    const float sc = softmax_scale == 0.0f ? 1.0f / std::sqrt((float)c->head_dim) : softmax_scale;
+    return hip_status(launch_attn_distortion(*c, khat, vhat, k, v, s_max, q, lens, sc, logits, dk, dv,
+                                             (hipStream_t)stream));
 }
 
 dkv_status dkv_export(const dkv_config *c, const void *cache, const int32_t *bt, const int32_t *lens,

@@ -77,6 +77,7 @@ _SIGS = {
     "dkv_q4_0_export": ([_CFG, _P, _P, _I32, _P, _P, _P], _I32),
     "dkv_attn_decode_q4_0": ([_CFG, _P, _P, _P, _F, _P, _P, _SZ, _P], _I32),
     "dkv_attn_decode_f16": ([_CFG, _P, _P, _I32, _P, _P, _F, _P, _P, _SZ, _P], _I32),
+    "dkv_attn_distortion": ([_CFG, _P, _P, _P, _P, _I32, _P, _P, _F, _P, _P, _P, _P], _I32),
     "dkv_stream_read_sink_words": ([], _SZ),
     "dkv_stream_read": ([_P, _SZ, _P, _SZ, _P], _I32),
 }
@@ -226,6 +227,22 @@ def dkv_reconstruct(cfg: Config, cache, block_table, seq_lens, s_max: int, k_out
         _ptr(seq_lens, torch.int32, "seq_lens", cfg.batch), int(s_max),
         _ptr(k_out, torch.float32, "k_out", n), _ptr(v_out, torch.float32, "v_out", n), _stream(stream))
     _check("dkv_reconstruct", st)
+
+
+def dkv_attn_distortion(cfg: Config, k_hat, v_hat, k, v, s_max: int, q, seq_lens, d_k, d_v, logits,
+                        softmax_scale: float = 0.0, stream=None):
+    """Attention-preserving distortion d_k, d_v [B][Hq] of reconstructed K/V against fp16 originals."""
+    import torch
+    n = cfg.batch * cfg.n_kv_heads * s_max * cfg.head_dim
+    st = load().dkv_attn_distortion(
+        ctypes.byref(cfg.c()), _ptr(k_hat, torch.float32, "k_hat", n), _ptr(v_hat, torch.float32, "v_hat", n),
+        _f16(k, "k", n), _f16(v, "v", n), int(s_max),
+        _ptr(q, torch.float32, "q", cfg.batch * cfg.n_q_heads * cfg.head_dim),
+        _ptr(seq_lens, torch.int32, "seq_lens", cfg.batch), float(softmax_scale),
+        _ptr(logits, torch.float32, "logits", cfg.batch * cfg.n_q_heads * s_max),
+        _ptr(d_k, torch.float32, "d_k", cfg.batch * cfg.n_q_heads),
+        _ptr(d_v, torch.float32, "d_v", cfg.batch * cfg.n_q_heads), _stream(stream))
+    _check("dkv_attn_distortion", st)
 
 
 def export_shapes(cfg: Config, s_max: int):

@@ -99,6 +99,11 @@ def test_argument_errors_return_before_launch():
     assert lib.dkv_q4_0_encode(cpg, fake, fake, fake, fake, 10, null) == binding.DKV_ERR_UNSUPPORTED
     # F16 comparison: s_max beyond capacity
     assert lib.dkv_attn_decode_f16(cp, fake, fake, 5000, fake, fake, 0.0, fake, fake, 1 << 30, null) == binding.DKV_ERR_ARG
+    # attention distortion: null pointers, empty s_max, unsupported head_dim
+    d = [fake] * 4
+    assert lib.dkv_attn_distortion(cp, *d, 10, fake, fake, 0.0, fake, fake, null, null) == binding.DKV_ERR_ARG
+    assert lib.dkv_attn_distortion(cp, *d, 0, fake, fake, 0.0, fake, fake, fake, null) == binding.DKV_ERR_ARG
+    assert lib.dkv_attn_distortion(cbad, *d, 10, fake, fake, 0.0, fake, fake, fake, null) == binding.DKV_ERR_UNSUPPORTED
     assert lib.dkv_check_config(None) == binding.DKV_ERR_ARG
     assert dkv.status_str(binding.DKV_ERR_WORKSPACE) == "workspace missing or too small"
 

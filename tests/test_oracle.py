@@ -359,3 +359,70 @@ def test_delta_mse_far_below_q40_on_slow_walks():
     mse_d = np.mean((e.recon - xf) ** 2)
     mse_q = np.mean((deq - xf) ** 2)
     assert mse_d < mse_q / 100, (mse_d, mse_q)
+
+
+# ------------------------------------------------ attention-preserving distortion
+# ("KV 캐시 벡터 양자화와 주의 보존 변환", 어텐션 보존 왜곡): closed forms that pin
+# every part of the definition -- the squared logit error, the softmax scale,
+# the weights taken on the exact keys, and the normalisation of the weights.
+
+def _dist_inputs(S=7, D=32, G=3, seed=5):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((G, D)).astype(np.float32)
+    K = rng.standard_normal((S, D)).astype(np.float16).astype(np.float64)
+    V = rng.standard_normal((S, D)).astype(np.float16).astype(np.float64)
+    return q, K, V
+
+
+def test_distortion_zero_when_exact():
+    q, K, V = _dist_inputs()
+    d_k, d_v = oracle.attention_distortion_f64(q, K, V, K.copy(), V.copy(), 0.3)
+    assert np.all(d_k == 0) and np.all(d_v == 0)
+
+
+def test_distortion_key_offset_closed_form():
+    # K_hat = K + delta * e_c for every token: d_k = S * (q_c * delta)^2 per head,
+    # and d_v stays 0 (the weights use the exact keys, V_hat = V)
+    q, K, V = _dist_inputs()
+    S, c, delta = K.shape[0], 5, 0.125
+    Kh = K.copy()
+    Kh[:, c] += delta
+    d_k, d_v = oracle.attention_distortion_f64(q, K, V, Kh, V, 0.3)
+    np.testing.assert_allclose(d_k, S * (q[:, c].astype(np.float64) * delta) ** 2, rtol=1e-12)
+    assert np.all(d_v == 0)
+
+
+def test_distortion_value_offset_closed_form():
+    # V_hat = V + Delta for every token: the weights sum to 1, so d_v = ||Delta||^2
+    q, K, V = _dist_inputs()
+    Delta = np.linspace(-0.5, 0.5, V.shape[1])
+    d_k, d_v = oracle.attention_distortion_f64(q, K, V, K, V + Delta, 0.3)
+    np.testing.assert_allclose(d_v, np.full(q.shape[0], (Delta ** 2).sum()), rtol=1e-12)
+    assert np.all(d_k == 0)
+
+
+def test_distortion_two_tokens_logistic_weight():
+    # error only in V_0, channel 0, size 1: d_v = a_0^2 with a_0 the logistic of
+    # scale * q.(K_0 - K_1) on the EXACT keys (K_hat is perturbed to catch a
+    # definition that takes the weights from the reconstruction)
+    q, K, V = _dist_inputs(S=2, D=32, G=2)
+    scale = 0.7
+    Vh = V.copy()
+    Vh[0, 0] += 1.0
+    Kh = K + 0.25
+    _, d_v = oracle.attention_distortion_f64(q, K, V, Kh, Vh, scale)
+    # the scale is an fp32 value, as it crosses the C ABI
+    z = float(np.float32(scale)) * (q.astype(np.float64) @ (K[0] - K[1]))
+    a0 = 1.0 / (1.0 + np.exp(-z))
+    np.testing.assert_allclose(d_v, a0 ** 2, rtol=1e-12)
+
+
+def test_distortion_single_token_and_empty():
+    q, K, V = _dist_inputs(S=1)
+    Kh, Vh = K + 0.01, V - 0.02
+    d_k, d_v = oracle.attention_distortion_f64(q, K, V, Kh, Vh, 0.3)
+    np.testing.assert_allclose(d_k, (q.astype(np.float64) @ (Kh[0] - K[0])) ** 2, rtol=1e-12)
+    np.testing.assert_allclose(d_v, np.full(q.shape[0], ((Vh[0] - V[0]) ** 2).sum()), rtol=1e-12)
+    e = np.zeros((0, K.shape[1]))
+    d_k, d_v = oracle.attention_distortion_f64(q, e, e, e, e, 0.3)
+    assert np.all(d_k == 0) and np.all(d_v == 0)
