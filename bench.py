@@ -273,7 +273,10 @@ def run_mixed(args):
     """Serving loop of the mixed workload: paged cache (256-token pages, shuffled
     physical ids), bulk prefill, then per step one appended token per sequence
     followed by decode attention over the grown cache.  A step = append + decode
-    of one layer; the timed steps follow the warm-up steps."""
+    of one layer in one call (dkv_append_attn_decode: the append runs inside the
+    decode's split launch); the timed steps follow the warm-up steps.  The same
+    steps through separate dkv_append + dkv_attn_decode calls, on a copy of the
+    prefilled cache, are timed next to it and must leave identical bytes."""
     import numpy as np
     import torch
 
@@ -319,6 +322,7 @@ def run_mixed(args):
     dkv.dkv_encode_prefill(cfg, cache, state, bt, k, v, lens, w.k.shape[2])
     torch.cuda.synchronize()
     del k, v
+    cache_b, state_b = cache.clone(), state.clone()
     w.k = w.v = None
     kn_t = torch.from_numpy(kn).to(dev)
     vn_t = torch.from_numpy(vn).to(dev)
@@ -329,9 +333,14 @@ def run_mixed(args):
     ws = torch.zeros(dkv.dkv_workspace_bytes(cfg), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
+    out_b = torch.empty_like(out)
+
     def step(s):
-        dkv.dkv_append(cfg, cache, state, bt, kn_t[s], vn_t[s], pos[s])
-        dkv.dkv_attn_decode(cfg, cache, bt, q[s], lens_after[s], out, ws)
+        dkv.dkv_append_attn_decode(cfg, cache, state, bt, kn_t[s], vn_t[s], pos[s], q[s], lens_after[s], out, ws)
+
+    def step_unfused(s):
+        dkv.dkv_append(cfg, cache_b, state_b, bt, kn_t[s], vn_t[s], pos[s])
+        dkv.dkv_attn_decode(cfg, cache_b, bt, q[s], lens_after[s], out_b, ws)
 
     # clocks settle on decode-only calls over the prefilled cache (appends would
     # advance the workload)
@@ -347,6 +356,18 @@ def run_mixed(args):
     ev1.record(stream)
     torch.cuda.synchronize()
     ms_step = ev0.elapsed_time(ev1) / args.steps
+    # the same steps as separate append and decode calls, on the copy
+    for s in range(args.warmup):
+        step_unfused(s)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for s in range(args.warmup, args.warmup + args.steps):
+        step_unfused(s)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_unfused = ev0.elapsed_time(ev1) / args.steps
+    same = bool(torch.equal(cache, cache_b) and torch.equal(state, state_b) and torch.equal(out, out_b))
+    del cache_b, state_b
 
     # the decode kernel alone on the final cache (launches back to back between
     # two events on the kernel's stream: the mean launch duration), and the append alone
@@ -387,6 +408,9 @@ def run_mixed(args):
             "kernel": "fused",
         },
         "layer_steps_per_s": round(1000.0 / ms_step, 2),
+        "unfused": {"ms_per_step": round(ms_unfused, 5), "layer_steps_per_s": round(1000.0 / ms_unfused, 2),
+                    "how": "dkv_append then dkv_attn_decode (3 launches per step) on a copy of the cache",
+                    "identical_cache_state_output": same},
         "compressed_GBps": round((comp_avg + qo) / (ms_step * 1e-3) / 1e9, 2),
         "hbm_frac_step": round((comp_avg + qo) / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "roofline": {

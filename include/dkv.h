@@ -145,6 +145,24 @@ dkv_status dkv_attn_decode(const dkv_config *cfg, const void *cache,
                            const int32_t *seq_lens, float softmax_scale, float *out,
                            void *workspace, size_t workspace_bytes, dkv_stream_t stream);
 
+/*
+ * One serving step in one call: dkv_append of each sequence's new token, then
+ * dkv_attn_decode over the grown cache (the decode step that follows an
+ * append, Delta-KV article "구현"), with the same arguments as those two
+ * calls.  seq_lens must already count the new token.  Where the kf = 32,
+ * GQA <= 8 decode kernel runs (every benchmark workload), the append is done
+ * inside its split launch by the workgroup whose run holds the new token's
+ * group, before it reads that group: two launches per step (split phase,
+ * combine).  Elsewhere the append kernel runs first (three launches).  The
+ * cache bytes, state and output equal those of dkv_append followed by
+ * dkv_attn_decode.  Errors as those two calls.
+ */
+dkv_status dkv_append_attn_decode(const dkv_config *cfg, void *cache, float *state,
+                                  const int32_t *block_table, const uint16_t *k_new,
+                                  const uint16_t *v_new, const int32_t *positions, const float *q,
+                                  const int32_t *seq_lens, float softmax_scale, float *out,
+                                  void *workspace, size_t workspace_bytes, dkv_stream_t stream);
+
 /* The split phase of dkv_attn_decode alone: writes the per-split partial
  * results (acc[D], running max, running sum) to the workspace and launches no
  * combine.  For callers that overlap or merge the combine themselves, and for

@@ -33,7 +33,7 @@ hipError_t launch_attn_fused_long(const dkv_config &, const void *, const int32_
                                   const int32_t *, float, float *, int, int, hipStream_t);
 bool fused_long_supported(const dkv_config &);
 hipError_t launch_attn_g8(const dkv_config &, const void *, const int32_t *, const float *, const int32_t *,
-                          float, float *, int, int, hipStream_t);
+                          float, float *, int, int, hipStream_t, const AppendArgs *);
 bool fused_g8_supported(const dkv_config &);
 bool fused_long_g8_supported(const dkv_config &);
 hipError_t launch_q40_encode(const dkv_config &, void *, const uint16_t *, const uint16_t *,
@@ -197,12 +197,22 @@ static dkv_status attn_common(const dkv_config *c, const void *cache, const int3
     return DKV_OK;
 }
 
+// With `ap` (non-null positions), each sequence's new token is appended first:
+// inside the split kernel where the kf = 32, GQA <= 8 kernel runs, else by the
+// append kernel ahead of it.
 static hipError_t launch_split_phase(const dkv_config &c, const void *cache, const int32_t *bt, const float *q,
-                                     const int32_t *lens, float scale, void *ws, const Plan &p, hipStream_t st)
+                                     const int32_t *lens, float scale, void *ws, const Plan &p, hipStream_t st,
+                                     const AppendArgs *ap = nullptr)
 {
     const int32_t *btp = c.page_tokens > 0 ? bt : nullptr;
+    if (ap && !fused_g8_supported(c)) {
+        const hipError_t e = launch_append(c, ap->cache, ap->state, btp, ap->knew, ap->vnew, ap->positions, st);
+        if (e != hipSuccess) return e;
+        ap = nullptr;
+    }
     if (fused_g8_supported(c) || fused_long_g8_supported(c))
-        return launch_attn_g8(c, cache, btp, q, lens, resolve_scale(c, scale), (float *)ws, p.nsplit, p.chunk, st);
+        return launch_attn_g8(c, cache, btp, q, lens, resolve_scale(c, scale), (float *)ws, p.nsplit, p.chunk, st,
+                              ap);
     if (fused_supported(c))
         return launch_attn_fused(c, cache, btp, q, lens, resolve_scale(c, scale), (float *)ws, p.nsplit, p.chunk,
                                  st);
@@ -220,6 +230,21 @@ dkv_status dkv_attn_decode(const dkv_config *c, const void *cache, const int32_t
     if (st != DKV_OK) return st;
     const Plan p = delta_plan(*c);
     hipError_t e = launch_split_phase(*c, cache, bt, q, lens, scale, ws, p, (hipStream_t)stream);
+    if (e != hipSuccess) return DKV_ERR_HIP;
+    return hip_status(launch_combine(*c, (const float *)ws, p.nsplit, out, (hipStream_t)stream));
+}
+
+dkv_status dkv_append_attn_decode(const dkv_config *c, void *cache, float *state, const int32_t *bt,
+                                  const uint16_t *k, const uint16_t *v, const int32_t *pos, const float *q,
+                                  const int32_t *lens, float scale, float *out, void *ws, size_t ws_bytes,
+                                  dkv_stream_t stream)
+{
+    dkv_status st = attn_common(c, cache, bt, q, lens, out, ws, ws_bytes);
+    if (st != DKV_OK) return st;
+    if (!state || !k || !v || !pos) return DKV_ERR_ARG;
+    const Plan p = delta_plan(*c);
+    const AppendArgs ap{(uint8_t *)cache, state, k, v, pos};
+    hipError_t e = launch_split_phase(*c, cache, bt, q, lens, scale, ws, p, (hipStream_t)stream, &ap);
     if (e != hipSuccess) return DKV_ERR_HIP;
     return hip_status(launch_combine(*c, (const float *)ws, p.nsplit, out, (hipStream_t)stream));
 }

@@ -19,9 +19,11 @@
 // Two kernels: kf = 32 (one tile per group, two groups in flight) and
 // kf = 32*NT, NT = 2..16 (a K pass over the tiles keeps the prefix logits in
 // LDS, a V pass runs over them in reverse carrying the suffix sums).
+#include "dkv_append.h"
 #include "dkv_fused_common.h"
 
 namespace dkv {
+
 
 bool fused_g8_supported(const dkv_config &c) { return vbp_layout(c) != 0 && c.kf == 32; }
 bool fused_long_g8_supported(const dkv_config &c) { return vbp_layout(c) != 0 && c.kf > 32 && c.kf <= 512; }
@@ -691,9 +693,9 @@ __device__ inline int64_t uniform_offset(const int64_t *list, int k)
 // so its update changes nothing and its logits are not used.
 template <int D>
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
-    k_attn_g8(dkv_config cfg, const uint8_t *__restrict__ cache, const int32_t *__restrict__ bt,
+    k_attn_g8(dkv_config cfg, const uint8_t *cache, const int32_t *__restrict__ bt,
               const float *__restrict__ q, const int32_t *__restrict__ seq_lens, float scale_log2,
-              float *__restrict__ ws, int nsplit, int chunk)
+              float *__restrict__ ws, int nsplit, int chunk, AppendArgs ap)
 {
     constexpr int NB = D / 32, NCC = D / 16;
     constexpr int SIDE_LANES = D / 4;
@@ -705,6 +707,20 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
     const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int lane = threadIdx.x, j = lane >> 4, n = lane & 15;
     const int G = g.G;
+    if (ap.positions) {
+        // the run that holds the new token's group appends it first (both
+        // streams), and makes the bytes visible to its own loads below
+        const int pos = ap.positions[b];
+        if (pos >= 0 && pos < g.cap_tokens && (pos >> 5) / chunk == split) {
+            append_token_stream<D>(g, ap.cache, ap.state, bt, ap.knew, ap.vnew, pos, b, h, 0, threadIdx.x);
+            append_token_stream<D>(g, ap.cache, ap.state, bt, ap.knew, ap.vnew, pos, b, h, 1, threadIdx.x);
+            // the stores complete (in this XCD's L2, which the loads below also
+            // use), then the L1 lines the read-modify-write of the V codes
+            // brought in are dropped
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        }
+    }
     const int L = min(seq_lens[b], g.cap_tokens);
     const int ng = (L + 31) >> 5;
     const int g0 = split * chunk, g1 = min(ng, g0 + chunk);
@@ -1129,19 +1145,24 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
     write_partial_g8<D>(st, ws, row0, G, nsplit, split, lane, j, n);
 }
 
+// With `append` (kf = 32 only), the kernel appends each sequence's new token
+// before it decodes: append->positions null means no append.
 hipError_t launch_attn_g8(const dkv_config &c, const void *cache, const int32_t *bt, const float *q,
-                          const int32_t *lens, float scale_log2, float *ws, int nsplit, int chunk, hipStream_t st)
+                          const int32_t *lens, float scale_log2, float *ws, int nsplit, int chunk, hipStream_t st,
+                          const AppendArgs *append)
 {
     dim3 grid(nsplit, c.n_kv_heads, c.batch);
     if (c.kf == 32) {
         if (chunk > 64) return hipErrorInvalidValue;     // a run's group list holds 64 groups
+        const AppendArgs ap = append ? *append : AppendArgs{nullptr, nullptr, nullptr, nullptr, nullptr};
         if (c.head_dim == 64)
             hipLaunchKernelGGL(k_attn_g8<64>, grid, dim3(64), 0, st, c, (const uint8_t *)cache, bt, q, lens,
-                               scale_log2, ws, nsplit, chunk);
+                               scale_log2, ws, nsplit, chunk, ap);
         else
             hipLaunchKernelGGL(k_attn_g8<128>, grid, dim3(64), 0, st, c, (const uint8_t *)cache, bt, q, lens,
-                               scale_log2, ws, nsplit, chunk);
+                               scale_log2, ws, nsplit, chunk, ap);
     } else {
+        if (append && append->positions) return hipErrorInvalidValue;     // the long-interval kernel does not append
         // logit rows (see the kernel): 32 per tile and a spare row when at most
         // 4 query heads share a kv-head, 64 per tile otherwise
         const int nt = (c.kf + 31) / 32;

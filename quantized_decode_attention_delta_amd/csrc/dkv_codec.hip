@@ -19,24 +19,9 @@
 //   code   = min(15, trunc((d*id) + 8.5))
 //   scale  = fp16(s) round-to-nearest-even
 //   xhat  += (code-8) * float(scale)     (exact product, one rounding)
-#include "dkv_q40.h"
+#include "dkv_append.h"
 
 namespace dkv {
-
-struct StreamPtrs {
-    uint8_t *kf;     // keyframe (fp16, permuted)
-    uint16_t *sc;    // scales [kf][nb]
-    uint8_t *cd;     // codes
-};
-
-__device__ inline StreamPtrs stream_ptrs(const Geom &g, uint8_t *rec, int s)
-{
-    StreamPtrs p;
-    p.kf = rec + (s ? g.off_vkf : 0);
-    p.sc = (uint16_t *)(rec + (s ? g.off_vsc : g.off_ksc));
-    p.cd = rec + (s ? g.off_vcd : g.off_kcd);
-    return p;
-}
 
 // ------------------------------------------------------------------------
 // Bulk prefill: grid (groups, Hkv*2, B), one wavefront per (b, h, stream, group).
@@ -150,48 +135,9 @@ __global__ void __launch_bounds__(64) k_append(dkv_config cfg, uint8_t *cache, f
                                                const int32_t *bt, const uint16_t *knew,
                                                const uint16_t *vnew, const int32_t *positions)
 {
-    constexpr int NC = D / 64;
-    constexpr int nb = D / 32;
     const Geom g = make_geom(cfg);
     const int h = blockIdx.y >> 1, s = blockIdx.y & 1, b = blockIdx.z;
-    const int pos = positions[b];
-    if (pos < 0 || pos >= g.cap_tokens) return;
-    const int gi = pos / g.kf, r = pos % g.kf;
-    const int64_t off = group_offset(g, bt, b, h, gi);
-    if (off < 0) return;
-    StreamPtrs p = stream_ptrs(g, cache + off, s);
-    const uint16_t *x = (s ? vnew : knew) + ((int64_t)b * g.Hkv + h) * D;
-    float *st = state + (((int64_t)b * g.Hkv + h) * 2 + s) * D;
-    const int lane = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < NC; ++i) {
-        const int c = lane + 64 * i;
-        const int blk = c >> 5;
-        const uint16_t xv = x[c];
-        if (r == 0) {
-            ((uint16_t *)p.kf)[s ? vkf_pos(D, c, g.vbp) : kkf_pos(nb, c)] = xv;
-            if ((lane & 31) == 0) p.sc[blk] = 0;       // new group: reset the max-|scale| slot
-            st[c] = h2f(xv);
-        } else {
-            float xh = st[c];
-            int code;
-            uint16_t s16;
-            q40_delta_step(h2f(xv), xh, code, s16);
-            if ((lane & 31) == 0) {
-                p.sc[r * nb + blk] = s16;
-                p.sc[blk] = (uint16_t)max((int)p.sc[blk], (int)habs_bits(s16));
-            }
-            if (s == 0) {
-                store_k_codes<D>(p.cd + (int64_t)(r - 1) * (D / 2), blk, code);
-            } else {
-                const int tau = r & 31;
-                uint32_t *w = (uint32_t *)(p.cd + (int64_t)(r >> 5) * 16 * D) + vcode_word(D, tau, c, g.vbp);
-                const int sh = 4 * vcode_nibble(tau);
-                *w = (*w & ~(0xFu << sh)) | ((uint32_t)code << sh);
-            }
-            st[c] = xh;
-        }
-    }
+    append_token_stream<D>(g, cache, state, bt, knew, vnew, positions[b], b, h, s, threadIdx.x);
 }
 
 // ------------------------------------------------------------------------

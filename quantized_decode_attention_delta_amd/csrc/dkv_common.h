@@ -103,6 +103,15 @@ __host__ __device__ inline Geom make_geom(const dkv_config &c)
 
 // Byte offset of the group record of (sequence b, kv-head h, group gi).
 // Returns -1 for an unmapped (or out-of-range) page in paged mode.
+// The new token of each sequence, appended by the decode kernel itself (one
+// launch per serving step): null `positions` means no append.
+struct AppendArgs {
+    uint8_t *cache;                 // the cache the kernel reads, writable
+    float *state;                   // reconstruction state [B][Hkv][2][D]
+    const uint16_t *knew, *vnew;    // fp16 [B][Hkv][D]
+    const int32_t *positions;       // [B]: index of the new token
+};
+
 __host__ __device__ inline int64_t group_offset(const Geom &g, const int32_t *block_table,
                                                 int b, int h, int gi)
 {

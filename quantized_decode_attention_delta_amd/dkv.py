@@ -68,6 +68,7 @@ _SIGS = {
     "dkv_encode_prefill": ([_CFG, _P, _P, _P, _P, _P, _P, _I32, _P], _I32),
     "dkv_append": ([_CFG, _P, _P, _P, _P, _P, _P, _P], _I32),
     "dkv_attn_decode": ([_CFG, _P, _P, _P, _P, _F, _P, _P, _SZ, _P], _I32),
+    "dkv_append_attn_decode": ([_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _F, _P, _P, _SZ, _P], _I32),
     "dkv_attn_decode_ref": ([_CFG, _P, _P, _P, _P, _F, _P, _P, _SZ, _P], _I32),
     "dkv_attn_decode_partial": ([_CFG, _P, _P, _P, _P, _F, _P, _SZ, _P], _I32),
     "dkv_reconstruct": ([_CFG, _P, _P, _P, _I32, _P, _P, _P], _I32),
@@ -200,6 +201,22 @@ def _attn(fn, cfg, cache, block_table, q, seq_lens, out, workspace, softmax_scal
 def dkv_attn_decode(cfg: Config, cache, block_table, q, seq_lens, out, workspace, softmax_scale=0.0,
                     stream=None):
     _attn("dkv_attn_decode", cfg, cache, block_table, q, seq_lens, out, workspace, softmax_scale, stream)
+
+
+def dkv_append_attn_decode(cfg: Config, cache, state, block_table, k_new, v_new, positions, q, seq_lens, out,
+                           workspace, softmax_scale=0.0, stream=None):
+    """dkv_append then dkv_attn_decode in one call (the append fused into the split launch)."""
+    import torch
+    B, H, Hq, D = cfg.batch, cfg.n_kv_heads, cfg.n_q_heads, cfg.head_dim
+    st = load().dkv_append_attn_decode(
+        ctypes.byref(cfg.c()), _ptr(cache, torch.uint8, "cache", dkv_cache_bytes(cfg)),
+        _ptr(state, torch.float32, "state", B * H * 2 * D), _ptr(block_table, torch.int32, "block_table"),
+        _f16(k_new, "k_new", B * H * D), _f16(v_new, "v_new", B * H * D),
+        _ptr(positions, torch.int32, "positions", B), _ptr(q, torch.float32, "q", B * Hq * D),
+        _ptr(seq_lens, torch.int32, "seq_lens", B), float(softmax_scale), _ptr(out, torch.float32, "out", B * Hq * D),
+        _ptr(workspace, torch.uint8, "workspace"), workspace.numel() if workspace is not None else 0,
+        _stream(stream))
+    _check("dkv_append_attn_decode", st)
 
 
 def dkv_attn_decode_ref(cfg: Config, cache, block_table, q, seq_lens, out, workspace, softmax_scale=0.0,

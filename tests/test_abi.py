@@ -99,6 +99,11 @@ def test_argument_errors_return_before_launch():
     assert lib.dkv_q4_0_encode(cpg, fake, fake, fake, fake, 10, null) == binding.DKV_ERR_UNSUPPORTED
     # F16 comparison: s_max beyond capacity
     assert lib.dkv_attn_decode_f16(cp, fake, fake, 5000, fake, fake, 0.0, fake, fake, 1 << 30, null) == binding.DKV_ERR_ARG
+    # one serving step: null state / new rows, short workspace
+    assert lib.dkv_append_attn_decode(cp, fake, null, null, fake, fake, fake, fake, fake, 0.0, fake, fake,
+                                      1 << 30, null) == binding.DKV_ERR_ARG
+    assert lib.dkv_append_attn_decode(cp, fake, fake, null, fake, fake, fake, fake, fake, 0.0, fake, fake,
+                                      16, null) == binding.DKV_ERR_WORKSPACE
     # attention distortion: null pointers, empty s_max, unsupported head_dim
     d = [fake] * 4
     assert lib.dkv_attn_distortion(cp, *d, 10, fake, fake, 0.0, fake, fake, null, null) == binding.DKV_ERR_ARG
