@@ -216,7 +216,8 @@ def comparisons(w, cfg, k, v, q, lens, ws, steps, stream, qo):
 
 def quality(w, cfg, cache, q4, k, v, lens, q):
     """Reconstruction MSE against the fp16 input, over every valid token, from
-    the GPU's own outputs: Delta-KV via dkv_reconstruct, Q4_0 via its export.
+    the GPU's own outputs: Delta-KV via dkv_reconstruct, Q4_0 via its export,
+    Q8_0 (the 8-bit reference, quality only) via dkv_q8_0_encode.
     Next to it the attention-preserving distortion of the same reconstructions
     (dkv_attn_distortion): the mean over (sequence, query head) of
     d_k = ||q.Khat^T - q.K^T||^2 and d_v = ||a.Vhat - a.V||^2 for this step's
@@ -256,13 +257,27 @@ def quality(w, cfg, cache, q4, k, v, lens, q):
         deqs.append(deq)
         del c, full
     dist_q = distortion(deqs[0], deqs[1])
-    del deqs
+    del deqs, codes, scales
+    # Q8_0 of the absolute rows (quality comparison only)
+    c8 = torch.empty(B, H, 2, S, D, dtype=torch.int8, device=dev)
+    s8 = torch.empty(B, H, 2, S, D // 32, dtype=torch.int16, device=dev)
+    dkv.dkv_q8_0_encode(cfg, k, v, lens, S, c8, s8)
+    mse_8, deq8 = [], []
+    for s, x in enumerate((k, v)):
+        sc = s8[:, :, s].view(torch.float16).float()[..., None]
+        deq = (c8[:, :, s].reshape(B, H, S, D // 32, 32).float() * sc).reshape(B, H, S, D).contiguous()
+        mse_8.append(float((((deq - x.float()) ** 2) * valid).sum()) / nval)
+        deq8.append(deq)
+    dist_8 = distortion(deq8[0], deq8[1])
+    del deq8, c8, s8
     md, mq = sum(mse_d) / 2, sum(mse_q) / 2
     return {"mse_delta_kv": md, "mse_q4_0": mq, "ratio_q4_0_over_delta_kv": round(mq / md, 2) if md > 0 else None,
             "mse_delta_kv_kv": mse_d, "mse_q4_0_kv": mse_q,
+            "mse_q8_0": sum(mse_8) / 2, "mse_q8_0_kv": mse_8,
             "attention_distortion": {
                 "d_k_delta_kv": dist_d[0], "d_v_delta_kv": dist_d[1],
                 "d_k_q4_0": dist_q[0], "d_v_q4_0": dist_q[1],
+                "d_k_q8_0": dist_8[0], "d_v_q8_0": dist_8[1],
                 "ratio_d_k_q4_0_over_delta_kv": round(dist_q[0] / dist_d[0], 2) if dist_d[0] > 0 else None,
                 "ratio_d_v_q4_0_over_delta_kv": round(dist_q[1] / dist_d[1], 2) if dist_d[1] > 0 else None,
                 "how": "mean over (sequence, query head) of ||q.Khat^T - q.K^T||^2 and ||a.Vhat - a.V||^2, "

@@ -233,6 +233,25 @@ dkv_status dkv_attn_decode_f16(const dkv_config *cfg, const uint16_t *k, const u
                                size_t workspace_bytes, dkv_stream_t stream);
 
 /*
+ * Quality comparison: plain Q8_0 of absolute values, the 8-bit reference the
+ * Delta-KV article's "벤치마크" section sets Delta-KV against (34 bytes per 32
+ * elements).  Per block of 32 channels of a token: d = max|x| / 127, code =
+ * round-half-away-from-zero(x * (1/d)) in -127..127, stored scale fp16(d)
+ * (round to nearest even); the value it stands for is code * scale.
+ *  k, v     (device) fp16 bits [batch][n_kv_heads][s_max][head_dim]
+ *  seq_lens (device) int32 [batch]; rows t >= min(seq_lens[b], s_max) are
+ *           left untouched
+ *  codes    (device) int8  [batch][n_kv_heads][2][s_max][head_dim]
+ *  scales   (device) uint16 [batch][n_kv_heads][2][s_max][head_dim/32]
+ * Only the quantised arrays are produced (no attention kernel reads them).
+ * Errors: as dkv_check_config, DKV_ERR_ARG (null pointer, s_max < 0),
+ * DKV_ERR_HIP.  Asynchronous on `stream`.
+ */
+dkv_status dkv_q8_0_encode(const dkv_config *cfg, const uint16_t *k, const uint16_t *v,
+                           const int32_t *seq_lens, int32_t s_max, int8_t *codes, uint16_t *scales,
+                           dkv_stream_t stream);
+
+/*
  * Diagnostic: attention-preserving distortion of reconstructed keys and values
  * ("KV 캐시 벡터 양자화와 주의 보존 변환", section 어텐션 보존 왜곡), one
  * decode step, per (sequence b, query head hq) over the sequence's tokens

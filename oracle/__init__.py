@@ -67,9 +67,13 @@ def _load():
     lib.oracle_q40_abs_stream.argtypes = [P, L, I, P, P]
     lib.oracle_q40_dequant_stream.argtypes = [P, P, L, I, P]
     lib.oracle_attention_f64.argtypes = [P, I, P, P, L, I, ctypes.c_float, P]
+    lib.oracle_q80_block.argtypes = [P, P, P]
+    lib.oracle_q80_abs_stream.argtypes = [P, L, I, P, P]
+    lib.oracle_q80_dequant_stream.argtypes = [P, P, L, I, P]
     for name in ("oracle_step", "oracle_encode_stream", "oracle_reconstruct_stream",
                  "oracle_q40_abs_stream", "oracle_q40_dequant_stream", "oracle_attention_f64",
-                 "oracle_q40_pack", "oracle_q40_unpack"):
+                 "oracle_q40_pack", "oracle_q40_unpack", "oracle_q80_block", "oracle_q80_abs_stream",
+                 "oracle_q80_dequant_stream"):
         getattr(lib, name).restype = None
     _lib = lib
     return lib
@@ -191,6 +195,35 @@ def q40_dequant_stream(codes, scales) -> np.ndarray:
     S, D = codes.shape[0], codes.shape[1] * 2
     out = np.zeros((S, D), np.float32)
     _load().oracle_q40_dequant_stream(_p(codes), _p(scales), S, D, _p(out))
+    return out
+
+
+def q80_block(v) -> tuple[int, np.ndarray]:
+    """Q8_0 of one 32-value block (fp32 inputs): (fp16 bits of the scale, int8 codes[32])."""
+    v = np.ascontiguousarray(np.asarray(v, dtype=np.float32))
+    assert v.shape == (32,)
+    d = np.zeros(1, np.uint16)
+    c = np.zeros(32, np.int8)
+    _load().oracle_q80_block(_p(v), _p(d), _p(c))
+    return int(d[0]), c
+
+
+def q80_abs_stream(x) -> tuple[np.ndarray, np.ndarray]:
+    """Q8_0 of the absolute rows of one stream x[S][D] (fp16): codes int8 [S][D], scales uint16 [S][D/32]."""
+    x = _as_f16_bits(x)
+    S, D = x.shape
+    codes = np.zeros((S, D), np.int8)
+    scales = np.zeros((S, D // 32), np.uint16)
+    _load().oracle_q80_abs_stream(_p(x), S, D, _p(codes), _p(scales))
+    return codes, scales
+
+
+def q80_dequant_stream(codes, scales) -> np.ndarray:
+    codes = np.ascontiguousarray(np.asarray(codes, dtype=np.int8))
+    scales = _as_f16_bits(scales)
+    S, D = codes.shape
+    out = np.zeros((S, D), np.float32)
+    _load().oracle_q80_dequant_stream(_p(codes), _p(scales), S, D, _p(out))
     return out
 
 

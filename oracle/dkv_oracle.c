@@ -254,6 +254,54 @@ void oracle_q40_dequant_stream(const uint8_t *codes, const uint16_t *scales,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Plain Q8_0 of absolute values: the 8-bit reference the Delta-KV article's   */
+/* "벤치마크" section compares against (near-lossless next to F16).  The block */
+/* rule is the publicly documented convention of that format: per 32 values,  */
+/*   amax = max |v|,  d = amax / 127,  id = d != 0 ? 1/d : 0,                 */
+/*   code_j = round-half-away-from-zero(v_j * id)  (|code| <= 127),            */
+/*   stored scale = fp16(d) (round to nearest even);                          */
+/*   dequantised value = code_j * float(stored scale).                        */
+/* Each operation is one correctly rounded fp32 step (no FMA).               */
+/* ------------------------------------------------------------------------ */
+
+void oracle_q80_block(const float *v, uint16_t *d16, int8_t *codes)
+{
+    float amax = 0.0f;
+    for (int j = 0; j < 32; ++j) {
+        float a = fabsf(v[j]);
+        if (a > amax) amax = a;
+    }
+    float d = amax / 127.0f;
+    float id = (d != 0.0f) ? 1.0f / d : 0.0f;
+    for (int j = 0; j < 32; ++j) {
+        float t = v[j] * id;
+        codes[j] = (int8_t)roundf(t);     /* |t| <= 127 up to rounding: no clamp needed */
+    }
+    *d16 = oracle_f32_to_f16(d);
+}
+
+void oracle_q80_abs_stream(const uint16_t *x, long S, int D, int8_t *codes, uint16_t *scales)
+{
+    float v[32];
+    for (long t = 0; t < S; ++t)
+        for (int b = 0; b < D / 32; ++b) {
+            for (int j = 0; j < 32; ++j)
+                v[j] = oracle_f16_to_f32(x[t * (long)D + 32 * b + j]);
+            oracle_q80_block(v, &scales[t * (long)(D / 32) + b], codes + t * (long)D + 32 * b);
+        }
+}
+
+void oracle_q80_dequant_stream(const int8_t *codes, const uint16_t *scales, long S, int D, float *out)
+{
+    for (long t = 0; t < S; ++t)
+        for (int b = 0; b < D / 32; ++b) {
+            float sf = oracle_f16_to_f32(scales[t * (long)(D / 32) + b]);
+            for (int j = 0; j < 32; ++j)
+                out[t * (long)D + 32 * b + j] = (float)codes[t * (long)D + 32 * b + j] * sf;
+        }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Decode attention in float64 ([VQ] "왜 복원 오차가 틀린 기준인가")              */
 /*                                                                          */
 /* G query heads that share one kv-head: q[G][D], keys/values K[S][D],       */

@@ -22,6 +22,8 @@ hipError_t launch_attn_ref(const dkv_config &, const void *, const int32_t *, co
                            const int32_t *, float, float *, int, int, hipStream_t);
 hipError_t launch_combine(const dkv_config &, const float *, int, float *, hipStream_t);
 hipError_t launch_stream_read(const void *, size_t, uint32_t *, hipStream_t);
+hipError_t launch_q80_encode(const dkv_config &, const uint16_t *, const uint16_t *, const int32_t *, int, int8_t *,
+                             uint16_t *, hipStream_t);
 hipError_t launch_attn_distortion(const dkv_config &, const float *, const float *, const uint16_t *,
                                   const uint16_t *, int, const float *, const int32_t *, float, float *, float *,
                                   float *, hipStream_t);
@@ -282,6 +284,16 @@ dkv_status dkv_reconstruct(const dkv_config *c, const void *cache, const int32_t
     if (s_max == 0) return DKV_OK;
     return hip_status(launch_reconstruct(*c, cache, c->page_tokens > 0 ? bt : nullptr, lens, s_max, ko, vo,
                                          (hipStream_t)stream));
+}
+
+dkv_status dkv_q8_0_encode(const dkv_config *c, const uint16_t *k, const uint16_t *v, const int32_t *lens,
+                           int32_t s_max, int8_t *codes, uint16_t *scales, dkv_stream_t stream)
+{
+    dkv_status st = dkv_check_config(c);
+    if (st != DKV_OK) return st;
+    if (!k || !v || !lens || !codes || !scales || s_max < 0) return DKV_ERR_ARG;
+    if (s_max == 0) return DKV_OK;
+    return hip_status(launch_q80_encode(*c, k, v, lens, s_max, codes, scales, (hipStream_t)stream));
 }
 
 dkv_status dkv_attn_distortion(const dkv_config *c, const float *khat, const float *vhat, const uint16_t *k,

@@ -532,6 +532,44 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
 }
 
 // ------------------------------------------------------------------------
+// Plain Q8_0 of absolute values (quality comparison only): the 8-bit reference
+// of the Delta-KV article's "벤치마크" section.  Per block of 32 values:
+// d = max|v| / 127, code = round-half-away-from-zero(v * (1/d)), scale fp16(d).
+// One wavefront per run of kQ80Tokens tokens of a (sequence, kv-head, stream);
+// each 32-lane half takes one block.  Writes the canonical arrays directly:
+// codes int8 [B][Hkv][2][s_max][D], scales fp16 [B][Hkv][2][s_max][D/32].
+// ------------------------------------------------------------------------
+constexpr int kQ80Tokens = 16;
+
+template <int D>
+__global__ void __launch_bounds__(64) k_q80_encode(dkv_config cfg, const uint16_t *__restrict__ k,
+                                                   const uint16_t *__restrict__ v, const int32_t *__restrict__ lens,
+                                                   int s_max, int8_t *__restrict__ codes,
+                                                   uint16_t *__restrict__ scales)
+{
+    const int h = blockIdx.y >> 1, s = blockIdx.y & 1, b = blockIdx.z;
+    const int lane = threadIdx.x;
+    const int L = min(lens[b], s_max);
+    const int t0 = blockIdx.x * kQ80Tokens, t1 = min(L, t0 + kQ80Tokens);
+    const int64_t row = (((int64_t)b * cfg.n_kv_heads + h) * 2 + s) * s_max;
+    const uint16_t *x = (s ? v : k) + ((int64_t)b * cfg.n_kv_heads + h) * s_max * D;
+    for (int t = t0; t < t1; ++t) {
+#pragma unroll
+        for (int i = 0; i < D / 64; ++i) {
+            const int c = 64 * i + lane;
+            const float val = h2f(x[(int64_t)t * D + c]);
+            float amax = fabsf(val);
+#pragma unroll
+            for (int o = 16; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 32));
+            const float d = amax / 127.0f;
+            const float id = d != 0.0f ? 1.0f / d : 0.0f;
+            codes[(row + t) * D + c] = (int8_t)roundf(val * id);
+            if ((lane & 31) == 0) scales[(row + t) * (D / 32) + (c >> 5)] = f2h_rn(d);
+        }
+    }
+}
+
+// ------------------------------------------------------------------------
 // Launchers
 // ------------------------------------------------------------------------
 hipError_t launch_q40_encode(const dkv_config &c, void *q4, const uint16_t *k, const uint16_t *v,
@@ -543,6 +581,17 @@ hipError_t launch_q40_encode(const dkv_config &c, void *q4, const uint16_t *k, c
         hipLaunchKernelGGL(k_q40_encode<64>, grid, dim3(64), 0, st, c, (uint8_t *)q4, k, v, lens, s_max);
     else
         hipLaunchKernelGGL(k_q40_encode<128>, grid, dim3(64), 0, st, c, (uint8_t *)q4, k, v, lens, s_max);
+    return hipGetLastError();
+}
+
+hipError_t launch_q80_encode(const dkv_config &c, const uint16_t *k, const uint16_t *v, const int32_t *lens,
+                             int s_max, int8_t *codes, uint16_t *scales, hipStream_t st)
+{
+    dim3 grid((s_max + kQ80Tokens - 1) / kQ80Tokens, c.n_kv_heads * 2, c.batch);
+    if (c.head_dim == 64)
+        hipLaunchKernelGGL(k_q80_encode<64>, grid, dim3(64), 0, st, c, k, v, lens, s_max, codes, scales);
+    else
+        hipLaunchKernelGGL(k_q80_encode<128>, grid, dim3(64), 0, st, c, k, v, lens, s_max, codes, scales);
     return hipGetLastError();
 }
 

@@ -78,6 +78,7 @@ _SIGS = {
     "dkv_q4_0_export": ([_CFG, _P, _P, _I32, _P, _P, _P], _I32),
     "dkv_attn_decode_q4_0": ([_CFG, _P, _P, _P, _F, _P, _P, _SZ, _P], _I32),
     "dkv_attn_decode_f16": ([_CFG, _P, _P, _I32, _P, _P, _F, _P, _P, _SZ, _P], _I32),
+    "dkv_q8_0_encode": ([_CFG, _P, _P, _P, _I32, _P, _P, _P], _I32),
     "dkv_attn_distortion": ([_CFG, _P, _P, _P, _P, _I32, _P, _P, _F, _P, _P, _P, _P], _I32),
     "dkv_stream_read_sink_words": ([], _SZ),
     "dkv_stream_read": ([_P, _SZ, _P, _SZ, _P], _I32),
@@ -244,6 +245,18 @@ def dkv_reconstruct(cfg: Config, cache, block_table, seq_lens, s_max: int, k_out
         _ptr(seq_lens, torch.int32, "seq_lens", cfg.batch), int(s_max),
         _ptr(k_out, torch.float32, "k_out", n), _ptr(v_out, torch.float32, "v_out", n), _stream(stream))
     _check("dkv_reconstruct", st)
+
+
+def dkv_q8_0_encode(cfg: Config, k, v, seq_lens, s_max: int, codes, scales, stream=None):
+    """Q8_0 of the absolute K/V rows: codes int8 [B][Hkv][2][s_max][D], scales fp16 bits [B][Hkv][2][s_max][D/32]."""
+    import torch
+    B, H, D = cfg.batch, cfg.n_kv_heads, cfg.head_dim
+    n = B * H * s_max * D
+    st = load().dkv_q8_0_encode(
+        ctypes.byref(cfg.c()), _f16(k, "k", n), _f16(v, "v", n), _ptr(seq_lens, torch.int32, "seq_lens", B),
+        int(s_max), _ptr(codes, torch.int8, "codes", 2 * n),
+        _ptr(scales, (torch.int16, torch.float16), "scales", 2 * n // 32), _stream(stream))
+    _check("dkv_q8_0_encode", st)
 
 
 def dkv_attn_distortion(cfg: Config, k_hat, v_hat, k, v, s_max: int, q, seq_lens, d_k, d_v, logits,

@@ -147,3 +147,34 @@ def test_delta_kv_closer_to_f16_than_q40():
     e_q = np.abs(outs["q40"] - outs["f16"]).max()
     e_d = np.abs(outs["dkv"] - outs["f16"]).max()
     assert e_d < e_q, (e_d, e_q)
+
+
+@pytest.mark.parametrize("name,kw,lens", [
+    ("tiny", dict(), None),
+    ("8b", dict(S=700, Hq=8, Hkv=2), None),
+    ("8b", dict(S=400, Hq=8, Hkv=2, D=64), None),
+    ("long", dict(S=900, B=2, Hq=8, Hkv=2), None),
+    ("8b", dict(S=300, B=6, Hq=8, Hkv=2), [0, 1, 31, 32, 33, 300]),
+])
+def test_q8_0_encode_bit_exact(name, kw, lens):
+    """Q8_0 codes and fp16 scale bit patterns equal the oracle's Q8_0 of the
+    absolute rows; rows past each sequence's length keep their contents."""
+    w, lens_np, cfg = _setup(name, kw, lens)
+    print(f"q8_0 case {name} {kw} lens={lens}", flush=True)
+    B, H, S, D = w.B, w.Hkv, w.S, w.D
+    k = torch.from_numpy(np.ascontiguousarray(w.k)).to(U.DEV)
+    v = torch.from_numpy(np.ascontiguousarray(w.v)).to(U.DEV)
+    codes = torch.full((B, H, 2, S, D), 0x55, dtype=torch.int8, device=U.DEV)
+    scales = torch.full((B, H, 2, S, D // 32), 0x1234, dtype=torch.int16, device=U.DEV)
+    dkv.dkv_q8_0_encode(cfg, k, v, torch.from_numpy(lens_np).to(U.DEV), S, codes, scales)
+    torch.cuda.synchronize()
+    gc = codes.cpu().numpy()
+    gs = scales.cpu().numpy().view(np.uint16)
+    for b in range(B):
+        L = int(lens_np[b])
+        for h in range(H):
+            for s, x in enumerate((w.k, w.v)):
+                rc, rs = oracle.q80_abs_stream(x[b, h, :L])
+                assert np.array_equal(gc[b, h, s, :L], rc), (b, h, s)
+                assert np.array_equal(gs[b, h, s, :L], rs), (b, h, s)
+                assert np.all(gc[b, h, s, L:] == 0x55) and np.all(gs[b, h, s, L:] == 0x1234)

@@ -426,3 +426,51 @@ def test_distortion_single_token_and_empty():
     e = np.zeros((0, K.shape[1]))
     d_k, d_v = oracle.attention_distortion_f64(q, e, e, e, e, 0.3)
     assert np.all(d_k == 0) and np.all(d_v == 0)
+
+
+# ---------------------------------------------------------------- Q8_0 comparison
+# The 8-bit reference of the Delta-KV article's "벤치마크" section, under the
+# documented rule of that format: d = max|v| / 127, code = round-half-away(v/d),
+# scale stored as fp16(d).  Values below are worked by hand.
+
+def test_q80_hand_blocks():
+    # single spike 1.0: d = 1/127 = 0.0078740..., fp16 RNE: 2^-7 * (1 + 8/1024) -> 0x2008
+    d, c = oracle.q80_block(np.array([1.0] + [0.0] * 31, np.float32))
+    assert d == 0x2008 and c[0] == 127 and not c[1:].any()
+    # d = 1 exactly (max 127): ties round away from zero, both signs
+    v = np.zeros(32, np.float32)
+    v[:7] = [127.0, 2.5, -2.5, 0.5, -0.5, 1.49, -126.5]
+    d, c = oracle.q80_block(v)
+    assert d == 0x3C00
+    assert list(c[:7]) == [127, 3, -3, 1, -1, 1, -127]
+    # all zero: scale +0, codes 0
+    d, c = oracle.q80_block(np.zeros(32, np.float32))
+    assert d == 0x0000 and not c.any()
+
+
+def test_q80_error_bound_and_symmetry():
+    rng = np.random.default_rng(11)
+    for trial in range(300):
+        v = (rng.standard_normal(32) * 10.0 ** rng.uniform(-3, 3)).astype(np.float16).astype(np.float32)
+        d16, c = oracle.q80_block(v)
+        d = np.float64(np.float32(np.abs(v).max()) / np.float32(127.0))
+        ds = np.float64(oracle.f16_to_f32(d16))
+        assert np.abs(c.astype(np.int64)).max() <= 127
+        err = np.abs(v.astype(np.float64) - c.astype(np.float64) * ds)
+        bound = d / 2 * (1 + 1e-6) + 127 * abs(d - ds)
+        assert np.all(err <= bound + 1e-12), (trial, err.max(), bound)
+        d16n, cn = oracle.q80_block(-v)
+        assert d16n == d16 and np.array_equal(cn, -c)
+
+
+def test_q80_stream_matches_blocks():
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((5, 64)).astype(np.float16)
+    codes, scales = oracle.q80_abs_stream(x)
+    for t in range(5):
+        for b in range(2):
+            d, c = oracle.q80_block(x[t, 32 * b:32 * b + 32].astype(np.float32))
+            assert scales[t, b] == d and np.array_equal(codes[t, 32 * b:32 * b + 32], c)
+    deq = oracle.q80_dequant_stream(codes, scales)
+    sc = np.repeat(scales.view(np.float16).astype(np.float32), 32, axis=1)
+    assert np.array_equal(deq, codes.astype(np.float32) * sc)
