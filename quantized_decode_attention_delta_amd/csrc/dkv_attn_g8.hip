@@ -1138,7 +1138,30 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
             if (cc2.g < g1) cc2 = next_pos(cc2);
             return cc0.g < g1;
         };
-        while (step(ra, rc) && step(rb, ra) && step(rc, rb)) {
+        // The run's steps: 2 per tile of each mapped group (only the sequence's
+        // last group can be short).  Whole rounds of 3 steps, then the 0..2
+        // left through one step that rotates the buffers by value: no exit
+        // from inside a round (an exit path that shares the back edge makes
+        // the compiler drain every fetch in flight at the top of each round).
+        int total;
+        {
+            const int xg = g0 + lane;
+            const uint64_t mm = __ballot(xg < g1 && group_offset(g, bt, b, h, xg) >= 0);
+            total = 2 * ntmax * __popcll(mm);
+            if (g1 == ng && ng > g0 && ((mm >> (ng - 1 - g0)) & 1) != 0) total += 2 * (ntiles(ng - 1) - ntmax);
+        }
+        const int nround = total / 3, nrest = total % 3;
+        for (int r = 0; r < nround; ++r) {
+            step(ra, rc);
+            step(rb, ra);
+            step(rc, rb);
+        }
+        for (int x = 0; x < nrest; ++x) {
+            step(ra, rc);
+            const TileRegs<D> t = ra;
+            ra = rb;
+            rb = rc;
+            rc = t;
         }
         __builtin_amdgcn_s_setprio(0);
     }
@@ -1163,6 +1186,7 @@ hipError_t launch_attn_g8(const dkv_config &c, const void *cache, const int32_t 
                                scale_log2, ws, nsplit, chunk, ap);
     } else {
         if (append && append->positions) return hipErrorInvalidValue;     // the long-interval kernel does not append
+        if (chunk > 64) return hipErrorInvalidValue;     // a run's groups are counted over one wave
         // logit rows (see the kernel): 32 per tile and a spare row when at most
         // 4 query heads share a kv-head, 64 per tile otherwise
         const int nt = (c.kf + 31) / 32;
