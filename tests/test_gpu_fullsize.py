@@ -92,3 +92,42 @@ def test_mixed_serving_full_lengths():
     longest = int(np.argmax(w.seq_lens))
     shortest = int(np.argmin(w.seq_lens))
     _run(w, 32, [(longest, 0), (shortest, 3), (2, 7), (12, 1)], paged=True)
+
+
+def test_mixed_fused_serving_steps_full_lengths():
+    """The fused serving step at the benchmark's sizes (16 mixed sequences at
+    their full lengths, shuffled pages, the benchmark's split plan): eight
+    steps leave cache bytes, state and outputs bit-identical to dkv_append
+    followed by dkv_attn_decode."""
+    w = synth.make("mixed", B=16, extra_tokens=8)
+    cfg = U.make_cfg(w, 32, w.page_tokens)
+    table, n = synth.page_table(w)
+    cfg.n_pages = n
+    cfg.max_pages_per_seq = table.shape[1]
+    bt = torch.from_numpy(table).to(U.DEV)
+    lens_np = np.asarray(w.seq_lens, np.int32)
+    s_max = w.k.shape[2]
+    cache = torch.empty(dkv.dkv_cache_bytes(cfg), dtype=torch.uint8, device=U.DEV)
+    state = torch.zeros(w.B, w.Hkv, 2, w.D, dtype=torch.float32, device=U.DEV)
+    k = torch.from_numpy(w.k).to(U.DEV)
+    v = torch.from_numpy(w.v).to(U.DEV)
+    dkv.dkv_encode_prefill(cfg, cache, state, bt, k, v, torch.from_numpy(lens_np).to(U.DEV), s_max)
+    cache_b, state_b = cache.clone(), state.clone()
+    ws = torch.zeros(dkv.dkv_workspace_bytes(cfg), dtype=torch.uint8, device=U.DEV)
+    ws_b = torch.zeros_like(ws)
+    oa = torch.zeros(w.B, w.Hq, w.D, dtype=torch.float32, device=U.DEV)
+    ob = torch.zeros_like(oa)
+    lens = lens_np.copy()
+    for step in range(8):
+        pos = torch.from_numpy(lens.astype(np.int32)).to(U.DEV)
+        kn = torch.stack([k[b, :, int(lens[b])] for b in range(w.B)]).contiguous()
+        vn = torch.stack([v[b, :, int(lens[b])] for b in range(w.B)]).contiguous()
+        lens += 1
+        ln = torch.from_numpy(lens.astype(np.int32)).to(U.DEV)
+        q = torch.from_numpy(synth.queries(w, step=step)).to(U.DEV)
+        dkv.dkv_append(cfg, cache, state, bt, kn, vn, pos)
+        dkv.dkv_attn_decode(cfg, cache, bt, q, ln, oa, ws)
+        dkv.dkv_append_attn_decode(cfg, cache_b, state_b, bt, kn, vn, pos, q, ln, ob, ws_b)
+        torch.cuda.synchronize()
+        assert torch.equal(cache, cache_b) and torch.equal(state, state_b) and torch.equal(oa, ob), step
+    assert torch.isfinite(ob).all()
