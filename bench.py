@@ -37,9 +37,9 @@ HBM_PEAK_GBPS = 8000.0
 # what the counter reads for a 1 GiB device copy.  Valid only for the kernel
 # sources it was measured on (sha256 below); otherwise traffic is null.
 MEASURED_TRAFFIC = {
-    "workload": "70b", "kf": 32, "bytes": 692364365,
+    "workload": "70b", "kf": 32, "bytes": 692390917,
     "sources": {
-        "dkv_attn_g8.hip": "f0abe5b36a44c4f9f57efe8e5557023c7656fc106dba2dbefcd0a73328683caa",
+        "dkv_attn_g8.hip": "0c343f056b996ccd86343ee0541bfcd9fe4e684bb2ca9085089d8036a6c4df02",
         "dkv_fused_common.h": "fdaf23f919b7f5576833b80881851acabb27f65d569c3f957be0ac5f1f8f35bd",
         "dkv_common.h": "3b302839f810f8e0f48d1491035b2d391a13053c69aed1c169162f01349d5e17",
     },
