@@ -104,6 +104,9 @@ def parse():
                     help="run the decode kernels this long before the warmup steps (GPU clocks settle)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-compare", action="store_true", help="skip the F16 / Q4_0 comparisons and the MSE report")
+    ap.add_argument("--graph-layers", type=int, default=None,
+                    help="decode steps of this many layers captured in one HIP graph and replayed "
+                         "(default 32 for the launch-bound tiny and 8b workloads, 0 otherwise)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first copy a 1 GiB device buffer 3 times (a plain copy kernel of known size, "
                          "to scale the FETCH_SIZE / WRITE_SIZE counters of a profiled run)")
@@ -172,6 +175,46 @@ def cpu_baseline(w, kf, budget_s, threads, min_s=10.0):
                   f"+ float64 attention of {G} query heads, pairs on {threads} host threads, {t_total:.1f} s",
         "layer_steps_per_s_extrapolated": round(done / t_total / len(pairs), 6),
     }
+
+
+def graph_layers(cfg, caches, q, lens, layers, stream, replays=50):
+    """A decoder's view of a launch-bound layer: the decode steps of `layers`
+    layers (each its own copy of the cache) captured in one HIP graph (two
+    kernels per layer, no host launch in between) and replayed; the replays are
+    timed with HIP events on the replay stream."""
+    import torch
+
+    import quantized_decode_attention_delta_amd as dkv
+    if len(caches) < layers:
+        caches = caches + [caches[0].clone() for _ in range(layers - len(caches))]
+    out = torch.empty(cfg.batch, cfg.n_q_heads, cfg.head_dim, dtype=torch.float32, device=q.device)
+    ws = torch.zeros(dkv.dkv_workspace_bytes(cfg), dtype=torch.uint8, device=q.device)
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):                  # warm-up outside the capture
+        for l in range(layers):
+            dkv.dkv_attn_decode(cfg, caches[l], None, q, lens, out, ws)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for l in range(layers):
+            dkv.dkv_attn_decode(cfg, caches[l], None, q, lens, out, ws)
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    rs = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(rs)
+    for _ in range(replays):
+        g.replay()
+    e1.record(rs)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (replays * layers)
+    return {"layers": layers, "ms_per_layer_step": round(ms, 5), "layer_steps_per_s": round(1000.0 / ms, 2),
+            "how": f"{layers} layers' decode steps (split + combine each, a cache copy per layer) in one "
+                   f"HIP graph, {replays} replays timed with HIP events"}
 
 
 def _time(fn, n, stream):
@@ -575,6 +618,9 @@ def main():
         "stream_read_ceiling": {"GBps": round(sr_gbps, 1), "frac_of_peak": round(sr_gbps / HBM_PEAK_GBPS, 4),
                                 "bytes": cache_bytes, "how": "dkv_stream_read over the same cache replicas"},
     }
+    layers = args.graph_layers if args.graph_layers is not None else (32 if args.workload in ("tiny", "8b") else 0)
+    if layers > 0:
+        res["graph_layers"] = graph_layers(cfg, caches, q, lens, layers, stream)
     if not args.no_compare:
         res["comparisons"], q4 = comparisons(w, cfg, k, v, q, lens, ws, args.steps, stream, qo)
         res["comparisons"]["delta_kv"] = {"ms_per_step": res["ms_per_step"], "GBps": res["compressed_GBps"],
