@@ -26,6 +26,7 @@ CASES = [
     ("70b", dict(S=200, B=2, Hq=16, Hkv=2, extra_tokens=40), 0, 32, 35),
     ("8b", dict(S=200, B=2, Hq=8, Hkv=2, D=64, extra_tokens=40), 0, 32, 35),
     ("8b", dict(S=300, B=2, Hq=8, Hkv=2, extra_tokens=70), 0, 64, 70),      # long-interval kernel: append first
+    ("70b", dict(S=200, B=2, Hq=16, Hkv=1, extra_tokens=40), 0, 32, 35),    # 16 heads per kv-head: append first
 ]
 
 
