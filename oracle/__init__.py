@@ -15,6 +15,10 @@ Canonical encoded layout of one stream (what every function here produces):
 
 with ``n_delta = S - ceil(S/kf)``; delta token t sits at row
 ``(t//kf)*(kf-1) + t%kf - 1``.
+
+``strided_encode_stream`` is the strided-reference variant: every token's Q4_0
+residual against the nearest of the references at positions 0, stride, ...
+(fp16 rows kept exactly), with the reference index stored per token.
 """
 from __future__ import annotations
 
@@ -70,10 +74,13 @@ def _load():
     lib.oracle_q80_block.argtypes = [P, P, P]
     lib.oracle_q80_abs_stream.argtypes = [P, L, I, P, P]
     lib.oracle_q80_dequant_stream.argtypes = [P, P, L, I, P]
+    lib.oracle_sqdist_f16.argtypes = [P, P, I]
+    lib.oracle_sqdist_f16.restype = ctypes.c_double
+    lib.oracle_strided_encode_stream.argtypes = [P, L, I, I, I, P, P, P, P, P]
     for name in ("oracle_step", "oracle_encode_stream", "oracle_reconstruct_stream",
                  "oracle_q40_abs_stream", "oracle_q40_dequant_stream", "oracle_attention_f64",
                  "oracle_q40_pack", "oracle_q40_unpack", "oracle_q80_block", "oracle_q80_abs_stream",
-                 "oracle_q80_dequant_stream"):
+                 "oracle_q80_dequant_stream", "oracle_strided_encode_stream"):
         getattr(lib, name).restype = None
     _lib = lib
     return lib
@@ -225,6 +232,38 @@ def q80_dequant_stream(codes, scales) -> np.ndarray:
     out = np.zeros((S, D), np.float32)
     _load().oracle_q80_dequant_stream(_p(codes), _p(scales), S, D, _p(out))
     return out
+
+
+class StridedStream:
+    """One stream coded against strided references: ``refs`` uint16
+    [ceil(S/stride), D] (fp16 bits of tokens 0, stride, ...), ``ref_idx`` int32
+    [S], ``codes`` uint8 [S, D/2] and ``scales`` uint16 [S, D/32] (the Q4_0
+    residual of every token, in the canonical byte order above), ``recon``
+    float32 [S, D]."""
+    __slots__ = ("refs", "ref_idx", "codes", "scales", "recon")
+
+
+def sqdist_f16(a, b) -> float:
+    """Squared distance of two fp16 rows, summed in double in channel order."""
+    a, b = _as_f16_bits(a), _as_f16_bits(b)
+    assert a.shape == b.shape and a.ndim == 1
+    return float(_load().oracle_sqdist_f16(_p(a), _p(b), a.shape[0]))
+
+
+def strided_encode_stream(x, stride: int, window: int = 0) -> StridedStream:
+    """Strided-reference residual coding of one stream x[S][D] (fp16)."""
+    x = _as_f16_bits(x)
+    S, D = x.shape
+    e = StridedStream()
+    e.refs = np.zeros(((S + stride - 1) // stride, D), np.uint16)
+    e.ref_idx = np.zeros(S, np.int32)
+    e.codes = np.zeros((S, D // 2), np.uint8)
+    e.scales = np.zeros((S, D // 32), np.uint16)
+    e.recon = np.zeros((S, D), np.float32)
+    if S:
+        _load().oracle_strided_encode_stream(_p(x), S, D, stride, window, _p(e.refs), _p(e.ref_idx),
+                                             _p(e.codes), _p(e.scales), _p(e.recon))
+    return e
 
 
 def attention_f64(q, K, V, scale: float) -> np.ndarray:

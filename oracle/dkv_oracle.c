@@ -337,3 +337,73 @@ void oracle_attention_f64(const float *q, int G, const float *K, const float *V,
     }
     free(l);
 }
+
+/* ------------------------------------------------------------------------ */
+/* Strided-reference residual coding (the gist.science explainer of DeltaKV,
+ * "3. 제안 방법론", A: "Strided Reference Selection", "Residual Encoding",
+ * "Reconstruction"; section 2 motivates references far back in the history).
+ *
+ * References: the tokens at positions 0, stride, 2*stride, ... , kept as their
+ * exact fp16 rows.  Token t chooses, among the references k with
+ * k*stride <= t (and, when window > 0, k > t/stride - window), the one nearest
+ * to it: smallest squared Euclidean distance between the fp16 rows.  The
+ * distance is summed in double over channels 0..D-1 in order, each product
+ * and each sum rounded on its own (the difference of two fp16 values is exact
+ * in double); the lowest index wins ties.  The residual x_t - r (one fp32
+ * subtraction per channel) is coded with the Q4_0 block rule above, and
+ * xhat_t = r + (code - 8) * scale (exact product, one rounding).  A reference
+ * token picks itself (distance 0) or an identical earlier row, so it is
+ * reconstructed exactly.  Plain reading: the mean of the most similar
+ * references is taken over one reference (the nearest); the residual coder is
+ * Q4_0 instead of a trained compressor. */
+double oracle_sqdist_f16(const uint16_t *a, const uint16_t *b, int D)
+{
+    double s = 0.0;
+    for (int c = 0; c < D; ++c) {
+        double d = (double)oracle_f16_to_f32(a[c]) - (double)oracle_f16_to_f32(b[c]);
+        double sq = d * d;
+        s = s + sq;
+    }
+    return s;
+}
+
+void oracle_strided_encode_stream(const uint16_t *x, long S, int D, int stride, int window,
+                                  uint16_t *refs, int32_t *ref_idx, uint8_t *codes, uint16_t *scales,
+                                  float *recon)
+{
+    float v[32];
+    uint8_t q[32];
+    for (long k = 0; k * stride < S; ++k) memcpy(refs + k * (long)D, x + k * stride * (long)D, 2 * (size_t)D);
+    for (long t = 0; t < S; ++t) {
+        const uint16_t *xt = x + t * (long)D;
+        const long kt = t / stride;
+        const long k0 = (window > 0 && kt - window + 1 > 0) ? kt - window + 1 : 0;
+        long best = k0;
+        double bd = oracle_sqdist_f16(xt, refs + k0 * (long)D, D);
+        for (long k = k0 + 1; k <= kt; ++k) {
+            double d = oracle_sqdist_f16(xt, refs + k * (long)D, D);
+            if (d < bd) {
+                bd = d;
+                best = k;
+            }
+        }
+        ref_idx[t] = (int32_t)best;
+        const uint16_t *r = refs + best * (long)D;
+        for (int b = 0; b < D / 32; ++b) {
+            for (int j = 0; j < 32; ++j) {
+                int c = 32 * b + j;
+                v[j] = oracle_f16_to_f32(xt[c]) - oracle_f16_to_f32(r[c]);
+            }
+            uint16_t s16;
+            oracle_q40_block(v, &s16, q);
+            scales[t * (long)(D / 32) + b] = s16;
+            oracle_q40_pack(q, codes + t * (long)(D / 2) + 16 * b);
+            float sf = oracle_f16_to_f32(s16);
+            for (int j = 0; j < 32; ++j) {
+                int c = 32 * b + j;
+                float step = (float)((int)q[j] - 8) * sf;
+                recon[t * (long)D + c] = oracle_f16_to_f32(r[c]) + step;
+            }
+        }
+    }
+}
