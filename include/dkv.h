@@ -296,6 +296,57 @@ size_t dkv_stream_read_sink_words(void);
 dkv_status dkv_stream_read(const void *buf, size_t bytes, uint32_t *sink, size_t sink_words,
                            dkv_stream_t stream);
 
+/*
+ * Strided-reference residual cache (the gist.science explainer of DeltaKV,
+ * section 3.A: "Strided Reference Selection", "Residual Encoding",
+ * "Reconstruction").  The tokens at positions 0, kf, 2*kf, ... (cfg->kf is the
+ * stride) are kept as exact fp16 reference rows; every token stores the index
+ * of its nearest reference and the Q4_0 code of its residual against it, and
+ * decodes as reference + (code - 8) * scale.  Nearest: smallest squared
+ * distance of the fp16 rows, summed in double over the channels in order
+ * without fused multiply-add, lowest index on ties, among references
+ * k <= t / kf (and k > t / kf - window when window > 0).  Contiguous mode only
+ * (page_tokens must be 0), at most 65536 references per sequence; otherwise
+ * DKV_ERR_UNSUPPORTED.
+ *
+ * Cache: streams [batch][n_kv_heads][K, V] of dkv_strided_layout()[4] bytes
+ * each; inside a stream, at the offsets of dkv_strided_layout():
+ *   [0] refs   fp16 [nref][head_dim]        nref = layout[5] = ceil(capacity / kf)
+ *   [1] codes  u8   [capacity][head_dim/2]  Q4_0 bytes, byte i of a block: code i | code i+16 << 4
+ *   [2] scales fp16 [capacity][head_dim/32]
+ *   [3] idx    u16  [capacity]              reference index per token
+ */
+size_t dkv_strided_cache_bytes(const dkv_config *cfg);  /* 0 if cfg is invalid or unsupported */
+
+/* layout (host) int64 [6]: plane offsets [0..3], stream bytes [4], nref [5]. */
+dkv_status dkv_strided_layout(const dkv_config *cfg, int64_t *layout);
+
+/*
+ * Encode tokens [0, min(seq_lens[b], s_max, capacity)) of every sequence.
+ *  k, v     (device) fp16 [batch][n_kv_heads][s_max][head_dim]
+ *  seq_lens (device) int32 [batch]
+ *  cache    (device) dkv_strided_cache_bytes(cfg) bytes; the encoded tokens'
+ *           entries and references are written, the rest is left untouched
+ *  window   0: every earlier reference is a candidate; else the last `window`
+ * One workgroup per (32-token tile, kv-head, K/V, sequence).  Errors: as
+ * dkv_check_config, DKV_ERR_UNSUPPORTED (see above), DKV_ERR_ARG (null
+ * pointer, s_max < 0, window < 0), DKV_ERR_HIP.  Asynchronous on `stream`.
+ */
+dkv_status dkv_strided_encode_prefill(const dkv_config *cfg, void *cache, const uint16_t *k,
+                                      const uint16_t *v, const int32_t *seq_lens, int32_t s_max,
+                                      int32_t window, dkv_stream_t stream);
+
+/*
+ * Decode attention over the strided-reference cache: out[b][hq] =
+ * softmax(scale * q . K_hat^T) V_hat over tokens t < min(seq_lens[b], capacity),
+ * arguments as dkv_attn_decode (workspace of dkv_workspace_bytes(cfg) bytes).
+ * Two launches on `stream`: the split phase (32-token tiles rebuilt in fp32),
+ * then the split combine.  A sequence of length 0 gives zero rows.
+ */
+dkv_status dkv_strided_attn_decode(const dkv_config *cfg, const void *cache, const float *q,
+                                   const int32_t *seq_lens, float softmax_scale, float *out,
+                                   void *workspace, size_t workspace_bytes, dkv_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -28,6 +28,12 @@ hipError_t launch_attn_distortion(const dkv_config &, const float *, const float
                                   const uint16_t *, int, const float *, const int32_t *, float, float *, float *,
                                   float *, hipStream_t);
 size_t stream_read_sink_words();
+int64_t strided_cache_bytes(const dkv_config &);
+void strided_plane_offsets(const dkv_config &, int64_t *);
+hipError_t launch_strided_encode(const dkv_config &, void *, const uint16_t *, const uint16_t *, const int32_t *, int,
+                                 int, hipStream_t);
+hipError_t launch_strided_attn(const dkv_config &, const void *, const float *, const int32_t *, float, float *, int,
+                               int, hipStream_t);
 hipError_t launch_attn_fused(const dkv_config &, const void *, const int32_t *, const float *,
                              const int32_t *, float, float *, int, int, hipStream_t);
 bool fused_supported(const dkv_config &);
@@ -384,6 +390,57 @@ dkv_status dkv_attn_decode_f16(const dkv_config *c, const uint16_t *k, const uin
     if (!ws || ws_bytes < workspace_total(*c)) return DKV_ERR_WORKSPACE;
     hipError_t e = launch_attn_f16(*c, k, v, s_max, q, lens, resolve_scale(*c, scale), (float *)ws, p.nsplit,
                                    p.chunk, (hipStream_t)stream);
+    if (e != hipSuccess) return DKV_ERR_HIP;
+    return hip_status(launch_combine(*c, (const float *)ws, p.nsplit, out, (hipStream_t)stream));
+}
+
+// ---------------------------------------------------------- strided references
+// Contiguous mode only; the reference index of a token is 16 bits.
+static dkv_status strided_check(const dkv_config *c)
+{
+    dkv_status st = dkv_check_config(c);
+    if (st != DKV_OK) return st;
+    if (c->page_tokens != 0) return DKV_ERR_UNSUPPORTED;
+    if ((c->max_tokens + (int64_t)c->kf - 1) / c->kf > 65536) return DKV_ERR_UNSUPPORTED;
+    if (c->n_kv_heads > 32767 || c->batch > 65535) return DKV_ERR_UNSUPPORTED;
+    return DKV_OK;
+}
+
+size_t dkv_strided_cache_bytes(const dkv_config *c)
+{
+    if (strided_check(c) != DKV_OK) return 0;
+    return (size_t)strided_cache_bytes(*c);
+}
+
+dkv_status dkv_strided_layout(const dkv_config *c, int64_t *layout)
+{
+    dkv_status st = strided_check(c);
+    if (st != DKV_OK) return st;
+    if (!layout) return DKV_ERR_ARG;
+    strided_plane_offsets(*c, layout);
+    return DKV_OK;
+}
+
+dkv_status dkv_strided_encode_prefill(const dkv_config *c, void *cache, const uint16_t *k, const uint16_t *v,
+                                      const int32_t *lens, int32_t s_max, int32_t window, dkv_stream_t stream)
+{
+    dkv_status st = strided_check(c);
+    if (st != DKV_OK) return st;
+    if (!cache || !k || !v || !lens || s_max < 0 || window < 0) return DKV_ERR_ARG;
+    if (s_max == 0) return DKV_OK;
+    return hip_status(launch_strided_encode(*c, cache, k, v, lens, s_max, window, (hipStream_t)stream));
+}
+
+dkv_status dkv_strided_attn_decode(const dkv_config *c, const void *cache, const float *q, const int32_t *lens,
+                                   float scale, float *out, void *ws, size_t ws_bytes, dkv_stream_t stream)
+{
+    dkv_status st = strided_check(c);
+    if (st != DKV_OK) return st;
+    if (!cache || !q || !lens || !out) return DKV_ERR_ARG;
+    if (!ws || ws_bytes < workspace_total(*c)) return DKV_ERR_WORKSPACE;
+    const Plan p = tile_plan(*c);
+    hipError_t e = launch_strided_attn(*c, cache, q, lens, resolve_scale(*c, scale), (float *)ws, p.nsplit, p.chunk,
+                                       (hipStream_t)stream);
     if (e != hipSuccess) return DKV_ERR_HIP;
     return hip_status(launch_combine(*c, (const float *)ws, p.nsplit, out, (hipStream_t)stream));
 }

@@ -1,0 +1,345 @@
+// Strided-reference residual KV cache: encode and decode attention.
+//
+// The variant of the gist.science explainer of DeltaKV (section 3.A,
+// "Strided Reference Selection", "Residual Encoding", "Reconstruction";
+// section 2 on similar tokens far apart): the tokens at positions 0, stride,
+// 2*stride, ... are kept as exact fp16 reference rows; every token stores the
+// index of its nearest reference and the Q4_0 code of its residual against
+// it, and decodes as reference + residual.  The residual coder is the Q4_0
+// block rule of the Delta-KV codec (dkv_q40.h) in place of a trained
+// compressor, and the "mean of the most similar references" is taken over the
+// single nearest one.
+//
+// Nearest: smallest squared distance between the fp16 rows, summed in double
+// over the channels in order with every product and sum rounded on its own
+// (no fused multiply-add), lowest index on ties, among references k with
+// k*stride <= t and, when window > 0, k > t/stride - window.  The difference of
+// two fp16 values is exact in double, so the choice is a fixed function of the
+// inputs.
+//
+// Layout of one stream (sequence b, kv-head h, K or V), streams [b][h][K,V]
+// back to back, every plane 256-byte aligned:
+//   refs    fp16 [nref][D]    nref = ceil(capacity / stride)
+//   codes   u8   [cap][D/2]   Q4_0 bytes, byte i of a block: code i | code i+16 << 4
+//   scales  fp16 [cap][D/32]
+//   idx     u16  [cap]        reference index of every token
+//
+// Decode attention: one workgroup of 256 threads per run of 32-token tiles
+// of one (sequence, kv-head), all the kv-head's query heads.  Per tile the
+// threads rebuild K and V (reference row gathered by index + dequantised
+// residual) in fp32, take the logits, run the online softmax and accumulate
+// the weighted V rows; the partial (acc, m, l) goes to the split-K combine
+// shared with the Delta-KV kernels.  HBM traffic per token is the two
+// streams' codes, scales and index (74 bytes each at D = 128); the reference
+// rows, 1/stride of the tokens, are gathered from the L2 and Infinity caches.
+#include "dkv_fused_common.h"
+#include "dkv_q40.h"
+
+namespace dkv {
+
+__host__ __device__ inline int64_t pad256(int64_t x) { return (x + 255) & ~int64_t(255); }
+
+struct StridedLayout {
+    int nref;
+    int64_t off_codes, off_scales, off_idx, stream_bytes;
+};
+
+__host__ __device__ inline StridedLayout strided_layout(const dkv_config &c)
+{
+    StridedLayout l;
+    const int64_t cap = c.max_tokens, D = c.head_dim;
+    l.nref = (int)((cap + c.kf - 1) / c.kf);
+    l.off_codes = pad256((int64_t)l.nref * D * 2);
+    l.off_scales = l.off_codes + pad256(cap * D / 2);
+    l.off_idx = l.off_scales + pad256(cap * (D / 32) * 2);
+    l.stream_bytes = l.off_idx + pad256(cap * 2);
+    return l;
+}
+
+constexpr int kStridedThreads = 256;
+constexpr int kStridedMaxG = 16;
+
+// Squared distance of two fp16 rows in double, channel order, no contraction.
+template <int D>
+__device__ inline double sqdist_rows(const uint16_t *__restrict__ a, const uint16_t *__restrict__ b)
+{
+#pragma clang fp contract(off)
+    double s = 0.0;
+#pragma unroll 2
+    for (int c8 = 0; c8 < D / 8; ++c8) {
+        const u4 av = ((const u4 *)a)[c8], bv = ((const u4 *)b)[c8];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const double d0 = (double)h2f((uint16_t)(av[w] & 0xFFFF)) - (double)h2f((uint16_t)(bv[w] & 0xFFFF));
+            const double q0 = d0 * d0;
+            s = s + q0;
+            const double d1 = (double)h2f((uint16_t)(av[w] >> 16)) - (double)h2f((uint16_t)(bv[w] >> 16));
+            const double q1 = d1 * d1;
+            s = s + q1;
+        }
+    }
+    return s;
+}
+
+// grid (ceil(s_max / 32), n_kv_heads * 2, batch): one 32-token tile of one stream.
+template <int D>
+__global__ void __launch_bounds__(kStridedThreads)
+    k_strided_encode(dkv_config cfg, uint8_t *__restrict__ cache, const uint16_t *__restrict__ k,
+                     const uint16_t *__restrict__ v, const int32_t *__restrict__ lens, int s_max, int window)
+{
+    constexpr int NB = D / 32;
+    const StridedLayout ly = strided_layout(cfg);
+    const int stride = cfg.kf;
+    const int tile = blockIdx.x, h = blockIdx.y >> 1, s = blockIdx.y & 1, b = blockIdx.z;
+    const int tid = threadIdx.x;
+    const int L = max(0, min(lens[b], min(s_max, cfg.max_tokens)));
+    const int t0 = tile * 32;
+    if (t0 >= L) return;
+    const uint16_t *x = (s ? v : k) + ((int64_t)b * cfg.n_kv_heads + h) * s_max * D;
+    uint8_t *base = cache + (((int64_t)b * cfg.n_kv_heads + h) * 2 + s) * ly.stream_bytes;
+    uint16_t *refs = (uint16_t *)base;
+    uint8_t *codes = base + ly.off_codes;
+    uint16_t *scales = (uint16_t *)(base + ly.off_scales);
+    uint16_t *idx = (uint16_t *)(base + ly.off_idx);
+
+    // the tile's reference rows, copied exactly
+    for (int e = tid; e < 32 * D; e += kStridedThreads) {
+        const int t = t0 + e / D, c = e % D;
+        if (t < L && t % stride == 0) refs[(int64_t)(t / stride) * D + c] = x[(int64_t)t * D + c];
+    }
+
+    // nearest reference: 8 lanes per token, each scanning every 8th candidate
+    __shared__ int sidx[32];
+    {
+        const int tt = tid >> 3, sl = tid & 7, t = t0 + tt;
+        double bd = INFINITY;
+        int bk = 0x7FFFFFFF;
+        if (t < L) {
+            const int kt = t / stride;
+            const int k0 = (window > 0 && kt - window + 1 > 0) ? kt - window + 1 : 0;
+            for (int kk = k0 + sl; kk <= kt; kk += 8) {
+                const double d = sqdist_rows<D>(x + (int64_t)t * D, x + (int64_t)kk * stride * D);
+                if (d < bd) {
+                    bd = d;
+                    bk = kk;
+                }
+            }
+        }
+#pragma unroll
+        for (int off = 1; off < 8; off <<= 1) {
+            const double d2 = __shfl_xor(bd, off, 8);
+            const int k2 = __shfl_xor(bk, off, 8);
+            if (d2 < bd || (d2 == bd && k2 < bk)) {
+                bd = d2;
+                bk = k2;
+            }
+        }
+        if (sl == 0) {
+            sidx[tt] = t < L ? bk : 0;
+            if (t < L) idx[t] = (uint16_t)bk;
+        }
+    }
+    __syncthreads();
+
+    // Q4_0 residuals: one 32-lane half-wave per (token, block)
+    const int hw = tid >> 5, ln = tid & 31;
+    for (int p = hw; p < 32 * NB; p += kStridedThreads / 32) {
+        const int tt = p / NB, blk = p % NB, t = t0 + tt;
+        if (t >= L) continue;                       // uniform over the half-wave
+        const int c = 32 * blk + ln;
+        const float xv = h2f(x[(int64_t)t * D + c]);
+        float xh = h2f(x[(int64_t)sidx[tt] * stride * D + c]);
+        int code;
+        uint16_t s16;
+        q40_delta_step(xv, xh, code, s16);
+        const int hi = __shfl_down(code, 16, 32);
+        if (ln < 16) codes[(int64_t)t * (D / 2) + 16 * blk + ln] = (uint8_t)(code | (hi << 4));
+        if (ln == 0) scales[(int64_t)t * NB + blk] = s16;
+    }
+}
+
+// Rebuild CPT channels [c0, c0 + CPT) of token t of one stream in fp32.
+template <int D>
+__device__ inline void strided_row(const uint8_t *__restrict__ base, const StridedLayout &ly, int t, int c0,
+                                   float (&out)[D / 8])
+{
+    constexpr int NB = D / 32, CPT = D / 8;
+    // clamped: a token never encoded reads a wrong row, not past the plane
+    const int k = min((int)((const uint16_t *)(base + ly.off_idx))[t], ly.nref - 1);
+    const int blk = c0 >> 5, e0 = c0 & 31, sh = 4 * (e0 >> 4);
+    const float sf = h2f(((const uint16_t *)(base + ly.off_scales))[(int64_t)t * NB + blk]);
+    const uint8_t *cb = base + ly.off_codes + (int64_t)t * (D / 2) + 16 * blk + (e0 & 15);
+    const uint16_t *r = (const uint16_t *)base + (int64_t)k * D + c0;
+    uint32_t cw[CPT / 4];
+    if constexpr (CPT == 16) {
+        const u4 w = *(const u4 *)cb;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cw[i] = w[i];
+    } else {
+        const u2 w = *(const u2 *)cb;
+        cw[0] = w[0];
+        cw[1] = w[1];
+    }
+    uint32_t rw[CPT / 2];
+#pragma unroll
+    for (int i = 0; i < CPT / 8; ++i) {
+        const u4 w = ((const u4 *)r)[i];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) rw[4 * i + j] = w[j];
+    }
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+        const int code = (int)((cw[i >> 2] >> (8 * (i & 3) + sh)) & 15u);
+        const uint16_t rh = (uint16_t)((i & 1) ? (rw[i >> 1] >> 16) : (rw[i >> 1] & 0xFFFF));
+        out[i] = __builtin_fmaf((float)(code - 8), sf, h2f(rh));     // exact product, one rounding
+    }
+}
+
+// grid (nsplit, n_kv_heads, batch): the split's run of 32-token tiles.
+template <int D>
+__global__ void __launch_bounds__(kStridedThreads)
+    k_strided_attn(dkv_config cfg, const uint8_t *__restrict__ cache, const float *__restrict__ q,
+                   const int32_t *__restrict__ lens, float scale_log2, float *__restrict__ ws, int nsplit, int chunk)
+{
+    constexpr int CPT = D / 8;
+    constexpr int ACC = (kStridedMaxG * D + kStridedThreads - 1) / kStridedThreads;
+    const StridedLayout ly = strided_layout(cfg);
+    const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+    const int Hq = cfg.n_q_heads, G = Hq / cfg.n_kv_heads;
+    const int L = max(0, min(lens[b], cfg.max_tokens));
+    const int ntile = (L + 31) / 32;
+    const int tb0 = split * chunk, tb1 = min(ntile, tb0 + chunk);
+    const int64_t row0 = (int64_t)b * Hq + (int64_t)h * G;
+
+    __shared__ float sq[kStridedMaxG][D];
+    __shared__ float vt[32][D];
+    __shared__ float lg[kStridedMaxG][32];
+    __shared__ float al[kStridedMaxG];
+    for (int e = tid; e < G * D; e += kStridedThreads) sq[e / D][e % D] = q[row0 * D + e] * scale_log2;
+    __syncthreads();
+
+    const uint8_t *kb = cache + (((int64_t)b * cfg.n_kv_heads + h) * 2) * ly.stream_bytes;
+    const uint8_t *vb = kb + ly.stream_bytes;
+    float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.0f, 0.0f};
+    float acc[ACC];
+#pragma unroll
+    for (int a = 0; a < ACC; ++a) acc[a] = 0.0f;
+
+    const int tt = tid >> 3, sl = tid & 7, c0 = sl * CPT;
+    for (int tile = tb0; tile < tb1; ++tile) {
+        const int t0 = tile * 32, nt = min(32, L - t0);
+        const bool valid = tt < nt;
+        float kh[CPT], vh[CPT];
+        if (valid) {
+            strided_row<D>(kb, ly, t0 + tt, c0, kh);
+            strided_row<D>(vb, ly, t0 + tt, c0, vh);
+        } else {
+#pragma unroll
+            for (int i = 0; i < CPT; ++i) kh[i] = vh[i] = 0.0f;
+        }
+        for (int g = 0; g < G; ++g) {
+            float part = 0.0f;
+#pragma unroll
+            for (int i = 0; i < CPT; ++i) part = __builtin_fmaf(sq[g][c0 + i], kh[i], part);
+            part += __shfl_xor(part, 1, 8);
+            part += __shfl_xor(part, 2, 8);
+            part += __shfl_xor(part, 4, 8);
+            if (sl == 0) lg[g][tt] = valid ? part : -INFINITY;
+        }
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) vt[tt][c0 + i] = vh[i];
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int g = (tid >> 5) + 8 * i;
+            if (g < G) {                             // uniform over the half-wave
+                const float x = lg[g][tid & 31];
+                float mx = x;
+#pragma unroll
+                for (int off = 16; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 32));
+                const float m_new = fmaxf(m_run[i], mx);
+                const float p = x == -INFINITY ? 0.0f : exp2f(x - m_new);
+                const float alpha = exp2f(m_run[i] - m_new);
+                float sum = p;
+#pragma unroll
+                for (int off = 16; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 32);
+                l_run[i] = l_run[i] * alpha + sum;
+                m_run[i] = m_new;
+                lg[g][tid & 31] = p;
+                if ((tid & 31) == 0) al[g] = alpha;
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int a = 0; a < ACC; ++a) {
+            const int e = tid + a * kStridedThreads;
+            if (e < G * D) {
+                const int g = e / D, c = e % D;
+                float s = acc[a] * al[g];
+#pragma unroll 8
+                for (int u = 0; u < 32; ++u) s = __builtin_fmaf(lg[g][u], vt[u][c], s);
+                acc[a] = s;
+            }
+        }
+        __syncthreads();
+    }
+    constexpr int R = part_stride(D);
+#pragma unroll
+    for (int a = 0; a < ACC; ++a) {
+        const int e = tid + a * kStridedThreads;
+        if (e < G * D) ws[((row0 + e / D) * nsplit + split) * R + e % D] = acc[a];
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int g = (tid >> 5) + 8 * i;
+        if (g < G && (tid & 31) == 0) {
+            float *rec = ws + ((row0 + g) * nsplit + split) * R;
+            rec[D] = m_run[i];
+            rec[D + 1] = l_run[i];
+        }
+    }
+}
+
+int64_t strided_cache_bytes(const dkv_config &c)
+{
+    return strided_layout(c).stream_bytes * 2 * c.batch * c.n_kv_heads;
+}
+
+void strided_plane_offsets(const dkv_config &c, int64_t *off)
+{
+    const StridedLayout l = strided_layout(c);
+    off[0] = 0;
+    off[1] = l.off_codes;
+    off[2] = l.off_scales;
+    off[3] = l.off_idx;
+    off[4] = l.stream_bytes;
+    off[5] = l.nref;
+}
+
+hipError_t launch_strided_encode(const dkv_config &c, void *cache, const uint16_t *k, const uint16_t *v,
+                                 const int32_t *lens, int s_max, int window, hipStream_t st)
+{
+    dim3 grid((s_max + 31) / 32, c.n_kv_heads * 2, c.batch);
+    if (c.head_dim == 64)
+        hipLaunchKernelGGL(k_strided_encode<64>, grid, dim3(kStridedThreads), 0, st, c, (uint8_t *)cache, k, v,
+                           lens, s_max, window);
+    else
+        hipLaunchKernelGGL(k_strided_encode<128>, grid, dim3(kStridedThreads), 0, st, c, (uint8_t *)cache, k, v,
+                           lens, s_max, window);
+    return hipGetLastError();
+}
+
+hipError_t launch_strided_attn(const dkv_config &c, const void *cache, const float *q, const int32_t *lens,
+                               float scale_log2, float *ws, int nsplit, int chunk, hipStream_t st)
+{
+    dim3 grid(nsplit, c.n_kv_heads, c.batch);
+    if (c.head_dim == 64)
+        hipLaunchKernelGGL(k_strided_attn<64>, grid, dim3(kStridedThreads), 0, st, c, (const uint8_t *)cache, q,
+                           lens, scale_log2, ws, nsplit, chunk);
+    else
+        hipLaunchKernelGGL(k_strided_attn<128>, grid, dim3(kStridedThreads), 0, st, c, (const uint8_t *)cache, q,
+                           lens, scale_log2, ws, nsplit, chunk);
+    return hipGetLastError();
+}
+
+}  // namespace dkv

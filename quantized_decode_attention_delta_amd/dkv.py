@@ -82,6 +82,10 @@ _SIGS = {
     "dkv_attn_distortion": ([_CFG, _P, _P, _P, _P, _I32, _P, _P, _F, _P, _P, _P, _P], _I32),
     "dkv_stream_read_sink_words": ([], _SZ),
     "dkv_stream_read": ([_P, _SZ, _P, _SZ, _P], _I32),
+    "dkv_strided_cache_bytes": ([_CFG], _SZ),
+    "dkv_strided_layout": ([_CFG, _P], _I32),
+    "dkv_strided_encode_prefill": ([_CFG, _P, _P, _P, _P, _I32, _I32, _P], _I32),
+    "dkv_strided_attn_decode": ([_CFG, _P, _P, _P, _F, _P, _P, _SZ, _P], _I32),
 }
 
 
@@ -350,3 +354,42 @@ def dkv_stream_read(buf, sink, nbytes=None, stream=None):
     st = load().dkv_stream_read(_ptr(buf, None, "buf"), n, _ptr(sink, (torch.int32,), "sink"), sink.numel(),
                                 _stream(stream))
     _check("dkv_stream_read", st)
+
+
+# ------------------------------------------------------------------ strided references
+def dkv_strided_cache_bytes(cfg: Config) -> int:
+    return load().dkv_strided_cache_bytes(ctypes.byref(cfg.c()))
+
+
+def dkv_strided_layout(cfg: Config) -> dict:
+    """Plane offsets inside one stream, the stream's bytes and the reference rows per stream."""
+    import numpy as np
+    out = np.zeros(6, np.int64)
+    st = load().dkv_strided_layout(ctypes.byref(cfg.c()), out.ctypes.data_as(ctypes.c_void_p))
+    _check("dkv_strided_layout", st)
+    return dict(refs=int(out[0]), codes=int(out[1]), scales=int(out[2]), idx=int(out[3]),
+                stream_bytes=int(out[4]), nref=int(out[5]))
+
+
+def dkv_strided_encode_prefill(cfg: Config, cache, k, v, seq_lens, s_max: int, window: int = 0, stream=None):
+    """Strided-reference residual encode of tokens [0, seq_lens[b]) (k, v fp16 [B][Hkv][s_max][D])."""
+    import torch
+    B, H, D = cfg.batch, cfg.n_kv_heads, cfg.head_dim
+    n = B * H * s_max * D
+    st = load().dkv_strided_encode_prefill(
+        ctypes.byref(cfg.c()), _ptr(cache, torch.uint8, "cache", dkv_strided_cache_bytes(cfg)),
+        _f16(k, "k", n), _f16(v, "v", n), _ptr(seq_lens, torch.int32, "seq_lens", B), int(s_max), int(window),
+        _stream(stream))
+    _check("dkv_strided_encode_prefill", st)
+
+
+def dkv_strided_attn_decode(cfg: Config, cache, q, seq_lens, out, workspace, softmax_scale=0.0, stream=None):
+    """Decode attention over the strided-reference cache."""
+    import torch
+    B, Hq, D = cfg.batch, cfg.n_q_heads, cfg.head_dim
+    st = load().dkv_strided_attn_decode(
+        ctypes.byref(cfg.c()), _ptr(cache, torch.uint8, "cache", dkv_strided_cache_bytes(cfg)),
+        _ptr(q, torch.float32, "q", B * Hq * D), _ptr(seq_lens, torch.int32, "seq_lens", B), float(softmax_scale),
+        _ptr(out, torch.float32, "out", B * Hq * D), _ptr(workspace, torch.uint8, "workspace"),
+        workspace.numel() if workspace is not None else 0, _stream(stream))
+    _check("dkv_strided_attn_decode", st)

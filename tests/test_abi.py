@@ -73,6 +73,14 @@ def test_sizes():
     assert dkv.dkv_workspace_bytes(c) > 0
     assert dkv.dkv_q4_0_cache_bytes(c) == 16 * 8 * 2 * 32768 * 128 // 32 * 18
     assert dkv.dkv_cache_bytes(_cfg(head_dim=96)) == 0
+    # strided references: per stream 1024 fp16 reference rows, 32768 tokens of
+    # 64 code bytes, 8 scale bytes and a 2-byte index, planes 256-byte aligned
+    lay = dkv.dkv_strided_layout(c)
+    assert lay == dict(refs=0, codes=1024 * 256, scales=1024 * 256 + 32768 * 64,
+                       idx=1024 * 256 + 32768 * 72, stream_bytes=1024 * 256 + 32768 * 74, nref=1024)
+    assert dkv.dkv_strided_cache_bytes(c) == 16 * 8 * 2 * lay["stream_bytes"]
+    assert dkv.dkv_strided_cache_bytes(_cfg(page_tokens=256, n_pages=8, max_pages_per_seq=4)) == 0
+    assert dkv.dkv_strided_cache_bytes(_cfg(kf=1, max_tokens=70000)) == 0      # 70000 references > 65536
 
 
 def test_argument_errors_return_before_launch():
@@ -109,6 +117,13 @@ def test_argument_errors_return_before_launch():
     assert lib.dkv_attn_distortion(cp, *d, 10, fake, fake, 0.0, fake, fake, null, null) == binding.DKV_ERR_ARG
     assert lib.dkv_attn_distortion(cp, *d, 0, fake, fake, 0.0, fake, fake, fake, null) == binding.DKV_ERR_ARG
     assert lib.dkv_attn_distortion(cbad, *d, 10, fake, fake, 0.0, fake, fake, fake, null) == binding.DKV_ERR_UNSUPPORTED
+    # strided references: contiguous only, null pointers, negative window, short workspace
+    assert lib.dkv_strided_encode_prefill(cpg, fake, fake, fake, fake, 10, 0, null) == binding.DKV_ERR_UNSUPPORTED
+    assert lib.dkv_strided_encode_prefill(cp, fake, null, fake, fake, 10, 0, null) == binding.DKV_ERR_ARG
+    assert lib.dkv_strided_encode_prefill(cp, fake, fake, fake, fake, 10, -1, null) == binding.DKV_ERR_ARG
+    assert lib.dkv_strided_attn_decode(cp, fake, null, fake, 0.0, fake, fake, 1 << 30, null) == binding.DKV_ERR_ARG
+    assert lib.dkv_strided_attn_decode(cp, fake, fake, fake, 0.0, fake, fake, 16, null) == binding.DKV_ERR_WORKSPACE
+    assert lib.dkv_strided_layout(cp, null) == binding.DKV_ERR_ARG
     assert lib.dkv_check_config(None) == binding.DKV_ERR_ARG
     assert dkv.status_str(binding.DKV_ERR_WORKSPACE) == "workspace missing or too small"
 
