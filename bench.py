@@ -265,6 +265,76 @@ def comparisons(w, cfg, k, v, q, lens, ws, steps, stream, qo):
     return res, q4
 
 
+def strided_bytes(w, stride, lens_np):
+    """Algorithmic bytes of one strided-reference decode launch: per stream and
+    token the Q4_0 residual (D/2 code bytes, D/16 scale bytes) and a 2-byte
+    reference index, plus every reference row (2*D bytes) once."""
+    D = w.D
+    per_tok = D // 2 + 2 * (D // 32) + 2
+    total = 0
+    for L in lens_np:
+        L = int(L)
+        total += L * per_tok + -(-L // stride) * 2 * D
+    return 2 * w.Hkv * total
+
+
+def strided(w, k, v, q, lens, steps, stream, qo, window=64):
+    """Strided-reference residual cache (references every kf tokens, nearest
+    within the last `window` references) on the same K/V and queries: encode
+    time, decode time against its algorithmic bytes, and the quality of its
+    reconstruction, dequantised here from its own planes on the GPU."""
+    import numpy as np
+    import torch
+
+    import quantized_decode_attention_delta_amd as dkv
+    dev = k.device
+    B, H, S, D, stride = w.B, w.Hkv, w.S, w.D, w.kf
+    cfg = dkv.Config(batch=B, n_q_heads=w.Hq, n_kv_heads=H, head_dim=D, kf=stride, max_tokens=S)
+    nbytes = dkv.dkv_strided_cache_bytes(cfg)
+    cache = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    dkv.dkv_strided_encode_prefill(cfg, cache, k, v, lens, S, window)
+    torch.cuda.synchronize()
+    enc_ms = (time.perf_counter() - t0) * 1e3
+    reps = max(1, math.ceil((1 << 30) / nbytes))
+    caches = [cache] + [cache.clone() for _ in range(reps - 1)]
+    out = torch.empty(B, w.Hq, D, dtype=torch.float32, device=dev)
+    ws = torch.zeros(dkv.dkv_workspace_bytes(cfg), dtype=torch.uint8, device=dev)
+    ms = _time(lambda i: dkv.dkv_strided_attn_decode(cfg, caches[i % reps], q, lens, out, ws), steps, stream)
+    del caches
+    alg = strided_bytes(w, stride, lens.cpu().numpy())
+    res = {"ms_per_step": round(ms, 5), "GBps": round((alg + qo) / (ms * 1e-3) / 1e9, 2),
+           "hbm_frac": round((alg + qo) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), "bytes": alg,
+           "stride": stride, "window": window, "encode_ms": round(enc_ms, 1), "replicas": reps,
+           "how": "dkv_strided_attn_decode (split phase + combine)"}
+
+    lay = dkv.dkv_strided_layout(cfg)
+    c = cache.view(B, H, 2, lay["stream_bytes"])
+    nref = lay["nref"]
+    refs = c[..., :nref * D * 2].contiguous().view(torch.float16).view(B, H, 2, nref, D).float()
+    codes = c[..., lay["codes"]:lay["codes"] + S * D // 2].reshape(B, H, 2, S, D // 32, 16)
+    full = torch.cat([codes & 15, codes >> 4], dim=-1).float() - 8.0
+    sc = c[..., lay["scales"]:lay["scales"] + S * D // 16].contiguous().view(torch.float16)
+    sc = sc.view(B, H, 2, S, D // 32, 1).float()
+    idx = c[..., lay["idx"]:lay["idx"] + 2 * S].contiguous().view(torch.int16).view(B, H, 2, S).long() & 0xFFFF
+    rr = torch.gather(refs, 3, idx.clamp(max=nref - 1)[..., None].expand(-1, -1, -1, -1, D))
+    recon = rr + (full * sc).reshape(B, H, 2, S, D)
+    del refs, codes, full, sc, idx, rr
+    valid = (torch.arange(S, device=dev)[None, :] < lens[:, None].long())[:, None, :, None]
+    nval = float(valid.sum()) * H * D
+    mse = [float((((recon[:, :, s] - x.float()) ** 2) * valid).sum()) / nval for s, x in enumerate((k, v))]
+    kh = recon[:, :, 0].contiguous()
+    vh = recon[:, :, 1].contiguous()
+    del recon
+    logits = torch.empty(B * w.Hq * S, dtype=torch.float32, device=dev)
+    dk = torch.empty(B, w.Hq, dtype=torch.float32, device=dev)
+    dv = torch.empty_like(dk)
+    dkv.dkv_attn_distortion(cfg, kh, vh, k, v, S, q, lens, dk, dv, logits)
+    qual = {"mse": sum(mse) / 2, "mse_kv": mse, "d_k": float(dk.double().mean()), "d_v": float(dv.double().mean())}
+    return res, qual
+
+
 def quality(w, cfg, cache, q4, k, v, lens, q):
     """Reconstruction MSE against the fp16 input, over every valid token, from
     the GPU's own outputs: Delta-KV via dkv_reconstruct, Q4_0 via its export,
@@ -627,6 +697,9 @@ def main():
                                           "hbm_frac": res["hbm_frac_step"], "bytes": comp}
         res["quality"] = quality(w, cfg, cache0, q4, k, v, lens, q)
         del q4
+        if w.S <= 65536 * w.kf:
+            res["comparisons"]["strided"], res["quality"]["strided"] = strided(w, k, v, q, lens, args.steps, stream,
+                                                                              qo)
     if not args.no_cpu_baseline:
         threads = args.cpu_threads or min(16, os.cpu_count() or 1)
         res["cpu_baseline"] = cpu_baseline(w, kf, args.cpu_seconds, threads)

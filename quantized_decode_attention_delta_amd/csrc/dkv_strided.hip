@@ -158,41 +158,89 @@ __global__ void __launch_bounds__(kStridedThreads)
     }
 }
 
-// Rebuild CPT channels [c0, c0 + CPT) of token t of one stream in fp32.
+// Raw data of channels [c0, c0 + D/8) of one token of one stream: its code
+// bytes, block scale and reference row slice (the row found through the
+// token's index, clamped so that a token never encoded reads a wrong row, not
+// past the plane).
 template <int D>
-__device__ inline void strided_row(const uint8_t *__restrict__ base, const StridedLayout &ly, int t, int c0,
-                                   float (&out)[D / 8])
+struct RowRaw {
+    uint32_t cw[D / 32];     // D/8 code bytes
+    uint32_t rw[D / 16];     // D/8 fp16 reference values
+    uint32_t sc;             // fp16 scale bits
+};
+
+template <int D>
+__device__ inline void strided_fetch(const uint8_t *__restrict__ base, const StridedLayout &ly, int t, int c0,
+                                     RowRaw<D> &w)
 {
     constexpr int NB = D / 32, CPT = D / 8;
-    // clamped: a token never encoded reads a wrong row, not past the plane
     const int k = min((int)((const uint16_t *)(base + ly.off_idx))[t], ly.nref - 1);
-    const int blk = c0 >> 5, e0 = c0 & 31, sh = 4 * (e0 >> 4);
-    const float sf = h2f(((const uint16_t *)(base + ly.off_scales))[(int64_t)t * NB + blk]);
+    const int blk = c0 >> 5, e0 = c0 & 31;
+    w.sc = ((const uint16_t *)(base + ly.off_scales))[(int64_t)t * NB + blk];
     const uint8_t *cb = base + ly.off_codes + (int64_t)t * (D / 2) + 16 * blk + (e0 & 15);
-    const uint16_t *r = (const uint16_t *)base + (int64_t)k * D + c0;
-    uint32_t cw[CPT / 4];
     if constexpr (CPT == 16) {
-        const u4 w = *(const u4 *)cb;
+        const u4 x = *(const u4 *)cb;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) cw[i] = w[i];
+        for (int i = 0; i < 4; ++i) w.cw[i] = x[i];
     } else {
-        const u2 w = *(const u2 *)cb;
-        cw[0] = w[0];
-        cw[1] = w[1];
+        const u2 x = *(const u2 *)cb;
+        w.cw[0] = x[0];
+        w.cw[1] = x[1];
     }
-    uint32_t rw[CPT / 2];
+    const uint16_t *r = (const uint16_t *)base + (int64_t)k * D + c0;
 #pragma unroll
     for (int i = 0; i < CPT / 8; ++i) {
-        const u4 w = ((const u4 *)r)[i];
+        const u4 x = ((const u4 *)r)[i];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) rw[4 * i + j] = w[j];
+        for (int j = 0; j < 4; ++j) w.rw[4 * i + j] = x[j];
     }
+}
+
+// Rebuild the channels in fp32: reference + (code - 8) * scale.
+template <int D>
+__device__ inline void strided_rebuild(const RowRaw<D> &w, int c0, float (&out)[D / 8])
+{
+    constexpr int CPT = D / 8;
+    const int sh = 4 * ((c0 & 31) >> 4);
+    const float sf = h2f((uint16_t)w.sc);
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-        const int code = (int)((cw[i >> 2] >> (8 * (i & 3) + sh)) & 15u);
-        const uint16_t rh = (uint16_t)((i & 1) ? (rw[i >> 1] >> 16) : (rw[i >> 1] & 0xFFFF));
+        const int code = (int)((w.cw[i >> 2] >> (8 * (i & 3) + sh)) & 15u);
+        const uint16_t rh = (uint16_t)((i & 1) ? (w.rw[i >> 1] >> 16) : (w.rw[i >> 1] & 0xFFFF));
         out[i] = __builtin_fmaf((float)(code - 8), sf, h2f(rh));     // exact product, one rounding
     }
+}
+
+// Lane reductions in registers (DPP moves within a row of 16 lanes, the
+// row-pair swap across rows): every lane of the group gets the result.
+template <int CTRL>
+__device__ inline float dpp_f(float x)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+__device__ inline float sum8_lanes(float x)          // groups of 8 aligned lanes
+{
+    x += dpp_f<0xB1>(x);     // quad_perm [1,0,3,2]
+    x += dpp_f<0x4E>(x);     // quad_perm [2,3,0,1]
+    return x + dpp_f<0x141>(x);   // row_half_mirror: the other quad of the 8
+}
+__device__ inline float sum32_lanes(float x)         // groups of 32 aligned lanes
+{
+    x = sum8_lanes(x);
+    x += dpp_f<0x140>(x);    // row_mirror: the other 8 of the row
+    float a0, a1;
+    swap16(x, a0, a1);
+    return a0 + a1;
+}
+__device__ inline float max32_lanes(float x)
+{
+    x = fmaxf(x, dpp_f<0xB1>(x));
+    x = fmaxf(x, dpp_f<0x4E>(x));
+    x = fmaxf(x, dpp_f<0x141>(x));
+    x = fmaxf(x, dpp_f<0x140>(x));
+    float a0, a1;
+    swap16(x, a0, a1);
+    return fmaxf(a0, a1);
 }
 
 // grid (nsplit, n_kv_heads, batch): the split's run of 32-token tiles.
@@ -213,7 +261,7 @@ __global__ void __launch_bounds__(kStridedThreads)
 
     __shared__ float sq[kStridedMaxG][D];
     __shared__ float vt[32][D];
-    __shared__ float lg[kStridedMaxG][32];
+    __shared__ __attribute__((aligned(16))) float lg[kStridedMaxG][32];
     __shared__ float al[kStridedMaxG];
     for (int e = tid; e < G * D; e += kStridedThreads) sq[e / D][e % D] = q[row0 * D + e] * scale_log2;
     __syncthreads();
@@ -226,24 +274,32 @@ __global__ void __launch_bounds__(kStridedThreads)
     for (int a = 0; a < ACC; ++a) acc[a] = 0.0f;
 
     const int tt = tid >> 3, sl = tid & 7, c0 = sl * CPT;
+    // the next tile's rows are fetched while the current one is processed
+    RowRaw<D> nk, nv;
+    if (tb0 < tb1 && tb0 * 32 + tt < L) {
+        strided_fetch<D>(kb, ly, tb0 * 32 + tt, c0, nk);
+        strided_fetch<D>(vb, ly, tb0 * 32 + tt, c0, nv);
+    }
     for (int tile = tb0; tile < tb1; ++tile) {
         const int t0 = tile * 32, nt = min(32, L - t0);
         const bool valid = tt < nt;
         float kh[CPT], vh[CPT];
         if (valid) {
-            strided_row<D>(kb, ly, t0 + tt, c0, kh);
-            strided_row<D>(vb, ly, t0 + tt, c0, vh);
+            strided_rebuild<D>(nk, c0, kh);
+            strided_rebuild<D>(nv, c0, vh);
         } else {
 #pragma unroll
             for (int i = 0; i < CPT; ++i) kh[i] = vh[i] = 0.0f;
+        }
+        if (tile + 1 < tb1 && t0 + 32 + tt < L) {
+            strided_fetch<D>(kb, ly, t0 + 32 + tt, c0, nk);
+            strided_fetch<D>(vb, ly, t0 + 32 + tt, c0, nv);
         }
         for (int g = 0; g < G; ++g) {
             float part = 0.0f;
 #pragma unroll
             for (int i = 0; i < CPT; ++i) part = __builtin_fmaf(sq[g][c0 + i], kh[i], part);
-            part += __shfl_xor(part, 1, 8);
-            part += __shfl_xor(part, 2, 8);
-            part += __shfl_xor(part, 4, 8);
+            part = sum8_lanes(part);
             if (sl == 0) lg[g][tt] = valid ? part : -INFINITY;
         }
 #pragma unroll
@@ -254,15 +310,11 @@ __global__ void __launch_bounds__(kStridedThreads)
             const int g = (tid >> 5) + 8 * i;
             if (g < G) {                             // uniform over the half-wave
                 const float x = lg[g][tid & 31];
-                float mx = x;
-#pragma unroll
-                for (int off = 16; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 32));
+                const float mx = max32_lanes(x);
                 const float m_new = fmaxf(m_run[i], mx);
                 const float p = x == -INFINITY ? 0.0f : exp2f(x - m_new);
                 const float alpha = exp2f(m_run[i] - m_new);
-                float sum = p;
-#pragma unroll
-                for (int off = 16; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 32);
+                const float sum = sum32_lanes(p);
                 l_run[i] = l_run[i] * alpha + sum;
                 m_run[i] = m_new;
                 lg[g][tid & 31] = p;
@@ -270,15 +322,26 @@ __global__ void __launch_bounds__(kStridedThreads)
             }
         }
         __syncthreads();
+        // every thread keeps one channel c; its heads are e / D for e = tid + a * 256
+        {
+            const int c = tid % D;
 #pragma unroll
-        for (int a = 0; a < ACC; ++a) {
-            const int e = tid + a * kStridedThreads;
-            if (e < G * D) {
-                const int g = e / D, c = e % D;
-                float s = acc[a] * al[g];
-#pragma unroll 8
-                for (int u = 0; u < 32; ++u) s = __builtin_fmaf(lg[g][u], vt[u][c], s);
-                acc[a] = s;
+            for (int u4i = 0; u4i < 8; ++u4i) {
+                float vv[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) vv[j] = vt[4 * u4i + j][c];
+#pragma unroll
+                for (int a = 0; a < ACC; ++a) {
+                    const int e = tid + a * kStridedThreads;
+                    if (e < G * D) {
+                        const int g = e / D;
+                        const f4 pw = *(const f4 *)&lg[g][4 * u4i];      // four weights, one read
+                        float s = u4i == 0 ? acc[a] * al[g] : acc[a];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) s = __builtin_fmaf(pw[j], vv[j], s);
+                        acc[a] = s;
+                    }
+                }
             }
         }
         __syncthreads();
