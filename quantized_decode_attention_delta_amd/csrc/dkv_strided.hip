@@ -169,12 +169,18 @@ struct RowRaw {
     uint32_t sc;             // fp16 scale bits
 };
 
+// The token's reference index, clamped to the plane.
+__device__ inline int strided_ref(const uint8_t *__restrict__ base, const StridedLayout &ly, int t)
+{
+    return min((int)((const uint16_t *)(base + ly.off_idx))[t], ly.nref - 1);
+}
+
+// Codes, scale and reference slice of token t with reference index k.
 template <int D>
-__device__ inline void strided_fetch(const uint8_t *__restrict__ base, const StridedLayout &ly, int t, int c0,
+__device__ inline void strided_fetch(const uint8_t *__restrict__ base, const StridedLayout &ly, int t, int k, int c0,
                                      RowRaw<D> &w)
 {
     constexpr int NB = D / 32, CPT = D / 8;
-    const int k = min((int)((const uint16_t *)(base + ly.off_idx))[t], ly.nref - 1);
     const int blk = c0 >> 5, e0 = c0 & 31;
     w.sc = ((const uint16_t *)(base + ly.off_scales))[(int64_t)t * NB + blk];
     const uint8_t *cb = base + ly.off_codes + (int64_t)t * (D / 2) + 16 * blk + (e0 & 15);
@@ -244,13 +250,22 @@ __device__ inline float max32_lanes(float x)
 }
 
 // grid (nsplit, n_kv_heads, batch): the split's run of 32-token tiles.
+// Per tile the 256 threads rebuild K and V (8 lanes per token, 16 B loads)
+// into LDS; the logits (32 tokens x 16 head columns over D channels) and the
+// weighted V rows (16 head rows x D channels over 32 tokens) are fp32
+// matrix-core products (v_mfma_f32_16x16x4_f32: lane 16*j + n supplies row n
+// of A and column n of B at k = j; it holds rows 4j..4j+3 of column n of the
+// result), the query held in registers.  Head columns beyond the group are
+// zero.  The next tile's rows are fetched while the current one is processed.
 template <int D>
 __global__ void __launch_bounds__(kStridedThreads)
     k_strided_attn(dkv_config cfg, const uint8_t *__restrict__ cache, const float *__restrict__ q,
                    const int32_t *__restrict__ lens, float scale_log2, float *__restrict__ ws, int nsplit, int chunk)
 {
     constexpr int CPT = D / 8;
-    constexpr int ACC = (kStridedMaxG * D + kStridedThreads - 1) / kStridedThreads;
+    constexpr int KS = D + 4, VS = D + 16;       // LDS row strides: conflict-free operand reads
+    constexpr int NKK = D / 8;                   // k-steps of 4 channels over half the channels
+    constexpr int NCB = D / 64;                  // 16-channel column blocks per wave
     const StridedLayout ly = strided_layout(cfg);
     const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
     const int Hq = cfg.n_q_heads, G = Hq / cfg.n_kv_heads;
@@ -258,58 +273,79 @@ __global__ void __launch_bounds__(kStridedThreads)
     const int ntile = (L + 31) / 32;
     const int tb0 = split * chunk, tb1 = min(ntile, tb0 + chunk);
     const int64_t row0 = (int64_t)b * Hq + (int64_t)h * G;
+    const int wv = tid >> 6, lane = tid & 63, jj = lane >> 4, nn = lane & 15;
+    const int th = wv & 1, ch = wv >> 1;         // logits: token half, channel half of this wave
 
-    __shared__ float sq[kStridedMaxG][D];
-    __shared__ float vt[32][D];
-    __shared__ __attribute__((aligned(16))) float lg[kStridedMaxG][32];
+    __shared__ __attribute__((aligned(16))) float kt[32 * KS];
+    __shared__ __attribute__((aligned(16))) float vt[32 * VS];
+    __shared__ float lgp[2][kStridedMaxG][32];
+    __shared__ float lg[kStridedMaxG][32];
     __shared__ float al[kStridedMaxG];
-    for (int e = tid; e < G * D; e += kStridedThreads) sq[e / D][e % D] = q[row0 * D + e] * scale_log2;
+    for (int e = tid; e < kStridedMaxG * 32; e += kStridedThreads) (&lg[0][0])[e] = 0.0f;
+    if (tid < kStridedMaxG) al[tid] = 1.0f;
+
+    // query operand: head nn, channels ch*D/2 + 4*kk + jj (zero beyond the group)
+    float qb[NKK];
+    {
+        const float *qr = q + (row0 + min(nn, G - 1)) * D + ch * (D / 2) + jj;
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+            const float x = qr[4 * kk] * scale_log2;
+            qb[kk] = nn < G ? x : 0.0f;
+        }
+    }
     __syncthreads();
 
     const uint8_t *kb = cache + (((int64_t)b * cfg.n_kv_heads + h) * 2) * ly.stream_bytes;
     const uint8_t *vb = kb + ly.stream_bytes;
     float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.0f, 0.0f};
-    float acc[ACC];
+    f4 acc[NCB];
 #pragma unroll
-    for (int a = 0; a < ACC; ++a) acc[a] = 0.0f;
+    for (int u = 0; u < NCB; ++u) acc[u] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 
     const int tt = tid >> 3, sl = tid & 7, c0 = sl * CPT;
-    // the next tile's rows are fetched while the current one is processed
     RowRaw<D> nk, nv;
     if (tb0 < tb1 && tb0 * 32 + tt < L) {
-        strided_fetch<D>(kb, ly, tb0 * 32 + tt, c0, nk);
-        strided_fetch<D>(vb, ly, tb0 * 32 + tt, c0, nv);
+        strided_fetch<D>(kb, ly, tb0 * 32 + tt, strided_ref(kb, ly, tb0 * 32 + tt), c0, nk);
+        strided_fetch<D>(vb, ly, tb0 * 32 + tt, strided_ref(vb, ly, tb0 * 32 + tt), c0, nv);
     }
     for (int tile = tb0; tile < tb1; ++tile) {
         const int t0 = tile * 32, nt = min(32, L - t0);
-        const bool valid = tt < nt;
-        float kh[CPT], vh[CPT];
-        if (valid) {
-            strided_rebuild<D>(nk, c0, kh);
-            strided_rebuild<D>(nv, c0, vh);
-        } else {
+        {
+            float kh[CPT], vh[CPT];
+            if (tt < nt) {
+                strided_rebuild<D>(nk, c0, kh);
+                strided_rebuild<D>(nv, c0, vh);
+            } else {
 #pragma unroll
-            for (int i = 0; i < CPT; ++i) kh[i] = vh[i] = 0.0f;
-        }
-        if (tile + 1 < tb1 && t0 + 32 + tt < L) {
-            strided_fetch<D>(kb, ly, t0 + 32 + tt, c0, nk);
-            strided_fetch<D>(vb, ly, t0 + 32 + tt, c0, nv);
-        }
-        for (int g = 0; g < G; ++g) {
-            float part = 0.0f;
+                for (int i = 0; i < CPT; ++i) kh[i] = vh[i] = 0.0f;
+            }
+            if (tile + 1 < tb1 && t0 + 32 + tt < L) {
+                strided_fetch<D>(kb, ly, t0 + 32 + tt, strided_ref(kb, ly, t0 + 32 + tt), c0, nk);
+                strided_fetch<D>(vb, ly, t0 + 32 + tt, strided_ref(vb, ly, t0 + 32 + tt), c0, nv);
+            }
 #pragma unroll
-            for (int i = 0; i < CPT; ++i) part = __builtin_fmaf(sq[g][c0 + i], kh[i], part);
-            part = sum8_lanes(part);
-            if (sl == 0) lg[g][tt] = valid ? part : -INFINITY;
+            for (int i = 0; i < CPT; i += 4) {
+                *(f4 *)&kt[tt * KS + c0 + i] = f4{kh[i], kh[i + 1], kh[i + 2], kh[i + 3]};
+                *(f4 *)&vt[tt * VS + c0 + i] = f4{vh[i], vh[i + 1], vh[i + 2], vh[i + 3]};
+            }
         }
+        __syncthreads();
+        // logits of tokens 16*th + row over channels [ch*D/2, (ch+1)*D/2)
+        {
+            f4 C = f4{0.0f, 0.0f, 0.0f, 0.0f};
+            const float *ka = kt + (16 * th + nn) * KS + ch * (D / 2) + jj;
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) vt[tt][c0 + i] = vh[i];
+            for (int kk = 0; kk < NKK; ++kk) C = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[4 * kk], qb[kk], C, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) lgp[ch][nn][16 * th + 4 * jj + i] = C[i];
+        }
         __syncthreads();
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            const int g = (tid >> 5) + 8 * i;
+            const int g = (tid >> 5) + 8 * i, t = tid & 31;
             if (g < G) {                             // uniform over the half-wave
-                const float x = lg[g][tid & 31];
+                const float x = t < nt ? lgp[0][g][t] + lgp[1][g][t] : -INFINITY;
                 const float mx = max32_lanes(x);
                 const float m_new = fmaxf(m_run[i], mx);
                 const float p = x == -INFINITY ? 0.0f : exp2f(x - m_new);
@@ -317,30 +353,28 @@ __global__ void __launch_bounds__(kStridedThreads)
                 const float sum = sum32_lanes(p);
                 l_run[i] = l_run[i] * alpha + sum;
                 m_run[i] = m_new;
-                lg[g][tid & 31] = p;
-                if ((tid & 31) == 0) al[g] = alpha;
+                lg[g][t] = p;
+                if (t == 0) al[g] = alpha;
             }
         }
         __syncthreads();
-        // every thread keeps one channel c; its heads are e / D for e = tid + a * 256
+        // weighted V rows: heads 4*jj + i, channels 16*cb + nn
         {
-            const int c = tid % D;
+            float alr[4];
 #pragma unroll
-            for (int u4i = 0; u4i < 8; ++u4i) {
-                float vv[4];
+            for (int i = 0; i < 4; ++i) alr[i] = al[4 * jj + i];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) vv[j] = vt[4 * u4i + j][c];
+            for (int u = 0; u < NCB; ++u)
 #pragma unroll
-                for (int a = 0; a < ACC; ++a) {
-                    const int e = tid + a * kStridedThreads;
-                    if (e < G * D) {
-                        const int g = e / D;
-                        const f4 pw = *(const f4 *)&lg[g][4 * u4i];      // four weights, one read
-                        float s = u4i == 0 ? acc[a] * al[g] : acc[a];
+                for (int i = 0; i < 4; ++i) acc[u][i] *= alr[i];
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) s = __builtin_fmaf(pw[j], vv[j], s);
-                        acc[a] = s;
-                    }
+            for (int kk = 0; kk < 8; ++kk) {
+                const float pa = lg[nn][4 * kk + jj];
+#pragma unroll
+                for (int u = 0; u < NCB; ++u) {
+                    const int cb = wv * NCB + u;
+                    acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa, vt[(4 * kk + jj) * VS + 16 * cb + nn], acc[u],
+                                                                  0, 0, 0);
                 }
             }
         }
@@ -348,9 +382,13 @@ __global__ void __launch_bounds__(kStridedThreads)
     }
     constexpr int R = part_stride(D);
 #pragma unroll
-    for (int a = 0; a < ACC; ++a) {
-        const int e = tid + a * kStridedThreads;
-        if (e < G * D) ws[((row0 + e / D) * nsplit + split) * R + e % D] = acc[a];
+    for (int u = 0; u < NCB; ++u) {
+        const int cb = wv * NCB + u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int g = 4 * jj + i;
+            if (g < G) ws[((row0 + g) * nsplit + split) * R + 16 * cb + nn] = acc[u][i];
+        }
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
