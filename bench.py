@@ -278,6 +278,68 @@ def strided_bytes(w, stride, lens_np):
     return 2 * w.Hkv * total
 
 
+def strided_recon(cfg, cache, S):
+    """Dequantise a strided-reference cache from its planes on the GPU:
+    float [B][Hkv][2][S][D] = reference row + (code - 8) * scale."""
+    import torch
+
+    import quantized_decode_attention_delta_amd as dkv
+    B, H, D = cfg.batch, cfg.n_kv_heads, cfg.head_dim
+    lay = dkv.dkv_strided_layout(cfg)
+    c = cache.view(B, H, 2, lay["stream_bytes"])
+    nref = lay["nref"]
+    refs = c[..., :nref * D * 2].contiguous().view(torch.float16).view(B, H, 2, nref, D).float()
+    codes = c[..., lay["codes"]:lay["codes"] + S * D // 2].reshape(B, H, 2, S, D // 32, 16)
+    full = torch.cat([codes & 15, codes >> 4], dim=-1).float() - 8.0
+    sc = c[..., lay["scales"]:lay["scales"] + S * D // 16].contiguous().view(torch.float16)
+    sc = sc.view(B, H, 2, S, D // 32, 1).float()
+    idx = c[..., lay["idx"]:lay["idx"] + 2 * S].contiguous().view(torch.int16).view(B, H, 2, S).long() & 0xFFFF
+    rr = torch.gather(refs, 3, idx.clamp(max=nref - 1)[..., None].expand(-1, -1, -1, -1, D))
+    return rr + (full * sc).reshape(B, H, 2, S, D)
+
+
+def strided_mixed_quality(dev, B=8, S=8192):
+    """Reconstruction MSE of Delta-KV and of strided references (stride 32 with
+    a window of 64 references, stride 8 with 256) on the mixed workload's two
+    halves: periodic rows (period 8..64) and regime-switching rows.  Delta-KV
+    via dkv_reconstruct; strided dequantised from its planes."""
+    import torch
+
+    import quantized_decode_attention_delta_amd as dkv
+    from quantized_decode_attention_delta_amd import synth
+    w = synth.make("mixed", B=B, S=S, extra_tokens=0)
+    H, D = w.Hkv, w.D
+    k = torch.from_numpy(w.k).to(dev)
+    v = torch.from_numpy(w.v).to(dev)
+    lens = torch.from_numpy(w.seq_lens).to(dev)
+    x = torch.stack([k, v], dim=2).float()                       # [B][H][2][S][D]
+    valid = (torch.arange(S, device=dev)[None, :] < lens[:, None].long())[:, None, None, :, None]
+    halves = {"periodic": slice(0, B // 2), "regime": slice(B // 2, B)}
+
+    def mse(rec):
+        err = ((rec - x) ** 2) * valid
+        return {n: float(err[sl].sum()) / (float(valid[sl].sum()) * H * 2 * D) for n, sl in halves.items()}
+
+    out = {"how": f"mixed workload, {B} sequences (first half periodic, second regime-switching), "
+                  f"lengths up to {S}, contiguous caches"}
+    cfg = dkv.Config(batch=B, n_q_heads=w.Hq, n_kv_heads=H, head_dim=D, kf=32, max_tokens=S)
+    cache = torch.empty(dkv.dkv_cache_bytes(cfg), dtype=torch.uint8, device=dev)
+    state = torch.zeros(B, H, 2, D, dtype=torch.float32, device=dev)
+    dkv.dkv_encode_prefill(cfg, cache, state, None, k, v, lens, S)
+    kr = torch.zeros(B, H, S, D, dtype=torch.float32, device=dev)
+    vr = torch.zeros_like(kr)
+    dkv.dkv_reconstruct(cfg, cache, None, lens, S, kr, vr)
+    out["delta_kv_kf32"] = mse(torch.stack([kr, vr], dim=2))
+    del cache, kr, vr
+    for stride, window in ((32, 64), (8, 256)):
+        cs = dkv.Config(batch=B, n_q_heads=w.Hq, n_kv_heads=H, head_dim=D, kf=stride, max_tokens=S)
+        sc = torch.zeros(dkv.dkv_strided_cache_bytes(cs), dtype=torch.uint8, device=dev)
+        dkv.dkv_strided_encode_prefill(cs, sc, k, v, lens, S, window)
+        out[f"strided_{stride}_w{window}"] = mse(strided_recon(cs, sc, S))
+        del sc
+    return out
+
+
 def strided(w, k, v, q, lens, steps, stream, qo, window=64):
     """Strided-reference residual cache (references every kf tokens, nearest
     within the last `window` references) on the same K/V and queries: encode
@@ -309,18 +371,7 @@ def strided(w, k, v, q, lens, steps, stream, qo, window=64):
            "stride": stride, "window": window, "encode_ms": round(enc_ms, 1), "replicas": reps,
            "how": "dkv_strided_attn_decode (split phase + combine)"}
 
-    lay = dkv.dkv_strided_layout(cfg)
-    c = cache.view(B, H, 2, lay["stream_bytes"])
-    nref = lay["nref"]
-    refs = c[..., :nref * D * 2].contiguous().view(torch.float16).view(B, H, 2, nref, D).float()
-    codes = c[..., lay["codes"]:lay["codes"] + S * D // 2].reshape(B, H, 2, S, D // 32, 16)
-    full = torch.cat([codes & 15, codes >> 4], dim=-1).float() - 8.0
-    sc = c[..., lay["scales"]:lay["scales"] + S * D // 16].contiguous().view(torch.float16)
-    sc = sc.view(B, H, 2, S, D // 32, 1).float()
-    idx = c[..., lay["idx"]:lay["idx"] + 2 * S].contiguous().view(torch.int16).view(B, H, 2, S).long() & 0xFFFF
-    rr = torch.gather(refs, 3, idx.clamp(max=nref - 1)[..., None].expand(-1, -1, -1, -1, D))
-    recon = rr + (full * sc).reshape(B, H, 2, S, D)
-    del refs, codes, full, sc, idx, rr
+    recon = strided_recon(cfg, cache, S)
     valid = (torch.arange(S, device=dev)[None, :] < lens[:, None].long())[:, None, :, None]
     nval = float(valid.sum()) * H * D
     mse = [float((((recon[:, :, s] - x.float()) ** 2) * valid).sum()) / nval for s, x in enumerate((k, v))]
@@ -700,6 +751,7 @@ def main():
         if w.S <= 65536 * w.kf:
             res["comparisons"]["strided"], res["quality"]["strided"] = strided(w, k, v, q, lens, args.steps, stream,
                                                                               qo)
+        res["quality"]["strided_vs_delta_kv_mixed"] = strided_mixed_quality(dev)
     if not args.no_cpu_baseline:
         threads = args.cpu_threads or min(16, os.cpu_count() or 1)
         res["cpu_baseline"] = cpu_baseline(w, kf, args.cpu_seconds, threads)
