@@ -337,6 +337,22 @@ dkv_status dkv_strided_encode_prefill(const dkv_config *cfg, void *cache, const 
                                       int32_t window, dkv_stream_t stream);
 
 /*
+ * Append one token per sequence to the strided-reference cache, coded exactly
+ * as dkv_strided_encode_prefill codes it (the candidates are read from the
+ * cache's reference rows; with the same window the bytes equal those of a
+ * prefill over the grown sequence).
+ *  k_new, v_new (device) fp16 [batch][n_kv_heads][head_dim]
+ *  positions    (device) int32 [batch]: the token's index t; a sequence with
+ *               t < 0 or t >= capacity is skipped.  Tokens 0..t-1 must
+ *               already be encoded (prefill or earlier appends).
+ * One workgroup per (kv-head, K/V, sequence).  Errors: as
+ * dkv_strided_encode_prefill.  Asynchronous on `stream`.
+ */
+dkv_status dkv_strided_append(const dkv_config *cfg, void *cache, const uint16_t *k_new,
+                              const uint16_t *v_new, const int32_t *positions, int32_t window,
+                              dkv_stream_t stream);
+
+/*
  * Decode attention over the strided-reference cache: out[b][hq] =
  * softmax(scale * q . K_hat^T) V_hat over tokens t < min(seq_lens[b], capacity),
  * arguments as dkv_attn_decode (workspace of dkv_workspace_bytes(cfg) bytes).

@@ -34,6 +34,8 @@ hipError_t launch_strided_encode(const dkv_config &, void *, const uint16_t *, c
                                  int, hipStream_t);
 hipError_t launch_strided_attn(const dkv_config &, const void *, const float *, const int32_t *, float, float *, int,
                                int, hipStream_t);
+hipError_t launch_strided_append(const dkv_config &, void *, const uint16_t *, const uint16_t *, const int32_t *, int,
+                                 hipStream_t);
 hipError_t launch_attn_fused(const dkv_config &, const void *, const int32_t *, const float *,
                              const int32_t *, float, float *, int, int, hipStream_t);
 bool fused_supported(const dkv_config &);
@@ -429,6 +431,15 @@ dkv_status dkv_strided_encode_prefill(const dkv_config *c, void *cache, const ui
     if (!cache || !k || !v || !lens || s_max < 0 || window < 0) return DKV_ERR_ARG;
     if (s_max == 0) return DKV_OK;
     return hip_status(launch_strided_encode(*c, cache, k, v, lens, s_max, window, (hipStream_t)stream));
+}
+
+dkv_status dkv_strided_append(const dkv_config *c, void *cache, const uint16_t *k_new, const uint16_t *v_new,
+                              const int32_t *positions, int32_t window, dkv_stream_t stream)
+{
+    dkv_status st = strided_check(c);
+    if (st != DKV_OK) return st;
+    if (!cache || !k_new || !v_new || !positions || window < 0) return DKV_ERR_ARG;
+    return hip_status(launch_strided_append(*c, cache, k_new, v_new, positions, window, (hipStream_t)stream));
 }
 
 dkv_status dkv_strided_attn_decode(const dkv_config *c, const void *cache, const float *q, const int32_t *lens,

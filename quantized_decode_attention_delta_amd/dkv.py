@@ -86,6 +86,7 @@ _SIGS = {
     "dkv_strided_layout": ([_CFG, _P], _I32),
     "dkv_strided_encode_prefill": ([_CFG, _P, _P, _P, _P, _I32, _I32, _P], _I32),
     "dkv_strided_attn_decode": ([_CFG, _P, _P, _P, _F, _P, _P, _SZ, _P], _I32),
+    "dkv_strided_append": ([_CFG, _P, _P, _P, _P, _I32, _P], _I32),
 }
 
 
@@ -393,3 +394,14 @@ def dkv_strided_attn_decode(cfg: Config, cache, q, seq_lens, out, workspace, sof
         _ptr(out, torch.float32, "out", B * Hq * D), _ptr(workspace, torch.uint8, "workspace"),
         workspace.numel() if workspace is not None else 0, _stream(stream))
     _check("dkv_strided_attn_decode", st)
+
+
+def dkv_strided_append(cfg: Config, cache, k_new, v_new, positions, window: int = 0, stream=None):
+    """Append one token per sequence (k_new, v_new fp16 [B][Hkv][D]) at positions[b] (< 0: none)."""
+    import torch
+    B, H, D = cfg.batch, cfg.n_kv_heads, cfg.head_dim
+    st = load().dkv_strided_append(
+        ctypes.byref(cfg.c()), _ptr(cache, torch.uint8, "cache", dkv_strided_cache_bytes(cfg)),
+        _f16(k_new, "k_new", B * H * D), _f16(v_new, "v_new", B * H * D),
+        _ptr(positions, torch.int32, "positions", B), int(window), _stream(stream))
+    _check("dkv_strided_append", st)

@@ -134,3 +134,54 @@ def test_strided_periodic_sequence_reconstructs_exactly():
             ref = oracle.attention_f64(q_np[b, h * G:(h + 1) * G], rk.recon, rv.recon, scale)
             g = out[b, h * G:(h + 1) * G].cpu().numpy()
             assert U.rel_err(g[None], ref[None]) <= U.ATTN_TOL
+
+
+@pytest.mark.parametrize("kw,stride,window", [
+    (dict(S=300, B=3, Hq=8, Hkv=2, extra_tokens=40), 32, 0),
+    (dict(S=300, B=3, Hq=8, Hkv=2, D=64, extra_tokens=40), 8, 16),
+])
+def test_strided_append_matches_prefill(kw, stride, window):
+    """Prefill of a prefix, then one token per step (one sequence skipping some
+    steps with a negative position): the cache bytes of every encoded token
+    and reference equal those of a prefill over the grown sequences, and so do
+    the attention outputs."""
+    w = synth.make("8b", **kw)
+    print(f"strided append {kw} stride={stride} window={window}", flush=True)
+    cfg = _cfg(w, stride)
+    lay = dkv.dkv_strided_layout(cfg)
+    s_max = w.k.shape[2]
+    k = torch.from_numpy(np.ascontiguousarray(w.k)).to(U.DEV)
+    v = torch.from_numpy(np.ascontiguousarray(w.v)).to(U.DEV)
+    lens = np.array([100, 0, 257], np.int32)
+    a = torch.full((dkv.dkv_strided_cache_bytes(cfg),), 0xA5, dtype=torch.uint8, device=U.DEV)
+    dkv.dkv_strided_encode_prefill(cfg, a, k, v, torch.from_numpy(lens).to(U.DEV), s_max, window)
+    for step in range(40):
+        pos = lens.copy()
+        if step % 3 == 1:
+            pos[1] = -1
+        kn = torch.stack([k[b, :, max(int(pos[b]), 0)] for b in range(w.B)]).contiguous()
+        vn = torch.stack([v[b, :, max(int(pos[b]), 0)] for b in range(w.B)]).contiguous()
+        dkv.dkv_strided_append(cfg, a, kn, vn, torch.from_numpy(pos).to(U.DEV), window)
+        lens = lens + (pos >= 0)
+    bcache = torch.full_like(a, 0x5A)
+    lens_d = torch.from_numpy(lens.astype(np.int32)).to(U.DEV)
+    dkv.dkv_strided_encode_prefill(cfg, bcache, k, v, lens_d, s_max, window)
+    torch.cuda.synchronize()
+    ha, hb = a.cpu().numpy(), bcache.cpu().numpy()
+    D, sb = w.D, lay["stream_bytes"]
+    for b in range(w.B):
+        L = int(lens[b])
+        for h in range(w.Hkv):
+            for s in range(2):
+                o = ((b * w.Hkv + h) * 2 + s) * sb
+                for lo, n in ((0, -(-L // stride) * D * 2), (lay["codes"], L * D // 2),
+                              (lay["scales"], L * D // 16), (lay["idx"], 2 * L)):
+                    assert np.array_equal(ha[o + lo:o + lo + n], hb[o + lo:o + lo + n]), (b, h, s, lo)
+    q = torch.from_numpy(synth.queries(w)).to(U.DEV)
+    oa = torch.zeros(w.B, w.Hq, D, dtype=torch.float32, device=U.DEV)
+    ob = torch.zeros_like(oa)
+    ws = torch.zeros(dkv.dkv_workspace_bytes(cfg), dtype=torch.uint8, device=U.DEV)
+    dkv.dkv_strided_attn_decode(cfg, a, q, lens_d, oa, ws)
+    dkv.dkv_strided_attn_decode(cfg, bcache, q, lens_d, ob, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(oa, ob)
