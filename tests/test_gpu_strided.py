@@ -35,6 +35,9 @@ CASES = [
     ("70b", dict(S=600, B=2, Hq=16, Hkv=2), 32, 0, None, None),
     ("70b", dict(S=300, B=2, Hq=32, Hkv=2), 16, 0, None, None),
     ("70b", dict(S=2048, B=32, Hq=32, Hkv=8), 32, 0, "ragged", [(1, 0), (7, 5), (20, 3), (31, 7)]),
+    ("8b", dict(S=200, Hq=8, Hkv=2), 1, 0, None, None),            # every token its own reference
+    ("8b", dict(S=600, Hq=8, Hkv=2), 32, 1, None, None),           # only the latest reference
+    ("70b", dict(S=300, B=2, Hq=32, Hkv=2, D=64), 32, 0, None, None),
 ]
 
 
