@@ -88,6 +88,12 @@ Plan tile_plan(const dkv_config &c)
     const int tiles = (c.max_tokens + 31) / 32;
     return make_plan(tiles, c.batch, c.n_kv_heads, 64);
 }
+// strided-reference decode: one wave per run, so runs of at most 16 tiles
+Plan strided_plan(const dkv_config &c)
+{
+    const int tiles = (c.max_tokens + 31) / 32;
+    return make_plan(tiles, c.batch, c.n_kv_heads, 16);
+}
 static size_t ws_for(const dkv_config &c, const Plan &p)
 {
     return (size_t)c.batch * c.n_q_heads * p.nsplit * part_stride(c.head_dim) * sizeof(float);
@@ -96,7 +102,8 @@ static size_t workspace_total(const dkv_config &c)
 {
     const size_t a = ws_for(c, delta_plan(c));
     const size_t b = c.page_tokens == 0 ? ws_for(c, tile_plan(c)) : 0;
-    return a > b ? a : b;
+    const size_t d = c.page_tokens == 0 ? ws_for(c, strided_plan(c)) : 0;
+    return a > b ? (a > d ? a : d) : (b > d ? b : d);
 }
 
 static dkv_status hip_status(hipError_t e) { return e == hipSuccess ? DKV_OK : DKV_ERR_HIP; }
@@ -449,7 +456,7 @@ dkv_status dkv_strided_attn_decode(const dkv_config *c, const void *cache, const
     if (st != DKV_OK) return st;
     if (!cache || !q || !lens || !out) return DKV_ERR_ARG;
     if (!ws || ws_bytes < workspace_total(*c)) return DKV_ERR_WORKSPACE;
-    const Plan p = tile_plan(*c);
+    const Plan p = strided_plan(*c);
     hipError_t e = launch_strided_attn(*c, cache, q, lens, resolve_scale(*c, scale), (float *)ws, p.nsplit, p.chunk,
                                        (hipStream_t)stream);
     if (e != hipSuccess) return DKV_ERR_HIP;

@@ -324,155 +324,187 @@ __device__ inline float max32_lanes(float x)
     return fmaxf(a0, a1);
 }
 
-// grid (nsplit, n_kv_heads, batch): the split's run of 32-token tiles.
-// Per tile the 256 threads rebuild K and V (8 lanes per token, 16 B loads)
-// into LDS; the logits (32 tokens x 16 head columns over D channels) and the
-// weighted V rows (16 head rows x D channels over 32 tokens) are fp32
-// matrix-core products (v_mfma_f32_16x16x4_f32: lane 16*j + n supplies row n
-// of A and column n of B at k = j; it holds rows 4j..4j+3 of column n of the
-// result), the query held in registers.  Head columns beyond the group are
-// zero.  The next tile's rows are fetched while the current one is processed.
+// Raw data of D/4 channels [c0, c0 + D/4) of one token of one stream (one
+// block at D = 128, half a block at D = 64): the block's 16 code bytes, its
+// scale and the reference row slice.
 template <int D>
-__global__ void __launch_bounds__(kStridedThreads)
+struct RowQ {
+    uint32_t cw[4];
+    uint32_t rw[D / 8];
+    uint32_t sc;
+};
+
+template <int D>
+__device__ inline void strided_fetch_q(const uint8_t *__restrict__ base, const StridedLayout &ly, int t, int c0,
+                                       RowQ<D> &w)
+{
+    constexpr int NB = D / 32;
+    const int k = strided_ref(base, ly, t);
+    const int blk = c0 >> 5;
+    w.sc = ((const uint16_t *)(base + ly.off_scales))[(int64_t)t * NB + blk];
+    const u4 x = *(const u4 *)(base + ly.off_codes + (int64_t)t * (D / 2) + 16 * blk);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w.cw[i] = x[i];
+    const u4 *r = (const u4 *)((const uint16_t *)base + (int64_t)k * D + c0);
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) {
+        const u4 y = r[i];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w.rw[4 * i + j] = y[j];
+    }
+}
+
+// reference + (code - 8) * scale of the D/4 channels, written to an LDS row
+template <int D>
+__device__ inline void strided_rebuild_q(const RowQ<D> &w, int c0, float *__restrict__ dst)
+{
+    constexpr int CH = D / 4;
+    const float sf = h2f((uint16_t)w.sc);
+#pragma unroll
+    for (int i = 0; i < CH; i += 4) {
+        f4 o;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int ci = i + u;                                   // channel c0 + ci
+            const int e = (c0 & 31) + ci;                           // its place in the block
+            const int code = (int)((w.cw[(e & 15) >> 2] >> (8 * (e & 3) + 4 * (e >> 4))) & 15u);
+            const uint16_t rh = (uint16_t)((ci & 1) ? (w.rw[ci >> 1] >> 16) : (w.rw[ci >> 1] & 0xFFFF));
+            o[u] = __builtin_fmaf((float)(code - 8), sf, h2f(rh));   // exact product, one rounding
+        }
+        *(f4 *)&dst[i] = o;
+    }
+}
+
+// grid (nsplit, n_kv_heads, batch), one wave per workgroup: the split's run of
+// 32-token tiles, taken as 16-token sub-tiles with no barrier between waves.
+// Per sub-tile: lane (token lane/4, a quarter of the channels) rebuilds K and
+// V into the wave's LDS; the logits (16 tokens x 16 head columns over D
+// channels) and the weighted V rows (16 head rows x D channels over the 16
+// tokens) are fp32 matrix-core products (v_mfma_f32_16x16x4_f32: lane 16*j + n
+// supplies row n of A and column n of B at k = j, and holds rows 4j..4j+3 of
+// column n of the result); the softmax runs down each head column.  Head
+// columns beyond the group are zero.  The next sub-tile's rows are fetched
+// while the current one is processed.
+template <int D>
+__global__ void __launch_bounds__(64)
     k_strided_attn(dkv_config cfg, const uint8_t *__restrict__ cache, const float *__restrict__ q,
                    const int32_t *__restrict__ lens, float scale_log2, float *__restrict__ ws, int nsplit, int chunk)
 {
-    constexpr int CPT = D / 8;
     constexpr int KS = D + 4, VS = D + 16;       // LDS row strides: conflict-free operand reads
-    constexpr int NKK = D / 8;                   // k-steps of 4 channels over half the channels
-    constexpr int NCB = D / 64;                  // 16-channel column blocks per wave
+    constexpr int NKK = D / 4;                   // k-steps of the logits
+    constexpr int NCB = D / 16;                  // 16-channel column blocks of the weighted V rows
     const StridedLayout ly = strided_layout(cfg);
-    const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+    const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
+    const int jj = lane >> 4, nn = lane & 15;
     const int Hq = cfg.n_q_heads, G = Hq / cfg.n_kv_heads;
     const int L = max(0, min(lens[b], cfg.max_tokens));
-    const int ntile = (L + 31) / 32;
-    const int tb0 = split * chunk, tb1 = min(ntile, tb0 + chunk);
+    const int t_begin = split * chunk * 32, t_end = min(L, t_begin + chunk * 32);
     const int64_t row0 = (int64_t)b * Hq + (int64_t)h * G;
-    const int wv = tid >> 6, lane = tid & 63, jj = lane >> 4, nn = lane & 15;
-    const int th = wv & 1, ch = wv >> 1;         // logits: token half, channel half of this wave
 
-    __shared__ __attribute__((aligned(16))) float kt[32 * KS];
-    __shared__ __attribute__((aligned(16))) float vt[32 * VS];
-    __shared__ float lgp[2][kStridedMaxG][32];
-    __shared__ float lg[kStridedMaxG][32];
+    __shared__ __attribute__((aligned(16))) float kt[16 * KS];
+    __shared__ __attribute__((aligned(16))) float vt[16 * VS];
+    __shared__ float pl[kStridedMaxG][17];
     __shared__ float al[kStridedMaxG];
-    for (int e = tid; e < kStridedMaxG * 32; e += kStridedThreads) (&lg[0][0])[e] = 0.0f;
-    if (tid < kStridedMaxG) al[tid] = 1.0f;
 
-    // query operand: head nn, channels ch*D/2 + 4*kk + jj (zero beyond the group)
+    // query operand: head nn, channels 4*kk + jj (zero beyond the group)
     float qb[NKK];
     {
-        const float *qr = q + (row0 + min(nn, G - 1)) * D + ch * (D / 2) + jj;
+        const float *qr = q + (row0 + min(nn, G - 1)) * D + jj;
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
             const float x = qr[4 * kk] * scale_log2;
             qb[kk] = nn < G ? x : 0.0f;
         }
     }
-    __syncthreads();
-
     const uint8_t *kb = cache + (((int64_t)b * cfg.n_kv_heads + h) * 2) * ly.stream_bytes;
     const uint8_t *vb = kb + ly.stream_bytes;
-    float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.0f, 0.0f};
+    float m_run = -INFINITY, l_run = 0.0f;       // of head nn
     f4 acc[NCB];
 #pragma unroll
     for (int u = 0; u < NCB; ++u) acc[u] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    const int tt = tid >> 3, sl = tid & 7, c0 = sl * CPT;
-    RowRaw<D> nk, nv;
-    if (tb0 < tb1 && tb0 * 32 + tt < L) {
-        strided_fetch<D>(kb, ly, tb0 * 32 + tt, strided_ref(kb, ly, tb0 * 32 + tt), c0, nk);
-        strided_fetch<D>(vb, ly, tb0 * 32 + tt, strided_ref(vb, ly, tb0 * 32 + tt), c0, nv);
+    const int r = lane >> 2, c0 = (lane & 3) * (D / 4);
+    RowQ<D> nk, nv;
+    if (t_begin + r < t_end) {
+        strided_fetch_q<D>(kb, ly, t_begin + r, c0, nk);
+        strided_fetch_q<D>(vb, ly, t_begin + r, c0, nv);
     }
-    for (int tile = tb0; tile < tb1; ++tile) {
-        const int t0 = tile * 32, nt = min(32, L - t0);
-        {
-            float kh[CPT], vh[CPT];
-            if (tt < nt) {
-                strided_rebuild<D>(nk, c0, kh);
-                strided_rebuild<D>(nv, c0, vh);
-            } else {
+    for (int t0 = t_begin; t0 < t_end; t0 += 16) {
+        const int nt = min(16, t_end - t0);
+        if (r < nt) {
+            strided_rebuild_q<D>(nk, c0, kt + r * KS + c0);
+            strided_rebuild_q<D>(nv, c0, vt + r * VS + c0);
+        } else {
 #pragma unroll
-                for (int i = 0; i < CPT; ++i) kh[i] = vh[i] = 0.0f;
+            for (int i = 0; i < D / 4; i += 4) {
+                *(f4 *)&kt[r * KS + c0 + i] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+                *(f4 *)&vt[r * VS + c0 + i] = f4{0.0f, 0.0f, 0.0f, 0.0f};
             }
-            if (tile + 1 < tb1 && t0 + 32 + tt < L) {
-                strided_fetch<D>(kb, ly, t0 + 32 + tt, strided_ref(kb, ly, t0 + 32 + tt), c0, nk);
-                strided_fetch<D>(vb, ly, t0 + 32 + tt, strided_ref(vb, ly, t0 + 32 + tt), c0, nv);
-            }
-#pragma unroll
-            for (int i = 0; i < CPT; i += 4) {
-                *(f4 *)&kt[tt * KS + c0 + i] = f4{kh[i], kh[i + 1], kh[i + 2], kh[i + 3]};
-                *(f4 *)&vt[tt * VS + c0 + i] = f4{vh[i], vh[i + 1], vh[i + 2], vh[i + 3]};
-            }
+        }
+        if (t0 + 16 + r < t_end) {
+            strided_fetch_q<D>(kb, ly, t0 + 16 + r, c0, nk);
+            strided_fetch_q<D>(vb, ly, t0 + 16 + r, c0, nv);
         }
         __syncthreads();
-        // logits of tokens 16*th + row over channels [ch*D/2, (ch+1)*D/2)
+        // logits of tokens 4*jj + i for head nn, in two chains
+        f4 C0 = f4{0.0f, 0.0f, 0.0f, 0.0f}, C1 = C0;
         {
-            f4 C = f4{0.0f, 0.0f, 0.0f, 0.0f};
-            const float *ka = kt + (16 * th + nn) * KS + ch * (D / 2) + jj;
+            const float *ka = kt + nn * KS + jj;
 #pragma unroll
-            for (int kk = 0; kk < NKK; ++kk) C = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[4 * kk], qb[kk], C, 0, 0, 0);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) lgp[ch][nn][16 * th + 4 * jj + i] = C[i];
-        }
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int g = (tid >> 5) + 8 * i, t = tid & 31;
-            if (g < G) {                             // uniform over the half-wave
-                const float x = t < nt ? lgp[0][g][t] + lgp[1][g][t] : -INFINITY;
-                const float mx = max32_lanes(x);
-                const float m_new = fmaxf(m_run[i], mx);
-                const float p = x == -INFINITY ? 0.0f : exp2f(x - m_new);
-                const float alpha = exp2f(m_run[i] - m_new);
-                const float sum = sum32_lanes(p);
-                l_run[i] = l_run[i] * alpha + sum;
-                m_run[i] = m_new;
-                lg[g][t] = p;
-                if (t == 0) al[g] = alpha;
+            for (int kk = 0; kk < NKK; kk += 2) {
+                C0 = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[4 * kk], qb[kk], C0, 0, 0, 0);
+                C1 = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[4 * kk + 4], qb[kk + 1], C1, 0, 0, 0);
             }
         }
+        float x[4], mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[i] = 4 * jj + i < nt ? C0[i] + C1[i] : -INFINITY;
+            mx = fmaxf(mx, x[i]);
+        }
+        mx = rows_max(mx);
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = exp2f(m_run - m_new);
+        float ps = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float p = x[i] == -INFINITY ? 0.0f : exp2f(x[i] - m_new);
+            pl[nn][4 * jj + i] = p;
+            ps += p;
+        }
+        l_run = l_run * alpha + rows_sum(ps);
+        m_run = m_new;
+        if (jj == 0) al[nn] = alpha;
         __syncthreads();
         // weighted V rows: heads 4*jj + i, channels 16*cb + nn
-        {
-            float alr[4];
+        float alr[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) alr[i] = al[4 * jj + i];
+        for (int i = 0; i < 4; ++i) alr[i] = al[4 * jj + i];
 #pragma unroll
-            for (int u = 0; u < NCB; ++u)
+        for (int u = 0; u < NCB; ++u)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[u][i] *= alr[i];
+            for (int i = 0; i < 4; ++i) acc[u][i] *= alr[i];
 #pragma unroll
-            for (int kk = 0; kk < 8; ++kk) {
-                const float pa = lg[nn][4 * kk + jj];
+        for (int kk = 0; kk < 4; ++kk) {
+            const float pa = pl[nn][4 * kk + jj];
+            const float *vr = vt + (4 * kk + jj) * VS + nn;
 #pragma unroll
-                for (int u = 0; u < NCB; ++u) {
-                    const int cb = wv * NCB + u;
-                    acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa, vt[(4 * kk + jj) * VS + 16 * cb + nn], acc[u],
-                                                                  0, 0, 0);
-                }
-            }
+            for (int u = 0; u < NCB; ++u) acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa, vr[16 * u], acc[u], 0, 0, 0);
         }
         __syncthreads();
     }
     constexpr int R = part_stride(D);
 #pragma unroll
-    for (int u = 0; u < NCB; ++u) {
-        const int cb = wv * NCB + u;
+    for (int u = 0; u < NCB; ++u)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int g = 4 * jj + i;
-            if (g < G) ws[((row0 + g) * nsplit + split) * R + 16 * cb + nn] = acc[u][i];
+            if (g < G) ws[((row0 + g) * nsplit + split) * R + 16 * u + nn] = acc[u][i];
         }
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int g = (tid >> 5) + 8 * i;
-        if (g < G && (tid & 31) == 0) {
-            float *rec = ws + ((row0 + g) * nsplit + split) * R;
-            rec[D] = m_run[i];
-            rec[D + 1] = l_run[i];
-        }
+    if (jj == 0 && nn < G) {
+        float *rec = ws + ((row0 + nn) * nsplit + split) * R;
+        rec[D] = m_run;
+        rec[D + 1] = l_run;
     }
 }
 
@@ -523,11 +555,11 @@ hipError_t launch_strided_attn(const dkv_config &c, const void *cache, const flo
 {
     dim3 grid(nsplit, c.n_kv_heads, c.batch);
     if (c.head_dim == 64)
-        hipLaunchKernelGGL(k_strided_attn<64>, grid, dim3(kStridedThreads), 0, st, c, (const uint8_t *)cache, q,
-                           lens, scale_log2, ws, nsplit, chunk);
+        hipLaunchKernelGGL(k_strided_attn<64>, grid, dim3(64), 0, st, c, (const uint8_t *)cache, q, lens,
+                           scale_log2, ws, nsplit, chunk);
     else
-        hipLaunchKernelGGL(k_strided_attn<128>, grid, dim3(kStridedThreads), 0, st, c, (const uint8_t *)cache, q,
-                           lens, scale_log2, ws, nsplit, chunk);
+        hipLaunchKernelGGL(k_strided_attn<128>, grid, dim3(64), 0, st, c, (const uint8_t *)cache, q, lens,
+                           scale_log2, ws, nsplit, chunk);
     return hipGetLastError();
 }
 
