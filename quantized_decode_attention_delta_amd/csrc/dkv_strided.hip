@@ -386,13 +386,14 @@ __device__ inline void strided_rebuild_q(const RowQ<D> &w, int c0, float *__rest
 // columns beyond the group are zero.  The next sub-tile's rows are fetched
 // while the current one is processed.
 template <int D>
-__global__ void __launch_bounds__(64)
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3)))
     k_strided_attn(dkv_config cfg, const uint8_t *__restrict__ cache, const float *__restrict__ q,
                    const int32_t *__restrict__ lens, float scale_log2, float *__restrict__ ws, int nsplit, int chunk)
 {
     constexpr int KS = D + 4, VS = D + 16;       // LDS row strides: conflict-free operand reads
     constexpr int NKK = D / 4;                   // k-steps of the logits
     constexpr int NCB = D / 16;                  // 16-channel column blocks of the weighted V rows
+    // K and V of a sub-tile take turns in one LDS tile (V is rebuilt after the logits)
     const StridedLayout ly = strided_layout(cfg);
     const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
     const int jj = lane >> 4, nn = lane & 15;
@@ -401,8 +402,9 @@ __global__ void __launch_bounds__(64)
     const int t_begin = split * chunk * 32, t_end = min(L, t_begin + chunk * 32);
     const int64_t row0 = (int64_t)b * Hq + (int64_t)h * G;
 
-    __shared__ __attribute__((aligned(16))) float kt[16 * KS];
-    __shared__ __attribute__((aligned(16))) float vt[16 * VS];
+    __shared__ __attribute__((aligned(16))) float tile[16 * VS];
+    float *const kt = tile;
+    float *const vt = tile;
     __shared__ float pl[kStridedMaxG][17];
     __shared__ float al[kStridedMaxG];
 
@@ -433,18 +435,11 @@ __global__ void __launch_bounds__(64)
         const int nt = min(16, t_end - t0);
         if (r < nt) {
             strided_rebuild_q<D>(nk, c0, kt + r * KS + c0);
-            strided_rebuild_q<D>(nv, c0, vt + r * VS + c0);
         } else {
 #pragma unroll
-            for (int i = 0; i < D / 4; i += 4) {
-                *(f4 *)&kt[r * KS + c0 + i] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-                *(f4 *)&vt[r * VS + c0 + i] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-            }
+            for (int i = 0; i < D / 4; i += 4) *(f4 *)&kt[r * KS + c0 + i] = f4{0.0f, 0.0f, 0.0f, 0.0f};
         }
-        if (t0 + 16 + r < t_end) {
-            strided_fetch_q<D>(kb, ly, t0 + 16 + r, c0, nk);
-            strided_fetch_q<D>(vb, ly, t0 + 16 + r, c0, nv);
-        }
+        if (t0 + 16 + r < t_end) strided_fetch_q<D>(kb, ly, t0 + 16 + r, c0, nk);
         __syncthreads();
         // logits of tokens 4*jj + i for head nn, in two chains
         f4 C0 = f4{0.0f, 0.0f, 0.0f, 0.0f}, C1 = C0;
@@ -475,6 +470,14 @@ __global__ void __launch_bounds__(64)
         l_run = l_run * alpha + rows_sum(ps);
         m_run = m_new;
         if (jj == 0) al[nn] = alpha;
+        __syncthreads();                         // the logits have read the K tile
+        if (r < nt) {
+            strided_rebuild_q<D>(nv, c0, vt + r * VS + c0);
+        } else {
+#pragma unroll
+            for (int i = 0; i < D / 4; i += 4) *(f4 *)&vt[r * VS + c0 + i] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+        if (t0 + 16 + r < t_end) strided_fetch_q<D>(vb, ly, t0 + 16 + r, c0, nv);
         __syncthreads();
         // weighted V rows: heads 4*jj + i, channels 16*cb + nn
         float alr[4];
