@@ -24,12 +24,12 @@
 //   scales  fp16 [cap][D/32]
 //   idx     u16  [cap]        reference index of every token
 //
-// Decode attention: one workgroup of 256 threads per run of 32-token tiles
-// of one (sequence, kv-head), all the kv-head's query heads.  Per tile the
-// threads rebuild K and V (reference row gathered by index + dequantised
-// residual) in fp32, take the logits, run the online softmax and accumulate
-// the weighted V rows; the partial (acc, m, l) goes to the split-K combine
-// shared with the Delta-KV kernels.  HBM traffic per token is the two
+// Decode attention: one wave per run of 32-token tiles of one (sequence,
+// kv-head), all the kv-head's query heads.  Per 16-token sub-tile the wave
+// rebuilds K and V (reference row gathered by index + dequantised residual)
+// in fp32, takes the logits and the weighted V rows on fp32 matrix cores and
+// runs the online softmax; the partial (acc, m, l) goes to the split-K
+// combine shared with the Delta-KV kernels.  HBM traffic per token is the two
 // streams' codes, scales and index (74 bytes each at D = 128); the reference
 // rows, 1/stride of the tokens, are gathered from the L2 and Infinity caches.
 #include "dkv_fused_common.h"
@@ -158,48 +158,10 @@ __global__ void __launch_bounds__(kStridedThreads)
     }
 }
 
-// Raw data of channels [c0, c0 + D/8) of one token of one stream: its code
-// bytes, block scale and reference row slice (the row found through the
-// token's index, clamped so that a token never encoded reads a wrong row, not
-// past the plane).
-template <int D>
-struct RowRaw {
-    uint32_t cw[D / 32];     // D/8 code bytes
-    uint32_t rw[D / 16];     // D/8 fp16 reference values
-    uint32_t sc;             // fp16 scale bits
-};
-
 // The token's reference index, clamped to the plane.
 __device__ inline int strided_ref(const uint8_t *__restrict__ base, const StridedLayout &ly, int t)
 {
     return min((int)((const uint16_t *)(base + ly.off_idx))[t], ly.nref - 1);
-}
-
-// Codes, scale and reference slice of token t with reference index k.
-template <int D>
-__device__ inline void strided_fetch(const uint8_t *__restrict__ base, const StridedLayout &ly, int t, int k, int c0,
-                                     RowRaw<D> &w)
-{
-    constexpr int NB = D / 32, CPT = D / 8;
-    const int blk = c0 >> 5, e0 = c0 & 31;
-    w.sc = ((const uint16_t *)(base + ly.off_scales))[(int64_t)t * NB + blk];
-    const uint8_t *cb = base + ly.off_codes + (int64_t)t * (D / 2) + 16 * blk + (e0 & 15);
-    if constexpr (CPT == 16) {
-        const u4 x = *(const u4 *)cb;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) w.cw[i] = x[i];
-    } else {
-        const u2 x = *(const u2 *)cb;
-        w.cw[0] = x[0];
-        w.cw[1] = x[1];
-    }
-    const uint16_t *r = (const uint16_t *)base + (int64_t)k * D + c0;
-#pragma unroll
-    for (int i = 0; i < CPT / 8; ++i) {
-        const u4 x = ((const u4 *)r)[i];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) w.rw[4 * i + j] = x[j];
-    }
 }
 
 // One new token per sequence at positions[b] (negative: none), the same
@@ -277,53 +239,6 @@ __global__ void __launch_bounds__(kStridedThreads)
     if (is_ref && tid < D) refs[(int64_t)kt * D + tid] = x[tid];
 }
 
-// Rebuild the channels in fp32: reference + (code - 8) * scale.
-template <int D>
-__device__ inline void strided_rebuild(const RowRaw<D> &w, int c0, float (&out)[D / 8])
-{
-    constexpr int CPT = D / 8;
-    const int sh = 4 * ((c0 & 31) >> 4);
-    const float sf = h2f((uint16_t)w.sc);
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-        const int code = (int)((w.cw[i >> 2] >> (8 * (i & 3) + sh)) & 15u);
-        const uint16_t rh = (uint16_t)((i & 1) ? (w.rw[i >> 1] >> 16) : (w.rw[i >> 1] & 0xFFFF));
-        out[i] = __builtin_fmaf((float)(code - 8), sf, h2f(rh));     // exact product, one rounding
-    }
-}
-
-// Lane reductions in registers (DPP moves within a row of 16 lanes, the
-// row-pair swap across rows): every lane of the group gets the result.
-template <int CTRL>
-__device__ inline float dpp_f(float x)
-{
-    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
-}
-__device__ inline float sum8_lanes(float x)          // groups of 8 aligned lanes
-{
-    x += dpp_f<0xB1>(x);     // quad_perm [1,0,3,2]
-    x += dpp_f<0x4E>(x);     // quad_perm [2,3,0,1]
-    return x + dpp_f<0x141>(x);   // row_half_mirror: the other quad of the 8
-}
-__device__ inline float sum32_lanes(float x)         // groups of 32 aligned lanes
-{
-    x = sum8_lanes(x);
-    x += dpp_f<0x140>(x);    // row_mirror: the other 8 of the row
-    float a0, a1;
-    swap16(x, a0, a1);
-    return a0 + a1;
-}
-__device__ inline float max32_lanes(float x)
-{
-    x = fmaxf(x, dpp_f<0xB1>(x));
-    x = fmaxf(x, dpp_f<0x4E>(x));
-    x = fmaxf(x, dpp_f<0x141>(x));
-    x = fmaxf(x, dpp_f<0x140>(x));
-    float a0, a1;
-    swap16(x, a0, a1);
-    return fmaxf(a0, a1);
-}
-
 // Raw data of D/4 channels [c0, c0 + D/4) of one token of one stream (one
 // block at D = 128, half a block at D = 64): the block's 16 code bytes, its
 // scale and the reference row slice.
@@ -377,8 +292,8 @@ __device__ inline void strided_rebuild_q(const RowQ<D> &w, int c0, float *__rest
 
 // grid (nsplit, n_kv_heads, batch), one wave per workgroup: the split's run of
 // 32-token tiles, taken as 16-token sub-tiles with no barrier between waves.
-// Per sub-tile: lane (token lane/4, a quarter of the channels) rebuilds K and
-// V into the wave's LDS; the logits (16 tokens x 16 head columns over D
+// Per sub-tile: lane (token lane/4, a quarter of the channels) rebuilds K,
+// and after the logits V, into the wave's one LDS tile; the logits (16 tokens x 16 head columns over D
 // channels) and the weighted V rows (16 head rows x D channels over the 16
 // tokens) are fp32 matrix-core products (v_mfma_f32_16x16x4_f32: lane 16*j + n
 // supplies row n of A and column n of B at k = j, and holds rows 4j..4j+3 of
