@@ -353,6 +353,21 @@ dkv_status dkv_strided_append(const dkv_config *cfg, void *cache, const uint16_t
                               dkv_stream_t stream);
 
 /*
+ * One serving step on the strided-reference cache in one call:
+ * dkv_strided_append (k_new, v_new, positions, window) followed by
+ * dkv_strided_attn_decode (q, seq_lens, ...), with the append done inside the
+ * decode's split launch by the workgroup whose run holds the new token.  The
+ * cache bytes and the output are identical to the two separate calls.
+ * seq_lens must already count the new token (position + 1).  Errors: as the
+ * two calls.  Two launches on `stream` (split phase with the append, combine).
+ */
+dkv_status dkv_strided_append_attn_decode(const dkv_config *cfg, void *cache, const uint16_t *k_new,
+                                          const uint16_t *v_new, const int32_t *positions,
+                                          int32_t window, const float *q, const int32_t *seq_lens,
+                                          float softmax_scale, float *out, void *workspace,
+                                          size_t workspace_bytes, dkv_stream_t stream);
+
+/*
  * Decode attention over the strided-reference cache: out[b][hq] =
  * softmax(scale * q . K_hat^T) V_hat over tokens t < min(seq_lens[b], capacity),
  * arguments as dkv_attn_decode (workspace of dkv_workspace_bytes(cfg) bytes).

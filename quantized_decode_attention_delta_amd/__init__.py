@@ -12,5 +12,5 @@ from .dkv import (  # noqa: F401
     dkv_reconstruct, dkv_export, export_shapes, dkv_q4_0_encode, dkv_q4_0_export, dkv_attn_decode_q4_0,
     dkv_attn_decode_f16, dkv_stream_read_sink_words, dkv_stream_read, dkv_attn_distortion,
     dkv_q8_0_encode, dkv_strided_cache_bytes, dkv_strided_layout, dkv_strided_encode_prefill,
-    dkv_strided_attn_decode, dkv_strided_append,
+    dkv_strided_attn_decode, dkv_strided_append, dkv_strided_append_attn_decode,
 )

@@ -33,7 +33,7 @@ void strided_plane_offsets(const dkv_config &, int64_t *);
 hipError_t launch_strided_encode(const dkv_config &, void *, const uint16_t *, const uint16_t *, const int32_t *, int,
                                  int, hipStream_t);
 hipError_t launch_strided_attn(const dkv_config &, const void *, const float *, const int32_t *, float, float *, int,
-                               int, hipStream_t);
+                               int, const uint16_t *, const uint16_t *, const int32_t *, int, hipStream_t);
 hipError_t launch_strided_append(const dkv_config &, void *, const uint16_t *, const uint16_t *, const int32_t *, int,
                                  hipStream_t);
 hipError_t launch_attn_fused(const dkv_config &, const void *, const int32_t *, const float *,
@@ -458,7 +458,23 @@ dkv_status dkv_strided_attn_decode(const dkv_config *c, const void *cache, const
     if (!ws || ws_bytes < workspace_total(*c)) return DKV_ERR_WORKSPACE;
     const Plan p = strided_plan(*c);
     hipError_t e = launch_strided_attn(*c, cache, q, lens, resolve_scale(*c, scale), (float *)ws, p.nsplit, p.chunk,
-                                       (hipStream_t)stream);
+                                       nullptr, nullptr, nullptr, 0, (hipStream_t)stream);
+    if (e != hipSuccess) return DKV_ERR_HIP;
+    return hip_status(launch_combine(*c, (const float *)ws, p.nsplit, out, (hipStream_t)stream));
+}
+
+dkv_status dkv_strided_append_attn_decode(const dkv_config *c, void *cache, const uint16_t *k_new,
+                                          const uint16_t *v_new, const int32_t *positions, int32_t window,
+                                          const float *q, const int32_t *lens, float scale, float *out, void *ws,
+                                          size_t ws_bytes, dkv_stream_t stream)
+{
+    dkv_status st = strided_check(c);
+    if (st != DKV_OK) return st;
+    if (!cache || !k_new || !v_new || !positions || window < 0 || !q || !lens || !out) return DKV_ERR_ARG;
+    if (!ws || ws_bytes < workspace_total(*c)) return DKV_ERR_WORKSPACE;
+    const Plan p = strided_plan(*c);
+    hipError_t e = launch_strided_attn(*c, cache, q, lens, resolve_scale(*c, scale), (float *)ws, p.nsplit, p.chunk,
+                                       k_new, v_new, positions, window, (hipStream_t)stream);
     if (e != hipSuccess) return DKV_ERR_HIP;
     return hip_status(launch_combine(*c, (const float *)ws, p.nsplit, out, (hipStream_t)stream));
 }

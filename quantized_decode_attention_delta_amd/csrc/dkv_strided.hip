@@ -239,6 +239,56 @@ __global__ void __launch_bounds__(kStridedThreads)
     if (is_ref && tid < D) refs[(int64_t)kt * D + tid] = x[tid];
 }
 
+// The append of one token t of one stream by one wave (the coding of
+// k_strided_append): candidates scanned by the 64 lanes, the argmin over
+// (distance, index) across the wave, then the Q4_0 blocks two half-waves at a
+// time, and the token's row kept when it is a reference.
+template <int D>
+__device__ inline void strided_append_wave(const StridedLayout &ly, int stride, uint8_t *base,
+                                           const uint16_t *__restrict__ x, int t, int window, int lane)
+{
+    constexpr int NB = D / 32;
+    uint16_t *refs = (uint16_t *)base;
+    const int kt = t / stride;
+    const bool is_ref = t % stride == 0;
+    const int k0 = (window > 0 && kt - window + 1 > 0) ? kt - window + 1 : 0;
+    double bd = INFINITY;
+    int bk = 0x7FFFFFFF;
+    for (int kk = k0 + lane; kk <= kt; kk += 64) {
+        const uint16_t *r = (is_ref && kk == kt) ? x : refs + (int64_t)kk * D;
+        const double d = sqdist_rows<D>(x, r);
+        if (d < bd) {
+            bd = d;
+            bk = kk;
+        }
+    }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const double d2 = __shfl_xor(bd, off);
+        const int k2 = __shfl_xor(bk, off);
+        if (d2 < bd || (d2 == bd && k2 < bk)) {
+            bd = d2;
+            bk = k2;
+        }
+    }
+    const uint16_t *r = (is_ref && bk == kt) ? x : refs + (int64_t)bk * D;
+    if (lane == 0) ((uint16_t *)(base + ly.off_idx))[t] = (uint16_t)bk;
+    const int ln = lane & 31;
+    for (int blk = lane >> 5; blk < NB; blk += 2) {       // the same count for both half-waves
+        const int c = 32 * blk + ln;
+        const float xv = h2f(x[c]);
+        float xh = h2f(r[c]);
+        int code;
+        uint16_t s16;
+        q40_delta_step(xv, xh, code, s16);
+        const int hi = __shfl_down(code, 16, 32);
+        if (ln < 16) base[ly.off_codes + (int64_t)t * (D / 2) + 16 * blk + ln] = (uint8_t)(code | (hi << 4));
+        if (ln == 0) ((uint16_t *)(base + ly.off_scales))[(int64_t)t * NB + blk] = s16;
+    }
+    if (is_ref)
+        for (int c = lane; c < D; c += 64) refs[(int64_t)kt * D + c] = x[c];
+}
+
 // Raw data of D/4 channels [c0, c0 + D/4) of one token of one stream (one
 // block at D = 128, half a block at D = 64): the block's 16 code bytes, its
 // scale and the reference row slice.
@@ -300,10 +350,15 @@ __device__ inline void strided_rebuild_q(const RowQ<D> &w, int c0, float *__rest
 // column n of the result); the softmax runs down each head column.  Head
 // columns beyond the group are zero.  The next sub-tile's rows are fetched
 // while the current one is processed.
+// With positions (not null) the workgroup whose run holds a sequence's new
+// token appends it first (k_new, v_new fp16 [B][Hkv][D]; the cache is written
+// through the same pointer it is read through, hence no __restrict__ on it).
 template <int D>
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3)))
-    k_strided_attn(dkv_config cfg, const uint8_t *__restrict__ cache, const float *__restrict__ q,
-                   const int32_t *__restrict__ lens, float scale_log2, float *__restrict__ ws, int nsplit, int chunk)
+    k_strided_attn(dkv_config cfg, const uint8_t *cache, const float *__restrict__ q,
+                   const int32_t *__restrict__ lens, float scale_log2, float *__restrict__ ws, int nsplit, int chunk,
+                   const uint16_t *__restrict__ knew, const uint16_t *__restrict__ vnew,
+                   const int32_t *__restrict__ positions, int window)
 {
     constexpr int KS = D + 4, VS = D + 16;       // LDS row strides: conflict-free operand reads
     constexpr int NKK = D / 4;                   // k-steps of the logits
@@ -313,6 +368,18 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3)))
     const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
     const int jj = lane >> 4, nn = lane & 15;
     const int Hq = cfg.n_q_heads, G = Hq / cfg.n_kv_heads;
+    if (positions) {
+        const int pos = positions[b];
+        if (pos >= 0 && pos < cfg.max_tokens && (pos >> 5) / chunk == split) {
+            const int64_t sh = ((int64_t)b * cfg.n_kv_heads + h) * 2;
+            uint8_t *wc = (uint8_t *)cache;
+            const int64_t xo = ((int64_t)b * cfg.n_kv_heads + h) * D;
+            strided_append_wave<D>(ly, cfg.kf, wc + sh * ly.stream_bytes, knew + xo, pos, window, lane);
+            strided_append_wave<D>(ly, cfg.kf, wc + (sh + 1) * ly.stream_bytes, vnew + xo, pos, window, lane);
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        }
+    }
     const int L = max(0, min(lens[b], cfg.max_tokens));
     const int t_begin = split * chunk * 32, t_end = min(L, t_begin + chunk * 32);
     const int64_t row0 = (int64_t)b * Hq + (int64_t)h * G;
@@ -468,16 +535,18 @@ hipError_t launch_strided_append(const dkv_config &c, void *cache, const uint16_
     return hipGetLastError();
 }
 
+// knew/vnew/positions null: decode only.
 hipError_t launch_strided_attn(const dkv_config &c, const void *cache, const float *q, const int32_t *lens,
-                               float scale_log2, float *ws, int nsplit, int chunk, hipStream_t st)
+                               float scale_log2, float *ws, int nsplit, int chunk, const uint16_t *knew,
+                               const uint16_t *vnew, const int32_t *positions, int window, hipStream_t st)
 {
     dim3 grid(nsplit, c.n_kv_heads, c.batch);
     if (c.head_dim == 64)
         hipLaunchKernelGGL(k_strided_attn<64>, grid, dim3(64), 0, st, c, (const uint8_t *)cache, q, lens,
-                           scale_log2, ws, nsplit, chunk);
+                           scale_log2, ws, nsplit, chunk, knew, vnew, positions, window);
     else
         hipLaunchKernelGGL(k_strided_attn<128>, grid, dim3(64), 0, st, c, (const uint8_t *)cache, q, lens,
-                           scale_log2, ws, nsplit, chunk);
+                           scale_log2, ws, nsplit, chunk, knew, vnew, positions, window);
     return hipGetLastError();
 }
 

@@ -87,6 +87,7 @@ _SIGS = {
     "dkv_strided_encode_prefill": ([_CFG, _P, _P, _P, _P, _I32, _I32, _P], _I32),
     "dkv_strided_attn_decode": ([_CFG, _P, _P, _P, _F, _P, _P, _SZ, _P], _I32),
     "dkv_strided_append": ([_CFG, _P, _P, _P, _P, _I32, _P], _I32),
+    "dkv_strided_append_attn_decode": ([_CFG, _P, _P, _P, _P, _I32, _P, _P, _F, _P, _P, _SZ, _P], _I32),
 }
 
 
@@ -405,3 +406,18 @@ def dkv_strided_append(cfg: Config, cache, k_new, v_new, positions, window: int 
         _f16(k_new, "k_new", B * H * D), _f16(v_new, "v_new", B * H * D),
         _ptr(positions, torch.int32, "positions", B), int(window), _stream(stream))
     _check("dkv_strided_append", st)
+
+
+def dkv_strided_append_attn_decode(cfg: Config, cache, k_new, v_new, positions, q, seq_lens, out, workspace,
+                                   window: int = 0, softmax_scale=0.0, stream=None):
+    """dkv_strided_append then dkv_strided_attn_decode in one call (the append inside the split launch)."""
+    import torch
+    B, H, Hq, D = cfg.batch, cfg.n_kv_heads, cfg.n_q_heads, cfg.head_dim
+    st = load().dkv_strided_append_attn_decode(
+        ctypes.byref(cfg.c()), _ptr(cache, torch.uint8, "cache", dkv_strided_cache_bytes(cfg)),
+        _f16(k_new, "k_new", B * H * D), _f16(v_new, "v_new", B * H * D),
+        _ptr(positions, torch.int32, "positions", B), int(window), _ptr(q, torch.float32, "q", B * Hq * D),
+        _ptr(seq_lens, torch.int32, "seq_lens", B), float(softmax_scale), _ptr(out, torch.float32, "out", B * Hq * D),
+        _ptr(workspace, torch.uint8, "workspace"), workspace.numel() if workspace is not None else 0,
+        _stream(stream))
+    _check("dkv_strided_append_attn_decode", st)

@@ -125,6 +125,10 @@ def test_argument_errors_return_before_launch():
     assert lib.dkv_strided_attn_decode(cp, fake, fake, fake, 0.0, fake, fake, 16, null) == binding.DKV_ERR_WORKSPACE
     assert lib.dkv_strided_layout(cp, null) == binding.DKV_ERR_ARG
     assert lib.dkv_strided_append(cp, fake, fake, fake, null, 0, null) == binding.DKV_ERR_ARG
+    assert lib.dkv_strided_append_attn_decode(cp, fake, fake, fake, fake, 0, fake, fake, 0.0, fake, fake, 16,
+                                              null) == binding.DKV_ERR_WORKSPACE
+    assert lib.dkv_strided_append_attn_decode(cp, fake, fake, fake, null, 0, fake, fake, 0.0, fake, fake, 1 << 30,
+                                              null) == binding.DKV_ERR_ARG
     assert lib.dkv_strided_append(cpg, fake, fake, fake, fake, 0, null) == binding.DKV_ERR_UNSUPPORTED
     assert lib.dkv_check_config(None) == binding.DKV_ERR_ARG
     assert dkv.status_str(binding.DKV_ERR_WORKSPACE) == "workspace missing or too small"

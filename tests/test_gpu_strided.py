@@ -188,3 +188,44 @@ def test_strided_append_matches_prefill(kw, stride, window):
     dkv.dkv_strided_attn_decode(cfg, bcache, q, lens_d, ob, ws)
     torch.cuda.synchronize()
     assert torch.equal(oa, ob)
+
+
+@pytest.mark.parametrize("kw,stride,window", [
+    (dict(S=300, B=3, Hq=8, Hkv=2, extra_tokens=40), 32, 64),
+    (dict(S=300, B=3, Hq=16, Hkv=2, D=64, extra_tokens=40), 8, 0),
+    (dict(S=2048, B=32, Hq=32, Hkv=8, extra_tokens=8), 32, 64),     # runs of 16 tiles
+])
+def test_strided_fused_step_matches_append_then_decode(kw, stride, window):
+    """dkv_strided_append_attn_decode leaves the same cache bytes and gives the
+    same output as dkv_strided_append followed by dkv_strided_attn_decode."""
+    w = synth.make("8b" if kw.get("Hkv") == 2 else "70b", **kw)
+    print(f"strided fused step {kw} stride={stride} window={window}", flush=True)
+    cfg = _cfg(w, stride)
+    s_max = w.k.shape[2]
+    k = torch.from_numpy(np.ascontiguousarray(w.k)).to(U.DEV)
+    v = torch.from_numpy(np.ascontiguousarray(w.v)).to(U.DEV)
+    lens = np.minimum(np.asarray(w.seq_lens, np.int32), w.S - 5)
+    lens[0] = 0
+    a = torch.zeros(dkv.dkv_strided_cache_bytes(cfg), dtype=torch.uint8, device=U.DEV)
+    dkv.dkv_strided_encode_prefill(cfg, a, k, v, torch.from_numpy(lens).to(U.DEV), s_max, window)
+    bcache = a.clone()
+    ws_a = torch.zeros(dkv.dkv_workspace_bytes(cfg), dtype=torch.uint8, device=U.DEV)
+    ws_b = torch.zeros_like(ws_a)
+    oa = torch.zeros(w.B, w.Hq, w.D, dtype=torch.float32, device=U.DEV)
+    ob = torch.zeros_like(oa)
+    for step in range(8):
+        pos = lens.copy()
+        if step % 3 == 2:
+            pos[1] = -1
+        kn = torch.stack([k[b, :, max(int(pos[b]), 0)] for b in range(w.B)]).contiguous()
+        vn = torch.stack([v[b, :, max(int(pos[b]), 0)] for b in range(w.B)]).contiguous()
+        lens = lens + (pos >= 0)
+        pd = torch.from_numpy(pos).to(U.DEV)
+        ld = torch.from_numpy(lens.astype(np.int32)).to(U.DEV)
+        q = torch.from_numpy(synth.queries(w, step=step)).to(U.DEV)
+        dkv.dkv_strided_append(cfg, a, kn, vn, pd, window)
+        dkv.dkv_strided_attn_decode(cfg, a, q, ld, oa, ws_a)
+        dkv.dkv_strided_append_attn_decode(cfg, bcache, kn, vn, pd, q, ld, ob, ws_b, window=window)
+        torch.cuda.synchronize()
+        assert torch.equal(a, bcache), f"cache differs after step {step}"
+        assert torch.equal(oa, ob), f"output differs after step {step}"
