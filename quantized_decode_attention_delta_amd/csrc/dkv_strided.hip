@@ -164,83 +164,8 @@ __device__ inline int strided_ref(const uint8_t *__restrict__ base, const Stride
     return min((int)((const uint16_t *)(base + ly.off_idx))[t], ly.nref - 1);
 }
 
-// One new token per sequence at positions[b] (negative: none), the same
-// coding as the prefill encode: candidates are read from the reference plane,
-// which holds the rows the prefill read from its input, and the token itself
-// when it is a reference.  grid (1, n_kv_heads * 2, batch).
-template <int D>
-__global__ void __launch_bounds__(kStridedThreads)
-    k_strided_append(dkv_config cfg, uint8_t *__restrict__ cache, const uint16_t *__restrict__ knew,
-                     const uint16_t *__restrict__ vnew, const int32_t *__restrict__ positions, int window)
-{
-    constexpr int NB = D / 32;
-    const StridedLayout ly = strided_layout(cfg);
-    const int stride = cfg.kf;
-    const int h = blockIdx.y >> 1, s = blockIdx.y & 1, b = blockIdx.z;
-    const int tid = threadIdx.x;
-    const int t = positions[b];
-    if (t < 0 || t >= cfg.max_tokens) return;
-    const uint16_t *x = (s ? vnew : knew) + ((int64_t)b * cfg.n_kv_heads + h) * D;
-    uint8_t *base = cache + (((int64_t)b * cfg.n_kv_heads + h) * 2 + s) * ly.stream_bytes;
-    uint16_t *refs = (uint16_t *)base;
-    const int kt = t / stride;
-    const bool is_ref = t % stride == 0;
-    const int k0 = (window > 0 && kt - window + 1 > 0) ? kt - window + 1 : 0;
-
-    __shared__ double sd[kStridedThreads / 64];
-    __shared__ int sk[kStridedThreads / 64];
-    double bd = INFINITY;
-    int bk = 0x7FFFFFFF;
-    for (int kk = k0 + tid; kk <= kt; kk += kStridedThreads) {
-        const uint16_t *r = (is_ref && kk == kt) ? x : refs + (int64_t)kk * D;
-        const double d = sqdist_rows<D>(x, r);
-        if (d < bd) {
-            bd = d;
-            bk = kk;
-        }
-    }
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const double d2 = __shfl_xor(bd, off);
-        const int k2 = __shfl_xor(bk, off);
-        if (d2 < bd || (d2 == bd && k2 < bk)) {
-            bd = d2;
-            bk = k2;
-        }
-    }
-    if ((tid & 63) == 0) {
-        sd[tid >> 6] = bd;
-        sk[tid >> 6] = bk;
-    }
-    __syncthreads();
-    bd = sd[0];
-    bk = sk[0];
-#pragma unroll
-    for (int w = 1; w < kStridedThreads / 64; ++w)
-        if (sd[w] < bd || (sd[w] == bd && sk[w] < bk)) {
-            bd = sd[w];
-            bk = sk[w];
-        }
-    const uint16_t *r = (is_ref && bk == kt) ? x : refs + (int64_t)bk * D;
-    if (tid == 0) ((uint16_t *)(base + ly.off_idx))[t] = (uint16_t)bk;
-    // Q4_0 residual: one half-wave per block
-    const int hw = tid >> 5, ln = tid & 31;
-    if (hw < NB) {
-        const int c = 32 * hw + ln;
-        const float xv = h2f(x[c]);
-        float xh = h2f(r[c]);
-        int code;
-        uint16_t s16;
-        q40_delta_step(xv, xh, code, s16);
-        const int hi = __shfl_down(code, 16, 32);
-        if (ln < 16) base[ly.off_codes + (int64_t)t * (D / 2) + 16 * hw + ln] = (uint8_t)(code | (hi << 4));
-        if (ln == 0) ((uint16_t *)(base + ly.off_scales))[(int64_t)t * NB + hw] = s16;
-    }
-    if (is_ref && tid < D) refs[(int64_t)kt * D + tid] = x[tid];
-}
-
-// The append of one token t of one stream by one wave (the coding of
-// k_strided_append): candidates scanned by the 64 lanes, the argmin over
+// The append of one token t of one stream by one wave: candidates scanned
+// by the 64 lanes, the argmin over
 // (distance, index) across the wave, then the Q4_0 blocks two half-waves at a
 // time, and the token's row kept when it is a reference.
 template <int D>
@@ -287,6 +212,24 @@ __device__ inline void strided_append_wave(const StridedLayout &ly, int stride, 
     }
     if (is_ref)
         for (int c = lane; c < D; c += 64) refs[(int64_t)kt * D + c] = x[c];
+}
+
+// One new token per sequence at positions[b] (negative: none), the same
+// coding as the prefill encode: candidates are read from the reference plane,
+// which holds the rows the prefill read from its input, and the token itself
+// when it is a reference.  grid (1, n_kv_heads * 2, batch), one wave.
+template <int D>
+__global__ void __launch_bounds__(64)
+    k_strided_append(dkv_config cfg, uint8_t *__restrict__ cache, const uint16_t *__restrict__ knew,
+                     const uint16_t *__restrict__ vnew, const int32_t *__restrict__ positions, int window)
+{
+    const StridedLayout ly = strided_layout(cfg);
+    const int h = blockIdx.y >> 1, s = blockIdx.y & 1, b = blockIdx.z;
+    const int t = positions[b];
+    if (t < 0 || t >= cfg.max_tokens) return;
+    const uint16_t *x = (s ? vnew : knew) + ((int64_t)b * cfg.n_kv_heads + h) * D;
+    uint8_t *base = cache + (((int64_t)b * cfg.n_kv_heads + h) * 2 + s) * ly.stream_bytes;
+    strided_append_wave<D>(ly, cfg.kf, base, x, t, window, threadIdx.x);
 }
 
 // Raw data of D/4 channels [c0, c0 + D/4) of one token of one stream (one
@@ -527,11 +470,11 @@ hipError_t launch_strided_append(const dkv_config &c, void *cache, const uint16_
 {
     dim3 grid(1, c.n_kv_heads * 2, c.batch);
     if (c.head_dim == 64)
-        hipLaunchKernelGGL(k_strided_append<64>, grid, dim3(kStridedThreads), 0, st, c, (uint8_t *)cache, knew, vnew,
-                           positions, window);
+        hipLaunchKernelGGL(k_strided_append<64>, grid, dim3(64), 0, st, c, (uint8_t *)cache, knew, vnew, positions,
+                           window);
     else
-        hipLaunchKernelGGL(k_strided_append<128>, grid, dim3(kStridedThreads), 0, st, c, (uint8_t *)cache, knew,
-                           vnew, positions, window);
+        hipLaunchKernelGGL(k_strided_append<128>, grid, dim3(64), 0, st, c, (uint8_t *)cache, knew, vnew, positions,
+                           window);
     return hipGetLastError();
 }
 
