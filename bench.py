@@ -617,7 +617,7 @@ def run_mixed(args):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py: runs on one GPU; --gpus {args.gpus} is not supported "
               "(the multi-GPU sharding is a design note only)", file=sys.stderr)
         sys.exit(2)
     import numpy as np
