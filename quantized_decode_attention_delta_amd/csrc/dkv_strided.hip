@@ -283,30 +283,75 @@ __device__ inline void strided_rebuild_q(const RowQ<D> &w, int c0, float *__rest
     }
 }
 
+// K operands of one token for the fp16 matrix instructions: lane 16*j + n
+// holds row n of A at k = 8j..8j+7, so for each block b it takes the
+// reference channels 32b + 8j .. 32b + 8j + 7 (exact fp16) and the same
+// channels' code bytes (8 bytes of the block, nibble plane j >> 1).
+template <int D>
+struct KOps {
+    u4 ref[D / 32];
+    u2 code[D / 32];
+    uint32_t sc;                                 // scale bits of block min(j, D/32 - 1)
+};
+
+template <int D>
+__device__ inline void strided_fetch_k(const uint8_t *__restrict__ base, const StridedLayout &ly, int t, int j,
+                                       KOps<D> &o)
+{
+    constexpr int NB = D / 32;
+    const int k = strided_ref(base, ly, t);
+    const uint16_t *r = (const uint16_t *)base + (int64_t)k * D + 8 * j;
+    const uint8_t *cb = base + ly.off_codes + (int64_t)t * (D / 2) + 8 * (j & 1);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        o.ref[b] = *(const u4 *)(r + 32 * b);
+        o.code[b] = *(const u2 *)(cb + 16 * b);
+    }
+    o.sc = ((const uint16_t *)(base + ly.off_scales))[(int64_t)t * NB + min(j, NB - 1)];
+}
+
+// (c - 8) of 8 codes as exact fp16: 1024 + c built by placing each nibble in
+// the low mantissa of 0x6400, then 1032 subtracted.
+__device__ inline h8 codes_f16(u2 w, int sh)
+{
+    u4 o;
+    const h2 off = h2{(_Float16)1032.0f, (_Float16)1032.0f};
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const uint32_t n4 = (w[i] >> sh) & 0x0F0F0F0Fu;
+        const uint32_t p0 = __builtin_amdgcn_perm(0u, n4, 0x0C010C00u) | 0x64006400u;   // bytes 0, 1
+        const uint32_t p1 = __builtin_amdgcn_perm(0u, n4, 0x0C030C02u) | 0x64006400u;   // bytes 2, 3
+        o[2 * i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, p0) - off);
+        o[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, p1) - off);
+    }
+    return __builtin_bit_cast(h8, o);
+}
+
 // grid (nsplit, n_kv_heads, batch), one wave per workgroup: the split's run of
 // 32-token tiles, taken as 16-token sub-tiles with no barrier between waves.
-// Per sub-tile: lane (token lane/4, a quarter of the channels) rebuilds K,
-// and after the logits V, into the wave's one LDS tile; the logits (16 tokens x 16 head columns over D
+// Per sub-tile the logits are taken in the residual domain on fp16 matrix
+// instructions (v_mfma_f32_16x16x32_f16: lane 16*j + n holds row n of A and
+// column n of B at k = 8j..8j+7, and rows 4j..4j+3 of column n of the result):
+//   q.khat_t = q.r_idx(t) + sum_b s_t,b * sum_(j in b) q_j (c_t,j - 8)
+// with the reference rows (exact fp16) and the codes (c - 8, exact fp16) as A
+// operands and q, scaled by 2^-E and split hi + lo, as B.  V is rebuilt in
+// fp32 into the wave's LDS tile (lane: token lane/4, a quarter of the
 // channels) and the weighted V rows (16 head rows x D channels over the 16
-// tokens) are fp32 matrix-core products (v_mfma_f32_16x16x4_f32: lane 16*j + n
-// supplies row n of A and column n of B at k = j, and holds rows 4j..4j+3 of
-// column n of the result); the softmax runs down each head column.  Head
-// columns beyond the group are zero.  The next sub-tile's rows are fetched
-// while the current one is processed.
+// tokens) are fp32 matrix products (v_mfma_f32_16x16x4_f32).  The softmax runs
+// down each head column; head columns beyond the group are zero.  The next
+// sub-tile's operands are fetched while the current one is processed.
 // With positions (not null) the workgroup whose run holds a sequence's new
 // token appends it first (k_new, v_new fp16 [B][Hkv][D]; the cache is written
 // through the same pointer it is read through, hence no __restrict__ on it).
 template <int D>
-__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3)))
+__global__ void __launch_bounds__(64)
     k_strided_attn(dkv_config cfg, const uint8_t *cache, const float *__restrict__ q,
                    const int32_t *__restrict__ lens, float scale_log2, float *__restrict__ ws, int nsplit, int chunk,
                    const uint16_t *__restrict__ knew, const uint16_t *__restrict__ vnew,
                    const int32_t *__restrict__ positions, int window)
 {
-    constexpr int KS = D + 4, VS = D + 16;       // LDS row strides: conflict-free operand reads
-    constexpr int NKK = D / 4;                   // k-steps of the logits
+    constexpr int VS = D + 16;                   // LDS row stride: conflict-free operand reads
     constexpr int NCB = D / 16;                  // 16-channel column blocks of the weighted V rows
-    // K and V of a sub-tile take turns in one LDS tile (V is rebuilt after the logits)
     const StridedLayout ly = strided_layout(cfg);
     const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
     const int jj = lane >> 4, nn = lane & 15;
@@ -327,21 +372,42 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3)))
     const int t_begin = split * chunk * 32, t_end = min(L, t_begin + chunk * 32);
     const int64_t row0 = (int64_t)b * Hq + (int64_t)h * G;
 
-    __shared__ __attribute__((aligned(16))) float tile[16 * VS];
-    float *const kt = tile;
-    float *const vt = tile;
+    __shared__ __attribute__((aligned(16))) float vt[16 * VS];
     __shared__ float pl[kStridedMaxG][17];
     __shared__ float al[kStridedMaxG];
+    __shared__ __attribute__((aligned(16))) float scl[16][4];   // the sub-tile's block scales [token][block]
 
-    // query operand: head nn, channels 4*kk + jj (zero beyond the group)
-    float qb[NKK];
+    // query operand: head nn, channels 32b + 8jj + e, scaled by 2^-E (E from
+    // the largest |q| of the kv-head's group) and split into hi + lo fp16
+    constexpr int NB = D / 32;
+    h8 qh[NB], ql[NB];
+    float unq;
     {
-        const float *qr = q + (row0 + min(nn, G - 1)) * D + jj;
+        const float *qr = q + (row0 + min(nn, G - 1)) * D + 8 * jj;
+        float qv[NB][8], qm = 0.0f;
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-            const float x = qr[4 * kk] * scale_log2;
-            qb[kk] = nn < G ? x : 0.0f;
-        }
+        for (int bb = 0; bb < NB; ++bb)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float x = qr[32 * bb + e] * scale_log2;
+                qv[bb][e] = nn < G ? x : 0.0f;
+                qm = fmaxf(qm, fabsf(qv[bb][e]));
+            }
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) qm = fmaxf(qm, __shfl_xor(qm, off));
+        int E = 0;
+        if (qm > 0.0f) frexpf(qm, &E);
+        const float qsc = ldexpf(1.0f, -E);
+        unq = ldexpf(1.0f, E);
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float y = qv[bb][e] * qsc;
+                const _Float16 hi = (_Float16)y;
+                qh[bb][e] = hi;
+                ql[bb][e] = (_Float16)(y - (float)hi);
+            }
     }
     const uint8_t *kb = cache + (((int64_t)b * cfg.n_kv_heads + h) * 2) * ly.stream_bytes;
     const uint8_t *vb = kb + ly.stream_bytes;
@@ -351,35 +417,43 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3)))
     for (int u = 0; u < NCB; ++u) acc[u] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 
     const int r = lane >> 2, c0 = (lane & 3) * (D / 4);
-    RowQ<D> nk, nv;
-    if (t_begin + r < t_end) {
-        strided_fetch_q<D>(kb, ly, t_begin + r, c0, nk);
-        strided_fetch_q<D>(vb, ly, t_begin + r, c0, nv);
-    }
+    const int csh = 4 * (jj >> 1);               // nibble plane of this lane's k-range
+    KOps<D> ck;                                  // K operands of token t0 + nn
+    RowQ<D> nv;                                  // V raw data of token t0 + r
+    if (t_begin + nn < t_end) strided_fetch_k<D>(kb, ly, t_begin + nn, jj, ck);
+    if (t_begin + r < t_end) strided_fetch_q<D>(vb, ly, t_begin + r, c0, nv);
     for (int t0 = t_begin; t0 < t_end; t0 += 16) {
         const int nt = min(16, t_end - t0);
         if (r < nt) {
-            strided_rebuild_q<D>(nk, c0, kt + r * KS + c0);
+            strided_rebuild_q<D>(nv, c0, vt + r * VS + c0);
         } else {
 #pragma unroll
-            for (int i = 0; i < D / 4; i += 4) *(f4 *)&kt[r * KS + c0 + i] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+            for (int i = 0; i < D / 4; i += 4) *(f4 *)&vt[r * VS + c0 + i] = f4{0.0f, 0.0f, 0.0f, 0.0f};
         }
-        if (t0 + 16 + r < t_end) strided_fetch_q<D>(kb, ly, t0 + 16 + r, c0, nk);
-        __syncthreads();
-        // logits of tokens 4*jj + i for head nn, in two chains
-        f4 C0 = f4{0.0f, 0.0f, 0.0f, 0.0f}, C1 = C0;
-        {
-            const float *ka = kt + nn * KS + jj;
+        if (jj < NB) scl[nn][jj] = nn < nt ? h2f((uint16_t)ck.sc) : 0.0f;
+        // residual-domain logits of row token nn: reference part and per-block code parts
+        f4 Cr = f4{0.0f, 0.0f, 0.0f, 0.0f};
+        f4 Rb[NB];
 #pragma unroll
-            for (int kk = 0; kk < NKK; kk += 2) {
-                C0 = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[4 * kk], qb[kk], C0, 0, 0, 0);
-                C1 = __builtin_amdgcn_mfma_f32_16x16x4f32(ka[4 * kk + 4], qb[kk + 1], C1, 0, 0, 0);
-            }
+        for (int bb = 0; bb < NB; ++bb) {
+            const h8 ar = __builtin_bit_cast(h8, ck.ref[bb]);
+            Cr = mfma(ar, qh[bb], Cr);
+            Cr = mfma(ar, ql[bb], Cr);
+            const h8 ac = codes_f16(ck.code[bb], csh);
+            Rb[bb] = mfma(ac, qh[bb], f4{0.0f, 0.0f, 0.0f, 0.0f});
+            Rb[bb] = mfma(ac, ql[bb], Rb[bb]);
         }
+        if (t0 + 16 + nn < t_end) strided_fetch_k<D>(kb, ly, t0 + 16 + nn, jj, ck);
+        if (t0 + 16 + r < t_end) strided_fetch_q<D>(vb, ly, t0 + 16 + r, c0, nv);
+        __syncthreads();
         float x[4], mx = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            x[i] = 4 * jj + i < nt ? C0[i] + C1[i] : -INFINITY;
+            const int t = 4 * jj + i;
+            float lg = Cr[i];
+#pragma unroll
+            for (int bb = 0; bb < NB; ++bb) lg = __builtin_fmaf(scl[t][bb], Rb[bb][i], lg);
+            x[i] = t < nt ? lg * unq : -INFINITY;
             mx = fmaxf(mx, x[i]);
         }
         mx = rows_max(mx);
@@ -395,14 +469,6 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3)))
         l_run = l_run * alpha + rows_sum(ps);
         m_run = m_new;
         if (jj == 0) al[nn] = alpha;
-        __syncthreads();                         // the logits have read the K tile
-        if (r < nt) {
-            strided_rebuild_q<D>(nv, c0, vt + r * VS + c0);
-        } else {
-#pragma unroll
-            for (int i = 0; i < D / 4; i += 4) *(f4 *)&vt[r * VS + c0 + i] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-        }
-        if (t0 + 16 + r < t_end) strided_fetch_q<D>(vb, ly, t0 + 16 + r, c0, nv);
         __syncthreads();
         // weighted V rows: heads 4*jj + i, channels 16*cb + nn
         float alr[4];
