@@ -229,3 +229,32 @@ def test_strided_fused_step_matches_append_then_decode(kw, stride, window):
         torch.cuda.synchronize()
         assert torch.equal(a, bcache), f"cache differs after step {step}"
         assert torch.equal(oa, ob), f"output differs after step {step}"
+
+
+@pytest.mark.parametrize("qscale", [1e3, 1e-3])
+def test_strided_query_scale(qscale):
+    """Queries far from unit size (a very peaked or a nearly flat softmax): the
+    logits' fp16 query operands are scaled by 2^-E first, so attention stays
+    within 2e-3 of the oracle."""
+    w = synth.make("8b", S=500, Hq=8, Hkv=2)
+    print(f"strided query scale {qscale}", flush=True)
+    cfg = _cfg(w, 32)
+    lens_np = np.asarray(w.seq_lens, np.int32)
+    cache = torch.zeros(dkv.dkv_strided_cache_bytes(cfg), dtype=torch.uint8, device=U.DEV)
+    lens = torch.from_numpy(lens_np).to(U.DEV)
+    dkv.dkv_strided_encode_prefill(cfg, cache, torch.from_numpy(w.k).to(U.DEV), torch.from_numpy(w.v).to(U.DEV),
+                                   lens, w.k.shape[2], 0)
+    q_np = (synth.queries(w) * np.float32(qscale)).astype(np.float32)
+    out = torch.zeros(w.B, w.Hq, w.D, dtype=torch.float32, device=U.DEV)
+    ws = torch.zeros(dkv.dkv_workspace_bytes(cfg), dtype=torch.uint8, device=U.DEV)
+    dkv.dkv_strided_attn_decode(cfg, cache, torch.from_numpy(q_np).to(U.DEV), lens, out, ws)
+    torch.cuda.synchronize()
+    G = w.Hq // w.Hkv
+    ref = np.zeros((w.B, w.Hq, w.D))
+    for b in range(w.B):
+        L = int(lens_np[b])
+        for h in range(w.Hkv):
+            rec = [oracle.strided_encode_stream(np.ascontiguousarray(x[b, h, :L]), 32, 0).recon for x in (w.k, w.v)]
+            ref[b, h * G:(h + 1) * G] = oracle.attention_f64(q_np[b, h * G:(h + 1) * G], rec[0], rec[1],
+                                                             np.float32(1 / math.sqrt(w.D)))
+    assert U.rel_err(out.cpu().numpy(), ref) <= U.ATTN_TOL
