@@ -174,6 +174,24 @@ def test_softmax_scale_argument():
     assert U.rel_err(out.cpu().numpy(), ref) <= U.ATTN_TOL
 
 
+@pytest.mark.parametrize("qscale", [1e3, 1e-3])
+@pytest.mark.parametrize("name,kw,kf", [("8b", dict(S=600, Hq=8, Hkv=2), 32),
+                                        ("70b", dict(S=600, B=2, Hq=16, Hkv=2), 32),
+                                        ("long", dict(S=1100, B=2, Hq=8, Hkv=2, kf=512), 512)])
+def test_query_scale(name, kw, kf, qscale):
+    """Queries far from unit size (a very peaked or a nearly flat softmax):
+    the matrix-core kernels scale the query operands by 2^-E before the fp16
+    split, so attention stays within 2e-3 of the oracle."""
+    w = _case(name, **kw)
+    print(f"query scale {name} {kw} kf={kf} x{qscale}", flush=True)
+    r = U.prefill(w, kf=kf)
+    enc = U.oracle_encode(w, kf, r.lens_np)
+    q = (synth.queries(w) * np.float32(qscale)).astype(np.float32)
+    got = U.attention(r, q)
+    ref = U.oracle_attention(enc, w, q, r.lens_np)
+    assert U.rel_err(got, ref) <= U.ATTN_TOL
+
+
 # Runs of several whole groups per workgroup: 32 sequences x 8 kv-heads make
 # the split plan cut each sequence into 8 runs (8 groups at kf = 32, 2 at
 # kf = 128), and the lengths put every count of whole groups in a run, with
