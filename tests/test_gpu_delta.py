@@ -192,6 +192,28 @@ def test_query_scale(name, kw, kf, qscale):
     assert U.rel_err(got, ref) <= U.ATTN_TOL
 
 
+@pytest.mark.parametrize("vscale", [100.0, 0.01])
+@pytest.mark.parametrize("name,kw,kf", [("8b", dict(S=600, Hq=8, Hkv=2), 32),
+                                        ("long", dict(S=1100, B=2, Hq=8, Hkv=2, kf=128), 128)])
+def test_value_scale(name, kw, kf, vscale):
+    """K and V far from unit size (the 8b data's lognormal channels times 100
+    reach about 2,000): the codec stays bit-exact with the oracle, and the V
+    weights' range bias (from the group's largest scale) keeps attention
+    within 2e-3."""
+    w = _case(name, **kw)
+    print(f"value scale {name} {kw} kf={kf} x{vscale}", flush=True)
+    w.k = (w.k.astype(np.float32) * np.float32(vscale)).astype(np.float16)
+    w.v = (w.v.astype(np.float32) * np.float32(vscale)).astype(np.float16)
+    assert np.isfinite(w.k.astype(np.float32)).all() and np.isfinite(w.v.astype(np.float32)).all()
+    r = U.prefill(w, kf=kf)
+    enc = U.oracle_encode(w, kf, r.lens_np)
+    U.assert_codec_exact(r, enc, kf)
+    q = synth.queries(w) / np.float32(vscale)
+    got = U.attention(r, q)
+    ref = U.oracle_attention(enc, w, q, r.lens_np)
+    assert U.rel_err(got, ref) <= U.ATTN_TOL
+
+
 # Runs of several whole groups per workgroup: 32 sequences x 8 kv-heads make
 # the split plan cut each sequence into 8 runs (8 groups at kf = 32, 2 at
 # kf = 128), and the lengths put every count of whole groups in a run, with
