@@ -371,8 +371,10 @@ dkv_status dkv_strided_append_attn_decode(const dkv_config *cfg, void *cache, co
  * Decode attention over the strided-reference cache: out[b][hq] =
  * softmax(scale * q . K_hat^T) V_hat over tokens t < min(seq_lens[b], capacity),
  * arguments as dkv_attn_decode (workspace of dkv_workspace_bytes(cfg) bytes).
- * Two launches on `stream`: the split phase (32-token tiles rebuilt in fp32),
- * then the split combine.  A sequence of length 0 gives zero rows.
+ * Two launches on `stream`: the split phase (one wave per run of 32-token
+ * tiles; logits in the residual domain, q.r_idx + sum_b s_b q_b.(c_b - 8), on
+ * fp16 matrix instructions; V rebuilt in fp32), then the split combine.  A
+ * sequence of length 0 gives zero rows.
  */
 dkv_status dkv_strided_attn_decode(const dkv_config *cfg, const void *cache, const float *q,
                                    const int32_t *seq_lens, float softmax_scale, float *out,
