@@ -305,7 +305,9 @@ dkv_status dkv_stream_read(const void *buf, size_t bytes, uint32_t *sink, size_t
  * decodes as reference + (code - 8) * scale.  Nearest: smallest squared
  * distance of the fp16 rows, summed in double over the channels in order
  * without fused multiply-add, lowest index on ties, among references
- * k <= t / kf (and k > t / kf - window when window > 0).  Contiguous mode only
+ * k <= t / kf (and k > t / kf - window when window > 0).  A NaN distance
+ * (non-finite rows, outside the finite-input contract) ranks above every
+ * number, so such a row still takes one of its candidates.  Contiguous mode only
  * (page_tokens must be 0), at most 65536 references per sequence; otherwise
  * DKV_ERR_UNSUPPORTED.
  *

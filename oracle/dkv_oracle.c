@@ -367,6 +367,18 @@ double oracle_sqdist_f16(const uint16_t *a, const uint16_t *b, int D)
     return s;
 }
 
+/* Order of two distances for the nearest-reference choice: the usual order of
+ * numbers (+infinity included), with a NaN distance (a NaN in either row, or
+ * infinities of one sign in the same channel of both) ranked above every
+ * number and equal to another NaN.  Inputs are meant to be finite; this only
+ * fixes which reference such a row takes. */
+static int oracle_dist_less(double a, double b)
+{
+    if (isnan(a)) return 0;
+    if (isnan(b)) return 1;
+    return a < b;
+}
+
 void oracle_strided_encode_stream(const uint16_t *x, long S, int D, int stride, int window,
                                   uint16_t *refs, int32_t *ref_idx, uint8_t *codes, uint16_t *scales,
                                   float *recon)
@@ -382,7 +394,7 @@ void oracle_strided_encode_stream(const uint16_t *x, long S, int D, int stride, 
         double bd = oracle_sqdist_f16(xt, refs + k0 * (long)D, D);
         for (long k = k0 + 1; k <= kt; ++k) {
             double d = oracle_sqdist_f16(xt, refs + k * (long)D, D);
-            if (d < bd) {
+            if (oracle_dist_less(d, bd)) {
                 bd = d;
                 best = k;
             }

@@ -81,6 +81,25 @@ __device__ inline double sqdist_rows(const uint16_t *__restrict__ a, const uint1
     return s;
 }
 
+// Ordering key of a distance for the nearest-reference choice: distances are
+// +0 or positive, so their bit patterns order like the numbers (+infinity
+// included); a NaN distance (a NaN in either row, or infinities of one sign
+// in the same channel of both) is ranked above every number.  The nearest
+// reference is the smallest (key, index) pair, so a row holding a NaN takes
+// the first candidate.
+__device__ inline uint64_t dist_key(double d)
+{
+    return d != d ? 0x7FF8000000000000ull : (uint64_t)__builtin_bit_cast(int64_t, d);
+}
+// (key, index) lexicographic minimum of two candidates, kept in (bd, bk).
+__device__ inline void keep_nearer(uint64_t &bd, int &bk, uint64_t d2, int k2)
+{
+    if (d2 < bd || (d2 == bd && k2 < bk)) {
+        bd = d2;
+        bk = k2;
+    }
+}
+
 // grid (ceil(s_max / 32), n_kv_heads * 2, batch): one 32-token tile of one stream.
 template <int D>
 __global__ void __launch_bounds__(kStridedThreads)
@@ -112,28 +131,23 @@ __global__ void __launch_bounds__(kStridedThreads)
     __shared__ int sidx[32];
     {
         const int tt = tid >> 3, sl = tid & 7, t = t0 + tt;
-        double bd = INFINITY;
+        // a lane without candidates keeps the largest key and loses to every
+        // real candidate; every token has at least one (k0 <= t / stride)
+        uint64_t bd = ~0ull;
         int bk = 0x7FFFFFFF;
+        const int kt = t / stride;
         if (t < L) {
-            const int kt = t / stride;
             const int k0 = (window > 0 && kt - window + 1 > 0) ? kt - window + 1 : 0;
-            for (int kk = k0 + sl; kk <= kt; kk += 8) {
-                const double d = sqdist_rows<D>(x + (int64_t)t * D, x + (int64_t)kk * stride * D);
-                if (d < bd) {
-                    bd = d;
-                    bk = kk;
-                }
-            }
+            for (int kk = k0 + sl; kk <= kt; kk += 8)
+                keep_nearer(bd, bk, dist_key(sqdist_rows<D>(x + (int64_t)t * D, x + (int64_t)kk * stride * D)), kk);
         }
 #pragma unroll
         for (int off = 1; off < 8; off <<= 1) {
-            const double d2 = __shfl_xor(bd, off, 8);
+            const uint64_t d2 = __shfl_xor(bd, off, 8);
             const int k2 = __shfl_xor(bk, off, 8);
-            if (d2 < bd || (d2 == bd && k2 < bk)) {
-                bd = d2;
-                bk = k2;
-            }
+            keep_nearer(bd, bk, d2, k2);
         }
+        bk = min(bk, kt);
         if (sl == 0) {
             sidx[tt] = t < L ? bk : 0;
             if (t < L) idx[t] = (uint16_t)bk;
@@ -177,25 +191,19 @@ __device__ inline void strided_append_wave(const StridedLayout &ly, int stride, 
     const int kt = t / stride;
     const bool is_ref = t % stride == 0;
     const int k0 = (window > 0 && kt - window + 1 > 0) ? kt - window + 1 : 0;
-    double bd = INFINITY;
+    uint64_t bd = ~0ull;        // as in k_strided_encode: no candidate loses to any
     int bk = 0x7FFFFFFF;
     for (int kk = k0 + lane; kk <= kt; kk += 64) {
         const uint16_t *r = (is_ref && kk == kt) ? x : refs + (int64_t)kk * D;
-        const double d = sqdist_rows<D>(x, r);
-        if (d < bd) {
-            bd = d;
-            bk = kk;
-        }
+        keep_nearer(bd, bk, dist_key(sqdist_rows<D>(x, r)), kk);
     }
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
-        const double d2 = __shfl_xor(bd, off);
+        const uint64_t d2 = __shfl_xor(bd, off);
         const int k2 = __shfl_xor(bk, off);
-        if (d2 < bd || (d2 == bd && k2 < bk)) {
-            bd = d2;
-            bk = k2;
-        }
+        keep_nearer(bd, bk, d2, k2);
     }
+    bk = min(bk, kt);
     const uint16_t *r = (is_ref && bk == kt) ? x : refs + (int64_t)bk * D;
     if (lane == 0) ((uint16_t *)(base + ly.off_idx))[t] = (uint16_t)bk;
     const int ln = lane & 31;

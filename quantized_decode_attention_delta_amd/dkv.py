@@ -148,15 +148,20 @@ def _ptr(t, dtype=None, name="tensor", numel=None):
         return None
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be on the GPU")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
     if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if numel is not None and t.numel() < numel:
         raise ValueError(f"{name} has {t.numel()} elements, needs {numel}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
     return ctypes.c_void_p(t.data_ptr())
+
+
+def _bt_numel(cfg: Config) -> int:
+    """Entries of a block table [batch][max_pages_per_seq] (paged mode only)."""
+    return cfg.batch * cfg.max_pages_per_seq if cfg.page_tokens > 0 else 0
 
 
 def _stream(stream=None):
@@ -176,7 +181,8 @@ def dkv_encode_prefill(cfg: Config, cache, state, block_table, k, v, seq_lens, s
     B, H, D = cfg.batch, cfg.n_kv_heads, cfg.head_dim
     st = load().dkv_encode_prefill(
         ctypes.byref(cfg.c()), _ptr(cache, torch.uint8, "cache", dkv_cache_bytes(cfg)),
-        _ptr(state, torch.float32, "state", B * H * 2 * D), _ptr(block_table, torch.int32, "block_table"),
+        _ptr(state, torch.float32, "state", B * H * 2 * D),
+        _ptr(block_table, torch.int32, "block_table", _bt_numel(cfg)),
         _f16(k, "k", B * H * s_max * D), _f16(v, "v", B * H * s_max * D),
         _ptr(seq_lens, torch.int32, "seq_lens", B), int(s_max), _stream(stream))
     _check("dkv_encode_prefill", st)
@@ -187,7 +193,8 @@ def dkv_append(cfg: Config, cache, state, block_table, k_new, v_new, positions, 
     B, H, D = cfg.batch, cfg.n_kv_heads, cfg.head_dim
     st = load().dkv_append(
         ctypes.byref(cfg.c()), _ptr(cache, torch.uint8, "cache", dkv_cache_bytes(cfg)),
-        _ptr(state, torch.float32, "state", B * H * 2 * D), _ptr(block_table, torch.int32, "block_table"),
+        _ptr(state, torch.float32, "state", B * H * 2 * D),
+        _ptr(block_table, torch.int32, "block_table", _bt_numel(cfg)),
         _f16(k_new, "k_new", B * H * D), _f16(v_new, "v_new", B * H * D),
         _ptr(positions, torch.int32, "positions", B), _stream(stream))
     _check("dkv_append", st)
@@ -197,7 +204,8 @@ def _attn(fn, cfg, cache, block_table, q, seq_lens, out, workspace, softmax_scal
     import torch
     B, Hq, D = cfg.batch, cfg.n_q_heads, cfg.head_dim
     st = getattr(load(), fn)(
-        ctypes.byref(cfg.c()), _ptr(cache, torch.uint8, "cache"), _ptr(block_table, torch.int32, "block_table"),
+        ctypes.byref(cfg.c()), _ptr(cache, torch.uint8, "cache", dkv_cache_bytes(cfg)),
+        _ptr(block_table, torch.int32, "block_table", _bt_numel(cfg)),
         _ptr(q, torch.float32, "q", B * Hq * D), _ptr(seq_lens, torch.int32, "seq_lens", B),
         float(softmax_scale), _ptr(out, torch.float32, "out", B * Hq * D),
         _ptr(workspace, torch.uint8, "workspace"), workspace.numel() if workspace is not None else 0,
@@ -217,7 +225,8 @@ def dkv_append_attn_decode(cfg: Config, cache, state, block_table, k_new, v_new,
     B, H, Hq, D = cfg.batch, cfg.n_kv_heads, cfg.n_q_heads, cfg.head_dim
     st = load().dkv_append_attn_decode(
         ctypes.byref(cfg.c()), _ptr(cache, torch.uint8, "cache", dkv_cache_bytes(cfg)),
-        _ptr(state, torch.float32, "state", B * H * 2 * D), _ptr(block_table, torch.int32, "block_table"),
+        _ptr(state, torch.float32, "state", B * H * 2 * D),
+        _ptr(block_table, torch.int32, "block_table", _bt_numel(cfg)),
         _f16(k_new, "k_new", B * H * D), _f16(v_new, "v_new", B * H * D),
         _ptr(positions, torch.int32, "positions", B), _ptr(q, torch.float32, "q", B * Hq * D),
         _ptr(seq_lens, torch.int32, "seq_lens", B), float(softmax_scale), _ptr(out, torch.float32, "out", B * Hq * D),
@@ -236,7 +245,8 @@ def dkv_attn_decode_partial(cfg: Config, cache, block_table, q, seq_lens, worksp
     import torch
     B, Hq, D = cfg.batch, cfg.n_q_heads, cfg.head_dim
     st = load().dkv_attn_decode_partial(
-        ctypes.byref(cfg.c()), _ptr(cache, torch.uint8, "cache"), _ptr(block_table, torch.int32, "block_table"),
+        ctypes.byref(cfg.c()), _ptr(cache, torch.uint8, "cache", dkv_cache_bytes(cfg)),
+        _ptr(block_table, torch.int32, "block_table", _bt_numel(cfg)),
         _ptr(q, torch.float32, "q", B * Hq * D), _ptr(seq_lens, torch.int32, "seq_lens", B),
         float(softmax_scale), _ptr(workspace, torch.uint8, "workspace"),
         workspace.numel() if workspace is not None else 0, _stream(stream))
@@ -247,7 +257,8 @@ def dkv_reconstruct(cfg: Config, cache, block_table, seq_lens, s_max: int, k_out
     import torch
     n = cfg.batch * cfg.n_kv_heads * s_max * cfg.head_dim
     st = load().dkv_reconstruct(
-        ctypes.byref(cfg.c()), _ptr(cache, torch.uint8, "cache"), _ptr(block_table, torch.int32, "block_table"),
+        ctypes.byref(cfg.c()), _ptr(cache, torch.uint8, "cache", dkv_cache_bytes(cfg)),
+        _ptr(block_table, torch.int32, "block_table", _bt_numel(cfg)),
         _ptr(seq_lens, torch.int32, "seq_lens", cfg.batch), int(s_max),
         _ptr(k_out, torch.float32, "k_out", n), _ptr(v_out, torch.float32, "v_out", n), _stream(stream))
     _check("dkv_reconstruct", st)
@@ -292,7 +303,8 @@ def dkv_export(cfg: Config, cache, block_table, seq_lens, s_max: int, kf_rows, c
     import torch
     skf, scd, ssc = export_shapes(cfg, s_max)
     st = load().dkv_export(
-        ctypes.byref(cfg.c()), _ptr(cache, torch.uint8, "cache"), _ptr(block_table, torch.int32, "block_table"),
+        ctypes.byref(cfg.c()), _ptr(cache, torch.uint8, "cache", dkv_cache_bytes(cfg)),
+        _ptr(block_table, torch.int32, "block_table", _bt_numel(cfg)),
         _ptr(seq_lens, torch.int32, "seq_lens", cfg.batch), int(s_max),
         _f16(kf_rows, "kf_rows", math.prod(skf)), _ptr(codes, torch.uint8, "codes", math.prod(scd)),
         _f16(scales, "scales", math.prod(ssc)), _stream(stream))
@@ -313,7 +325,7 @@ def dkv_q4_0_export(cfg: Config, q4_cache, seq_lens, s_max: int, codes, scales, 
     import torch
     B, H, D = cfg.batch, cfg.n_kv_heads, cfg.head_dim
     st = load().dkv_q4_0_export(
-        ctypes.byref(cfg.c()), _ptr(q4_cache, torch.uint8, "q4_cache"),
+        ctypes.byref(cfg.c()), _ptr(q4_cache, torch.uint8, "q4_cache", dkv_q4_0_cache_bytes(cfg)),
         _ptr(seq_lens, torch.int32, "seq_lens", B), int(s_max),
         _ptr(codes, torch.uint8, "codes", B * H * 2 * s_max * D // 2),
         _f16(scales, "scales", B * H * 2 * s_max * D // 32), _stream(stream))
@@ -324,7 +336,7 @@ def dkv_attn_decode_q4_0(cfg: Config, q4_cache, q, seq_lens, out, workspace, sof
     import torch
     B, Hq, D = cfg.batch, cfg.n_q_heads, cfg.head_dim
     st = load().dkv_attn_decode_q4_0(
-        ctypes.byref(cfg.c()), _ptr(q4_cache, torch.uint8, "q4_cache"), _ptr(q, torch.float32, "q", B * Hq * D),
+        ctypes.byref(cfg.c()), _ptr(q4_cache, torch.uint8, "q4_cache", dkv_q4_0_cache_bytes(cfg)), _ptr(q, torch.float32, "q", B * Hq * D),
         _ptr(seq_lens, torch.int32, "seq_lens", B), float(softmax_scale),
         _ptr(out, torch.float32, "out", B * Hq * D), _ptr(workspace, torch.uint8, "workspace"),
         workspace.numel() if workspace is not None else 0, _stream(stream))

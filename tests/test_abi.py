@@ -141,3 +141,28 @@ def test_binding_refuses_cpu_tensors():
     t = torch.zeros(10)
     with pytest.raises((ValueError, TypeError)):
         dkv.dkv_encode_prefill(c, t, t, None, t, t, t, 10)
+
+
+def test_binding_rejects_undersized_caches():
+    """Every call that reads or writes a cache checks its size against the
+    library's size query before anything else reaches the C ABI (a short
+    buffer would otherwise be read or written past its end on the GPU)."""
+    import torch
+    _lib()
+    c = _cfg()
+    short = torch.zeros(dkv.dkv_cache_bytes(c) - 1, dtype=torch.uint8)
+    q = torch.zeros(c.batch * c.n_q_heads * c.head_dim)
+    lens = torch.zeros(c.batch, dtype=torch.int32)
+    ws = torch.zeros(dkv.dkv_workspace_bytes(c), dtype=torch.uint8)
+    calls = [
+        lambda: dkv.dkv_attn_decode(c, short, None, q, lens, q, ws),
+        lambda: dkv.dkv_attn_decode_ref(c, short, None, q, lens, q, ws),
+        lambda: dkv.dkv_attn_decode_partial(c, short, None, q, lens, ws),
+        lambda: dkv.dkv_reconstruct(c, short, None, lens, 4, q, q),
+        lambda: dkv.dkv_export(c, short, None, lens, 4, q, q, q),
+        lambda: dkv.dkv_q4_0_export(c, torch.zeros(dkv.dkv_q4_0_cache_bytes(c) - 1, dtype=torch.uint8), lens, 4,
+                                    short, short),
+    ]
+    for i, f in enumerate(calls):
+        with pytest.raises(ValueError, match="elements, needs"):
+            f()

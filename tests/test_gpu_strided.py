@@ -258,3 +258,41 @@ def test_strided_query_scale(qscale):
             ref[b, h * G:(h + 1) * G] = oracle.attention_f64(q_np[b, h * G:(h + 1) * G], rec[0], rec[1],
                                                              np.float32(1 / math.sqrt(w.D)))
     assert U.rel_err(out.cpu().numpy(), ref) <= U.ATTN_TOL
+
+
+@pytest.mark.parametrize("window", [0, 2, 3])
+def test_strided_nonfinite_rows_take_the_oracle_reference(window):
+    """Rows holding NaN or infinities (outside the finite-input contract) take
+    the reference the oracle's order gives them (a NaN distance ranks above
+    every number, lowest index among equals), in the prefill and in the
+    append; tokens whose row and reference are finite keep bit-exact codes."""
+    D, S, stride = 64, 10, 2
+    x = np.zeros((S, D), np.float16)
+    x[:, 0] = np.arange(S, dtype=np.float16)
+    x[:, 5] = np.linspace(-1, 1, S).astype(np.float16)
+    x[3, 7] = np.float16("nan")
+    x[4, 3] = np.float16("nan")
+    x[5, 2] = np.float16("inf")
+    x[6, 1] = -np.float16("inf")
+    cfg = dkv.Config(batch=1, n_q_heads=1, n_kv_heads=1, head_dim=D, kf=stride, max_tokens=S)
+    lay = dkv.dkv_strided_layout(cfg)
+    kx = torch.from_numpy(x[None, None].copy()).to(U.DEV)
+    lens = torch.full((1,), S, dtype=torch.int32, device=U.DEV)
+    pre = torch.zeros(dkv.dkv_strided_cache_bytes(cfg), dtype=torch.uint8, device=U.DEV)
+    dkv.dkv_strided_encode_prefill(cfg, pre, kx, kx, lens, S, window)
+    app = torch.zeros_like(pre)
+    for t in range(S):
+        row = kx[:, :, t].contiguous()
+        dkv.dkv_strided_append(cfg, app, row, row, torch.full((1,), t, dtype=torch.int32, device=U.DEV), window)
+    torch.cuda.synchronize()
+    e = oracle.strided_encode_stream(x, stride, window)
+    finite = np.isfinite(x.astype(np.float32)).all(axis=1)
+    for name, c in (("prefill", pre), ("append", app)):
+        st = c.cpu().numpy()[:lay["stream_bytes"]]
+        idx = st[lay["idx"]:lay["idx"] + 2 * S].view(np.uint16).astype(np.int32)
+        assert np.array_equal(idx, e.ref_idx), (name, idx, e.ref_idx)
+        codes = st[lay["codes"]:lay["codes"] + S * D // 2].reshape(S, D // 2)
+        scales = st[lay["scales"]:lay["scales"] + S * D // 16].view(np.uint16).reshape(S, D // 32)
+        for t in range(S):
+            if finite[t] and finite[e.ref_idx[t] * stride]:
+                assert np.array_equal(codes[t], e.codes[t]) and np.array_equal(scales[t], e.scales[t]), (name, t)

@@ -474,3 +474,104 @@ def test_q80_stream_matches_blocks():
     deq = oracle.q80_dequant_stream(codes, scales)
     sc = np.repeat(scales.view(np.float16).astype(np.float32), 32, axis=1)
     assert np.array_equal(deq, codes.astype(np.float32) * sc)
+
+
+# ------------------------------------------------ dequantisers, pinned by hand
+# The dequantised value of a Q4_0 code c under stored scale s16 is
+# (c - 8) * float(s16); of a Q8_0 code c it is c * float(s16).  The blocks
+# below are fed to the oracle's stream dequantisers as raw bytes and fp16
+# scale bits, and every output is compared with a value written out by hand.
+
+def test_q40_dequant_stream_golden_blocks():
+    """Every hand-worked block of tests/golden/q40_hand_blocks.txt, as packed
+    bytes + scale bits, dequantises to its golden values.  Blocks are laid two
+    per row (D = 64) in a 3-row stream, so a wrong block or row index, a
+    missing scale or a wrong code offset changes some value."""
+    cases = _golden_blocks()
+    assert len(cases) == 6
+    codes = np.full((3, 32), 0x88, np.uint8)
+    scales = np.zeros((3, 2), np.uint16)
+    want = np.zeros((3, 64), np.float32)
+    for i, (name, ins, scale, code_over, byte_over, deq_over) in enumerate(cases):
+        t, b = divmod(i, 2)
+        for j, by in byte_over.items():
+            codes[t, 16 * b + j] = by
+        scales[t, b] = scale
+        for j, d in deq_over.items():
+            want[t, 32 * b + j] = d
+    got = oracle.q40_dequant_stream(codes, scales)
+    assert got.dtype == np.float32 and got.shape == (3, 64)
+    assert np.array_equal(got, want), np.argwhere(got != want)
+
+
+def test_q40_dequant_stream_every_code_literal():
+    """All 16 codes under a negative and a positive scale, written out: block 0
+    has byte i = i | (15 - i) << 4 (low nibbles code i, high nibbles code
+    15 - i) with scale -2.0 (0xC000); block 1 repeats the bytes with scale
+    0.25 (0x3400)."""
+    row = np.array([i | ((15 - i) << 4) for i in range(16)], np.uint8)
+    codes = np.concatenate([row, row])[None, :]
+    scales = np.array([[0xC000, 0x3400]], np.uint16)
+    want_b0 = [16, 14, 12, 10, 8, 6, 4, 2, 0, -2, -4, -6, -8, -10, -12, -14,
+               -14, -12, -10, -8, -6, -4, -2, 0, 2, 4, 6, 8, 10, 12, 14, 16]
+    want_b1 = [-2.0, -1.75, -1.5, -1.25, -1.0, -0.75, -0.5, -0.25, 0.0, 0.25, 0.5, 0.75, 1.0, 1.25, 1.5, 1.75,
+               1.75, 1.5, 1.25, 1.0, 0.75, 0.5, 0.25, 0.0, -0.25, -0.5, -0.75, -1.0, -1.25, -1.5, -1.75, -2.0]
+    got = oracle.q40_dequant_stream(codes, scales)
+    assert np.array_equal(got[0], np.array(want_b0 + want_b1, np.float32))
+
+
+def test_q80_dequant_stream_literal():
+    """Q8_0 codes times their fp16 scale, written out: block 0 under 1.0
+    (0x3C00), block 1 under 0x2008 = 129/16384 (127 * 129/16384 = 16383/16384),
+    row 1 under -2.0 (0xC000) and +0 (0x0000)."""
+    codes = np.zeros((2, 64), np.int8)
+    codes[0, :7] = [127, 3, -3, 1, -1, 0, -127]
+    codes[0, 32:35] = [127, -127, 2]
+    codes[1, :3] = [-5, 100, -128]
+    codes[1, 32:34] = [50, -50]
+    scales = np.array([[0x3C00, 0x2008], [0xC000, 0x0000]], np.uint16)
+    want = np.zeros((2, 64), np.float64)
+    want[0, :7] = [127.0, 3.0, -3.0, 1.0, -1.0, 0.0, -127.0]
+    want[0, 32:35] = [16383 / 16384, -16383 / 16384, 258 / 16384]
+    want[1, :3] = [10.0, -200.0, 256.0]
+    got = oracle.q80_dequant_stream(codes, scales)
+    assert np.array_equal(got.astype(np.float64), want), np.argwhere(got != want)
+
+
+def _gqa_workload(G, seed):
+    """B = 2 sequences, Hkv = 3 kv-heads whose K/V differ by head (offsets of
+    +4 * head), G query heads per kv-head."""
+    rng = np.random.default_rng(seed)
+    B, H, S, D = 2, 3, 40, 64
+    base = rng.standard_normal((B, H, S, D))
+    k = (base + 4.0 * np.arange(H)[None, :, None, None]).astype(np.float16)
+    v = (rng.standard_normal((B, H, S, D)) - 3.0 * np.arange(H)[None, :, None, None]).astype(np.float16)
+    q = rng.standard_normal((B, H * G, D)).astype(np.float32)
+    lens = np.array([S, 23], np.int32)
+    return k, v, q, lens, H
+
+
+@pytest.mark.parametrize("G", [1, 4, 8])
+def test_cache_helpers_map_query_head_to_kv_head(G):
+    """Query head hq of a group of G reads kv-head hq // G: the cache-level
+    helpers (attention_cache, attention_distortion_cache) equal the per-head
+    float64 routines called on that kv-head's rows, for every (sequence,
+    query head); a mapping such as hq % Hkv would pick another head's K/V."""
+    k, v, q, lens, H = _gqa_workload(G, 40 + G)
+    enc = oracle.encode_cache(k, v, lens, 8)
+    scale = np.float32(0.125)
+    att = oracle.attention_cache(enc, q, lens, H, scale)
+    dk, dv = oracle.attention_distortion_cache(enc, k, v, q, lens, H, scale)
+    for b in range(2):
+        S = int(lens[b])
+        for hq in range(H * G):
+            kv = hq // G
+            kr = oracle.reconstruct_stream(enc[(b, kv, 0)].kf_rows, enc[(b, kv, 0)].codes, enc[(b, kv, 0)].scales,
+                                           S, 64, 8)
+            vr = oracle.reconstruct_stream(enc[(b, kv, 1)].kf_rows, enc[(b, kv, 1)].codes, enc[(b, kv, 1)].scales,
+                                           S, 64, 8)
+            ref = _sdpa_f64(q[b, hq:hq + 1], kr, vr, scale)
+            np.testing.assert_allclose(att[b, hq], ref[0], rtol=1e-12, atol=1e-12)
+            e_k, e_v = oracle.attention_distortion_f64(q[b, hq:hq + 1], k[b, kv, :S].astype(np.float64),
+                                                       v[b, kv, :S].astype(np.float64), kr, vr, scale)
+            np.testing.assert_allclose([dk[b, hq], dv[b, hq]], [e_k[0], e_v[0]], rtol=1e-12, atol=0)

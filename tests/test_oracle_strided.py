@@ -115,3 +115,33 @@ def test_sqdist_closed_form():
     a = np.array([1.0, -2.0, 0.5, 0.0], np.float16)
     b = np.array([0.0, 1.0, 0.5, -3.0], np.float16)
     assert oracle.sqdist_f16(a, b) == 1.0 + 9.0 + 0.0 + 9.0
+
+
+def test_rows_with_inf_or_nan_take_a_defined_reference():
+    """Non-finite rows (outside the cache's finite-input contract) still pick
+    one defined reference: a NaN distance ranks above every number, +inf
+    included, and the lowest index wins among equals.  Stride 2, D = 32:
+      t = 3 holds a NaN: every distance is NaN, so reference 0;
+      t = 5 holds +inf: every distance is +inf (references finite), so 0;
+      t = 6 is reference 3 itself, whose row holds -inf in channel 1: its
+        distance to itself is NaN (-inf - -inf), to references 0..2 +inf, so
+        reference 0;
+      t = 9 (window 2: references 3 and 4) is finite: reference 3 (the -inf
+        row) is at distance +inf, so reference 4 is chosen."""
+    D = 32
+    x = np.zeros((10, D), np.float16)
+    x[:, 0] = np.arange(10, dtype=np.float16)
+    x[3, 7] = np.float16("nan")
+    x[5, 2] = np.float16("inf")
+    x[6, 1] = -np.float16("inf")
+    got = oracle.strided_encode_stream(x, 2, window=0).ref_idx
+    assert got[3] == 0 and got[5] == 0 and got[6] == 0
+    got_w = oracle.strided_encode_stream(x, 2, window=2).ref_idx
+    assert got_w[9] == 4
+    # a NaN distance must not stick as the running best: t = 9 with window 3
+    # sees references 2, 3, 4 in that order; 2 and 4 are finite, 4 is nearer
+    x2 = x.copy()
+    x2[4, 3] = np.float16("nan")       # reference 2 (t = 4) now at NaN distance
+    assert oracle.strided_encode_stream(x2, 2, window=3).ref_idx[9] == 4
+    x2[8, 3] = np.float16("nan")       # reference 4 too: only reference 3 (+inf) is left ranked
+    assert oracle.strided_encode_stream(x2, 2, window=3).ref_idx[9] == 3
