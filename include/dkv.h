@@ -67,7 +67,8 @@ typedef enum {
     DKV_ERR_ARG = 1,         /* null pointer, non-positive size, inconsistent shape */
     DKV_ERR_UNSUPPORTED = 2, /* valid but not built: head_dim not 64/128, kf > 1024 ... */
     DKV_ERR_WORKSPACE = 3,   /* workspace missing or smaller than dkv_workspace_bytes() */
-    DKV_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
+    DKV_ERR_HIP = 4,         /* a HIP runtime call or kernel launch failed */
+    DKV_ERR_SCRATCH = 5      /* needs more than the fixed scratch of dkv_attn_decode_noalloc */
 } dkv_status;
 
 typedef struct {
@@ -144,6 +145,30 @@ dkv_status dkv_attn_decode(const dkv_config *cfg, const void *cache,
                            const int32_t *block_table, const float *q,
                            const int32_t *seq_lens, float softmax_scale, float *out,
                            void *workspace, size_t workspace_bytes, dkv_stream_t stream);
+
+/*
+ * dkv_attn_decode without a workspace, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, kernels, launches and results as
+ * dkv_attn_decode, except that the split-K partial results go to a scratch
+ * array of 64 MiB that the library holds in each GPU's memory (static device
+ * memory, resolved once per device on the first call there, held until the
+ * process ends).  It allocates nothing, on the device or the host.
+ *  - Needs batch * n_q_heads * nsplit * (head_dim + 4) * 4 bytes of scratch,
+ *    nsplit being dkv_attn_decode's split count (dkv_workspace_bytes(cfg) is
+ *    an upper bound); a configuration needing more than 64 MiB returns
+ *    DKV_ERR_SCRATCH before anything is launched.
+ *  - Every call on one GPU shares that GPU's scratch array: calls that may
+ *    overlap on one GPU (several streams, several host threads) race and must
+ *    be serialised by the caller.  Nothing in it needs clearing: each call
+ *    writes every record it reads.
+ *  - Errors: as dkv_attn_decode, DKV_ERR_SCRATCH, and DKV_ERR_HIP if the
+ *    scratch array's device address cannot be obtained.
+ */
+dkv_status dkv_attn_decode_noalloc(const dkv_config *cfg, const void *cache,
+                                   const int32_t *block_table, const float *q,
+                                   const int32_t *seq_lens, float softmax_scale, float *out,
+                                   dkv_stream_t stream);
 
 /*
  * One serving step in one call: dkv_append of each sequence's new token, then

@@ -114,6 +114,14 @@ static float resolve_scale(const dkv_config &c, float s)
     return sc * 1.4426950408889634f;     // logits kept in log2 units
 }
 
+// Bytes of split-K partials the decode (dkv_attn_decode's split plan) writes for c.
+size_t decode_partials_bytes(const dkv_config &c) { return ws_for(c, delta_plan(c)); }
+
+// The decode of dkv_attn_decode after its argument checks: split phase into
+// `ws` (at least decode_partials_bytes(c) bytes), then the combine.
+dkv_status attn_decode_launch(const dkv_config &c, const void *cache, const int32_t *bt, const float *q,
+                              const int32_t *lens, float scale, float *out, void *ws, hipStream_t st);
+
 }  // namespace dkv
 
 using namespace dkv;
@@ -128,6 +136,7 @@ const char *dkv_status_str(dkv_status s)
     case DKV_ERR_UNSUPPORTED: return "unsupported configuration";
     case DKV_ERR_WORKSPACE: return "workspace missing or too small";
     case DKV_ERR_HIP: return "HIP runtime error";
+    case DKV_ERR_SCRATCH: return "needs more than the fixed scratch of the no-allocation entry point";
     }
     return "unknown status";
 }
@@ -245,10 +254,7 @@ dkv_status dkv_attn_decode(const dkv_config *c, const void *cache, const int32_t
 {
     dkv_status st = attn_common(c, cache, bt, q, lens, out, ws, ws_bytes);
     if (st != DKV_OK) return st;
-    const Plan p = delta_plan(*c);
-    hipError_t e = launch_split_phase(*c, cache, bt, q, lens, scale, ws, p, (hipStream_t)stream);
-    if (e != hipSuccess) return DKV_ERR_HIP;
-    return hip_status(launch_combine(*c, (const float *)ws, p.nsplit, out, (hipStream_t)stream));
+    return dkv::attn_decode_launch(*c, cache, bt, q, lens, scale, out, ws, (hipStream_t)stream);
 }
 
 dkv_status dkv_append_attn_decode(const dkv_config *c, void *cache, float *state, const int32_t *bt,
@@ -488,4 +494,13 @@ dkv_status dkv_stream_read(const void *buf, size_t bytes, uint32_t *sink, size_t
     if (!buf || !sink || bytes < 16) return DKV_ERR_ARG;
     if (sink_words < dkv::stream_read_sink_words()) return DKV_ERR_WORKSPACE;
     return dkv::hip_status(dkv::launch_stream_read(buf, bytes, sink, (hipStream_t)stream));
+}
+
+dkv_status dkv::attn_decode_launch(const dkv_config &c, const void *cache, const int32_t *bt, const float *q,
+                                   const int32_t *lens, float scale, float *out, void *ws, hipStream_t st)
+{
+    const Plan p = delta_plan(c);
+    hipError_t e = launch_split_phase(c, cache, bt, q, lens, scale, ws, p, st);
+    if (e != hipSuccess) return DKV_ERR_HIP;
+    return hip_status(launch_combine(c, (const float *)ws, p.nsplit, out, st));
 }

@@ -15,7 +15,7 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libdkv.so")
 
-DKV_OK, DKV_ERR_ARG, DKV_ERR_UNSUPPORTED, DKV_ERR_WORKSPACE, DKV_ERR_HIP = range(5)
+DKV_OK, DKV_ERR_ARG, DKV_ERR_UNSUPPORTED, DKV_ERR_WORKSPACE, DKV_ERR_HIP, DKV_ERR_SCRATCH = range(6)
 
 
 class DkvError(RuntimeError):
@@ -68,6 +68,7 @@ _SIGS = {
     "dkv_encode_prefill": ([_CFG, _P, _P, _P, _P, _P, _P, _I32, _P], _I32),
     "dkv_append": ([_CFG, _P, _P, _P, _P, _P, _P, _P], _I32),
     "dkv_attn_decode": ([_CFG, _P, _P, _P, _P, _F, _P, _P, _SZ, _P], _I32),
+    "dkv_attn_decode_noalloc": ([_CFG, _P, _P, _P, _P, _F, _P, _P], _I32),
     "dkv_append_attn_decode": ([_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _F, _P, _P, _SZ, _P], _I32),
     "dkv_attn_decode_ref": ([_CFG, _P, _P, _P, _P, _F, _P, _P, _SZ, _P], _I32),
     "dkv_attn_decode_partial": ([_CFG, _P, _P, _P, _P, _F, _P, _SZ, _P], _I32),
@@ -216,6 +217,18 @@ def _attn(fn, cfg, cache, block_table, q, seq_lens, out, workspace, softmax_scal
 def dkv_attn_decode(cfg: Config, cache, block_table, q, seq_lens, out, workspace, softmax_scale=0.0,
                     stream=None):
     _attn("dkv_attn_decode", cfg, cache, block_table, q, seq_lens, out, workspace, softmax_scale, stream)
+
+
+def dkv_attn_decode_noalloc(cfg: Config, cache, block_table, q, seq_lens, out, softmax_scale=0.0, stream=None):
+    """dkv_attn_decode with its split-K partials in the library's fixed scratch array (no workspace)."""
+    import torch
+    B, Hq, D = cfg.batch, cfg.n_q_heads, cfg.head_dim
+    st = load().dkv_attn_decode_noalloc(
+        ctypes.byref(cfg.c()), _ptr(cache, torch.uint8, "cache", dkv_cache_bytes(cfg)),
+        _ptr(block_table, torch.int32, "block_table", _bt_numel(cfg)),
+        _ptr(q, torch.float32, "q", B * Hq * D), _ptr(seq_lens, torch.int32, "seq_lens", B),
+        float(softmax_scale), _ptr(out, torch.float32, "out", B * Hq * D), _stream(stream))
+    _check("dkv_attn_decode_noalloc", st)
 
 
 def dkv_append_attn_decode(cfg: Config, cache, state, block_table, k_new, v_new, positions, q, seq_lens, out,

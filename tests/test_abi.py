@@ -166,3 +166,20 @@ def test_binding_rejects_undersized_caches():
     for i, f in enumerate(calls):
         with pytest.raises(ValueError, match="elements, needs"):
             f()
+
+
+def test_noalloc_decode_rejects_before_touching_the_gpu():
+    """dkv_attn_decode_noalloc checks its arguments and that the split-K
+    partials fit its fixed 64 MiB scratch before anything reaches the GPU."""
+    lib = _lib()
+    fake = ctypes.c_void_p(0x1000)
+    ok = ctypes.byref(_cfg().c())
+    assert lib.dkv_attn_decode_noalloc(ok, fake, None, None, fake, 0.0, fake, None) == binding.DKV_ERR_ARG
+    cpg = ctypes.byref(_cfg(page_tokens=256, n_pages=8, max_pages_per_seq=4).c())
+    assert lib.dkv_attn_decode_noalloc(cpg, fake, None, fake, fake, 0.0, fake, None) == binding.DKV_ERR_ARG
+    # 64 sequences x 128 query heads x 32 splits x 132 floats = 138 MB of partials
+    big = _cfg(batch=64, n_q_heads=128, n_kv_heads=8, max_tokens=65536)
+    assert dkv.dkv_workspace_bytes(big) > 64 << 20
+    assert lib.dkv_attn_decode_noalloc(ctypes.byref(big.c()), fake, None, fake, fake, 0.0, fake,
+                                       None) == binding.DKV_ERR_SCRATCH
+    assert "scratch" in dkv.status_str(binding.DKV_ERR_SCRATCH)
