@@ -246,7 +246,7 @@ def comparisons(w, cfg, k, v, q, lens, ws, steps, stream, qo):
     reps = max(1, math.ceil((1 << 30) / f16_bytes))
     ks = [k] + [k.clone() for _ in range(reps - 1)]
     vs = [v] + [v.clone() for _ in range(reps - 1)]
-    ms = _time(lambda i: dkv.dkv_attn_decode_f16(cfg, ks[i % reps], vs[i % reps], w.S, q, lens, out, ws),
+    ms = _time(lambda i: dkv.dkv_attn_decode_f16(cfg, ks[i % reps], vs[i % reps], None, q, lens, out, ws),
                steps, stream)
     res["f16"] = {"ms_per_step": round(ms, 5), "GBps": round((f16_bytes + qo) / (ms * 1e-3) / 1e9, 2),
                   "hbm_frac": round((f16_bytes + qo) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
@@ -254,10 +254,10 @@ def comparisons(w, cfg, k, v, q, lens, ws, steps, stream, qo):
     del ks, vs
     q4_bytes = 2 * w.B * w.Hkv * w.S * (w.D // 32) * 18
     q4 = torch.empty(dkv.dkv_q4_0_cache_bytes(cfg), dtype=torch.uint8, device=k.device)
-    dkv.dkv_q4_0_encode(cfg, q4, k, v, lens, w.S)
+    dkv.dkv_q4_0_encode(cfg, q4, None, k, v, lens, w.S)
     reps = max(1, math.ceil((1 << 30) / q4.numel()))
     q4s = [q4] + [q4.clone() for _ in range(reps - 1)]
-    ms = _time(lambda i: dkv.dkv_attn_decode_q4_0(cfg, q4s[i % reps], q, lens, out, ws), steps, stream)
+    ms = _time(lambda i: dkv.dkv_attn_decode_q4_0(cfg, q4s[i % reps], None, q, lens, out, ws), steps, stream)
     res["q4_0"] = {"ms_per_step": round(ms, 5), "GBps": round((q4_bytes + qo) / (ms * 1e-3) / 1e9, 2),
                    "hbm_frac": round((q4_bytes + qo) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                    "bytes": q4_bytes, "replicas": reps}
@@ -418,7 +418,7 @@ def quality(w, cfg, cache, q4, k, v, lens, q):
     del kr, vr
     codes = torch.empty(B, H, 2, S, D // 2, dtype=torch.uint8, device=dev)
     scales = torch.empty(B, H, 2, S, D // 32, dtype=torch.int16, device=dev)
-    dkv.dkv_q4_0_export(cfg, q4, lens, S, codes, scales)
+    dkv.dkv_q4_0_export(cfg, q4, None, lens, S, codes, scales)
     mse_q, deqs = [], []
     for s, x in enumerate((k, v)):
         c = codes[:, :, s].reshape(B, H, S, D // 32, 16)

@@ -232,30 +232,53 @@ dkv_status dkv_export(const dkv_config *cfg, const void *cache, const int32_t *b
                       uint8_t *codes, uint16_t *scales, dkv_stream_t stream);
 
 /*
- * In-run comparison: plain Q4_0 cache of absolute values (the 4-bit baseline
- * of the Delta-KV article's "벤치마크" section), 18 bytes per 32 elements.
- * Contiguous layout only (page_tokens must be 0); kf is ignored.
+ * In-run comparisons (the Delta-KV article's "벤치마크" section sets Delta-KV
+ * against an F16 cache and a plain Q4_0 cache of absolute values).  Both
+ * comparison caches are cut in 32-token tiles:
+ *  - contiguous mode (page_tokens == 0): per (sequence, kv-head) a run of
+ *    ceil(max_tokens/32) tiles, sequences and kv-heads in order;
+ *  - paged mode: page_tokens must be a multiple of 32 (else
+ *    DKV_ERR_UNSUPPORTED); a physical page holds every kv-head's tiles,
+ *    [n_kv_heads][page_tokens/32], and block_table (device, int32
+ *    [batch][max_pages_per_seq]) maps logical pages as for the Delta-KV cache.
+ *    Tokens on an unmapped page (id < 0 or >= n_pages) are not attended.
+ * kf is ignored.  Errors: as dkv_check_config, DKV_ERR_UNSUPPORTED,
+ * DKV_ERR_ARG (null pointer; no block table in paged mode; s_max < 0),
+ * DKV_ERR_WORKSPACE (workspace below dkv_workspace_bytes), DKV_ERR_HIP.
+ *
+ * Plain Q4_0 cache: 18 bytes per 32 elements (Q4_0 of the absolute values,
+ * the block rule of the Delta-KV deltas with reference 0).  One tile is 36*D
+ * bytes: [K scales 2D][K codes 16D][V scales 2D][V codes 16D].
  */
-size_t dkv_q4_0_cache_bytes(const dkv_config *cfg);
-dkv_status dkv_q4_0_encode(const dkv_config *cfg, void *q4_cache, const uint16_t *k,
-                           const uint16_t *v, const int32_t *seq_lens, int32_t s_max,
-                           dkv_stream_t stream);
-dkv_status dkv_attn_decode_q4_0(const dkv_config *cfg, const void *q4_cache, const float *q,
+size_t dkv_q4_0_cache_bytes(const dkv_config *cfg);   /* 0 if cfg is invalid or unsupported */
+/* Encodes tokens [0, min(seq_lens[b], s_max)) of k, v (device, fp16
+ * [batch][n_kv_heads][s_max][head_dim]) into q4_cache (dkv_q4_0_cache_bytes). */
+dkv_status dkv_q4_0_encode(const dkv_config *cfg, void *q4_cache, const int32_t *block_table,
+                           const uint16_t *k, const uint16_t *v, const int32_t *seq_lens,
+                           int32_t s_max, dkv_stream_t stream);
+/* Decode attention over the Q4_0 cache; arguments as dkv_attn_decode. */
+dkv_status dkv_attn_decode_q4_0(const dkv_config *cfg, const void *q4_cache,
+                                const int32_t *block_table, const float *q,
                                 const int32_t *seq_lens, float softmax_scale, float *out,
                                 void *workspace, size_t workspace_bytes, dkv_stream_t stream);
 /* Canonical export of the Q4_0 cache: codes uint8 [batch][Hkv][2][s_max][D/2],
- * scales uint16 [batch][Hkv][2][s_max][D/32]. */
-dkv_status dkv_q4_0_export(const dkv_config *cfg, const void *q4_cache, const int32_t *seq_lens,
-                           int32_t s_max, uint8_t *codes, uint16_t *scales, dkv_stream_t stream);
+ * scales uint16 [batch][Hkv][2][s_max][D/32]; rows past a sequence's length or
+ * on an unmapped page are left untouched. */
+dkv_status dkv_q4_0_export(const dkv_config *cfg, const void *q4_cache, const int32_t *block_table,
+                           const int32_t *seq_lens, int32_t s_max, uint8_t *codes,
+                           uint16_t *scales, dkv_stream_t stream);
 
 /*
- * In-run comparison: F16 cache (the unquantised baseline of the same section).
- *  k, v (device) fp16 [batch][n_kv_heads][s_max][head_dim]; kf and paging ignored.
+ * Decode attention over an F16 cache (the unquantised baseline): k and v are
+ * two arrays of fp16 token rows in the tile layout above, i.e. (device)
+ *  contiguous: fp16 [batch][n_kv_heads][max_tokens][head_dim];
+ *  paged:      fp16 [n_pages][n_kv_heads][page_tokens][head_dim].
+ * Other arguments as dkv_attn_decode.
  */
 dkv_status dkv_attn_decode_f16(const dkv_config *cfg, const uint16_t *k, const uint16_t *v,
-                               int32_t s_max, const float *q, const int32_t *seq_lens,
-                               float softmax_scale, float *out, void *workspace,
-                               size_t workspace_bytes, dkv_stream_t stream);
+                               const int32_t *block_table, const float *q,
+                               const int32_t *seq_lens, float softmax_scale, float *out,
+                               void *workspace, size_t workspace_bytes, dkv_stream_t stream);
 
 /*
  * Quality comparison: plain Q8_0 of absolute values, the 8-bit reference the

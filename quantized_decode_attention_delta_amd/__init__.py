@@ -10,7 +10,7 @@ from .dkv import (  # noqa: F401
     dkv_q4_0_cache_bytes, dkv_encode_prefill, dkv_append, dkv_attn_decode, dkv_append_attn_decode,
     dkv_attn_decode_ref, dkv_attn_decode_partial,
     dkv_reconstruct, dkv_export, export_shapes, dkv_q4_0_encode, dkv_q4_0_export, dkv_attn_decode_q4_0,
-    dkv_attn_decode_f16, dkv_stream_read_sink_words, dkv_stream_read, dkv_attn_distortion,
+    dkv_attn_decode_f16, f16_cache_shape, dkv_stream_read_sink_words, dkv_stream_read, dkv_attn_distortion,
     dkv_q8_0_encode, dkv_strided_cache_bytes, dkv_strided_layout, dkv_strided_encode_prefill,
     dkv_strided_attn_decode, dkv_strided_append, dkv_strided_append_attn_decode,
 )

@@ -46,13 +46,13 @@ hipError_t launch_attn_g8(const dkv_config &, const void *, const int32_t *, con
                           float, float *, int, int, hipStream_t, const AppendArgs *);
 bool fused_g8_supported(const dkv_config &);
 bool fused_long_g8_supported(const dkv_config &);
-hipError_t launch_q40_encode(const dkv_config &, void *, const uint16_t *, const uint16_t *,
+hipError_t launch_q40_encode(const dkv_config &, void *, const int32_t *, const uint16_t *, const uint16_t *,
                              const int32_t *, int, hipStream_t);
-hipError_t launch_q40_export(const dkv_config &, const void *, const int32_t *, int, uint8_t *,
+hipError_t launch_q40_export(const dkv_config &, const void *, const int32_t *, const int32_t *, int, uint8_t *,
                              uint16_t *, hipStream_t);
-hipError_t launch_attn_q40(const dkv_config &, const void *, const float *, const int32_t *, float,
+hipError_t launch_attn_q40(const dkv_config &, const void *, const int32_t *, const float *, const int32_t *, float,
                            float *, int, int, hipStream_t);
-hipError_t launch_attn_f16(const dkv_config &, const uint16_t *, const uint16_t *, int, const float *,
+hipError_t launch_attn_f16(const dkv_config &, const uint16_t *, const uint16_t *, const int32_t *, const float *,
                            const int32_t *, float, float *, int, int, hipStream_t);
 
 // Split plan: runs of whole units (groups, or 32-token tiles) per workgroup,
@@ -83,11 +83,8 @@ Plan delta_plan(const dkv_config &c)
     const Geom g = make_geom(c);
     return make_plan(g.ng_cap, c.batch, c.n_kv_heads, c.kf >= 2048 ? 1 : 2048 / c.kf);
 }
-Plan tile_plan(const dkv_config &c)
-{
-    const int tiles = (c.max_tokens + 31) / 32;
-    return make_plan(tiles, c.batch, c.n_kv_heads, 64);
-}
+// the comparison caches (32-token tiles, contiguous or paged)
+Plan tile_plan(const dkv_config &c) { return make_plan(cmp_ntiles(c), c.batch, c.n_kv_heads, 64); }
 // strided-reference decode: one wave per run, so runs of at most 16 tiles
 Plan strided_plan(const dkv_config &c)
 {
@@ -101,7 +98,7 @@ static size_t ws_for(const dkv_config &c, const Plan &p)
 static size_t workspace_total(const dkv_config &c)
 {
     const size_t a = ws_for(c, delta_plan(c));
-    const size_t b = c.page_tokens == 0 ? ws_for(c, tile_plan(c)) : 0;
+    const size_t b = (c.page_tokens == 0 || c.page_tokens % 32 == 0) ? ws_for(c, tile_plan(c)) : 0;
     const size_t d = c.page_tokens == 0 ? ws_for(c, strided_plan(c)) : 0;
     return a > b ? (a > d ? a : d) : (b > d ? b : d);
 }
@@ -345,66 +342,73 @@ dkv_status dkv_export(const dkv_config *c, const void *cache, const int32_t *bt,
                                     codes, scales, (hipStream_t)stream));
 }
 
-size_t dkv_q4_0_cache_bytes(const dkv_config *c)
-{
-    if (dkv_check_config(c) != DKV_OK || c->page_tokens != 0) return 0;
-    const int64_t tiles = (c->max_tokens + 31) / 32;
-    return (size_t)c->batch * c->n_kv_heads * tiles * 2 * (16 * c->head_dim + 64 * (c->head_dim / 32));
-}
-
-static dkv_status q40_common(const dkv_config *c)
+// The comparison caches are cut in 32-token tiles, so paged mode needs
+// page_tokens % 32 == 0 (a tile never straddles two pages).
+static dkv_status cmp_check(const dkv_config *c, const int32_t *bt)
 {
     dkv_status st = dkv_check_config(c);
     if (st != DKV_OK) return st;
-    if (c->page_tokens != 0) return DKV_ERR_UNSUPPORTED;
+    if (c->page_tokens > 0 && c->page_tokens % 32 != 0) return DKV_ERR_UNSUPPORTED;
+    if (c->page_tokens > 0 && !bt) return DKV_ERR_ARG;
     return DKV_OK;
 }
 
-dkv_status dkv_q4_0_encode(const dkv_config *c, void *q4, const uint16_t *k, const uint16_t *v,
+size_t dkv_q4_0_cache_bytes(const dkv_config *c)
+{
+    if (dkv_check_config(c) != DKV_OK || (c->page_tokens > 0 && c->page_tokens % 32 != 0)) return 0;
+    const int64_t tiles = c->page_tokens > 0 ? (int64_t)c->n_pages * (c->page_tokens / 32)
+                                             : (int64_t)c->batch * cmp_ntiles(*c);
+    return (size_t)tiles * c->n_kv_heads * (size_t)q40_tile_bytes(c->head_dim);
+}
+
+dkv_status dkv_q4_0_encode(const dkv_config *c, void *q4, const int32_t *bt, const uint16_t *k, const uint16_t *v,
                            const int32_t *lens, int32_t s_max, dkv_stream_t stream)
 {
-    dkv_status st = q40_common(c);
+    dkv_status st = cmp_check(c, bt);
     if (st != DKV_OK) return st;
     if (!q4 || !k || !v || !lens || s_max < 0) return DKV_ERR_ARG;
     if (s_max == 0) return DKV_OK;
-    return hip_status(launch_q40_encode(*c, q4, k, v, lens, s_max, (hipStream_t)stream));
+    return hip_status(launch_q40_encode(*c, q4, c->page_tokens > 0 ? bt : nullptr, k, v, lens, s_max,
+                                        (hipStream_t)stream));
 }
 
-dkv_status dkv_q4_0_export(const dkv_config *c, const void *q4, const int32_t *lens, int32_t s_max,
-                           uint8_t *codes, uint16_t *scales, dkv_stream_t stream)
+dkv_status dkv_q4_0_export(const dkv_config *c, const void *q4, const int32_t *bt, const int32_t *lens,
+                           int32_t s_max, uint8_t *codes, uint16_t *scales, dkv_stream_t stream)
 {
-    dkv_status st = q40_common(c);
+    dkv_status st = cmp_check(c, bt);
     if (st != DKV_OK) return st;
     if (!q4 || !lens || !codes || !scales || s_max < 0) return DKV_ERR_ARG;
     if (s_max == 0) return DKV_OK;
-    return hip_status(launch_q40_export(*c, q4, lens, s_max, codes, scales, (hipStream_t)stream));
+    return hip_status(launch_q40_export(*c, q4, c->page_tokens > 0 ? bt : nullptr, lens, s_max, codes, scales,
+                                        (hipStream_t)stream));
 }
 
-dkv_status dkv_attn_decode_q4_0(const dkv_config *c, const void *q4, const float *q, const int32_t *lens,
-                                float scale, float *out, void *ws, size_t ws_bytes, dkv_stream_t stream)
+dkv_status dkv_attn_decode_q4_0(const dkv_config *c, const void *q4, const int32_t *bt, const float *q,
+                                const int32_t *lens, float scale, float *out, void *ws, size_t ws_bytes,
+                                dkv_stream_t stream)
 {
-    dkv_status st = q40_common(c);
+    dkv_status st = cmp_check(c, bt);
     if (st != DKV_OK) return st;
     if (!q4 || !q || !lens || !out) return DKV_ERR_ARG;
     const Plan p = tile_plan(*c);
     if (!ws || ws_bytes < workspace_total(*c)) return DKV_ERR_WORKSPACE;
-    hipError_t e = launch_attn_q40(*c, q4, q, lens, resolve_scale(*c, scale), (float *)ws, p.nsplit, p.chunk,
-                                   (hipStream_t)stream);
+    hipError_t e = launch_attn_q40(*c, q4, c->page_tokens > 0 ? bt : nullptr, q, lens, resolve_scale(*c, scale),
+                                   (float *)ws, p.nsplit, p.chunk, (hipStream_t)stream);
     if (e != hipSuccess) return DKV_ERR_HIP;
     return hip_status(launch_combine(*c, (const float *)ws, p.nsplit, out, (hipStream_t)stream));
 }
 
-dkv_status dkv_attn_decode_f16(const dkv_config *c, const uint16_t *k, const uint16_t *v, int32_t s_max,
+dkv_status dkv_attn_decode_f16(const dkv_config *c, const uint16_t *k, const uint16_t *v, const int32_t *bt,
                                const float *q, const int32_t *lens, float scale, float *out, void *ws,
                                size_t ws_bytes, dkv_stream_t stream)
 {
-    dkv_status st = q40_common(c);
+    dkv_status st = cmp_check(c, bt);
     if (st != DKV_OK) return st;
-    if (!k || !v || !q || !lens || !out || s_max < 1 || s_max > c->max_tokens) return DKV_ERR_ARG;
+    if (!k || !v || !q || !lens || !out) return DKV_ERR_ARG;
     const Plan p = tile_plan(*c);
     if (!ws || ws_bytes < workspace_total(*c)) return DKV_ERR_WORKSPACE;
-    hipError_t e = launch_attn_f16(*c, k, v, s_max, q, lens, resolve_scale(*c, scale), (float *)ws, p.nsplit,
-                                   p.chunk, (hipStream_t)stream);
+    hipError_t e = launch_attn_f16(*c, k, v, c->page_tokens > 0 ? bt : nullptr, q, lens, resolve_scale(*c, scale),
+                                   (float *)ws, p.nsplit, p.chunk, (hipStream_t)stream);
     if (e != hipSuccess) return DKV_ERR_HIP;
     return hip_status(launch_combine(*c, (const float *)ws, p.nsplit, out, (hipStream_t)stream));
 }

@@ -1207,9 +1207,9 @@ hipError_t launch_attn_g8(const dkv_config &c, const void *cache, const int32_t 
 // tile's largest |V scale| (the V weight range) is reduced over the wave.
 template <int D>
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
-    k_attn_q40_g8(dkv_config cfg, const uint8_t *__restrict__ q4, const float *__restrict__ q,
-                  const int32_t *__restrict__ seq_lens, float scale_log2, float *__restrict__ ws, int nsplit,
-                  int chunk)
+    k_attn_q40_g8(dkv_config cfg, const uint8_t *__restrict__ q4, const int32_t *__restrict__ bt,
+                  const float *__restrict__ q, const int32_t *__restrict__ seq_lens, float scale_log2,
+                  float *__restrict__ ws, int nsplit, int chunk)
 {
     constexpr int NB = D / 32;
     const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -1224,6 +1224,23 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
     // [unused 2D][K scales 2D][unused 2D][V scales 2D]: the side layout of the phases
     __shared__ __attribute__((aligned(16))) uint32_t side[2 * D];
     __shared__ G8Shared<D> sh;
+    // the run's mapped tiles (a run has at most 64: the split plan caps it),
+    // listed with their byte offsets; paged mode may leave pages unmapped
+    __shared__ int64_t toffs[64];
+    __shared__ int tnum[64];
+    int ntl;
+    {
+        const int x = t0 + lane;
+        const int64_t o = x < t1 ? q40_tile_offset(cfg, bt, b, h, x) : -1;
+        const uint64_t mk = __ballot(o >= 0);
+        ntl = __popcll(mk);
+        if (o >= 0) {
+            const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mk, 0u));
+            toffs[pos] = o;
+            tnum[pos] = x;
+        }
+        __syncthreads();
+    }
 
     G8Ops op;
     float qraw[NB][8];
@@ -1239,9 +1256,9 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
     const int ok0 = 2 * D + n * (D / 2) + 4 * j * NB;
     const int ok1 = 2 * D + (16 + n) * (D / 2) + 4 * j * NB;
     const int ov = 20 * D + (j * 16 + n) * (D / 16) * 4;
-    auto load_tile = [&](G8Regs<D> &r, int tl) {
+    auto load_tile = [&](G8Regs<D> &r, int k) {
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(q4 + q40_tile_offset(cfg, b, h, tl)), (short)0, tbytes, 0x00020000);
+            (void *)(q4 + uniform_offset(toffs, k)), (short)0, tbytes, 0x00020000);
         r.side = __builtin_amdgcn_raw_buffer_load_b128(rs, so, 0, kStream);
         if constexpr (NB == 4) {
             const u4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, ok0, 0, kStream);
@@ -1268,7 +1285,8 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
             for (int k = 0; k < 4; ++k) r.vc[k] = v0[k];
         }
     };
-    auto run = [&](const G8Regs<D> &r, int tl) {
+    auto run = [&](const G8Regs<D> &r, int k) {
+        const int tl = __builtin_amdgcn_readfirstlane(tnum[k]);
         __syncthreads();
         if (lane < D / 2) ((u4 *)side)[fresh_lane_id()] = r.side;
         __syncthreads();
@@ -1301,16 +1319,16 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
         else
             v_phase_g8<D, false, false, false>(st, r.vc, sb + 4 * D, Lg, nval, j, n, c2E, AZ, 0.0f);
     };
-    if (t0 < t1) {
+    if (ntl > 0) {
         G8Regs<D> ra, rb;
-        int tl = t0;
-        load_tile(ra, tl);
+        int k = 0;
+        load_tile(ra, k);
         auto step = [&](const G8Regs<D> &cur, G8Regs<D> &pf) {
             // prefetch unconditionally (past the end: the current tile again)
-            load_tile(pf, tl + 1 < t1 ? tl + 1 : tl);
-            run(cur, tl);
-            ++tl;
-            return tl < t1;
+            load_tile(pf, k + 1 < ntl ? k + 1 : k);
+            run(cur, k);
+            ++k;
+            return k < ntl;
         };
         while (step(ra, rb) && step(rb, ra)) {
         }
@@ -1318,16 +1336,17 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
     write_partial_g8<D>(st, ws, row0, G, nsplit, split, lane, j, n);
 }
 
-hipError_t launch_attn_q40_g8(const dkv_config &c, const void *q4, const float *q, const int32_t *lens,
-                              float scale_log2, float *ws, int nsplit, int chunk, hipStream_t st)
+hipError_t launch_attn_q40_g8(const dkv_config &c, const void *q4, const int32_t *bt, const float *q,
+                              const int32_t *lens, float scale_log2, float *ws, int nsplit, int chunk, hipStream_t st)
 {
+    if (chunk > 64) return hipErrorInvalidValue;      // the kernel lists at most 64 tiles per run
     dim3 grid(nsplit, c.n_kv_heads, c.batch);
     if (c.head_dim == 64)
-        hipLaunchKernelGGL(k_attn_q40_g8<64>, grid, dim3(64), 0, st, c, (const uint8_t *)q4, q, lens, scale_log2, ws,
-                           nsplit, chunk);
-    else
-        hipLaunchKernelGGL(k_attn_q40_g8<128>, grid, dim3(64), 0, st, c, (const uint8_t *)q4, q, lens, scale_log2,
+        hipLaunchKernelGGL(k_attn_q40_g8<64>, grid, dim3(64), 0, st, c, (const uint8_t *)q4, bt, q, lens, scale_log2,
                            ws, nsplit, chunk);
+    else
+        hipLaunchKernelGGL(k_attn_q40_g8<128>, grid, dim3(64), 0, st, c, (const uint8_t *)q4, bt, q, lens,
+                           scale_log2, ws, nsplit, chunk);
     return hipGetLastError();
 }
 

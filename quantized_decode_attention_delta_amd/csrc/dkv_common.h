@@ -124,16 +124,51 @@ __host__ __device__ inline int64_t group_offset(const Geom &g, const int32_t *bl
     return (int64_t)b * g.page_bytes + ((int64_t)h * g.gpp + gi) * g.rec;
 }
 
-// ---- plain Q4_0 comparison cache --------------------------------------------
-// Per (sequence, kv-head) a run of 32-token tiles of 36*D bytes:
-// [K scales 2D][K codes 16D][V scales 2D][V codes 16D], codes in the same
-// orders as the Delta-KV K code rows and V code tiles (V in block-pair order
-// under the same condition on G and D).
-__host__ __device__ inline int64_t q40_tile_bytes(int D) { return 36LL * D; }
-__host__ __device__ inline int q40_ntiles(const dkv_config &c) { return (c.max_tokens + 31) / 32; }
-__host__ __device__ inline int64_t q40_tile_offset(const dkv_config &c, int b, int h, int tile)
+// ---- comparison caches (plain Q4_0, F16): 32-token tiles ----------------------
+// Both comparison caches are cut in 32-token tiles.  Contiguous mode: per
+// (sequence, kv-head) a run of ceil(max_tokens/32) tiles.  Paged mode (the
+// layout of the Delta-KV cache's pages, which needs page_tokens % 32 == 0 here):
+// a page of page_tokens tokens holds every kv-head's tiles,
+// [n_kv_heads][page_tokens/32], and block_table maps a sequence's logical page
+// to a physical one.  cmp_tile_index returns the tile's index in units of one
+// tile of one kv-head, or -1 for an unmapped (or out-of-range) page.
+__host__ __device__ inline int cmp_ntiles(const dkv_config &c)
 {
-    return (((int64_t)b * c.n_kv_heads + h) * q40_ntiles(c) + tile) * q40_tile_bytes(c.head_dim);
+    return c.page_tokens > 0 ? c.max_pages_per_seq * (c.page_tokens / 32) : (c.max_tokens + 31) / 32;
+}
+__host__ __device__ inline int64_t cmp_tile_index(const dkv_config &c, const int32_t *block_table, int b, int h,
+                                                  int tile)
+{
+    if (c.page_tokens > 0) {
+        const int tpp = c.page_tokens / 32;
+        const int phys = block_table[(int64_t)b * c.max_pages_per_seq + tile / tpp];
+        if (phys < 0 || phys >= c.n_pages) return -1;
+        return ((int64_t)phys * c.n_kv_heads + h) * tpp + tile % tpp;
+    }
+    return ((int64_t)b * c.n_kv_heads + h) * cmp_ntiles(c) + tile;
+}
+
+// Plain Q4_0 tile: 36*D bytes, [K scales 2D][K codes 16D][V scales 2D][V codes
+// 16D], codes in the same orders as the Delta-KV K code rows and V code tiles
+// (V in block-pair order under the same condition on G and D).
+__host__ __device__ inline int64_t q40_tile_bytes(int D) { return 36LL * D; }
+__host__ __device__ inline int q40_ntiles(const dkv_config &c) { return cmp_ntiles(c); }
+__host__ __device__ inline int64_t q40_tile_offset(const dkv_config &c, const int32_t *block_table, int b, int h,
+                                                   int tile)
+{
+    const int64_t t = cmp_tile_index(c, block_table, b, h, tile);
+    return t < 0 ? -1 : t * q40_tile_bytes(c.head_dim);
+}
+// F16 tile: 32 token rows of D fp16 values, separately for K and V (two
+// arrays of the same layout); element offset of the tile's first row, or -1.
+__host__ __device__ inline int64_t f16_tile_elem(const dkv_config &c, const int32_t *block_table, int b, int h,
+                                                 int tile)
+{
+    if (c.page_tokens > 0) {
+        const int64_t t = cmp_tile_index(c, block_table, b, h, tile);
+        return t < 0 ? -1 : t * 32 * c.head_dim;
+    }
+    return (((int64_t)b * c.n_kv_heads + h) * c.max_tokens + 32LL * tile) * c.head_dim;
 }
 __host__ __device__ inline int q40_vbp(const dkv_config &c)
 {

@@ -20,7 +20,7 @@ namespace dkv {
 // absolute value (reference 0).
 // ------------------------------------------------------------------------
 template <int D>
-__global__ void __launch_bounds__(64) k_q40_encode(dkv_config cfg, uint8_t *q4, const uint16_t *kin,
+__global__ void __launch_bounds__(64) k_q40_encode(dkv_config cfg, uint8_t *q4, const int32_t *bt, const uint16_t *kin,
                                                    const uint16_t *vin, const int32_t *seq_lens, int s_max)
 {
     constexpr int NC = D / 64, nb = D / 32;
@@ -28,8 +28,10 @@ __global__ void __launch_bounds__(64) k_q40_encode(dkv_config cfg, uint8_t *q4, 
     const int L = min(min(seq_lens[b], q40_ntiles(cfg) * 32), s_max);
     const int t0 = tile * 32;
     if (t0 >= L) return;
+    const int64_t toff = q40_tile_offset(cfg, bt, b, h, tile);
+    if (toff < 0) return;                       // unmapped page
     const int n = min(32, L - t0);
-    uint8_t *base = q4 + q40_tile_offset(cfg, b, h, tile) + (s ? 18 * D : 0);
+    uint8_t *base = q4 + toff + (s ? 18 * D : 0);
     uint16_t *sc = (uint16_t *)base;
     uint8_t *cd = base + 2 * D;
     const uint16_t *x = (s ? vin : kin) + (((int64_t)b * cfg.n_kv_heads + h) * s_max + t0) * D;
@@ -76,8 +78,9 @@ __global__ void __launch_bounds__(64) k_q40_encode(dkv_config cfg, uint8_t *q4, 
 // code i | code i+16 << 4), scales uint16 [B][Hkv][2][s_max][D/32].
 // grid (ceil(s_max*D/2 / 256), Hkv*2, B), one thread per output code byte.
 template <int D>
-__global__ void __launch_bounds__(256) k_q40_export(dkv_config cfg, const uint8_t *q4, const int32_t *seq_lens,
-                                                    int s_max, uint8_t *codes, uint16_t *scales)
+__global__ void __launch_bounds__(256) k_q40_export(dkv_config cfg, const uint8_t *q4, const int32_t *bt,
+                                                    const int32_t *seq_lens, int s_max, uint8_t *codes,
+                                                    uint16_t *scales)
 {
     constexpr int nb = D / 32, RB = D / 2;
     const int h = blockIdx.y >> 1, s = blockIdx.y & 1, b = blockIdx.z;
@@ -85,7 +88,9 @@ __global__ void __launch_bounds__(256) k_q40_export(dkv_config cfg, const uint8_
     const int t = (int)(e / RB), byte = (int)(e % RB);
     const int L = min(min(seq_lens[b], q40_ntiles(cfg) * 32), s_max);
     if (t >= L) return;
-    const uint8_t *base = q4 + q40_tile_offset(cfg, b, h, t >> 5) + (s ? 18 * D : 0);
+    const int64_t toff = q40_tile_offset(cfg, bt, b, h, t >> 5);
+    if (toff < 0) return;                       // unmapped page: the row is left untouched
+    const uint8_t *base = q4 + toff + (s ? 18 * D : 0);
     const int tau = t & 31, blk = byte >> 4, i = byte & 15;
     uint8_t out;
     if (s == 0) {
@@ -161,8 +166,9 @@ __device__ inline void setup_query(float (*sq)[D + 4], u4 *qB, const float *q, i
 // ------------------------------------------------------------------------
 template <int D>
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
-    k_attn_q40(dkv_config cfg, const uint8_t *__restrict__ q4, const float *__restrict__ q,
-               const int32_t *__restrict__ seq_lens, float scale_log2, float *__restrict__ ws, int nsplit, int chunk)
+    k_attn_q40(dkv_config cfg, const uint8_t *__restrict__ q4, const int32_t *__restrict__ bt,
+               const float *__restrict__ q, const int32_t *__restrict__ seq_lens, float scale_log2,
+               float *__restrict__ ws, int nsplit, int chunk)
 {
     constexpr int NB = D / 32, NCC = D / 16;
     const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -208,7 +214,9 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
     const int tb = (int)q40_tile_bytes(D);
 
     for (int tl = t0; tl < t1; ++tl) {
-        const uint8_t *tp = q4 + q40_tile_offset(cfg, b, h, tl);
+        const int64_t toff = q40_tile_offset(cfg, bt, b, h, tl);
+        if (toff < 0) continue;                 // unmapped page: its tokens are not attended
+        const uint8_t *tp = q4 + toff;
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)tp, (short)0, tb, 0x00020000);
         const int nvt = min(32, L - 32 * tl);
         __syncthreads();
@@ -395,9 +403,9 @@ constexpr int kStreamF16 = 2;
 
 template <int D>
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
-    k_attn_f16(dkv_config cfg, const uint16_t *__restrict__ kin, const uint16_t *__restrict__ vin, int s_max,
-               const float *__restrict__ q, const int32_t *__restrict__ seq_lens, float scale_log2,
-               float *__restrict__ ws, int nsplit, int chunk)
+    k_attn_f16(dkv_config cfg, const uint16_t *__restrict__ kin, const uint16_t *__restrict__ vin,
+               const int32_t *__restrict__ bt, const float *__restrict__ q, const int32_t *__restrict__ seq_lens,
+               float scale_log2, float *__restrict__ ws, int nsplit, int chunk)
 {
     constexpr int NB = D / 32;
     constexpr int CPL = D / 16;             // channels per lane per V token load
@@ -405,7 +413,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
     const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int lane = threadIdx.x, j = lane >> 4, n = lane & 15;
     const int G = cfg.n_q_heads / cfg.n_kv_heads;
-    const int L = min(seq_lens[b], s_max);
+    const int L = min(seq_lens[b], cmp_ntiles(cfg) * 32);
     const int nt = (L + 31) >> 5;
     const int t0 = split * chunk, t1 = min(nt, t0 + chunk);
     const int64_t row0 = (int64_t)b * cfg.n_q_heads + h * G;
@@ -419,11 +427,12 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
 #pragma unroll
     for (int r = 0; r < CPL; ++r) acc[r] = f4{0, 0, 0, 0};
     float m = -INFINITY, l = 0.0f;
-    const int64_t sbase = ((int64_t)b * cfg.n_kv_heads + h) * s_max;
 
     for (int tl = t0; tl < t1; ++tl) {
-        const int64_t e0 = (sbase + 32 * tl) * D;
-        const int bytes = (s_max - 32 * tl) * D * 2;      // rest of this stream: loads past it return 0
+        const int64_t e0 = f16_tile_elem(cfg, bt, b, h, tl);
+        if (e0 < 0) continue;                   // unmapped page: its tokens are not attended
+        // the tile's rows (contiguous: up to the end of the stream; loads past it return 0)
+        const int bytes = (cfg.page_tokens > 0 ? 32 : min(32, cfg.max_tokens - 32 * tl)) * D * 2;
         const __amdgpu_buffer_rsrc_t rk =
             __builtin_amdgcn_make_buffer_rsrc((void *)(kin + e0), (short)0, bytes, 0x00020000);
         const __amdgpu_buffer_rsrc_t rv =
@@ -572,15 +581,15 @@ __global__ void __launch_bounds__(64) k_q80_encode(dkv_config cfg, const uint16_
 // ------------------------------------------------------------------------
 // Launchers
 // ------------------------------------------------------------------------
-hipError_t launch_q40_encode(const dkv_config &c, void *q4, const uint16_t *k, const uint16_t *v,
+hipError_t launch_q40_encode(const dkv_config &c, void *q4, const int32_t *bt, const uint16_t *k, const uint16_t *v,
                              const int32_t *lens, int s_max, hipStream_t st)
 {
     const int tiles = min(q40_ntiles(c), (s_max + 31) / 32);
     dim3 grid(tiles, c.n_kv_heads * 2, c.batch);
     if (c.head_dim == 64)
-        hipLaunchKernelGGL(k_q40_encode<64>, grid, dim3(64), 0, st, c, (uint8_t *)q4, k, v, lens, s_max);
+        hipLaunchKernelGGL(k_q40_encode<64>, grid, dim3(64), 0, st, c, (uint8_t *)q4, bt, k, v, lens, s_max);
     else
-        hipLaunchKernelGGL(k_q40_encode<128>, grid, dim3(64), 0, st, c, (uint8_t *)q4, k, v, lens, s_max);
+        hipLaunchKernelGGL(k_q40_encode<128>, grid, dim3(64), 0, st, c, (uint8_t *)q4, bt, k, v, lens, s_max);
     return hipGetLastError();
 }
 
@@ -595,46 +604,47 @@ hipError_t launch_q80_encode(const dkv_config &c, const uint16_t *k, const uint1
     return hipGetLastError();
 }
 
-hipError_t launch_q40_export(const dkv_config &c, const void *q4, const int32_t *lens, int s_max, uint8_t *codes,
-                             uint16_t *scales, hipStream_t st)
+hipError_t launch_q40_export(const dkv_config &c, const void *q4, const int32_t *bt, const int32_t *lens, int s_max,
+                             uint8_t *codes, uint16_t *scales, hipStream_t st)
 {
     const int64_t per = (int64_t)s_max * (c.head_dim / 2);
     dim3 grid((unsigned)((per + 255) / 256), c.n_kv_heads * 2, c.batch);
     if (c.head_dim == 64)
-        hipLaunchKernelGGL(k_q40_export<64>, grid, dim3(256), 0, st, c, (const uint8_t *)q4, lens, s_max, codes,
+        hipLaunchKernelGGL(k_q40_export<64>, grid, dim3(256), 0, st, c, (const uint8_t *)q4, bt, lens, s_max, codes,
                            scales);
     else
-        hipLaunchKernelGGL(k_q40_export<128>, grid, dim3(256), 0, st, c, (const uint8_t *)q4, lens, s_max, codes,
+        hipLaunchKernelGGL(k_q40_export<128>, grid, dim3(256), 0, st, c, (const uint8_t *)q4, bt, lens, s_max, codes,
                            scales);
     return hipGetLastError();
 }
 
-hipError_t launch_attn_q40_g8(const dkv_config &c, const void *q4, const float *q, const int32_t *lens,
-                              float scale_log2, float *ws, int nsplit, int chunk, hipStream_t st);
+hipError_t launch_attn_q40_g8(const dkv_config &c, const void *q4, const int32_t *bt, const float *q,
+                              const int32_t *lens, float scale_log2, float *ws, int nsplit, int chunk, hipStream_t st);
 
-hipError_t launch_attn_q40(const dkv_config &c, const void *q4, const float *q, const int32_t *lens, float scale_log2,
-                           float *ws, int nsplit, int chunk, hipStream_t st)
+hipError_t launch_attn_q40(const dkv_config &c, const void *q4, const int32_t *bt, const float *q, const int32_t *lens,
+                           float scale_log2, float *ws, int nsplit, int chunk, hipStream_t st)
 {
-    if (q40_vbp(c)) return launch_attn_q40_g8(c, q4, q, lens, scale_log2, ws, nsplit, chunk, st);
+    if (q40_vbp(c)) return launch_attn_q40_g8(c, q4, bt, q, lens, scale_log2, ws, nsplit, chunk, st);
     dim3 grid(nsplit, c.n_kv_heads, c.batch);
     if (c.head_dim == 64)
-        hipLaunchKernelGGL(k_attn_q40<64>, grid, dim3(64), 0, st, c, (const uint8_t *)q4, q, lens, scale_log2, ws,
+        hipLaunchKernelGGL(k_attn_q40<64>, grid, dim3(64), 0, st, c, (const uint8_t *)q4, bt, q, lens, scale_log2, ws,
                            nsplit, chunk);
     else
-        hipLaunchKernelGGL(k_attn_q40<128>, grid, dim3(64), 0, st, c, (const uint8_t *)q4, q, lens, scale_log2, ws,
-                           nsplit, chunk);
+        hipLaunchKernelGGL(k_attn_q40<128>, grid, dim3(64), 0, st, c, (const uint8_t *)q4, bt, q, lens, scale_log2,
+                           ws, nsplit, chunk);
     return hipGetLastError();
 }
 
-hipError_t launch_attn_f16(const dkv_config &c, const uint16_t *k, const uint16_t *v, int s_max, const float *q,
-                           const int32_t *lens, float scale_log2, float *ws, int nsplit, int chunk, hipStream_t st)
+hipError_t launch_attn_f16(const dkv_config &c, const uint16_t *k, const uint16_t *v, const int32_t *bt,
+                           const float *q, const int32_t *lens, float scale_log2, float *ws, int nsplit, int chunk,
+                           hipStream_t st)
 {
     dim3 grid(nsplit, c.n_kv_heads, c.batch);
     if (c.head_dim == 64)
-        hipLaunchKernelGGL(k_attn_f16<64>, grid, dim3(64), 0, st, c, k, v, s_max, q, lens, scale_log2, ws, nsplit,
+        hipLaunchKernelGGL(k_attn_f16<64>, grid, dim3(64), 0, st, c, k, v, bt, q, lens, scale_log2, ws, nsplit,
                            chunk);
     else
-        hipLaunchKernelGGL(k_attn_f16<128>, grid, dim3(64), 0, st, c, k, v, s_max, q, lens, scale_log2, ws, nsplit,
+        hipLaunchKernelGGL(k_attn_f16<128>, grid, dim3(64), 0, st, c, k, v, bt, q, lens, scale_log2, ws, nsplit,
                            chunk);
     return hipGetLastError();
 }

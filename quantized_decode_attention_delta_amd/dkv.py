@@ -75,10 +75,10 @@ _SIGS = {
     "dkv_reconstruct": ([_CFG, _P, _P, _P, _I32, _P, _P, _P], _I32),
     "dkv_export": ([_CFG, _P, _P, _P, _I32, _P, _P, _P, _P], _I32),
     "dkv_q4_0_cache_bytes": ([_CFG], _SZ),
-    "dkv_q4_0_encode": ([_CFG, _P, _P, _P, _P, _I32, _P], _I32),
-    "dkv_q4_0_export": ([_CFG, _P, _P, _I32, _P, _P, _P], _I32),
-    "dkv_attn_decode_q4_0": ([_CFG, _P, _P, _P, _F, _P, _P, _SZ, _P], _I32),
-    "dkv_attn_decode_f16": ([_CFG, _P, _P, _I32, _P, _P, _F, _P, _P, _SZ, _P], _I32),
+    "dkv_q4_0_encode": ([_CFG, _P, _P, _P, _P, _P, _I32, _P], _I32),
+    "dkv_q4_0_export": ([_CFG, _P, _P, _P, _I32, _P, _P, _P], _I32),
+    "dkv_attn_decode_q4_0": ([_CFG, _P, _P, _P, _P, _F, _P, _P, _SZ, _P], _I32),
+    "dkv_attn_decode_f16": ([_CFG, _P, _P, _P, _P, _P, _F, _P, _P, _SZ, _P], _I32),
     "dkv_q8_0_encode": ([_CFG, _P, _P, _P, _I32, _P, _P, _P], _I32),
     "dkv_attn_distortion": ([_CFG, _P, _P, _P, _P, _I32, _P, _P, _F, _P, _P, _P, _P], _I32),
     "dkv_stream_read_sink_words": ([], _SZ),
@@ -324,45 +324,58 @@ def dkv_export(cfg: Config, cache, block_table, seq_lens, s_max: int, kf_rows, c
     _check("dkv_export", st)
 
 
-def dkv_q4_0_encode(cfg: Config, q4_cache, k, v, seq_lens, s_max: int, stream=None):
+def f16_cache_shape(cfg: Config):
+    """Shape of each of the two fp16 arrays (K, V) dkv_attn_decode_f16 reads."""
+    if cfg.page_tokens > 0:
+        return (cfg.n_pages, cfg.n_kv_heads, cfg.page_tokens, cfg.head_dim)
+    return (cfg.batch, cfg.n_kv_heads, cfg.max_tokens, cfg.head_dim)
+
+
+def dkv_q4_0_encode(cfg: Config, q4_cache, block_table, k, v, seq_lens, s_max: int, stream=None):
     import torch
     n = cfg.batch * cfg.n_kv_heads * s_max * cfg.head_dim
     st = load().dkv_q4_0_encode(
         ctypes.byref(cfg.c()), _ptr(q4_cache, torch.uint8, "q4_cache", dkv_q4_0_cache_bytes(cfg)),
+        _ptr(block_table, torch.int32, "block_table", _bt_numel(cfg)),
         _f16(k, "k", n), _f16(v, "v", n), _ptr(seq_lens, torch.int32, "seq_lens", cfg.batch), int(s_max),
         _stream(stream))
     _check("dkv_q4_0_encode", st)
 
 
-def dkv_q4_0_export(cfg: Config, q4_cache, seq_lens, s_max: int, codes, scales, stream=None):
+def dkv_q4_0_export(cfg: Config, q4_cache, block_table, seq_lens, s_max: int, codes, scales, stream=None):
     import torch
     B, H, D = cfg.batch, cfg.n_kv_heads, cfg.head_dim
     st = load().dkv_q4_0_export(
         ctypes.byref(cfg.c()), _ptr(q4_cache, torch.uint8, "q4_cache", dkv_q4_0_cache_bytes(cfg)),
+        _ptr(block_table, torch.int32, "block_table", _bt_numel(cfg)),
         _ptr(seq_lens, torch.int32, "seq_lens", B), int(s_max),
         _ptr(codes, torch.uint8, "codes", B * H * 2 * s_max * D // 2),
         _f16(scales, "scales", B * H * 2 * s_max * D // 32), _stream(stream))
     _check("dkv_q4_0_export", st)
 
 
-def dkv_attn_decode_q4_0(cfg: Config, q4_cache, q, seq_lens, out, workspace, softmax_scale=0.0, stream=None):
+def dkv_attn_decode_q4_0(cfg: Config, q4_cache, block_table, q, seq_lens, out, workspace, softmax_scale=0.0,
+                         stream=None):
     import torch
     B, Hq, D = cfg.batch, cfg.n_q_heads, cfg.head_dim
     st = load().dkv_attn_decode_q4_0(
-        ctypes.byref(cfg.c()), _ptr(q4_cache, torch.uint8, "q4_cache", dkv_q4_0_cache_bytes(cfg)), _ptr(q, torch.float32, "q", B * Hq * D),
+        ctypes.byref(cfg.c()), _ptr(q4_cache, torch.uint8, "q4_cache", dkv_q4_0_cache_bytes(cfg)),
+        _ptr(block_table, torch.int32, "block_table", _bt_numel(cfg)), _ptr(q, torch.float32, "q", B * Hq * D),
         _ptr(seq_lens, torch.int32, "seq_lens", B), float(softmax_scale),
         _ptr(out, torch.float32, "out", B * Hq * D), _ptr(workspace, torch.uint8, "workspace"),
         workspace.numel() if workspace is not None else 0, _stream(stream))
     _check("dkv_attn_decode_q4_0", st)
 
 
-def dkv_attn_decode_f16(cfg: Config, k, v, s_max: int, q, seq_lens, out, workspace, softmax_scale=0.0,
+def dkv_attn_decode_f16(cfg: Config, k, v, block_table, q, seq_lens, out, workspace, softmax_scale=0.0,
                         stream=None):
+    """F16 decode attention; k, v fp16 of f16_cache_shape(cfg) each."""
     import torch
     B, Hq, D = cfg.batch, cfg.n_q_heads, cfg.head_dim
-    n = B * cfg.n_kv_heads * s_max * D
+    n = math.prod(f16_cache_shape(cfg))
     st = load().dkv_attn_decode_f16(
-        ctypes.byref(cfg.c()), _f16(k, "k", n), _f16(v, "v", n), int(s_max),
+        ctypes.byref(cfg.c()), _f16(k, "k", n), _f16(v, "v", n),
+        _ptr(block_table, torch.int32, "block_table", _bt_numel(cfg)),
         _ptr(q, torch.float32, "q", B * Hq * D), _ptr(seq_lens, torch.int32, "seq_lens", B),
         float(softmax_scale), _ptr(out, torch.float32, "out", B * Hq * D),
         _ptr(workspace, torch.uint8, "workspace"), workspace.numel() if workspace is not None else 0,

@@ -72,6 +72,10 @@ def test_sizes():
     assert dkv.dkv_state_bytes(c) == 16 * 8 * 2 * 128 * 4
     assert dkv.dkv_workspace_bytes(c) > 0
     assert dkv.dkv_q4_0_cache_bytes(c) == 16 * 8 * 2 * 32768 * 128 // 32 * 18
+    # paged comparison caches: a page of 256 tokens holds 8 tiles per kv-head
+    cpg = _cfg(page_tokens=256, n_pages=5, max_pages_per_seq=3)
+    assert dkv.dkv_q4_0_cache_bytes(cpg) == 5 * 2 * 8 * 36 * 128
+    assert dkv.f16_cache_shape(cpg) == (5, 2, 256, 128) and dkv.f16_cache_shape(c) == (16, 8, 32768, 128)
     assert dkv.dkv_cache_bytes(_cfg(head_dim=96)) == 0
     # strided references: per stream 1024 fp16 reference rows, 32768 tokens of
     # 64 code bytes, 8 scale bytes and a 2-byte index, planes 256-byte aligned
@@ -103,10 +107,15 @@ def test_argument_errors_return_before_launch():
     # unsupported config propagates
     cbad = ctypes.byref(_cfg(head_dim=96).c())
     assert lib.dkv_append(cbad, fake, fake, null, fake, fake, fake, null) == binding.DKV_ERR_UNSUPPORTED
-    # Q4_0 comparison is contiguous only
-    assert lib.dkv_q4_0_encode(cpg, fake, fake, fake, fake, 10, null) == binding.DKV_ERR_UNSUPPORTED
-    # F16 comparison: s_max beyond capacity
-    assert lib.dkv_attn_decode_f16(cp, fake, fake, 5000, fake, fake, 0.0, fake, fake, 1 << 30, null) == binding.DKV_ERR_ARG
+    # comparison caches: paged mode needs a block table and 32-token-aligned pages
+    assert lib.dkv_q4_0_encode(cpg, fake, null, fake, fake, fake, 10, null) == binding.DKV_ERR_ARG
+    assert lib.dkv_attn_decode_f16(cpg, fake, fake, null, fake, fake, 0.0, fake, fake, 1 << 30,
+                                   null) == binding.DKV_ERR_ARG
+    cp16 = ctypes.byref(_cfg(kf=16, page_tokens=48, n_pages=8, max_pages_per_seq=4).c())
+    assert lib.dkv_attn_decode_q4_0(cp16, fake, fake, fake, fake, 0.0, fake, fake, 1 << 30,
+                                    null) == binding.DKV_ERR_UNSUPPORTED
+    assert dkv.dkv_q4_0_cache_bytes(_cfg(kf=16, page_tokens=48, n_pages=8, max_pages_per_seq=4)) == 0
+    assert lib.dkv_attn_decode_f16(cp, fake, fake, null, fake, fake, 0.0, fake, fake, 16, null) == binding.DKV_ERR_WORKSPACE
     # one serving step: null state / new rows, short workspace
     assert lib.dkv_append_attn_decode(cp, fake, null, null, fake, fake, fake, fake, fake, 0.0, fake, fake,
                                       1 << 30, null) == binding.DKV_ERR_ARG
@@ -160,8 +169,8 @@ def test_binding_rejects_undersized_caches():
         lambda: dkv.dkv_attn_decode_partial(c, short, None, q, lens, ws),
         lambda: dkv.dkv_reconstruct(c, short, None, lens, 4, q, q),
         lambda: dkv.dkv_export(c, short, None, lens, 4, q, q, q),
-        lambda: dkv.dkv_q4_0_export(c, torch.zeros(dkv.dkv_q4_0_cache_bytes(c) - 1, dtype=torch.uint8), lens, 4,
-                                    short, short),
+        lambda: dkv.dkv_q4_0_export(c, torch.zeros(dkv.dkv_q4_0_cache_bytes(c) - 1, dtype=torch.uint8), None, lens,
+                                    4, short, short),
     ]
     for i, f in enumerate(calls):
         with pytest.raises(ValueError, match="elements, needs"):

@@ -21,52 +21,101 @@ pytestmark = pytest.mark.gpu
 import gpu_util as U  # noqa: E402
 
 CASES = [
-    ("tiny", dict(), None),
-    ("8b", dict(S=700, Hq=8, Hkv=2), None),
-    ("8b", dict(S=400, Hq=8, Hkv=2, D=64), None),
-    ("70b", dict(S=333, B=3, Hq=16, Hkv=1), None),
-    ("8b", dict(S=300, B=6, Hq=8, Hkv=2), [0, 1, 31, 32, 33, 300]),
+    # (workload, overrides, lengths, page_tokens)
+    ("tiny", dict(), None, 0),
+    ("8b", dict(S=700, Hq=8, Hkv=2), None, 0),
+    ("8b", dict(S=400, Hq=8, Hkv=2, D=64), None, 0),
+    ("70b", dict(S=333, B=3, Hq=16, Hkv=1), None, 0),
+    ("8b", dict(S=300, B=6, Hq=8, Hkv=2), [0, 1, 31, 32, 33, 300], 0),
+    # paged: shuffled 256-token pages, lengths around the tile and page edges
+    ("8b", dict(S=700, B=6, Hq=8, Hkv=2), [0, 1, 31, 33, 256, 700], 256),
+    ("8b", dict(S=600, B=3, Hq=8, Hkv=2, D=64), [600, 255, 257], 256),
+    ("70b", dict(S=520, B=2, Hq=32, Hkv=2), [520, 64], 256),
+    ("mixed", dict(B=4, S=2100, Hq=8, Hkv=2, min_len=100, extra_tokens=0), None, 256),
 ]
 
 
-def _setup(name, kw, lens):
-    w = synth.make(name, **kw)
-    lens_np = np.asarray(w.seq_lens if lens is None else lens, np.int32)
-    cfg = dkv.Config(batch=w.B, n_q_heads=w.Hq, n_kv_heads=w.Hkv, head_dim=w.D, kf=32, max_tokens=w.S)
-    return w, lens_np, cfg
+class _Cmp:
+    pass
 
 
-def _f16_inputs(w, lens_np, poison=True):
-    """fp16 K/V on the device; rows past each sequence's length hold NaN."""
-    k = np.ascontiguousarray(w.k).copy()
-    v = np.ascontiguousarray(w.v).copy()
-    if poison:
-        for b, L in enumerate(lens_np):
-            k[b, :, L:] = np.float16(np.nan)
-            v[b, :, L:] = np.float16(np.nan)
-    return torch.from_numpy(k).to(U.DEV), torch.from_numpy(v).to(U.DEV)
+def _setup(name, kw, lens, page_tokens=0):
+    """Workload, lengths, config (contiguous or paged) and, in paged mode, a
+    shuffled block table with one extra unmapped logical page per sequence."""
+    r = _Cmp()
+    r.w = w = synth.make(name, **kw)
+    r.lens_np = np.asarray(w.seq_lens if lens is None else lens, np.int32)
+    r.bt_np = r.bt = None
+    if page_tokens:
+        need = [-(-int(L) // page_tokens) for L in r.lens_np]
+        maxp = max(need) + 1
+        perm = np.random.default_rng(17).permutation(int(sum(need))).astype(np.int32)
+        table = np.full((w.B, maxp), -1, np.int32)
+        pos = 0
+        for b, k in enumerate(need):
+            table[b, :k] = perm[pos:pos + k]
+            pos += k
+        r.cfg = dkv.Config(batch=w.B, n_q_heads=w.Hq, n_kv_heads=w.Hkv, head_dim=w.D, kf=32,
+                           page_tokens=page_tokens, n_pages=max(1, int(sum(need))), max_pages_per_seq=maxp)
+        r.bt_np = table
+        r.bt = torch.from_numpy(table).to(U.DEV)
+    else:
+        r.cfg = dkv.Config(batch=w.B, n_q_heads=w.Hq, n_kv_heads=w.Hkv, head_dim=w.D, kf=32, max_tokens=w.S)
+    r.lens = torch.from_numpy(r.lens_np).to(U.DEV)
+    return r
 
 
-def _q40_encode(w, lens_np, cfg):
-    q4 = torch.full((dkv.dkv_q4_0_cache_bytes(cfg),), 0xA5, dtype=torch.uint8, device=U.DEV)
-    k, v = _f16_inputs(w, lens_np, poison=False)
-    lens = torch.from_numpy(lens_np).to(U.DEV)
-    dkv.dkv_q4_0_encode(cfg, q4, k, v, lens, w.S)
-    return q4, lens
+def _f16_cache(r, poison=True):
+    """The F16 cache (K, V) in the comparison tile layout: contiguous, the rows
+    themselves; paged, the rows copied to their physical pages.  Rows past each
+    sequence's length (and unused page rows) hold NaN when poisoned."""
+    w, cfg = r.w, r.cfg
+    fill = np.float16(np.nan) if poison else np.float16(0)
+    out = []
+    for x in (w.k, w.v):
+        if cfg.page_tokens == 0:
+            y = np.ascontiguousarray(x).copy()
+            if poison:
+                for b, L in enumerate(r.lens_np):
+                    y[b, :, L:] = fill
+        else:
+            P = cfg.page_tokens
+            y = np.full(dkv.f16_cache_shape(cfg), fill, np.float16)
+            for b, L in enumerate(r.lens_np):
+                for lp in range(-(-int(L) // P)):
+                    n = min(P, int(L) - lp * P)
+                    y[r.bt_np[b, lp], :, :n] = x[b, :, lp * P:lp * P + n]
+        out.append(torch.from_numpy(y).to(U.DEV))
+    return out
 
 
-@pytest.mark.parametrize("name,kw,lens", CASES, ids=lambda x: str(x))
-def test_q40_encode_bit_exact(name, kw, lens):
-    w, lens_np, cfg = _setup(name, kw, lens)
-    q4, lens_t = _q40_encode(w, lens_np, cfg)
-    S, D = w.S, w.D
+def _q40_encode(r):
+    w = r.w
+    q4 = torch.full((dkv.dkv_q4_0_cache_bytes(r.cfg),), 0xA5, dtype=torch.uint8, device=U.DEV)
+    k = torch.from_numpy(np.ascontiguousarray(w.k)).to(U.DEV)
+    v = torch.from_numpy(np.ascontiguousarray(w.v)).to(U.DEV)
+    dkv.dkv_q4_0_encode(r.cfg, q4, r.bt, k, v, r.lens, w.k.shape[2])
+    return q4
+
+
+def _ids(x):
+    return str(x)
+
+
+@pytest.mark.parametrize("name,kw,lens,page_tokens", CASES, ids=_ids)
+def test_q40_encode_bit_exact(name, kw, lens, page_tokens):
+    r = _setup(name, kw, lens, page_tokens)
+    w = r.w
+    print(f"q4_0 encode {name} {kw} lens={lens} pages={page_tokens}", flush=True)
+    q4 = _q40_encode(r)
+    S, D = w.k.shape[2], w.D
     codes = torch.zeros((w.B, w.Hkv, 2, S, D // 2), dtype=torch.uint8, device=U.DEV)
     scales = torch.zeros((w.B, w.Hkv, 2, S, D // 32), dtype=torch.int16, device=U.DEV)
-    dkv.dkv_q4_0_export(cfg, q4, lens_t, S, codes, scales)
+    dkv.dkv_q4_0_export(r.cfg, q4, r.bt, r.lens, S, codes, scales)
     codes = codes.cpu().numpy()
     scales = scales.cpu().numpy().view(np.uint16)
     for b in range(w.B):
-        L = int(lens_np[b])
+        L = int(r.lens_np[b])
         for h in range(w.Hkv):
             for s, x in enumerate((w.k, w.v)):
                 oc, osc = oracle.q40_abs_stream(np.ascontiguousarray(x[b, h, :L]))
@@ -74,76 +123,128 @@ def test_q40_encode_bit_exact(name, kw, lens):
                 assert np.array_equal(scales[b, h, s, :L], osc), ("scales", b, h, s)
 
 
-@pytest.mark.parametrize("name,kw,lens", CASES, ids=lambda x: str(x))
-def test_q40_attention_parity(name, kw, lens):
-    w, lens_np, cfg = _setup(name, kw, lens)
-    q4, lens_t = _q40_encode(w, lens_np, cfg)
-    q_np = synth.queries(w)
-    q = torch.from_numpy(q_np).to(U.DEV)
-    out = torch.full((w.B, w.Hq, w.D), float("nan"), dtype=torch.float32, device=U.DEV)
-    ws = torch.zeros(dkv.dkv_workspace_bytes(cfg), dtype=torch.uint8, device=U.DEV)
-    dkv.dkv_attn_decode_q4_0(cfg, q4, q, lens_t, out, ws)
-    got = out.cpu().numpy()
+def _oracle_attention(r, q_np, rows):
+    w = r.w
     G = w.Hq // w.Hkv
     scale = np.float32(1 / math.sqrt(w.D))
     ref = np.zeros((w.B, w.Hq, w.D))
     for b in range(w.B):
-        L = int(lens_np[b])
+        L = int(r.lens_np[b])
         for h in range(w.Hkv):
-            kr = oracle.q40_dequant_stream(*oracle.q40_abs_stream(np.ascontiguousarray(w.k[b, h, :L])))
-            vr = oracle.q40_dequant_stream(*oracle.q40_abs_stream(np.ascontiguousarray(w.v[b, h, :L])))
+            kr, vr = rows(b, h, L)
             ref[b, h * G:(h + 1) * G] = oracle.attention_f64(q_np[b, h * G:(h + 1) * G], kr, vr, scale)
-    for b in range(w.B):
-        if lens_np[b] == 0:
-            assert np.all(got[b] == 0.0)
-    assert U.rel_err(got, ref) <= U.ATTN_TOL
+    return ref
 
 
-@pytest.mark.parametrize("name,kw,lens", CASES, ids=lambda x: str(x))
-def test_f16_attention_parity(name, kw, lens):
-    w, lens_np, cfg = _setup(name, kw, lens)
-    k, v = _f16_inputs(w, lens_np, poison=True)
-    lens_t = torch.from_numpy(lens_np).to(U.DEV)
+@pytest.mark.parametrize("name,kw,lens,page_tokens", CASES, ids=_ids)
+def test_q40_attention_parity(name, kw, lens, page_tokens):
+    r = _setup(name, kw, lens, page_tokens)
+    w = r.w
+    print(f"q4_0 attention {name} {kw} lens={lens} pages={page_tokens}", flush=True)
+    q4 = _q40_encode(r)
     q_np = synth.queries(w)
     q = torch.from_numpy(q_np).to(U.DEV)
     out = torch.full((w.B, w.Hq, w.D), float("nan"), dtype=torch.float32, device=U.DEV)
-    ws = torch.zeros(dkv.dkv_workspace_bytes(cfg), dtype=torch.uint8, device=U.DEV)
-    dkv.dkv_attn_decode_f16(cfg, k, v, w.S, q, lens_t, out, ws)
+    ws = torch.zeros(dkv.dkv_workspace_bytes(r.cfg), dtype=torch.uint8, device=U.DEV)
+    dkv.dkv_attn_decode_q4_0(r.cfg, q4, r.bt, q, r.lens, out, ws)
     got = out.cpu().numpy()
-    G = w.Hq // w.Hkv
-    scale = np.float32(1 / math.sqrt(w.D))
-    ref = np.zeros((w.B, w.Hq, w.D))
+
+    def rows(b, h, L):
+        return (oracle.q40_dequant_stream(*oracle.q40_abs_stream(np.ascontiguousarray(w.k[b, h, :L]))),
+                oracle.q40_dequant_stream(*oracle.q40_abs_stream(np.ascontiguousarray(w.v[b, h, :L]))))
+
+    ref = _oracle_attention(r, q_np, rows)
     for b in range(w.B):
-        L = int(lens_np[b])
-        for h in range(w.Hkv):
-            kr = w.k[b, h, :L].astype(np.float32)
-            vr = w.v[b, h, :L].astype(np.float32)
-            ref[b, h * G:(h + 1) * G] = oracle.attention_f64(q_np[b, h * G:(h + 1) * G], kr, vr, scale)
-    for b in range(w.B):
-        if lens_np[b] == 0:
+        if r.lens_np[b] == 0:
             assert np.all(got[b] == 0.0)
     assert U.rel_err(got, ref) <= U.ATTN_TOL
+
+
+@pytest.mark.parametrize("name,kw,lens,page_tokens", CASES, ids=_ids)
+def test_f16_attention_parity(name, kw, lens, page_tokens):
+    r = _setup(name, kw, lens, page_tokens)
+    w = r.w
+    print(f"f16 attention {name} {kw} lens={lens} pages={page_tokens}", flush=True)
+    k, v = _f16_cache(r, poison=True)
+    q_np = synth.queries(w)
+    q = torch.from_numpy(q_np).to(U.DEV)
+    out = torch.full((w.B, w.Hq, w.D), float("nan"), dtype=torch.float32, device=U.DEV)
+    ws = torch.zeros(dkv.dkv_workspace_bytes(r.cfg), dtype=torch.uint8, device=U.DEV)
+    dkv.dkv_attn_decode_f16(r.cfg, k, v, r.bt, q, r.lens, out, ws)
+    got = out.cpu().numpy()
+    ref = _oracle_attention(r, q_np, lambda b, h, L: (w.k[b, h, :L].astype(np.float32),
+                                                       w.v[b, h, :L].astype(np.float32)))
+    for b in range(w.B):
+        if r.lens_np[b] == 0:
+            assert np.all(got[b] == 0.0)
+    assert U.rel_err(got, ref) <= U.ATTN_TOL
+
+
+def test_paged_comparisons_skip_unmapped_pages():
+    """A sequence whose middle page is unmapped: the F16 and Q4_0 decodes
+    attend only the tokens of its mapped pages (as the Delta-KV decode does)."""
+    r = _setup("8b", dict(S=768, B=2, Hq=8, Hkv=2), [768, 500], 256)
+    w = r.w
+    table = r.bt_np.copy()
+    table[0, 1] = -1                      # tokens 256..511 of sequence 0
+    r.bt = torch.from_numpy(table).to(U.DEV)
+    r.bt_np = table
+    q_np = synth.queries(w)
+    q = torch.from_numpy(q_np).to(U.DEV)
+    ws = torch.zeros(dkv.dkv_workspace_bytes(r.cfg), dtype=torch.uint8, device=U.DEV)
+    out = torch.empty((w.B, w.Hq, w.D), dtype=torch.float32, device=U.DEV)
+    kept = {0: np.r_[0:256, 512:768], 1: np.arange(500)}
+    G = w.Hq // w.Hkv
+    scale = np.float32(1 / math.sqrt(w.D))
+    for path in ("f16", "q4_0"):
+        if path == "f16":
+            # pages of sequence 0 except the unmapped one, filled from the rows
+            k = np.zeros(dkv.f16_cache_shape(r.cfg), np.float16)
+            v = np.zeros_like(k)
+            for b, L in enumerate(r.lens_np):
+                for lp in range(-(-int(L) // 256)):
+                    if table[b, lp] < 0:
+                        continue
+                    n = min(256, int(L) - lp * 256)
+                    k[table[b, lp], :, :n] = w.k[b, :, lp * 256:lp * 256 + n]
+                    v[table[b, lp], :, :n] = w.v[b, :, lp * 256:lp * 256 + n]
+            dkv.dkv_attn_decode_f16(r.cfg, torch.from_numpy(k).to(U.DEV), torch.from_numpy(v).to(U.DEV), r.bt, q,
+                                    r.lens, out, ws)
+        else:
+            dkv.dkv_attn_decode_q4_0(r.cfg, _q40_encode(r), r.bt, q, r.lens, out, ws)
+        got = out.cpu().numpy()
+        ref = np.zeros((w.B, w.Hq, w.D))
+        for b in range(w.B):
+            for h in range(w.Hkv):
+                kx = np.ascontiguousarray(w.k[b, h, kept[b]])
+                vx = np.ascontiguousarray(w.v[b, h, kept[b]])
+                if path == "q4_0":
+                    kr = oracle.q40_dequant_stream(*oracle.q40_abs_stream(kx))
+                    vr = oracle.q40_dequant_stream(*oracle.q40_abs_stream(vx))
+                else:
+                    kr, vr = kx.astype(np.float32), vx.astype(np.float32)
+                ref[b, h * G:(h + 1) * G] = oracle.attention_f64(q_np[b, h * G:(h + 1) * G], kr, vr, scale)
+        assert U.rel_err(got, ref) <= U.ATTN_TOL, path
 
 
 def test_delta_kv_closer_to_f16_than_q40():
     """On the 1 % AR(1) data the Delta-KV attention output is closer to F16
     attention than plain Q4_0 attention is (the quality claim of the Delta-KV
     article's benchmark section, measured here on attention outputs)."""
-    w, lens_np, cfg = _setup("8b", dict(S=1024, Hq=8, Hkv=2), None)
+    r = _setup("8b", dict(S=1024, Hq=8, Hkv=2), None)
+    w = r.w
     q_np = synth.queries(w)
     q = torch.from_numpy(q_np).to(U.DEV)
-    lens_t = torch.from_numpy(lens_np).to(U.DEV)
-    ws = torch.zeros(dkv.dkv_workspace_bytes(cfg), dtype=torch.uint8, device=U.DEV)
+    ws = torch.zeros(dkv.dkv_workspace_bytes(r.cfg), dtype=torch.uint8, device=U.DEV)
     outs = {}
-    k, v = _f16_inputs(w, lens_np, poison=False)
+    k, v = _f16_cache(r, poison=False)
     out = torch.empty((w.B, w.Hq, w.D), dtype=torch.float32, device=U.DEV)
-    dkv.dkv_attn_decode_f16(cfg, k, v, w.S, q, lens_t, out, ws)
+    dkv.dkv_attn_decode_f16(r.cfg, k, v, None, q, r.lens, out, ws)
     outs["f16"] = out.cpu().numpy()
-    q4, _ = _q40_encode(w, lens_np, cfg)
-    dkv.dkv_attn_decode_q4_0(cfg, q4, q, lens_t, out, ws)
+    dkv.dkv_attn_decode_q4_0(r.cfg, _q40_encode(r), None, q, r.lens, out, ws)
     outs["q40"] = out.cpu().numpy()
-    r = U.prefill(w, kf=32)
-    outs["dkv"] = U.attention(r, q_np)
+    rr = U.prefill(w, kf=32)
+    outs["dkv"] = U.attention(rr, q_np)
     e_q = np.abs(outs["q40"] - outs["f16"]).max()
     e_d = np.abs(outs["dkv"] - outs["f16"]).max()
     assert e_d < e_q, (e_d, e_q)
@@ -159,7 +260,8 @@ def test_delta_kv_closer_to_f16_than_q40():
 def test_q8_0_encode_bit_exact(name, kw, lens):
     """Q8_0 codes and fp16 scale bit patterns equal the oracle's Q8_0 of the
     absolute rows; rows past each sequence's length keep their contents."""
-    w, lens_np, cfg = _setup(name, kw, lens)
+    r = _setup(name, kw, lens)
+    w, lens_np, cfg = r.w, r.lens_np, r.cfg
     print(f"q8_0 case {name} {kw} lens={lens}", flush=True)
     B, H, S, D = w.B, w.Hkv, w.S, w.D
     k = torch.from_numpy(np.ascontiguousarray(w.k)).to(U.DEV)

@@ -83,11 +83,11 @@ def test_q4_0_distortion_matches_oracle():
     v = torch.from_numpy(np.ascontiguousarray(w.v)).to(U.DEV)
     lens = torch.from_numpy(lens_np).to(U.DEV)
     q4 = torch.zeros(dkv.dkv_q4_0_cache_bytes(cfg), dtype=torch.uint8, device=U.DEV)
-    dkv.dkv_q4_0_encode(cfg, q4, k, v, lens, w.S)
+    dkv.dkv_q4_0_encode(cfg, q4, None, k, v, lens, w.S)
     B, H, S, D = w.B, w.Hkv, w.S, w.D
     codes = torch.zeros(B, H, 2, S, D // 2, dtype=torch.uint8, device=U.DEV)
     scales = torch.zeros(B, H, 2, S, D // 32, dtype=torch.int16, device=U.DEV)
-    dkv.dkv_q4_0_export(cfg, q4, lens, S, codes, scales)
+    dkv.dkv_q4_0_export(cfg, q4, None, lens, S, codes, scales)
     deq = []
     for s in range(2):
         c = codes[:, :, s].reshape(B, H, S, D // 32, 16)
