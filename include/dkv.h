@@ -99,8 +99,19 @@ size_t dkv_cache_bytes(const dkv_config *cfg);
  * (the last reconstructed K and V row of each sequence). */
 size_t dkv_state_bytes(const dkv_config *cfg);
 
-/* Bytes of the split-K workspace that dkv_attn_decode needs for cfg. */
+/* Bytes of the workspace the decode calls need for cfg.  Layout: one 32-bit
+ * arrival counter per (sequence, kv-head), padded to a multiple of 256 bytes,
+ * then the split-K partial records.  The counters must be zero before the
+ * first call that uses the workspace (allocate it zero-filled); every decode
+ * call leaves them at zero again.  The partial records need no initial
+ * contents. */
 size_t dkv_workspace_bytes(const dkv_config *cfg);
+
+/* Kernel launches dkv_attn_decode issues for cfg: 1 where its split kernel
+ * merges its own partial results, else 2 (split phase, combine); 0 if cfg is
+ * invalid.  dkv_append_attn_decode issues the same number, plus one for the
+ * append where it is not done inside the split launch (kf other than 32). */
+int32_t dkv_attn_decode_launches(const dkv_config *cfg);
 
 /*
  * Bulk prefill encode.  Encodes tokens [0, seq_lens[b]) of every sequence.
@@ -136,10 +147,15 @@ dkv_status dkv_append(const dkv_config *cfg, void *cache, float *state,
  *  seq_lens (device) int32 [batch]: tokens attended (0 gives a zero row)
  *  softmax_scale: logit scale; 0 means 1/sqrt(head_dim)
  *  out      (device) fp32 [batch][n_q_heads][head_dim]
- *  workspace (device) at least dkv_workspace_bytes(cfg) bytes of scratch for
- *           the split-K partial results (no initial contents needed; calls
- *           that share a workspace must not run concurrently)
- * Two launches on `stream`: the fused split phase, then the split combine.
+ *  workspace (device) at least dkv_workspace_bytes(cfg) bytes (see there:
+ *           its arrival counters start at zero; calls that share a
+ *           workspace must not run concurrently)
+ * Launches: the split phase, then the split-K combine.  Where kf is a
+ * multiple of 32 up to 512, at most 8 query heads share a kv-head and the
+ * split launch is small (at most 256 workgroups, at most 16 splits per
+ * (sequence, kv-head); on MI355X a second launch costs more than the merge
+ * there), ONE kernel: the last workgroup of each (sequence, kv-head) to finish
+ * merges that row's split-K partial results into out.
  */
 dkv_status dkv_attn_decode(const dkv_config *cfg, const void *cache,
                            const int32_t *block_table, const float *q,
@@ -154,14 +170,17 @@ dkv_status dkv_attn_decode(const dkv_config *cfg, const void *cache,
  * array of 64 MiB that the library holds in each GPU's memory (static device
  * memory, resolved once per device on the first call there, held until the
  * process ends).  It allocates nothing, on the device or the host.
- *  - Needs batch * n_q_heads * nsplit * (head_dim + 4) * 4 bytes of scratch,
- *    nsplit being dkv_attn_decode's split count (dkv_workspace_bytes(cfg) is
- *    an upper bound); a configuration needing more than 64 MiB returns
- *    DKV_ERR_SCRATCH before anything is launched.
+ *  - Needs the arrival counters (4 * batch * n_kv_heads bytes, rounded up to
+ *    256) plus batch * n_q_heads * nsplit * (head_dim + 4) * 4 bytes of
+ *    scratch, nsplit being dkv_attn_decode's split count
+ *    (dkv_workspace_bytes(cfg) is an upper bound); a configuration needing
+ *    more than 64 MiB returns DKV_ERR_SCRATCH before anything is launched.
  *  - Every call on one GPU shares that GPU's scratch array: calls that may
  *    overlap on one GPU (several streams, several host threads) race and must
  *    be serialised by the caller.  Nothing in it needs clearing: each call
- *    writes every record it reads.
+ *    writes every partial record it reads, and the arrival counters at its
+ *    start (see dkv_workspace_bytes) are zero when the library is loaded
+ *    (static device memory is zero-filled) and zero again after every call.
  *  - Errors: as dkv_attn_decode, DKV_ERR_SCRATCH, and DKV_ERR_HIP if the
  *    scratch array's device address cannot be obtained.
  */
@@ -177,8 +196,9 @@ dkv_status dkv_attn_decode_noalloc(const dkv_config *cfg, const void *cache,
  * calls.  seq_lens must already count the new token.  Where the kf = 32,
  * GQA <= 8 decode kernel runs (every benchmark workload), the append is done
  * inside its split launch by the workgroup whose run holds the new token's
- * group, before it reads that group: two launches per step (split phase,
- * combine).  Elsewhere the append kernel runs first (three launches).  The
+ * group, before it reads that group: the launches of dkv_attn_decode and no
+ * more (ONE launch per serving step where that kernel also merges its
+ * partials).  Elsewhere the append kernel runs first.  The
  * cache bytes, state and output equal those of dkv_append followed by
  * dkv_attn_decode.  Errors as those two calls.
  */
@@ -189,10 +209,14 @@ dkv_status dkv_append_attn_decode(const dkv_config *cfg, void *cache, float *sta
                                   void *workspace, size_t workspace_bytes, dkv_stream_t stream);
 
 /* The split phase of dkv_attn_decode alone: writes the per-split partial
- * results (acc[D], running max, running sum) to the workspace and launches no
- * combine.  For callers that overlap or merge the combine themselves, and for
- * timing the fused kernel on its own.  Same arguments as dkv_attn_decode
- * without `out`. */
+ * results to the workspace and merges nothing (the arrival counters are left
+ * untouched).  Partial record of (sequence b, query head hq, split s), at float
+ * offset ((b*n_q_heads + hq)*nsplit + s)*(head_dim + 4) after the counters:
+ * acc[head_dim] (sum of softmax weights times V over the split's tokens, the
+ * weights relative to the running max), running max (log2 units: logits times
+ * log2(e)), running sum, 2 pad floats.  For callers that merge the splits
+ * themselves, and for timing the split phase alone.  Same arguments as
+ * dkv_attn_decode without `out`. */
 dkv_status dkv_attn_decode_partial(const dkv_config *cfg, const void *cache,
                                    const int32_t *block_table, const float *q,
                                    const int32_t *seq_lens, float softmax_scale,

@@ -43,7 +43,7 @@ hipError_t launch_attn_fused_long(const dkv_config &, const void *, const int32_
                                   const int32_t *, float, float *, int, int, hipStream_t);
 bool fused_long_supported(const dkv_config &);
 hipError_t launch_attn_g8(const dkv_config &, const void *, const int32_t *, const float *, const int32_t *,
-                          float, float *, int, int, hipStream_t, const AppendArgs *);
+                          float, float *, int, int, hipStream_t, const AppendArgs *, CombineTail);
 bool fused_g8_supported(const dkv_config &);
 bool fused_long_g8_supported(const dkv_config &);
 hipError_t launch_q40_encode(const dkv_config &, void *, const int32_t *, const uint16_t *, const uint16_t *,
@@ -83,6 +83,17 @@ Plan delta_plan(const dkv_config &c)
     const Geom g = make_geom(c);
     return make_plan(g.ng_cap, c.batch, c.n_kv_heads, c.kf >= 2048 ? 1 : 2048 / c.kf);
 }
+// Whether the GQA <= 8 decode kernels merge their own partial records (one
+// launch per step) for plan p: only for launches of at most 256 workgroups with
+// at most 16 splits per row.  The merge is a chain of memory round trips in
+// the last workgroup of each row (records written through to memory, arrival
+// count, L2 invalidate, loads); measured on MI355X it takes longer than a
+// second launch on every larger workload (1 to 18 us per step), while on the
+// launch-bound small ones it saves the second launch (about 2 us of 15).
+static bool merge_in_kernel(const dkv_config &c, const Plan &p)
+{
+    return p.nsplit <= 16 && (int64_t)p.nsplit * c.batch * c.n_kv_heads <= 256;
+}
 // the comparison caches (32-token tiles, contiguous or paged)
 Plan tile_plan(const dkv_config &c) { return make_plan(cmp_ntiles(c), c.batch, c.n_kv_heads, 64); }
 // strided-reference decode: one wave per run, so runs of at most 16 tiles
@@ -95,13 +106,16 @@ static size_t ws_for(const dkv_config &c, const Plan &p)
 {
     return (size_t)c.batch * c.n_q_heads * p.nsplit * part_stride(c.head_dim) * sizeof(float);
 }
+// [arrival counters, counter_bytes(c)][partial records of the largest plan]
 static size_t workspace_total(const dkv_config &c)
 {
     const size_t a = ws_for(c, delta_plan(c));
     const size_t b = (c.page_tokens == 0 || c.page_tokens % 32 == 0) ? ws_for(c, tile_plan(c)) : 0;
     const size_t d = c.page_tokens == 0 ? ws_for(c, strided_plan(c)) : 0;
-    return a > b ? (a > d ? a : d) : (b > d ? b : d);
+    return (size_t)counter_bytes(c) + (a > b ? (a > d ? a : d) : (b > d ? b : d));
 }
+// the partial records start after the arrival counters
+static float *partials(const dkv_config &c, void *ws) { return (float *)((uint8_t *)ws + counter_bytes(c)); }
 
 static dkv_status hip_status(hipError_t e) { return e == hipSuccess ? DKV_OK : DKV_ERR_HIP; }
 
@@ -111,8 +125,9 @@ static float resolve_scale(const dkv_config &c, float s)
     return sc * 1.4426950408889634f;     // logits kept in log2 units
 }
 
-// Bytes of split-K partials the decode (dkv_attn_decode's split plan) writes for c.
-size_t decode_partials_bytes(const dkv_config &c) { return ws_for(c, delta_plan(c)); }
+// Workspace bytes dkv_attn_decode uses for c: the arrival counters and its
+// split plan's partial records.
+size_t decode_partials_bytes(const dkv_config &c) { return (size_t)counter_bytes(c) + ws_for(c, delta_plan(c)); }
 
 // The decode of dkv_attn_decode after its argument checks: split phase into
 // `ws` (at least decode_partials_bytes(c) bytes), then the combine.
@@ -185,6 +200,13 @@ size_t dkv_workspace_bytes(const dkv_config *c)
     return workspace_total(*c);
 }
 
+int32_t dkv_attn_decode_launches(const dkv_config *c)
+{
+    if (dkv_check_config(c) != DKV_OK) return 0;
+    const bool g8 = fused_g8_supported(*c) || fused_long_g8_supported(*c);
+    return g8 && merge_in_kernel(*c, delta_plan(*c)) ? 1 : 2;
+}
+
 dkv_status dkv_encode_prefill(const dkv_config *c, void *cache, float *state, const int32_t *bt,
                               const uint16_t *k, const uint16_t *v, const int32_t *lens, int32_t s_max,
                               dkv_stream_t stream)
@@ -223,26 +245,33 @@ static dkv_status attn_common(const dkv_config *c, const void *cache, const int3
 // With `ap` (non-null positions), each sequence's new token is appended first:
 // inside the split kernel where the kf = 32, GQA <= 8 kernel runs, else by the
 // append kernel ahead of it.
+// With `out`, the split kernel merges its own partials into out where that is
+// faster (the GQA <= 8 kernels on small launches, merge_in_kernel): one
+// launch; *merged tells whether it did, else the caller launches the combine.
 static hipError_t launch_split_phase(const dkv_config &c, const void *cache, const int32_t *bt, const float *q,
                                      const int32_t *lens, float scale, void *ws, const Plan &p, hipStream_t st,
-                                     const AppendArgs *ap = nullptr)
+                                     const AppendArgs *ap = nullptr, float *out = nullptr, bool *merged = nullptr)
 {
     const int32_t *btp = c.page_tokens > 0 ? bt : nullptr;
+    float *part = partials(c, ws);
+    if (merged) *merged = false;
     if (ap && !fused_g8_supported(c)) {
         const hipError_t e = launch_append(c, ap->cache, ap->state, btp, ap->knew, ap->vnew, ap->positions, st);
         if (e != hipSuccess) return e;
         ap = nullptr;
     }
-    if (fused_g8_supported(c) || fused_long_g8_supported(c))
-        return launch_attn_g8(c, cache, btp, q, lens, resolve_scale(c, scale), (float *)ws, p.nsplit, p.chunk, st,
-                              ap);
+    if (fused_g8_supported(c) || fused_long_g8_supported(c)) {
+        const bool mk = out != nullptr && merge_in_kernel(c, p);
+        const CombineTail ct{mk ? out : nullptr, mk ? (uint32_t *)ws : nullptr};
+        if (merged) *merged = mk;
+        return launch_attn_g8(c, cache, btp, q, lens, resolve_scale(c, scale), part, p.nsplit, p.chunk, st, ap, ct);
+    }
     if (fused_supported(c))
-        return launch_attn_fused(c, cache, btp, q, lens, resolve_scale(c, scale), (float *)ws, p.nsplit, p.chunk,
-                                 st);
+        return launch_attn_fused(c, cache, btp, q, lens, resolve_scale(c, scale), part, p.nsplit, p.chunk, st);
     if (fused_long_supported(c))
-        return launch_attn_fused_long(c, cache, btp, q, lens, resolve_scale(c, scale), (float *)ws, p.nsplit,
-                                      p.chunk, st);
-    return launch_attn_ref(c, cache, btp, q, lens, resolve_scale(c, scale), (float *)ws, p.nsplit, p.chunk, st);
+        return launch_attn_fused_long(c, cache, btp, q, lens, resolve_scale(c, scale), part, p.nsplit, p.chunk,
+                                      st);
+    return launch_attn_ref(c, cache, btp, q, lens, resolve_scale(c, scale), part, p.nsplit, p.chunk, st);
 }
 
 dkv_status dkv_attn_decode(const dkv_config *c, const void *cache, const int32_t *bt, const float *q,
@@ -264,9 +293,11 @@ dkv_status dkv_append_attn_decode(const dkv_config *c, void *cache, float *state
     if (!state || !k || !v || !pos) return DKV_ERR_ARG;
     const Plan p = delta_plan(*c);
     const AppendArgs ap{(uint8_t *)cache, state, k, v, pos};
-    hipError_t e = launch_split_phase(*c, cache, bt, q, lens, scale, ws, p, (hipStream_t)stream, &ap);
+    bool merged = false;
+    hipError_t e = launch_split_phase(*c, cache, bt, q, lens, scale, ws, p, (hipStream_t)stream, &ap, out, &merged);
     if (e != hipSuccess) return DKV_ERR_HIP;
-    return hip_status(launch_combine(*c, (const float *)ws, p.nsplit, out, (hipStream_t)stream));
+    if (merged) return DKV_OK;
+    return hip_status(launch_combine(*c, partials(*c, ws), p.nsplit, out, (hipStream_t)stream));
 }
 
 dkv_status dkv_attn_decode_partial(const dkv_config *c, const void *cache, const int32_t *bt, const float *q,
@@ -286,10 +317,10 @@ dkv_status dkv_attn_decode_ref(const dkv_config *c, const void *cache, const int
     if (st != DKV_OK) return st;
     const Plan p = delta_plan(*c);
     hipError_t e = launch_attn_ref(*c, cache, c->page_tokens > 0 ? bt : nullptr, q, lens,
-                                   resolve_scale(*c, scale), (float *)ws, p.nsplit, p.chunk,
+                                   resolve_scale(*c, scale), partials(*c, ws), p.nsplit, p.chunk,
                                    (hipStream_t)stream);
     if (e != hipSuccess) return DKV_ERR_HIP;
-    return hip_status(launch_combine(*c, (const float *)ws, p.nsplit, out, (hipStream_t)stream));
+    return hip_status(launch_combine(*c, partials(*c, ws), p.nsplit, out, (hipStream_t)stream));
 }
 
 dkv_status dkv_reconstruct(const dkv_config *c, const void *cache, const int32_t *bt, const int32_t *lens,
@@ -393,9 +424,9 @@ dkv_status dkv_attn_decode_q4_0(const dkv_config *c, const void *q4, const int32
     const Plan p = tile_plan(*c);
     if (!ws || ws_bytes < workspace_total(*c)) return DKV_ERR_WORKSPACE;
     hipError_t e = launch_attn_q40(*c, q4, c->page_tokens > 0 ? bt : nullptr, q, lens, resolve_scale(*c, scale),
-                                   (float *)ws, p.nsplit, p.chunk, (hipStream_t)stream);
+                                   partials(*c, ws), p.nsplit, p.chunk, (hipStream_t)stream);
     if (e != hipSuccess) return DKV_ERR_HIP;
-    return hip_status(launch_combine(*c, (const float *)ws, p.nsplit, out, (hipStream_t)stream));
+    return hip_status(launch_combine(*c, partials(*c, ws), p.nsplit, out, (hipStream_t)stream));
 }
 
 dkv_status dkv_attn_decode_f16(const dkv_config *c, const uint16_t *k, const uint16_t *v, const int32_t *bt,
@@ -408,9 +439,9 @@ dkv_status dkv_attn_decode_f16(const dkv_config *c, const uint16_t *k, const uin
     const Plan p = tile_plan(*c);
     if (!ws || ws_bytes < workspace_total(*c)) return DKV_ERR_WORKSPACE;
     hipError_t e = launch_attn_f16(*c, k, v, c->page_tokens > 0 ? bt : nullptr, q, lens, resolve_scale(*c, scale),
-                                   (float *)ws, p.nsplit, p.chunk, (hipStream_t)stream);
+                                   partials(*c, ws), p.nsplit, p.chunk, (hipStream_t)stream);
     if (e != hipSuccess) return DKV_ERR_HIP;
-    return hip_status(launch_combine(*c, (const float *)ws, p.nsplit, out, (hipStream_t)stream));
+    return hip_status(launch_combine(*c, partials(*c, ws), p.nsplit, out, (hipStream_t)stream));
 }
 
 // ---------------------------------------------------------- strided references
@@ -467,10 +498,10 @@ dkv_status dkv_strided_attn_decode(const dkv_config *c, const void *cache, const
     if (!cache || !q || !lens || !out) return DKV_ERR_ARG;
     if (!ws || ws_bytes < workspace_total(*c)) return DKV_ERR_WORKSPACE;
     const Plan p = strided_plan(*c);
-    hipError_t e = launch_strided_attn(*c, cache, q, lens, resolve_scale(*c, scale), (float *)ws, p.nsplit, p.chunk,
+    hipError_t e = launch_strided_attn(*c, cache, q, lens, resolve_scale(*c, scale), partials(*c, ws), p.nsplit, p.chunk,
                                        nullptr, nullptr, nullptr, 0, (hipStream_t)stream);
     if (e != hipSuccess) return DKV_ERR_HIP;
-    return hip_status(launch_combine(*c, (const float *)ws, p.nsplit, out, (hipStream_t)stream));
+    return hip_status(launch_combine(*c, partials(*c, ws), p.nsplit, out, (hipStream_t)stream));
 }
 
 dkv_status dkv_strided_append_attn_decode(const dkv_config *c, void *cache, const uint16_t *k_new,
@@ -483,10 +514,10 @@ dkv_status dkv_strided_append_attn_decode(const dkv_config *c, void *cache, cons
     if (!cache || !k_new || !v_new || !positions || window < 0 || !q || !lens || !out) return DKV_ERR_ARG;
     if (!ws || ws_bytes < workspace_total(*c)) return DKV_ERR_WORKSPACE;
     const Plan p = strided_plan(*c);
-    hipError_t e = launch_strided_attn(*c, cache, q, lens, resolve_scale(*c, scale), (float *)ws, p.nsplit, p.chunk,
+    hipError_t e = launch_strided_attn(*c, cache, q, lens, resolve_scale(*c, scale), partials(*c, ws), p.nsplit, p.chunk,
                                        k_new, v_new, positions, window, (hipStream_t)stream);
     if (e != hipSuccess) return DKV_ERR_HIP;
-    return hip_status(launch_combine(*c, (const float *)ws, p.nsplit, out, (hipStream_t)stream));
+    return hip_status(launch_combine(*c, partials(*c, ws), p.nsplit, out, (hipStream_t)stream));
 }
 
 }  // extern "C"
@@ -504,7 +535,9 @@ dkv_status dkv::attn_decode_launch(const dkv_config &c, const void *cache, const
                                    const int32_t *lens, float scale, float *out, void *ws, hipStream_t st)
 {
     const Plan p = delta_plan(c);
-    hipError_t e = launch_split_phase(c, cache, bt, q, lens, scale, ws, p, st);
+    bool merged = false;
+    hipError_t e = launch_split_phase(c, cache, bt, q, lens, scale, ws, p, st, nullptr, out, &merged);
     if (e != hipSuccess) return DKV_ERR_HIP;
-    return hip_status(launch_combine(c, (const float *)ws, p.nsplit, out, st));
+    if (merged) return DKV_OK;
+    return hip_status(launch_combine(c, partials(c, ws), p.nsplit, out, st));
 }

@@ -524,12 +524,48 @@ __device__ inline void init_state(RunState<D> &st)
     st.bsc = 0x1p127f;
 }
 
+// The split-K combine as the kernel's tail (one launch per decode step), used
+// where the launch is small enough that a second kernel launch costs more than
+// the tail (the host picks it).  Every workgroup of a (sequence, kv-head) row
+// writes its partial records for the row's G query heads and counts its
+// arrival; the last of the row's nsplit workgroups resets the counter for the
+// next call and merges the records into out.  The row's workgroups run on
+// different XCDs, each with its own L2, so the records are published at device
+// scope: written with device-scope (sc1) stores, which write through the
+// writer's L2; the writer waits for them to complete (vmcnt(0)) before it
+// counts its arrival; the merging workgroup's agent-scope acquire fence drops
+// stale lines from its own L1 and L2 before it reads them.  (An agent-scope
+// release fence in every workgroup instead writes back the whole L2, and
+// device-scope loads instead of the acquire fence were slower still.)
+constexpr int kCpolSc1 = 16;        // buffer cache-policy bit of gfx950: sc1 (device scope)
+
+__device__ inline __amdgpu_buffer_rsrc_t ws_rsrc(const float *base, int nbytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, nbytes, 0x00020000);
+}
+// Record stores: write-through (wt) when the kernel merges its own records.
+__device__ inline void store_rec4(float *p, f4 v, bool wt)
+{
+    if (wt)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), ws_rsrc(p, 16), 0, 0, kCpolSc1);
+    else
+        *(f4 *)p = v;
+}
+__device__ inline void store_rec2(float *p, float a, float b, bool wt)
+{
+    if (wt)
+        __builtin_amdgcn_raw_buffer_store_b64(u2{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b)},
+                                              ws_rsrc(p, 8), 0, 0, kCpolSc1);
+    else
+        *(f2 *)p = f2{a, b};
+}
+
 // Split-K partial record of the wave's run: lane (j, n) keeps rows 4j..4j+3
 // of each V slice; they belong to its column half's block when
 // (j < 2) == (h2 == 0).
 template <int D>
 __device__ inline void write_partial_g8(const RunState<D> &st, float *ws, int64_t row0, int G, int nsplit, int split,
-                                        int lane, int j, int n)
+                                        int lane, int j, int n, bool wt)
 {
     constexpr int NCC = D / 16;
     const int h2 = n >> 3, hq = n & 7;
@@ -542,13 +578,99 @@ __device__ inline void write_partial_g8(const RunState<D> &st, float *ws, int64_
             f4 o;
 #pragma unroll
             for (int i = 0; i < 4; ++i) o[i] = (st.acc[cc][i] + st.Z[cc >> 2][i]) * un;
-            *(f4 *)(recp + vchan(D, cc, 4 * j, 1)) = o;
+            store_rec4(recp + vchan(D, cc, 4 * j, 1), o, wt);
         }
     }
-    if (lane == hq) {
-        recp[D] = st.m;
-        recp[D + 1] = st.l;
+    if (lane == hq) store_rec2(recp + D, st.m, st.l, wt);
+}
+
+// Merge of one row by the last workgroup, in one pass over the splits (running
+// max in log2 units, the sums rescaled when it grows; splits with l = 0, i.e.
+// runs past the end or on unmapped pages, are skipped; an empty row gives
+// zeros).  The row's G heads are spread over the wave: GP = G rounded up to a
+// power of two, 64/GP lanes per head, CPL = D*GP/64 channels per lane, so every
+// lane carries the same running max and sum as the other lanes of its head and
+// no lane-to-lane reduction is needed.  UB splits are loaded per batch, all
+// their loads in flight before the first is used (each batch costs one round
+// trip to the memory side).
+template <int D, int GP>
+__device__ __forceinline__ void merge_row_gp(const float *ws, float *out, int64_t row0, int G, int nsplit, int lane)
+{
+    constexpr int R = part_stride(D), LPH = 64 / GP, CPL = D / LPH;
+    constexpr int UB = CPL >= 16 ? 8 : 16;
+    const int hq = lane / LPH, sub = lane % LPH;
+    const int hqc = hq < G ? hq : 0;          // lanes past the group read head 0 and discard it
+    const float *rec0 = ws + (row0 + hqc) * nsplit * R;
+    float M = -INFINITY, den = 0.0f;
+    float num[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) num[c] = 0.0f;
+    for (int s0 = 0; s0 < nsplit; s0 += UB) {
+        f2 ml[UB];
+        float a[UB][CPL];
+#pragma unroll
+        for (int u = 0; u < UB; ++u) {
+            const float *r = rec0 + (int64_t)min(s0 + u, nsplit - 1) * R;
+            ml[u] = *(const f2 *)(r + D);
+            if constexpr (CPL >= 4) {
+#pragma unroll
+                for (int k = 0; k < CPL / 4; ++k) {
+                    const f4 v = *(const f4 *)(r + sub * CPL + 4 * k);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) a[u][4 * k + i] = v[i];
+                }
+            } else if constexpr (CPL == 2) {
+                const f2 v = *(const f2 *)(r + sub * CPL);
+                a[u][0] = v[0];
+                a[u][1] = v[1];
+            } else {
+                a[u][0] = r[sub];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < UB; ++u) {
+            const float m = ml[u][0], l = ml[u][1];
+            if (s0 + u < nsplit && l > 0.0f) {
+                const float mn = fmaxf(M, m);
+                const float al = exp2f(M - mn), w = exp2f(m - mn);
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) num[c] = fmaf(w, a[u][c], num[c] * al);
+                den = fmaf(w, l, den * al);
+                M = mn;
+            }
+        }
     }
+    if (hq >= G) return;
+    float *o = out + (row0 + hq) * D + sub * CPL;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) o[c] = den > 0.0f ? num[c] / den : 0.0f;
+}
+
+template <int D>
+__device__ __forceinline__ void merge_row_g8(const float *ws, float *out, int64_t row0, int G, int nsplit, int lane)
+{
+    if (G > 4) merge_row_gp<D, 8>(ws, out, row0, G, nsplit, lane);
+    else if (G > 2) merge_row_gp<D, 4>(ws, out, row0, G, nsplit, lane);
+    else if (G > 1) merge_row_gp<D, 2>(ws, out, row0, G, nsplit, lane);
+    else merge_row_gp<D, 1>(ws, out, row0, G, nsplit, lane);
+}
+
+// After write_partial_g8 with wt = true: count this workgroup's arrival; the
+// last of the row merges.
+template <int D>
+__device__ __forceinline__ void combine_tail_g8(const float *ws, const CombineTail &tl, int64_t row0, int G, int nsplit,
+                                       int64_t pair, int lane)
+{
+    __builtin_amdgcn_s_waitcnt(0x0F70);          // vmcnt(0): the write-through record stores have completed
+    __syncthreads();
+    uint32_t *ctr = tl.counter + pair;
+    uint32_t old = 0;
+    if (lane == 0) old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    old = __builtin_amdgcn_readfirstlane(old);
+    if (old != (uint32_t)(nsplit - 1)) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    if (lane == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    merge_row_g8<D>(ws, tl.out, row0, G, nsplit, lane);
 }
 
 // "-8" operand of the V side: -8 * 2^-24 * f(hh) as fp16 subnormals
@@ -695,7 +817,7 @@ template <int D>
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
     k_attn_g8(dkv_config cfg, const uint8_t *cache, const int32_t *__restrict__ bt,
               const float *__restrict__ q, const int32_t *__restrict__ seq_lens, float scale_log2,
-              float *__restrict__ ws, int nsplit, int chunk, AppendArgs ap)
+              float *ws, int nsplit, int chunk, AppendArgs ap, CombineTail ct)
 {
     constexpr int NB = D / 32, NCC = D / 16;
     constexpr int SIDE_LANES = D / 4;
@@ -748,7 +870,8 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
         // a run past the sequence's end (or wholly unmapped): an empty record
         RunState<D> st;
         init_state<D>(st);
-        write_partial_g8<D>(st, ws, row0, G, nsplit, split, lane, j, n);
+        write_partial_g8<D>(st, ws, row0, G, nsplit, split, lane, j, n, ct.out != nullptr);
+        if (ct.out) combine_tail_g8<D>(ws, ct, row0, G, nsplit, (int64_t)b * g.Hkv + h, lane);
         return;
     }
     if (o0 >= 0) glist[__builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mk, 0u))] = o0;
@@ -915,7 +1038,8 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
         update_g8_vmx<D>(st, m, group_vmax<D>(sbp(nfull)), 5, kfw);
         v_phase_g8<D, false, true>(st, vr.vc, sbp(nfull) + 4 * D, Lg, nval, j, n, c2Eu, AZ, -0.0f);
     }
-    write_partial_g8<D>(st, ws, row0, G, nsplit, split, lane, j, n);
+    write_partial_g8<D>(st, ws, row0, G, nsplit, split, lane, j, n, ct.out != nullptr);
+    if (ct.out) combine_tail_g8<D>(ws, ct, row0, G, nsplit, (int64_t)b * g.Hkv + h, lane);
 }
 
 // ==================================================================== kf = 32*NT
@@ -932,7 +1056,7 @@ template <int D>
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
     k_attn_long_g8(dkv_config cfg, const uint8_t *__restrict__ cache, const int32_t *__restrict__ bt,
                    const float *__restrict__ q, const int32_t *__restrict__ seq_lens, float scale_log2,
-                   float *__restrict__ ws, int nsplit, int chunk)
+                   float *ws, int nsplit, int chunk, CombineTail ct)
 {
     constexpr int NB = D / 32, NCC = D / 16;
     const Geom g = make_geom(cfg);
@@ -1165,14 +1289,17 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
         }
         __builtin_amdgcn_s_setprio(0);
     }
-    write_partial_g8<D>(st, ws, row0, G, nsplit, split, lane, j, n);
+    write_partial_g8<D>(st, ws, row0, G, nsplit, split, lane, j, n, ct.out != nullptr);
+    if (ct.out) combine_tail_g8<D>(ws, ct, row0, G, nsplit, (int64_t)b * g.Hkv + h, lane);
 }
 
 // With `append` (kf = 32 only), the kernel appends each sequence's new token
 // before it decodes: append->positions null means no append.
+// With `tail` (non-null out), the kernel also merges the partial records
+// into out (one launch per decode step).
 hipError_t launch_attn_g8(const dkv_config &c, const void *cache, const int32_t *bt, const float *q,
                           const int32_t *lens, float scale_log2, float *ws, int nsplit, int chunk, hipStream_t st,
-                          const AppendArgs *append)
+                          const AppendArgs *append, CombineTail ct)
 {
     dim3 grid(nsplit, c.n_kv_heads, c.batch);
     if (c.kf == 32) {
@@ -1180,10 +1307,10 @@ hipError_t launch_attn_g8(const dkv_config &c, const void *cache, const int32_t 
         const AppendArgs ap = append ? *append : AppendArgs{nullptr, nullptr, nullptr, nullptr, nullptr};
         if (c.head_dim == 64)
             hipLaunchKernelGGL(k_attn_g8<64>, grid, dim3(64), 0, st, c, (const uint8_t *)cache, bt, q, lens,
-                               scale_log2, ws, nsplit, chunk, ap);
+                               scale_log2, ws, nsplit, chunk, ap, ct);
         else
             hipLaunchKernelGGL(k_attn_g8<128>, grid, dim3(64), 0, st, c, (const uint8_t *)cache, bt, q, lens,
-                               scale_log2, ws, nsplit, chunk, ap);
+                               scale_log2, ws, nsplit, chunk, ap, ct);
     } else {
         if (append && append->positions) return hipErrorInvalidValue;     // the long-interval kernel does not append
         if (chunk > 64) return hipErrorInvalidValue;     // a run's groups are counted over one wave
@@ -1193,10 +1320,10 @@ hipError_t launch_attn_g8(const dkv_config &c, const void *cache, const int32_t 
         const size_t lds = (c.n_q_heads / c.n_kv_heads <= 4 ? (size_t)nt * 32 + 1 : (size_t)nt * 64) * sizeof(f4);
         if (c.head_dim == 64)
             hipLaunchKernelGGL(k_attn_long_g8<64>, grid, dim3(64), lds, st, c, (const uint8_t *)cache, bt, q, lens,
-                               scale_log2, ws, nsplit, chunk);
+                               scale_log2, ws, nsplit, chunk, ct);
         else
             hipLaunchKernelGGL(k_attn_long_g8<128>, grid, dim3(64), lds, st, c, (const uint8_t *)cache, bt, q, lens,
-                               scale_log2, ws, nsplit, chunk);
+                               scale_log2, ws, nsplit, chunk, ct);
     }
     return hipGetLastError();
 }
@@ -1333,7 +1460,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
         while (step(ra, rb) && step(rb, ra)) {
         }
     }
-    write_partial_g8<D>(st, ws, row0, G, nsplit, split, lane, j, n);
+    write_partial_g8<D>(st, ws, row0, G, nsplit, split, lane, j, n, false);
 }
 
 hipError_t launch_attn_q40_g8(const dkv_config &c, const void *q4, const int32_t *bt, const float *q,

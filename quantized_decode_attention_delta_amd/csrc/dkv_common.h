@@ -36,6 +36,23 @@ __host__ __device__ inline int64_t pad16(int64_t x) { return (x + 15) & ~int64_t
 // max (log2 units), running sum, two pad floats (16-byte aligned records).
 __host__ __device__ constexpr int part_stride(int D) { return D + 4; }
 
+// Workspace of the decode calls: first one 32-bit arrival counter per
+// (sequence, kv-head) (zero between calls: the split kernels that merge their
+// own partials count their arrivals there and the last one resets it), padded
+// to 256 bytes, then the split-K partial records.
+__host__ __device__ inline int64_t counter_bytes(const dkv_config &c)
+{
+    return ((int64_t)c.batch * c.n_kv_heads * 4 + 255) & ~int64_t(255);
+}
+
+// Where a split kernel that merges its own partial records writes the result:
+// out[B][Hq][D]; counter[B][Hkv] are the arrival counters.  out == nullptr:
+// partial records only (a separate combine kernel merges them).
+struct CombineTail {
+    float *out;
+    uint32_t *counter;
+};
+
 struct Geom {
     int D, nb, kf, Hkv, Hq, G, B;
     int ntiles_v;              // 32-token tiles of V codes per group

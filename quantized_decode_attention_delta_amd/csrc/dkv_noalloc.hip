@@ -55,6 +55,8 @@ extern "C" dkv_status dkv_attn_decode_noalloc(const dkv_config *c, const void *c
     void *ws = dkv::scratch_on_current_device();
     if (!ws) return DKV_ERR_HIP;
     // every partial record the combine reads is written by the split phase of
-    // the same call, so nothing in the array needs clearing between calls
+    // the same call, and the arrival counters at the array's start are zero
+    // from the load of the library (zero-filled static memory) and left at
+    // zero by every call, so nothing in the array needs clearing
     return dkv::attn_decode_launch(*c, cache, bt, q, lens, scale, out, ws, (hipStream_t)stream);
 }

@@ -65,6 +65,7 @@ _SIGS = {
     "dkv_cache_bytes": ([_CFG], _SZ),
     "dkv_state_bytes": ([_CFG], _SZ),
     "dkv_workspace_bytes": ([_CFG], _SZ),
+    "dkv_attn_decode_launches": ([_CFG], _I32),
     "dkv_encode_prefill": ([_CFG, _P, _P, _P, _P, _P, _P, _I32, _P], _I32),
     "dkv_append": ([_CFG, _P, _P, _P, _P, _P, _P, _P], _I32),
     "dkv_attn_decode": ([_CFG, _P, _P, _P, _P, _F, _P, _P, _SZ, _P], _I32),
@@ -136,6 +137,10 @@ def dkv_state_bytes(cfg: Config) -> int:
 
 def dkv_workspace_bytes(cfg: Config) -> int:
     return load().dkv_workspace_bytes(ctypes.byref(cfg.c()))
+
+
+def dkv_attn_decode_launches(cfg: Config) -> int:
+    return load().dkv_attn_decode_launches(ctypes.byref(cfg.c()))
 
 
 def dkv_q4_0_cache_bytes(cfg: Config) -> int:

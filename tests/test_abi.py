@@ -71,6 +71,13 @@ def test_sizes():
     assert dkv.dkv_cache_bytes(c) == 16 * 8 * 1024 * rec
     assert dkv.dkv_state_bytes(c) == 16 * 8 * 2 * 128 * 4
     assert dkv.dkv_workspace_bytes(c) > 0
+    # one launch (the split kernel merges its own partials) only on small
+    # launches: at most 16 splits per row and 256 workgroups
+    assert dkv.dkv_attn_decode_launches(c) == 2
+    assert dkv.dkv_attn_decode_launches(_cfg(batch=1, n_q_heads=1, n_kv_heads=1, head_dim=64, max_tokens=256)) == 1
+    assert dkv.dkv_attn_decode_launches(_cfg(batch=1, n_q_heads=32, n_kv_heads=8, max_tokens=4096)) == 2
+    assert dkv.dkv_attn_decode_launches(_cfg(batch=1, n_q_heads=32, n_kv_heads=8, max_tokens=512)) == 1
+    assert dkv.dkv_attn_decode_launches(_cfg(head_dim=96)) == 0
     assert dkv.dkv_q4_0_cache_bytes(c) == 16 * 8 * 2 * 32768 * 128 // 32 * 18
     # paged comparison caches: a page of 256 tokens holds 8 tiles per kv-head
     cpg = _cfg(page_tokens=256, n_pages=5, max_pages_per_seq=3)

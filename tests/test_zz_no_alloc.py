@@ -3,8 +3,9 @@ in the library's fixed device scratch array) against dkv_attn_decode with a
 caller-owned workspace, through the C ABI: two calls in a row on one GPU, the
 second with a smaller input, each output bit-identical to dkv_attn_decode's
 (same kernels and split plan) and within 2e-3 of the float64 oracle on
-sampled rows.  The reference workspace is filled with NaN bytes, so neither
-path may read partial records it has not written."""
+sampled rows.  The reference workspace's partial records are filled with NaN
+bytes (its arrival counters with zeros), so neither path may read partial
+records it has not written."""
 import math
 
 import numpy as np
@@ -25,6 +26,7 @@ def _one_call(w, kf, page_tokens, pairs):
     q_np = synth.queries(w)
     q = torch.from_numpy(q_np).to(U.DEV)
     ws = torch.full((dkv.dkv_workspace_bytes(r.cfg),), 0xFF, dtype=torch.uint8, device=U.DEV)
+    ws[:(r.cfg.batch * r.cfg.n_kv_heads * 4 + 255) // 256 * 256] = 0      # arrival counters start at zero
     ref = torch.empty(w.B, w.Hq, w.D, dtype=torch.float32, device=U.DEV)
     got = torch.full_like(ref, float("nan"))
     dkv.dkv_attn_decode(r.cfg, r.cache, r.bt, q, r.lens, ref, ws)
