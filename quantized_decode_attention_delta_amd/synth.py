@@ -28,7 +28,9 @@ because the cache API takes fp16 K/V.  Queries are fp32 N(0,1).
 """
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
+import threading
 
 import numpy as np
 from scipy.signal import lfilter
@@ -96,9 +98,12 @@ def _ar1_stream_block(rng, T, H, D, sigma, scales, jump_p=0.0, jump_sigma=0.0):
     return z
 
 
-def make(name: str, seed: int = 0, progress=None, **over) -> Workload:
+def make(name: str, seed: int = 0, progress=None, workers: int = 1, **over) -> Workload:
     """Build a workload.  Keyword overrides (B, S, Hq, Hkv, D, kf, ...) shrink it.
-    ``progress(b)``, if given, is called after each sequence of the mixed workload."""
+    ``progress(n)``, if given, is called with the number of sequences done after
+    each sequence of the mixed workload.  ``workers`` > 1 draws the sequences on
+    that many host threads; every sequence has its own generator, so the arrays
+    do not depend on it."""
     p = default_sizes(name)
     p.update(over)
     B, Hq, Hkv, D, S, kf = p["B"], p["Hq"], p["Hkv"], p["D"], p["S"], p["kf"]
@@ -117,9 +122,17 @@ def make(name: str, seed: int = 0, progress=None, **over) -> Workload:
     k = np.zeros((B, Hkv, T, D), np.float16)
     v = np.zeros((B, Hkv, T, D), np.float16)
 
-    if name == "tiny":
-        for b in range(B):
-            rng = rngs[b]
+    scales = None
+    if name in ("8b", "long"):
+        scales = np.exp(meta_rng.standard_normal((2, Hkv, D)))
+    elif name not in ("tiny", "70b", "mixed"):
+        raise ValueError(name)
+    done = [0]
+    lock = threading.Lock()
+
+    def fill(b):
+        rng = rngs[b]
+        if name == "tiny":
             x = np.zeros((2, Hkv, T, D), np.float32)
             x[:, :, 0] = rng.standard_normal((2, Hkv, D), dtype=np.float32)
             eps = rng.standard_normal((T, 2, Hkv, D), dtype=np.float32)
@@ -127,22 +140,14 @@ def make(name: str, seed: int = 0, progress=None, **over) -> Workload:
                 prev = x[:, :, t - 1]
                 x[:, :, t] = prev + np.float32(0.01) * np.abs(prev) * eps[t]
             k[b], v[b] = x[0].astype(np.float16), x[1].astype(np.float16)
-    elif name in ("8b", "long", "70b"):
-        if name == "70b":
-            scales = None
-        else:
-            scales = np.exp(meta_rng.standard_normal((2, Hkv, D)))
-        jp, js = (0.01, 0.5) if name == "long" else (0.0, 0.0)
-        for b in range(B):
-            z = _ar1_stream_block(rngs[b], T, Hkv, D, 0.01, scales, jp, js)
+        elif name in ("8b", "long", "70b"):
+            jp, js = (0.01, 0.5) if name == "long" else (0.0, 0.0)
+            z = _ar1_stream_block(rng, T, Hkv, D, 0.01, scales, jp, js)
             k[b] = z[0].astype(np.float16)
             v[b] = z[1].astype(np.float16)
-    elif name == "mixed":
-        half = B // 2
-        for b in range(B):
-            rng = rngs[b]
+        else:
             Tb = int(seq_lens[b]) + extra
-            if b < half:
+            if b < B // 2:
                 P = int(rng.integers(8, 65))
                 tmpl = rng.standard_normal((2, Hkv, P, D))
                 idx_t = np.arange(Tb) % P
@@ -163,9 +168,16 @@ def make(name: str, seed: int = 0, progress=None, **over) -> Workload:
             k[b, :, :Tb] = x[0].astype(np.float16)
             v[b, :, :Tb] = x[1].astype(np.float16)
             if progress is not None:
-                progress(b)
+                with lock:
+                    done[0] += 1
+                    progress(done[0])
+
+    if workers > 1 and B > 1:
+        with concurrent.futures.ThreadPoolExecutor(min(workers, B)) as ex:
+            list(ex.map(fill, range(B)))
     else:
-        raise ValueError(name)
+        for b in range(B):
+            fill(b)
 
     return Workload(name=name, B=B, Hq=Hq, Hkv=Hkv, D=D, S=S, kf=kf, seq_lens=seq_lens,
                     k=k, v=v, page_tokens=page_tokens, extra_tokens=extra, seed=seed)
