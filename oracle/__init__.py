@@ -16,6 +16,10 @@ Canonical encoded layout of one stream (what every function here produces):
 with ``n_delta = S - ceil(S/kf)``; delta token t sits at row
 ``(t//kf)*(kf-1) + t%kf - 1``.
 
+``q4k_encode_stream`` is the Q4-keyframe variant: the keyframe itself is
+stored as Q4_0 of its absolute values, so every token is one plain Q4_0 row
+(``codes`` [S, D/2], ``scales`` [S, D/32]); with kf = 1 it is plain Q4_0.
+
 ``strided_encode_stream`` is the strided-reference variant: every token's Q4_0
 residual against the nearest of the references at positions 0, stride, ...
 (fp16 rows kept exactly), with the reference index stored per token.
@@ -77,10 +81,14 @@ def _load():
     lib.oracle_sqdist_f16.argtypes = [P, P, I]
     lib.oracle_sqdist_f16.restype = ctypes.c_double
     lib.oracle_strided_encode_stream.argtypes = [P, L, I, I, I, P, P, P, P, P]
+    lib.oracle_q4k_step.argtypes = [P, L, I, I, P, P, P]
+    lib.oracle_q4k_encode_stream.argtypes = [P, L, I, I, P, P, P, P]
+    lib.oracle_q4k_reconstruct_stream.argtypes = [P, P, L, I, I, P]
     for name in ("oracle_step", "oracle_encode_stream", "oracle_reconstruct_stream",
                  "oracle_q40_abs_stream", "oracle_q40_dequant_stream", "oracle_attention_f64",
                  "oracle_q40_pack", "oracle_q40_unpack", "oracle_q80_block", "oracle_q80_abs_stream",
-                 "oracle_q80_dequant_stream", "oracle_strided_encode_stream"):
+                 "oracle_q80_dequant_stream", "oracle_strided_encode_stream", "oracle_q4k_step",
+                 "oracle_q4k_encode_stream", "oracle_q4k_reconstruct_stream"):
         getattr(lib, name).restype = None
     _lib = lib
     return lib
@@ -202,6 +210,67 @@ def q40_dequant_stream(codes, scales) -> np.ndarray:
     S, D = codes.shape[0], codes.shape[1] * 2
     out = np.zeros((S, D), np.float32)
     _load().oracle_q40_dequant_stream(_p(codes), _p(scales), S, D, _p(out))
+    return out
+
+
+class Q4KStream:
+    """One stream of the Q4-keyframe variant: ``codes`` uint8 [S, D/2] and
+    ``scales`` uint16 [S, D/32] (one plain-Q4_0 row per token), the
+    reconstruction ``recon`` float32 [S, D] and the final ``state`` [D]."""
+    __slots__ = ("codes", "scales", "recon", "state", "S", "D", "kf")
+
+    def __init__(self, S, D, kf):
+        self.S, self.D, self.kf = S, D, kf
+        self.codes = np.zeros((S, D // 2), np.uint8)
+        self.scales = np.zeros((S, D // 32), np.uint16)
+        self.recon = None
+        self.state = np.zeros(D, np.float32)
+
+
+def q4k_encode_stream(x, kf: int, want_recon: bool = True) -> Q4KStream:
+    """Q4-keyframe encode of one stream x[S][D] (fp16): the row at every
+    multiple of kf is Q4_0 of its absolute values, every other row Q4_0 of
+    its closed-loop delta ([DKV] "핵심 아이디어", "벤치마크")."""
+    x = _as_f16_bits(x)
+    S, D = x.shape
+    assert D % 32 == 0 and kf >= 1
+    e = Q4KStream(S, D, kf)
+    if want_recon:
+        e.recon = np.zeros((S, D), np.float32)
+    _load().oracle_q4k_encode_stream(_p(x), S, D, kf, _p(e.codes), _p(e.scales),
+                                     _p(e.recon) if want_recon else None, _p(e.state))
+    return e
+
+
+def q4k_step(e: Q4KStream, x_row, t: int, xh: np.ndarray) -> None:
+    """Append token t of a Q4-keyframe stream into its arrays (in place)."""
+    x_row = _as_f16_bits(x_row)
+    assert xh.dtype == np.float32 and xh.flags["C_CONTIGUOUS"]
+    _load().oracle_q4k_step(_p(x_row), t, e.D, e.kf, _p(e.codes), _p(e.scales), _p(xh))
+
+
+def q4k_reconstruct_stream(codes, scales, kf: int) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = _as_f16_bits(scales)
+    S, D = codes.shape[0], codes.shape[1] * 2
+    out = np.zeros((S, D), np.float32)
+    _load().oracle_q4k_reconstruct_stream(_p(codes), _p(scales), S, D, kf, _p(out))
+    return out
+
+
+def q4k_encode_cache(k, v, seq_lens, kf: int, want_recon: bool = True):
+    """Q4-keyframe encode of every stream of fp16 K/V [B][Hkv][s_max][D]:
+    a dict of Q4KStream keyed (b, h, s), s = 0 for K and 1 for V (usable with
+    attention_cache)."""
+    k = _as_f16_bits(k)
+    v = _as_f16_bits(v)
+    B, H, _, D = k.shape
+    out = {}
+    for b in range(B):
+        S = int(seq_lens[b])
+        for h in range(H):
+            for s, x in ((0, k), (1, v)):
+                out[(b, h, s)] = q4k_encode_stream(np.ascontiguousarray(x[b, h, :S]), kf, want_recon)
     return out
 
 

@@ -30,7 +30,11 @@
  *  - reconstruction: xhat_t = fp32(xhat_{t-1} + (code-8)*float(s16)), one
  *    rounding per token and channel, folded left to right from the keyframe;
  *  - attention: float64 over the reconstructed fp32 rows, scale given in fp32;
- *    an empty sequence yields a zero output row.
+ *    an empty sequence yields a zero output row;
+ *  - Q4-keyframe variant ([DKV] "벤치마크": the same 4-bit storage as Q4_0):
+ *    the keyframe row is coded as Q4_0 against a zero reference and decoded
+ *    as 0 + (code-8)*scale; every other row as in the delta rule above, so
+ *    each row is one plain Q4_0 row and kf = 1 is plain Q4_0.
  */
 #include <math.h>
 #include <stdint.h>
@@ -251,6 +255,76 @@ void oracle_q40_dequant_stream(const uint8_t *codes, const uint16_t *scales,
                 out[t * (long)D + 32 * b + j] = (float)((int)q[j] - 8) * sf;
         }
     }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Q4-keyframe variant: the keyframe itself stored as Q4_0 of its absolute    */
+/* values, so every row of a stream takes the 4-bit storage of Q4_0 ([DKV]    */
+/* "벤치마크": Delta-KV keeps Q4_0's storage at 4 bits).  Row t of a stream:   */
+/*   reference r_t = 0 when t % kf == 0 (a keyframe), else xhat_{t-1};        */
+/*   d_t = x_t - r_t, quantised one Q4_0 block per 32 channels;               */
+/*   xhat_t = fp32(r_t + (code-8)*float(s16)), one rounding per channel.      */
+/* Storage per row: codes [D/2] and scales [D/32] exactly as a plain Q4_0 row */
+/* (18 bytes per 32 values); with kf = 1 every row is a keyframe and the     */
+/* stream is plain Q4_0 of x.                                                 */
+/* ------------------------------------------------------------------------ */
+
+void oracle_q4k_step(const uint16_t *x, long t, int D, int kf, uint8_t *codes, uint16_t *scales, float *xh)
+{
+    int key = (t % kf) == 0;
+    float d[32];
+    uint8_t q[32];
+    for (int b = 0; b < D / 32; ++b) {
+        for (int j = 0; j < 32; ++j) {
+            int c = 32 * b + j;
+            float ref = key ? 0.0f : xh[c];
+            d[j] = oracle_f16_to_f32(x[c]) - ref;
+        }
+        uint16_t s16;
+        oracle_q40_block(d, &s16, q);
+        scales[t * (long)(D / 32) + b] = s16;
+        oracle_q40_pack(q, codes + t * (long)(D / 2) + 16 * b);
+        float sf = oracle_f16_to_f32(s16);
+        for (int j = 0; j < 32; ++j) {
+            int c = 32 * b + j;
+            float ref = key ? 0.0f : xh[c];
+            float step = (float)((int)q[j] - 8) * sf;     /* exact product */
+            xh[c] = ref + step;                            /* one rounding */
+        }
+    }
+}
+
+void oracle_q4k_encode_stream(const uint16_t *x, long S, int D, int kf, uint8_t *codes, uint16_t *scales,
+                              float *recon, float *state)
+{
+    float *xh = (float *)calloc((size_t)D, sizeof(float));
+    for (long t = 0; t < S; ++t) {
+        oracle_q4k_step(x + t * (long)D, t, D, kf, codes, scales, xh);
+        if (recon) memcpy(recon + t * (long)D, xh, sizeof(float) * (size_t)D);
+    }
+    if (state) memcpy(state, xh, sizeof(float) * (size_t)D);
+    free(xh);
+}
+
+/* Decoder of the Q4-keyframe stream: the same recurrence read back. */
+void oracle_q4k_reconstruct_stream(const uint8_t *codes, const uint16_t *scales, long S, int D, int kf, float *out)
+{
+    float *xh = (float *)calloc((size_t)D, sizeof(float));
+    uint8_t q[32];
+    for (long t = 0; t < S; ++t) {
+        int key = (t % kf) == 0;
+        for (int b = 0; b < D / 32; ++b) {
+            oracle_q40_unpack(codes + t * (long)(D / 2) + 16 * b, q);
+            float sf = oracle_f16_to_f32(scales[t * (long)(D / 32) + b]);
+            for (int j = 0; j < 32; ++j) {
+                int c = 32 * b + j;
+                float ref = key ? 0.0f : xh[c];
+                xh[c] = ref + (float)((int)q[j] - 8) * sf;
+            }
+        }
+        memcpy(out + t * (long)D, xh, sizeof(float) * (size_t)D);
+    }
+    free(xh);
 }
 
 /* ------------------------------------------------------------------------ */
