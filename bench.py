@@ -329,7 +329,7 @@ def cpu_baseline(w, kf, lens, q, gpu_out, budget_s, threads):
 
 
 # ------------------------------------------------------------ quality report
-def quality_sums(cfg, cache, q4, bt, k, v, lens, q, s_max):
+def quality_sums(cfg, cache, q4, bt, k, v, lens, q, s_max, q4k=None, cfg_q4k=None):
     """Squared errors against the fp16 input over every valid token, and sums of
     the attention-preserving distortions over (sequence, query head), from the
     GPU's own outputs: Delta-KV via dkv_reconstruct, Q4_0 via dkv_q4_0_export,
@@ -385,6 +385,13 @@ def quality_sums(cfg, cache, q4, bt, k, v, lens, q, s_max):
     del c8, s8
     res["q8_0"] = [sse(deq8[0], k), sse(deq8[1], v)]
     res["dist_q8_0"] = distortion(deq8[0], deq8[1])
+    del deq8
+    if q4k is not None:
+        kr = torch.empty(B, H, S, D, dtype=torch.float32, device=dev)
+        vr = torch.empty_like(kr)
+        dkv.dkv_q4k_reconstruct(cfg_q4k, q4k, bt, lens, S, kr, vr)
+        res["q4k"] = [sse(kr, k), sse(vr, v)]
+        res["dist_q4k"] = distortion(kr, vr)
     return res
 
 
@@ -401,7 +408,14 @@ def quality_report(parts):
     md, mq, m8 = mse("delta_kv"), mse("q4_0"), mse("q8_0")
     dd, dq, d8 = dist("dist_delta_kv"), dist("dist_q4_0"), dist("dist_q8_0")
     a, b = sum(md) / 2, sum(mq) / 2
-    return {"mse_delta_kv": a, "mse_q4_0": b, "ratio_q4_0_over_delta_kv": round(b / a, 2) if a > 0 else None,
+    extra = {}
+    if all("q4k" in p for p in parts):
+        mk, dk_ = mse("q4k"), dist("dist_q4k")
+        extra = {"mse_q4k_kf32": sum(mk) / 2, "mse_q4k_kf32_kv": mk,
+                 "d_k_q4k_kf32": dk_[0], "d_v_q4k_kf32": dk_[1],
+                 "q4k_how": "Q4-keyframe variant at kf 32: keyframes as Q4_0 of their absolute values, "
+                            "4.5 bits per value like Q4_0 (dkv_q4k_reconstruct)"}
+    return {**extra, "mse_delta_kv": a, "mse_q4_0": b, "ratio_q4_0_over_delta_kv": round(b / a, 2) if a > 0 else None,
             "mse_delta_kv_kv": md, "mse_q4_0_kv": mq, "mse_q8_0": sum(m8) / 2, "mse_q8_0_kv": m8,
             "attention_distortion": {
                 "d_k_delta_kv": dd[0], "d_v_delta_kv": dd[1], "d_k_q4_0": dq[0], "d_v_q4_0": dq[1],
@@ -593,7 +607,22 @@ def static_comparisons(w, cfg, k, v, q, lens, ws, steps, stream, qo, delta_out):
                    "bytes": q4_bytes, "replicas": reps}
     res["q4_0_vs_f16_attention_max_rel_err"] = rel_err_rows(out, f16_out)
     del q4s
-    return res, q4
+    # the Q4-keyframe variant at kf 32 (same 4.5-bit storage as Q4_0)
+    c32 = dkv.Config(batch=w.B, n_q_heads=w.Hq, n_kv_heads=w.Hkv, head_dim=w.D, kf=32, max_tokens=w.S)
+    q4k = torch.empty(dkv.dkv_q4_0_cache_bytes(c32), dtype=torch.uint8, device=k.device)
+    st = torch.zeros(w.B, w.Hkv, 2, w.D, dtype=torch.float32, device=k.device)
+    dkv.dkv_q4k_encode_prefill(c32, q4k, st, None, k, v, lens, w.S)
+    reps = max(1, math.ceil((1 << 30) / q4k.numel()))
+    q4ks = [q4k] + [q4k.clone() for _ in range(reps - 1)]
+    ms = _time(lambda i: dkv.dkv_attn_decode_q4k(c32, q4ks[i % reps], None, q, lens, out, ws), steps, stream)
+    res["q4k_kf32"] = {"ms_per_step": round(ms, 5), "GBps": round((q4_bytes + qo) / (ms * 1e-3) / 1e9, 2),
+                       "hbm_frac": round((q4_bytes + qo) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                       "bytes": q4_bytes, "replicas": reps,
+                       "how": "dkv_attn_decode_q4k: Q4-keyframe variant at kf 32 (keyframes as Q4_0 of their "
+                              "absolute values)"}
+    res["q4k_kf32_vs_f16_attention_max_rel_err"] = rel_err_rows(out, f16_out)
+    del q4ks
+    return res, q4, (q4k, c32)
 
 
 def static_config(w, kf, args, label, traffic_key, graph=0, strided_on=False, compare=True):
@@ -690,11 +719,12 @@ def static_config(w, kf, args, label, traffic_key, graph=0, strided_on=False, co
     if graph > 0 and fused:
         res["graph_layers"] = graph_layers(cfg, caches, q, lens, graph, stream)
     if compare:
-        res["comparisons"], q4 = static_comparisons(w, cfg, k, v, q, lens, ws, args.steps, stream, qo, delta_out)
+        res["comparisons"], q4, (q4k, c32) = static_comparisons(w, cfg, k, v, q, lens, ws, args.steps, stream, qo,
+                                                                delta_out)
         res["comparisons"]["delta_kv"] = {"ms_per_step": res["ms_per_step"], "GBps": res["compressed_GBps"],
                                           "hbm_frac": res["hbm_frac_step"], "bytes": comp}
-        res["quality"] = quality_report([quality_sums(cfg, cache0, q4, None, k, v, lens, q, w.S)])
-        del q4
+        res["quality"] = quality_report([quality_sums(cfg, cache0, q4, None, k, v, lens, q, w.S, q4k, c32)])
+        del q4, q4k
         if strided_on and w.S <= 65536 * kf:
             res["comparisons"]["strided"], res["quality"]["strided"] = strided(w, k, v, q, lens, args.steps, stream,
                                                                               qo)
@@ -750,6 +780,14 @@ def mixed_comparisons(w, cfg, bt, k, v, lens, q, ws, cache, steps, stream, s_max
     res["q4_0"] = {"ms_per_step": round(ms, 5), "GBps": round((q4_bytes + qo) / (ms * 1e-3) / 1e9, 2),
                    "hbm_frac": round((q4_bytes + qo) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4), "bytes": q4_bytes}
     res["q4_0_vs_f16_attention_max_rel_err"] = rel_err_rows(out, f16_out)
+    q4k = torch.zeros(dkv.dkv_q4_0_cache_bytes(cfg), dtype=torch.uint8, device=dev)
+    st = torch.zeros(w.B, w.Hkv, 2, w.D, dtype=torch.float32, device=dev)
+    dkv.dkv_q4k_encode_prefill(cfg, q4k, st, bt, k, v, lens, s_max)
+    ms = _time(lambda i: dkv.dkv_attn_decode_q4k(cfg, q4k, bt, q, lens, out, ws), steps, stream)
+    res["q4k_kf32"] = {"ms_per_step": round(ms, 5), "GBps": round((q4_bytes + qo) / (ms * 1e-3) / 1e9, 2),
+                       "hbm_frac": round((q4_bytes + qo) / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                       "bytes": q4_bytes, "how": "dkv_attn_decode_q4k: Q4-keyframe variant at kf 32"}
+    res["q4k_kf32_vs_f16_attention_max_rel_err"] = rel_err_rows(out, f16_out)
     res["how"] = ("paged caches (the same shuffled 256-token pages), the prefilled batch before any append, "
                   "the first step's queries; each kernel timed back to back with HIP events")
     parts = []
@@ -760,8 +798,9 @@ def mixed_comparisons(w, cfg, bt, k, v, lens, q, ws, cache, steps, stream, s_max
                         page_tokens=cfg.page_tokens, n_pages=cfg.n_pages, max_pages_per_seq=cfg.max_pages_per_seq)
         S = int(lens_np[b0:b1].max())
         parts.append(quality_sums(cs, cache, q4, bt[b0:b1].contiguous(), k[b0:b1, :, :S].contiguous(),
-                                  v[b0:b1, :, :S].contiguous(), lens[b0:b1].contiguous(), q[b0:b1].contiguous(), S))
-    del q4
+                                  v[b0:b1, :, :S].contiguous(), lens[b0:b1].contiguous(), q[b0:b1].contiguous(), S,
+                                  q4k, cs))
+    del q4, q4k
     qual = quality_report(parts)
     qual["how"] = "every sequence of the prefilled batch, sub-batches of 8 sequences"
     return res, qual

@@ -293,6 +293,48 @@ dkv_status dkv_q4_0_export(const dkv_config *cfg, const void *q4_cache, const in
                            uint16_t *scales, dkv_stream_t stream);
 
 /*
+ * Q4-keyframe variant of the Delta-KV cache: the keyframe itself is stored as
+ * Q4_0 of its absolute values, so every token takes the 4-bit storage of
+ * Q4_0 (Delta-KV article, "벤치마크": the same 4-bit storage).  Token t of a
+ * stream is one Q4_0 row (18 bytes per 32 values): at t % kf == 0 the row is
+ * coded against zero, otherwise its closed-loop delta against the running
+ * reconstruction, with the block rule of the Delta-KV codec; the
+ * reconstruction is ref + (code - 8) * scale, ref = 0 at a keyframe, else the
+ * previous reconstruction (one fp32 rounding).  With kf = 1 the cache is plain
+ * Q4_0 byte for byte.
+ * Layout and size: those of the plain Q4_0 cache (dkv_q4_0_cache_bytes, 32-token
+ * tiles, contiguous or paged with page_tokens % 32 == 0); dkv_q4_0_export
+ * gives its canonical codes and scales.  state: as dkv_state_bytes (the last
+ * reconstructed K and V row of each sequence).
+ * kf must divide 32 or be a multiple of 32 (else DKV_ERR_UNSUPPORTED); paged
+ * mode also needs page_tokens % kf == 0 (dkv_check_config).
+ */
+/* Bulk prefill encode: arguments as dkv_encode_prefill, cache of
+ * dkv_q4_0_cache_bytes(cfg) bytes. */
+dkv_status dkv_q4k_encode_prefill(const dkv_config *cfg, void *cache, float *state,
+                                  const int32_t *block_table, const uint16_t *k,
+                                  const uint16_t *v, const int32_t *seq_lens, int32_t s_max,
+                                  dkv_stream_t stream);
+/* One token per sequence: arguments as dkv_append (negative position skips). */
+dkv_status dkv_q4k_append(const dkv_config *cfg, void *cache, float *state,
+                          const int32_t *block_table, const uint16_t *k_new,
+                          const uint16_t *v_new, const int32_t *positions, dkv_stream_t stream);
+/* Reconstructed K and V of tokens [0, min(seq_lens[b], s_max)): k_out, v_out
+ * (device) fp32 [batch][n_kv_heads][s_max][head_dim]; other rows untouched. */
+dkv_status dkv_q4k_reconstruct(const dkv_config *cfg, const void *cache,
+                               const int32_t *block_table, const int32_t *seq_lens, int32_t s_max,
+                               float *k_out, float *v_out, dkv_stream_t stream);
+/* Decode attention over the Q4-keyframe cache; arguments as dkv_attn_decode.
+ * kf = 1 (plain Q4_0) or kf = 32, at most 8 query heads per kv-head; else
+ * DKV_ERR_UNSUPPORTED.  Two launches: split phase (logits by prefix sums and
+ * weights by suffix sums over each 32-token tile, as in the Delta-KV kernel),
+ * then the split combine. */
+dkv_status dkv_attn_decode_q4k(const dkv_config *cfg, const void *cache,
+                               const int32_t *block_table, const float *q,
+                               const int32_t *seq_lens, float softmax_scale, float *out,
+                               void *workspace, size_t workspace_bytes, dkv_stream_t stream);
+
+/*
  * Decode attention over an F16 cache (the unquantised baseline): k and v are
  * two arrays of fp16 token rows in the tile layout above, i.e. (device)
  *  contiguous: fp16 [batch][n_kv_heads][max_tokens][head_dim];

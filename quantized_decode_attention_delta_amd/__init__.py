@@ -14,4 +14,5 @@ from .dkv import (  # noqa: F401
     dkv_attn_decode_f16, f16_cache_shape, dkv_stream_read_sink_words, dkv_stream_read, dkv_attn_distortion,
     dkv_q8_0_encode, dkv_strided_cache_bytes, dkv_strided_layout, dkv_strided_encode_prefill,
     dkv_strided_attn_decode, dkv_strided_append, dkv_strided_append_attn_decode,
+    dkv_q4k_encode_prefill, dkv_q4k_append, dkv_q4k_reconstruct, dkv_attn_decode_q4k,
 )

@@ -52,6 +52,14 @@ hipError_t launch_q40_export(const dkv_config &, const void *, const int32_t *, 
                              uint16_t *, hipStream_t);
 hipError_t launch_attn_q40(const dkv_config &, const void *, const int32_t *, const float *, const int32_t *, float,
                            float *, int, int, hipStream_t);
+hipError_t launch_q4k_encode(const dkv_config &, void *, float *, const int32_t *, const uint16_t *,
+                             const uint16_t *, const int32_t *, int, hipStream_t);
+hipError_t launch_q4k_append(const dkv_config &, void *, float *, const int32_t *, const uint16_t *,
+                             const uint16_t *, const int32_t *, hipStream_t);
+hipError_t launch_q4k_reconstruct(const dkv_config &, const void *, const int32_t *, const int32_t *, int, float *,
+                                  float *, hipStream_t);
+hipError_t launch_attn_q4k(const dkv_config &, const void *, const int32_t *, const float *, const int32_t *, float,
+                           float *, int, int, hipStream_t);
 hipError_t launch_attn_f16(const dkv_config &, const uint16_t *, const uint16_t *, const int32_t *, const float *,
                            const int32_t *, float, float *, int, int, hipStream_t);
 
@@ -424,6 +432,66 @@ dkv_status dkv_attn_decode_q4_0(const dkv_config *c, const void *q4, const int32
     const Plan p = tile_plan(*c);
     if (!ws || ws_bytes < workspace_total(*c)) return DKV_ERR_WORKSPACE;
     hipError_t e = launch_attn_q40(*c, q4, c->page_tokens > 0 ? bt : nullptr, q, lens, resolve_scale(*c, scale),
+                                   partials(*c, ws), p.nsplit, p.chunk, (hipStream_t)stream);
+    if (e != hipSuccess) return DKV_ERR_HIP;
+    return hip_status(launch_combine(*c, partials(*c, ws), p.nsplit, out, (hipStream_t)stream));
+}
+
+// ------------------------------------------------------- Q4-keyframe variant
+// The plain Q4_0 tile layout and size; groups must lie in whole tiles.
+static dkv_status q4k_check(const dkv_config *c, const int32_t *bt)
+{
+    dkv_status st = cmp_check(c, bt);
+    if (st != DKV_OK) return st;
+    if (32 % c->kf != 0 && c->kf % 32 != 0) return DKV_ERR_UNSUPPORTED;
+    return DKV_OK;
+}
+
+dkv_status dkv_q4k_encode_prefill(const dkv_config *c, void *cache, float *state, const int32_t *bt,
+                                  const uint16_t *k, const uint16_t *v, const int32_t *lens, int32_t s_max,
+                                  dkv_stream_t stream)
+{
+    dkv_status st = q4k_check(c, bt);
+    if (st != DKV_OK) return st;
+    if (!cache || !state || !k || !v || !lens || s_max < 0) return DKV_ERR_ARG;
+    if (s_max == 0) return DKV_OK;
+    return hip_status(launch_q4k_encode(*c, cache, state, c->page_tokens > 0 ? bt : nullptr, k, v, lens, s_max,
+                                        (hipStream_t)stream));
+}
+
+dkv_status dkv_q4k_append(const dkv_config *c, void *cache, float *state, const int32_t *bt, const uint16_t *k_new,
+                          const uint16_t *v_new, const int32_t *positions, dkv_stream_t stream)
+{
+    dkv_status st = q4k_check(c, bt);
+    if (st != DKV_OK) return st;
+    if (!cache || !state || !k_new || !v_new || !positions) return DKV_ERR_ARG;
+    return hip_status(launch_q4k_append(*c, cache, state, c->page_tokens > 0 ? bt : nullptr, k_new, v_new, positions,
+                                        (hipStream_t)stream));
+}
+
+dkv_status dkv_q4k_reconstruct(const dkv_config *c, const void *cache, const int32_t *bt, const int32_t *lens,
+                               int32_t s_max, float *k_out, float *v_out, dkv_stream_t stream)
+{
+    dkv_status st = q4k_check(c, bt);
+    if (st != DKV_OK) return st;
+    if (!cache || !lens || !k_out || !v_out || s_max < 0) return DKV_ERR_ARG;
+    if (s_max == 0) return DKV_OK;
+    return hip_status(launch_q4k_reconstruct(*c, cache, c->page_tokens > 0 ? bt : nullptr, lens, s_max, k_out, v_out,
+                                             (hipStream_t)stream));
+}
+
+dkv_status dkv_attn_decode_q4k(const dkv_config *c, const void *cache, const int32_t *bt, const float *q,
+                               const int32_t *lens, float scale, float *out, void *ws, size_t ws_bytes,
+                               dkv_stream_t stream)
+{
+    dkv_status st = q4k_check(c, bt);
+    if (st != DKV_OK) return st;
+    if (c->kf != 1 && c->kf != 32) return DKV_ERR_UNSUPPORTED;
+    if (!q40_vbp(*c)) return DKV_ERR_UNSUPPORTED;           // at most 8 query heads per kv-head
+    if (!cache || !q || !lens || !out) return DKV_ERR_ARG;
+    const Plan p = tile_plan(*c);
+    if (!ws || ws_bytes < workspace_total(*c)) return DKV_ERR_WORKSPACE;
+    hipError_t e = launch_attn_q4k(*c, cache, c->page_tokens > 0 ? bt : nullptr, q, lens, resolve_scale(*c, scale),
                                    partials(*c, ws), p.nsplit, p.chunk, (hipStream_t)stream);
     if (e != hipSuccess) return DKV_ERR_HIP;
     return hip_status(launch_combine(*c, partials(*c, ws), p.nsplit, out, (hipStream_t)stream));

@@ -1192,9 +1192,12 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
                            (gridDim.x * gridDim.y * gridDim.z) / 2;
         const int ntmax = (kf + 31) >> 5;
         const int run_steps = (g1 - g0) * 2 * ntmax;
+        // quarter marks of the run (step counts), computed once: no division per step
+        const int q1 = (run_steps + 3) / 4, q2 = (2 * run_steps + 3) / 4, q3 = (3 * run_steps + 3) / 4;
         auto set_priority = [&](int gc, int s) {
             const int done = (gc - g0) * 2 * ntmax + s;
-            const int lvl = 3 - min(3, (4 * done) / run_steps) - (older ? 1 : 0);
+            const int quarters = (done >= q1) + (done >= q2) + (done >= q3);
+            const int lvl = 3 - quarters - (older ? 1 : 0);
             if (lvl <= 0)
                 __builtin_amdgcn_s_setprio(0);
             else if (lvl == 1)
@@ -1332,7 +1335,11 @@ hipError_t launch_attn_g8(const dkv_config &c, const void *cache, const int32_t 
 // The same layout tricks on the plain Q4_0 comparison cache: one 32-token tile
 // per step, the next tile fetched while the current one is processed.  The
 // tile's largest |V scale| (the V weight range) is reduced over the wave.
-template <int D>
+// DELTA: the Q4-keyframe cache at kf = 32 in the same tiles (row 0 of each tile
+// coded against zero, rows 1..31 closed-loop deltas): the logits take prefix
+// sums and the weights suffix sums over the tile, both starting at zero, and
+// the V weight range allows suffix sums of up to 32 weights.
+template <int D, bool DELTA>
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
     k_attn_q40_g8(dkv_config cfg, const uint8_t *__restrict__ q4, const int32_t *__restrict__ bt,
                   const float *__restrict__ q, const int32_t *__restrict__ seq_lens, float scale_log2,
@@ -1355,8 +1362,8 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
     // listed with their byte offsets; paged mode may leave pages unmapped
     __shared__ int64_t toffs[64];
     __shared__ int tnum[64];
-    int ntl;
-    {
+    int ntl = max(t1 - t0, 0);              // contiguous: every tile of the run is mapped
+    if (bt) {
         const int x = t0 + lane;
         const int64_t o = x < t1 ? q40_tile_offset(cfg, bt, b, h, x) : -1;
         const uint64_t mk = __ballot(o >= 0);
@@ -1385,7 +1392,8 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
     const int ov = 20 * D + (j * 16 + n) * (D / 16) * 4;
     auto load_tile = [&](G8Regs<D> &r, int k) {
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(q4 + uniform_offset(toffs, k)), (short)0, tbytes, 0x00020000);
+            (void *)(q4 + (bt ? uniform_offset(toffs, k) : q40_tile_offset(cfg, nullptr, b, h, t0 + k))), (short)0,
+            tbytes, 0x00020000);
         r.side = __builtin_amdgcn_raw_buffer_load_b128(rs, so, 0, kStream);
         if constexpr (NB == 4) {
             const u4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, ok0, 0, kStream);
@@ -1413,7 +1421,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
         }
     };
     auto run = [&](const G8Regs<D> &r, int k) {
-        const int tl = __builtin_amdgcn_readfirstlane(tnum[k]);
+        const int tl = bt ? __builtin_amdgcn_readfirstlane(tnum[k]) : t0 + k;    // contiguous: every tile mapped
         __syncthreads();
         if (lane < D / 2) ((u4 *)side)[fresh_lane_id()] = r.side;
         __syncthreads();
@@ -1436,15 +1444,15 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
         const u4 *none = sh.qz;
         float mt;
         if (nval == 32)
-            mt = k_phase_g8<D, true, false, false>(r.kc, sb, none, nval, j, n, op, c2E, 0.0f, Lg, tot);
+            mt = k_phase_g8<D, true, false, DELTA>(r.kc, sb, none, nval, j, n, op, c2E, 0.0f, Lg, tot);
         else
-            mt = k_phase_g8<D, false, false, false>(r.kc, sb, none, nval, j, n, op, c2E, 0.0f, Lg, tot);
+            mt = k_phase_g8<D, false, false, DELTA>(r.kc, sb, none, nval, j, n, op, c2E, 0.0f, Lg, tot);
         float no_kf = 0.0f;
-        update_g8_vmx<D>(st, mt, vmx, 0, no_kf);
+        update_g8_vmx<D>(st, mt, vmx, DELTA ? 5 : 0, no_kf);       // weights (suffix sums) <= 2^lkf
         if (nval == 32)
-            v_phase_g8<D, true, false, false>(st, r.vc, sb + 4 * D, Lg, nval, j, n, c2E, AZ, 0.0f);
+            v_phase_g8<D, true, false, DELTA>(st, r.vc, sb + 4 * D, Lg, nval, j, n, c2E, AZ, 0.0f);
         else
-            v_phase_g8<D, false, false, false>(st, r.vc, sb + 4 * D, Lg, nval, j, n, c2E, AZ, 0.0f);
+            v_phase_g8<D, false, false, DELTA>(st, r.vc, sb + 4 * D, Lg, nval, j, n, c2E, AZ, 0.0f);
     };
     if (ntl > 0) {
         G8Regs<D> ra, rb;
@@ -1463,17 +1471,29 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
     write_partial_g8<D>(st, ws, row0, G, nsplit, split, lane, j, n, false);
 }
 
+// delta: the Q4-keyframe cache at kf = 32 (see the kernel)
 hipError_t launch_attn_q40_g8(const dkv_config &c, const void *q4, const int32_t *bt, const float *q,
-                              const int32_t *lens, float scale_log2, float *ws, int nsplit, int chunk, hipStream_t st)
+                              const int32_t *lens, float scale_log2, float *ws, int nsplit, int chunk, hipStream_t st,
+                              bool delta)
 {
     if (chunk > 64) return hipErrorInvalidValue;      // the kernel lists at most 64 tiles per run
     dim3 grid(nsplit, c.n_kv_heads, c.batch);
-    if (c.head_dim == 64)
-        hipLaunchKernelGGL(k_attn_q40_g8<64>, grid, dim3(64), 0, st, c, (const uint8_t *)q4, bt, q, lens, scale_log2,
-                           ws, nsplit, chunk);
-    else
-        hipLaunchKernelGGL(k_attn_q40_g8<128>, grid, dim3(64), 0, st, c, (const uint8_t *)q4, bt, q, lens,
-                           scale_log2, ws, nsplit, chunk);
+    const uint8_t *p = (const uint8_t *)q4;
+    if (c.head_dim == 64) {
+        if (delta)
+            hipLaunchKernelGGL((k_attn_q40_g8<64, true>), grid, dim3(64), 0, st, c, p, bt, q, lens, scale_log2, ws,
+                               nsplit, chunk);
+        else
+            hipLaunchKernelGGL((k_attn_q40_g8<64, false>), grid, dim3(64), 0, st, c, p, bt, q, lens, scale_log2, ws,
+                               nsplit, chunk);
+    } else {
+        if (delta)
+            hipLaunchKernelGGL((k_attn_q40_g8<128, true>), grid, dim3(64), 0, st, c, p, bt, q, lens, scale_log2, ws,
+                               nsplit, chunk);
+        else
+            hipLaunchKernelGGL((k_attn_q40_g8<128, false>), grid, dim3(64), 0, st, c, p, bt, q, lens, scale_log2, ws,
+                               nsplit, chunk);
+    }
     return hipGetLastError();
 }
 

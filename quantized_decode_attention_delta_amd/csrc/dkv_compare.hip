@@ -428,23 +428,40 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
     for (int r = 0; r < CPL; ++r) acc[r] = f4{0, 0, 0, 0};
     float m = -INFINITY, l = 0.0f;
 
-    for (int tl = t0; tl < t1; ++tl) {
-        const int64_t e0 = f16_tile_elem(cfg, bt, b, h, tl);
-        if (e0 < 0) continue;                   // unmapped page: its tokens are not attended
-        // the tile's rows (contiguous: up to the end of the stream; loads past it return 0)
-        const int bytes = (cfg.page_tokens > 0 ? 32 : min(32, cfg.max_tokens - 32 * tl)) * D * 2;
-        const __amdgpu_buffer_rsrc_t rk =
-            __builtin_amdgcn_make_buffer_rsrc((void *)(kin + e0), (short)0, bytes, 0x00020000);
-        const __amdgpu_buffer_rsrc_t rv =
-            __builtin_amdgcn_make_buffer_rsrc((void *)(vin + e0), (short)0, bytes, 0x00020000);
-        const int nvt = min(32, L - 32 * tl);
+    // Software pipeline over the run's mapped tiles: the next tile's K rows are
+    // fetched (into the other of two K buffers) before the current tile's
+    // logits, its V rows as soon as the current V rows have gone into the
+    // matrix instructions.  Past the run (or where only unmapped tiles follow)
+    // the current tile is fetched again (an L2 hit) and not used.
+    struct KRegs {
         u4 kr[2][NB];
+    };
+    struct VRegs {
+        uint32_t vr[2][4][VW];
+    };
+    auto next_mapped = [&](int t, int64_t &e) {
+        for (; t < t1; ++t) {
+            e = f16_tile_elem(cfg, bt, b, h, t);
+            if (e >= 0) break;                  // unmapped page: its tokens are not attended
+        }
+        return t;
+    };
+    // the tile's rows (contiguous: up to the end of the stream; loads past it return 0)
+    auto tile_rsrc = [&](const uint16_t *base, int tl, int64_t e0) {
+        const int bytes = (cfg.page_tokens > 0 ? 32 : min(32, cfg.max_tokens - 32 * tl)) * D * 2;
+        return __builtin_amdgcn_make_buffer_rsrc((void *)(base + e0), (short)0, bytes, 0x00020000);
+    };
+    auto load_k = [&](KRegs &r, int tl, int64_t e0) {
+        const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kin, tl, e0);
 #pragma unroll
         for (int T = 0; T < 2; ++T)
 #pragma unroll
             for (int bb = 0; bb < NB; ++bb)
-                kr[T][bb] = __builtin_amdgcn_raw_buffer_load_b128(rk, ((16 * T + n) * D + 32 * bb + 8 * j) * 2, 0, kStreamF16);
-        uint32_t vr[2][4][VW];
+                r.kr[T][bb] =
+                    __builtin_amdgcn_raw_buffer_load_b128(rk, ((16 * T + n) * D + 32 * bb + 8 * j) * 2, 0, kStreamF16);
+    };
+    auto load_v = [&](VRegs &r, int tl, int64_t e0) {
+        const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vin, tl, e0);
 #pragma unroll
         for (int T = 0; T < 2; ++T)
 #pragma unroll
@@ -453,14 +470,18 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
                 if constexpr (VW == 4) {
                     const u4 a = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, kStreamF16);
 #pragma unroll
-                    for (int k = 0; k < 4; ++k) vr[T][i][k] = a[k];
+                    for (int k = 0; k < 4; ++k) r.vr[T][i][k] = a[k];
                 } else {
                     const u2 a = __builtin_amdgcn_raw_buffer_load_b64(rv, off, 0, kStreamF16);
 #pragma unroll
-                    for (int k = 0; k < 2; ++k) vr[T][i][k] = a[k];
+                    for (int k = 0; k < 2; ++k) r.vr[T][i][k] = a[k];
                 }
             }
-
+    };
+    // tile tl from K rows rk and V rows r; then the V rows of tile tn (at e_n)
+    // are fetched into r
+    auto compute_tile = [&](const KRegs &rk, VRegs &r, int tl, int tn, int64_t e_n) {
+        const int nvt = min(32, L - 32 * tl);
         // ---- logits (units: q * 2^-E)
         float Lg[2][4];
 #pragma unroll
@@ -468,7 +489,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
             f4 P = f4{0, 0, 0, 0};
 #pragma unroll
             for (int bb = 0; bb < NB; ++bb) {
-                const h8 A = as_h8(kr[T][bb]);
+                const h8 A = as_h8(rk.kr[T][bb]);
                 P = mfma(A, as_h8(qB[(2 * bb) * 64 + lane]), P);
                 P = mfma(A, as_h8(qB[(2 * bb + 1) * 64 + lane]), P);
             }
@@ -486,7 +507,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
         const float a_m = __builtin_amdgcn_exp2f(m - m_new);
         if (__any(m_new != m)) {
 #pragma unroll
-            for (int r = 0; r < CPL; ++r) acc[r] *= a_m;
+            for (int c = 0; c < CPL; ++c) acc[c] *= a_m;
             l *= a_m;
         }
         m = m_new;
@@ -508,22 +529,45 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
                 Wl[2 * i + T] = (_Float16)(w - (float)hi);
                 if (!ok) {
 #pragma unroll
-                    for (int k = 0; k < VW; ++k) vr[T][i][k] = 0u;      // rows past the end may hold non-finite values
+                    for (int k = 0; k < VW; ++k) r.vr[T][i][k] = 0u;      // rows past the end may hold non-finite values
                 }
             }
         l += rows_sum(ps);
 
-        // ---- V operands per channel offset r, then P.V
+        // ---- V operands per channel offset c, then P.V
 #pragma unroll
-        for (int r = 0; r < CPL; ++r) {
+        for (int c = 0; c < CPL; ++c) {
             u4 a;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const uint32_t w0 = vr[0][i][r >> 1], w1 = vr[1][i][r >> 1];
-                a[i] = (r & 1) ? pack_hi16(w0, w1) : pack_lo16(w0, w1);
+                const uint32_t w0 = r.vr[0][i][c >> 1], w1 = r.vr[1][i][c >> 1];
+                a[i] = (c & 1) ? pack_hi16(w0, w1) : pack_lo16(w0, w1);
             }
-            acc[r] = mfma(as_h8(a), Wh, acc[r]);
-            acc[r] = mfma(as_h8(a), Wl, acc[r]);
+            acc[c] = mfma(as_h8(a), Wh, acc[c]);
+            acc[c] = mfma(as_h8(a), Wl, acc[c]);
+        }
+        load_v(r, tn, e_n);
+    };
+
+    int64_t e_cur = -1;
+    int tl = next_mapped(t0, e_cur);
+    if (tl < t1) {
+        KRegs ka, kb;
+        VRegs vr;
+        load_k(ka, tl, e_cur);
+        load_v(vr, tl, e_cur);
+        // one step: the next mapped tile's K into pf, then tile tl
+        auto step = [&](const KRegs &cur, KRegs &pf) {
+            int64_t e_n = -1;
+            const int tn = next_mapped(tl + 1, e_n);
+            const bool more = tn < t1;
+            load_k(pf, more ? tn : tl, more ? e_n : e_cur);
+            compute_tile(cur, vr, tl, more ? tn : tl, more ? e_n : e_cur);
+            tl = tn;
+            e_cur = e_n;
+            return more;
+        };
+        while (step(ka, kb) && step(kb, ka)) {
         }
     }
 
@@ -579,6 +623,169 @@ __global__ void __launch_bounds__(64) k_q80_encode(dkv_config cfg, const uint16_
 }
 
 // ------------------------------------------------------------------------
+// Q4-keyframe variant (Delta-KV article, "벤치마크": the same 4-bit storage as
+// Q4_0).  The cache is the plain Q4_0 tile layout; token t is one Q4_0 row,
+// coded against zero at a keyframe (t % kf == 0) and against the running
+// reconstruction otherwise, with the block quantiser of the Delta-KV codec.
+// kf divides 32 or is a multiple of 32, so every group lies in whole tiles.
+// ------------------------------------------------------------------------
+__host__ __device__ inline int q4k_tiles_per_segment(int kf) { return kf >= 32 ? kf / 32 : 1; }
+
+// One Q4-keyframe row of a stream: lane = channel mod 64 (NC channels per
+// lane), xh the lanes' reconstruction of the previous token; writes the row's
+// scales and K codes into the tile at `base` (the stream's part), slot tau.
+// V codes: into the lane's tile words vw (the bulk encoder writes whole words
+// per tile, unused slots holding code 8), or with RMW read-modify-write of the
+// word in the cache (the append).
+template <int D, bool RMW>
+__device__ inline void q4k_row(const dkv_config &cfg, uint8_t *base, int s, int tau, bool key, const uint16_t *x,
+                               float (&xh)[D / 64], uint32_t (&vw)[D / 64][4], int lane)
+{
+    constexpr int NC = D / 64, nb = D / 32;
+    uint16_t *sc = (uint16_t *)base;
+    uint8_t *cd = base + 2 * D;
+    const int sh = 4 * vcode_nibble(tau);
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+        const int c = lane + 64 * i;
+        const int blk = c >> 5;
+        float ref = key ? 0.0f : xh[i];
+        int code;
+        uint16_t s16;
+        q40_delta_step(h2f(x[c]), ref, code, s16);
+        if ((lane & 31) == 0) sc[tau * nb + blk] = s16;
+        if (s == 0) {
+            store_k_codes<D>(cd + tau * (D / 2), blk, code);
+        } else if constexpr (RMW) {
+            uint32_t *w = (uint32_t *)cd + vcode_word(D, tau, c, q40_vbp(cfg));
+            *w = (*w & ~(0xFu << sh)) | ((uint32_t)code << sh);
+        } else {
+            const int j = (tau & 15) >> 2;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+                if (jj == j) vw[i][jj] = (vw[i][jj] & ~(0xFu << sh)) | ((uint32_t)code << sh);
+        }
+        xh[i] = ref;
+    }
+}
+
+// Bulk encode.  grid (segments, Hkv*2, B): a segment is one tile when kf
+// divides 32 and one group (kf/32 tiles) otherwise; one wave per segment and
+// stream, rows in order.  The segment holding a sequence's last token writes
+// the reconstruction state.
+template <int D>
+__global__ void __launch_bounds__(64) k_q4k_encode(dkv_config cfg, uint8_t *q4, float *state, const int32_t *bt,
+                                                   const uint16_t *kin, const uint16_t *vin, const int32_t *seq_lens,
+                                                   int s_max)
+{
+    constexpr int NC = D / 64;
+    const int seg = blockIdx.x, h = blockIdx.y >> 1, s = blockIdx.y & 1, b = blockIdx.z;
+    const int L = min(min(seq_lens[b], q40_ntiles(cfg) * 32), s_max);
+    const int tps = q4k_tiles_per_segment(cfg.kf);
+    const int lane = threadIdx.x;
+    const uint16_t *xs = (s ? vin : kin) + ((int64_t)b * cfg.n_kv_heads + h) * s_max * D;
+    float xh[NC];
+#pragma unroll
+    for (int i = 0; i < NC; ++i) xh[i] = 0.0f;
+    for (int tile = seg * tps; tile < (seg + 1) * tps && tile * 32 < L; ++tile) {
+        const int64_t toff = q40_tile_offset(cfg, bt, b, h, tile);
+        if (toff < 0) return;                   // unmapped page (a page holds whole groups)
+        uint8_t *base = q4 + toff + (s ? 18 * D : 0);
+        const int n = min(32, L - tile * 32);
+        uint32_t vw[NC][4];
+#pragma unroll
+        for (int i = 0; i < NC; ++i)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) vw[i][jj] = 0x88888888u;
+        for (int r = 0; r < n; ++r) {
+            const int t = tile * 32 + r;
+            q4k_row<D, false>(cfg, base, s, r, t % cfg.kf == 0, xs + (int64_t)t * D, xh, vw, lane);
+        }
+        if (s == 1) {
+            uint32_t *tw = (uint32_t *)(base + 2 * D);
+#pragma unroll
+            for (int i = 0; i < NC; ++i)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) tw[vcode_word(D, 4 * jj, lane + 64 * i, q40_vbp(cfg))] = vw[i][jj];
+        }
+        if (tile * 32 + n == L) {
+            float *st = state + (((int64_t)b * cfg.n_kv_heads + h) * 2 + s) * D;
+#pragma unroll
+            for (int i = 0; i < NC; ++i) st[lane + 64 * i] = xh[i];
+        }
+    }
+}
+
+// Append one token per sequence at positions[b] (negative: skipped).
+// grid (Hkv*2, B), one wave per (sequence, kv-head, stream).
+template <int D>
+__global__ void __launch_bounds__(64) k_q4k_append(dkv_config cfg, uint8_t *q4, float *state, const int32_t *bt,
+                                                   const uint16_t *knew, const uint16_t *vnew,
+                                                   const int32_t *positions)
+{
+    constexpr int NC = D / 64;
+    const int h = blockIdx.x >> 1, s = blockIdx.x & 1, b = blockIdx.y;
+    const int pos = positions[b];
+    if (pos < 0 || pos >= q40_ntiles(cfg) * 32) return;
+    const int64_t toff = q40_tile_offset(cfg, bt, b, h, pos >> 5);
+    if (toff < 0) return;
+    const int lane = threadIdx.x;
+    float *st = state + (((int64_t)b * cfg.n_kv_heads + h) * 2 + s) * D;
+    float xh[NC];
+    uint32_t vw[NC][4];                         // (unused: the append rewrites words in place)
+#pragma unroll
+    for (int i = 0; i < NC; ++i) xh[i] = st[lane + 64 * i];
+    q4k_row<D, true>(cfg, q4 + toff + (s ? 18 * D : 0), s, pos & 31, pos % cfg.kf == 0,
+                     (s ? vnew : knew) + ((int64_t)b * cfg.n_kv_heads + h) * D, xh, vw, lane);
+#pragma unroll
+    for (int i = 0; i < NC; ++i) st[lane + 64 * i] = xh[i];
+}
+
+// Reconstruction of every token t < seq_lens[b] (rows in order per segment):
+// out_k, out_v float [B][Hkv][s_max][D].
+template <int D>
+__global__ void __launch_bounds__(64) k_q4k_reconstruct(dkv_config cfg, const uint8_t *q4, const int32_t *bt,
+                                                        const int32_t *seq_lens, int s_max, float *ok, float *ov)
+{
+    constexpr int NC = D / 64, nb = D / 32;
+    const int seg = blockIdx.x, h = blockIdx.y >> 1, s = blockIdx.y & 1, b = blockIdx.z;
+    const int L = min(min(seq_lens[b], q40_ntiles(cfg) * 32), s_max);
+    const int tps = q4k_tiles_per_segment(cfg.kf);
+    const int lane = threadIdx.x;
+    const int bp = q40_vbp(cfg);
+    float *out = (s ? ov : ok) + ((int64_t)b * cfg.n_kv_heads + h) * s_max * D;
+    float xh[NC];
+#pragma unroll
+    for (int i = 0; i < NC; ++i) xh[i] = 0.0f;
+    for (int tile = seg * tps; tile < (seg + 1) * tps && tile * 32 < L; ++tile) {
+        const int64_t toff = q40_tile_offset(cfg, bt, b, h, tile);
+        if (toff < 0) return;
+        const uint8_t *base = q4 + toff + (s ? 18 * D : 0);
+        const uint16_t *sc = (const uint16_t *)base;
+        const uint8_t *cd = base + 2 * D;
+        const int n = min(32, L - tile * 32);
+        for (int r = 0; r < n; ++r) {
+            const int t = tile * 32 + r;
+            const bool key = t % cfg.kf == 0;
+#pragma unroll
+            for (int i = 0; i < NC; ++i) {
+                const int c = lane + 64 * i, blk = c >> 5, w = c & 31;
+                int code;
+                if (s == 0) {
+                    const uint8_t byte = cd[r * (D / 2) + kcode_byte(nb, blk, w & 15)];
+                    code = w < 16 ? (byte & 0xF) : (byte >> 4);
+                } else {
+                    code = (((const uint32_t *)cd)[vcode_word(D, r, c, bp)] >> (4 * vcode_nibble(r))) & 0xF;
+                }
+                const float ref = key ? 0.0f : xh[i];
+                xh[i] = __fadd_rn(ref, __fmul_rn((float)(code - 8), h2f(sc[r * nb + blk])));
+                out[(int64_t)t * D + c] = xh[i];
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------------
 // Launchers
 // ------------------------------------------------------------------------
 hipError_t launch_q40_encode(const dkv_config &c, void *q4, const int32_t *bt, const uint16_t *k, const uint16_t *v,
@@ -619,12 +826,13 @@ hipError_t launch_q40_export(const dkv_config &c, const void *q4, const int32_t 
 }
 
 hipError_t launch_attn_q40_g8(const dkv_config &c, const void *q4, const int32_t *bt, const float *q,
-                              const int32_t *lens, float scale_log2, float *ws, int nsplit, int chunk, hipStream_t st);
+                              const int32_t *lens, float scale_log2, float *ws, int nsplit, int chunk, hipStream_t st,
+                              bool delta);
 
 hipError_t launch_attn_q40(const dkv_config &c, const void *q4, const int32_t *bt, const float *q, const int32_t *lens,
                            float scale_log2, float *ws, int nsplit, int chunk, hipStream_t st)
 {
-    if (q40_vbp(c)) return launch_attn_q40_g8(c, q4, bt, q, lens, scale_log2, ws, nsplit, chunk, st);
+    if (q40_vbp(c)) return launch_attn_q40_g8(c, q4, bt, q, lens, scale_log2, ws, nsplit, chunk, st, false);
     dim3 grid(nsplit, c.n_kv_heads, c.batch);
     if (c.head_dim == 64)
         hipLaunchKernelGGL(k_attn_q40<64>, grid, dim3(64), 0, st, c, (const uint8_t *)q4, bt, q, lens, scale_log2, ws,
@@ -647,6 +855,56 @@ hipError_t launch_attn_f16(const dkv_config &c, const uint16_t *k, const uint16_
         hipLaunchKernelGGL(k_attn_f16<128>, grid, dim3(64), 0, st, c, k, v, bt, q, lens, scale_log2, ws, nsplit,
                            chunk);
     return hipGetLastError();
+}
+
+static int q4k_segments(const dkv_config &c, int s_max)
+{
+    const int tiles = min(q40_ntiles(c), (s_max + 31) / 32);
+    const int tps = q4k_tiles_per_segment(c.kf);
+    return (tiles + tps - 1) / tps;
+}
+
+hipError_t launch_q4k_encode(const dkv_config &c, void *q4, float *state, const int32_t *bt, const uint16_t *k,
+                             const uint16_t *v, const int32_t *lens, int s_max, hipStream_t st)
+{
+    dim3 grid(q4k_segments(c, s_max), c.n_kv_heads * 2, c.batch);
+    if (c.head_dim == 64)
+        hipLaunchKernelGGL(k_q4k_encode<64>, grid, dim3(64), 0, st, c, (uint8_t *)q4, state, bt, k, v, lens, s_max);
+    else
+        hipLaunchKernelGGL(k_q4k_encode<128>, grid, dim3(64), 0, st, c, (uint8_t *)q4, state, bt, k, v, lens, s_max);
+    return hipGetLastError();
+}
+
+hipError_t launch_q4k_append(const dkv_config &c, void *q4, float *state, const int32_t *bt, const uint16_t *k,
+                             const uint16_t *v, const int32_t *pos, hipStream_t st)
+{
+    dim3 grid(c.n_kv_heads * 2, c.batch);
+    if (c.head_dim == 64)
+        hipLaunchKernelGGL(k_q4k_append<64>, grid, dim3(64), 0, st, c, (uint8_t *)q4, state, bt, k, v, pos);
+    else
+        hipLaunchKernelGGL(k_q4k_append<128>, grid, dim3(64), 0, st, c, (uint8_t *)q4, state, bt, k, v, pos);
+    return hipGetLastError();
+}
+
+hipError_t launch_q4k_reconstruct(const dkv_config &c, const void *q4, const int32_t *bt, const int32_t *lens,
+                                  int s_max, float *ok, float *ov, hipStream_t st)
+{
+    dim3 grid(q4k_segments(c, s_max), c.n_kv_heads * 2, c.batch);
+    if (c.head_dim == 64)
+        hipLaunchKernelGGL(k_q4k_reconstruct<64>, grid, dim3(64), 0, st, c, (const uint8_t *)q4, bt, lens, s_max, ok,
+                           ov);
+    else
+        hipLaunchKernelGGL(k_q4k_reconstruct<128>, grid, dim3(64), 0, st, c, (const uint8_t *)q4, bt, lens, s_max, ok,
+                           ov);
+    return hipGetLastError();
+}
+
+// Decode attention over the Q4-keyframe cache: kf = 1 is plain Q4_0 (the
+// plain kernel); kf = 32 the same kernel with prefix / suffix sums per tile.
+hipError_t launch_attn_q4k(const dkv_config &c, const void *q4, const int32_t *bt, const float *q,
+                           const int32_t *lens, float scale_log2, float *ws, int nsplit, int chunk, hipStream_t st)
+{
+    return launch_attn_q40_g8(c, q4, bt, q, lens, scale_log2, ws, nsplit, chunk, st, c.kf == 32);
 }
 
 }  // namespace dkv

@@ -80,6 +80,10 @@ _SIGS = {
     "dkv_q4_0_export": ([_CFG, _P, _P, _P, _I32, _P, _P, _P], _I32),
     "dkv_attn_decode_q4_0": ([_CFG, _P, _P, _P, _P, _F, _P, _P, _SZ, _P], _I32),
     "dkv_attn_decode_f16": ([_CFG, _P, _P, _P, _P, _P, _F, _P, _P, _SZ, _P], _I32),
+    "dkv_q4k_encode_prefill": ([_CFG, _P, _P, _P, _P, _P, _P, _I32, _P], _I32),
+    "dkv_q4k_append": ([_CFG, _P, _P, _P, _P, _P, _P, _P], _I32),
+    "dkv_q4k_reconstruct": ([_CFG, _P, _P, _P, _I32, _P, _P, _P], _I32),
+    "dkv_attn_decode_q4k": ([_CFG, _P, _P, _P, _P, _F, _P, _P, _SZ, _P], _I32),
     "dkv_q8_0_encode": ([_CFG, _P, _P, _P, _I32, _P, _P, _P], _I32),
     "dkv_attn_distortion": ([_CFG, _P, _P, _P, _P, _I32, _P, _P, _F, _P, _P, _P, _P], _I32),
     "dkv_stream_read_sink_words": ([], _SZ),
@@ -370,6 +374,56 @@ def dkv_attn_decode_q4_0(cfg: Config, q4_cache, block_table, q, seq_lens, out, w
         _ptr(out, torch.float32, "out", B * Hq * D), _ptr(workspace, torch.uint8, "workspace"),
         workspace.numel() if workspace is not None else 0, _stream(stream))
     _check("dkv_attn_decode_q4_0", st)
+
+
+# ------------------------------------------------------- Q4-keyframe variant
+def dkv_q4k_encode_prefill(cfg: Config, cache, state, block_table, k, v, seq_lens, s_max: int, stream=None):
+    """Q4-keyframe encode into a cache of dkv_q4_0_cache_bytes(cfg) bytes."""
+    import torch
+    B, H, D = cfg.batch, cfg.n_kv_heads, cfg.head_dim
+    st = load().dkv_q4k_encode_prefill(
+        ctypes.byref(cfg.c()), _ptr(cache, torch.uint8, "cache", dkv_q4_0_cache_bytes(cfg)),
+        _ptr(state, torch.float32, "state", B * H * 2 * D),
+        _ptr(block_table, torch.int32, "block_table", _bt_numel(cfg)),
+        _f16(k, "k", B * H * s_max * D), _f16(v, "v", B * H * s_max * D),
+        _ptr(seq_lens, torch.int32, "seq_lens", B), int(s_max), _stream(stream))
+    _check("dkv_q4k_encode_prefill", st)
+
+
+def dkv_q4k_append(cfg: Config, cache, state, block_table, k_new, v_new, positions, stream=None):
+    import torch
+    B, H, D = cfg.batch, cfg.n_kv_heads, cfg.head_dim
+    st = load().dkv_q4k_append(
+        ctypes.byref(cfg.c()), _ptr(cache, torch.uint8, "cache", dkv_q4_0_cache_bytes(cfg)),
+        _ptr(state, torch.float32, "state", B * H * 2 * D),
+        _ptr(block_table, torch.int32, "block_table", _bt_numel(cfg)),
+        _f16(k_new, "k_new", B * H * D), _f16(v_new, "v_new", B * H * D),
+        _ptr(positions, torch.int32, "positions", B), _stream(stream))
+    _check("dkv_q4k_append", st)
+
+
+def dkv_q4k_reconstruct(cfg: Config, cache, block_table, seq_lens, s_max: int, k_out, v_out, stream=None):
+    import torch
+    n = cfg.batch * cfg.n_kv_heads * s_max * cfg.head_dim
+    st = load().dkv_q4k_reconstruct(
+        ctypes.byref(cfg.c()), _ptr(cache, torch.uint8, "cache", dkv_q4_0_cache_bytes(cfg)),
+        _ptr(block_table, torch.int32, "block_table", _bt_numel(cfg)),
+        _ptr(seq_lens, torch.int32, "seq_lens", cfg.batch), int(s_max),
+        _ptr(k_out, torch.float32, "k_out", n), _ptr(v_out, torch.float32, "v_out", n), _stream(stream))
+    _check("dkv_q4k_reconstruct", st)
+
+
+def dkv_attn_decode_q4k(cfg: Config, cache, block_table, q, seq_lens, out, workspace, softmax_scale=0.0,
+                        stream=None):
+    import torch
+    B, Hq, D = cfg.batch, cfg.n_q_heads, cfg.head_dim
+    st = load().dkv_attn_decode_q4k(
+        ctypes.byref(cfg.c()), _ptr(cache, torch.uint8, "cache", dkv_q4_0_cache_bytes(cfg)),
+        _ptr(block_table, torch.int32, "block_table", _bt_numel(cfg)), _ptr(q, torch.float32, "q", B * Hq * D),
+        _ptr(seq_lens, torch.int32, "seq_lens", B), float(softmax_scale),
+        _ptr(out, torch.float32, "out", B * Hq * D), _ptr(workspace, torch.uint8, "workspace"),
+        workspace.numel() if workspace is not None else 0, _stream(stream))
+    _check("dkv_attn_decode_q4k", st)
 
 
 def dkv_attn_decode_f16(cfg: Config, k, v, block_table, q, seq_lens, out, workspace, softmax_scale=0.0,

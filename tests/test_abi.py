@@ -146,6 +146,18 @@ def test_argument_errors_return_before_launch():
     assert lib.dkv_strided_append_attn_decode(cp, fake, fake, fake, null, 0, fake, fake, 0.0, fake, fake, 1 << 30,
                                               null) == binding.DKV_ERR_ARG
     assert lib.dkv_strided_append(cpg, fake, fake, fake, fake, 0, null) == binding.DKV_ERR_UNSUPPORTED
+    # Q4-keyframe variant: groups in whole tiles (kf divides 32 or is a multiple
+    # of 32); attention at kf 1 and 32 only; null pointers
+    c48 = ctypes.byref(_cfg(kf=48).c())
+    assert lib.dkv_q4k_encode_prefill(c48, fake, fake, null, fake, fake, fake, 10, null) == binding.DKV_ERR_UNSUPPORTED
+    assert lib.dkv_q4k_append(c48, fake, fake, null, fake, fake, fake, null) == binding.DKV_ERR_UNSUPPORTED
+    c8 = ctypes.byref(_cfg(kf=8).c())
+    assert lib.dkv_attn_decode_q4k(c8, fake, null, fake, fake, 0.0, fake, fake, 1 << 30,
+                                   null) == binding.DKV_ERR_UNSUPPORTED
+    assert lib.dkv_q4k_encode_prefill(c8, fake, null, null, fake, fake, fake, 10, null) == binding.DKV_ERR_ARG
+    assert lib.dkv_q4k_reconstruct(cp, fake, null, fake, 10, fake, null, null) == binding.DKV_ERR_ARG
+    assert lib.dkv_attn_decode_q4k(cp, fake, null, fake, fake, 0.0, fake, fake, 16, null) == binding.DKV_ERR_WORKSPACE
+    assert lib.dkv_attn_decode_q4k(cpg, fake, null, fake, fake, 0.0, fake, fake, 1 << 30, null) == binding.DKV_ERR_ARG
     assert lib.dkv_check_config(None) == binding.DKV_ERR_ARG
     assert dkv.status_str(binding.DKV_ERR_WORKSPACE) == "workspace missing or too small"
 
