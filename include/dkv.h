@@ -38,7 +38,8 @@
  *              block's 16 canonical bytes split into four 4-byte pieces;
  *              V: ceil(kf/32) tiles of 32 token slots, each channel's nibbles
  *              of 8 tokens packed in one 32-bit word (slot 0 of a group is the
- *              keyframe and carries no code).
+ *              keyframe and carries no code);
+ *  then padding to a multiple of 128 bytes (whole cache lines per record).
  *  Contiguous mode (page_tokens == 0): records are ordered
  *  [batch][n_kv_heads][ceil(max_tokens/kf)].  Paged mode (page_tokens > 0,
  *  page_tokens % kf == 0): a page holds page_tokens tokens of every kv-head,

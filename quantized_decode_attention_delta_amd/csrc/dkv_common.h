@@ -98,7 +98,10 @@ __host__ __device__ inline Geom make_geom(const dkv_config &c)
     g.off_vkf = g.off_kcd + kcb;
     g.off_vsc = g.off_vkf + kfb;
     g.off_vcd = g.off_vsc + scb;
-    g.rec = g.off_vcd + (int64_t)g.ntiles_v * 16 * g.D;
+    // records padded to whole 128-byte cache lines: a record's lines are its
+    // own, so the keyframe lines the decode reads ahead of the rest of the
+    // record are never fetched a second time with a neighbour's data
+    g.rec = (g.off_vcd + (int64_t)g.ntiles_v * 16 * g.D + 127) & ~int64_t(127);
     g.paged = c.page_tokens > 0;
     if (g.paged) {
         g.gpp = c.page_tokens / c.kf;

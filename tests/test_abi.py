@@ -66,8 +66,10 @@ def test_sizes():
     c = _cfg(batch=16, n_q_heads=64, n_kv_heads=8, max_tokens=32768)
     rec = dkv.dkv_group_record_bytes(c)
     # two streams of 2,488 algorithmic bytes per 32-token group, plus 64 bytes of
-    # V code padding (the keyframe slot) and 8+8 bytes of scale slot 0
-    assert rec == 2 * 2488 + 64 + 16
+    # V code padding (the keyframe slot) and 8+8 bytes of scale slot 0, padded
+    # to whole 128-byte lines
+    assert rec == 5120 and 2 * 2488 + 64 + 16 == 5056
+    assert dkv.dkv_group_record_bytes(_cfg(head_dim=64)) == 2560           # 2528 rounded up
     assert dkv.dkv_cache_bytes(c) == 16 * 8 * 1024 * rec
     assert dkv.dkv_state_bytes(c) == 16 * 8 * 2 * 128 * 4
     assert dkv.dkv_workspace_bytes(c) > 0

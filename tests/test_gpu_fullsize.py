@@ -1,7 +1,9 @@
 """Parity at the benchmark sizes, in the launch configuration bench.py times.
 
-The 70B-layer workload (B=16, 64 q / 8 kv heads, D=128, S=32768, kf=32), the
-long-context workload (B=8, S=16384, kf=512 and 128) and the mixed serving
+The tiny workload, the 8B-shaped layer (B=1, 32 q / 8 kv heads, S=4096, every
+kv-head), the 70B-layer workload (B=16, 64 q / 8 kv heads, D=128, S=32768,
+kf=32; also its Q4-keyframe variant), the long-context workload (B=8,
+S=16384, kf=512, 128 and 32) and the mixed serving
 workload (full lengths 1K..64K in shuffled 256-token pages, 16 of its 64
 sequences) are encoded and attended on the GPU exactly as the benchmark does.
 The oracle checks sampled (sequence, kv-head) pairs: keyframes, Q4_0 codes,
@@ -76,18 +78,70 @@ def _run(w, kf, pairs, paged=False):
     assert np.isfinite(got).all()
 
 
+def test_tiny_full_size():
+    print("full size: tiny", flush=True)
+    _run(synth.make("tiny"), 32, [(0, 0)])
+
+
+def test_8b_layer_full_size():
+    """The 8B-shaped layer (B=1, 32 q / 8 kv heads, S=4096): every kv-head."""
+    print("full size: 8b", flush=True)
+    _run(synth.make("8b"), 32, [(0, h) for h in range(8)])
+
+
 def test_70b_layer_full_size():
+    print("full size: 70b", flush=True)
     w = synth.make("70b")
-    _run(w, 32, [(0, 0), (5, 3), (9, 6), (15, 7)])
+    _run(w, 32, [(0, 0), (2, 1), (5, 3), (7, 2), (9, 6), (11, 4), (13, 5), (15, 7)])
 
 
-@pytest.mark.parametrize("kf", [512, 128])
+@pytest.mark.parametrize("kf", [512, 128, 32])
 def test_long_context_full_size(kf):
+    print(f"full size: long kf={kf}", flush=True)
     w = synth.make("long")
-    _run(w, kf, [(0, 0), (3, 5), (7, 7)])
+    _run(w, kf, [(0, 0), (1, 2), (3, 5), (4, 1), (6, 3), (7, 7)])
+
+
+def test_q4k_70b_layer_full_size():
+    """The Q4-keyframe variant (kf 32) at the 70B-layer size: codes and scale
+    bits of sampled pairs bit-exact with the oracle, attention within 2e-3."""
+    print("full size: q4k 70b", flush=True)
+    w = synth.make("70b")
+    cfg = U.make_cfg(w, 32)
+    lens_np = np.asarray(w.seq_lens, np.int32)
+    lens = torch.from_numpy(lens_np).to(U.DEV)
+    S = w.k.shape[2]
+    cache = torch.empty(dkv.dkv_q4_0_cache_bytes(cfg), dtype=torch.uint8, device=U.DEV)
+    state = torch.zeros(w.B, w.Hkv, 2, w.D, dtype=torch.float32, device=U.DEV)
+    k = torch.from_numpy(w.k).to(U.DEV)
+    v = torch.from_numpy(w.v).to(U.DEV)
+    dkv.dkv_q4k_encode_prefill(cfg, cache, state, None, k, v, lens, S)
+    del k, v
+    q_np = synth.queries(w)
+    out = torch.full((w.B, w.Hq, w.D), float("nan"), dtype=torch.float32, device=U.DEV)
+    ws = torch.zeros(dkv.dkv_workspace_bytes(cfg), dtype=torch.uint8, device=U.DEV)
+    dkv.dkv_attn_decode_q4k(cfg, cache, None, torch.from_numpy(q_np).to(U.DEV), lens, out, ws)
+    got = out.cpu().numpy()
+    codes = torch.zeros((w.B, w.Hkv, 2, S, w.D // 2), dtype=torch.uint8, device=U.DEV)
+    scales = torch.zeros((w.B, w.Hkv, 2, S, w.D // 32), dtype=torch.int16, device=U.DEV)
+    dkv.dkv_q4_0_export(cfg, cache, None, lens, S, codes, scales)
+    G = w.Hq // w.Hkv
+    scale = np.float32(1 / math.sqrt(w.D))
+    for (b, h) in [(0, 0), (6, 3), (15, 7)]:
+        recon = []
+        for s, x in ((0, w.k), (1, w.v)):
+            e = oracle.q4k_encode_stream(np.ascontiguousarray(x[b, h]), 32)
+            assert np.array_equal(codes[b, h, s].cpu().numpy(), e.codes), ("codes", b, h, s)
+            assert np.array_equal(scales[b, h, s].cpu().numpy().view(np.uint16), e.scales), ("scales", b, h, s)
+            recon.append(e.recon)
+        ref = oracle.attention_f64(q_np[b, h * G:(h + 1) * G], recon[0], recon[1], scale)
+        g = got[b, h * G:(h + 1) * G].astype(np.float64)
+        assert float((np.abs(g - ref).max(-1) / np.abs(ref).max(-1)).max()) <= U.ATTN_TOL
+    assert np.isfinite(got).all()
 
 
 def test_mixed_serving_full_lengths():
+    print("full size: mixed", flush=True)
     w = synth.make("mixed", B=16, extra_tokens=0)
     longest = int(np.argmax(w.seq_lens))
     shortest = int(np.argmin(w.seq_lens))
