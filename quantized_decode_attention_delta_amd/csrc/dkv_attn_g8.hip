@@ -355,6 +355,15 @@ __device__ inline void kf_logits_g8(float *out, const u4 (&a)[4][D / 32], int cn
     }
 }
 
+// Lazy running max (log2 units): the reference max moves only when a group's
+// maximum exceeds it by more than kLazyMax, so the softmax weights stay below
+// 2^kLazyMax and the accumulators are rescaled rarely.  On slowly drifting
+// logits (a random-walk cache) nearly every group used to raise the max and
+// cost a rescale; with a fixed reference the 70B-layer split kernel measured
+// 124 us against 136 us.  The partial records carry their reference max, so
+// the split combine is unaffected.
+constexpr int kLazyMax = 8;
+
 // Softmax state update for a group with maximum m_g: new running max and V
 // range bias from the group's largest |V scale| (slot 0 of the V scale plane,
 // vs0) and kf <= 2^lkf; the accumulators are rescaled only when either changes,
@@ -364,9 +373,10 @@ __device__ inline void update_g8_vmx(RunState<D> &st, float m_g, uint32_t vmx, i
 {
     constexpr int NB = D / 32, NCC = D / 16, NP = NB / 2;
     const int ev = (vmx >> 10) == 0 ? -14 : (int)(vmx >> 10) - 15;
-    const int beta_g = vmx == 0 ? 24 - lkf : 10 - lkf - ev;       // kf * 16 * |s| * 2^beta < 2^15
+    // kf * 16 * |s| * 2^kLazyMax * 2^beta < 2^15 (weights below 2^kLazyMax)
+    const int beta_g = (vmx == 0 ? 24 - lkf : 10 - lkf - ev) - kLazyMax;
 
-    const float m_new = fmax_nc(st.m, m_g);
+    const float m_new = m_g > st.m + (float)kLazyMax ? m_g : st.m;
     const int beta_new = min(st.beta, beta_g);
     const float a_m = __builtin_amdgcn_exp2f(st.m - m_new);
     if (__any(m_new != st.m || beta_new != st.beta)) {
