@@ -168,14 +168,14 @@ dkv_status dkv_attn_decode(const dkv_config *cfg, const void *cache,
  * memory: code under HIP graph capture, tight serving loops, harnesses that
  * forbid hipMalloc.  Same arguments, kernels, launches and results as
  * dkv_attn_decode, except that the split-K partial results go to a scratch
- * array of 64 MiB that the library holds in each GPU's memory (static device
+ * array of 160 MiB that the library holds in each GPU's memory (static device
  * memory, resolved once per device on the first call there, held until the
  * process ends).  It allocates nothing, on the device or the host.
  *  - Needs the arrival counters (4 * batch * n_kv_heads bytes, rounded up to
  *    256) plus batch * n_q_heads * nsplit * (head_dim + 4) * 4 bytes of
  *    scratch, nsplit being dkv_attn_decode's split count
  *    (dkv_workspace_bytes(cfg) is an upper bound); a configuration needing
- *    more than 64 MiB returns DKV_ERR_SCRATCH before anything is launched.
+ *    more than 160 MiB returns DKV_ERR_SCRATCH before anything is launched.
  *  - Every call on one GPU shares that GPU's scratch array: calls that may
  *    overlap on one GPU (several streams, several host threads) race and must
  *    be serialised by the caller.  Nothing in it needs clearing: each call
@@ -209,15 +209,25 @@ dkv_status dkv_append_attn_decode(const dkv_config *cfg, void *cache, float *sta
                                   const int32_t *seq_lens, float softmax_scale, float *out,
                                   void *workspace, size_t workspace_bytes, dkv_stream_t stream);
 
+/* Split plan of dkv_attn_decode for cfg: *nsplit splits per (sequence,
+ * kv-head), split s covering tokens [s * split_tokens, (s + 1) * split_tokens)
+ * of the sequence.  Runs are at most 2048 tokens, 1024 in paged mode (ragged
+ * serving batches: shorter runs keep the last partial round of runs short).
+ * Errors: as dkv_check_config, DKV_ERR_ARG for null outputs. */
+dkv_status dkv_attn_decode_plan(const dkv_config *cfg, int32_t *nsplit, int32_t *split_tokens);
+
 /* The split phase of dkv_attn_decode alone: writes the per-split partial
  * results to the workspace and merges nothing (the arrival counters are left
  * untouched).  Partial record of (sequence b, query head hq, split s), at float
- * offset ((b*n_q_heads + hq)*nsplit + s)*(head_dim + 4) after the counters:
- * acc[head_dim] (sum of softmax weights times V over the split's tokens, the
- * weights relative to the running max), running max (log2 units: logits times
- * log2(e)), running sum, 2 pad floats.  For callers that merge the splits
- * themselves, and for timing the split phase alone.  Same arguments as
- * dkv_attn_decode without `out`. */
+ * offset ((b*n_q_heads + hq)*nsplit + s)*(head_dim + 4) after the counters
+ * (nsplit from dkv_attn_decode_plan): acc[head_dim] (sum of softmax weights
+ * times V over the split's tokens, the weights relative to the running max),
+ * running max (log2 units: logits times log2(e)), running sum, 2 pad floats.
+ * A split whose run starts at or past min(seq_lens[b], capacity) holds no
+ * token: its record may be left unwritten, and a merge reads only splits
+ * s < ceil(min(seq_lens[b], capacity) / split_tokens).  For callers that merge
+ * the splits themselves, and for timing the split phase alone.  Same
+ * arguments as dkv_attn_decode without `out`. */
 dkv_status dkv_attn_decode_partial(const dkv_config *cfg, const void *cache,
                                    const int32_t *block_table, const float *q,
                                    const int32_t *seq_lens, float softmax_scale,

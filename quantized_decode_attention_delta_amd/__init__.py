@@ -7,7 +7,7 @@ and :mod:`.synth` draws the seeded synthetic workloads.
 from .dkv import (  # noqa: F401
     Config, DkvError, load, status_str,
     dkv_check_config, dkv_group_record_bytes, dkv_attn_decode_noalloc, dkv_cache_bytes, dkv_state_bytes, dkv_workspace_bytes,
-    dkv_attn_decode_launches,
+    dkv_attn_decode_launches, dkv_attn_decode_plan,
     dkv_q4_0_cache_bytes, dkv_encode_prefill, dkv_append, dkv_attn_decode, dkv_append_attn_decode,
     dkv_attn_decode_ref, dkv_attn_decode_partial,
     dkv_reconstruct, dkv_export, export_shapes, dkv_q4_0_encode, dkv_q4_0_export, dkv_attn_decode_q4_0,

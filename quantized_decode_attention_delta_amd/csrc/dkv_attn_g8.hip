@@ -877,7 +877,11 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
     const bool last_partial = (L & 31) != 0 && g1 == ng && ng > g0 && ((mk >> (ng - 1 - g0)) & 1) != 0;
     const int nfull = cnt - (last_partial ? 1 : 0);
     if (cnt == 0) {
-        // a run past the sequence's end (or wholly unmapped): an empty record
+        // a run past the sequence's end: no record (the combine reads only
+        // the runs that start before the end), unless this launch merges
+        // its own records, which counts every run's arrival
+        if (g0 >= ng && !ct.out) return;
+        // a wholly unmapped run: an empty record
         RunState<D> st;
         init_state<D>(st);
         write_partial_g8<D>(st, ws, row0, G, nsplit, split, lane, j, n, ct.out != nullptr);
@@ -1079,6 +1083,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
     const int ng = (L + kf - 1) / kf;
     const int g0 = split * chunk, g1 = min(ng, g0 + chunk);
     const int64_t row0 = (int64_t)b * g.Hq + h * G;
+    if (g0 >= ng && !ct.out) return;       // past the sequence's end: no record (see k_attn_g8)
 
     // side: [keyframe 2D bytes][scales of the tile 2D bytes] of the current step;
     // vslot0: slot 0 (max |scale|) of the group's V scale plane
@@ -1363,6 +1368,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
     const int nt = (L + 31) >> 5;
     const int t0 = split * chunk, t1 = min(nt, t0 + chunk);
     const int64_t row0 = (int64_t)b * cfg.n_q_heads + h * G;
+    if (t0 >= nt) return;                  // past the sequence's end: no record (the combine skips it)
     const int tbytes = (int)q40_tile_bytes(D);
 
     // [unused 2D][K scales 2D][unused 2D][V scales 2D]: the side layout of the phases

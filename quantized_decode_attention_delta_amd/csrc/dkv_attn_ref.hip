@@ -146,27 +146,33 @@ __global__ void __launch_bounds__(kRefThreads)
 // holds channels c and c+64.  Wave w merges splits w, w+4, w+8, ...: all loads
 // of a run of 8 of its splits are issued before the merge arithmetic, so a row
 // costs about one memory round trip per 32 splits.  The four waves' (max, sum,
-// numerators) are then merged through LDS by wave 0.
+// numerators) are then merged through LDS by wave 0.  Only the splits whose
+// run starts before the sequence's end are read: ceil(min(len, cap) /
+// split_tokens) of them.
 constexpr int kCombineWaves = 4;
 
 template <int D>
 __global__ void __launch_bounds__(64 * kCombineWaves) k_combine(const float *__restrict__ ws, int nsplit,
-                                                                float *__restrict__ out)
+                                                                float *__restrict__ out,
+                                                                const int32_t *__restrict__ lens, int Hq,
+                                                                int cap_tokens, int split_tokens)
 {
     constexpr int R = part_stride(D);
     constexpr int NCH = D / 64;
     const int64_t row = blockIdx.x;
     const int c = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int L = max(0, min(lens[row / Hq], cap_tokens));
+    const int used = min(nsplit, (L + split_tokens - 1) / split_tokens);
     const float *p = ws + row * nsplit * R;
     float M = -INFINITY, den = 0.0f, num[NCH];
 #pragma unroll
     for (int k = 0; k < NCH; ++k) num[k] = 0.0f;
-    for (int s0 = wv; s0 < nsplit; s0 += 8 * kCombineWaves) {
+    for (int s0 = wv; s0 < used; s0 += 8 * kCombineWaves) {
         float ms[8], ls[8], a[8][NCH];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const int sp = s0 + u * kCombineWaves;
-            const bool ok = sp < nsplit;
+            const bool ok = sp < used;
             const float *r = p + (int64_t)(ok ? sp : 0) * R;
             ms[u] = r[D];
             ls[u] = ok ? r[D + 1] : 0.0f;
@@ -229,13 +235,17 @@ hipError_t launch_attn_ref(const dkv_config &c, const void *cache, const int32_t
     return hipGetLastError();
 }
 
-hipError_t launch_combine(const dkv_config &c, const float *ws, int nsplit, float *out, hipStream_t st)
+hipError_t launch_combine(const dkv_config &c, const float *ws, int nsplit, float *out, const int32_t *lens,
+                          int cap_tokens, int split_tokens, hipStream_t st)
 {
+    if (split_tokens < 1) return hipErrorInvalidValue;
     dim3 grid(c.batch * c.n_q_heads);
     if (c.head_dim == 64)
-        hipLaunchKernelGGL(k_combine<64>, grid, dim3(64 * kCombineWaves), 0, st, ws, nsplit, out);
+        hipLaunchKernelGGL(k_combine<64>, grid, dim3(64 * kCombineWaves), 0, st, ws, nsplit, out, lens, c.n_q_heads,
+                           cap_tokens, split_tokens);
     else
-        hipLaunchKernelGGL(k_combine<128>, grid, dim3(64 * kCombineWaves), 0, st, ws, nsplit, out);
+        hipLaunchKernelGGL(k_combine<128>, grid, dim3(64 * kCombineWaves), 0, st, ws, nsplit, out, lens,
+                           c.n_q_heads, cap_tokens, split_tokens);
     return hipGetLastError();
 }
 

@@ -417,6 +417,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
     const int nt = (L + 31) >> 5;
     const int t0 = split * chunk, t1 = min(nt, t0 + chunk);
     const int64_t row0 = (int64_t)b * cfg.n_q_heads + h * G;
+    if (t0 >= nt) return;                  // past the sequence's end: no record (the combine skips it)
 
     __shared__ float sq[16][D + 4];
     __shared__ u4 qB[2 * NB * 64];

@@ -21,7 +21,7 @@ size_t decode_partials_bytes(const dkv_config &c);
 dkv_status attn_decode_launch(const dkv_config &c, const void *cache, const int32_t *bt, const float *q,
                               const int32_t *lens, float scale, float *out, void *ws, hipStream_t st);
 
-constexpr size_t kScratchBytes = size_t(64) << 20;   // 64 MiB per device
+constexpr size_t kScratchBytes = size_t(160) << 20;  // 160 MiB per device
 static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
 // Device address of `scratch` per device ordinal, resolved on first use.

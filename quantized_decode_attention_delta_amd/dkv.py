@@ -66,6 +66,7 @@ _SIGS = {
     "dkv_state_bytes": ([_CFG], _SZ),
     "dkv_workspace_bytes": ([_CFG], _SZ),
     "dkv_attn_decode_launches": ([_CFG], _I32),
+    "dkv_attn_decode_plan": ([_CFG, _P, _P], _I32),
     "dkv_encode_prefill": ([_CFG, _P, _P, _P, _P, _P, _P, _I32, _P], _I32),
     "dkv_append": ([_CFG, _P, _P, _P, _P, _P, _P, _P], _I32),
     "dkv_attn_decode": ([_CFG, _P, _P, _P, _P, _F, _P, _P, _SZ, _P], _I32),
@@ -145,6 +146,14 @@ def dkv_workspace_bytes(cfg: Config) -> int:
 
 def dkv_attn_decode_launches(cfg: Config) -> int:
     return load().dkv_attn_decode_launches(ctypes.byref(cfg.c()))
+
+
+def dkv_attn_decode_plan(cfg: Config) -> tuple:
+    """(nsplit, split_tokens) of dkv_attn_decode's split plan for cfg."""
+    ns, tk = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check("dkv_attn_decode_plan", load().dkv_attn_decode_plan(ctypes.byref(cfg.c()), ctypes.byref(ns),
+                                                               ctypes.byref(tk)))
+    return ns.value, tk.value
 
 
 def dkv_q4_0_cache_bytes(cfg: Config) -> int:

@@ -80,6 +80,10 @@ def test_sizes():
     assert dkv.dkv_attn_decode_launches(_cfg(batch=1, n_q_heads=32, n_kv_heads=8, max_tokens=4096)) == 2
     assert dkv.dkv_attn_decode_launches(_cfg(batch=1, n_q_heads=32, n_kv_heads=8, max_tokens=512)) == 1
     assert dkv.dkv_attn_decode_launches(_cfg(head_dim=96)) == 0
+    # split plan: 2048-token runs for full caches, 1024 in paged mode
+    assert dkv.dkv_attn_decode_plan(c) == (16, 2048)
+    assert dkv.dkv_attn_decode_plan(_cfg(batch=64, n_q_heads=32, n_kv_heads=8, page_tokens=256, n_pages=8400,
+                                         max_pages_per_seq=257)) == (65, 1024)
     assert dkv.dkv_q4_0_cache_bytes(c) == 16 * 8 * 2 * 32768 * 128 // 32 * 18
     # paged comparison caches: a page of 256 tokens holds 8 tiles per kv-head
     cpg = _cfg(page_tokens=256, n_pages=5, max_pages_per_seq=3)
@@ -200,16 +204,16 @@ def test_binding_rejects_undersized_caches():
 
 def test_noalloc_decode_rejects_before_touching_the_gpu():
     """dkv_attn_decode_noalloc checks its arguments and that the split-K
-    partials fit its fixed 64 MiB scratch before anything reaches the GPU."""
+    partials fit its fixed 160 MiB scratch before anything reaches the GPU."""
     lib = _lib()
     fake = ctypes.c_void_p(0x1000)
     ok = ctypes.byref(_cfg().c())
     assert lib.dkv_attn_decode_noalloc(ok, fake, None, None, fake, 0.0, fake, None) == binding.DKV_ERR_ARG
     cpg = ctypes.byref(_cfg(page_tokens=256, n_pages=8, max_pages_per_seq=4).c())
     assert lib.dkv_attn_decode_noalloc(cpg, fake, None, fake, fake, 0.0, fake, None) == binding.DKV_ERR_ARG
-    # 64 sequences x 128 query heads x 32 splits x 132 floats = 138 MB of partials
-    big = _cfg(batch=64, n_q_heads=128, n_kv_heads=8, max_tokens=65536)
-    assert dkv.dkv_workspace_bytes(big) > 64 << 20
+    # 64 sequences x 256 query heads x 32 splits x 132 floats = 277 MB of partials
+    big = _cfg(batch=64, n_q_heads=256, n_kv_heads=16, max_tokens=65536)
+    assert dkv.dkv_workspace_bytes(big) > 160 << 20
     assert lib.dkv_attn_decode_noalloc(ctypes.byref(big.c()), fake, None, fake, fake, 0.0, fake,
                                        None) == binding.DKV_ERR_SCRATCH
     assert "scratch" in dkv.status_str(binding.DKV_ERR_SCRATCH)
