@@ -44,14 +44,18 @@ STATIC_CONFIGS = ("tiny", "8b", "long_kf32", "long_kf128", "long_kf512", "70b")
 # HBM bytes (read + written) per launch of the split-phase kernel, from
 # rocprofv3 FETCH_SIZE (x2.0) and WRITE_SIZE (x1.0) counters, each scaled by
 # what the counter reads for a 1 GiB device copy.  Valid only for the kernel
-# sources they were measured on (sha256 below); otherwise traffic is null.
+# and split-plan sources they were measured on (sha256 below); otherwise
+# traffic is null.
 MEASURED_TRAFFIC = {
     "sources": {
-        "dkv_attn_g8.hip": "0c343f056b996ccd86343ee0541bfcd9fe4e684bb2ca9085089d8036a6c4df02",
-        "dkv_fused_common.h": "fdaf23f919b7f5576833b80881851acabb27f65d569c3f957be0ac5f1f8f35bd",
-        "dkv_common.h": "3b302839f810f8e0f48d1491035b2d391a13053c69aed1c169162f01349d5e17",
+        "dkv_attn_g8.hip": "4c15d131d85da40d9b134a199a5b97110da5b2d46a1227aae2d5a97d1871feb8",
+        "dkv_fused_common.h": "79601ea867ca8f07e95b7c0f547216f6aa9900bf97aefdfe8dbcd5b4ab895fa2",
+        "dkv_common.h": "449c2571a6f5c87c7b0e87a22e301314a1a48d9589aa90f7c26c8087b7128561",
+        "dkv_append.h": "be07c04e9857cdcd9f08e6a2526b04f9ce5e0a510bffa70e7ff091ce2d00e7dc",
+        "dkv_q40.h": "d4b0a8142dfd210e9daa6a9ef282fe5ccb37c516b007f54681f8c9f93af0c73c",
+        "dkv_api.cpp": "8b9042e9f895f86f9663a2ee931362d03e769725770dfcca41e87d8a2c4f4abb",
     },
-    "per_launch": {"70b": 692390917},
+    "per_launch": {"mixed": 3161777369, "70b": 684723848, "long_kf512": 159041587, "long_kf128": 161551214},
 }
 
 
