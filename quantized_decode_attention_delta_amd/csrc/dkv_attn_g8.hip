@@ -260,10 +260,12 @@ __device__ inline float k_phase_g8(const uint32_t *kc, const uint8_t *sb, const 
 // Token 0 is the keyframe: its code row reads as zeros and its scale slot
 // holds the group's largest |scale| (used by the V side), so its delta term
 // is dropped here and its logit is the carry alone.
+// For a tile inside a long group (forward kernel below) `first` is false: the
+// tile's token 0 is a delta like the others; `total` is the tile's sum.
 template <int D, bool FULL>
 __device__ inline float k_phase_g8b(const uint32_t *kc, const uint8_t *sb, int nval, int j, int n, const G8Ops &op,
                                     const h8 (&qh)[2][D / 32], const f4 (&bias)[D / 32], float c2E, float carry,
-                                    float (&Lg)[4])
+                                    float (&Lg)[4], bool first, float &total)
 {
     constexpr int NB = D / 32, NP = NB / 2;
     const int h2 = n >> 3;
@@ -293,12 +295,13 @@ __device__ inline float k_phase_g8b(const uint32_t *kc, const uint8_t *sb, int n
     // units); the factor 2^20 is folded into c2E
 #pragma unroll
     for (int i = 0; i < 4; ++i) Lg[i] = (FULL || tb + i < nval) ? u[i] : 0.0f;
-    Lg[0] = tb == 0 ? 0.0f : Lg[0];
+    Lg[0] = (first && tb == 0) ? 0.0f : Lg[0];
 #pragma unroll
     for (int i = 1; i < 4; ++i) Lg[i] += Lg[i - 1];
     float incl, all;
     rows_prefix(Lg[3], j, incl, all);
     const float allx = other_half(all);           // (every lane takes part in the exchange)
+    total = all + allx;
     const float off = (incl - Lg[3]) + (h2 ? allx : 0.0f) + carry;
 #pragma unroll
     for (int i = 0; i < 4; ++i) Lg[i] += off;
@@ -319,23 +322,24 @@ __device__ inline float k_phase_g8b(const uint32_t *kc, const uint8_t *sb, int n
 // cnt re-read the last group), kf_logits_g8 writes out[x * 8 + hq]: the logit
 // of head hq for the group at position x, in the units of k_phase_g8b's logits
 // (2^-20 of the query units).
-template <int D>
-__device__ inline void kf_load_g8(u4 (&a)[4][D / 32], const int64_t *list, int cnt, const uint8_t *cache, int j, int n)
+template <int D, int NSET = 4>
+__device__ inline void kf_load_g8(u4 (&a)[NSET][D / 32], const int64_t *list, int cnt, const uint8_t *cache, int j,
+                                  int n)
 {
     constexpr int NB = D / 32;
 #pragma unroll
-    for (int c4 = 0; c4 < 4; ++c4) {
+    for (int c4 = 0; c4 < NSET; ++c4) {
         const u4 *kfp = (const u4 *)(cache + list[min(16 * c4 + n, cnt - 1)]) + j * NB;
 #pragma unroll
         for (int bb = 0; bb < NB; ++bb) a[c4][bb] = kfp[bb];
     }
 }
-template <int D>
-__device__ inline void kf_logits_g8(float *out, const u4 (&a)[4][D / 32], int cnt, const G8Ops &op, int j, int n)
+template <int D, int NSET = 4>
+__device__ inline void kf_logits_g8(float *out, const u4 (&a)[NSET][D / 32], int cnt, const G8Ops &op, int j, int n)
 {
     constexpr int NB = D / 32;
 #pragma unroll
-    for (int c4 = 0; c4 < 4; ++c4) {
+    for (int c4 = 0; c4 < NSET; ++c4) {
         const int c = 16 * c4;
         if (c >= cnt) break;
         f4 C = f4{0, 0, 0, 0};
@@ -406,13 +410,6 @@ __device__ inline void update_g8(RunState<D> &st, float m_g, const uint32_t *vs0
     update_g8_vmx<D>(st, m_g, vmx, lkf, none);
 }
 
-// V phase of one 32-token tile.  sb: the tile's V side data in LDS ([keyframe
-// 2D bytes][scales 2D bytes]); Lg: the tile's prefixed logits from the K phase;
-// carry: the sum of the softmax weights of the later tiles of the group.
-// Adds the tile's weighted V codes to the accumulators; a FIRST tile (the last
-// one processed) also adds the keyframe with the group's total weight.
-// Returns the tile's weight sum.  DELTA = false: plain Q4_0 tile (the weight of
-// token t is p_t itself, no suffix sums, no keyframe).
 // Keyframe term of a group: acc += pk * x0, pk = the group's weight in
 // accumulator units 2^(beta-20); sb: the group's V side data in LDS.
 template <int D>
@@ -430,6 +427,66 @@ __device__ inline void kf_fma_g8(RunState<D> &st, const uint8_t *sb, float pk, i
     }
 }
 
+// The weighted V codes of one tile: Sp[T][i] is the weight (in the units
+// 2^beta, times 16 on the slots i even) of token 16T + 4j + i for this lane's
+// head column; it is multiplied by the token's scale of the lane's block of
+// each pair, split hi + lo fp16, and the code tile's products accumulate
+// into st.acc (the codes) and st.Z (their "-8").
+template <int D, bool FULL>
+__device__ inline void v_accumulate_g8(RunState<D> &st, const uint32_t *vc, const uint8_t *sb, const float (&Sp)[2][4],
+                                       int nval, int j, int n, h8 AZ)
+{
+    constexpr int NB = D / 32, NP = NB / 2;
+    const int h2 = n >> 3;
+    // scales of the 8 token slots for this lane's block of each pair
+    uint32_t vs[2][4];
+    {
+        const int wsel = NB == 4 ? h2 : 0;
+#pragma unroll
+        for (int T = 0; T < 2; ++T) {
+            const uint32_t *sp = (const uint32_t *)(sb + 2 * D + (16 * T + 4 * j) * 2 * NB) + wsel;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                uint32_t w = sp[i * NP];
+                if constexpr (NB == 2) w >>= 16 * h2;        // block h2 of the single pair
+                vs[T][i] = (FULL || 16 * T + 4 * j + i < nval) ? w : 0u;
+            }
+        }
+    }
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        uint32_t whd[4], wld[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            uint32_t hi, lo;
+            if (NB == 4 && p == 1)
+                split_w<1>(vs[0][i], vs[1][i], Sp[0][i], Sp[1][i], hi, lo);
+            else
+                split_w<0>(vs[0][i], vs[1][i], Sp[0][i], Sp[1][i], hi, lo);
+            whd[i] = hi;
+            wld[i] = lo;
+        }
+        const h8 Wh = __builtin_bit_cast(h8, u4{whd[0], whd[1], whd[2], whd[3]});
+        const h8 Wl = __builtin_bit_cast(h8, u4{wld[0], wld[1], wld[2], wld[3]});
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) {
+            const int cc = 4 * p + c4;
+            const h8 A = unpack8(vc[cc]);
+            st.acc[cc] = mfma(A, Wh, st.acc[cc]);
+            st.acc[cc] = mfma(A, Wl, st.acc[cc]);
+        }
+        st.Z[p] = mfma(AZ, Wh, st.Z[p]);
+        st.Z[p] = mfma(AZ, Wl, st.Z[p]);
+    }
+}
+
+// V phase of one 32-token tile.  sb: the tile's V side data in LDS ([keyframe
+// 2D bytes][scales 2D bytes]); Lg: the tile's prefixed logits from the K phase;
+// carry: the sum of the softmax weights of the later tiles of the group.
+// Adds the tile's weighted V codes to the accumulators; a FIRST tile (the last
+// one processed) also adds the keyframe with the group's total weight.
+// Returns the tile's weight sum.  DELTA = false: plain Q4_0 tile (the weight of
+// token t is p_t itself, no suffix sums, no keyframe).
 // KFD = false: a FIRST tile leaves the keyframe term to the caller (the return
 // value plus carry is the group's weight).
 template <int D, bool FULL, bool FIRST, bool DELTA = true, bool KFD = true>
@@ -476,47 +533,7 @@ __device__ inline float v_phase_g8(RunState<D> &st, const uint32_t *vc, const ui
         Sp[1][i] = h2 ? y : x;
     }
     if constexpr (FIRST) Sp[0][0] = j == 0 ? 0.0f : Sp[0][0];      // keyframe slot
-
-    // scales of the 8 token slots for this lane's block of each pair
-    uint32_t vs[2][4];
-    {
-        const int wsel = NB == 4 ? h2 : 0;
-#pragma unroll
-        for (int T = 0; T < 2; ++T) {
-            const uint32_t *sp = (const uint32_t *)(sb + 2 * D + (16 * T + 4 * j) * 2 * NB) + wsel;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                uint32_t w = sp[i * NP];
-                if constexpr (NB == 2) w >>= 16 * h2;        // block h2 of the single pair
-                vs[T][i] = (FULL || 16 * T + 4 * j + i < nval) ? w : 0u;
-            }
-        }
-    }
-#pragma unroll
-    for (int p = 0; p < NP; ++p) {
-        uint32_t whd[4], wld[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            uint32_t hi, lo;
-            if (NB == 4 && p == 1)
-                split_w<1>(vs[0][i], vs[1][i], Sp[0][i], Sp[1][i], hi, lo);
-            else
-                split_w<0>(vs[0][i], vs[1][i], Sp[0][i], Sp[1][i], hi, lo);
-            whd[i] = hi;
-            wld[i] = lo;
-        }
-        const h8 Wh = __builtin_bit_cast(h8, u4{whd[0], whd[1], whd[2], whd[3]});
-        const h8 Wl = __builtin_bit_cast(h8, u4{wld[0], wld[1], wld[2], wld[3]});
-#pragma unroll
-        for (int c4 = 0; c4 < 4; ++c4) {
-            const int cc = 4 * p + c4;
-            const h8 A = unpack8(vc[cc]);
-            st.acc[cc] = mfma(A, Wh, st.acc[cc]);
-            st.acc[cc] = mfma(A, Wl, st.acc[cc]);
-        }
-        st.Z[p] = mfma(AZ, Wh, st.Z[p]);
-        st.Z[p] = mfma(AZ, Wl, st.Z[p]);
-    }
+    v_accumulate_g8<D, FULL>(st, vc, sb, Sp, nval, j, n, AZ);
     if constexpr (FIRST && KFD) kf_fma_g8<D>(st, sb, (Pt + carry) * (st.bsc * 0x1p-20f), j);
     return Pt;
 }
@@ -944,6 +961,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
     // weight of head column n of the batch's group j (the B operand of an
     // fp32 16x16x4 matrix instruction whose A operand holds the 4 keyframes)
     float kfw = 0.0f;
+    float tot_unused;                         // (runs of kf = 32 groups carry no logits between tiles)
 
     auto sbp = [&](int x) { return (const uint8_t *)side[x & (NSLOT - 1)]; };
     auto stage = [&](const G8KRegs<D> &r, int x) {
@@ -974,7 +992,8 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
         stage(kb[1], 1);
         __syncthreads();
         {
-            const float m = k_phase_g8b<D, true>(kb[0].kc, sbp(0), 32, j, n, op, qh, kbias, c2Eu, klog(0), Lg);
+            const float m = k_phase_g8b<D, true>(kb[0].kc, sbp(0), 32, j, n, op, qh, kbias, c2Eu, klog(0), Lg,
+                                                 true, tot_unused);
             update_g8_vmx<D>(st, m, group_vmax<D>(sbp(0)), 5, kfw);
         }
         // step i (u = i % NBUF): fetch the K part of group i + 1 + LEAD and the
@@ -992,7 +1011,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
             kfw = j == u ? pt * (st.bsc * 0x1p-20f) : kfw;
             if constexpr (u == NBUF - 1) kf_flush(i, true);
             const float m = k_phase_g8b<D, true>(kb[un].kc, sbp(i + 1), 32, j, n, op, qh, kbias, c2Eu,
-                                                 klog(min(i + 1, nfull - 1)), Lg);
+                                                 klog(min(i + 1, nfull - 1)), Lg, true, tot_unused);
             update_g8_vmx<D>(st, m, group_vmax<D>(sbp(i + 1)), 5, kfw);
             stage(kb[u2], i + 2);
             return i + 1 < nfull;
@@ -1048,7 +1067,8 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
         __syncthreads();
         const int nval = L - (ng - 1) * 32;
         float Lg[4];
-        const float m = k_phase_g8b<D, false>(kr.kc, sbp(nfull), nval, j, n, op, qh, kbias, c2Eu, klog(nfull), Lg);
+        const float m = k_phase_g8b<D, false>(kr.kc, sbp(nfull), nval, j, n, op, qh, kbias, c2Eu, klog(nfull), Lg,
+                                              true, tot_unused);
         update_g8_vmx<D>(st, m, group_vmax<D>(sbp(nfull)), 5, kfw);
         v_phase_g8<D, false, true>(st, vr.vc, sbp(nfull) + 4 * D, Lg, nval, j, n, c2Eu, AZ, -0.0f);
     }
@@ -1311,6 +1331,395 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
     if (ct.out) combine_tail_g8<D>(ws, ct, row0, G, nsplit, (int64_t)b * g.Hkv + h, lane);
 }
 
+// ============================================================ kf = 32*NT, G <= 4
+// Long groups (kf = 64..512) with at most 4 query heads per kv-head, in one
+// forward pass.  With P the group's total softmax weight, d_t the delta of
+// token t and E_t the weight of the group's tokens before t, the weighted sum
+// of the group's reconstructions is
+//   sum_t p_t xhat_t = P * (x0 + sum_t d_t) - sum_t E_t * d_t,
+// so every tile's V codes can be weighted as soon as its logits are known
+// (with -E_t), and the K and V sides of a tile share one step, pipelined as
+// in the kf = 32 kernel: step x runs the V phase of tile x and the K phase of
+// tile x + 1.  Operand column 4 of each column half is spare when G <= 4; it
+// weights every delta with 1 and so sums the group's deltas.  At the group's
+// last tile every head adds P times its keyframe and that sum.  Against the
+// two-pass kernel (K pass, then V pass in reverse) a tile takes one step
+// instead of two and no logits go through LDS.
+
+// Softmax state update of the forward kernel: as update_g8_vmx, but the
+// lanes of the delta-sum column (dcol) are rescaled only for the change of
+// the weight units, and the running weight of the open group (ecarry) with
+// the max.
+template <int D>
+__device__ inline void update_fwd(RunState<D> &st, float m_g, uint32_t vmx, int lkf, bool dcol, float &ecarry)
+{
+    constexpr int NCC = D / 16, NP = D / 64;
+    const int ev = (vmx >> 10) == 0 ? -14 : (int)(vmx >> 10) - 15;
+    const int beta_g = (vmx == 0 ? 24 - lkf : 10 - lkf - ev) - kLazyMax;
+    const float m_new = m_g > st.m + (float)kLazyMax ? m_g : st.m;
+    const int beta_new = min(st.beta, beta_g);
+    const float a_m = __builtin_amdgcn_exp2f(st.m - m_new);
+    if (__any(m_new != st.m || beta_new != st.beta)) {
+        st.bsc = ldexpf(1.0f, beta_new);
+        const float ab = ldexpf(1.0f, beta_new - st.beta);
+        const float alpha = dcol ? ab : a_m * ab;
+#pragma unroll
+        for (int cc = 0; cc < NCC; ++cc) st.acc[cc] *= alpha;
+#pragma unroll
+        for (int p = 0; p < NP; ++p) st.Z[p] *= alpha;
+        st.l *= a_m;
+        ecarry *= a_m;
+    }
+    st.m = m_new;
+    st.beta = beta_new;
+}
+
+// V phase of one tile of a long group in the forward kernel: the weight of
+// token t's codes is -E_t (E_t: the weight of the group's tokens before t,
+// ecarry from the earlier tiles), 1 in the delta-sum column; the group's
+// keyframe slot (token 0 of its first tile) gets none.  Returns the tile's
+// weight sum.
+template <int D, bool FULL>
+__device__ inline float v_phase_fwd(RunState<D> &st, const uint32_t *vc, const uint8_t *sb, const float (&Lg)[4],
+                                    int nval, int j, int n, float c2E, h8 AZ, float ecarry, bool first, bool dcol)
+{
+    const int h2 = n >> 3;
+    const int tb = 16 * h2 + 4 * j;
+    float S[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(Lg[i], c2E, -st.m));
+        S[i] = (FULL || tb + i < nval) ? p : 0.0f;
+    }
+    // exclusive prefix: in-lane, over rows j, then the first half's total
+    const float s01 = S[0] + S[1], s012 = s01 + S[2], s0123 = s012 + S[3];
+    float incl, all;
+    rows_prefix(s0123, j, incl, all);
+    const float allx = other_half(all);
+    const float Pt = all + allx;
+    const float off = (incl - s0123) + (h2 ? allx : 0.0f) + ecarry;
+    const float E[4] = {off, off + S[0], off + s01, off + s012};
+    st.l += Pt;
+    const float bsc = st.bsc, bsc16 = 16.0f * bsc;
+    float Sp[2][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float w = dcol ? 1.0f : -E[i];
+        const float y = w * ((i & 1) ? bsc : bsc16);
+        const float x = other_half(y);
+        Sp[0][i] = h2 ? x : y;
+        Sp[1][i] = h2 ? y : x;
+    }
+    Sp[0][0] = (first && j == 0) ? 0.0f : Sp[0][0];      // keyframe slot
+    v_accumulate_g8<D, FULL>(st, vc, sb, Sp, nval, j, n, AZ);
+    return Pt;
+}
+
+// Close a group in the forward kernel: every head adds P (the group's total
+// weight) times its keyframe (vkf: the group's V keyframe, 2D bytes in LDS)
+// plus the group's delta sum, which the delta-sum column's lane of the same
+// row and column half passes through LDS (rbuf, 8 x D/16 f4); the column then
+// starts the next group at zero.  The barrier keeps the other lanes' reads
+// after those stores: the stores are conditional, and without it the compiler
+// may move a lane's read ahead of another lane's store (for the hardware one
+// wave's LDS accesses are in order; for the compiler they are separate threads).
+template <int D>
+__device__ inline void group_end_fwd(RunState<D> &st, f4 *rbuf, const uint8_t *vkf, float P, int j, int n, bool dcol)
+{
+    constexpr int NCC = D / 16, NP = D / 64;
+    f4 *rb = rbuf + ((n >> 3) * 4 + j) * NCC;
+    if (dcol) {
+#pragma unroll
+        for (int cc = 0; cc < NCC; ++cc) rb[cc] = st.acc[cc] + st.Z[cc >> 2];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int cc = 0; cc < NCC; ++cc) {
+        const f4 r = rb[cc];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st.acc[cc][i] = __builtin_fmaf(P, r[i], st.acc[cc][i]);
+    }
+    kf_fma_g8<D>(st, vkf, P * (st.bsc * 0x1p-20f), j);
+#pragma unroll
+    for (int cc = 0; cc < NCC; ++cc)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st.acc[cc][i] = dcol ? 0.0f : st.acc[cc][i];
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st.Z[p][i] = dcol ? 0.0f : st.Z[p][i];
+}
+
+// Fetch of one tile part: the side data (per-lane offset with the tile's
+// term folded in) and the K code pieces, or the V code words; `soff` is the
+// tile's offset in the code planes.
+template <int D>
+__device__ inline void load_tile_k(G8KRegs<D> &r, const uint8_t *rec, int rec_bytes, int side, int k0, int k1,
+                                   int soff)
+{
+    constexpr int NB = D / 32;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)rec, (short)0, rec_bytes, 0x00020000);
+    r.side = __builtin_amdgcn_raw_buffer_load_b128(rs, side, 0, kStream);
+    if constexpr (NB == 4) {
+        const u4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, k0, soff, kStream);
+        const u4 c = __builtin_amdgcn_raw_buffer_load_b128(rs, k1, soff, kStream);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            r.kc[k] = a[k];
+            r.kc[NB + k] = c[k];
+        }
+    } else {
+        const u2 a = __builtin_amdgcn_raw_buffer_load_b64(rs, k0, soff, kStream);
+        const u2 c = __builtin_amdgcn_raw_buffer_load_b64(rs, k1, soff, kStream);
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            r.kc[k] = a[k];
+            r.kc[NB + k] = c[k];
+        }
+    }
+}
+template <int D>
+__device__ inline void load_tile_v(G8VRegs<D> &r, const uint8_t *rec, int rec_bytes, int v, int soff)
+{
+    constexpr int NCC = D / 16;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)rec, (short)0, rec_bytes, 0x00020000);
+#pragma unroll
+    for (int q4 = 0; q4 < NCC / 4; ++q4) {
+        const u4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, v + 16 * q4, soff, kStream);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) r.vc[4 * q4 + k] = a[k];
+    }
+}
+
+template <int D>
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
+    k_attn_lfwd_g8(dkv_config cfg, const uint8_t *cache, const int32_t *__restrict__ bt,
+                   const float *__restrict__ q, const int32_t *__restrict__ seq_lens, float scale_log2,
+                   float *ws, int nsplit, int chunk, CombineTail ct)
+{
+    constexpr int NB = D / 32, NCC = D / 16;
+    constexpr int SIDE_LANES = D / 4;
+    constexpr int BATCH = 32;                 // groups per run (runs of at most 2048 tokens, kf >= 64)
+    constexpr int LEAD = kG8Lead, NBUF = LEAD + 1;
+    static_assert(NBUF == 4, "rounds of 4 steps rotate the 4 fetch buffers");
+    constexpr int NSLOT = 4;                  // a tile's side data lives from its staging to its V phase
+    const Geom g = make_geom(cfg);
+    const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int lane = threadIdx.x, j = lane >> 4, n = lane & 15;
+    const int G = g.G;
+    const int kf = g.kf, NT = kf >> 5;
+    const int lkf = 32 - __builtin_clz((unsigned)kf - 1u);       // kf <= 2^lkf
+    const int L = min(seq_lens[b], g.cap_tokens);
+    const int ng = (L + kf - 1) / kf;
+    const int g0 = split * chunk, g1 = min(ng, g0 + chunk);
+    const int64_t row0 = (int64_t)b * g.Hq + h * G;
+    const bool dcol = (n & 7) == 4;           // the delta-sum column of each column half
+
+    __shared__ __attribute__((aligned(16))) uint32_t side[NSLOT][2 * D];
+    __shared__ __attribute__((aligned(16))) uint32_t vkf[2][D / 2];     // V keyframes of the open groups
+    __shared__ f4 rbuf[8 * NCC];                                       // delta sums at a group's end
+    __shared__ int64_t glist[BATCH];
+    __shared__ G8Shared<D> sh;
+    __shared__ float kls[BATCH * 8];          // keyframe logits [position][head]
+
+    const int x0 = g0 + lane;
+    const int64_t o0 = (lane < BATCH && x0 < g1) ? group_offset(g, bt, b, h, x0) : -1;
+    const uint64_t mk = __ballot(o0 >= 0);
+    const int cnt = __popcll(mk);
+    if (cnt == 0) {
+        // past the sequence's end: no record (the combine reads only the runs
+        // that start before the end), unless this launch merges its records
+        if (g0 >= ng && !ct.out) return;
+        RunState<D> st;
+        init_state<D>(st);
+        write_partial_g8<D>(st, ws, row0, G, nsplit, split, lane, j, n, ct.out != nullptr);
+        if (ct.out) combine_tail_g8<D>(ws, ct, row0, G, nsplit, (int64_t)b * g.Hkv + h, lane);
+        return;
+    }
+    if (o0 >= 0) glist[__builtin_amdgcn_mbcnt_hi((uint32_t)(mk >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mk, 0u))] = o0;
+    __syncthreads();
+    // the run's tiles: NT per group, fewer for the sequence's last group; a
+    // partial last tile is taken on its own after the pipeline
+    const bool lastg = g1 == ng && ng > g0 && ((mk >> (ng - 1 - g0)) & 1) != 0;
+    const int ntot = lastg ? (cnt - 1) * NT + ((L - (ng - 1) * kf + 31) >> 5) : cnt * NT;
+    const bool last_partial = lastg && (L & 31) != 0;
+    const int nfull = ntot - (last_partial ? 1 : 0);
+    const uint32_t magic = (65536u + (uint32_t)NT - 1u) / (uint32_t)NT;     // x / NT for x < 65536 / NT
+    auto grp = [&](int x) { return (int)(((uint32_t)x * magic) >> 16); };
+
+    // lane offsets in a group record for its first tile (t0) and for later
+    // tiles (tn, to which the tile's code offset 16*D*t is added as soffset;
+    // the scale lanes of the side data add 64*NB*t)
+    const LaneOffsets lo = lane_offsets<D>(g, lane, j, n, true);
+    const bool kf_lane = lane < D / 8, vkf_lane = lane >= SIDE_LANES && lane < SIDE_LANES + D / 8;
+    const int side_t0 = kf_lane ? 0x40000000 : lo.side;              // K keyframes: read by the prologue
+    const int side_tn = (kf_lane || vkf_lane) ? 0x40000000 : lo.side;
+    const int side_mul = (lane < 2 * SIDE_LANES && !kf_lane && !vkf_lane) ? 64 * NB : 0;
+    const int k0_t0 = lo.k0;                                         // token 0 of the group: zeros
+    const int k0_tn = n == 0 ? (int)g.off_kcd - D / 2 + 4 * j * NB : lo.k0;
+    const int rec_bytes = (int)g.rec;
+    // tile x's record (past the whole tiles: the last whole one again, still in
+    // L2; a run of only a partial tile fetches that one)
+    auto rec_of = [&](int x) { return cache + uniform_offset(glist, grp(x)); };
+    auto clampx = [&](int x) { return x < nfull ? x : max(nfull - 1, 0); };
+    auto fetch_k = [&](G8KRegs<D> &r, int x) {
+        const int xc = clampx(x), t = xc - grp(xc) * NT;
+        load_tile_k<D>(r, rec_of(xc), rec_bytes, (t == 0 ? side_t0 : side_tn) + side_mul * t,
+                       t == 0 ? k0_t0 : k0_tn, lo.k1, 16 * D * t);
+    };
+    auto fetch_v = [&](G8VRegs<D> &r, int x) {
+        const int xc = clampx(x), t = xc - grp(xc) * NT;
+        load_tile_v<D>(r, rec_of(xc), rec_bytes, lo.v, 16 * D * t);
+    };
+
+    float qraw[NB][8];
+    load_q_g8<D>(qraw, q, row0, G, j, n);
+    u4 kfa[2][NB];
+    kf_load_g8<D, 2>(kfa, glist, cnt, cache, j, n);
+    G8KRegs<D> kb[NBUF];
+    G8VRegs<D> vb[NBUF];
+#pragma unroll
+    for (int y = 0; y <= LEAD; ++y) {
+        fetch_k(kb[y % NBUF], y);
+        if (y < LEAD) fetch_v(vb[y % NBUF], y);
+    }
+
+    G8Ops op;
+    float qs[NB];
+    const float c2E = setup_g8<D>(sh, op, qraw, G, scale_log2, j, n, qs);
+    const h8 AZ = v_minus8_operand();
+    f4 kbias[NB];
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) {
+        const float xb = -8.0f * 0x1p-20f * qs[bb];
+        kbias[bb] = f4{xb, xb, xb, xb};
+    }
+    kf_logits_g8<D, 2>(kls, kfa, cnt, op, j, n);
+    auto klog = [&](int k) { return kls[k * 8 + (n & 7)]; };
+    const float c2Eu = c2E * 1048576.0f;
+    h8 qh[2][NB];
+#pragma unroll
+    for (int T = 0; T < 2; ++T)
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb) qh[T][bb] = as_h8(op.qk[T][(2 * bb) * 32]);
+
+    RunState<D> st;
+    init_state<D>(st);
+    float ecarry = 0.0f;                      // weight of the open group's earlier tokens
+    float kcin = 0.0f, kcarry = 0.0f;         // logit carry into the last K phase, and out of it
+    uint32_t vmx = 0;                         // the open group's largest |V scale|
+
+    auto sbp = [&](int x) { return (const uint8_t *)side[x & (NSLOT - 1)]; };
+    // staging of tile x (group k, tile t of it) in slot x % NSLOT: its side
+    // data, and for a group's first tile its V keyframe, kept for the group's end
+    auto stage_at = [&](const G8KRegs<D> &r, int x, int k, int t) {
+        if (2 * SIDE_LANES == 64 || lane < 2 * SIDE_LANES) ((u4 *)side[x & (NSLOT - 1)])[fresh_lane_id()] = r.side;
+        if (t == 0 && vkf_lane) ((u4 *)vkf[k & 1])[lane - SIDE_LANES] = r.side;
+    };
+    auto stage = [&](const G8KRegs<D> &r, int x) {
+        const int xc = clampx(x), k = grp(xc);
+        stage_at(r, x, k, xc - k * NT);
+    };
+    // K phase of tile x (FULL) with its carry; x past the whole tiles repeats
+    // the last one with the carry it had, so its maximum changes nothing
+    auto kphase = [&](const G8KRegs<D> &r, int x, float (&Lg)[4]) {
+        const bool past = x >= nfull;
+        const int xc = clampx(x), k = grp(xc), t = xc - k * NT;
+        const bool first = t == 0;
+        const float cin = past ? kcin : first ? klog(k) : kcarry;
+        float tot;
+        const float m = k_phase_g8b<D, true>(r.kc, sbp(x), 32, j, n, op, qh, kbias, c2Eu, cin, Lg, first, tot);
+        kcin = cin;
+        kcarry = cin + tot;
+        vmx = first ? group_vmax<D>(sbp(x)) : vmx;
+        update_fwd<D>(st, m, vmx, lkf, dcol, ecarry);
+    };
+    // after tile x's V phase (its weight already in ecarry) and the next K
+    // phase's update: close x's group at the group's last tile
+    auto close = [&](int x) {
+        const int k = grp(x), t = x - k * NT;
+        if (t == NT - 1 || x == ntot - 1) {
+            group_end_fwd<D>(st, rbuf, (const uint8_t *)vkf[k & 1], ecarry, j, n, dcol);
+            ecarry = 0.0f;
+        }
+    };
+
+    if (nfull > 0) {
+        float Lg[4];
+        __syncthreads();
+        stage(kb[0], 0);
+        stage(kb[1], 1);
+        __syncthreads();
+        kphase(kb[0], 0, Lg);
+        // step x (u = x % NBUF): fetch the K part of tile x + 1 + LEAD and the V
+        // part of tile x + LEAD, V phase of x, K phase of x + 1, stage x + 2;
+        // then close x's group if x is its last tile
+        auto step = [&](int x, auto uc) {
+            constexpr int u = decltype(uc)::value;
+            constexpr int un = (u + 1) % NBUF, u2 = (u + 2) % NBUF, ulast = (u + LEAD) % NBUF;
+            fetch_k(kb[u], x + 1 + LEAD);
+            fetch_v(vb[ulast], x + LEAD);
+            const int t = x - grp(x) * NT;
+            ecarry += v_phase_fwd<D, true>(st, vb[u].vc, sbp(x) + 4 * D, Lg, 32, j, n, c2Eu, AZ, ecarry, t == 0,
+                                           dcol);
+            // (the V phase reads Lg before the K phase of x + 1 overwrites it)
+            kphase(kb[un], x + 1, Lg);
+            stage(kb[u2], x + 2);
+            close(x);
+        };
+        const bool older = (blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z)) <
+                           (gridDim.x * gridDim.y * gridDim.z) / 2;
+        const int q1 = nfull >> 2, q2 = nfull >> 1, q3 = (3 * nfull) >> 2;
+        if (older) __builtin_amdgcn_s_setprio(2); else __builtin_amdgcn_s_setprio(3);
+        const int nround = nfull / NBUF, nrest = nfull % NBUF;
+        for (int r = 0; r < nround; ++r) {
+            const int x = r * NBUF;
+            if (x >= q1) {
+                const int lvl = (x >= q3 ? 0 : x >= q2 ? 1 : 2) - (older ? 1 : 0);
+                if (lvl <= 0)
+                    __builtin_amdgcn_s_setprio(0);
+                else if (lvl == 1)
+                    __builtin_amdgcn_s_setprio(1);
+                else
+                    __builtin_amdgcn_s_setprio(2);
+            }
+            step(x, IC<0>{});
+            step(x + 1, IC<1>{});
+            step(x + 2, IC<2>{});
+            step(x + 3, IC<3>{});
+        }
+        if (nrest > 0) {
+            const int x = nround * NBUF;
+            step(x, IC<0>{});
+            if (nrest > 1) step(x + 1, IC<1>{});
+            if (nrest > 2) step(x + 2, IC<2>{});
+        }
+        __builtin_amdgcn_s_setprio(0);
+    }
+    if (last_partial) {
+        const int x = ntot - 1, k = grp(x), t = x - k * NT;
+        G8KRegs<D> kr;
+        G8VRegs<D> vr;
+        const uint8_t *rec = cache + uniform_offset(glist, k);
+        load_tile_k<D>(kr, rec, rec_bytes, (t == 0 ? side_t0 : side_tn) + side_mul * t, t == 0 ? k0_t0 : k0_tn,
+                       lo.k1, 16 * D * t);
+        load_tile_v<D>(vr, rec, rec_bytes, lo.v, 16 * D * t);
+        __syncthreads();
+        stage_at(kr, x, k, t);
+        __syncthreads();
+        const int nval = L - (ng - 1) * kf - 32 * t;
+        const float cin = t == 0 ? klog(k) : kcarry;
+        float Lg[4], tot;
+        const float m = k_phase_g8b<D, false>(kr.kc, sbp(x), nval, j, n, op, qh, kbias, c2Eu, cin, Lg, t == 0, tot);
+        vmx = t == 0 ? group_vmax<D>(sbp(x)) : vmx;
+        update_fwd<D>(st, m, vmx, lkf, dcol, ecarry);
+        ecarry += v_phase_fwd<D, false>(st, vr.vc, sbp(x) + 4 * D, Lg, nval, j, n, c2Eu, AZ, ecarry, t == 0, dcol);
+        close(x);
+    }
+    write_partial_g8<D>(st, ws, row0, G, nsplit, split, lane, j, n, ct.out != nullptr);
+    if (ct.out) combine_tail_g8<D>(ws, ct, row0, G, nsplit, (int64_t)b * g.Hkv + h, lane);
+}
+
 // With `append` (kf = 32 only), the kernel appends each sequence's new token
 // before it decodes: append->positions null means no append.
 // With `tail` (non-null out), the kernel also merges the partial records
@@ -1330,8 +1739,18 @@ hipError_t launch_attn_g8(const dkv_config &c, const void *cache, const int32_t 
             hipLaunchKernelGGL(k_attn_g8<128>, grid, dim3(64), 0, st, c, (const uint8_t *)cache, bt, q, lens,
                                scale_log2, ws, nsplit, chunk, ap, ct);
     } else {
-        if (append && append->positions) return hipErrorInvalidValue;     // the long-interval kernel does not append
+        if (append && append->positions) return hipErrorInvalidValue;     // the long-interval kernels do not append
         if (chunk > 64) return hipErrorInvalidValue;     // a run's groups are counted over one wave
+        if (c.n_q_heads / c.n_kv_heads <= 4 && chunk <= 32) {
+            // one forward pass (operand column 4 is spare)
+            if (c.head_dim == 64)
+                hipLaunchKernelGGL(k_attn_lfwd_g8<64>, grid, dim3(64), 0, st, c, (const uint8_t *)cache, bt, q, lens,
+                                   scale_log2, ws, nsplit, chunk, ct);
+            else
+                hipLaunchKernelGGL(k_attn_lfwd_g8<128>, grid, dim3(64), 0, st, c, (const uint8_t *)cache, bt, q, lens,
+                                   scale_log2, ws, nsplit, chunk, ct);
+            return hipGetLastError();
+        }
         // logit rows (see the kernel): 32 per tile and a spare row when at most
         // 4 query heads share a kv-head, 64 per tile otherwise
         const int nt = (c.kf + 31) / 32;

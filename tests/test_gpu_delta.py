@@ -219,14 +219,16 @@ def test_value_scale(name, kw, kf, vscale):
 # kf = 128), and the lengths put every count of whole groups in a run, with
 # and without a partial last group, through the pipelined kernels (keyframe
 # batches of 4 closed early, a run of one group, the partial group after it).
-# With at most 4 query heads per kv-head the kf = 32 kernel takes two groups
-# per step, so odd and even group counts and both groups of a pair are covered.
+# At kf > 32 with at most 4 query heads per kv-head the forward kernel takes
+# the groups tile by tile (NT = kf/32 tiles, 3 at kf = 96), so a group's last
+# tile, a partial last tile and a run that ends inside a group all occur.
 RUN_LENS = [0, 1, 31, 32, 33, 63, 64, 65, 96, 97, 127, 128, 129, 160, 192, 224,
             255, 256, 257, 300, 511, 512, 513, 640, 1000, 1024, 1025, 1500, 2000, 2016, 2047, 2048]
 
 
 @pytest.mark.parametrize("kf,Hq,D", [(32, 64, 128), (128, 64, 128), (32, 32, 128), (32, 16, 128), (32, 8, 128),
-                                     (32, 32, 64), (128, 32, 128)])
+                                     (32, 32, 64), (128, 32, 128), (128, 16, 128), (128, 8, 128), (512, 32, 128),
+                                     (64, 32, 64), (96, 32, 128)])
 def test_runs_of_every_length(kf, Hq, D):
     print(f"runs of every length kf={kf} Hq={Hq} D={D}", flush=True)
     w = _case("70b", S=2048, B=32, Hq=Hq, D=D)
