@@ -130,11 +130,12 @@ Plan tile_plan(const dkv_config &c)
     p.cap_tokens = cmp_ntiles(c) * 32;
     return p;
 }
-// strided-reference decode: one wave per run, so runs of at most 16 tiles
+// strided-reference decode: runs of at most 64 tiles (2048 tokens), as the
+// Delta-KV decode (16-tile runs measured 3 % slower on the 70B layer)
 Plan strided_plan(const dkv_config &c)
 {
     const int tiles = (c.max_tokens + 31) / 32;
-    Plan p = make_plan(tiles, c.batch, c.n_kv_heads, 16);
+    Plan p = make_plan(tiles, c.batch, c.n_kv_heads, 64);
     p.split_tokens = p.chunk * 32;
     p.cap_tokens = c.max_tokens;
     return p;

@@ -125,6 +125,29 @@ __device__ inline uint32_t pack_h2(float lo, float hi)
     return __builtin_bit_cast(uint32_t, v);
 }
 
+// V weights of two token slots: w0 = s0 * x0 into the low half and w1 = s1 * x1
+// into the high half of `hi` (fp16, round to nearest), and the fp16 residues
+// x*s - w into `lo`.  s0, s1: fp16 in half SEL of sw0, sw1; the residue reads
+// its w straight from the half of `hi` it sits in.
+template <int SEL>
+__device__ inline void split_w(uint32_t sw0, uint32_t sw1, float x0, float x1, uint32_t &hi, uint32_t &lo)
+{
+    if constexpr (SEL == 0)
+        asm("v_fma_mixlo_f16 %0, %2, %4, 0 op_sel_hi:[1,0,0]\n\t"
+            "v_fma_mixhi_f16 %0, %3, %5, 0 op_sel_hi:[1,0,0]\n\t"
+            "v_fma_mixlo_f16 %1, %2, %4, -%0 op_sel_hi:[1,0,1]\n\t"
+            "v_fma_mixhi_f16 %1, %3, %5, -%0 op_sel:[0,0,1] op_sel_hi:[1,0,1]"
+            : "=&v"(hi), "=&v"(lo)
+            : "v"(sw0), "v"(sw1), "v"(x0), "v"(x1));
+    else
+        asm("v_fma_mixlo_f16 %0, %2, %4, 0 op_sel:[1,0,0] op_sel_hi:[1,0,0]\n\t"
+            "v_fma_mixhi_f16 %0, %3, %5, 0 op_sel:[1,0,0] op_sel_hi:[1,0,0]\n\t"
+            "v_fma_mixlo_f16 %1, %2, %4, -%0 op_sel:[1,0,0] op_sel_hi:[1,0,1]\n\t"
+            "v_fma_mixhi_f16 %1, %3, %5, -%0 op_sel:[1,0,1] op_sel_hi:[1,0,1]"
+            : "=&v"(hi), "=&v"(lo)
+            : "v"(sw0), "v"(sw1), "v"(x0), "v"(x1));
+}
+
 // Byte offsets of a lane's loads inside a group record (the same for every group).
 struct LaneOffsets {
     int side, k0, k1, v;

@@ -240,57 +240,6 @@ __global__ void __launch_bounds__(64)
     strided_append_wave<D>(ly, cfg.kf, base, x, t, window, threadIdx.x);
 }
 
-// Raw data of D/4 channels [c0, c0 + D/4) of one token of one stream (one
-// block at D = 128, half a block at D = 64): the block's 16 code bytes, its
-// scale and the reference row slice.
-template <int D>
-struct RowQ {
-    uint32_t cw[4];
-    uint32_t rw[D / 8];
-    uint32_t sc;
-};
-
-template <int D>
-__device__ inline void strided_fetch_q(const uint8_t *__restrict__ base, const StridedLayout &ly, int t, int c0,
-                                       RowQ<D> &w)
-{
-    constexpr int NB = D / 32;
-    const int k = strided_ref(base, ly, t);
-    const int blk = c0 >> 5;
-    w.sc = ((const uint16_t *)(base + ly.off_scales))[(int64_t)t * NB + blk];
-    const u4 x = *(const u4 *)(base + ly.off_codes + (int64_t)t * (D / 2) + 16 * blk);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) w.cw[i] = x[i];
-    const u4 *r = (const u4 *)((const uint16_t *)base + (int64_t)k * D + c0);
-#pragma unroll
-    for (int i = 0; i < D / 32; ++i) {
-        const u4 y = r[i];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) w.rw[4 * i + j] = y[j];
-    }
-}
-
-// reference + (code - 8) * scale of the D/4 channels, written to an LDS row
-template <int D>
-__device__ inline void strided_rebuild_q(const RowQ<D> &w, int c0, float *__restrict__ dst)
-{
-    constexpr int CH = D / 4;
-    const float sf = h2f((uint16_t)w.sc);
-#pragma unroll
-    for (int i = 0; i < CH; i += 4) {
-        f4 o;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int ci = i + u;                                   // channel c0 + ci
-            const int e = (c0 & 31) + ci;                           // its place in the block
-            const int code = (int)((w.cw[(e & 15) >> 2] >> (8 * (e & 3) + 4 * (e >> 4))) & 15u);
-            const uint16_t rh = (uint16_t)((ci & 1) ? (w.rw[ci >> 1] >> 16) : (w.rw[ci >> 1] & 0xFFFF));
-            o[u] = __builtin_fmaf((float)(code - 8), sf, h2f(rh));   // exact product, one rounding
-        }
-        *(f4 *)&dst[i] = o;
-    }
-}
-
 // K operands of one token for the fp16 matrix instructions: lane 16*j + n
 // holds row n of A at k = 8j..8j+7, so for each block b it takes the
 // reference channels 32b + 8j .. 32b + 8j + 7 (exact fp16) and the same
@@ -302,20 +251,33 @@ struct KOps {
     uint32_t sc;                                 // scale bits of block min(j, D/32 - 1)
 };
 
+// Buffer resource over one stream (its planes are addressed with 32-bit
+// offsets; loads past the stream return zeros).
+__device__ inline __amdgpu_buffer_rsrc_t stream_rsrc(const uint8_t *base, int64_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, (int)bytes, 0x00020000);
+}
+// The token's reference index, clamped to the plane, through the stream's resource.
+__device__ inline int strided_ref_rs(__amdgpu_buffer_rsrc_t rs, const StridedLayout &ly, int t)
+{
+    return min((int)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rs, (int)ly.off_idx + 2 * t, 0, kStream),
+               ly.nref - 1);
+}
+
 template <int D>
-__device__ inline void strided_fetch_k(const uint8_t *__restrict__ base, const StridedLayout &ly, int t, int j,
-                                       KOps<D> &o)
+__device__ inline void strided_fetch_k(__amdgpu_buffer_rsrc_t rs, const StridedLayout &ly, int t, int j, KOps<D> &o)
 {
     constexpr int NB = D / 32;
-    const int k = strided_ref(base, ly, t);
-    const uint16_t *r = (const uint16_t *)base + (int64_t)k * D + 8 * j;
-    const uint8_t *cb = base + ly.off_codes + (int64_t)t * (D / 2) + 8 * (j & 1);
+    const int k = strided_ref_rs(rs, ly, t);
+    const int ro = k * (2 * D) + 16 * j;
+    const int co = (int)ly.off_codes + t * (D / 2) + 8 * (j & 1);
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-        o.ref[b] = *(const u4 *)(r + 32 * b);
-        o.code[b] = *(const u2 *)(cb + 16 * b);
+        o.ref[b] = __builtin_amdgcn_raw_buffer_load_b128(rs, ro + 64 * b, 0, 0);
+        o.code[b] = __builtin_amdgcn_raw_buffer_load_b64(rs, co + 16 * b, 0, kStream);
     }
-    o.sc = ((const uint16_t *)(base + ly.off_scales))[(int64_t)t * NB + min(j, NB - 1)];
+    o.sc = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rs, (int)ly.off_scales + (t * NB + min(j, NB - 1)) * 2, 0,
+                                                          kStream);
 }
 
 // (c - 8) of 8 codes as exact fp16: 1024 + c built by placing each nibble in
@@ -327,39 +289,83 @@ __device__ inline h8 codes_f16(u2 w, int sh)
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const uint32_t n4 = (w[i] >> sh) & 0x0F0F0F0Fu;
-        const uint32_t p0 = __builtin_amdgcn_perm(0u, n4, 0x0C010C00u) | 0x64006400u;   // bytes 0, 1
-        const uint32_t p1 = __builtin_amdgcn_perm(0u, n4, 0x0C030C02u) | 0x64006400u;   // bytes 2, 3
+        // bytes 0, 1 (2, 3) of n4 under a 0x64 byte each
+        const uint32_t p0 = __builtin_amdgcn_perm(0x64646464u, n4, 0x04010400u);
+        const uint32_t p1 = __builtin_amdgcn_perm(0x64646464u, n4, 0x04030402u);
         o[2 * i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, p0) - off);
         o[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, p1) - off);
     }
     return __builtin_bit_cast(h8, o);
 }
 
+// fp16 (c - 8) of the 8 codes in word w (byte i: code i of the block in the
+// low nibble, code i + 16 in the high one) for 4 channels of each nibble
+// plane: lo[0..1] = channels i..i+3 (low nibbles), hi[0..1] = i+16..i+19.
+// 0x64 above a nibble is the fp16 1024 + c; 1032 is subtracted exactly.
+__device__ inline void codes_pairs(uint32_t w, uint32_t (&lo)[2], uint32_t (&hi)[2])
+{
+    const h2 off = h2{(_Float16)1032.0f, (_Float16)1032.0f};
+    const uint32_t nl = w & 0x0F0F0F0Fu, nh = (w >> 4) & 0x0F0F0F0Fu;
+    const uint32_t p64 = 0x64646464u;
+    const uint32_t l0 = __builtin_amdgcn_perm(p64, nl, 0x04010400u), l1 = __builtin_amdgcn_perm(p64, nl, 0x04030402u);
+    const uint32_t h0 = __builtin_amdgcn_perm(p64, nh, 0x04010400u), h1 = __builtin_amdgcn_perm(p64, nh, 0x04030402u);
+    lo[0] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, l0) - off);
+    lo[1] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, l1) - off);
+    hi[0] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, h0) - off);
+    hi[1] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, h1) - off);
+}
+
+// V data of one token for one lane: half h of its channels, the reference
+// row's slice (fp16), the code bytes of the same channels and their scales.
+template <int D>
+struct VHalf {
+    u4 ref[D / 16];                 // D/2 channels: D bytes
+    uint32_t code[D / 16];          // D/4 bytes of codes (D/2 channels)
+    uint32_t sc;                    // scales of the half's blocks (D = 128: 2, D = 64: 1)
+};
+
+// fp16 transpose read (ds_read_b64_tr_b16): in each group of 16 lanes, lane L
+// returns element L % 4 of the 8-byte pieces addressed by lanes L/4, L/4 + 4,
+// L/4 + 8 and L/4 + 12 of its group.
+__device__ inline u2 lds_tr16(const uint8_t *p)
+{
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    const v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4s *)(__attribute__((address_space(3))) uint8_t *)p);
+    return __builtin_bit_cast(u2, r);
+}
+
 // grid (nsplit, n_kv_heads, batch), one wave per workgroup: the split's run of
-// 32-token tiles, taken as 16-token sub-tiles with no barrier between waves.
-// Per sub-tile the logits are taken in the residual domain on fp16 matrix
-// instructions (v_mfma_f32_16x16x32_f16: lane 16*j + n holds row n of A and
-// column n of B at k = 8j..8j+7, and rows 4j..4j+3 of column n of the result):
-//   q.khat_t = q.r_idx(t) + sum_b s_t,b * sum_(j in b) q_j (c_t,j - 8)
-// with the reference rows (exact fp16) and the codes (c - 8, exact fp16) as A
-// operands and q, scaled by 2^-E and split hi + lo, as B.  V is rebuilt in
-// fp32 into the wave's LDS tile (lane: token lane/4, a quarter of the
-// channels) and the weighted V rows (16 head rows x D channels over the 16
-// tokens) are fp32 matrix products (v_mfma_f32_16x16x4_f32).  The softmax runs
-// down each head column; head columns beyond the group are zero.  The next
-// sub-tile's operands are fetched while the current one is processed.
+// 32-token tiles.  Per tile:
+//  - logits in the residual domain on fp16 matrix instructions
+//    (v_mfma_f32_16x16x32_f16: lane 16*j + n holds row n of A and column n
+//    of B at k = 8j..8j+7, and rows 4j..4j+3 of column n of the result):
+//      q.khat_t = q.r_idx(t) + sum_b s_t,b * sum_(i in b) q_i (c_t,i - 8)
+//    with the reference rows and the codes (c - 8) as exact fp16 A operands
+//    (rows: tokens) and q, scaled by 2^-E and split hi + lo, as B;
+//  - the online softmax down each head column (head columns past the group
+//    have a zero query);
+//  - the weighted V rows in the residual domain on the same instructions:
+//      sum_t p_t vhat_t = sum_t p_t r_idx(t) + sum_b sum_t (p_t s_t,b)(c_t - 8)
+//    The tile's reference rows and its codes (c - 8, exact fp16) are written
+//    to LDS as token rows and read back transposed (ds_read_b64_tr_b16), so
+//    A holds 16 channels x 32 tokens; B holds the weights p (for the
+//    reference rows) and p * s_b (for the codes of block b), split hi + lo.
+//    V is never rebuilt.
+//  The next tile's operands are fetched while the current one is processed.
 // With positions (not null) the workgroup whose run holds a sequence's new
 // token appends it first (k_new, v_new fp16 [B][Hkv][D]; the cache is written
 // through the same pointer it is read through, hence no __restrict__ on it).
 template <int D>
-__global__ void __launch_bounds__(64)
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
     k_strided_attn(dkv_config cfg, const uint8_t *cache, const float *__restrict__ q,
                    const int32_t *__restrict__ lens, float scale_log2, float *__restrict__ ws, int nsplit, int chunk,
                    const uint16_t *__restrict__ knew, const uint16_t *__restrict__ vnew,
                    const int32_t *__restrict__ positions, int window)
 {
-    constexpr int VS = D + 16;                   // LDS row stride: conflict-free operand reads
-    constexpr int NCB = D / 16;                  // 16-channel column blocks of the weighted V rows
+    constexpr int NB = D / 32, NCB = D / 16;
+    constexpr int VS = 4 * D + 32;               // LDS bytes per V token row: [reference 2D][codes 2D][pad]
+    constexpr int PS = 36;                       // floats per weight row
     const StridedLayout ly = strided_layout(cfg);
     const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
     const int jj = lane >> 4, nn = lane & 15;
@@ -380,14 +386,15 @@ __global__ void __launch_bounds__(64)
     const int t_begin = split * chunk * 32, t_end = min(L, t_begin + chunk * 32);
     const int64_t row0 = (int64_t)b * Hq + (int64_t)h * G;
 
-    __shared__ __attribute__((aligned(16))) float vt[16 * VS];
-    __shared__ float pl[kStridedMaxG][17];
-    __shared__ float al[kStridedMaxG];
-    __shared__ __attribute__((aligned(16))) float scl[16][4];   // the sub-tile's block scales [token][block]
+    // per token of the tile: its reference row and its codes as fp16 (c - 8);
+    // the 32-byte pad puts the 4 rows of a transposed read on separate banks
+    __shared__ __attribute__((aligned(16))) uint8_t vdat[32 * VS];
+    __shared__ __attribute__((aligned(16))) float pl[kStridedMaxG * PS]; // p [head][token]
+    __shared__ __attribute__((aligned(16))) uint16_t vsh[32 * NB];    // V scales (fp16) [token][block]
+    __shared__ float ksl[32][NB];                                     // K scales [token][block]
 
     // query operand: head nn, channels 32b + 8jj + e, scaled by 2^-E (E from
     // the largest |q| of the kv-head's group) and split into hi + lo fp16
-    constexpr int NB = D / 32;
     h8 qh[NB], ql[NB];
     float unq;
     {
@@ -419,94 +426,212 @@ __global__ void __launch_bounds__(64)
     }
     const uint8_t *kb = cache + (((int64_t)b * cfg.n_kv_heads + h) * 2) * ly.stream_bytes;
     const uint8_t *vb = kb + ly.stream_bytes;
+    const __amdgpu_buffer_rsrc_t krs = stream_rsrc(kb, ly.stream_bytes), vrs = stream_rsrc(vb, ly.stream_bytes);
     float m_run = -INFINITY, l_run = 0.0f;       // of head nn
     f4 acc[NCB];
 #pragma unroll
     for (int u = 0; u < NCB; ++u) acc[u] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    const int r = lane >> 2, c0 = (lane & 3) * (D / 4);
-    const int csh = 4 * (jj >> 1);               // nibble plane of this lane's k-range
-    KOps<D> ck;                                  // K operands of token t0 + nn
-    RowQ<D> nv;                                  // V raw data of token t0 + r
-    if (t_begin + nn < t_end) strided_fetch_k<D>(kb, ly, t_begin + nn, jj, ck);
-    if (t_begin + r < t_end) strided_fetch_q<D>(vb, ly, t_begin + r, c0, nv);
-    for (int t0 = t_begin; t0 < t_end; t0 += 16) {
-        const int nt = min(16, t_end - t0);
-        if (r < nt) {
-            strided_rebuild_q<D>(nv, c0, vt + r * VS + c0);
-        } else {
+    // V fetch: lane = token vt (of the tile) and half vh of the channels
+    const int vt = lane >> 1, vh = lane & 1;
+    const int csh = 4 * (jj >> 1);               // K: nibble plane of this lane's k-range
+    auto fetch_v_idx = [&](int t) { return t < t_end ? strided_ref_rs(vrs, ly, t) : 0; };
+    auto fetch_v_rest = [&](int t, VHalf<D> &v) {
+        const int tc = t < t_end ? t : t_begin;  // past the end: a valid row (its weight is zero)
+        const int co = (int)ly.off_codes + tc * (D / 2) + vh * (D / 4);
 #pragma unroll
-            for (int i = 0; i < D / 4; i += 4) *(f4 *)&vt[r * VS + c0 + i] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-        }
-        if (jj < NB) scl[nn][jj] = nn < nt ? h2f((uint16_t)ck.sc) : 0.0f;
-        // residual-domain logits of row token nn: reference part and per-block code parts
-        f4 Cr = f4{0.0f, 0.0f, 0.0f, 0.0f};
-        f4 Rb[NB];
+        for (int i = 0; i < D / 64; ++i) {
+            const u4 x = __builtin_amdgcn_raw_buffer_load_b128(vrs, co + 16 * i, 0, kStream);
 #pragma unroll
-        for (int bb = 0; bb < NB; ++bb) {
-            const h8 ar = __builtin_bit_cast(h8, ck.ref[bb]);
-            Cr = mfma(ar, qh[bb], Cr);
-            Cr = mfma(ar, ql[bb], Cr);
-            const h8 ac = codes_f16(ck.code[bb], csh);
-            Rb[bb] = mfma(ac, qh[bb], f4{0.0f, 0.0f, 0.0f, 0.0f});
-            Rb[bb] = mfma(ac, ql[bb], Rb[bb]);
+            for (int e = 0; e < 4; ++e) v.code[4 * i + e] = x[e];
         }
-        if (t0 + 16 + nn < t_end) strided_fetch_k<D>(kb, ly, t0 + 16 + nn, jj, ck);
-        if (t0 + 16 + r < t_end) strided_fetch_q<D>(vb, ly, t0 + 16 + r, c0, nv);
+        if constexpr (NB == 4)
+            v.sc = __builtin_amdgcn_raw_buffer_load_b32(vrs, (int)ly.off_scales + tc * 8 + 4 * vh, 0, kStream);
+        else
+            v.sc = (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(vrs, (int)ly.off_scales + tc * 4 + 2 * vh, 0,
+                                                                  kStream);
+    };
+    auto fetch_v_ref = [&](int k, VHalf<D> &v) {
+        const int ro = k * (2 * D) + vh * D;
+#pragma unroll
+        for (int i = 0; i < D / 16; ++i) v.ref[i] = __builtin_amdgcn_raw_buffer_load_b128(vrs, ro + 16 * i, 0, 0);
+    };
+    // K operands of token t (row nn of the tile's half T), as strided_fetch_k;
+    // tokens past the end read token t_begin (their logits are masked)
+    auto fetch_k = [&](int t, KOps<D> &o) { strided_fetch_k<D>(krs, ly, t < t_end ? t : t_begin, jj, o); };
+
+    KOps<D> ck[2];
+    VHalf<D> cv;
+    int vk = 0;
+    if (t_begin < t_end) {
+        fetch_k(t_begin + nn, ck[0]);
+        fetch_k(t_begin + 16 + nn, ck[1]);
+        vk = fetch_v_idx(t_begin + vt);
+        fetch_v_rest(t_begin + vt, cv);
+        fetch_v_ref(vk, cv);
+    }
+    for (int t0 = t_begin; t0 < t_end; t0 += 32) {
+        const int nt = min(32, t_end - t0);
+        // stage the tile's V rows (reference slice and codes as fp16 (c - 8)),
+        // its V scales and its K scales
+        {
+            uint8_t *rr = vdat + vt * VS + vh * D;
+            uint8_t *cr = rr + 2 * D;
+#pragma unroll
+            for (int i = 0; i < D / 16; ++i) ((u4 *)rr)[i] = cv.ref[i];
+            // code words: D/64 blocks per half, 4 words (16 bytes) each
+#pragma unroll
+            for (int bl = 0; bl < D / 64; ++bl) {
+                uint32_t lo[8], hi[8];
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    uint32_t l2[2], h2_[2];
+                    codes_pairs(cv.code[4 * bl + w], l2, h2_);
+                    lo[2 * w] = l2[0];
+                    lo[2 * w + 1] = l2[1];
+                    hi[2 * w] = h2_[0];
+                    hi[2 * w + 1] = h2_[1];
+                }
+                u4 *dst = (u4 *)(cr + 64 * bl);           // block: channels 0..15 (low nibbles), 16..31 (high)
+                dst[0] = u4{lo[0], lo[1], lo[2], lo[3]};
+                dst[1] = u4{lo[4], lo[5], lo[6], lo[7]};
+                dst[2] = u4{hi[0], hi[1], hi[2], hi[3]};
+                dst[3] = u4{hi[4], hi[5], hi[6], hi[7]};
+            }
+            if constexpr (NB == 4)
+                ((uint32_t *)vsh)[vt * 2 + vh] = cv.sc;
+            else
+                vsh[vt * 2 + vh] = (uint16_t)cv.sc;
+            if (nt < 32 && vt >= nt) {
+                // rows past the end (re-reads of a valid token) become zeros:
+                // their weights are zero, and zero rows keep 0 * inf out
+#pragma unroll
+                for (int i = 0; i < D / 16; ++i) ((u4 *)rr)[i] = u4{0, 0, 0, 0};
+#pragma unroll
+                for (int i = 0; i < D / 16; ++i) ((u4 *)cr)[i] = u4{0, 0, 0, 0};
+                if constexpr (NB == 4)
+                    ((uint32_t *)vsh)[vt * 2 + vh] = 0u;
+                else
+                    vsh[vt * 2 + vh] = (uint16_t)0;
+            }
+            if (jj < NB) {
+                ksl[nn][jj] = h2f((uint16_t)ck[0].sc);
+                ksl[16 + nn][jj] = h2f((uint16_t)ck[1].sc);
+            }
+        }
+        // K side: both halves of the tile from the registers fetched last tile
+        f4 Cr[2], Rb[2][NB];
+#pragma unroll
+        for (int T = 0; T < 2; ++T) {
+            Cr[T] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int bb = 0; bb < NB; ++bb) {
+                const h8 ar = __builtin_bit_cast(h8, ck[T].ref[bb]);
+                Cr[T] = mfma(ar, qh[bb], Cr[T]);
+                Cr[T] = mfma(ar, ql[bb], Cr[T]);
+                const h8 ac = codes_f16(ck[T].code[bb], csh);
+                Rb[T][bb] = mfma(ac, qh[bb], f4{0.0f, 0.0f, 0.0f, 0.0f});
+                Rb[T][bb] = mfma(ac, ql[bb], Rb[T][bb]);
+            }
+        }
+        // fetch the next tile (the reference rows once their indices are in)
+        const int t1 = t0 + 32;
+        int vk1 = 0;
+        VHalf<D> nv;
+        if (t1 < t_end) {
+            fetch_k(t1 + nn, ck[0]);
+            fetch_k(t1 + 16 + nn, ck[1]);
+            vk1 = fetch_v_idx(t1 + vt);
+            fetch_v_rest(t1 + vt, nv);
+        }
         __syncthreads();
-        float x[4], mx = -INFINITY;
+        // logits of tokens 16T + 4jj + i, the tile maximum, softmax weights
+        float x[2][4], mx = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int t = 4 * jj + i;
-            float lg = Cr[i];
+        for (int T = 0; T < 2; ++T)
 #pragma unroll
-            for (int bb = 0; bb < NB; ++bb) lg = __builtin_fmaf(scl[t][bb], Rb[bb][i], lg);
-            x[i] = t < nt ? lg * unq : -INFINITY;
-            mx = fmaxf(mx, x[i]);
-        }
+            for (int i = 0; i < 4; ++i) {
+                const int t = 16 * T + 4 * jj + i;
+                float lg = Cr[T][i];
+#pragma unroll
+                for (int bb = 0; bb < NB; ++bb) lg = __builtin_fmaf(ksl[t][bb], Rb[T][bb][i], lg);
+                x[T][i] = t < nt ? lg * unq : -INFINITY;
+                mx = fmaxf(mx, x[T][i]);
+            }
         mx = rows_max(mx);
         const float m_new = fmaxf(m_run, mx);
-        const float alpha = exp2f(m_run - m_new);
+        if (__any(m_new != m_run)) {
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+            for (int u = 0; u < NCB; ++u) acc[u] *= alpha;
+            l_run *= alpha;
+        }
+        m_run = m_new;
         float ps = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float p = x[i] == -INFINITY ? 0.0f : exp2f(x[i] - m_new);
-            pl[nn][4 * jj + i] = p;
-            ps += p;
+        for (int T = 0; T < 2; ++T) {
+            f4 pv;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float p = __builtin_amdgcn_exp2f(x[T][i] - m_new);     // exp2(-inf) = 0
+                pv[i] = p;
+                ps += p;
+            }
+            *(f4 *)&pl[nn * PS + 16 * T + 4 * jj] = pv;
         }
-        l_run = l_run * alpha + rows_sum(ps);
-        m_run = m_new;
-        if (jj == 0) al[nn] = alpha;
+        l_run += rows_sum(ps);
+        if (t1 < t_end) fetch_v_ref(vk1, nv);
         __syncthreads();
-        // weighted V rows: heads 4*jj + i, channels 16*cb + nn
-        float alr[4];
+        // weights of head nn for tokens 8jj..8jj+7: p (reference rows) and
+        // p * s_b (codes of block b), each split hi + lo, token pairs per word
+        uint32_t wph[4], wpl[4], wsh[NB][4], wsl[NB][4];
+        {
+            const f4 p0 = *(const f4 *)&pl[nn * PS + 8 * jj], p1 = *(const f4 *)&pl[nn * PS + 8 * jj + 4];
+            const float p[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+            const uint32_t *sw = (const uint32_t *)vsh + 8 * jj * (NB / 2);
+            constexpr uint32_t kOne = 0x3C003C00u;               // fp16 1.0 in both halves
 #pragma unroll
-        for (int i = 0; i < 4; ++i) alr[i] = al[4 * jj + i];
+            for (int e2 = 0; e2 < 4; ++e2) {
+                split_w<0>(kOne, kOne, p[2 * e2], p[2 * e2 + 1], wph[e2], wpl[e2]);
 #pragma unroll
-        for (int u = 0; u < NCB; ++u)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[u][i] *= alr[i];
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const float pa = pl[nn][4 * kk + jj];
-            const float *vr = vt + (4 * kk + jj) * VS + nn;
-#pragma unroll
-            for (int u = 0; u < NCB; ++u) acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa, vr[16 * u], acc[u], 0, 0, 0);
+                for (int bb = 0; bb < NB; ++bb) {
+                    const uint32_t s0 = sw[(2 * e2) * (NB / 2) + (bb >> 1)], s1 = sw[(2 * e2 + 1) * (NB / 2) + (bb >> 1)];
+                    if (bb & 1)
+                        split_w<1>(s0, s1, p[2 * e2], p[2 * e2 + 1], wsh[bb][e2], wsl[bb][e2]);
+                    else
+                        split_w<0>(s0, s1, p[2 * e2], p[2 * e2 + 1], wsh[bb][e2], wsl[bb][e2]);
+                }
+            }
         }
+        // transposed reads: lane L of group jj gets channel 16cb + L of tokens
+        // 8jj..8jj+3, then 8jj+4..8jj+7 (lane L addresses token 8jj + L/4,
+        // channels 16cb + 4(L % 4) .. + 3)
+        const int ro = (8 * jj + (nn >> 2)) * VS + 8 * (nn & 3);
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+            const u2 r0 = lds_tr16(vdat + ro + 32 * cb), r1 = lds_tr16(vdat + ro + 4 * VS + 32 * cb);
+            const u2 c0 = lds_tr16(vdat + 2 * D + ro + 32 * cb), c1 = lds_tr16(vdat + 2 * D + ro + 4 * VS + 32 * cb);
+            const h8 ar = __builtin_bit_cast(h8, u4{r0[0], r0[1], r1[0], r1[1]});
+            const h8 ac = __builtin_bit_cast(h8, u4{c0[0], c0[1], c1[0], c1[1]});
+            const int bb = cb >> 1;
+            acc[cb] = mfma(ar, as_h8(u4{wph[0], wph[1], wph[2], wph[3]}), acc[cb]);
+            acc[cb] = mfma(ar, as_h8(u4{wpl[0], wpl[1], wpl[2], wpl[3]}), acc[cb]);
+            acc[cb] = mfma(ac, as_h8(u4{wsh[bb][0], wsh[bb][1], wsh[bb][2], wsh[bb][3]}), acc[cb]);
+            acc[cb] = mfma(ac, as_h8(u4{wsl[bb][0], wsl[bb][1], wsl[bb][2], wsl[bb][3]}), acc[cb]);
+        }
+        cv = nv;
         __syncthreads();
     }
+    // lane (jj, nn) holds channels 16cb + 4jj + i of head nn
     constexpr int R = part_stride(D);
-#pragma unroll
-    for (int u = 0; u < NCB; ++u)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int g = 4 * jj + i;
-            if (g < G) ws[((row0 + g) * nsplit + split) * R + 16 * u + nn] = acc[u][i];
-        }
-    if (jj == 0 && nn < G) {
+    if (nn < G) {
         float *rec = ws + ((row0 + nn) * nsplit + split) * R;
-        rec[D] = m_run;
-        rec[D + 1] = l_run;
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) *(f4 *)&rec[16 * cb + 4 * jj] = acc[cb];
+        if (jj == 0) {
+            rec[D] = m_run;
+            rec[D + 1] = l_run;
+        }
     }
 }
 
