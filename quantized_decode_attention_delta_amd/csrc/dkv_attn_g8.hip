@@ -28,13 +28,6 @@ namespace dkv {
 bool fused_g8_supported(const dkv_config &c) { return vbp_layout(c) != 0 && c.kf == 32; }
 bool fused_long_g8_supported(const dkv_config &c) { return vbp_layout(c) != 0 && c.kf > 32 && c.kf <= 512; }
 
-// Value of lane n ^ 8 within each row of 16 lanes (DPP row rotate by 8).
-
-__device__ inline float other_half(float x)
-{
-    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x128, 0xF, 0xF, false));
-}
-
 // LDS images of the query-side operands, shared by all groups of a workgroup.
 // Entry e = 8*j + hq of each image holds lane (j, n)'s operand for head hq; a
 // lane of the other column half reads the all-zero image at the same index.

@@ -148,6 +148,12 @@ __device__ inline void split_w(uint32_t sw0, uint32_t sw1, float x0, float x1, u
             : "v"(sw0), "v"(sw1), "v"(x0), "v"(x1));
 }
 
+// Value of lane n ^ 8 within each row of 16 lanes (DPP row rotate by 8).
+__device__ inline float other_half(float x)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x128, 0xF, 0xF, false));
+}
+
 // Byte offsets of a lane's loads inside a group record (the same for every group).
 struct LaneOffsets {
     int side, k0, k1, v;

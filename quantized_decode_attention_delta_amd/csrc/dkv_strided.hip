@@ -353,10 +353,15 @@ __device__ inline u2 lds_tr16(const uint8_t *p)
 //    reference rows) and p * s_b (for the codes of block b), split hi + lo.
 //    V is never rebuilt.
 //  The next tile's operands are fetched while the current one is processed.
+// PAIR (at most 8 query heads per kv-head): the 8 spare columns of B carry the
+// same heads again, and the A rows of each instruction are 8 channels of a
+// block b (rows 0..7) and 8 of block b + nb/2 (rows 8..15), so column half h
+// takes the code weights of one block of each pair (half the weight work per
+// lane); only the (row half, column half) pairs that match are kept.
 // With positions (not null) the workgroup whose run holds a sequence's new
 // token appends it first (k_new, v_new fp16 [B][Hkv][D]; the cache is written
 // through the same pointer it is read through, hence no __restrict__ on it).
-template <int D>
+template <int D, bool PAIR>
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
     k_strided_attn(dkv_config cfg, const uint8_t *cache, const float *__restrict__ q,
                    const int32_t *__restrict__ lens, float scale_log2, float *__restrict__ ws, int nsplit, int chunk,
@@ -562,8 +567,16 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
         const float m_new = fmaxf(m_run, mx);
         if (__any(m_new != m_run)) {
             const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            // PAIR: the accumulators of column half 1 hold head nn - 8, whose
+            // softmax state is in lane nn - 8 of the row
+            // (every lane takes part in the exchange: the empty asm keeps the
+            // compiler from moving it under the lane condition, where the
+            // lanes it reads would be switched off)
+            float ao = other_half(alpha);
+            asm volatile("" : "+v"(ao));
+            const float av = (PAIR && (nn >> 3)) ? ao : alpha;
 #pragma unroll
-            for (int u = 0; u < NCB; ++u) acc[u] *= alpha;
+            for (int u = 0; u < NCB; ++u) acc[u] *= av;
             l_run *= alpha;
         }
         m_run = m_new;
@@ -582,11 +595,14 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
         l_run += rows_sum(ps);
         if (t1 < t_end) fetch_v_ref(vk1, nv);
         __syncthreads();
-        // weights of head nn for tokens 8jj..8jj+7: p (reference rows) and
-        // p * s_b (codes of block b), each split hi + lo, token pairs per word
-        uint32_t wph[4], wpl[4], wsh[NB][4], wsl[NB][4];
+        // weights of head hq for tokens 8jj..8jj+7: p (reference rows) and
+        // p * s_b (codes of block b), each split hi + lo, token pairs per word;
+        // PAIR: block wb + (nb/2)*h2 of each pair wb
+        constexpr int NWB = PAIR ? NB / 2 : NB;
+        const int h2 = nn >> 3, hq = PAIR ? (nn & 7) : nn;
+        uint32_t wph[4], wpl[4], wsh[NWB][4], wsl[NWB][4];
         {
-            const f4 p0 = *(const f4 *)&pl[nn * PS + 8 * jj], p1 = *(const f4 *)&pl[nn * PS + 8 * jj + 4];
+            const f4 p0 = *(const f4 *)&pl[hq * PS + 8 * jj], p1 = *(const f4 *)&pl[hq * PS + 8 * jj + 4];
             const float p[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
             const uint32_t *sw = (const uint32_t *)vsh + 8 * jj * (NB / 2);
             constexpr uint32_t kOne = 0x3C003C00u;               // fp16 1.0 in both halves
@@ -594,44 +610,63 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
             for (int e2 = 0; e2 < 4; ++e2) {
                 split_w<0>(kOne, kOne, p[2 * e2], p[2 * e2 + 1], wph[e2], wpl[e2]);
 #pragma unroll
-                for (int bb = 0; bb < NB; ++bb) {
-                    const uint32_t s0 = sw[(2 * e2) * (NB / 2) + (bb >> 1)], s1 = sw[(2 * e2 + 1) * (NB / 2) + (bb >> 1)];
-                    if (bb & 1)
-                        split_w<1>(s0, s1, p[2 * e2], p[2 * e2 + 1], wsh[bb][e2], wsl[bb][e2]);
-                    else
-                        split_w<0>(s0, s1, p[2 * e2], p[2 * e2 + 1], wsh[bb][e2], wsl[bb][e2]);
+                for (int wb = 0; wb < NWB; ++wb) {
+                    // block bb's scale: half bb & 1 of word bb >> 1 of the token's scales
+                    const int bb = PAIR ? wb + (NB / 2) * h2 : wb;
+                    uint32_t s0 = sw[(2 * e2) * (NB / 2) + (bb >> 1)], s1 = sw[(2 * e2 + 1) * (NB / 2) + (bb >> 1)];
+                    if constexpr (PAIR && NB == 2) {          // bb = h2: a lane-dependent half
+                        s0 = h2 ? s0 >> 16 : s0;
+                        s1 = h2 ? s1 >> 16 : s1;
+                        split_w<0>(s0, s1, p[2 * e2], p[2 * e2 + 1], wsh[wb][e2], wsl[wb][e2]);
+                    } else if (wb & 1) {
+                        split_w<1>(s0, s1, p[2 * e2], p[2 * e2 + 1], wsh[wb][e2], wsl[wb][e2]);
+                    } else {
+                        split_w<0>(s0, s1, p[2 * e2], p[2 * e2 + 1], wsh[wb][e2], wsl[wb][e2]);
+                    }
                 }
             }
         }
-        // transposed reads: lane L of group jj gets channel 16cb + L of tokens
-        // 8jj..8jj+3, then 8jj+4..8jj+7 (lane L addresses token 8jj + L/4,
-        // channels 16cb + 4(L % 4) .. + 3)
-        const int ro = (8 * jj + (nn >> 2)) * VS + 8 * (nn & 3);
+        // transposed reads: lane L of group jj gets the channel of row L of
+        // tokens 8jj..8jj+3, then 8jj+4..8jj+7; lane L addresses token
+        // 8jj + L/4 and the 4 channels its row quarter L % 4 takes:
+        //  plain: rows = channels 16cb .. 16cb + 15;
+        //  PAIR:  rows 0..7 = channels 8g .. 8g+7 of block wb, rows 8..15 those of block wb + nb/2
+        const int rrow = (8 * jj + (nn >> 2)) * VS;
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
-            const u2 r0 = lds_tr16(vdat + ro + 32 * cb), r1 = lds_tr16(vdat + ro + 4 * VS + 32 * cb);
-            const u2 c0 = lds_tr16(vdat + 2 * D + ro + 32 * cb), c1 = lds_tr16(vdat + 2 * D + ro + 4 * VS + 32 * cb);
+            const int ch = PAIR ? 32 * ((cb >> 2) + (NB / 2) * ((nn & 3) >> 1)) + 8 * (cb & 3) + 4 * (nn & 1)
+                                : 16 * cb + 4 * (nn & 3);
+            const uint8_t *pr = vdat + rrow + 2 * ch;
+            const u2 r0 = lds_tr16(pr), r1 = lds_tr16(pr + 4 * VS);
+            const u2 c0 = lds_tr16(pr + 2 * D), c1 = lds_tr16(pr + 2 * D + 4 * VS);
             const h8 ar = __builtin_bit_cast(h8, u4{r0[0], r0[1], r1[0], r1[1]});
             const h8 ac = __builtin_bit_cast(h8, u4{c0[0], c0[1], c1[0], c1[1]});
-            const int bb = cb >> 1;
+            const int wb = PAIR ? cb >> 2 : cb >> 1;
             acc[cb] = mfma(ar, as_h8(u4{wph[0], wph[1], wph[2], wph[3]}), acc[cb]);
             acc[cb] = mfma(ar, as_h8(u4{wpl[0], wpl[1], wpl[2], wpl[3]}), acc[cb]);
-            acc[cb] = mfma(ac, as_h8(u4{wsh[bb][0], wsh[bb][1], wsh[bb][2], wsh[bb][3]}), acc[cb]);
-            acc[cb] = mfma(ac, as_h8(u4{wsl[bb][0], wsl[bb][1], wsl[bb][2], wsl[bb][3]}), acc[cb]);
+            acc[cb] = mfma(ac, as_h8(u4{wsh[wb][0], wsh[wb][1], wsh[wb][2], wsh[wb][3]}), acc[cb]);
+            acc[cb] = mfma(ac, as_h8(u4{wsl[wb][0], wsl[wb][1], wsl[wb][2], wsl[wb][3]}), acc[cb]);
         }
         cv = nv;
         __syncthreads();
     }
-    // lane (jj, nn) holds channels 16cb + 4jj + i of head nn
+    // plain: lane (jj, nn) holds channels 16cb + 4jj + i of head nn; PAIR:
+    // lanes with (jj >> 1) == (nn >> 3) hold channels 8g + 4(jj & 1) + i of
+    // block cb/4 + (nb/2)(nn >> 3) (cb = 4 * pair + g) of head nn & 7
     constexpr int R = part_stride(D);
-    if (nn < G) {
-        float *rec = ws + ((row0 + nn) * nsplit + split) * R;
+    const int hq = PAIR ? (nn & 7) : nn;
+    if (hq < G && (!PAIR || (jj >> 1) == (nn >> 3))) {
+        float *rec = ws + ((row0 + hq) * nsplit + split) * R;
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) *(f4 *)&rec[16 * cb + 4 * jj] = acc[cb];
-        if (jj == 0) {
-            rec[D] = m_run;
-            rec[D + 1] = l_run;
+        for (int cb = 0; cb < NCB; ++cb) {
+            const int ch = PAIR ? 32 * ((cb >> 2) + (NB / 2) * (nn >> 3)) + 8 * (cb & 3) + 4 * (jj & 1) : 16 * cb + 4 * jj;
+            *(f4 *)&rec[ch] = acc[cb];
         }
+    }
+    if (jj == 0 && nn < G) {
+        float *rec = ws + ((row0 + nn) * nsplit + split) * R;
+        rec[D] = m_run;
+        rec[D + 1] = l_run;
     }
 }
 
@@ -683,12 +718,22 @@ hipError_t launch_strided_attn(const dkv_config &c, const void *cache, const flo
                                const uint16_t *vnew, const int32_t *positions, int window, hipStream_t st)
 {
     dim3 grid(nsplit, c.n_kv_heads, c.batch);
-    if (c.head_dim == 64)
-        hipLaunchKernelGGL(k_strided_attn<64>, grid, dim3(64), 0, st, c, (const uint8_t *)cache, q, lens,
-                           scale_log2, ws, nsplit, chunk, knew, vnew, positions, window);
-    else
-        hipLaunchKernelGGL(k_strided_attn<128>, grid, dim3(64), 0, st, c, (const uint8_t *)cache, q, lens,
-                           scale_log2, ws, nsplit, chunk, knew, vnew, positions, window);
+    const bool pair = c.n_q_heads / c.n_kv_heads <= 8;
+    if (c.head_dim == 64) {
+        if (pair)
+            hipLaunchKernelGGL((k_strided_attn<64, true>), grid, dim3(64), 0, st, c, (const uint8_t *)cache, q, lens,
+                               scale_log2, ws, nsplit, chunk, knew, vnew, positions, window);
+        else
+            hipLaunchKernelGGL((k_strided_attn<64, false>), grid, dim3(64), 0, st, c, (const uint8_t *)cache, q, lens,
+                               scale_log2, ws, nsplit, chunk, knew, vnew, positions, window);
+    } else {
+        if (pair)
+            hipLaunchKernelGGL((k_strided_attn<128, true>), grid, dim3(64), 0, st, c, (const uint8_t *)cache, q, lens,
+                               scale_log2, ws, nsplit, chunk, knew, vnew, positions, window);
+        else
+            hipLaunchKernelGGL((k_strided_attn<128, false>), grid, dim3(64), 0, st, c, (const uint8_t *)cache, q,
+                               lens, scale_log2, ws, nsplit, chunk, knew, vnew, positions, window);
+    }
     return hipGetLastError();
 }
 

@@ -38,6 +38,10 @@ CASES = [
     ("8b", dict(S=200, Hq=8, Hkv=2), 1, 0, None, None),            # every token its own reference
     ("8b", dict(S=600, Hq=8, Hkv=2), 32, 1, None, None),           # only the latest reference
     ("70b", dict(S=300, B=2, Hq=32, Hkv=2, D=64), 32, 0, None, None),
+    # runs of 8 tiles with at most 8 query heads per kv-head (the paired
+    # column halves rescaled as the running max moves), G = 8 and D = 64
+    ("70b", dict(S=2048, B=32, Hq=64, Hkv=8), 32, 64, "ragged", [(1, 0), (9, 6), (31, 7)]),
+    ("70b", dict(S=2048, B=32, Hq=32, Hkv=8, D=64), 32, 0, "ragged", [(1, 3), (12, 1), (30, 7)]),
 ]
 
 
