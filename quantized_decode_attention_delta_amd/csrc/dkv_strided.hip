@@ -264,11 +264,13 @@ __device__ inline int strided_ref_rs(__amdgpu_buffer_rsrc_t rs, const StridedLay
                ly.nref - 1);
 }
 
+// K operands of token t with reference index k (loaded ahead: the row load
+// does not wait for the index load).
 template <int D>
-__device__ inline void strided_fetch_k(__amdgpu_buffer_rsrc_t rs, const StridedLayout &ly, int t, int j, KOps<D> &o)
+__device__ inline void strided_fetch_k(__amdgpu_buffer_rsrc_t rs, const StridedLayout &ly, int t, int k, int j,
+                                       KOps<D> &o)
 {
     constexpr int NB = D / 32;
-    const int k = strided_ref_rs(rs, ly, t);
     const int ro = k * (2 * D) + 16 * j;
     const int co = (int)ly.off_codes + t * (D / 2) + 8 * (j & 1);
 #pragma unroll
@@ -440,7 +442,9 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
     // V fetch: lane = token vt (of the tile) and half vh of the channels
     const int vt = lane >> 1, vh = lane & 1;
     const int csh = 4 * (jj >> 1);               // K: nibble plane of this lane's k-range
-    auto fetch_v_idx = [&](int t) { return t < t_end ? strided_ref_rs(vrs, ly, t) : 0; };
+    // reference indices are loaded a tile before the rows they select
+    auto kidx = [&](int t) { return strided_ref_rs(krs, ly, t < t_end ? t : t_begin); };
+    auto vidx = [&](int t) { return strided_ref_rs(vrs, ly, t < t_end ? t : t_begin); };
     auto fetch_v_rest = [&](int t, VHalf<D> &v) {
         const int tc = t < t_end ? t : t_begin;  // past the end: a valid row (its weight is zero)
         const int co = (int)ly.off_codes + tc * (D / 2) + vh * (D / 4);
@@ -461,19 +465,21 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
 #pragma unroll
         for (int i = 0; i < D / 16; ++i) v.ref[i] = __builtin_amdgcn_raw_buffer_load_b128(vrs, ro + 16 * i, 0, 0);
     };
-    // K operands of token t (row nn of the tile's half T), as strided_fetch_k;
-    // tokens past the end read token t_begin (their logits are masked)
-    auto fetch_k = [&](int t, KOps<D> &o) { strided_fetch_k<D>(krs, ly, t < t_end ? t : t_begin, jj, o); };
+    // K operands of token t (row nn of the tile's half T) with its reference
+    // index k; tokens past the end read token t_begin (their logits are masked)
+    auto fetch_k = [&](int t, int k, KOps<D> &o) { strided_fetch_k<D>(krs, ly, t < t_end ? t : t_begin, k, jj, o); };
 
     KOps<D> ck[2];
     VHalf<D> cv;
-    int vk = 0;
+    int ki0 = 0, ki1 = 0, vi = 0;             // reference indices of the next tile's tokens
     if (t_begin < t_end) {
-        fetch_k(t_begin + nn, ck[0]);
-        fetch_k(t_begin + 16 + nn, ck[1]);
-        vk = fetch_v_idx(t_begin + vt);
+        fetch_k(t_begin + nn, kidx(t_begin + nn), ck[0]);
+        fetch_k(t_begin + 16 + nn, kidx(t_begin + 16 + nn), ck[1]);
         fetch_v_rest(t_begin + vt, cv);
-        fetch_v_ref(vk, cv);
+        fetch_v_ref(vidx(t_begin + vt), cv);
+        ki0 = kidx(t_begin + 32 + nn);
+        ki1 = kidx(t_begin + 48 + nn);
+        vi = vidx(t_begin + 32 + vt);
     }
     for (int t0 = t_begin; t0 < t_end; t0 += 32) {
         const int nt = min(32, t_end - t0);
@@ -541,13 +547,15 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
         }
         // fetch the next tile (the reference rows once their indices are in)
         const int t1 = t0 + 32;
-        int vk1 = 0;
         VHalf<D> nv;
         if (t1 < t_end) {
-            fetch_k(t1 + nn, ck[0]);
-            fetch_k(t1 + 16 + nn, ck[1]);
-            vk1 = fetch_v_idx(t1 + vt);
+            fetch_k(t1 + nn, ki0, ck[0]);
+            fetch_k(t1 + 16 + nn, ki1, ck[1]);
             fetch_v_rest(t1 + vt, nv);
+            fetch_v_ref(vi, nv);
+            ki0 = kidx(t1 + 32 + nn);
+            ki1 = kidx(t1 + 48 + nn);
+            vi = vidx(t1 + 32 + vt);
         }
         __syncthreads();
         // logits of tokens 16T + 4jj + i, the tile maximum, softmax weights
@@ -593,7 +601,6 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
             *(f4 *)&pl[nn * PS + 16 * T + 4 * jj] = pv;
         }
         l_run += rows_sum(ps);
-        if (t1 < t_end) fetch_v_ref(vk1, nv);
         __syncthreads();
         // weights of head hq for tokens 8jj..8jj+7: p (reference rows) and
         // p * s_b (codes of block b), each split hi + lo, token pairs per word;
