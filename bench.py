@@ -48,14 +48,14 @@ STATIC_CONFIGS = ("tiny", "8b", "long_kf32", "long_kf128", "long_kf512", "70b")
 # traffic is null.
 MEASURED_TRAFFIC = {
     "sources": {
-        "dkv_attn_g8.hip": "4c15d131d85da40d9b134a199a5b97110da5b2d46a1227aae2d5a97d1871feb8",
-        "dkv_fused_common.h": "79601ea867ca8f07e95b7c0f547216f6aa9900bf97aefdfe8dbcd5b4ab895fa2",
+        "dkv_attn_g8.hip": "96271a83fa8964ead8d2c01870b060c823d936e3c4143b70e78c5f9b2c398389",
+        "dkv_fused_common.h": "0a7daad2743ec9dae84c3bcbf95cd8da24f7f8015ab1443f8b040fdaa51fefcb",
         "dkv_common.h": "449c2571a6f5c87c7b0e87a22e301314a1a48d9589aa90f7c26c8087b7128561",
         "dkv_append.h": "be07c04e9857cdcd9f08e6a2526b04f9ce5e0a510bffa70e7ff091ce2d00e7dc",
         "dkv_q40.h": "d4b0a8142dfd210e9daa6a9ef282fe5ccb37c516b007f54681f8c9f93af0c73c",
-        "dkv_api.cpp": "8b9042e9f895f86f9663a2ee931362d03e769725770dfcca41e87d8a2c4f4abb",
+        "dkv_api.cpp": "7a0bbb0fe9ac11b2187b9e7a013c4955bbec4f20e6e31eb6f283d6dc00ac43ac",
     },
-    "per_launch": {"mixed": 3161777369, "70b": 684723848, "long_kf512": 159041587, "long_kf128": 161551214},
+    "per_launch": {"mixed": 3161628285, "70b": 684872599, "long_kf512": 158624364, "long_kf128": 161529604},
 }
 
 
@@ -679,7 +679,9 @@ def static_config(w, kf, args, label, traffic_key, graph=0, strided_on=False, co
     # merges), launched back to back between two events on its stream
     n_k = max(10, args.steps)
     if fused and launches == 2:
-        kernel = "split phase (k_attn_g8 / k_attn_long_g8)"
+        G = w.Hq // w.Hkv
+        name = "k_attn_g8" if kf == 32 else ("k_attn_lfwd_g8" if G <= 4 else "k_attn_long_g8")
+        kernel = f"split phase ({name})"
 
         def kern(i):
             dkv.dkv_attn_decode_partial(cfg, caches[i % replicas], None, q, lens, ws)
