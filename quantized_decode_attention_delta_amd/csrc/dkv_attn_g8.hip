@@ -44,54 +44,60 @@ struct G8Ops {
     const u4 *qc[2];   // + hl * 32
 };
 
-// The query elements lane (j, n) needs, in the K-code unpack order, of head
-// n & 7 of the kv-head's group (rows row0 ..).  Lanes of heads beyond the group
-// read head 0 (every load is unconditional, so they all go out together) and
-// setup_g8 zeroes them.
+// The query elements of head n & 7 of the kv-head's group (rows row0 ..) that
+// lane (j, n) prepares, in the K-code unpack order: the blocks of column half
+// h2 = n >> 3 (blocks h2*NB/2 .. h2*NB/2 + NB/2 - 1), so that the two halves
+// share the set-up.  Lanes of heads beyond the group read head 0 (every load
+// is unconditional, so they all go out together) and setup_g8 zeroes them.
 template <int D>
-__device__ inline void load_q_g8(float (&xq)[D / 32][8], const float *q, int64_t row0, int G, int j, int n)
+__device__ inline void load_q_g8(float (&xq)[D / 64][8], const float *q, int64_t row0, int G, int j, int n)
 {
-    const int hq = n & 7;
+    constexpr int NH = D / 64;
+    const int hq = n & 7, bb0 = (n >> 3) * NH;
     const float *qr = q + (row0 + (hq < G ? hq : 0)) * D;
 #pragma unroll
-    for (int bb = 0; bb < D / 32; ++bb)
+    for (int k = 0; k < NH; ++k)
 #pragma unroll
-        for (int hh = 0; hh < 8; ++hh) xq[bb][hh] = qr[32 * bb + kf_k_channel(j, hh)];
+        for (int hh = 0; hh < 8; ++hh) xq[k][hh] = qr[32 * (bb0 + k) + kf_k_channel(j, hh)];
 }
 
 // Query set-up from load_q_g8's elements: head hq's query scaled by
 // softmax_scale*log2(e) and by 2^-E (E = exponent of its largest element),
 // split in hi + lo fp16 in the K-code unpack order with the 16/f factors; the
-// "-8" operand -8*sum(q) per block.  Returns 2^E.
+// "-8" operand -8*sum(q) per block.  Each column half prepares the operands of
+// its own blocks (the head's maximum and the block sums are exchanged between
+// the halves).  Returns 2^E.
 template <int D>
-__device__ inline float setup_g8(G8Shared<D> &sh, G8Ops &op, const float (&qraw)[D / 32][8], int G, float scale_log2,
+__device__ inline float setup_g8(G8Shared<D> &sh, G8Ops &op, const float (&qraw)[D / 64][8], int G, float scale_log2,
                                  int j, int n, float *qs_out = nullptr)
 {
-    constexpr int NB = D / 32;
-    const int h2 = n >> 3, hq = n & 7, e = 8 * j + hq;
-    float xq[NB][8];
+    constexpr int NB = D / 32, NH = D / 64;
+    const int h2 = n >> 3, hq = n & 7, e = 8 * j + hq, bb0 = h2 * NH;
+    float xq[NH][8];
     float qm = 0.0f;
 #pragma unroll
-    for (int bb = 0; bb < NB; ++bb)
+    for (int k = 0; k < NH; ++k)
 #pragma unroll
         for (int hh = 0; hh < 8; ++hh) {
-            const float x = hq < G ? qraw[bb][hh] * scale_log2 : 0.0f;
-            xq[bb][hh] = x;
+            const float x = hq < G ? qraw[k][hh] * scale_log2 : 0.0f;
+            xq[k][hh] = x;
             qm = fmaxf(qm, fabsf(x));
         }
     qm = rows_max(qm);
+    qm = fmax_nc(qm, other_half(qm));        // the head's other blocks
     int E = 0;
     if (qm > 0.0f) frexpf(qm, &E);         // |q'| * 2^-E < 1
     const float qscale = ldexpf(1.0f, -E);
-    float Qs[NB];
+    float Qo[NH];
 #pragma unroll
-    for (int bb = 0; bb < NB; ++bb) {
+    for (int k = 0; k < NH; ++k) {
+        const int bb = bb0 + k;
         float qsum = 0.0f;
         h8 Bh, Bl;
 #pragma unroll
         for (int hh = 0; hh < 8; ++hh) {
             const bool f16x = ((hh >> 1) & 1) != 0;            // code half carries a factor 16
-            const float x = xq[bb][hh] * qscale * (f16x ? 1.0f : 16.0f);
+            const float x = xq[k][hh] * qscale * (f16x ? 1.0f : 16.0f);
             const _Float16 hi = (_Float16)x;
             const _Float16 lo = (_Float16)(x - (float)hi);
             Bh[hh] = hi;
@@ -100,16 +106,23 @@ __device__ inline float setup_g8(G8Shared<D> &sh, G8Ops &op, const float (&qraw)
         }
         float incl, all;
         rows_prefix(qsum, j, incl, all);
-        Qs[bb] = all;
-        if (qs_out) qs_out[bb] = all;
-        if (h2 == 0) {
-            sh.qk[(2 * bb) * 32 + e] = __builtin_bit_cast(u4, Bh);
-            sh.qk[(2 * bb + 1) * 32 + e] = __builtin_bit_cast(u4, Bl);
-        } else {
-            sh.qz[(2 * bb) * 32 + e] = u4{0, 0, 0, 0};
-            sh.qz[(2 * bb + 1) * 32 + e] = u4{0, 0, 0, 0};
-        }
+        Qo[k] = all;
+        sh.qk[(2 * bb) * 32 + e] = __builtin_bit_cast(u4, Bh);
+        sh.qk[(2 * bb + 1) * 32 + e] = __builtin_bit_cast(u4, Bl);
+        sh.qz[(2 * bb) * 32 + e] = u4{0, 0, 0, 0};
+        sh.qz[(2 * bb + 1) * 32 + e] = u4{0, 0, 0, 0};
     }
+    // block sums of every block: own half's and the other half's
+    float Qs[NB];
+#pragma unroll
+    for (int k = 0; k < NH; ++k) {
+        const float other = other_half(Qo[k]);
+        Qs[k] = h2 ? other : Qo[k];
+        Qs[NH + k] = h2 ? Qo[k] : other;
+    }
+    if (qs_out)
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb) qs_out[bb] = Qs[bb];
     if (h2 == 0) {
         h8 B2h, B2l;
 #pragma unroll
@@ -907,7 +920,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
         load_g8k<D>(kb[0], rec_at(0), rec_bytes, lo);
         load_g8v<D>(vb[0], rec_at(0), rec_bytes, lo);
         load_g8k<D>(kb[1], rec_at(1), rec_bytes, lo);
-        float qraw[NB][8];
+        float qraw[D / 64][8];
         load_q_g8<D>(qraw, q, row0, G, j, n);
         u4 kfa[NS][NB];
         kf_load_g8<D, NS>(kfa, glist, cnt, cache, j, n);
@@ -1191,7 +1204,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
         r.nt = r.g < g1 ? ntiles(r.g) : 1;
         return r;
     };
-    float qraw[NB][8];
+    float qraw[D / 64][8];
     load_q_g8<D>(qraw, q, row0, G, j, n);
     Cursor cc0;
     cc0.off = -1;
@@ -1568,7 +1581,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
         fetch_k(kb[0], 0);
         fetch_v(vb[0], 0);
         fetch_k(kb[1], 1);
-        float qraw[NB][8];
+        float qraw[D / 64][8];
         load_q_g8<D>(qraw, q, row0, G, j, n);
         u4 kfa[NS][NB];
         kf_load_g8<D, NS>(kfa, glist, cnt, cache, j, n);
@@ -1807,7 +1820,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
     }
 
     G8Ops op;
-    float qraw[NB][8];
+    float qraw[D / 64][8];
     load_q_g8<D>(qraw, q, row0, G, j, n);
     const float c2E = setup_g8<D>(sh, op, qraw, G, scale_log2, j, n);
     const h8 AZ = v_minus8_operand();
