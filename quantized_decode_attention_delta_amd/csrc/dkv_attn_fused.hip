@@ -71,7 +71,7 @@ __device__ inline void load_group(GroupRegs<D> &r, const uint8_t *rec, int rec_b
     }
 #pragma unroll
     for (int q4 = 0; q4 < NCC / 4; ++q4) {
-        u4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, o.v + 16 * q4, 0, kStream);
+        u4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, o.v + vcode_piece(D, 0, q4), 0, kStream);
 #pragma unroll
         for (int k = 0; k < 4; ++k) r.vc[4 * q4 + k] = a[k];
     }

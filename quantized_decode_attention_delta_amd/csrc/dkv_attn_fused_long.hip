@@ -275,7 +275,8 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
             uint32_t vc[NCC];
 #pragma unroll
             for (int q4 = 0; q4 < NCC / 4; ++q4) {
-                const u4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, lo.v + 16 * D * t + 16 * q4, 0, kStream);
+                const u4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, lo.v + 16 * D * t + vcode_piece(D, 0, q4), 0,
+                                                                   kStream);
 #pragma unroll
                 for (int k = 0; k < 4; ++k) vc[4 * q4 + k] = a[k];
             }

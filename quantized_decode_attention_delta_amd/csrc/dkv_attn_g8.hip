@@ -727,7 +727,7 @@ __device__ inline void load_g8(G8Regs<D> &r, const uint8_t *rec, int rec_bytes, 
     }
 #pragma unroll
     for (int q4 = 0; q4 < NCC / 4; ++q4) {
-        u4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, o.v + 16 * q4, 0, kStream);
+        u4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, o.v + vcode_piece(D, 0, q4), 0, kStream);
 #pragma unroll
         for (int k = 0; k < 4; ++k) r.vc[4 * q4 + k] = a[k];
     }
@@ -778,7 +778,7 @@ __device__ inline void load_g8v(G8VRegs<D> &r, const uint8_t *rec, int rec_bytes
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)rec, (short)0, rec_bytes, 0x00020000);
 #pragma unroll
     for (int q4 = 0; q4 < NCC / 4; ++q4) {
-        const u4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, o.v + 16 * q4, 0, kStream);
+        const u4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, o.v + vcode_piece(D, 0, q4), 0, kStream);
 #pragma unroll
         for (int k = 0; k < 4; ++k) r.vc[4 * q4 + k] = a[k];
     }
@@ -1144,10 +1144,11 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
             so = (kp && lane == D / 4) ? (int)g.off_vsc : 0x40000000;
         // K: token 32t + n is code row 32t + n - 1 (the keyframe row of tile 0 reads
         // as zeros), token 32t + 16 + n row 32t + 15 + n.  V: the lane's 2*NB tile words.
-        const int ov = (int)g.off_vcd + 16 * D * t + (j * 16 + n) * NCC * 4;
+        const int ov = (int)g.off_vcd + 16 * D * t + vcode_piece(D, lane, 0);
         const int o0 = kp ? ((t == 0 && n == 0) ? 0x40000000 : (int)g.off_kcd + (32 * t + n - 1) * (D / 2) + 4 * j * NB)
                           : ov;
-        const int o1 = kp ? (int)g.off_kcd + (32 * t + 15 + n) * (D / 2) + 4 * j * NB : ov + 4 * NB;
+        const int o1 = kp ? (int)g.off_kcd + (32 * t + 15 + n) * (D / 2) + 4 * j * NB
+                          : ov + (NB == 4 ? vcode_piece(D, 0, 1) : 4 * NB);
         r.side = __builtin_amdgcn_raw_buffer_load_b128(rs, so, 0, kStream);
         if constexpr (NB == 4) {
             const u4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, o0, 0, kStream);
@@ -1483,7 +1484,7 @@ __device__ inline void load_tile_v(G8VRegs<D> &r, const uint8_t *rec, int rec_by
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)rec, (short)0, rec_bytes, 0x00020000);
 #pragma unroll
     for (int q4 = 0; q4 < NCC / 4; ++q4) {
-        const u4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, v + 16 * q4, soff, kStream);
+        const u4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, v + vcode_piece(D, 0, q4), soff, kStream);
 #pragma unroll
         for (int k = 0; k < 4; ++k) r.vc[4 * q4 + k] = a[k];
     }
@@ -1832,7 +1833,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
                  : (lane >= 3 * D / 8 && lane < D / 2) ? 18 * D + 16 * (lane - 3 * D / 8) : 0x40000000;
     const int ok0 = 2 * D + n * (D / 2) + 4 * j * NB;
     const int ok1 = 2 * D + (16 + n) * (D / 2) + 4 * j * NB;
-    const int ov = 20 * D + (j * 16 + n) * (D / 16) * 4;
+    const int ov = 20 * D + vcode_piece(D, lane, 0);
     auto load_tile = [&](G8Regs<D> &r, int k) {
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
             (void *)(q4 + (bt ? uniform_offset(toffs, k) : q40_tile_offset(cfg, nullptr, b, h, t0 + k))), (short)0,
@@ -1842,7 +1843,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
             const u4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, ok0, 0, kStream);
             const u4 c = __builtin_amdgcn_raw_buffer_load_b128(rs, ok1, 0, kStream);
             const u4 v0 = __builtin_amdgcn_raw_buffer_load_b128(rs, ov, 0, kStream);
-            const u4 v1 = __builtin_amdgcn_raw_buffer_load_b128(rs, ov + 16, 0, kStream);
+            const u4 v1 = __builtin_amdgcn_raw_buffer_load_b128(rs, ov + vcode_piece(D, 0, 1), 0, kStream);
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 r.kc[k] = a[k];

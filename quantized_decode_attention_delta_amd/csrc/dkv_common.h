@@ -8,9 +8,10 @@
 //   codes (K)  pad16((kf-1)*D/2)  one row per delta token; the 16 canonical
 //                                 Q4_0 bytes of block b are split in four
 //                                 32-bit pieces, piece j at word j*nb + b
-//   codes (V)  ntiles*16*D        32-token tiles; word ((j*16+m)*(D/16)+cc)
-//                                 holds channel vchan(cc, m) for the 8 token
-//                                 slots 16*e+4*j+r (r<4, e<2) at nibble r+4*e
+//   codes (V)  ntiles*16*D        32-token tiles; word vcode_word: lane
+//                                 16*j+m's word cc holds channel vchan(cc, m)
+//                                 for the 8 token slots 16*e+4*j+r (r<4, e<2)
+//                                 at nibble r+4*e
 // The permutations line the data up with the operand layout of the gfx950
 // 16x16x32 fp16 matrix instruction (lane = 16*j + m, eight K values per lane).
 #pragma once
@@ -250,13 +251,23 @@ __host__ __device__ inline int vkf_pos(int D, int c, int bp)
 }
 // K code row: byte offset of canonical byte i (0..15) of block b.
 __host__ __device__ inline int kcode_byte(int nb, int b, int i) { return 4 * ((i >> 2) * nb + b) + (i & 3); }
+// V code tile: lane l = 16*j + m of the decode kernels holds the D/16 words
+// of row m (slices cc = 0 .. D/16-1) for its token slots.  With D/16 a
+// multiple of 4 the words go in 16-byte pieces: piece q4 (words 4*q4 .. 4*q4+3
+// of every lane) is one contiguous run over the 64 lanes, so that each
+// 16-byte load of a wave reads whole cache lines; otherwise a lane's words
+// are consecutive.  vcode_piece: byte offset of lane l's piece q4.
+__host__ __device__ inline int vcode_piece(int D, int lane, int q4)
+{
+    return (D / 16) % 4 == 0 ? 1024 * q4 + 16 * lane : lane * (D / 16) * 4 + 16 * q4;
+}
 // V code tile: word index and nibble of (token slot tau in 0..31, channel c).
 __host__ __device__ inline int vcode_word(int D, int tau, int c, int bp)
 {
     int j = (tau & 15) >> 2;
     int cc, m;
     vslot(D, c, bp, cc, m);
-    return (j * 16 + m) * (D / 16) + cc;
+    return vcode_piece(D, j * 16 + m, cc >> 2) / 4 + (cc & 3);
 }
 __host__ __device__ inline int vcode_nibble(int tau) { return (tau & 3) + 4 * (tau >> 4); }
 

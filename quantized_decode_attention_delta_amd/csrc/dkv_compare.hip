@@ -241,7 +241,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
         uint32_t vc[NCC];
 #pragma unroll
         for (int q4i = 0; q4i < NCC / 4; ++q4i) {
-            const u4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, 20 * D + (j * 16 + n) * NCC * 4 + 16 * q4i, 0, kStream);
+            const u4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, 20 * D + vcode_piece(D, j * 16 + n, q4i), 0, kStream);
 #pragma unroll
             for (int k = 0; k < 4; ++k) vc[4 * q4i + k] = a[k];
         }

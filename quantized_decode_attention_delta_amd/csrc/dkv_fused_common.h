@@ -172,7 +172,7 @@ __device__ inline LaneOffsets lane_offsets(const Geom &g, int lane, int j, int n
     const int row0 = n > 0 ? n - 1 : 0;        // token n of tile 0 (token 0 is the keyframe)
     o.k0 = (zero_kf_row && n == 0) ? 0x40000000 : (int)g.off_kcd + row0 * (D / 2) + 4 * j * NB;
     o.k1 = (int)g.off_kcd + (15 + n) * (D / 2) + 4 * j * NB;
-    o.v = (int)g.off_vcd + (j * 16 + n) * NCC * 4;
+    o.v = (int)g.off_vcd + vcode_piece(D, j * 16 + n, 0);
     return o;
 }
 
