@@ -27,7 +27,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
     constexpr int NB = D / 32, NCC = D / 16;
     const Geom g = make_geom(cfg);
     const int NT = g.kf / 32;
-    const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int split = grid_split(), h = blockIdx.y, b = blockIdx.z;
     const int lane = threadIdx.x, j = lane >> 4, n = lane & 15;
     const int G = g.G;
     const int L = min(seq_lens[b], g.cap_tokens);

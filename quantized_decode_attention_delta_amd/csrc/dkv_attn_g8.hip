@@ -836,7 +836,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
     static_assert(NBUF == 4, "the keyframe batches of 4 groups close on the last step of an unrolled round");
     constexpr int NSLOT = 8;
     const Geom g = make_geom(cfg);
-    const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int split = grid_split(), h = blockIdx.y, b = blockIdx.z;
     const int lane = threadIdx.x, j = lane >> 4, n = lane & 15;
     const int G = g.G;
     if (ap.positions) {
@@ -1094,7 +1094,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
     const Geom g = make_geom(cfg);
     const int kf = g.kf;
     const int lkf = 32 - __builtin_clz((unsigned)kf - 1u);       // kf <= 2^lkf
-    const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int split = grid_split(), h = blockIdx.y, b = blockIdx.z;
     const int lane = threadIdx.x, j = lane >> 4, n = lane & 15;
     const int G = g.G;
     const int L = min(seq_lens[b], g.cap_tokens);
@@ -1503,7 +1503,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
     static_assert(NBUF == 4, "rounds of 4 steps rotate the 4 fetch buffers");
     constexpr int NSLOT = 4;                  // a tile's side data lives from its staging to its V phase
     const Geom g = make_geom(cfg);
-    const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int split = grid_split(), h = blockIdx.y, b = blockIdx.z;
     const int lane = threadIdx.x, j = lane >> 4, n = lane & 15;
     const int G = g.G;
     const int kf = g.kf, NT = kf >> 5;
@@ -1789,7 +1789,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
                   float *__restrict__ ws, int nsplit, int chunk)
 {
     constexpr int NB = D / 32;
-    const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int split = grid_split(), h = blockIdx.y, b = blockIdx.z;
     const int lane = threadIdx.x, j = lane >> 4, n = lane & 15;
     const int G = cfg.n_q_heads / cfg.n_kv_heads;
     const int L = min(seq_lens[b], q40_ntiles(cfg) * 32);

@@ -40,7 +40,7 @@ __global__ void __launch_bounds__(kRefThreads)
     constexpr int nb = D / 32;
     constexpr int ACC = (kMaxG * D + kRefThreads - 1) / kRefThreads;
     const Geom g = make_geom(cfg);
-    const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int split = grid_split(), h = blockIdx.y, b = blockIdx.z;
     const int G = g.G;
     const int tid = threadIdx.x;
     const int L = min(seq_lens[b], g.cap_tokens);

@@ -272,6 +272,18 @@ __host__ __device__ inline int vcode_word(int D, int tau, int c, int bp)
 __host__ __device__ inline int vcode_nibble(int tau) { return (tau & 3) + 4 * (tau >> 4); }
 
 // ---- small device helpers --------------------------------------------------
+// Split (run) index of a workgroup of a (split, kv-head, batch) decode grid.
+// The chip hands workgroups to its 8 XCDs round-robin in linear order, so
+// with an even split count the same run positions of every row would land on
+// the same XCDs; in a ragged batch those are the first runs, the ones every
+// sequence has, and the XCDs that hold them get more work (10-13 % above the
+// mean on 1K..64K-token batches with 64 splits).  Rotating row r's runs by r
+// spreads them over all eight (an odd split count already does).
+__device__ inline int grid_split()
+{
+    const unsigned row = blockIdx.z * gridDim.y + blockIdx.y;
+    return (gridDim.x & 1u) ? (int)blockIdx.x : (int)((blockIdx.x + row) % gridDim.x);
+}
 // fp16 <-> fp32 through the compiler's _Float16 (v_cvt_f32_f16 / v_cvt_f16_f32,
 // round to nearest even, subnormals kept).
 __device__ inline float h2f(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }

@@ -171,7 +171,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
                float *__restrict__ ws, int nsplit, int chunk)
 {
     constexpr int NB = D / 32, NCC = D / 16;
-    const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int split = grid_split(), h = blockIdx.y, b = blockIdx.z;
     const int lane = threadIdx.x, j = lane >> 4, n = lane & 15;
     const int G = cfg.n_q_heads / cfg.n_kv_heads;
     const int ntiles = q40_ntiles(cfg);
@@ -410,7 +410,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
     constexpr int NB = D / 32;
     constexpr int CPL = D / 16;             // channels per lane per V token load
     constexpr int VW = CPL / 2;             // dwords per V load
-    const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int split = grid_split(), h = blockIdx.y, b = blockIdx.z;
     const int lane = threadIdx.x, j = lane >> 4, n = lane & 15;
     const int G = cfg.n_q_heads / cfg.n_kv_heads;
     const int L = min(seq_lens[b], cmp_ntiles(cfg) * 32);

@@ -374,7 +374,7 @@ __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
     constexpr int VS = 4 * D + 32;               // LDS bytes per V token row: [reference 2D][codes 2D][pad]
     constexpr int PS = 36;                       // floats per weight row
     const StridedLayout ly = strided_layout(cfg);
-    const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
+    const int split = grid_split(), h = blockIdx.y, b = blockIdx.z, lane = threadIdx.x;
     const int jj = lane >> 4, nn = lane & 15;
     const int Hq = cfg.n_q_heads, G = Hq / cfg.n_kv_heads;
     if (positions) {
