@@ -48,14 +48,14 @@ STATIC_CONFIGS = ("tiny", "8b", "long_kf32", "long_kf128", "long_kf512", "70b")
 # traffic is null.
 MEASURED_TRAFFIC = {
     "sources": {
-        "dkv_attn_g8.hip": "96271a83fa8964ead8d2c01870b060c823d936e3c4143b70e78c5f9b2c398389",
-        "dkv_fused_common.h": "0a7daad2743ec9dae84c3bcbf95cd8da24f7f8015ab1443f8b040fdaa51fefcb",
-        "dkv_common.h": "449c2571a6f5c87c7b0e87a22e301314a1a48d9589aa90f7c26c8087b7128561",
+        "dkv_attn_g8.hip": "1ed41445bf553025e7fbd3c0875cb7f4dfd005d9fa3d61902873c88975909983",
+        "dkv_fused_common.h": "c525d3bb9543ef7d48530cee671bc61a92708fc21a4bfb3bf73b9f44f9e1b74e",
+        "dkv_common.h": "57ec119a4bc9a80095dbe7da0e961e0c7a888ad6910487f1210451a0fa2dcbb9",
         "dkv_append.h": "be07c04e9857cdcd9f08e6a2526b04f9ce5e0a510bffa70e7ff091ce2d00e7dc",
         "dkv_q40.h": "d4b0a8142dfd210e9daa6a9ef282fe5ccb37c516b007f54681f8c9f93af0c73c",
         "dkv_api.cpp": "7a0bbb0fe9ac11b2187b9e7a013c4955bbec4f20e6e31eb6f283d6dc00ac43ac",
     },
-    "per_launch": {"mixed": 3161628285, "70b": 684872599, "long_kf512": 158624364, "long_kf128": 161529604},
+    "per_launch": {"mixed": 3161457517, "70b": 684899114, "long_kf512": 158607293, "long_kf128": 161545751},
 }
 
 
