@@ -53,9 +53,9 @@ MEASURED_TRAFFIC = {
         "dkv_common.h": "57ec119a4bc9a80095dbe7da0e961e0c7a888ad6910487f1210451a0fa2dcbb9",
         "dkv_append.h": "be07c04e9857cdcd9f08e6a2526b04f9ce5e0a510bffa70e7ff091ce2d00e7dc",
         "dkv_q40.h": "d4b0a8142dfd210e9daa6a9ef282fe5ccb37c516b007f54681f8c9f93af0c73c",
-        "dkv_api.cpp": "7a0bbb0fe9ac11b2187b9e7a013c4955bbec4f20e6e31eb6f283d6dc00ac43ac",
+        "dkv_api.cpp": "1f8eb005424fc0cd5858724d486d1af0683d7a8cfbac4a05bed2ff6a7318c0f6",
     },
-    "per_launch": {"mixed": 3161457517, "70b": 684899114, "long_kf512": 158607293, "long_kf128": 161545751},
+    "per_launch": {"mixed": 3161446633, "70b": 684889606, "long_kf512": 158607177, "long_kf128": 161538652},
 }
 
 

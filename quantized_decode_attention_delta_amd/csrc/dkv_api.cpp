@@ -3,6 +3,7 @@
 // launch; nothing here allocates device memory.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 #include <cmath>
 
@@ -74,12 +75,22 @@ struct Plan {
     int split_tokens;   // tokens per run (chunk units)
     int cap_tokens;     // tokens a sequence can hold: lengths are clamped to it
 };
-static Plan make_plan(int units_cap, int B, int Hkv, int max_units)
+static Plan make_plan(int units_cap, int B, int Hkv, int max_units, int min_units)
 {
     Plan p;
     const int64_t pairs = (int64_t)B * Hkv;
     int64_t ns = (2048 + pairs - 1) / pairs;
     if (ns < 1) ns = 1;
+    // at least min_units (128 tokens) per run while that leaves 256 or more
+    // workgroups: on a batch of a few (sequence, kv-head) pairs the
+    // 2048-workgroup target would make runs of one group, each paying a whole
+    // start-up (8B layer, 8 pairs of 4096 tokens: 32 runs of 4 groups against
+    // 128 runs of one, 0.0124 against 0.0139 ms per layer-step in a 32-layer
+    // graph).  Below 256 workgroups the runs' start-ups overlap anyway and
+    // fewer, longer runs only lengthen the launch (one 256-token sequence:
+    // 2 runs of 4 groups took 0.0088 ms per layer-step against 0.0071 for 8).
+    const int64_t ns_floor = std::max<int64_t>(units_cap / min_units, (256 + pairs - 1) / pairs);
+    if (ns > ns_floor) ns = ns_floor;
     if (ns > units_cap) ns = units_cap;
     if (ns < 1) ns = 1;
     p.chunk = (int)((units_cap + ns - 1) / ns);
@@ -98,6 +109,8 @@ static Plan make_plan(int units_cap, int B, int Hkv, int max_units)
 // at 1024-token runs, 0.691 at 512, 0.652 at 2048; of a random-walk batch of
 // the same shape: 0.656, 0.628 and 0.780 ms.
 constexpr int kRunTokens = 2048, kRunTokensPaged = 1024;
+// Shortest run: 128 tokens (whole units of unit_tokens).
+static int min_units(int unit_tokens) { return unit_tokens >= 128 ? 1 : 128 / unit_tokens; }
 static int run_units(const dkv_config &c, int unit_tokens)
 {
     const int rt = c.page_tokens > 0 ? kRunTokensPaged : kRunTokens;
@@ -106,7 +119,7 @@ static int run_units(const dkv_config &c, int unit_tokens)
 Plan delta_plan(const dkv_config &c)
 {
     const Geom g = make_geom(c);
-    Plan p = make_plan(g.ng_cap, c.batch, c.n_kv_heads, run_units(c, c.kf));
+    Plan p = make_plan(g.ng_cap, c.batch, c.n_kv_heads, run_units(c, c.kf), min_units(c.kf));
     p.split_tokens = p.chunk * c.kf;
     p.cap_tokens = g.cap_tokens;
     return p;
@@ -125,7 +138,7 @@ static bool merge_in_kernel(const dkv_config &c, const Plan &p)
 // the comparison caches (32-token tiles, contiguous or paged)
 Plan tile_plan(const dkv_config &c)
 {
-    Plan p = make_plan(cmp_ntiles(c), c.batch, c.n_kv_heads, run_units(c, 32));
+    Plan p = make_plan(cmp_ntiles(c), c.batch, c.n_kv_heads, run_units(c, 32), min_units(32));
     p.split_tokens = p.chunk * 32;
     p.cap_tokens = cmp_ntiles(c) * 32;
     return p;
@@ -135,7 +148,7 @@ Plan tile_plan(const dkv_config &c)
 Plan strided_plan(const dkv_config &c)
 {
     const int tiles = (c.max_tokens + 31) / 32;
-    Plan p = make_plan(tiles, c.batch, c.n_kv_heads, 64);
+    Plan p = make_plan(tiles, c.batch, c.n_kv_heads, 64, min_units(32));
     p.split_tokens = p.chunk * 32;
     p.cap_tokens = c.max_tokens;
     return p;
