@@ -212,7 +212,9 @@ dkv_status dkv_append_attn_decode(const dkv_config *cfg, void *cache, float *sta
 /* Split plan of dkv_attn_decode for cfg: *nsplit splits per (sequence,
  * kv-head), split s covering tokens [s * split_tokens, (s + 1) * split_tokens)
  * of the sequence.  Runs are at most 2048 tokens, 1024 in paged mode (ragged
- * serving batches: shorter runs keep the last partial round of runs short).
+ * serving batches: shorter runs keep the last partial round of runs short),
+ * and at least 128 tokens (whole keyframe intervals) while that leaves 256
+ * or more workgroups.
  * Errors: as dkv_check_config, DKV_ERR_ARG for null outputs. */
 dkv_status dkv_attn_decode_plan(const dkv_config *cfg, int32_t *nsplit, int32_t *split_tokens);
 

@@ -84,6 +84,18 @@ def test_sizes():
     assert dkv.dkv_attn_decode_plan(c) == (16, 2048)
     assert dkv.dkv_attn_decode_plan(_cfg(batch=64, n_q_heads=32, n_kv_heads=8, page_tokens=256, n_pages=8400,
                                          max_pages_per_seq=257)) == (65, 1024)
+    # runs of at least 128 tokens while 256 or more workgroups remain: the
+    # 8B layer (8 pairs of 4096 tokens) in 32 runs of 4 groups; a single
+    # 256-token sequence keeps its 8 runs of one group; kf = 512 runs stay one
+    # group (512 tokens) each
+    assert dkv.dkv_attn_decode_plan(_cfg(batch=1, n_q_heads=32, n_kv_heads=8, max_tokens=4096)) == (32, 128)
+    assert dkv.dkv_attn_decode_plan(_cfg(batch=1, n_q_heads=1, n_kv_heads=1, head_dim=64, max_tokens=256)) == (8, 32)
+    assert dkv.dkv_attn_decode_plan(_cfg(batch=8, n_q_heads=32, n_kv_heads=8, kf=512, max_tokens=16384)) == (32, 512)
+    assert dkv.dkv_attn_decode_plan(_cfg(batch=8, n_q_heads=32, n_kv_heads=8, max_tokens=16384)) == (32, 512)
+    for B, Hkv, S in ((1, 8, 4096), (2, 4, 1000), (3, 1, 70000), (64, 8, 65536), (1, 1, 64)):
+        ns, tk = dkv.dkv_attn_decode_plan(_cfg(batch=B, n_q_heads=Hkv, n_kv_heads=Hkv, max_tokens=S))
+        assert ns * tk >= S and (ns - 1) * tk < S                    # the runs tile the capacity
+        assert tk <= 2048 and (tk >= 128 or ns * B * Hkv >= 256 or ns * tk < 128 * 2)
     assert dkv.dkv_q4_0_cache_bytes(c) == 16 * 8 * 2 * 32768 * 128 // 32 * 18
     # paged comparison caches: a page of 256 tokens holds 8 tiles per kv-head
     cpg = _cfg(page_tokens=256, n_pages=5, max_pages_per_seq=3)
