@@ -244,6 +244,27 @@ def test_runs_of_every_length(kf, Hq, D):
     assert np.isfinite(got).all()
 
 
+@pytest.mark.parametrize("S,parity", [(4096, "even"), (4192, "odd")])
+def test_ragged_batch_every_pair(S, parity):
+    """A ragged batch (8 sequences of 1..S tokens, 8 kv-heads) with an even
+    split count, where each row's runs are rotated across the XCDs, and with an
+    odd one, where they are not: every (sequence, kv-head) pair's decode
+    attention against the oracle's float64 attention over its own encoding."""
+    print(f"ragged batch every pair S={S} ({parity} split count)", flush=True)
+    w = _case("8b", S=S, B=8, Hq=32, Hkv=8)
+    lens = np.random.default_rng(11).integers(1, S + 1, size=w.B).astype(np.int32)
+    lens[3] = S                                       # a full-length row
+    r = U.prefill(w, kf=32, lens=lens)
+    ns, _ = dkv.dkv_attn_decode_plan(r.cfg)
+    assert (ns % 2 == 0) == (parity == "even"), ns
+    enc = U.oracle_encode(w, 32, lens)
+    q = synth.queries(w)
+    got = U.attention(r, q)
+    ref = U.oracle_attention(enc, w, q, lens)
+    assert U.rel_err(got, ref) <= U.ATTN_TOL
+    assert np.isfinite(got).all()
+
+
 def test_stream_read_reads_every_word():
     """The streaming-read diagnostic: the XOR of its sink words is the XOR of
     every 32-bit word of the buffer (each word is read exactly once)."""
